@@ -1,0 +1,297 @@
+"""Thin Python binding over libdkv's C ABI (argument marshalling only).
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+path runs in libdkv's kernels.  Names follow the C functions:
+
+  project_rope_append  -> dkv_project_rope_append
+  decode_plan          -> dkv_decode_plan
+  decode_attn_split    -> dkv_decode_attn_split
+  merge_lse            -> dkv_merge_lse
+  host_alloc / HostBuffer -> dkv_host_alloc / dkv_host_free
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import KvDesc, PlanInfo, Tuning, BwResult, check, lib
+
+DKV_HOST_COHERENT = _lib.DKV_HOST_COHERENT
+DKV_HOST_NONCOHERENT = _lib.DKV_HOST_NONCOHERENT
+
+
+def _stream(stream):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return C.c_void_p(t.data_ptr())
+    if isinstance(t, np.ndarray):
+        return C.c_void_p(t.ctypes.data)
+    return C.c_void_p(int(t))
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def version() -> int:
+    return lib().dkv_version()
+
+
+def split_point(ratio: float, length: int) -> int:
+    out = C.c_int64()
+    check(lib().dkv_split_point(float(ratio), int(length), C.byref(out)))
+    return out.value
+
+
+class HostBuffer:
+    """Host-pinned block mapped into the GPU's address space (dkv_host_alloc)."""
+
+    def __init__(self, nbytes: int, flags: int = DKV_HOST_COHERENT):
+        h, d = C.c_void_p(), C.c_void_p()
+        check(lib().dkv_host_alloc(int(nbytes), int(flags), C.byref(h), C.byref(d)))
+        self.host_ptr = h.value
+        self.dev_ptr = d.value
+        self.nbytes = int(nbytes)
+        self.flags = flags
+
+    def numpy(self, dtype=np.uint16, shape=None) -> np.ndarray:
+        buf = (C.c_uint8 * self.nbytes).from_address(self.host_ptr)
+        a = np.frombuffer(buf, dtype=np.uint8).view(dtype)
+        return a.reshape(shape) if shape is not None else a
+
+    def free(self):
+        if self.host_ptr:
+            torch.cuda.synchronize()
+            check(lib().dkv_host_free(C.c_void_p(self.host_ptr)))
+            self.host_ptr = None
+            self.dev_ptr = None
+
+    def __del__(self):
+        try:
+            if self.host_ptr:
+                lib().dkv_host_free(C.c_void_p(self.host_ptr))
+        except Exception:
+            pass
+
+
+class KVCache:
+    """Two tier pools (host-pinned and HBM) plus the placement description.
+
+    Rows are tokens: [num_kv_heads][head_dim] bf16, K and V in separate pools.
+    ``page_table`` (paged placement) is an int32 array [batch][max_pages] with
+    entries phys << 1 | tier; it is uploaded to the device and kept on the host.
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, *, host_rows: int = 0, dev_rows: int = 0,
+                 page_size: int = 0, page_table=None, host_stride: int = 0, dev_stride: int = 0,
+                 host_flags: int = DKV_HOST_COHERENT, device: str = "cuda"):
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.page_size = int(page_size)
+        self.host_stride = int(host_stride)
+        self.dev_stride = int(dev_stride)
+        self.host_rows = int(host_rows)
+        self.dev_rows = int(dev_rows)
+        row_bytes = self.num_kv_heads * self.head_dim * 2
+        self.host_k = HostBuffer(max(1, self.host_rows) * row_bytes, host_flags) if self.host_rows else None
+        self.host_v = HostBuffer(max(1, self.host_rows) * row_bytes, host_flags) if self.host_rows else None
+        shape = (max(1, self.dev_rows), self.num_kv_heads, self.head_dim)
+        self.dev_k = torch.empty(shape, dtype=torch.bfloat16, device=device) if self.dev_rows else None
+        self.dev_v = torch.empty(shape, dtype=torch.bfloat16, device=device) if self.dev_rows else None
+        self.page_table_host = None
+        self.page_table = None
+        self.max_pages = 0
+        if self.page_size:
+            self.set_page_table(page_table)
+
+    def set_page_table(self, page_table):
+        pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+        assert pt.ndim == 2
+        self.page_table_host = pt
+        self.max_pages = int(pt.shape[1])
+        self.page_table = torch.from_numpy(pt).to("cuda")
+
+    def host_view(self, which: str) -> np.ndarray:
+        """uint16 numpy view [host_rows][Hkv][D] of a host pool ('k' or 'v')."""
+        buf = self.host_k if which == "k" else self.host_v
+        return buf.numpy(np.uint16, (self.host_rows, self.num_kv_heads, self.head_dim))
+
+    def desc(self) -> KvDesc:
+        d = KvDesc()
+        d.num_kv_heads = self.num_kv_heads
+        d.head_dim = self.head_dim
+        d.page_size = self.page_size
+        d.max_pages = self.max_pages
+        d.host_stride = self.host_stride
+        d.dev_stride = self.dev_stride
+        d.host_rows = self.host_rows
+        d.dev_rows = self.dev_rows
+        d.host_k = self.host_k.dev_ptr if self.host_k else None
+        d.host_v = self.host_v.dev_ptr if self.host_v else None
+        d.dev_k = self.dev_k.data_ptr() if self.dev_k is not None else None
+        d.dev_v = self.dev_v.data_ptr() if self.dev_v is not None else None
+        d.page_table = self.page_table.data_ptr() if self.page_table is not None else None
+        d.page_table_host = self.page_table_host.ctypes.data if self.page_table_host is not None else None
+        return d
+
+    def free(self):
+        for b in (self.host_k, self.host_v):
+            if b is not None:
+                b.free()
+
+
+def append_workspace_bytes(n_new: int, hidden: int, kv_dim: int) -> int:
+    return int(lib().dkv_append_workspace_bytes(int(n_new), int(hidden), int(kv_dim)))
+
+
+def project_rope_append(cache: KVCache, batch: int, seq_lens, ratio: float, seq_idx: torch.Tensor,
+                        pos: torch.Tensor, *, x=None, wk=None, wv=None, k_new=None, v_new=None,
+                        rope_theta: float = 1e4, workspace: torch.Tensor | None = None, stream=None):
+    """dkv_project_rope_append.  seq_lens / seq_idx / pos are device int32 tensors."""
+    n_new = int(seq_idx.numel())
+    hidden = int(x.shape[-1]) if x is not None else 0
+    ws_bytes = 0
+    if x is not None:
+        need = append_workspace_bytes(n_new, hidden, cache.num_kv_heads * cache.head_dim)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    d = cache.desc()
+    check(lib().dkv_project_rope_append(
+        C.byref(d), int(batch), _ptr(seq_lens), float(ratio), n_new, _ptr(seq_idx), _ptr(pos),
+        _ptr(x), hidden, _ptr(wk), _ptr(wv), _ptr(k_new), _ptr(v_new), float(rope_theta),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_plan(cache: KVCache, batch: int, num_q_heads: int, seq_lens, ratio: float) -> dict:
+    d = cache.desc()
+    sl = _host_i32(seq_lens)
+    info = PlanInfo()
+    check(lib().dkv_decode_plan(C.byref(d), int(batch), int(num_q_heads), _ptr(sl), float(ratio),
+                                C.byref(info)))
+    return info.as_dict()
+
+
+def plan_inspect(cache_or_desc, batch: int, num_q_heads: int, seq_lens, ratio: float, num_cus: int):
+    """dkv_plan_inspect: (items [n][5] int64, page_list, split_offsets, info)."""
+    d = cache_or_desc.desc() if isinstance(cache_or_desc, KVCache) else cache_or_desc
+    sl = _host_i32(seq_lens)
+    info = PlanInfo()
+    check(lib().dkv_plan_inspect(C.byref(d), int(batch), int(num_q_heads), _ptr(sl), float(ratio),
+                                 int(num_cus), None, 0, None, 0, None, C.byref(info)))
+    n = info.host_items + info.dev_items
+    items = np.zeros((max(n, 1), 5), dtype=np.int64)
+    npl = int(sum(int(x) for x in sl)) if d.page_size else 0
+    npl = (npl // max(1, d.page_size) + len(sl) + 1) if d.page_size else 1
+    plist = np.zeros(npl, dtype=np.int32)
+    offs = np.zeros(int(batch) + 1, dtype=np.int32)
+    check(lib().dkv_plan_inspect(C.byref(d), int(batch), int(num_q_heads), _ptr(sl), float(ratio),
+                                 int(num_cus), _ptr(items), n, _ptr(plist), len(plist), _ptr(offs),
+                                 C.byref(info)))
+    return items[:n], plist, offs, info.as_dict()
+
+
+@dataclass
+class DecodeBuffers:
+    workspace: torch.Tensor
+    part_o: torch.Tensor
+    part_lse: torch.Tensor
+    split_offsets: torch.Tensor
+    out_o: torch.Tensor
+    out_lse: torch.Tensor
+    info: dict
+
+
+def alloc_decode_buffers(cache: KVCache, batch: int, num_q_heads: int, seq_lens, ratio: float,
+                         device="cuda") -> DecodeBuffers:
+    info = decode_plan(cache, batch, num_q_heads, seq_lens, ratio)
+    S = max(1, info["num_splits"])
+    D = cache.head_dim
+    return DecodeBuffers(
+        workspace=torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=device),
+        part_o=torch.empty((S, num_q_heads, D), dtype=torch.float32, device=device),
+        part_lse=torch.empty((S, num_q_heads), dtype=torch.float32, device=device),
+        split_offsets=torch.empty(batch + 1, dtype=torch.int32, device=device),
+        out_o=torch.empty((batch, num_q_heads, D), dtype=torch.float32, device=device),
+        out_lse=torch.empty((batch, num_q_heads), dtype=torch.float32, device=device),
+        info=info,
+    )
+
+
+def decode_attn_split(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_lens, ratio: float,
+                      scale: float, rope_theta: float, *, bufs: DecodeBuffers | None = None,
+                      stream=None) -> DecodeBuffers:
+    """dkv_decode_attn_split.  q [B,Hq,D] bf16 and q_pos [B] int32 on the device;
+    seq_lens on the host.  Returns the buffers holding part_o/part_lse/split_offsets."""
+    B, Hq, D = q.shape
+    sl = _host_i32(seq_lens)
+    if bufs is None:
+        bufs = alloc_decode_buffers(cache, B, Hq, sl, ratio, q.device)
+    d = cache.desc()
+    check(lib().dkv_decode_attn_split(
+        C.byref(d), int(B), int(Hq), _ptr(q), _ptr(q_pos), _ptr(sl), float(ratio), float(scale),
+        float(rope_theta), _ptr(bufs.workspace), bufs.workspace.numel(), _ptr(bufs.part_o),
+        _ptr(bufs.part_lse), _ptr(bufs.split_offsets), int(bufs.part_o.shape[0]), _stream(stream)))
+    return bufs
+
+
+def merge_lse(part_o: torch.Tensor, part_lse: torch.Tensor, split_offsets: torch.Tensor, batch: int,
+              num_q_heads: int, head_dim: int, *, out_o=None, out_lse=None, stream=None):
+    """dkv_merge_lse -> (o [B,Hq,D] fp32, lse [B,Hq] fp32)."""
+    dev = part_o.device
+    if out_o is None:
+        out_o = torch.empty((batch, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((batch, num_q_heads), dtype=torch.float32, device=dev)
+    check(lib().dkv_merge_lse(_ptr(part_o), _ptr(part_lse), _ptr(split_offsets), int(batch),
+                              int(num_q_heads), int(head_dim), _ptr(out_o), _ptr(out_lse),
+                              _stream(stream)))
+    return out_o, out_lse
+
+
+def decode(cache: KVCache, q, q_pos, seq_lens, ratio, scale, rope_theta, *, bufs=None, stream=None):
+    """decode_attn_split followed by merge_lse on the same stream."""
+    B, Hq, D = q.shape
+    bufs = decode_attn_split(cache, q, q_pos, seq_lens, ratio, scale, rope_theta, bufs=bufs,
+                             stream=stream)
+    merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, B, Hq, D, out_o=bufs.out_o,
+              out_lse=bufs.out_lse, stream=stream)
+    return bufs.out_o, bufs.out_lse, bufs
+
+
+def set_tuning(**kw):
+    t = Tuning()
+    for k, v in kw.items():
+        setattr(t, k, v)
+    check(lib().dkv_set_tuning(C.byref(t)))
+
+
+def reset_tuning():
+    check(lib().dkv_set_tuning(None))
+
+
+def get_tuning() -> dict:
+    t = Tuning()
+    check(lib().dkv_get_tuning(C.byref(t)))
+    return {k: getattr(t, k) for k, _ in t._fields_}
+
+
+def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True, iters: int = 5,
+               dma_dst=None, dma_src_host=None, stream=None) -> dict:
+    r = BwResult()
+    check(lib().dkv_probe_read(C.c_void_p(int(src_dev_ptr)), int(nbytes), int(nwg), int(bool(nontemporal)),
+                               int(iters), _ptr(dma_dst), _ptr(dma_src_host), C.byref(r), _stream(stream)))
+    return {"read_gbs": r.read_gbs, "read_ms": r.read_ms, "dma_gbs": r.dma_gbs}

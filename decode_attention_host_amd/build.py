@@ -1,0 +1,72 @@
+"""Ahead-of-time build of libdkv.so for gfx950 with hipcc (no JIT, no torch extension).
+
+Usage: ``python -m decode_attention_host_amd.build`` (or ``build()`` from Python).
+The shared library lands next to this file so it ships with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdkv.so")
+
+SOURCES = ["dkv_api.cpp", "dkv_plan.cpp", "dkv_kernels.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-variable",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+# Device code: gfx950 only; packed fp32 instructions disabled.
+DEVICE = [
+    "--offload-arch=gfx950",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed ({r.returncode}) for {cmd[-3] if len(cmd) > 3 else cmd}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libdkv.so; returns its path."""
+    tmp = tempfile.mkdtemp(prefix="dkv_build_")
+    try:
+        objs = []
+        for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            obj = os.path.join(tmp, src + ".o")
+            if src.endswith(".hip"):
+                cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
+            else:
+                cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            _run(cmd)
+            objs.append(obj)
+        out_tmp = os.path.join(tmp, "libdkv.so")
+        cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        _run(cmd)
+        shutil.move(out_tmp, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,678 @@
+// dkv_api.cpp - the C ABI of libdkv: argument validation, plan cache, pinned
+// host allocation, bandwidth probe and kernel launches.
+//
+// Validation happens on the host before anything is enqueued; a failing call
+// launches nothing and leaves its message in dkv_last_error().
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <list>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "dkv.h"
+#include "dkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dkv_status set_err(dkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dkv_status ok() {
+  g_last_error.clear();
+  return DKV_OK;
+}
+
+dkv_status hip_err(hipError_t e, const char* what) {
+  return set_err(DKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool debug_validate() {
+  static const bool on = [] {
+    const char* v = getenv("DKV_DEBUG_VALIDATE");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+// ---------------------------------------------------------------- tuning
+std::mutex g_tune_mu;
+dkv_tuning g_tune{};
+uint64_t g_tune_gen = 1;
+
+dkv_tuning tuning_snapshot(uint64_t* gen) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  if (gen) *gen = g_tune_gen;
+  return g_tune;
+}
+
+int device_cus(int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (dev_out) *dev_out = dev;
+  return cus;
+}
+
+// ---------------------------------------------------------------- plan cache
+struct PlanEntry {
+  dkv::PlanLayout lay;
+  void* pinned = nullptr;  // immutable device image, source of every upload
+  size_t bytes = 0;
+};
+
+struct PlanCache {
+  std::mutex mu;
+  std::list<std::string> lru;
+  std::unordered_map<std::string, std::pair<std::shared_ptr<PlanEntry>, std::list<std::string>::iterator>>
+      map;
+  static constexpr size_t kCap = 64;
+};
+
+PlanCache& cache() {
+  static PlanCache* c = new PlanCache();  // never destroyed: entries may be in flight at exit
+  return *c;
+}
+
+template <class T>
+void put(std::string& k, const T& v) {
+  k.append(reinterpret_cast<const char*>(&v), sizeof(T));
+}
+
+uint64_t fnv1a(const void* data, size_t n, uint64_t h = 1469598103934665603ull) {
+  const uint8_t* p = static_cast<const uint8_t*>(data);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+dkv_status validate_desc(const dkv_kv_desc* kv) {
+  if (!kv) return set_err(DKV_ERR_INVALID, "kv descriptor is NULL");
+  if (kv->num_kv_heads < 1) return set_err(DKV_ERR_INVALID, "num_kv_heads must be >= 1");
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return set_err(DKV_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", kv->head_dim);
+  if (kv->page_size < 0 || (kv->page_size > 0 && (!is_pow2(kv->page_size) || kv->page_size > 1024)))
+    return set_err(DKV_ERR_INVALID, "page_size must be 0 or a power of two <= 1024 (got %d)",
+                   kv->page_size);
+  if (kv->host_rows < 0 || kv->dev_rows < 0)
+    return set_err(DKV_ERR_INVALID, "pool capacities must be >= 0");
+  if (kv->host_rows > 0 && (!kv->host_k || !kv->host_v))
+    return set_err(DKV_ERR_INVALID, "host_rows > 0 but host_k/host_v is NULL");
+  if (kv->dev_rows > 0 && (!kv->dev_k || !kv->dev_v))
+    return set_err(DKV_ERR_INVALID, "dev_rows > 0 but dev_k/dev_v is NULL");
+  if (kv->page_size == 0) {
+    if (kv->host_stride < 0 || kv->dev_stride < 0)
+      return set_err(DKV_ERR_INVALID, "strides must be >= 0");
+  } else {
+    if (kv->max_pages < 1) return set_err(DKV_ERR_INVALID, "paged layout needs max_pages >= 1");
+    if (!kv->page_table) return set_err(DKV_ERR_INVALID, "paged layout needs page_table");
+  }
+  const uintptr_t al = 16;
+  if ((uintptr_t)kv->host_k % al || (uintptr_t)kv->host_v % al || (uintptr_t)kv->dev_k % al ||
+      (uintptr_t)kv->dev_v % al)
+    return set_err(DKV_ERR_INVALID, "KV pools must be 16-byte aligned");
+  return DKV_OK;
+}
+
+dkv_status validate_ratio(double r) {
+  if (!(r >= 0.0 && r <= 1.0)) return set_err(DKV_ERR_INVALID, "offload_ratio must be in [0, 1]");
+  return DKV_OK;
+}
+
+// Builds or fetches the plan for a decode call.
+dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int32_t* seq_lens,
+                    double ratio, std::shared_ptr<PlanEntry>* out) {
+  if (batch < 1) return set_err(DKV_ERR_INVALID, "batch must be >= 1");
+  if (!seq_lens) return set_err(DKV_ERR_INVALID, "seq_lens is NULL");
+  if (hq < 1 || hq % kv->num_kv_heads)
+    return set_err(DKV_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                   hq, kv->num_kv_heads);
+  const int g = hq / kv->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return set_err(DKV_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", g);
+  if (kv->page_size > 0 && !kv->page_table_host)
+    return set_err(DKV_ERR_INVALID, "paged layout needs page_table_host to plan");
+  uint64_t gen = 0;
+  const dkv_tuning t = tuning_snapshot(&gen);
+  int dev = 0;
+  int cus = t.num_cus;
+  if (cus <= 0) {
+    cus = device_cus(&dev);
+    if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
+  }
+  std::string key;
+  key.reserve(128 + 4 * batch);
+  put(key, dev); put(key, cus); put(key, gen); put(key, batch); put(key, hq);
+  put(key, kv->num_kv_heads); put(key, kv->head_dim); put(key, kv->page_size); put(key, kv->max_pages);
+  put(key, kv->host_stride); put(key, kv->dev_stride); put(key, kv->host_rows); put(key, kv->dev_rows);
+  put(key, ratio);
+  key.append(reinterpret_cast<const char*>(seq_lens), sizeof(int32_t) * (size_t)batch);
+  if (kv->page_size > 0) {
+    uint64_t h = 1469598103934665603ull;
+    for (int b = 0; b < batch; ++b) {
+      const int64_t L = std::max(0, seq_lens[b]);
+      const int64_t npg = std::min<int64_t>((L + kv->page_size - 1) / kv->page_size, kv->max_pages);
+      h = fnv1a(kv->page_table_host + (int64_t)b * kv->max_pages, sizeof(int32_t) * npg, h);
+    }
+    put(key, h);
+  }
+  PlanCache& c = cache();
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    auto it = c.map.find(key);
+    if (it != c.map.end()) {
+      c.lru.splice(c.lru.begin(), c.lru, it->second.second);
+      *out = it->second.first;
+      return DKV_OK;
+    }
+  }
+  dkv::PlanInput in{};
+  in.batch = batch; in.hq = hq; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
+  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
+  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
+  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
+  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host; in.ratio = ratio;
+  in.num_cus = cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  auto e = std::make_shared<PlanEntry>();
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_plan(in, &e->lay, &blob, &err)) return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  e->bytes = blob.size();
+  hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
+  if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
+  memcpy(e->pinned, blob.data(), e->bytes);
+  std::vector<std::shared_ptr<PlanEntry>> evicted;
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    auto it = c.map.find(key);
+    if (it != c.map.end()) {  // another thread raced us: keep theirs
+      evicted.push_back(e);
+      e = it->second.first;
+    } else {
+      c.lru.push_front(key);
+      c.map.emplace(key, std::make_pair(e, c.lru.begin()));
+      while (c.map.size() > PlanCache::kCap) {
+        const std::string& victim = c.lru.back();
+        evicted.push_back(c.map[victim].first);
+        c.map.erase(victim);
+        c.lru.pop_back();
+      }
+    }
+  }
+  if (!evicted.empty()) {
+    // Evicted images may still feed queued uploads: wait for the device first.
+    (void)hipDeviceSynchronize();
+    for (auto& v : evicted)
+      if (v.use_count() == 1 && v->pinned) {
+        (void)hipHostFree(v->pinned);
+        v->pinned = nullptr;
+      }
+  }
+  *out = e;
+  return DKV_OK;
+}
+
+size_t qrot_bytes(int32_t batch, int32_t hq, int32_t d) { return (size_t)batch * hq * d * 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dkv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dkv_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+dkv_status dkv_split_point(double ratio, int64_t length, int64_t* n_host) {
+  if (!n_host) return set_err(DKV_ERR_INVALID, "n_host is NULL");
+  if (validate_ratio(ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (length < 0) return set_err(DKV_ERR_INVALID, "length must be >= 0");
+  *n_host = (int64_t)std::floor(ratio * (double)length);
+  return ok();
+}
+
+dkv_status dkv_set_tuning(const dkv_tuning* t) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  if (t) {
+    if (t->num_cus < 0 || t->host_wgs < 0 || t->dev_wgs < 0 || t->host_chunk < 0 ||
+        t->dev_chunk < 0 || !(t->host_bw_gbs >= 0) || !(t->dev_bw_gbs >= 0))
+      return set_err(DKV_ERR_INVALID, "tuning fields must be >= 0");
+    if (t->host_wgs > 65535 || t->dev_wgs > 65535)
+      return set_err(DKV_ERR_INVALID, "workgroup counts must be <= 65535");
+    g_tune = *t;
+  } else {
+    g_tune = dkv_tuning{};
+  }
+  ++g_tune_gen;
+  return ok();
+}
+
+dkv_status dkv_get_tuning(dkv_tuning* t) {
+  if (!t) return set_err(DKV_ERR_INVALID, "tuning is NULL");
+  *t = tuning_snapshot(nullptr);
+  return ok();
+}
+
+dkv_status dkv_decode_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                           const int32_t* seq_lens, double offload_ratio, dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  std::shared_ptr<PlanEntry> e;
+  st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  info->workspace_bytes = (int64_t)(L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim));
+  info->num_splits = L.num_splits;
+  info->host_items = L.n_host_items;
+  info->dev_items = L.n_dev_items;
+  info->host_wgs = L.host_wgs;
+  info->dev_wgs = L.dev_wgs;
+  info->host_chunk = L.host_chunk;
+  info->dev_chunk = L.dev_chunk;
+  info->host_bytes = L.host_bytes;
+  info->dev_bytes = L.dev_bytes;
+  return ok();
+}
+
+dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                            const int32_t* seq_lens, double offload_ratio, int32_t num_cus,
+                            int64_t* items, int32_t items_cap, int32_t* page_list,
+                            int32_t page_cap, int32_t* split_offsets, dkv_plan_info* info) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (batch < 1 || !seq_lens) return set_err(DKV_ERR_INVALID, "batch >= 1 and seq_lens required");
+  if (num_cus < 1) return set_err(DKV_ERR_INVALID, "num_cus must be >= 1");
+  if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads)
+    return set_err(DKV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  const dkv_tuning t = tuning_snapshot(nullptr);
+  dkv::PlanInput in{};
+  in.batch = batch; in.hq = num_q_heads; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
+  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
+  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
+  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
+  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host;
+  in.ratio = kv->page_size == 0 ? offload_ratio : 0.0;
+  in.num_cus = num_cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  dkv::PlanLayout L;
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_plan(in, &L, &blob, &err)) return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  const dkv::PlanItem* it = reinterpret_cast<const dkv::PlanItem*>(blob.data() + L.items_off);
+  const int n_items = L.n_host_items + L.n_dev_items;
+  if (items)
+    for (int i = 0; i < n_items && i < items_cap; ++i) {
+      items[5 * i + 0] = i < L.n_host_items ? 1 : 0;
+      items[5 * i + 1] = it[i].b;
+      items[5 * i + 2] = it[i].slot;
+      items[5 * i + 3] = it[i].n_tok;
+      items[5 * i + 4] = kv->page_size > 0 ? it[i].plist : it[i].row0;
+    }
+  if (page_list)
+    memcpy(page_list, blob.data() + L.plist_off, sizeof(int32_t) * std::min(L.n_plist, page_cap));
+  if (split_offsets) memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * (batch + 1));
+  if (info) {
+    info->workspace_bytes = (int64_t)(L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim));
+    info->num_splits = L.num_splits;
+    info->host_items = L.n_host_items;
+    info->dev_items = L.n_dev_items;
+    info->host_wgs = L.host_wgs;
+    info->dev_wgs = L.dev_wgs;
+    info->host_chunk = L.host_chunk;
+    info->dev_chunk = L.dev_chunk;
+    info->host_bytes = L.host_bytes;
+    info->dev_bytes = L.dev_bytes;
+  }
+  return ok();
+}
+
+dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                 const void* q, const int32_t* q_pos, const int32_t* seq_lens,
+                                 double offload_ratio, float scale, double rope_theta,
+                                 void* workspace, size_t workspace_bytes, float* part_o,
+                                 float* part_lse, int32_t* split_offsets, int32_t num_splits_cap,
+                                 void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (!q || !q_pos || !part_o || !part_lse || !split_offsets || !workspace)
+    return set_err(DKV_ERR_INVALID, "q, q_pos, part_o, part_lse, split_offsets and workspace are required");
+  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  std::shared_ptr<PlanEntry> e;
+  st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  const size_t need = L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim);
+  if (workspace_bytes < need)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (num_splits_cap < L.num_splits)
+    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %d splits", num_splits_cap, L.num_splits);
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_validate() && kv->page_size > 0) {
+    std::vector<int32_t> pt((size_t)batch * kv->max_pages);
+    hipError_t he = hipMemcpy(pt.data(), kv->page_table, pt.size() * 4, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_err(he, "debug copy of page_table");
+    for (int b = 0; b < batch; ++b) {
+      const int64_t npg = ((int64_t)seq_lens[b] + kv->page_size - 1) / kv->page_size;
+      for (int64_t j = 0; j < npg; ++j)
+        if (pt[(size_t)b * kv->max_pages + j] != kv->page_table_host[(size_t)b * kv->max_pages + j])
+          return set_err(DKV_ERR_INVALID, "page_table and page_table_host differ at [%d][%lld]", b,
+                         (long long)j);
+    }
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_err(he, "plan upload");
+  float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q), q_pos, q_rot, batch,
+                                      num_q_heads, kv->head_dim, rope_theta, scale_log2,
+                                      reinterpret_cast<const int32_t*>(ws + L.offsets_off),
+                                      split_offsets, stream);
+  if (he != hipSuccess) return hip_err(he, "rope_q launch");
+  dkv::AttnArgs a{};
+  a.host_items = reinterpret_cast<const dkv::PlanItem*>(ws + L.items_off);
+  a.dev_items = a.host_items + L.n_host_items;
+  a.plist = reinterpret_cast<const int32_t*>(ws + L.plist_off);
+  a.plan_offsets = reinterpret_cast<const int32_t*>(ws + L.offsets_off);
+  a.split_offsets = split_offsets;
+  a.n_host_units = L.n_host_items * kv->num_kv_heads;
+  a.n_dev_units = L.n_dev_items * kv->num_kv_heads;
+  a.host_wgs = L.host_wgs;
+  a.dev_wgs = L.dev_wgs;
+  a.host_k = static_cast<const uint16_t*>(kv->host_k);
+  a.host_v = static_cast<const uint16_t*>(kv->host_v);
+  a.dev_k = static_cast<const uint16_t*>(kv->dev_k);
+  a.dev_v = static_cast<const uint16_t*>(kv->dev_v);
+  a.host_rows = kv->host_rows;
+  a.dev_rows = kv->dev_rows;
+  a.page_table = kv->page_size > 0 ? kv->page_table : nullptr;
+  a.max_pages = kv->max_pages;
+  a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : -1;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_pos = q_pos;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.scale_log2 = scale_log2;
+  a.theta = rope_theta;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  he = (hipError_t)dkv::launch_attn_with_q(a, q_rot, stream);
+  if (he != hipSuccess) return hip_err(he, "attention launch");
+  return ok();
+}
+
+dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32_t* split_offsets,
+                         int32_t batch, int32_t num_q_heads, int32_t head_dim, float* out_o,
+                         float* out_lse, void* stream) {
+  if (!part_o || !part_lse || !split_offsets || !out_o)
+    return set_err(DKV_ERR_INVALID, "part_o, part_lse, split_offsets and out_o are required");
+  if (batch < 1 || num_q_heads < 1) return set_err(DKV_ERR_INVALID, "batch and num_q_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return set_err(DKV_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if ((int64_t)batch * num_q_heads > 0x7fffffff) return set_err(DKV_ERR_INVALID, "batch * heads too large");
+  dkv::MergeArgs a{};
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.split_offsets = split_offsets;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.head_dim = head_dim;
+  a.out_o = out_o;
+  a.out_lse = out_lse;
+  hipError_t he = (hipError_t)dkv::launch_merge(a, stream);
+  if (he != hipSuccess) return hip_err(he, "merge launch");
+  return ok();
+}
+
+size_t dkv_append_workspace_bytes(int32_t n_new, int32_t hidden, int32_t kv_dim) {
+  if (n_new <= 0 || hidden <= 0 || kv_dim <= 0) return 0;
+  const int64_t n_pad = ((int64_t)n_new + 15) / 16 * 16;
+  const int64_t ksplit = hidden / 256;
+  const int64_t part = ksplit * n_pad * 2 * kv_dim * 4;
+  const int64_t out = (int64_t)n_new * 2 * kv_dim * 4;
+  return (size_t)(((part + 255) / 256) * 256 + out);
+}
+
+dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch, const int32_t* seq_lens,
+                                   double offload_ratio, int32_t n_new, const int32_t* seq_idx,
+                                   const int32_t* pos, const void* x, int32_t hidden,
+                                   const void* wk, const void* wv, const void* k_new,
+                                   const void* v_new, double rope_theta, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (batch < 1) return set_err(DKV_ERR_INVALID, "batch must be >= 1");
+  if (n_new < 0) return set_err(DKV_ERR_INVALID, "n_new must be >= 0");
+  if (n_new == 0) return ok();
+  if (!seq_idx || !pos) return set_err(DKV_ERR_INVALID, "seq_idx and pos are required");
+  if (kv->page_size == 0) {
+    if (!seq_lens) return set_err(DKV_ERR_INVALID, "contiguous placement needs seq_lens");
+    if (validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  }
+  if (!(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "rope_theta must be > 0");
+  const int32_t kvd = kv->num_kv_heads * kv->head_dim;
+  const bool proj = x != nullptr;
+  if (proj) {
+    if (!wk || !wv) return set_err(DKV_ERR_INVALID, "projection mode needs wk and wv");
+    if (hidden < 256 || hidden % 256)
+      return set_err(DKV_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 256", hidden);
+    if ((2 * kvd) % 64) return set_err(DKV_ERR_UNSUPPORTED, "2*Hkv*D must be a multiple of 64");
+    const size_t need = dkv_append_workspace_bytes(n_new, hidden, kvd);
+    if (!workspace || workspace_bytes < need)
+      return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+    if ((uintptr_t)x % 16 || (uintptr_t)wk % 16 || (uintptr_t)wv % 16)
+      return set_err(DKV_ERR_INVALID, "x, wk, wv must be 16-byte aligned");
+  } else {
+    if (!k_new || !v_new) return set_err(DKV_ERR_INVALID, "no-projection mode needs k_new and v_new");
+    if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
+      return set_err(DKV_ERR_INVALID, "k_new, v_new must be 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_validate()) {
+    std::vector<int32_t> si(n_new), ps(n_new), sl(kv->page_size == 0 ? batch : 0);
+    hipError_t he = hipStreamSynchronize(s);
+    if (he == hipSuccess) he = hipMemcpy(si.data(), seq_idx, 4 * (size_t)n_new, hipMemcpyDeviceToHost);
+    if (he == hipSuccess) he = hipMemcpy(ps.data(), pos, 4 * (size_t)n_new, hipMemcpyDeviceToHost);
+    if (he == hipSuccess && !sl.empty())
+      he = hipMemcpy(sl.data(), seq_lens, 4 * (size_t)batch, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_err(he, "debug copy of append metadata");
+    std::vector<int32_t> pt;
+    if (kv->page_size > 0) {
+      pt.resize((size_t)batch * kv->max_pages);
+      he = hipMemcpy(pt.data(), kv->page_table, pt.size() * 4, hipMemcpyDeviceToHost);
+      if (he != hipSuccess) return hip_err(he, "debug copy of page_table");
+    }
+    for (int i = 0; i < n_new; ++i) {
+      const int b = si[i], p = ps[i];
+      if (b < 0 || b >= batch || p < 0) return set_err(DKV_ERR_INVALID, "token %d: bad sequence/position", i);
+      int64_t row;
+      bool host;
+      if (kv->page_size == 0) {
+        const int L = sl[b];
+        if (p >= L) return set_err(DKV_ERR_INVALID, "token %d: position %d >= seq_len %d", i, p, L);
+        const int64_t nh = (int64_t)std::floor(offload_ratio * (double)L);
+        host = p < nh;
+        if (host && nh > kv->host_stride) return set_err(DKV_ERR_INVALID, "token %d: host_stride too small", i);
+        if (!host && L - nh > kv->dev_stride) return set_err(DKV_ERR_INVALID, "token %d: dev_stride too small", i);
+        row = host ? (int64_t)b * kv->host_stride + p : (int64_t)b * kv->dev_stride + (p - nh);
+      } else {
+        const int lp = p / kv->page_size;
+        if (lp >= kv->max_pages) return set_err(DKV_ERR_INVALID, "token %d: page index beyond max_pages", i);
+        const int32_t e = pt[(size_t)b * kv->max_pages + lp];
+        if (e < 0) return set_err(DKV_ERR_INVALID, "token %d: unmapped page", i);
+        host = (e & 1) != 0;
+        row = (int64_t)(e >> 1) * kv->page_size + p % kv->page_size;
+      }
+      if (row >= (host ? kv->host_rows : kv->dev_rows))
+        return set_err(DKV_ERR_INVALID, "token %d: row %lld beyond the pool", i, (long long)row);
+    }
+  }
+  dkv::AppendArgs a{};
+  a.batch = batch;
+  a.n_new = n_new;
+  a.seq_lens = seq_lens;
+  a.ratio = offload_ratio;
+  a.seq_idx = seq_idx;
+  a.pos = pos;
+  a.host_k = static_cast<uint16_t*>(kv->host_k);
+  a.host_v = static_cast<uint16_t*>(kv->host_v);
+  a.dev_k = static_cast<uint16_t*>(kv->dev_k);
+  a.dev_v = static_cast<uint16_t*>(kv->dev_v);
+  a.host_rows = kv->host_rows;
+  a.dev_rows = kv->dev_rows;
+  a.host_stride = kv->host_stride;
+  a.dev_stride = kv->dev_stride;
+  a.page_table = kv->page_table;
+  a.max_pages = kv->max_pages;
+  a.page_size = kv->page_size;
+  a.hkv = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.theta = rope_theta;
+  if (proj) {
+    dkv::ProjArgs p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.wk = static_cast<const uint16_t*>(wk);
+    p.wv = static_cast<const uint16_t*>(wv);
+    p.n_new = n_new;
+    p.n_pad = (n_new + 15) / 16 * 16;
+    p.hidden = hidden;
+    p.kv_dim = kvd;
+    p.ksplit = hidden / 256;
+    p.kslice = 256;
+    const int64_t part = (int64_t)p.ksplit * p.n_pad * 2 * kvd * 4;
+    p.partial = static_cast<float*>(workspace);
+    p.out = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ((part + 255) / 256) * 256);
+    hipError_t he = (hipError_t)dkv::launch_project(p, stream);
+    if (he != hipSuccess) return hip_err(he, "projection launch");
+    a.kv_proj = p.out;
+  } else {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+  }
+  hipError_t he = (hipError_t)dkv::launch_append(a, stream);
+  if (he != hipSuccess) return hip_err(he, "append launch");
+  return ok();
+}
+
+dkv_status dkv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return set_err(DKV_ERR_INVALID, "host_ptr and dev_ptr are required");
+  if (bytes == 0) return set_err(DKV_ERR_INVALID, "bytes must be > 0");
+  if (flags > DKV_HOST_NONCOHERENT) return set_err(DKV_ERR_INVALID, "unknown flags %u", flags);
+  *host_ptr = nullptr;
+  *dev_ptr = nullptr;
+  unsigned hf = hipHostMallocMapped | hipHostMallocPortable |
+                (flags == DKV_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hf);
+  if (e != hipSuccess || !h)
+    return set_err(DKV_ERR_NOMEM, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return hip_err(e, "hipHostGetDevicePointer");
+  }
+  *host_ptr = h;
+  *dev_ptr = d;
+  return ok();
+}
+
+dkv_status dkv_host_free(void* host_ptr) {
+  if (!host_ptr) return ok();
+  hipError_t e = hipHostFree(host_ptr);
+  if (e != hipSuccess) return hip_err(e, "hipHostFree");
+  return ok();
+}
+
+dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t nontemporal,
+                          int32_t iters, void* dma_dst, const void* dma_src_host,
+                          dkv_bw_result* out, void* stream) {
+  if (!src || !out) return set_err(DKV_ERR_INVALID, "src and out are required");
+  if (bytes < 16 || bytes % 16) return set_err(DKV_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if (nwg < 1 || nwg > 65535 || iters < 1) return set_err(DKV_ERR_INVALID, "nwg in [1,65535], iters >= 1");
+  if ((uintptr_t)src % 16) return set_err(DKV_ERR_INVALID, "src must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  float* sink = nullptr;
+  hipError_t e = hipMalloc(&sink, 256);
+  if (e != hipSuccess) return hip_err(e, "probe sink");
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
+  dkv_status st = DKV_OK;
+  e = (hipError_t)dkv::launch_probe_read(src, bytes, nwg, nontemporal, sink, stream);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int i = 0; i < iters && e == hipSuccess; ++i)
+    e = (hipError_t)dkv::launch_probe_read(src, bytes, nwg, nontemporal, sink, stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e != hipSuccess) {
+    st = hip_err(e, "probe kernel");
+  } else {
+    out->read_ms = ms / iters;
+    out->read_gbs = (double)bytes / (out->read_ms * 1e6);
+    out->dma_gbs = 0.0;
+    if (dma_dst && dma_src_host) {
+      e = hipMemcpyAsync(dma_dst, dma_src_host, bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(e0, s);
+      for (int i = 0; i < iters && e == hipSuccess; ++i)
+        e = hipMemcpyAsync(dma_dst, dma_src_host, bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(e1, s);
+      if (e == hipSuccess) e = hipEventSynchronize(e1);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+      if (e != hipSuccess)
+        st = hip_err(e, "probe DMA");
+      else
+        out->dma_gbs = (double)bytes / ((ms / iters) * 1e6);
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
+  if (st != DKV_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

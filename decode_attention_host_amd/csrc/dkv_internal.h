@@ -1,0 +1,174 @@
+// dkv_internal.h - structures shared by the host runtime (C++) and the gfx950
+// kernels (HIP).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace dkv {
+
+// Tokens staged per tile by the attention kernel (4 waves x 16 tokens).
+constexpr int kTile = 64;
+// Threads per attention / merge / append workgroup.
+constexpr int kThreads = 256;
+
+// One work item: a run of tokens of one sequence that all live in one tier.
+// The attention kernel processes every item once per KV head ("unit").
+struct PlanItem {
+  int32_t b;      // sequence
+  int32_t slot;   // split slot (row of part_o / part_lse)
+  int32_t n_tok;  // tokens in the item (>= 1)
+  int32_t plist;  // paged: index of the item's first entry in the page list
+  int64_t row0;   // contiguous: pool row of the item's first token
+  int64_t pad;
+};
+static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
+
+// Host-side result of planning; the device image is `blob` (items, then the
+// page list, then split offsets), uploaded into the caller's workspace.
+struct PlanLayout {
+  int32_t n_host_items = 0;
+  int32_t n_dev_items = 0;
+  int32_t num_splits = 0;
+  int32_t batch = 0;
+  int32_t host_wgs = 0;
+  int32_t dev_wgs = 0;
+  int32_t host_chunk = 0;
+  int32_t dev_chunk = 0;
+  int64_t host_bytes = 0;
+  int64_t dev_bytes = 0;
+  size_t items_off = 0;    // byte offsets inside the blob
+  size_t plist_off = 0;
+  size_t offsets_off = 0;
+  size_t blob_bytes = 0;
+  int32_t n_plist = 0;
+};
+
+// Arguments of the split attention kernel.
+struct AttnArgs {
+  const PlanItem* host_items;
+  const PlanItem* dev_items;
+  const int32_t* plist;          // paged: logical page indices
+  const int32_t* plan_offsets;   // [batch+1] split offsets (in the workspace)
+  int32_t* split_offsets;        // [batch+1] caller copy (written by block 0)
+  int32_t n_host_units;          // host items x Hkv
+  int32_t n_dev_units;           // dev items x Hkv
+  int32_t host_wgs;
+  int32_t dev_wgs;
+  const uint16_t* host_k;
+  const uint16_t* host_v;
+  const uint16_t* dev_k;
+  const uint16_t* dev_v;
+  int64_t host_rows;
+  int64_t dev_rows;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t page_shift;            // log2(page_size) (paged)
+  const uint16_t* q;             // [batch][Hq][D]
+  const int32_t* q_pos;          // [batch]
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  float scale_log2;              // scale * log2(e)
+  float pad0;
+  double theta;
+  float* part_o;                 // [S][Hq][D]
+  float* part_lse;               // [S][Hq]
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* split_offsets;
+  int32_t batch;
+  int32_t hq;
+  int32_t head_dim;
+  int32_t pad;
+  float* out_o;
+  float* out_lse;
+};
+
+struct AppendArgs {
+  int32_t batch;
+  int32_t n_new;
+  const int32_t* seq_lens;       // contiguous only
+  double ratio;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const uint16_t* k_new;         // [n_new][Hkv][D] bf16, or NULL in projection mode
+  const uint16_t* v_new;
+  const float* kv_proj;          // projection mode: [n_new][2*Hkv*D] fp32 (K then V)
+  uint16_t* host_k;
+  uint16_t* host_v;
+  uint16_t* dev_k;
+  uint16_t* dev_v;
+  int64_t host_rows;
+  int64_t dev_rows;
+  int64_t host_stride;
+  int64_t dev_stride;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t page_size;             // 0 = contiguous
+  int32_t hkv;
+  int32_t head_dim;
+  double theta;
+};
+
+struct ProjArgs {
+  const uint16_t* x;     // [n_new][hidden]
+  const uint16_t* wk;    // [hidden][kv_dim]
+  const uint16_t* wv;
+  float* partial;        // [ksplit][n_pad][2*kv_dim]
+  float* out;            // [n_new][2*kv_dim] (reduced)
+  int32_t n_new;
+  int32_t n_pad;         // n_new rounded up to 16
+  int32_t hidden;
+  int32_t kv_dim;
+  int32_t ksplit;
+  int32_t kslice;        // hidden / ksplit
+};
+
+// Launchers (dkv_kernels.hip).  They return hipError_t as int.
+int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
+                  double theta, float scale_log2, const int32_t* plan_offsets,
+                  int32_t* split_offsets, void* stream);
+int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+int launch_append(const AppendArgs& a, void* stream);
+int launch_project(const ProjArgs& a, void* stream);
+int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
+                      void* stream);
+
+// Planner (dkv_plan.cpp), no HIP calls.
+struct PlanInput {
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages;
+  int64_t host_stride;
+  int64_t dev_stride;
+  int64_t host_rows;
+  int64_t dev_rows;
+  const int32_t* seq_lens;        // host
+  const int32_t* page_table_host; // host, paged
+  double ratio;
+  int32_t num_cus;
+  int32_t host_wgs;               // tuning (0 = default)
+  int32_t dev_wgs;
+  int32_t host_chunk;
+  int32_t dev_chunk;
+  double host_bw;
+  double dev_bw;
+};
+
+// Builds the plan and its device image; on failure returns false with `err`.
+bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
+                std::string* err);
+
+}  // namespace dkv

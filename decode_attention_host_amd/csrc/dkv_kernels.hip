@@ -1,0 +1,717 @@
+// dkv_kernels.hip - gfx950 kernels of the zero-copy split decode attention path.
+//
+//   rope_q_kernel       rotate each query head (Neox RoPE, fp64 angle) once per call
+//   attn_split_kernel   stream K/V tiles of one tier into LDS, Q.K on MFMA,
+//                       online softmax, P.V on the vector ALUs, write (o, lse)
+//   merge_lse_kernel    combine per-split partials by log-sum-exp
+//   append_kernel       Neox RoPE of new keys (fp64) + bf16 store into the cache slot
+//   proj_kernel         new-token K/V projection on MFMA (split over the hidden dim)
+//   probe_read_kernel   streaming-read bandwidth probe with the attention load pattern
+//
+// Method sources (page, section): DirectKV README, introduction (fused projection,
+// Neox RoPE and attention reading KV from CPU-pinned buffers) and Attribution
+// (online softmax; KV streamed from CPU memory with no GPU staging buffer);
+// SplitKernel README, Overview and Key Features (direct access of the remote
+// tier into on-chip memory; attention over a host/device partitioned KV cache).
+//
+// Design notes for CDNA4:
+//   * 64-lane waves, 256-thread workgroups (4 waves).  A tile is 64 tokens of one
+//     KV head: each thread moves D/32 16-byte chunks of K and of V per tile with
+//     coalesced loads (host-tier loads are non-temporal), stores them into LDS,
+//     and each wave then owns 16 of the 64 tokens.
+//   * Q.K^T runs on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims from LDS,
+//     B = the group's query heads; each rotated query (fp32) is split into a
+//     high and a low bf16 part placed in columns h and h+8, so the product keeps
+//     ~16 bits of the query and fp32 accumulation.
+//   * P.V runs on the vector ALUs with one or two output dims per lane: values
+//     are exact bf16, weights fp32, accumulation fp32.
+//   * Host-role and HBM-role workgroups are disjoint (blockIdx below / above the
+//     host workgroup count) so both tiers stream concurrently.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dkv_internal.h"
+
+namespace dkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// double -> bf16 bits with one rounding (nearest, ties to even).
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  const int e = (int)((u >> 52) & 0x7ff);
+  if (e == 0x7ff) return sign | ((u << 12) ? 0x7fc0u : 0x7f80u);
+  const double ax = fabs(x);
+  if (ax < 0x1p-126) {
+    // subnormal bf16 grid: quantum 2^-133
+    const double q = rint(ax * 0x1p133);  // 0 .. 128 (128 = smallest normal)
+    return sign | (uint32_t)q;
+  }
+  const uint64_t mant = u & ((1ull << 52) - 1);
+  uint64_t keep = mant >> 45;
+  const uint64_t rest = mant & ((1ull << 45) - 1);
+  const uint64_t half = 1ull << 44;
+  uint32_t em = (uint32_t)((e - 1023 + 127) << 7) | (uint32_t)keep;
+  if (rest > half || (rest == half && (keep & 1))) em += 1;  // may carry into the exponent
+  if (em >= 0x7f80u) em = 0x7f80u;                           // overflow -> inf
+  return sign | em;
+}
+
+// ---------------------------------------------------------------------------
+// Query rotation: q_rot[b][h][d] = scale*log2(e) * RoPE(q[b][h], q_pos[b])[d].
+// Angles pos * theta^(-2i/D) and sin/cos in fp64.  Block 0 also copies the
+// split offsets of the plan to the caller's array.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
+                                                          const int32_t* __restrict__ q_pos,
+                                                          float* __restrict__ q_rot, int hq, int d,
+                                                          double theta, float scale_log2,
+                                                          const int32_t* __restrict__ plan_offsets,
+                                                          int32_t* __restrict__ split_offsets,
+                                                          int batch) {
+  const int b = blockIdx.x;
+  const int half = d >> 1;
+  if (b == 0 && split_offsets)
+    for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
+  const double pos = (double)q_pos[b];
+  for (int idx = threadIdx.x; idx < hq * half; idx += blockDim.x) {
+    const int h = idx / half, i = idx - h * half;
+    const double f = pow(theta, -2.0 * (double)i / (double)d);
+    double s, c;
+    sincos(pos * f, &s, &c);
+    const uint16_t* qh = q + ((size_t)b * hq + h) * d;
+    const double xl = (double)bf16_to_f32(qh[i]);
+    const double xh = (double)bf16_to_f32(qh[i + half]);
+    float* o = q_rot + ((size_t)b * hq + h) * d;
+    o[i] = (float)(xl * c - xh * s) * scale_log2;
+    o[i + half] = (float)(xh * c + xl * s) * scale_log2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split decode attention.
+// ---------------------------------------------------------------------------
+template <int D>
+struct AttnShape {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kPitch = kRowBytes + 16;          // LDS row pitch (bytes)
+  static constexpr int kChunksPerRow = D / 8;            // 16-byte chunks per row
+  static constexpr int kChunksPerThread = kTile * kChunksPerRow / kThreads;  // D/32
+  static constexpr int kKSteps = D / 32;                 // MFMA k-steps per key
+  static constexpr int kDimsPerLane = D / 64;            // P.V output dims per lane
+};
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const float* __restrict__ q_rot) {
+  using S = AttnShape<D>;
+  constexpr int NC = S::kChunksPerThread;
+  constexpr int KS = S::kKSteps;
+  constexpr int DPL = S::kDimsPerLane;
+  static_assert(G >= 1 && G <= 8, "group size");
+  // per-wave state dump at the end of a unit must fit in the K tile buffer
+  static_assert(4 * G * (D + 2) * 4 <= kTile * S::kPitch, "epilogue scratch");
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * S::kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
+  __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
+  __shared__ float a_lds[4][8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;     // MFMA column / row-in-tile
+  const int j4 = lane >> 4;    // 0..3
+
+  const bool host_role = (int)blockIdx.x < a.host_wgs;
+  const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
+  const int nwg = host_role ? a.host_wgs : a.dev_wgs;
+  const int nunits = host_role ? a.n_host_units : a.n_dev_units;
+  const PlanItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
+  const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
+  const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
+  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
+  const int64_t row_elems = (int64_t)a.hkv * D;
+
+  for (int u = wg; u < nunits; u += nwg) {
+    const int item_idx = u / a.hkv;
+    const int kvh = u - item_idx * a.hkv;
+    const PlanItem it = items[item_idx];
+    const int ntiles = (it.n_tok + kTile - 1) / kTile;
+
+    // ---- query operand: columns h (high bf16 part) and h+8 (low part)
+    bf16x8_t qb[KS];
+    {
+      const int hsel = n & 7;
+      const bool active = hsel < G;
+      const float* qr = q_rot + ((size_t)it.b * a.hq + kvh * G + (active ? hsel : 0)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 32 + j4 * 8;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = active ? qr[d0 + 2 * e] : 0.f;
+          const float x1 = active ? qr[d0 + 2 * e + 1] : 0.f;
+          uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
+          if (n >= 8) {  // low part: residual after the high part
+            b0 = f32_to_bf16(x0 - bf16_to_f32(b0));
+            b1 = f32_to_bf16(x1 - bf16_to_f32(b1));
+          }
+          w[e] = b0 | (b1 << 16);
+        }
+        u32x4 wv = {w[0], w[1], w[2], w[3]};
+        qb[ks] = __builtin_bit_cast(bf16x8_t, wv);
+      }
+    }
+
+    float m_run = -INFINITY;  // per lane: state of head (n & 7)
+    float l_run = 0.f;
+    float acc[G][DPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+
+    u32x4 kreg[NC], vreg[NC];
+
+    auto load_tile = [&](int tile) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int r = chunk / S::kChunksPerRow;
+        const int col = chunk - r * S::kChunksPerRow;
+        const int tok = tile * kTile + r;
+        bool valid = tok < it.n_tok;
+        int64_t row = 0;
+        if (PAGED) {
+          if (valid) {
+            const int lp = a.plist[it.plist + (tok >> a.page_shift)];
+            const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
+            const int64_t phys = (int64_t)(e >> 1);
+            row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
+            valid = e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
+          }
+        } else {
+          row = it.row0 + tok;
+        }
+        const int64_t off = (row * a.hkv + kvh) * D + col * 8;
+        if (valid) {
+          const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + off);
+          const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + off);
+          if (host_role) {
+            kreg[c] = __builtin_nontemporal_load(kp);
+            vreg[c] = __builtin_nontemporal_load(vp);
+          } else {
+            kreg[c] = *kp;
+            vreg[c] = *vp;
+          }
+        } else {
+          kreg[c] = u32x4{0u, 0u, 0u, 0u};
+          vreg[c] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+
+    load_tile(0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      __syncthreads();  // previous tile's readers are done
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int r = chunk / S::kChunksPerRow;
+        const int col = chunk - r * S::kChunksPerRow;
+        *reinterpret_cast<u32x4*>(k_lds + r * S::kPitch + col * 16) = kreg[c];
+        *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
+      }
+      __syncthreads();
+      if (tile + 1 < ntiles) load_tile(tile + 1);
+
+      // ---- scores for this wave's 16 tokens: rows = tokens, columns = heads
+      floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = k_lds + (wave * 16 + n) * S::kPitch + j4 * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + ks * 64);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qb[ks], sc,
+                                                     0, 0, 0);
+      }
+      const int tok0 = tile * kTile + wave * 16 + j4 * 4;
+      float s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = sc[i] + __shfl_xor(sc[i], 8);
+        s[i] = (tok0 + i < it.n_tok) ? v : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (s[i] == -INFINITY) ? 0.f : exp2f(s[i] - m_new);
+        ps += p[i];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      if (n < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p_lds[wave][j4 * 4 + i][n] = p[i];
+        if (j4 == 0) a_lds[wave][n] = alpha;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- P.V: lane owns dims lane*DPL .. lane*DPL+DPL-1
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = a_lds[wave][h];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
+      }
+      const uint8_t* vbase = v_lds + (wave * 16) * S::kPitch + lane * DPL * 2;
+#pragma unroll 4
+      for (int t = 0; t < 16; ++t) {
+        float vv[DPL];
+        if (DPL == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vbase + t * S::kPitch);
+          vv[0] = __uint_as_float(w << 16);
+          vv[DPL - 1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint16_t*>(vbase + t * S::kPitch);
+          vv[0] = __uint_as_float(w << 16);
+        }
+        float pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pp[h] = p_lds[wave][t][h];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pp[h], vv[e], acc[h][e]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- combine the four waves of this unit and write the partial
+    __syncthreads();
+    float* sm_m = reinterpret_cast<float*>(k_lds);   // [4][G]
+    float* sm_l = sm_m + 4 * G;                      // [4][G]
+    float* sm_acc = sm_l + 4 * G;                    // [4][G][D]
+    if (lane < G) {
+      sm_m[wave * G + lane] = m_run;
+      sm_l[wave * G + lane] = l_run;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sm_acc[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int h = idx / D, d = idx - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * G + h]);
+      float o = 0.f, lsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = sm_m[w * G + h];
+          const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+          lsum += sw * sm_l[w * G + h];
+          o += sw * sm_acc[(w * G + h) * D + d];
+        }
+        o = o / lsum;
+      }
+      const int hq_idx = kvh * G + h;
+      a.part_o[((size_t)it.slot * a.hq + hq_idx) * D + d] = o;
+      if (d == 0)
+        a.part_lse[(size_t)it.slot * a.hq + hq_idx] =
+            (M == -INFINITY) ? -INFINITY : (M + log2f(lsum)) * 0.69314718055994530942f;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LSE merge: one workgroup per (b, h); wave w folds splits w, w+4, ... with an
+// online rescale, then the four waves combine through LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
+  constexpr int DPL = D / 64;
+  constexpr float kLog2e = 1.44269504088896340736f;
+  __shared__ float sm_m[4], sm_l[4];
+  __shared__ float sm_o[4][D];
+  const int bh = blockIdx.x;
+  const int b = bh / a.hq, h = bh - b * a.hq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
+  float M = -INFINITY, L = 0.f, o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int s = s0 + wave; s < s1; s += 4) {
+    const float l2 = a.part_lse[(size_t)s * a.hq + h] * kLog2e;
+    if (l2 == -INFINITY) continue;
+    const float m_new = fmaxf(M, l2);
+    const float so = (M == -INFINITY) ? 0.f : exp2f(M - m_new);
+    const float w = exp2f(l2 - m_new);
+    const float* po = a.part_o + ((size_t)s * a.hq + h) * D + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = o[e] * so + w * po[e];
+    L = L * so + w;
+    M = m_new;
+  }
+  if (lane == 0) {
+    sm_m[wave] = M;
+    sm_l[wave] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) sm_o[wave][lane * DPL + e] = o[e];
+  __syncthreads();
+  if (wave == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, sm_m[w]);
+    float Lt = 0.f, ot[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ot[e] = 0.f;
+    if (Mt != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sw = (sm_m[w] == -INFINITY) ? 0.f : exp2f(sm_m[w] - Mt);
+        Lt += sw * sm_l[w];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ot[e] += sw * sm_o[w][lane * DPL + e];
+      }
+    }
+    float* out = a.out_o + ((size_t)b * a.hq + h) * D + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) out[e] = (Mt == -INFINITY) ? 0.f : ot[e] / Lt;
+    if (lane == 0 && a.out_lse)
+      a.out_lse[(size_t)b * a.hq + h] =
+          (Mt == -INFINITY) ? -INFINITY : (Mt + log2f(Lt)) * 0.69314718055994530942f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: slot of (b, p) from the placement, K rotated in fp64 and rounded
+// once to bf16, V stored as is.  Thread = (token, group of 8 rotation pairs);
+// it loops over the KV heads so each angle's sin/cos is computed once.
+// ---------------------------------------------------------------------------
+struct Slot {
+  uint16_t* k;
+  uint16_t* v;
+  bool ok;
+};
+
+__device__ __forceinline__ Slot append_slot(const AppendArgs& a, int i) {
+  Slot s{nullptr, nullptr, false};
+  const int b = a.seq_idx[i];
+  const int p = a.pos[i];
+  if (b < 0 || b >= a.batch || p < 0) return s;
+  int64_t row;
+  bool host;
+  if (a.page_size == 0) {
+    const int L = a.seq_lens[b];
+    if (p >= L) return s;
+    const int64_t nh = (int64_t)floor(a.ratio * (double)L);
+    host = p < nh;
+    if (host) {
+      if (nh > a.host_stride) return s;
+      row = (int64_t)b * a.host_stride + p;
+    } else {
+      if (L - nh > a.dev_stride) return s;
+      row = (int64_t)b * a.dev_stride + (p - nh);
+    }
+  } else {
+    const int lp = p / a.page_size;
+    if (lp >= a.max_pages) return s;
+    const int32_t e = a.page_table[(int64_t)b * a.max_pages + lp];
+    if (e < 0) return s;
+    host = (e & 1) != 0;
+    row = (int64_t)(e >> 1) * a.page_size + (p % a.page_size);
+  }
+  const int64_t cap = host ? a.host_rows : a.dev_rows;
+  if (row < 0 || row >= cap) return s;
+  const int64_t off = row * (int64_t)a.hkv * a.head_dim;
+  s.k = (host ? a.host_k : a.dev_k) + off;
+  s.v = (host ? a.host_v : a.dev_v) + off;
+  s.ok = (host ? a.host_k : a.dev_k) != nullptr;
+  return s;
+}
+
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+  const int D = a.head_dim, half = D / 2, groups = half / 8;
+  const int kvd = a.hkv * D;
+  const int64_t total = (int64_t)a.n_new * groups;
+  for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total;
+       gidx += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(gidx / groups);
+    const int g = (int)(gidx - (int64_t)i * groups);
+    const Slot sl = append_slot(a, i);
+    if (!sl.ok) continue;
+    const double pos = (double)a.pos[i];
+    double cs[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pi = g * 8 + e;
+      const double f = pow(a.theta, -2.0 * (double)pi / (double)D);
+      sincos(pos * f, &sn[e], &cs[e]);
+    }
+    for (int h = 0; h < a.hkv; ++h) {
+      double xl[8], xh[8];
+      if (a.kv_proj) {
+        const float* kp = a.kv_proj + (size_t)i * 2 * kvd + h * D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xl[e] = (double)kp[g * 8 + e];
+          xh[e] = (double)kp[half + g * 8 + e];
+        }
+      } else {
+        const uint16_t* kp = a.k_new + (size_t)i * kvd + h * D;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + g * 8);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + half + g * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xl[2 * e] = (double)bf16_to_f32(lo[e] & 0xffffu);
+          xl[2 * e + 1] = (double)bf16_to_f32(lo[e] >> 16);
+          xh[2 * e] = (double)bf16_to_f32(hi[e] & 0xffffu);
+          xh[2 * e + 1] = (double)bf16_to_f32(hi[e] >> 16);
+        }
+      }
+      uint32_t yl[4], yh[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t l0 = f64_to_bf16(xl[2 * e] * cs[2 * e] - xh[2 * e] * sn[2 * e]);
+        const uint32_t l1 = f64_to_bf16(xl[2 * e + 1] * cs[2 * e + 1] - xh[2 * e + 1] * sn[2 * e + 1]);
+        const uint32_t h0 = f64_to_bf16(xh[2 * e] * cs[2 * e] + xl[2 * e] * sn[2 * e]);
+        const uint32_t h1 = f64_to_bf16(xh[2 * e + 1] * cs[2 * e + 1] + xl[2 * e + 1] * sn[2 * e + 1]);
+        yl[e] = l0 | (l1 << 16);
+        yh[e] = h0 | (h1 << 16);
+      }
+      uint16_t* dst = sl.k + h * D;
+      *reinterpret_cast<u32x4*>(dst + g * 8) = u32x4{yl[0], yl[1], yl[2], yl[3]};
+      *reinterpret_cast<u32x4*>(dst + half + g * 8) = u32x4{yh[0], yh[1], yh[2], yh[3]};
+      // V: the same thread moves the matching 2 x 8 values of this head
+      uint16_t* vd = sl.v + h * D;
+      if (a.kv_proj) {
+        const float* vp = a.kv_proj + (size_t)i * 2 * kvd + kvd + h * D;
+        uint32_t w0[4], w1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = f32_to_bf16(vp[g * 8 + 2 * e]) | (f32_to_bf16(vp[g * 8 + 2 * e + 1]) << 16);
+          w1[e] = f32_to_bf16(vp[half + g * 8 + 2 * e]) |
+                  (f32_to_bf16(vp[half + g * 8 + 2 * e + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(vd + g * 8) = u32x4{w0[0], w0[1], w0[2], w0[3]};
+        *reinterpret_cast<u32x4*>(vd + half + g * 8) = u32x4{w1[0], w1[1], w1[2], w1[3]};
+      } else {
+        const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
+        *reinterpret_cast<u32x4*>(vd + g * 8) = *reinterpret_cast<const u32x4*>(vs + g * 8);
+        *reinterpret_cast<u32x4*>(vd + half + g * 8) =
+            *reinterpret_cast<const u32x4*>(vs + half + g * 8);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Projection [n_new x hidden] . [hidden x 2*kv_dim] on MFMA 16x16x32 bf16.
+// Workgroup = 64 output columns x one slice of the hidden dim; the W slice is
+// transposed into LDS ([col][k]) on its way in so each lane reads its B operand
+// (8 consecutive k of one column) with one 16-byte LDS read.  Partials per
+// slice go to `partial`; the append kernel's reader sums them in slice order.
+// ---------------------------------------------------------------------------
+constexpr int kProjCols = 64;
+constexpr int kProjK = 256;  // hidden-dim slice per workgroup
+
+__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kProjCols][kProjK + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j4 = lane >> 4;
+  const int ncols = 2 * a.kv_dim;
+  const int col0 = blockIdx.x * kProjCols;
+  const int ks = blockIdx.y;            // hidden slice
+  const int k0 = ks * kProjK;
+  // ---- stage W[k0 .. k0+kProjK)[col0 .. col0+64) transposed
+  for (int c = tid; c < kProjK * (kProjCols / 8); c += kThreads) {
+    const int kr = c / (kProjCols / 8);
+    const int cc = (c - kr * (kProjCols / 8)) * 8;
+    const int gcol = col0 + cc;
+    const uint16_t* src = (gcol < a.kv_dim) ? a.wk + (size_t)(k0 + kr) * a.kv_dim + gcol
+                                            : a.wv + (size_t)(k0 + kr) * a.kv_dim + (gcol - a.kv_dim);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wt[cc + 2 * e][kr] = (uint16_t)(w[e] & 0xffffu);
+      wt[cc + 2 * e + 1][kr] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  // ---- wave w computes columns col0 + 16w .. +16 for every 16-token tile
+  const int ctile = wave * 16;
+  for (int m0 = 0; m0 < a.n_new; m0 += 16) {
+    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+    const int row = m0 + n;
+    const bool rv = row < a.n_new;
+    const uint16_t* xr = a.x + (size_t)(rv ? row : 0) * a.hidden + k0 + j4 * 8;
+#pragma unroll 4
+    for (int kk = 0; kk < kProjK; kk += 32) {
+      u32x4 av = rv ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(&wt[ctile + n][kk + j4 * 8]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                  __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+    }
+    // D layout: lane holds rows j4*4 + i, column n
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + j4 * 4 + i;
+      if (r < a.n_new)
+        a.partial[((size_t)ks * a.n_pad + r) * ncols + col0 + ctile + n] = c[i];
+    }
+  }
+}
+
+// Sum of the hidden-slice partials (fixed order) into [n_new][2*kv_dim].
+__global__ __launch_bounds__(kThreads) void proj_reduce_kernel(ProjArgs a) {
+  const int ncols = 2 * a.kv_dim;
+  const int64_t total = (int64_t)a.n_new * ncols;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(idx / ncols), c = (int)(idx - (int64_t)r * ncols);
+    float s = 0.f;
+    for (int k = 0; k < a.ksplit; ++k) s += a.partial[((size_t)k * a.n_pad + r) * ncols + c];
+    a.out[idx] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming read probe: 16 B per lane per load, coalesced, grid-stride.
+// ---------------------------------------------------------------------------
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ src,
+                                                             int64_t n16, float* sink) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = NT ? __builtin_nontemporal_load(src + i + k * stride) : src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9e3779b9u) sink[0] = (float)acc;  // keeps the loads alive
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int D, int G>
+static hipError_t launch_attn_dg(const AttnArgs& a, const float* q_rot, hipStream_t s) {
+  const int grid = a.host_wgs + a.dev_wgs;
+  if (a.page_shift >= 0 && a.page_table)
+    hipLaunchKernelGGL((attn_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_attn_d(const AttnArgs& a, const float* q_rot, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: return launch_attn_dg<D, 1>(a, q_rot, s);
+    case 2: return launch_attn_dg<D, 2>(a, q_rot, s);
+    case 4: return launch_attn_dg<D, 4>(a, q_rot, s);
+    case 8: return launch_attn_dg<D, 8>(a, q_rot, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
+                  double theta, float scale_log2, const int32_t* plan_offsets,
+                  int32_t* split_offsets, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(rope_q_kernel, dim3(batch), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, theta,
+                     scale_log2, plan_offsets, split_offsets, batch);
+  return (int)hipGetLastError();
+}
+
+int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.host_wgs + a.dev_wgs <= 0) return (int)hipSuccess;
+  if (a.head_dim == 64) return (int)launch_attn_d<64>(a, q_rot, s);
+  if (a.head_dim == 128) return (int)launch_attn_d<128>(a, q_rot, s);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_merge(const MergeArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = a.batch * a.hq;
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(merge_lse_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL(merge_lse_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_append(const AppendArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t total = (int64_t)a.n_new * (a.head_dim / 16);
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  const int grid = (int)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_project(const ProjArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int ncols = 2 * a.kv_dim;
+  hipLaunchKernelGGL(proj_kernel, dim3(ncols / kProjCols, a.ksplit), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  const int64_t total = (int64_t)a.n_new * ncols;
+  const int grid = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(proj_reduce_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
+                      void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (nontemporal)
+    hipLaunchKernelGGL(probe_read_kernel<true>, dim3(nwg), dim3(kThreads), 0, s,
+                       (const u32x4*)src, n16, sink);
+  else
+    hipLaunchKernelGGL(probe_read_kernel<false>, dim3(nwg), dim3(kThreads), 0, s,
+                       (const u32x4*)src, n16, sink);
+  return (int)hipGetLastError();
+}
+
+}  // namespace dkv

@@ -1,0 +1,198 @@
+// dkv_plan.cpp - split planner: offload ratio / page tiers -> per-tier work
+// items, split slots and the workgroup split between the host and HBM tiers.
+//
+// SplitKernel README, Overview: prefetching designs leave the aggregate
+// bandwidth of the local and remote tiers unused; here both tiers stream at
+// once, each on its own set of workgroups.  SplitKernel README, Usage: the
+// offloading ratio places the oldest floor(r * L) tokens in host memory.
+//
+// Pure C++: no HIP calls, so CPU tests can exercise it.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "dkv_internal.h"
+
+namespace dkv {
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+
+bool fail(std::string* err, const char* fmt, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, fmt, a, b, c);
+  *err = buf;
+  return false;
+}
+
+// Attention workgroups resident per CU (LDS ~37 KB each of the 160 KB).
+constexpr int kSlotsPerCu = 4;
+
+int32_t choose_chunk(int64_t tier_token_heads, int32_t wgs, int32_t units_per_wg, int32_t align,
+                     int32_t tuned) {
+  if (tuned > 0) return (int32_t)round_up(tuned, align);
+  if (tier_token_heads <= 0 || wgs <= 0) return align;
+  int64_t c = ceil_div(tier_token_heads, (int64_t)wgs * units_per_wg);
+  c = std::max<int64_t>(c, 256);
+  c = std::min<int64_t>(c, 1 << 16);
+  return (int32_t)round_up(c, align);
+}
+
+}  // namespace
+
+bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
+                std::string* err) {
+  *out = PlanLayout{};
+  const int B = in.batch;
+  if (B < 1) return fail(err, "batch must be >= 1 (got %lld)", B);
+  if (!in.seq_lens) return fail(err, "seq_lens is NULL");
+  const bool paged = in.page_size > 0;
+  const int64_t P = paged ? in.page_size : 1;
+  const int64_t row_bytes = (int64_t)in.hkv * in.head_dim * 2;
+
+  // ---- tokens per tier per sequence
+  std::vector<int64_t> n_host(B), n_dev(B);
+  std::vector<std::vector<int32_t>> host_pages(paged ? B : 0), dev_pages(paged ? B : 0);
+  int64_t host_tok = 0, dev_tok = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = in.seq_lens[b];
+    if (L < 1) return fail(err, "seq_lens[%lld] = %lld: every sequence needs >= 1 token", b, L);
+    if (!paged) {
+      const int64_t nh = (int64_t)std::floor(in.ratio * (double)L);
+      n_host[b] = nh;
+      n_dev[b] = L - nh;
+      if (nh > 0 && (nh > in.host_stride || (int64_t)b * in.host_stride + nh > in.host_rows))
+        return fail(err, "sequence %lld: host rows needed beyond host_stride/host_rows (n_host %lld)",
+                    b, nh);
+      if (L - nh > 0 &&
+          (L - nh > in.dev_stride || (int64_t)b * in.dev_stride + (L - nh) > in.dev_rows))
+        return fail(err, "sequence %lld: device rows needed beyond dev_stride/dev_rows (n_dev %lld)",
+                    b, L - nh);
+    } else {
+      if (!in.page_table_host) return fail(err, "paged layout needs page_table_host");
+      const int64_t npg = ceil_div(L, P);
+      if (npg > in.max_pages)
+        return fail(err, "sequence %lld needs %lld pages > max_pages %lld", b, npg, in.max_pages);
+      int64_t nh = 0, nd = 0;
+      for (int64_t j = 0; j < npg; ++j) {
+        const int32_t e = in.page_table_host[(int64_t)b * in.max_pages + j];
+        if (e < 0) return fail(err, "page_table[%lld][%lld] = %lld is negative", b, j, e);
+        const int64_t phys = (int64_t)(e >> 1);
+        const int64_t ntok = (j == npg - 1) ? L - j * P : P;
+        const bool host = (e & 1) != 0;
+        const int64_t cap = host ? in.host_rows : in.dev_rows;
+        if ((phys + 1) * P > cap)
+          return fail(err, "page_table[%lld][%lld]: page %lld beyond its tier's pool", b, j, phys);
+        (host ? host_pages[b] : dev_pages[b]).push_back((int32_t)j);
+        (host ? nh : nd) += ntok;
+      }
+      n_host[b] = nh;
+      n_dev[b] = nd;
+    }
+    if (n_host[b] > 0 && (!in.host_rows)) return fail(err, "host tier used but host_rows is 0");
+    if (n_dev[b] > 0 && (!in.dev_rows)) return fail(err, "device tier used but dev_rows is 0");
+    host_tok += n_host[b];
+    dev_tok += n_dev[b];
+  }
+
+  // ---- workgroup split between tiers
+  const int32_t cus = std::max(1, in.num_cus);
+  const int32_t resident = cus * kSlotsPerCu;
+  const double bw_h = in.host_bw > 0 ? in.host_bw : 50.0;
+  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5000.0;
+  int32_t wh = 0, wd = 0;
+  if (host_tok > 0 && dev_tok > 0) {
+    // Bandwidth-proportional share of the resident slots, with the host
+    // tier never below the count that keeps enough requests in flight.
+    const int32_t floor_h = in.host_wgs > 0 ? in.host_wgs : 32;
+    wh = std::max(floor_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d)));
+    wh = std::min(wh, resident / 2);
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
+  } else if (host_tok > 0) {
+    wh = in.host_wgs > 0 ? in.host_wgs : cus * 2;
+  } else {
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
+  }
+
+  const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
+  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, 4, align, in.host_chunk);
+  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 2, align, in.dev_chunk);
+
+  // ---- items
+  std::vector<PlanItem> hitems, ditems;
+  std::vector<int32_t> plist;
+  std::vector<int32_t> offsets(B + 1, 0);
+  int32_t slot = 0;
+  for (int b = 0; b < B; ++b) {
+    offsets[b] = slot;
+    for (int tier = 1; tier >= 0; --tier) {
+      std::vector<PlanItem>& dst = tier ? hitems : ditems;
+      const int64_t chunk = tier ? ch : cd;
+      if (!paged) {
+        const int64_t nh = n_host[b];
+        const int64_t begin = tier ? 0 : nh;
+        const int64_t end = tier ? nh : (int64_t)in.seq_lens[b];
+        for (int64_t t0 = begin; t0 < end; t0 += chunk) {
+          PlanItem it{};
+          it.b = b;
+          it.slot = slot++;
+          it.n_tok = (int32_t)std::min<int64_t>(chunk, end - t0);
+          it.plist = 0;
+          it.row0 = tier ? (int64_t)b * in.host_stride + t0 : (int64_t)b * in.dev_stride + (t0 - nh);
+          dst.push_back(it);
+        }
+      } else {
+        const std::vector<int32_t>& pages = tier ? host_pages[b] : dev_pages[b];
+        const int64_t L = in.seq_lens[b];
+        const int64_t per = chunk / P;
+        for (size_t k0 = 0; k0 < pages.size(); k0 += per) {
+          const size_t k1 = std::min(pages.size(), k0 + (size_t)per);
+          int64_t ntok = 0;
+          for (size_t k = k0; k < k1; ++k) ntok += std::min<int64_t>(P, L - (int64_t)pages[k] * P);
+          PlanItem it{};
+          it.b = b;
+          it.slot = slot++;
+          it.n_tok = (int32_t)ntok;
+          it.plist = (int32_t)plist.size();
+          it.row0 = 0;
+          for (size_t k = k0; k < k1; ++k) plist.push_back(pages[k]);
+          dst.push_back(it);
+        }
+      }
+    }
+  }
+  offsets[B] = slot;
+
+  out->n_host_items = (int32_t)hitems.size();
+  out->n_dev_items = (int32_t)ditems.size();
+  out->num_splits = slot;
+  out->batch = B;
+  out->host_wgs = hitems.empty() ? 0 : std::min<int64_t>(wh, (int64_t)hitems.size() * in.hkv);
+  out->dev_wgs = ditems.empty() ? 0 : std::min<int64_t>(wd, (int64_t)ditems.size() * in.hkv);
+  out->host_chunk = hitems.empty() ? 0 : ch;
+  out->dev_chunk = ditems.empty() ? 0 : cd;
+  out->host_bytes = host_tok * row_bytes * 2;
+  out->dev_bytes = dev_tok * row_bytes * 2;
+  out->n_plist = (int32_t)plist.size();
+  out->items_off = 0;
+  out->plist_off = (hitems.size() + ditems.size()) * sizeof(PlanItem);
+  out->offsets_off = round_up(out->plist_off + plist.size() * sizeof(int32_t), 16);
+  out->blob_bytes = round_up(out->offsets_off + (B + 1) * sizeof(int32_t), 256);
+  if ((int64_t)(hitems.size() + ditems.size()) * in.hkv > INT32_MAX)
+    return fail(err, "too many work units");
+  if (blob) {
+    blob->assign(out->blob_bytes, 0);
+    uint8_t* p = blob->data();
+    if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(PlanItem));
+    if (!ditems.empty())
+      memcpy(p + hitems.size() * sizeof(PlanItem), ditems.data(), ditems.size() * sizeof(PlanItem));
+    if (!plist.empty()) memcpy(p + out->plist_off, plist.data(), plist.size() * sizeof(int32_t));
+    memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
+  }
+  return true;
+}
+
+}  // namespace dkv

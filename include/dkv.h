@@ -1,0 +1,267 @@
+/*
+ * dkv.h - C ABI of libdkv: single-token decode attention over a KV cache that
+ * lives mostly in host-pinned memory, read by the GPU in place (zero-copy),
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are (page titles and sections of the method's pages):
+ *   - DirectKV README, introduction: the KV cache sits in CPU-pinned memory
+ *     instead of GPU HBM; one kernel fuses K/V projection, Neox RoPE and
+ *     multi-head attention, loading KV straight from the pinned buffers.
+ *   - DirectKV README, Attribution: FlashAttention-style online softmax,
+ *     extended from GPU-resident KV to KV streamed from CPU memory with no
+ *     staging copy in a GPU buffer.
+ *   - SplitKernel README, Overview and Key Features: kernels read offloaded
+ *     data directly from the remote tier into on-chip memory, and attention
+ *     runs over a KV cache partitioned between host and device memory.
+ *   - SplitKernel README, Usage: placement and offloading-ratio utilities.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns dkv_status.  On failure dkv_last_error() gives a
+ *     message for the calling thread.  Nothing is launched when validation
+ *     fails; no exception crosses the ABI.
+ *   - "device" pointers are GPU-visible addresses: HBM allocations or the
+ *     device address of a mapped host-pinned block (dkv_host_alloc).  "host"
+ *     pointers are ordinary CPU memory read during the call.
+ *   - bf16 tensors are raw 16-bit bfloat16 patterns.  A KV pool row is one
+ *     token: [num_kv_heads][head_dim] bf16, K and V in separate pools.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
+ *     runs asynchronously.  The caller owns every buffer and keeps it alive
+ *     until the stream has passed the call.
+ *   - The caller's current HIP device must be the device owning the buffers.
+ */
+#ifndef DKV_H
+#define DKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dkv_status {
+  DKV_OK = 0,
+  DKV_ERR_INVALID = 1,     /* bad argument: null pointer, size, range, layout */
+  DKV_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, group size, ... */
+  DKV_ERR_NOMEM = 3,       /* a host-pinned or library allocation failed */
+  DKV_ERR_HIP = 4          /* a HIP runtime call failed (message has the text) */
+} dkv_status;
+
+/* Message describing the last failure on this thread ("" if none). */
+const char* dkv_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t dkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * KV cache description.
+ *
+ * Two placements (SplitKernel README, Key Features: host/device KV split):
+ *
+ *  page_size == 0, contiguous split.  Sequence b holds L_b tokens; its oldest
+ *    n_host_b = floor(r * L_b) tokens (IEEE double product, r = offload ratio)
+ *    are in the host pools at rows b*host_stride + t, the rest in the device
+ *    pools at rows b*dev_stride + (t - n_host_b).  This describes a cache of
+ *    fixed length; use the paged placement for caches that grow.
+ *
+ *  page_size > 0 (a power of two), paged.  page_table[b*max_pages + t/page]
+ *    = phys << 1 | tier (tier 1 = host pools, 0 = device pools) and the row
+ *    is phys*page_size + t % page_size.  page_table lives in device memory;
+ *    page_table_host is an identical host copy used to plan the per-tier work
+ *    (the planner reads tiers from it; kernels read the device copy).
+ *
+ *  host_k/host_v are device addresses of host-pinned memory (zero-copy);
+ *  dev_k/dev_v are HBM.  host_rows / dev_rows are the pool capacities in rows
+ *  and bound every access.  Either tier may be NULL with 0 rows when no token
+ *  lives there.
+ * ---------------------------------------------------------------------- */
+typedef struct dkv_kv_desc {
+  int32_t num_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t page_size;      /* 0 = contiguous split, else power of two <= 1024 */
+  int32_t max_pages;      /* paged: row stride of page_table */
+  int64_t host_stride;    /* contiguous: host rows reserved per sequence */
+  int64_t dev_stride;     /* contiguous: device rows reserved per sequence */
+  int64_t host_rows;      /* capacity of host_k / host_v in rows */
+  int64_t dev_rows;       /* capacity of dev_k / dev_v in rows */
+  void* host_k;           /* device address of host-pinned K pool, bf16 */
+  void* host_v;           /* device address of host-pinned V pool, bf16 */
+  void* dev_k;            /* HBM K pool, bf16 */
+  void* dev_v;            /* HBM V pool, bf16 */
+  const int32_t* page_table;      /* device [B][max_pages] (paged only) */
+  const int32_t* page_table_host; /* host [B][max_pages] copy (paged only) */
+} dkv_kv_desc;
+
+/* floor(ratio * length) in IEEE double: the number of host-resident tokens of
+ * a contiguous-split sequence (SplitKernel README, Usage: offloading ratio).
+ * ratio must be in [0, 1] and length >= 0. */
+dkv_status dkv_split_point(double ratio, int64_t length, int64_t* n_host);
+
+/* ------------------------------------------------------------------------
+ * Fused projection + Neox RoPE + append of new tokens into the cache.
+ * (DirectKV README, introduction: the fused kernel projects K/V, rotates K
+ *  with Neox RoPE; Step 6 checks the new K and V after projection.)
+ *
+ * For each new token i (0 <= i < n_new), in sequence b = seq_idx[i] at
+ * position p = pos[i]:
+ *   projection mode (x != NULL):  k = x[i] . Wk, v = x[i] . Wv, accumulated
+ *     in fp32; x is [n_new][hidden] bf16, Wk/Wv are [hidden][Hkv*D] bf16
+ *     row-major with output column h*D + d; no bias.
+ *   no-projection mode (x == NULL): k = k_new[i], v = v_new[i], both
+ *     [n_new][Hkv][D] bf16.
+ *   Then every head of k is rotated by rotate-half RoPE at position p,
+ *   f_j = rope_theta^(-2j/D), angle and rotation in fp64, and written to the
+ *   slot of (b, p) as bf16 rounded to nearest even; v is written unrotated.
+ *
+ * seq_idx, pos: device int32 [n_new].  Contiguous placement also needs
+ * seq_lens (device int32 [batch], the lengths L_b that fix the split point
+ * floor(offload_ratio * L_b)); paged placement ignores seq_lens and the ratio.
+ * Tokens whose slot falls outside the layout (b outside [0,batch), p < 0,
+ * page index >= max_pages, negative page entry, row beyond the pool) are
+ * skipped: nothing is written for them.  Set DKV_DEBUG_VALIDATE=1 to have
+ * such tokens reported as DKV_ERR_INVALID instead (synchronous host check).
+ *
+ * workspace: device scratch of at least dkv_append_workspace_bytes(n_new,
+ * hidden, Hkv*D) bytes when x != NULL (may be NULL otherwise).  Calls that
+ * share a workspace on different streams race.
+ * ---------------------------------------------------------------------- */
+size_t dkv_append_workspace_bytes(int32_t n_new, int32_t hidden, int32_t kv_dim);
+
+dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
+                                   const int32_t* seq_lens, double offload_ratio,
+                                   int32_t n_new, const int32_t* seq_idx, const int32_t* pos,
+                                   const void* x, int32_t hidden, const void* wk, const void* wv,
+                                   const void* k_new, const void* v_new, double rope_theta,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Split decode attention (DirectKV README, introduction and Attribution;
+ * SplitKernel README, Key Features).
+ *
+ * One query token per sequence: q [batch][Hq][D] bf16 (device), rotated
+ * in-kernel by Neox RoPE at q_pos[b] (device int32 [batch]).  Query head h
+ * reads KV head h / (Hq/Hkv).  Sequence b attends to its seq_lens[b] cached
+ * tokens (host int32 [batch], each >= 1; keys already rotated by the append):
+ *   s_t = scale * q_rot . k_t,  o = sum_t softmax(s)_t v_t,  lse = ln sum_t e^s_t.
+ *
+ * The tokens of each sequence are cut into work items that each lie in one
+ * tier (host or HBM) and one KV head.  Items of the two tiers run at the same
+ * time on disjoint sets of workgroups; each item writes a normalised partial
+ * (part_o [S][Hq][D] fp32, part_lse [S][Hq] fp32, natural log) in the split
+ * slots of its sequence, and split_offsets (device int32 [batch+1]) receives
+ * the CSR bounds: sequence b owns splits [split_offsets[b], split_offsets[b+1]).
+ * dkv_merge_lse turns the partials into the final output.
+ *
+ * dkv_decode_plan returns the split count S and the workspace size for these
+ * arguments; part_o / part_lse must hold at least S splits (num_splits_cap)
+ * and the workspace (device memory) at least workspace_bytes.  Plans are
+ * cached per distinct shape inside the library.
+ * ---------------------------------------------------------------------- */
+typedef struct dkv_plan_info {
+  int64_t workspace_bytes; /* device workspace the call needs */
+  int32_t num_splits;      /* S: rows of part_o / part_lse */
+  int32_t host_items;      /* work items in the host tier (per KV head) */
+  int32_t dev_items;       /* work items in the HBM tier (per KV head) */
+  int32_t host_wgs;        /* workgroups streaming the host tier */
+  int32_t dev_wgs;         /* workgroups streaming the HBM tier */
+  int32_t host_chunk;      /* tokens per host work item */
+  int32_t dev_chunk;       /* tokens per HBM work item */
+  int64_t host_bytes;      /* K+V bytes read from host memory per call */
+  int64_t dev_bytes;       /* K+V bytes read from HBM per call */
+} dkv_plan_info;
+
+dkv_status dkv_decode_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                           const int32_t* seq_lens, double offload_ratio, dkv_plan_info* info);
+
+dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                 const void* q, const int32_t* q_pos, const int32_t* seq_lens,
+                                 double offload_ratio, float scale, double rope_theta,
+                                 void* workspace, size_t workspace_bytes,
+                                 float* part_o, float* part_lse, int32_t* split_offsets,
+                                 int32_t num_splits_cap, void* stream);
+
+/* Plan introspection with no GPU work: runs the planner for `num_cus`
+ * compute units (current tuning otherwise) and copies the plan out to host
+ * memory.  items receives up to items_cap rows of 5 int64 values
+ * (tier [1 host, 0 HBM], b, slot, n_tok, first) where `first` is the pool row
+ * of the item's first token (contiguous) or its index into page_list (paged);
+ * page_list receives up to page_cap logical page indices; split_offsets
+ * receives batch+1 values.  Any output pointer may be NULL.  Host tier items
+ * come first.  info as for dkv_decode_plan. */
+dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                            const int32_t* seq_lens, double offload_ratio, int32_t num_cus,
+                            int64_t* items, int32_t items_cap, int32_t* page_list,
+                            int32_t page_cap, int32_t* split_offsets, dkv_plan_info* info);
+
+/* ------------------------------------------------------------------------
+ * LSE merge of partial results (the combine step implied by splitting one
+ * sequence's KV over tiers and compute units: SplitKernel README, Key
+ * Features; DirectKV README, Step 6, "SM-Parallel" kernel).
+ *
+ * For each (b, h): M = max_i lse_i over splits i in [split_offsets[b],
+ * split_offsets[b+1]), w_i = exp(lse_i - M), out_o = sum w_i o_i / sum w_i,
+ * out_lse = M + ln sum w_i.  Splits with lse = -inf weigh 0; a sequence with
+ * no finite split gets out_o = 0, out_lse = -inf.  All device pointers;
+ * out_lse may be NULL.  head_dim is 64 or 128.
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32_t* split_offsets,
+                         int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                         float* out_o, float* out_lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-pinned memory for the host tier (DirectKV README, introduction:
+ * CPU-pinned KV pool).  Allocates `bytes` of page-locked host memory mapped
+ * into the GPU's address space; *host_ptr is the CPU address, *dev_ptr the
+ * address kernels use.  flags: DKV_HOST_COHERENT (fine-grained, default) or
+ * DKV_HOST_NONCOHERENT (coarse-grained; GPU caches may hold lines during a
+ * kernel).  Free with dkv_host_free(host_ptr) after all GPU work using it.
+ * ---------------------------------------------------------------------- */
+#define DKV_HOST_COHERENT 0u
+#define DKV_HOST_NONCOHERENT 1u
+
+dkv_status dkv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr);
+dkv_status dkv_host_free(void* host_ptr);
+
+/* ------------------------------------------------------------------------
+ * Planner tuning (SplitKernel README, Requirements: the build fixes the SM
+ * count and buffer slots; here they are run-time values).  Zero fields take
+ * the library defaults; host_bw_gbs / dev_bw_gbs weigh the split of
+ * workgroups between tiers.  Applies process-wide to later plans.
+ * ---------------------------------------------------------------------- */
+typedef struct dkv_tuning {
+  int32_t num_cus;       /* compute units to plan for (0: the current device) */
+  int32_t host_wgs;      /* workgroups for the host tier (0: default) */
+  int32_t dev_wgs;       /* workgroups for the HBM tier (0: default) */
+  int32_t host_chunk;    /* tokens per host work item, multiple of 64 (0: auto) */
+  int32_t dev_chunk;     /* tokens per HBM work item, multiple of 64 (0: auto) */
+  int32_t reserved;
+  double host_bw_gbs;    /* host-link read bandwidth (0: 50) */
+  double dev_bw_gbs;     /* HBM read bandwidth (0: 5000) */
+} dkv_tuning;
+
+dkv_status dkv_set_tuning(const dkv_tuning* tuning); /* NULL restores defaults */
+dkv_status dkv_get_tuning(dkv_tuning* tuning);
+
+/* ------------------------------------------------------------------------
+ * Bandwidth probe: reads `bytes` of memory with a streaming kernel that has
+ * the same load pattern as the attention kernel (16 B per lane, coalesced)
+ * and reports GB/s.  src is a device address (HBM or mapped host memory),
+ * nwg the number of workgroups (<= 65535), iters the timed repetitions.
+ * Also a DMA copy rate for host->device hipMemcpyAsync of the same block when
+ * dma_dst is non-NULL (device buffer of `bytes`).  Blocks until done.
+ * ---------------------------------------------------------------------- */
+typedef struct dkv_bw_result {
+  double read_gbs;   /* kernel read rate */
+  double read_ms;    /* average kernel time */
+  double dma_gbs;    /* hipMemcpyAsync rate (0 if not measured) */
+} dkv_bw_result;
+
+dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t nontemporal,
+                          int32_t iters, void* dma_dst, const void* dma_src_host,
+                          dkv_bw_result* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_H */

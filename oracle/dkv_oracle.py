@@ -197,7 +197,7 @@ def _stored_keys(k_raw_bits, theta, rounded=True, positions=None):
 
 
 def decode_sequence(q_bits, k_raw_bits, v_bits, q_pos: int, theta: float, scale: float,
-                    heads=None, rounded_keys: bool = True):
+                    heads=None, rounded_keys: bool = True, key_positions=None):
     """Decode attention of one sequence over its whole cache.
 
     q_bits [Hq, D], k_raw_bits / v_bits [N, Hkv, D] (bf16 bits, keys before
@@ -205,6 +205,8 @@ def decode_sequence(q_bits, k_raw_bits, v_bits, q_pos: int, theta: float, scale:
     With ``rounded_keys`` the attention reads bf16-rounded rotated keys, as
     held in the cache after append.  ``heads`` restricts the query heads (for
     sampling at full size); the KV work is done one KV head at a time.
+    ``key_positions`` overrides the rotation position of each cached token
+    (default: token t at position t).
     Returns o [len(heads), D], lse [len(heads)].
     """
     q = bf16_to_f64(q_bits)
@@ -219,7 +221,7 @@ def decode_sequence(q_bits, k_raw_bits, v_bits, q_pos: int, theta: float, scale:
     for j, h in enumerate(heads):
         by_kv.setdefault(h // g, []).append((j, h))
     for kvh, hs in by_kv.items():
-        kk = _stored_keys(k_raw_bits[:, kvh:kvh + 1, :], theta, rounded_keys)
+        kk = _stored_keys(k_raw_bits[:, kvh:kvh + 1, :], theta, rounded_keys, key_positions)
         vv = bf16_to_f64(v_bits[:, kvh:kvh + 1, :])
         sub_q = np.stack([q_rot[h] for _, h in hs])
         oo, ll = attention(sub_q, kk, vv, scale)
