@@ -16,6 +16,8 @@ from .api import (  # noqa: F401
     decode_attn_split,
     decode_plan,
     get_tuning,
+    kernel_timing,
+    kernel_timing_read,
     merge_lse,
     plan_inspect,
     probe_read,

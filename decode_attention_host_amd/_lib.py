@@ -110,7 +110,14 @@ SIGNATURES = {
     "dkv_set_tuning": (I32, [C.POINTER(Tuning)]),
     "dkv_get_tuning": (I32, [C.POINTER(Tuning)]),
     "dkv_probe_read": (I32, [P, SZ, I32, I32, I32, P, P, C.POINTER(BwResult), P]),
+    "dkv_kernel_timing": (I32, [I32]),
+    "dkv_kernel_timing_read": (I32, [I32, C.POINTER(I32), C.POINTER(F64)]),
 }
+
+DKV_KERNEL_ATTN = 0
+DKV_KERNEL_ROPE_Q = 1
+DKV_KERNEL_MERGE = 2
+DKV_KERNEL_APPEND = 3
 
 _lib = None
 

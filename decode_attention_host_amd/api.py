@@ -295,3 +295,20 @@ def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True
     check(lib().dkv_probe_read(C.c_void_p(int(src_dev_ptr)), int(nbytes), int(nwg), int(bool(nontemporal)),
                                int(iters), _ptr(dma_dst), _ptr(dma_src_host), C.byref(r), _stream(stream)))
     return {"read_gbs": r.read_gbs, "read_ms": r.read_ms, "dma_gbs": r.dma_gbs}
+
+
+KERNELS = {"attn": _lib.DKV_KERNEL_ATTN, "rope_q": _lib.DKV_KERNEL_ROPE_Q,
+           "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND}
+
+
+def kernel_timing(enable: bool):
+    """dkv_kernel_timing: bracket each launch with HIP events on its stream."""
+    check(lib().dkv_kernel_timing(int(bool(enable))))
+
+
+def kernel_timing_read(kernel: str) -> tuple[int, float]:
+    """dkv_kernel_timing_read -> (launches timed, summed ms); clears the record."""
+    n = C.c_int32()
+    ms = C.c_double()
+    check(lib().dkv_kernel_timing_read(KERNELS[kernel], C.byref(n), C.byref(ms)))
+    return n.value, ms.value

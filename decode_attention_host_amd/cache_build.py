@@ -63,3 +63,35 @@ def paged_cache(hkv: int, d: int, lens, page_table: np.ndarray, n_host_pages: in
             _append_rows(cache, B, b, 0, k_raw[b][:n], v_raw[b][:n], None, 0.0, theta)
     torch.cuda.synchronize()
     return cache
+
+
+class SplitView:
+    """Contiguous-split view of one sequence over full host and device copies
+    of its cache (both built with every token at row t): tokens [0, n_host)
+    are read from the host copy, the rest from the device copy.  Lets one
+    pair of copies serve every offload ratio."""
+
+    def __init__(self, host_full: KVCache, dev_full: KVCache, length: int, ratio: float):
+        self.host_full, self.dev_full = host_full, dev_full
+        self.head_dim = host_full.head_dim
+        self.num_kv_heads = host_full.num_kv_heads
+        self.length = int(length)
+        self.n_host = split_point(ratio, self.length)
+
+    def desc(self):
+        d = self.host_full.desc()
+        row_bytes = self.num_kv_heads * self.head_dim * 2
+        L, nh = self.length, self.n_host
+        d.host_stride = L
+        d.host_rows = nh
+        if nh == 0:
+            d.host_k = d.host_v = None
+        dd = self.dev_full.desc()
+        d.dev_stride = L
+        d.dev_rows = L - nh
+        if L - nh > 0:
+            d.dev_k = dd.dev_k + nh * row_bytes
+            d.dev_v = dd.dev_v + nh * row_bytes
+        else:
+            d.dev_k = d.dev_v = None
+        return d

@@ -245,6 +245,67 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
 
 size_t qrot_bytes(int32_t batch, int32_t hq, int32_t d) { return (size_t)batch * hq * d * 4; }
 
+// f_i = theta^(-2i/D) in IEEE double, the exponent formed as (-2 i) / D.
+dkv::RopeFreq rope_freq(double theta, int d) {
+  dkv::RopeFreq r{};
+  for (int i = 0; i < d / 2 && i < 64; ++i) r.f[i] = std::pow(theta, -2.0 * (double)i / (double)d);
+  return r;
+}
+
+// ---------------------------------------------------------------- kernel timing
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[4];
+};
+
+Timing& timing() {
+  static Timing* t = new Timing();
+  return *t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with an event pair when timing is on.
+struct TimedLaunch {
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t e0 = nullptr;
+  TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.on) return;
+    e0 = take_event(t);
+    if (e0 && hipEventRecord(e0, s) != hipSuccess) {
+      t.pool.push_back(e0);
+      e0 = nullptr;
+    }
+  }
+  void done() {
+    if (!e0) return;
+    Timing& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    hipEvent_t e1 = take_event(t);
+    if (e1 && hipEventRecord(e1, stream) == hipSuccess) {
+      t.rec[kernel].push_back({e0, e1});
+    } else {
+      t.pool.push_back(e0);
+      if (e1) t.pool.push_back(e1);
+    }
+    e0 = nullptr;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -401,10 +462,13 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   if (he != hipSuccess) return hip_err(he, "plan upload");
   float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
   const float scale_log2 = scale * 1.44269504088896340736f;
+  TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
   he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q), q_pos, q_rot, batch,
-                                      num_q_heads, kv->head_dim, rope_theta, scale_log2,
+                                      num_q_heads, kv->head_dim, rope_freq(rope_theta, kv->head_dim),
+                                      scale_log2,
                                       reinterpret_cast<const int32_t*>(ws + L.offsets_off),
                                       split_offsets, stream);
+  t_rope.done();
   if (he != hipSuccess) return hip_err(he, "rope_q launch");
   dkv::AttnArgs a{};
   a.host_items = reinterpret_cast<const dkv::PlanItem*>(ws + L.items_off);
@@ -435,7 +499,9 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   a.theta = rope_theta;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  TimedLaunch t_attn(DKV_KERNEL_ATTN, s);
   he = (hipError_t)dkv::launch_attn_with_q(a, q_rot, stream);
+  t_attn.done();
   if (he != hipSuccess) return hip_err(he, "attention launch");
   return ok();
 }
@@ -458,7 +524,9 @@ dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32
   a.head_dim = head_dim;
   a.out_o = out_o;
   a.out_lse = out_lse;
+  TimedLaunch tl(DKV_KERNEL_MERGE, (hipStream_t)stream);
   hipError_t he = (hipError_t)dkv::launch_merge(a, stream);
+  tl.done();
   if (he != hipSuccess) return hip_err(he, "merge launch");
   return ok();
 }
@@ -568,7 +636,7 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch, const i
   a.page_size = kv->page_size;
   a.hkv = kv->num_kv_heads;
   a.head_dim = kv->head_dim;
-  a.theta = rope_theta;
+  a.freq = rope_freq(rope_theta, kv->head_dim);
   if (proj) {
     dkv::ProjArgs p{};
     p.x = static_cast<const uint16_t*>(x);
@@ -590,7 +658,9 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch, const i
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
   }
+  TimedLaunch tl(DKV_KERNEL_APPEND, s);
   hipError_t he = (hipError_t)dkv::launch_append(a, stream);
+  tl.done();
   if (he != hipSuccess) return hip_err(he, "append launch");
   return ok();
 }
@@ -672,6 +742,43 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
   (void)hipEventDestroy(e1);
   (void)hipFree(sink);
   if (st != DKV_OK) return st;
+  return ok();
+}
+
+dkv_status dkv_kernel_timing(int32_t enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = enable != 0;
+  return ok();
+}
+
+dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms) {
+  if (kernel < 0 || kernel > 3 || !count || !total_ms)
+    return set_err(DKV_ERR_INVALID, "kernel id in [0,3] and outputs required");
+  Timing& t = timing();
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    rec.swap(t.rec[kernel]);
+  }
+  double tot = 0.0;
+  hipError_t err = hipSuccess;
+  for (auto& p : rec) {
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventSynchronize(p.second);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, p.first, p.second);
+    tot += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    for (auto& p : rec) {
+      t.pool.push_back(p.first);
+      t.pool.push_back(p.second);
+    }
+  }
+  if (err != hipSuccess) return hip_err(err, "kernel timing");
+  *count = (int32_t)rec.size();
+  *total_ms = tot;
   return ok();
 }
 

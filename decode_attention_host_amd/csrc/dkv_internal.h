@@ -10,6 +10,12 @@
 
 namespace dkv {
 
+// Rotary frequencies f_i = theta^(-2i/D), i < D/2, computed once on the host
+// in fp64 and passed by value to the kernels that rotate.
+struct RopeFreq {
+  double f[64];
+};
+
 // Tokens staged per tile by the attention kernel (4 waves x 16 tokens).
 constexpr int kTile = 64;
 // Threads per attention / merge / append workgroup.
@@ -115,7 +121,7 @@ struct AppendArgs {
   int32_t page_size;             // 0 = contiguous
   int32_t hkv;
   int32_t head_dim;
-  double theta;
+  RopeFreq freq;
 };
 
 struct ProjArgs {
@@ -134,7 +140,7 @@ struct ProjArgs {
 
 // Launchers (dkv_kernels.hip).  They return hipError_t as int.
 int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
-                  double theta, float scale_log2, const int32_t* plan_offsets,
+                  const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream);
 int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);

@@ -74,26 +74,25 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
 
 // ---------------------------------------------------------------------------
 // Query rotation: q_rot[b][h][d] = scale*log2(e) * RoPE(q[b][h], q_pos[b])[d].
-// Angles pos * theta^(-2i/D) and sin/cos in fp64.  Block 0 also copies the
-// split offsets of the plan to the caller's array.
+// Angle pos * f_i and sin/cos in fp64 (f_i from the host table).  Block 0 also
+// copies the split offsets of the plan to the caller's array.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ q_pos,
                                                           float* __restrict__ q_rot, int hq, int d,
-                                                          double theta, float scale_log2,
+                                                          RopeFreq freq, float scale_log2,
                                                           const int32_t* __restrict__ plan_offsets,
                                                           int32_t* __restrict__ split_offsets,
                                                           int batch) {
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int half = d >> 1;
-  if (b == 0 && split_offsets)
+  if (b == 0 && blockIdx.x == 0 && split_offsets)
     for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
   const double pos = (double)q_pos[b];
-  for (int idx = threadIdx.x; idx < hq * half; idx += blockDim.x) {
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < hq * half; idx += gridDim.x * blockDim.x) {
     const int h = idx / half, i = idx - h * half;
-    const double f = pow(theta, -2.0 * (double)i / (double)d);
     double s, c;
-    sincos(pos * f, &s, &c);
+    sincos(pos * freq.f[i], &s, &c);
     const uint16_t* qh = q + ((size_t)b * hq + h) * d;
     const double xl = (double)bf16_to_f32(qh[i]);
     const double xh = (double)bf16_to_f32(qh[i + half]);
@@ -352,63 +351,85 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
 }
 
 // ---------------------------------------------------------------------------
-// LSE merge: one workgroup per (b, h); wave w folds splits w, w+4, ... with an
-// online rescale, then the four waves combine through LDS.
+// LSE merge: one workgroup per (b, h).  The maximum and the weight sum of the
+// split LSEs are block reductions; then 256/D groups of D threads each fold a
+// strided subset of the splits (independent loads) and combine through LDS.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
-  constexpr int DPL = D / 64;
-  constexpr float kLog2e = 1.44269504088896340736f;
-  __shared__ float sm_m[4], sm_l[4];
-  __shared__ float sm_o[4][D];
-  const int bh = blockIdx.x;
-  const int b = bh / a.hq, h = bh - b * a.hq;
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* sm) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float w = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, w) : v + w;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
-  float M = -INFINITY, L = 0.f, o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int s = s0 + wave; s < s1; s += 4) {
-    const float l2 = a.part_lse[(size_t)s * a.hq + h] * kLog2e;
-    if (l2 == -INFINITY) continue;
-    const float m_new = fmaxf(M, l2);
-    const float so = (M == -INFINITY) ? 0.f : exp2f(M - m_new);
-    const float w = exp2f(l2 - m_new);
-    const float* po = a.part_o + ((size_t)s * a.hq + h) * D + lane * DPL;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = o[e] * so + w * po[e];
-    L = L * so + w;
-    M = m_new;
-  }
-  if (lane == 0) {
-    sm_m[wave] = M;
-    sm_l[wave] = L;
-  }
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) sm_o[wave][lane * DPL + e] = o[e];
   __syncthreads();
-  if (wave == 0) {
-    float Mt = -INFINITY;
+  if (lane == 0) sm[wave] = v;
+  __syncthreads();
+  v = sm[0];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, sm_m[w]);
-    float Lt = 0.f, ot[DPL];
+  for (int w = 1; w < kThreads / 64; ++w) v = is_max ? fmaxf(v, sm[w]) : v + sm[w];
+  return v;
+}
+
+// Workgroup = (b, h, 32-dim chunk of the head): 8 groups of 32 lanes each fold
+// every 8th split with four independent loads in flight, so a (b, h) merge is
+// spread over D/32 workgroups and many loads overlap.
+constexpr int kMergeDims = 32;
+constexpr int kMergeGroups = kThreads / kMergeDims;
+
+__global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
+  __shared__ float sm_red[kThreads / 64];
+  __shared__ float sm_o[kMergeGroups][kMergeDims];
+  const int D = a.head_dim;
+  const int nchunk = D / kMergeDims;
+  const int bh = blockIdx.x / nchunk;
+  const int dc = blockIdx.x - bh * nchunk;
+  const int b = bh / a.hq, h = bh - b * a.hq;
+  const int tid = threadIdx.x;
+  const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
+  const float* lse = a.part_lse + h;
+  float m = -INFINITY;
+  for (int s = s0 + tid; s < s1; s += kThreads) m = fmaxf(m, lse[(size_t)s * a.hq]);
+  const float M = block_reduce(m, true, sm_red);
+  float* out = a.out_o + ((size_t)b * a.hq + h) * D + dc * kMergeDims;
+  if (M == -INFINITY) {  // no finite split
+    if (tid < kMergeDims) out[tid] = 0.f;
+    if (tid == 0 && dc == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = -INFINITY;
+    return;
+  }
+  float l = 0.f;
+  for (int s = s0 + tid; s < s1; s += kThreads) {
+    const float x = lse[(size_t)s * a.hq];
+    l += (x == -INFINITY) ? 0.f : expf(x - M);
+  }
+  const float Lsum = block_reduce(l, false, sm_red);
+  const int g = tid / kMergeDims, d = tid - g * kMergeDims;
+  const float* po = a.part_o + (size_t)h * D + dc * kMergeDims + d;
+  const size_t srow = (size_t)a.hq * D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = s0 + g;
+  for (; s + 3 * kMergeGroups < s1; s += 4 * kMergeGroups) {
+    float x[4], o[4];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) ot[e] = 0.f;
-    if (Mt != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sw = (sm_m[w] == -INFINITY) ? 0.f : exp2f(sm_m[w] - Mt);
-        Lt += sw * sm_l[w];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) ot[e] += sw * sm_o[w][lane * DPL + e];
-      }
+    for (int k = 0; k < 4; ++k) {
+      x[k] = lse[(size_t)(s + k * kMergeGroups) * a.hq];
+      o[k] = po[(size_t)(s + k * kMergeGroups) * srow];
     }
-    float* out = a.out_o + ((size_t)b * a.hq + h) * D + lane * DPL;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) out[e] = (Mt == -INFINITY) ? 0.f : ot[e] / Lt;
-    if (lane == 0 && a.out_lse)
-      a.out_lse[(size_t)b * a.hq + h] =
-          (Mt == -INFINITY) ? -INFINITY : (Mt + log2f(Lt)) * 0.69314718055994530942f;
+    for (int k = 0; k < 4; ++k) acc[k] += (x[k] == -INFINITY) ? 0.f : expf(x[k] - M) * o[k];
+  }
+  for (; s < s1; s += kMergeGroups) {
+    const float x = lse[(size_t)s * a.hq];
+    acc[0] += (x == -INFINITY) ? 0.f : expf(x - M) * po[(size_t)s * srow];
+  }
+  sm_o[g][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (tid < kMergeDims) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) o += sm_o[k][tid];
+    out[tid] = o / Lsum;
+    if (tid == 0 && dc == 0 && a.out_lse)
+      a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
   }
 }
 
@@ -460,76 +481,72 @@ __device__ __forceinline__ Slot append_slot(const AppendArgs& a, int i) {
 }
 
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
-  const int D = a.head_dim, half = D / 2, groups = half / 8;
+  constexpr int QP = 4;  // rotation pairs per thread
+  const int D = a.head_dim, half = D / 2, groups = half / QP;
   const int kvd = a.hkv * D;
-  const int64_t total = (int64_t)a.n_new * groups;
+  const int per_tok = a.hkv * groups;
+  const int64_t total = (int64_t)a.n_new * per_tok;
   for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total;
        gidx += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(gidx / groups);
-    const int g = (int)(gidx - (int64_t)i * groups);
+    const int i = (int)(gidx / per_tok);
+    const int r = (int)(gidx - (int64_t)i * per_tok);
+    const int h = r / groups;
+    const int p0 = (r - h * groups) * QP;
     const Slot sl = append_slot(a, i);
     if (!sl.ok) continue;
     const double pos = (double)a.pos[i];
-    double cs[8], sn[8];
+    double xl[QP], xh[QP];
+    if (a.kv_proj) {
+      const float* kp = a.kv_proj + (size_t)i * 2 * kvd + h * D;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pi = g * 8 + e;
-      const double f = pow(a.theta, -2.0 * (double)pi / (double)D);
-      sincos(pos * f, &sn[e], &cs[e]);
+      for (int e = 0; e < QP; ++e) {
+        xl[e] = (double)kp[p0 + e];
+        xh[e] = (double)kp[half + p0 + e];
+      }
+    } else {
+      const uint16_t* kp = a.k_new + (size_t)i * kvd + h * D;
+      const uint2 lo = *reinterpret_cast<const uint2*>(kp + p0);
+      const uint2 hi = *reinterpret_cast<const uint2*>(kp + half + p0);
+      xl[0] = (double)bf16_to_f32(lo.x & 0xffffu);
+      xl[1] = (double)bf16_to_f32(lo.x >> 16);
+      xl[2] = (double)bf16_to_f32(lo.y & 0xffffu);
+      xl[3] = (double)bf16_to_f32(lo.y >> 16);
+      xh[0] = (double)bf16_to_f32(hi.x & 0xffffu);
+      xh[1] = (double)bf16_to_f32(hi.x >> 16);
+      xh[2] = (double)bf16_to_f32(hi.y & 0xffffu);
+      xh[3] = (double)bf16_to_f32(hi.y >> 16);
     }
-    for (int h = 0; h < a.hkv; ++h) {
-      double xl[8], xh[8];
-      if (a.kv_proj) {
-        const float* kp = a.kv_proj + (size_t)i * 2 * kvd + h * D;
+    double cs[QP], sn[QP];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xl[e] = (double)kp[g * 8 + e];
-          xh[e] = (double)kp[half + g * 8 + e];
-        }
-      } else {
-        const uint16_t* kp = a.k_new + (size_t)i * kvd + h * D;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + g * 8);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + half + g * 8);
+    for (int e = 0; e < QP; ++e) sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
+    uint32_t yl[QP / 2], yh[QP / 2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xl[2 * e] = (double)bf16_to_f32(lo[e] & 0xffffu);
-          xl[2 * e + 1] = (double)bf16_to_f32(lo[e] >> 16);
-          xh[2 * e] = (double)bf16_to_f32(hi[e] & 0xffffu);
-          xh[2 * e + 1] = (double)bf16_to_f32(hi[e] >> 16);
-        }
+    for (int e = 0; e < QP / 2; ++e) {
+      const int e0 = 2 * e, e1 = 2 * e + 1;
+      yl[e] = f64_to_bf16(xl[e0] * cs[e0] - xh[e0] * sn[e0]) |
+              (f64_to_bf16(xl[e1] * cs[e1] - xh[e1] * sn[e1]) << 16);
+      yh[e] = f64_to_bf16(xh[e0] * cs[e0] + xl[e0] * sn[e0]) |
+              (f64_to_bf16(xh[e1] * cs[e1] + xl[e1] * sn[e1]) << 16);
+    }
+    uint16_t* dst = sl.k + h * D;
+    *reinterpret_cast<uint2*>(dst + p0) = make_uint2(yl[0], yl[1]);
+    *reinterpret_cast<uint2*>(dst + half + p0) = make_uint2(yh[0], yh[1]);
+    // V: the same thread moves the matching 2 x 4 values of this head
+    uint16_t* vd = sl.v + h * D;
+    if (a.kv_proj) {
+      const float* vp = a.kv_proj + (size_t)i * 2 * kvd + kvd + h * D;
+      uint32_t w0[2], w1[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        w0[e] = f32_to_bf16(vp[p0 + 2 * e]) | (f32_to_bf16(vp[p0 + 2 * e + 1]) << 16);
+        w1[e] = f32_to_bf16(vp[half + p0 + 2 * e]) | (f32_to_bf16(vp[half + p0 + 2 * e + 1]) << 16);
       }
-      uint32_t yl[4], yh[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t l0 = f64_to_bf16(xl[2 * e] * cs[2 * e] - xh[2 * e] * sn[2 * e]);
-        const uint32_t l1 = f64_to_bf16(xl[2 * e + 1] * cs[2 * e + 1] - xh[2 * e + 1] * sn[2 * e + 1]);
-        const uint32_t h0 = f64_to_bf16(xh[2 * e] * cs[2 * e] + xl[2 * e] * sn[2 * e]);
-        const uint32_t h1 = f64_to_bf16(xh[2 * e + 1] * cs[2 * e + 1] + xl[2 * e + 1] * sn[2 * e + 1]);
-        yl[e] = l0 | (l1 << 16);
-        yh[e] = h0 | (h1 << 16);
-      }
-      uint16_t* dst = sl.k + h * D;
-      *reinterpret_cast<u32x4*>(dst + g * 8) = u32x4{yl[0], yl[1], yl[2], yl[3]};
-      *reinterpret_cast<u32x4*>(dst + half + g * 8) = u32x4{yh[0], yh[1], yh[2], yh[3]};
-      // V: the same thread moves the matching 2 x 8 values of this head
-      uint16_t* vd = sl.v + h * D;
-      if (a.kv_proj) {
-        const float* vp = a.kv_proj + (size_t)i * 2 * kvd + kvd + h * D;
-        uint32_t w0[4], w1[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[e] = f32_to_bf16(vp[g * 8 + 2 * e]) | (f32_to_bf16(vp[g * 8 + 2 * e + 1]) << 16);
-          w1[e] = f32_to_bf16(vp[half + g * 8 + 2 * e]) |
-                  (f32_to_bf16(vp[half + g * 8 + 2 * e + 1]) << 16);
-        }
-        *reinterpret_cast<u32x4*>(vd + g * 8) = u32x4{w0[0], w0[1], w0[2], w0[3]};
-        *reinterpret_cast<u32x4*>(vd + half + g * 8) = u32x4{w1[0], w1[1], w1[2], w1[3]};
-      } else {
-        const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
-        *reinterpret_cast<u32x4*>(vd + g * 8) = *reinterpret_cast<const u32x4*>(vs + g * 8);
-        *reinterpret_cast<u32x4*>(vd + half + g * 8) =
-            *reinterpret_cast<const u32x4*>(vs + half + g * 8);
-      }
+      *reinterpret_cast<uint2*>(vd + p0) = make_uint2(w0[0], w0[1]);
+      *reinterpret_cast<uint2*>(vd + half + p0) = make_uint2(w1[0], w1[1]);
+    } else {
+      const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
+      *reinterpret_cast<uint2*>(vd + p0) = *reinterpret_cast<const uint2*>(vs + p0);
+      *reinterpret_cast<uint2*>(vd + half + p0) = *reinterpret_cast<const uint2*>(vs + half + p0);
     }
   }
 }
@@ -652,10 +669,11 @@ static hipError_t launch_attn_d(const AttnArgs& a, const float* q_rot, hipStream
 }
 
 int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
-                  double theta, float scale_log2, const int32_t* plan_offsets,
+                  const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(rope_q_kernel, dim3(batch), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, theta,
+  const int bx = (hq * (d / 2) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(rope_q_kernel, dim3(bx, batch), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
                      scale_log2, plan_offsets, split_offsets, batch);
   return (int)hipGetLastError();
 }
@@ -670,21 +688,18 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int grid = a.batch * a.hq;
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL(merge_lse_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_lse_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    return (int)hipErrorInvalidValue;
+  if (a.head_dim != 64 && a.head_dim != 128) return (int)hipErrorInvalidValue;
+  const int64_t grid = (int64_t)a.batch * a.hq * (a.head_dim / kMergeDims);
+  if (grid > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 
 int launch_append(const AppendArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int64_t total = (int64_t)a.n_new * (a.head_dim / 16);
+  const int64_t total = (int64_t)a.n_new * a.hkv * (a.head_dim / 8);
   const int64_t blocks = (total + kThreads - 1) / kThreads;
-  const int grid = (int)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+  const int grid = (int)(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
   hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }

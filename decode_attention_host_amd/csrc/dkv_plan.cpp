@@ -28,8 +28,9 @@ bool fail(std::string* err, const char* fmt, long long a = 0, long long b = 0, l
   return false;
 }
 
-// Attention workgroups resident per CU (LDS ~37 KB each of the 160 KB).
-constexpr int kSlotsPerCu = 4;
+// Attention workgroups the planner places per CU.  Two per CU stream HBM at
+// its best measured rate; more only lengthen the tail of the persistent loop.
+constexpr int kSlotsPerCu = 2;
 
 int32_t choose_chunk(int64_t tier_token_heads, int32_t wgs, int32_t units_per_wg, int32_t align,
                      int32_t tuned) {
@@ -112,13 +113,15 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
     wh = std::min(wh, resident / 2);
     wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
   } else if (host_tok > 0) {
-    wh = in.host_wgs > 0 ? in.host_wgs : cus * 2;
+    // Host tier alone: a few dozen workgroups already keep the link full;
+    // more only add request contention.
+    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 8);
   } else {
     wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
   }
 
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
-  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, 4, align, in.host_chunk);
+  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, 2, align, in.host_chunk);
   const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 2, align, in.dev_chunk);
 
   // ---- items

@@ -260,6 +260,22 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
                           int32_t iters, void* dma_dst, const void* dma_src_host,
                           dkv_bw_result* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Live kernel timing for measurement.  While enabled, every launch of the
+ * named kernel is bracketed by a HIP event pair recorded on the stream the
+ * kernel runs on.  dkv_kernel_timing_read waits for the recorded events,
+ * returns how many launches were timed and their summed duration in ms, and
+ * clears the record.  kernel: DKV_KERNEL_ATTN (split attention),
+ * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND.
+ * ---------------------------------------------------------------------- */
+#define DKV_KERNEL_ATTN 0
+#define DKV_KERNEL_ROPE_Q 1
+#define DKV_KERNEL_MERGE 2
+#define DKV_KERNEL_APPEND 3
+
+dkv_status dkv_kernel_timing(int32_t enable);
+dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,7 +79,10 @@ def rope_neox(x, pos, theta: float) -> np.ndarray:
     D = x.shape[-1]
     half = D // 2
     f = rope_inv_freq(D, theta)
-    a = np.asarray(pos, dtype=np.float64)[..., None] * f
+    pos = np.asarray(pos, dtype=np.float64)
+    if np.broadcast_shapes(pos.shape, x.shape[:-1]) != x.shape[:-1]:
+        raise ValueError(f"positions {pos.shape} do not broadcast to the vectors {x.shape[:-1]}")
+    a = pos[..., None] * f
     c, s = np.cos(a), np.sin(a)
     lo, hi = x[..., :half], x[..., half:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)

@@ -10,6 +10,8 @@ from .generators import (  # noqa: F401
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     normal_bf16,
+    kv_raw,
+    query,
     ragged_lengths,
     paged_table,
     workload,

@@ -88,6 +88,21 @@ def normal_bf16(seed: int, tid: int, shape, std: float = 1.0, out: np.ndarray | 
     return out
 
 
+def kv_raw(seed: int, lens, hkv: int, d: int, threads: int | None = None):
+    """Raw (unrotated) keys and values per sequence: lists of uint16 [L_b, Hkv, D].
+    Sequence b draws from seed ``seed * 1000 + b`` (tensor ids K and V)."""
+    ks, vs = [], []
+    for b, n in enumerate(lens):
+        ks.append(normal_bf16(seed * 1000 + b, TensorId.K, (int(n), hkv, d), threads=threads))
+        vs.append(normal_bf16(seed * 1000 + b, TensorId.V, (int(n), hkv, d), threads=threads))
+    return ks, vs
+
+
+def query(seed: int, batch: int, hq: int, d: int) -> np.ndarray:
+    """Query bits [B, Hq, D], N(0, 1)."""
+    return normal_bf16(seed, TensorId.Q, (batch, hq, d))
+
+
 def ragged_lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
     """Integer lengths uniform on [lo, hi], both inclusive."""
     rng = np.random.default_rng([seed, int(TensorId.LENS)])
