@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     HostBuffer,
     KVCache,
     alloc_decode_buffers,
+    attn_trace,
     append_workspace_bytes,
     decode,
     decode_attn_split,

@@ -312,3 +312,13 @@ def kernel_timing_read(kernel: str) -> tuple[int, float]:
     ms = C.c_double()
     check(lib().dkv_kernel_timing_read(KERNELS[kernel], C.byref(n), C.byref(ms)))
     return n.value, ms.value
+
+
+def attn_trace(buffer: torch.Tensor | None):
+    """dkv_attn_trace: per-workgroup (start, end, role, units) of later attention
+    launches into ``buffer`` (int64 device tensor [n, 4]); None turns it off."""
+    if buffer is None:
+        check(lib().dkv_attn_trace(None, 0))
+    else:
+        assert buffer.dtype == torch.int64 and buffer.is_cuda and buffer.dim() == 2 and buffer.shape[1] == 4
+        check(lib().dkv_attn_trace(_ptr(buffer), int(buffer.shape[0])))

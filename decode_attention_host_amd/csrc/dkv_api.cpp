@@ -252,6 +252,11 @@ dkv::RopeFreq rope_freq(double theta, int d) {
   return r;
 }
 
+// ---------------------------------------------------------------- workgroup trace
+std::mutex g_trace_mu;
+uint64_t* g_trace_buf = nullptr;
+int32_t g_trace_cap = 0;
+
 // ---------------------------------------------------------------- kernel timing
 struct Timing {
   std::mutex mu;
@@ -475,6 +480,7 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   a.dev_items = a.host_items + L.n_host_items;
   a.plist = reinterpret_cast<const int32_t*>(ws + L.plist_off);
   a.plan_offsets = reinterpret_cast<const int32_t*>(ws + L.offsets_off);
+  a.unit_counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
   a.split_offsets = split_offsets;
   a.n_host_units = L.n_host_items * kv->num_kv_heads;
   a.n_dev_units = L.n_dev_items * kv->num_kv_heads;
@@ -499,6 +505,11 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   a.theta = rope_theta;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    a.wg_trace = g_trace_buf;
+    a.wg_trace_cap = g_trace_cap;
+  }
   TimedLaunch t_attn(DKV_KERNEL_ATTN, s);
   he = (hipError_t)dkv::launch_attn_with_q(a, q_rot, stream);
   t_attn.done();
@@ -779,6 +790,15 @@ dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_
   if (err != hipSuccess) return hip_err(err, "kernel timing");
   *count = (int32_t)rec.size();
   *total_ms = tot;
+  return ok();
+}
+
+dkv_status dkv_attn_trace(void* dev_buffer, int32_t capacity_wgs) {
+  if (capacity_wgs < 0 || (capacity_wgs > 0 && !dev_buffer))
+    return set_err(DKV_ERR_INVALID, "trace buffer required for a positive capacity");
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace_buf = capacity_wgs > 0 ? static_cast<uint64_t*>(dev_buffer) : nullptr;
+  g_trace_cap = capacity_wgs;
   return ok();
 }
 

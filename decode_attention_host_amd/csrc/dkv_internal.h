@@ -49,6 +49,7 @@ struct PlanLayout {
   size_t items_off = 0;    // byte offsets inside the blob
   size_t plist_off = 0;
   size_t offsets_off = 0;
+  size_t counters_off = 0;       // two int32 counters, zero in the image
   size_t blob_bytes = 0;
   int32_t n_plist = 0;
 };
@@ -59,6 +60,7 @@ struct AttnArgs {
   const PlanItem* dev_items;
   const int32_t* plist;          // paged: logical page indices
   const int32_t* plan_offsets;   // [batch+1] split offsets (in the workspace)
+  int32_t* unit_counters;        // [2] dynamic unit counters (HBM, host), zero at launch
   int32_t* split_offsets;        // [batch+1] caller copy (written by block 0)
   int32_t n_host_units;          // host items x Hkv
   int32_t n_dev_units;           // dev items x Hkv
@@ -84,6 +86,9 @@ struct AttnArgs {
   double theta;
   float* part_o;                 // [S][Hq][D]
   float* part_lse;               // [S][Hq]
+  uint64_t* wg_trace;            // optional [grid][4]: start, end, role, units (wall clock)
+  int32_t wg_trace_cap;
+  int32_t pad1;
 };
 
 struct MergeArgs {

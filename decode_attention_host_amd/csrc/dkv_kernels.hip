@@ -129,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
   __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
   __shared__ float a_lds[4][8];
+  __shared__ int s_next;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,6 +137,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
   const int n = lane & 15;     // MFMA column / row-in-tile
   const int j4 = lane >> 4;    // 0..3
 
+  // Role: the first host_wgs workgroups stream the host tier, the rest HBM.
   const bool host_role = (int)blockIdx.x < a.host_wgs;
   const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
   const int nwg = host_role ? a.host_wgs : a.dev_wgs;
@@ -144,12 +146,63 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
   const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
   const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
   const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
-  const int64_t row_elems = (int64_t)a.hkv * D;
+  // Units [0, nwg) go to workgroups by index; each later unit goes to the
+  // workgroup that finishes first (per-role counter, zeroed by the plan upload).
+  int* counter = a.unit_counters + (host_role ? 1 : 0);
 
-  for (int u = wg; u < nunits; u += nwg) {
-    const int item_idx = u / a.hkv;
-    const int kvh = u - item_idx * a.hkv;
-    const PlanItem it = items[item_idx];
+  const bool traced = a.wg_trace && (int)blockIdx.x < a.wg_trace_cap && tid == 0;
+  const uint64_t t_start = traced ? wall_clock64() : 0;
+  int units_done = 0;
+
+  u32x4 kreg[NC], vreg[NC];
+  auto load_tile = [&](const PlanItem& it, int kvh, int tile) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int r = chunk / S::kChunksPerRow;
+      const int col = chunk - r * S::kChunksPerRow;
+      const int tok = tile * kTile + r;
+      bool valid = tok < it.n_tok;
+      int64_t row = 0;
+      if (PAGED) {
+        if (valid) {
+          const int lp = a.plist[it.plist + (tok >> a.page_shift)];
+          const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
+          const int64_t phys = (int64_t)(e >> 1);
+          row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
+          valid = e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
+        }
+      } else {
+        row = it.row0 + tok;
+      }
+      const int64_t off = (row * a.hkv + kvh) * D + col * 8;
+      if (valid) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + off);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + off);
+        if (host_role) {
+          kreg[c] = __builtin_nontemporal_load(kp);
+          vreg[c] = __builtin_nontemporal_load(vp);
+        } else {
+          kreg[c] = *kp;
+          vreg[c] = *vp;
+        }
+      } else {
+        kreg[c] = u32x4{0u, 0u, 0u, 0u};
+        vreg[c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  int u = wg;
+  PlanItem it{};
+  int kvh = 0;
+  if (u < nunits) {
+    it = items[u / a.hkv];
+    kvh = u - (u / a.hkv) * a.hkv;
+    load_tile(it, kvh, 0);
+  }
+  while (u < nunits) {
+    ++units_done;
     const int ntiles = (it.n_tok + kTile - 1) / kTile;
 
     // ---- query operand: columns h (high bf16 part) and h+8 (low part)
@@ -186,47 +239,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
 
-    u32x4 kreg[NC], vreg[NC];
-
-    auto load_tile = [&](int tile) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int r = chunk / S::kChunksPerRow;
-        const int col = chunk - r * S::kChunksPerRow;
-        const int tok = tile * kTile + r;
-        bool valid = tok < it.n_tok;
-        int64_t row = 0;
-        if (PAGED) {
-          if (valid) {
-            const int lp = a.plist[it.plist + (tok >> a.page_shift)];
-            const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
-            const int64_t phys = (int64_t)(e >> 1);
-            row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
-            valid = e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
-          }
-        } else {
-          row = it.row0 + tok;
-        }
-        const int64_t off = (row * a.hkv + kvh) * D + col * 8;
-        if (valid) {
-          const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + off);
-          const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + off);
-          if (host_role) {
-            kreg[c] = __builtin_nontemporal_load(kp);
-            vreg[c] = __builtin_nontemporal_load(vp);
-          } else {
-            kreg[c] = *kp;
-            vreg[c] = *vp;
-          }
-        } else {
-          kreg[c] = u32x4{0u, 0u, 0u, 0u};
-          vreg[c] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    };
-
-    load_tile(0);
+    int next_u = nunits;
+    PlanItem nit{};
+    int nkvh = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
       __syncthreads();  // previous tile's readers are done
 #pragma unroll
@@ -237,8 +252,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
         *reinterpret_cast<u32x4*>(k_lds + r * S::kPitch + col * 16) = kreg[c];
         *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
       }
+      const bool last = tile + 1 == ntiles;
+      if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
       __syncthreads();
-      if (tile + 1 < ntiles) load_tile(tile + 1);
+      // keep one tile in flight: the next tile of this unit, or the first
+      // tile of the next unit while this unit's last tile is computed
+      if (!last) {
+        load_tile(it, kvh, tile + 1);
+      } else {
+        next_u = s_next;
+        if (next_u < nunits) {
+          nit = items[next_u / a.hkv];
+          nkvh = next_u - (next_u / a.hkv) * a.hkv;
+          load_tile(nit, nkvh, 0);
+        }
+      }
 
       // ---- scores for this wave's 16 tokens: rows = tokens, columns = heads
       floatx4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -346,16 +374,26 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
         a.part_lse[(size_t)it.slot * a.hq + hq_idx] =
             (M == -INFINITY) ? -INFINITY : (M + log2f(lsum)) * 0.69314718055994530942f;
     }
-    __syncthreads();
+    // the next unit's first tile is already in registers
+    u = next_u;
+    it = nit;
+    kvh = nkvh;
+  }
+  if (traced) {
+    uint64_t* t = a.wg_trace + 4 * (size_t)blockIdx.x;
+    t[0] = t_start;
+    t[1] = wall_clock64();
+    t[2] = host_role ? 1 : 0;
+    t[3] = (uint64_t)units_done;
   }
 }
 
 // ---------------------------------------------------------------------------
-// LSE merge: one workgroup per (b, h).  The maximum and the weight sum of the
-// split LSEs are block reductions; then 256/D groups of D threads each fold a
-// strided subset of the splits (independent loads) and combine through LDS.
+// LSE merge: the maximum and the weight sum of the split LSEs are block
+// reductions, then every split's partial is folded with weight exp(lse - M).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* sm) {
+template <int NT>
+__device__ __forceinline__ float block_reduce_n(float v, bool is_max, float* sm) {
   for (int o = 32; o >= 1; o >>= 1) {
     const float w = __shfl_xor(v, o);
     v = is_max ? fmaxf(v, w) : v + w;
@@ -366,70 +404,75 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* sm) {
   __syncthreads();
   v = sm[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) v = is_max ? fmaxf(v, sm[w]) : v + sm[w];
+  for (int w = 1; w < NT / 64; ++w) v = is_max ? fmaxf(v, sm[w]) : v + sm[w];
   return v;
 }
 
-// Workgroup = (b, h, 32-dim chunk of the head): 8 groups of 32 lanes each fold
-// every 8th split with four independent loads in flight, so a (b, h) merge is
-// spread over D/32 workgroups and many loads overlap.
-constexpr int kMergeDims = 32;
-constexpr int kMergeGroups = kThreads / kMergeDims;
+// Workgroup = (b, h), 1024 threads: D/4 lanes each own 4 dims (one 16-byte
+// load per split), 4096/D groups of lanes fold every group-th split with
+// several loads in flight, then the groups combine through LDS.
+constexpr int kMergeThreads = 1024;
 
-__global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
-  __shared__ float sm_red[kThreads / 64];
-  __shared__ float sm_o[kMergeGroups][kMergeDims];
-  const int D = a.head_dim;
-  const int nchunk = D / kMergeDims;
-  const int bh = blockIdx.x / nchunk;
-  const int dc = blockIdx.x - bh * nchunk;
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
+  constexpr int LANES = D / 4;
+  constexpr int NG = kMergeThreads / LANES;
+  constexpr int U = 4;
+  __shared__ float sm_red[kMergeThreads / 64];
+  __shared__ __attribute__((aligned(16))) float sm_o[NG][D];
+  const int bh = blockIdx.x;
   const int b = bh / a.hq, h = bh - b * a.hq;
   const int tid = threadIdx.x;
   const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
   const float* lse = a.part_lse + h;
   float m = -INFINITY;
-  for (int s = s0 + tid; s < s1; s += kThreads) m = fmaxf(m, lse[(size_t)s * a.hq]);
-  const float M = block_reduce(m, true, sm_red);
-  float* out = a.out_o + ((size_t)b * a.hq + h) * D + dc * kMergeDims;
+  for (int s = s0 + tid; s < s1; s += kMergeThreads) m = fmaxf(m, lse[(size_t)s * a.hq]);
+  const float M = block_reduce_n<kMergeThreads>(m, true, sm_red);
+  float* out = a.out_o + ((size_t)b * a.hq + h) * D;
   if (M == -INFINITY) {  // no finite split
-    if (tid < kMergeDims) out[tid] = 0.f;
-    if (tid == 0 && dc == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = -INFINITY;
+    if (tid < D) out[tid] = 0.f;
+    if (tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = -INFINITY;
     return;
   }
   float l = 0.f;
-  for (int s = s0 + tid; s < s1; s += kThreads) {
+  for (int s = s0 + tid; s < s1; s += kMergeThreads) {
     const float x = lse[(size_t)s * a.hq];
     l += (x == -INFINITY) ? 0.f : expf(x - M);
   }
-  const float Lsum = block_reduce(l, false, sm_red);
-  const int g = tid / kMergeDims, d = tid - g * kMergeDims;
-  const float* po = a.part_o + (size_t)h * D + dc * kMergeDims + d;
+  const float Lsum = block_reduce_n<kMergeThreads>(l, false, sm_red);
+  const int g = tid / LANES, d4 = (tid - g * LANES) * 4;
+  const float* po = a.part_o + (size_t)h * D + d4;
   const size_t srow = (size_t)a.hq * D;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   int s = s0 + g;
-  for (; s + 3 * kMergeGroups < s1; s += 4 * kMergeGroups) {
-    float x[4], o[4];
+  for (; s + (U - 1) * NG < s1; s += U * NG) {
+    float x[U];
+    float4 o[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = lse[(size_t)(s + k * kMergeGroups) * a.hq];
-      o[k] = po[(size_t)(s + k * kMergeGroups) * srow];
+    for (int k = 0; k < U; ++k) {
+      x[k] = lse[(size_t)(s + k * NG) * a.hq];
+      o[k] = *reinterpret_cast<const float4*>(po + (size_t)(s + k * NG) * srow);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] += (x[k] == -INFINITY) ? 0.f : expf(x[k] - M) * o[k];
+    for (int k = 0; k < U; ++k) {
+      const float w = (x[k] == -INFINITY) ? 0.f : expf(x[k] - M);
+      acc.x += w * o[k].x; acc.y += w * o[k].y; acc.z += w * o[k].z; acc.w += w * o[k].w;
+    }
   }
-  for (; s < s1; s += kMergeGroups) {
+  for (; s < s1; s += NG) {
     const float x = lse[(size_t)s * a.hq];
-    acc[0] += (x == -INFINITY) ? 0.f : expf(x - M) * po[(size_t)s * srow];
+    const float w = (x == -INFINITY) ? 0.f : expf(x - M);
+    const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * srow);
+    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
   }
-  sm_o[g][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  *reinterpret_cast<float4*>(&sm_o[g][d4]) = acc;
   __syncthreads();
-  if (tid < kMergeDims) {
+  if (tid < D) {
     float o = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergeGroups; ++k) o += sm_o[k][tid];
+#pragma unroll 8
+    for (int k = 0; k < NG; ++k) o += sm_o[k][tid];
     out[tid] = o / Lsum;
-    if (tid == 0 && dc == 0 && a.out_lse)
-      a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
+    if (tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
   }
 }
 
@@ -688,10 +731,14 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (a.head_dim != 64 && a.head_dim != 128) return (int)hipErrorInvalidValue;
-  const int64_t grid = (int64_t)a.batch * a.hq * (a.head_dim / kMergeDims);
+  const int64_t grid = (int64_t)a.batch * a.hq;
   if (grid > 0x7fffffff) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(merge_lse_kernel<64>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL(merge_lse_kernel<128>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

@@ -32,13 +32,17 @@ bool fail(std::string* err, const char* fmt, long long a = 0, long long b = 0, l
 // its best measured rate; more only lengthen the tail of the persistent loop.
 constexpr int kSlotsPerCu = 2;
 
-int32_t choose_chunk(int64_t tier_token_heads, int32_t wgs, int32_t units_per_wg, int32_t align,
-                     int32_t tuned) {
+// Tokens per work item.  Workgroups take units dynamically, so several units
+// per workgroup even out per-CU speed differences; the floor keeps each unit
+// long enough that its fixed cost (query operand, epilogue, partial write)
+// stays small next to its KV stream.
+int32_t choose_chunk(int64_t tier_token_heads, int32_t wgs, int32_t units_per_wg, int32_t floor_tok,
+                     int32_t cap_tok, int32_t align, int32_t tuned) {
   if (tuned > 0) return (int32_t)round_up(tuned, align);
   if (tier_token_heads <= 0 || wgs <= 0) return align;
   int64_t c = ceil_div(tier_token_heads, (int64_t)wgs * units_per_wg);
-  c = std::max<int64_t>(c, 256);
-  c = std::min<int64_t>(c, 1 << 16);
+  c = std::max<int64_t>(c, floor_tok);
+  c = std::min<int64_t>(c, cap_tok);
   return (int32_t)round_up(c, align);
 }
 
@@ -100,29 +104,33 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
   }
 
   // ---- workgroup split between tiers
+  // Measured on MI355X: 48-64 workgroups keep PCIe 5.0 x16 full for a host
+  // tier alone; while HBM streams at the same time, every extra host
+  // workgroup costs HBM throughput, so a balanced split uses 16.
   const int32_t cus = std::max(1, in.num_cus);
   const int32_t resident = cus * kSlotsPerCu;
-  const double bw_h = in.host_bw > 0 ? in.host_bw : 50.0;
-  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5000.0;
+  const double bw_h = in.host_bw > 0 ? in.host_bw : 57.0;
+  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5300.0;
+  const double t_h = (double)host_tok / bw_h;   // relative tier times
+  const double t_d = (double)dev_tok / bw_d;
   int32_t wh = 0, wd = 0;
   if (host_tok > 0 && dev_tok > 0) {
-    // Bandwidth-proportional share of the resident slots, with the host
-    // tier never below the count that keeps enough requests in flight.
-    const int32_t floor_h = in.host_wgs > 0 ? in.host_wgs : 32;
-    wh = std::max(floor_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d)));
+    const bool host_dominant = t_h > 1.5 * t_d;
+    const int32_t want_h = in.host_wgs > 0 ? in.host_wgs : (host_dominant ? std::max(8, cus * 3 / 16) : std::max(4, cus / 16));
+    // never below the bandwidth-proportional share of the resident slots
+    wh = std::max(want_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d)));
     wh = std::min(wh, resident / 2);
     wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
   } else if (host_tok > 0) {
-    // Host tier alone: a few dozen workgroups already keep the link full;
-    // more only add request contention.
-    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 8);
+    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 4);
   } else {
     wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
   }
 
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
-  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, 2, align, in.host_chunk);
-  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 2, align, in.dev_chunk);
+  const bool mixed = host_tok > 0 && dev_tok > 0;
+  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, mixed ? 4 : 2, 256, 16384, align, in.host_chunk);
+  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 8, 1024, 1 << 16, align, in.dev_chunk);
 
   // ---- items
   std::vector<PlanItem> hitems, ditems;
@@ -183,7 +191,8 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
   out->items_off = 0;
   out->plist_off = (hitems.size() + ditems.size()) * sizeof(PlanItem);
   out->offsets_off = round_up(out->plist_off + plist.size() * sizeof(int32_t), 16);
-  out->blob_bytes = round_up(out->offsets_off + (B + 1) * sizeof(int32_t), 256);
+  out->counters_off = round_up(out->offsets_off + (B + 1) * sizeof(int32_t), 16);
+  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
   if ((int64_t)(hitems.size() + ditems.size()) * in.hkv > INT32_MAX)
     return fail(err, "too many work units");
   if (blob) {

@@ -235,8 +235,8 @@ typedef struct dkv_tuning {
   int32_t host_chunk;    /* tokens per host work item, multiple of 64 (0: auto) */
   int32_t dev_chunk;     /* tokens per HBM work item, multiple of 64 (0: auto) */
   int32_t reserved;
-  double host_bw_gbs;    /* host-link read bandwidth (0: 50) */
-  double dev_bw_gbs;     /* HBM read bandwidth (0: 5000) */
+  double host_bw_gbs;    /* host-link read bandwidth (0: 57) */
+  double dev_bw_gbs;     /* HBM read bandwidth (0: 5300) */
 } dkv_tuning;
 
 dkv_status dkv_set_tuning(const dkv_tuning* tuning); /* NULL restores defaults */
@@ -274,6 +274,14 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
 #define DKV_KERNEL_APPEND 3
 
 dkv_status dkv_kernel_timing(int32_t enable);
+
+/* Per-workgroup trace of the attention kernel, for measuring how the host and
+ * HBM tiers overlap.  While set, every attention launch makes workgroup i
+ * (i < capacity_wgs) write 4 uint64 values at dev_buffer[4*i]: start and end
+ * of its work in wall-clock ticks (100 MHz), its role (1 host tier, 0 HBM)
+ * and the number of work units it processed.  dev_buffer is device memory of
+ * at least 32 * capacity_wgs bytes; capacity 0 (or NULL) turns tracing off. */
+dkv_status dkv_attn_trace(void* dev_buffer, int32_t capacity_wgs);
 dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms);
 
 #ifdef __cplusplus
