@@ -121,15 +121,32 @@ def run_probe(dk, w, nbytes_host):
                    host_zero_copy_nt=best[2], host_dma_gbs=round(dma["dma_gbs"], 2),
                    host_sweep=sweep)
         del dst
-    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
     big.fill_(1)
-    best = 0.0
-    for nwg in (1024, 2048, 4096):
-        r = dk.probe_read(big.data_ptr(), big.numel(), nwg, nontemporal=False, iters=5)
-        best = max(best, r["read_gbs"])
-    res["hbm_read_gbs"] = round(best, 1)
+    best = (0.0, 0, False)
+    hsweep = []
+    for nt in (True, False):
+        for nwg in (256, 512, 1024, 2048, 4096, 8192):
+            r = dk.probe_read(big.data_ptr(), big.numel(), nwg, nontemporal=nt, iters=5)
+            hsweep.append({"nwg": nwg, "nt": nt, "gbs": round(r["read_gbs"], 1)})
+            if r["read_gbs"] > best[0]:
+                best = (r["read_gbs"], nwg, nt)
+    res["hbm_read_gbs"] = round(best[0], 1)
+    res["hbm_read_wgs"] = best[1]
+    res["hbm_read_nt"] = best[2]
+    res["hbm_sweep"] = hsweep
     del big
     return res
+
+
+def gpu_warm(step, seconds=0.3):
+    """Run the step until the GPU is back at working clocks (it idles while the
+    host builds caches or runs the oracle)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
 
 
 def timed_loop(step, steps, warmup):
@@ -159,7 +176,9 @@ def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
     host_full = w["cache"] if w["cache"].host_rows == L else contiguous_cache(
         hkv, d, [L], 1.0, w["ks"], w["vs"], cfg["theta"])
     dev_full = contiguous_cache(hkv, d, [L], 0.0, w["ks"], w["vs"], cfg["theta"])
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # read-only cache flush between steps (a write flush would leave dirty
+    # lines to write back during the timed step)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     row = hkv * d * 2 * 2
     out = []
     for r in ratios:
@@ -167,18 +186,24 @@ def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
         nh = view.n_host
         bufs = dk.alloc_decode_buffers(view, 1, hq, [L], r)
         step = make_step(dk, cfg, w, view, r, bufs)
-        for _ in range(3):
+        gpu_warm(step, 0.3)
+        dk.kernel_timing(True)
+        for k in dk.api.KERNELS:
+            dk.kernel_timing_read(k)
+        # steps back to back with a flush between them; the host runs ahead, so
+        # each event pair brackets GPU work only
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        sink = torch.empty(iters, dtype=torch.float32, device="cuda")
+        for i in range(iters):
+            torch.sum(flush, dim=0, out=sink[i])
+            ev[i][0].record()
             step()
-        times = []
-        for _ in range(iters):
-            flush.zero_()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            step()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) for a, b in ev]
+        kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
+        dk.kernel_timing(False)
         med = statistics.median(times)
         hb, db = nh * row, (L - nh) * row
         t_star = max(hb / (bw_h * 1e6), db / (bw_d * 1e6))
@@ -189,8 +214,9 @@ def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
                     "eff_gbs": round((hb + db) / (med * 1e6), 2),
                     "roofline_ms_measured": round(t_star, 4), "frac_measured": round(t_star / med, 3),
                     "roofline_ms_nominal": round(t_nom, 4), "frac_nominal": round(t_nom / med, 3),
-                    "hbm_bytes_saved": hb, "plan": {k: bufs.info[k] for k in ("host_wgs", "dev_wgs",
-                                                                              "host_chunk", "dev_chunk")}})
+                    "hbm_bytes_saved": hb,
+                    "kernel_ms": {k: round(v[1] / max(1, v[0]), 5) for k, v in kt.items()},
+                    "plan": {k: bufs.info[k] for k in ("host_wgs", "dev_wgs", "host_chunk", "dev_chunk")}})
         log(f"[bench] sweep r={r:.4f}: {med:.3f} ms, {out[-1]['eff_gbs']} GB/s, "
             f"frac(measured) {out[-1]['frac_measured']}")
     del flush
@@ -198,6 +224,21 @@ def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
         host_full.free()
     dev_full.free()
     return out
+
+
+def best_split(sweep, bw_h, bw_d):
+    """Fastest measured ratio vs the combined roofline total / (BW_h + BW_d)."""
+    best = min(sweep, key=lambda e: e["ms_median"])
+    total = best["host_bytes"] + best["hbm_bytes"]
+    t_comb = total / ((bw_h + bw_d) * 1e6)
+    t_comb_nom = total / ((PCIE_PEAK_GBS + HBM_PEAK_GBS) * 1e6)
+    return {"ratio": best["ratio"], "ms_median": best["ms_median"],
+            "combined_roofline_ms_measured": round(t_comb, 4),
+            "frac_combined_measured": round(t_comb / best["ms_median"], 3),
+            "combined_roofline_ms_nominal": round(t_comb_nom, 4),
+            "frac_combined_nominal": round(t_comb_nom / best["ms_median"], 3),
+            "attn_ms": best["kernel_ms"]["attn"],
+            "frac_combined_measured_attn": round(t_comb / best["kernel_ms"]["attn"], 3)}
 
 
 def cpu_baseline(cfg, w, budget_s):
@@ -236,6 +277,7 @@ def measure_contiguous(dk, cfg, seed, flags, steps, warmup):
     B, hq, d, lens, ratio = cfg["batch"], cfg["hq"], cfg["d"], cfg["lens"], cfg["ratio"]
     bufs = dk.alloc_decode_buffers(w["cache"], B, hq, lens, ratio)
     step = make_step(dk, cfg, w, w["cache"], ratio, bufs)
+    gpu_warm(step)
     dk.kernel_timing(True)
     for k in dk.api.KERNELS:
         dk.kernel_timing_read(k)
@@ -300,6 +342,7 @@ def measure_fused_paged(dk, cfg, seed, flags, steps, warmup):
         dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, B, hq, d, out_o=bufs.out_o,
                      out_lse=bufs.out_lse)
 
+    gpu_warm(step)
     dk.kernel_timing(True)
     for k in dk.api.KERNELS:
         dk.kernel_timing_read(k)
@@ -335,7 +378,7 @@ def measure_long_sweep(dk, cfg, seed, flags, iters, bw_h, bw_d):
     ratios = [0.0, r_star, 0.25, 0.5, 0.75, 0.9, 1.0]
     out = ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d)
     host_full.free()
-    return out
+    return {"sweep": out, "best_split": best_split(out, bw_h, bw_d)}
 
 
 def load_traffic(workload_name):
@@ -409,6 +452,8 @@ def main():
         log(f"[bench] profile run: {args.steps} steps, {ms:.4f} ms/step")
         cache.free()
         return
+    # bring the GPU to its working clocks before anything is measured
+    gpu_warm(step, 0.5)
     dk.kernel_timing(False)
     # headline: W warm-up steps, then exactly K timed steps
     dk.kernel_timing(True)
@@ -426,7 +471,7 @@ def main():
     probe = {}
     if not args.no_probe:
         probe = run_probe(dk, w, 128 << 20)
-        log(f"[bench] probe: {json.dumps({k: v for k, v in probe.items() if k != 'host_sweep'})}")
+        log(f"[bench] probe: {json.dumps({k: v for k, v in probe.items() if 'sweep' not in k})}")
     nominal, link = pcie_nominal_gbs(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None))
     probe["host_link_nominal_gbs"] = round(nominal, 2) if nominal else None
     probe["host_link"] = link
@@ -455,6 +500,7 @@ def main():
         r_star = bw_h / (bw_h + bw_d)
         ratios = [0.0, r_star, 0.25, 0.5, 0.75, 0.9, 1.0]
         sweep = ratio_sweep(dk, cfg, w, ratios, args.sweep_iters, bw_h, bw_d)
+        sweep = {"sweep": sweep, "best_split": best_split(sweep, bw_h, bw_d)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -468,7 +514,7 @@ def main():
         if name == "llama3_8b_1m":
             bw_h = probe.get("host_zero_copy_gbs") or 50.0
             bw_d = probe.get("hbm_read_gbs") or 5000.0
-            workloads[name] = {"sweep": measure_long_sweep(dk, wcfg, args.seed, flags, 10, bw_h, bw_d)}
+            workloads[name] = measure_long_sweep(dk, wcfg, args.seed, flags, 10, bw_h, bw_d)
         elif wcfg["layout"] == "paged":
             workloads[name] = measure_fused_paged(dk, wcfg, args.seed, flags, 20, 5)
         else:
@@ -476,7 +522,7 @@ def main():
             ww["cache"].free()
             workloads[name] = res
         log(f"[bench] {name} measured in {time.time() - t0:.1f}s: "
-            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn')})}")
+            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn', 'best_split')})}")
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,

@@ -179,13 +179,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
       if (valid) {
         const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + off);
         const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + off);
-        if (host_role) {
-          kreg[c] = __builtin_nontemporal_load(kp);
-          vreg[c] = __builtin_nontemporal_load(vp);
-        } else {
-          kreg[c] = *kp;
-          vreg[c] = *vp;
-        }
+        // KV is read once per step: non-temporal loads on both tiers (on
+        // MI355X they also stream HBM faster than ordinary loads)
+        kreg[c] = __builtin_nontemporal_load(kp);
+        vreg[c] = __builtin_nontemporal_load(vp);
       } else {
         kreg[c] = u32x4{0u, 0u, 0u, 0u};
         vreg[c] = u32x4{0u, 0u, 0u, 0u};
@@ -670,15 +667,16 @@ __global__ __launch_bounds__(kThreads) void proj_reduce_kernel(ProjArgs a) {
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ src,
                                                              int64_t n16, float* sink) {
+  constexpr int U = 8;  // 16-byte loads in flight per thread
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v[4];
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = NT ? __builtin_nontemporal_load(src + i + k * stride) : src[i + k * stride];
+    for (int k = 0; k < U; ++k) v[k] = NT ? __builtin_nontemporal_load(src + i + k * stride) : src[i + k * stride];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    for (int k = 0; k < U; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
   }
   for (; i < n16; i += stride) {
     const u32x4 v = NT ? __builtin_nontemporal_load(src + i) : src[i];
