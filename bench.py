@@ -149,6 +149,23 @@ def gpu_warm(step, seconds=0.3):
         torch.cuda.synchronize()
 
 
+def graph_timing(dk, step, steps):
+    """The same step captured once into a HIP graph, K replays timed back to back."""
+    import torch
+    g = dk.StepGraph(step)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def timed_loop(step, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -286,6 +303,9 @@ def measure_contiguous(dk, cfg, seed, flags, steps, warmup):
     dk.kernel_timing(False)
     info = bufs.info
     res = summarize(cfg, info, ms, kt)
+    gms = graph_timing(dk, step, steps)
+    res["graph_ms_per_step"] = round(gms, 4)
+    res["graph_eff_kv_gbs"] = round((info["host_bytes"] + info["dev_bytes"]) / (gms * 1e6), 2)
     return res, w
 
 
@@ -351,6 +371,8 @@ def measure_fused_paged(dk, cfg, seed, flags, steps, warmup):
     dk.kernel_timing(False)
     res = summarize(cfg, bufs.info, ms, kt, extra_bytes=2 * hid * hkv * d * 2)
     res["lens"] = {"min": min(lens), "max": max(lens), "sum": sum(lens)}
+    gms = graph_timing(dk, step, steps)
+    res["graph_ms_per_step"] = round(gms, 4)
     cache.free()
     return res
 
@@ -405,7 +427,7 @@ def main():
     ap.add_argument("--sweep-iters", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--tune", default="", help="comma list of dkv_tuning fields, e.g. host_wgs=256")
-    ap.add_argument("--extra", default="opt_6_7b_b8,fused_ragged,llama3_8b_1m",
+    ap.add_argument("--extra", default="tiny,opt_6_7b_b8,fused_ragged,llama3_8b_1m",
                     help="other workloads measured after the headline ('' for none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: headline steps plus two calibration reads of known "
@@ -467,6 +489,8 @@ def main():
     log(f"[bench] step {ms:.4f} ms (wall {wall / args.steps * 1e3:.4f} ms), attention kernel {attn_ms:.4f} ms "
         f"over {n_attn} launches")
     value = kv_bytes / (ms * 1e6)
+    graph_ms = graph_timing(dk, step, args.steps)
+    log(f"[bench] graph replay of the same step: {graph_ms:.4f} ms")
 
     probe = {}
     if not args.no_probe:
@@ -522,7 +546,7 @@ def main():
             ww["cache"].free()
             workloads[name] = res
         log(f"[bench] {name} measured in {time.time() - t0:.1f}s: "
-            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn', 'best_split')})}")
+            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'graph_ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn', 'best_split')})}")
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
@@ -534,6 +558,8 @@ def main():
                    "offload_ratio": ratio, "layout": cfg["layout"], "rope_theta": cfg["theta"],
                    "host_memory": args.host_flags, "kv_bytes_per_step": kv_bytes},
         "latency_ms_per_token": round(ms / B, 5),
+        "graph": {"ms_per_step": round(graph_ms, 5), "eff_kv_gbs": round(kv_bytes / (graph_ms * 1e6), 3),
+                  "note": "the same step captured into one HIP graph and replayed"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "probe": probe,

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     DKV_HOST_NONCOHERENT,
     DecodeBuffers,
     HostBuffer,
+    StepGraph,
     KVCache,
     alloc_decode_buffers,
     attn_trace,

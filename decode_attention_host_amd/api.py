@@ -80,6 +80,7 @@ class HostBuffer:
             self.dev_ptr = None
 
     def __del__(self):
+        # hipHostFree waits for the device before releasing pinned memory
         try:
             if self.host_ptr:
                 lib().dkv_host_free(C.c_void_p(self.host_ptr))
@@ -118,8 +119,14 @@ class KVCache:
             self.set_page_table(page_table)
 
     def set_page_table(self, page_table):
+        """Replace the page table (host copy and device copy).  Work already
+        queued may still read the old device table, so the current stream is
+        synchronized before the old one is released."""
         pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
-        assert pt.ndim == 2
+        if pt.ndim != 2:
+            raise ValueError("page_table must be [batch][max_pages]")
+        if self.page_table is not None:
+            torch.cuda.current_stream().synchronize()
         self.page_table_host = pt
         self.max_pages = int(pt.shape[1])
         self.page_table = torch.from_numpy(pt).to("cuda")
@@ -322,3 +329,30 @@ def attn_trace(buffer: torch.Tensor | None):
     else:
         assert buffer.dtype == torch.int64 and buffer.is_cuda and buffer.dim() == 2 and buffer.shape[1] == 4
         check(lib().dkv_attn_trace(_ptr(buffer), int(buffer.shape[0])))
+
+
+class StepGraph:
+    """A decode step (any sequence of binding calls on the current stream)
+    captured once into a HIP graph and replayed.
+
+    ``fn`` is run ``warmup`` times on a side stream first, which also builds
+    and caches every plan it needs outside the capture.  Replays reuse the
+    buffers ``fn`` wrote during capture; inputs are read from the same device
+    addresses on every replay.
+    """
+
+    def __init__(self, fn, warmup: int = 2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()

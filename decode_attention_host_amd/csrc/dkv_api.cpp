@@ -86,7 +86,15 @@ struct PlanEntry {
   dkv::PlanLayout lay;
   void* pinned = nullptr;  // immutable device image, source of every upload
   size_t bytes = 0;
+  bool captured = false;   // referenced by a captured graph: never evicted
 };
+
+// True while `s` is capturing a graph (its work is recorded, not run).
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st == hipStreamCaptureStatusActive;
+}
 
 struct PlanCache {
   std::mutex mu;
@@ -222,11 +230,15 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
     } else {
       c.lru.push_front(key);
       c.map.emplace(key, std::make_pair(e, c.lru.begin()));
-      while (c.map.size() > PlanCache::kCap) {
-        const std::string& victim = c.lru.back();
-        evicted.push_back(c.map[victim].first);
-        c.map.erase(victim);
-        c.lru.pop_back();
+      // evict least recently used entries that no captured graph refers to
+      auto lit = c.lru.end();
+      while (c.map.size() > PlanCache::kCap && lit != c.lru.begin()) {
+        --lit;
+        auto mit = c.map.find(*lit);
+        if (mit->second.first->captured) continue;
+        evicted.push_back(mit->second.first);
+        c.map.erase(mit);
+        lit = c.lru.erase(lit);
       }
     }
   }
@@ -287,6 +299,7 @@ struct TimedLaunch {
   hipStream_t stream;
   hipEvent_t e0 = nullptr;
   TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+    if (stream_capturing(s)) return;  // graphs replay without the event pair
     Timing& t = timing();
     std::lock_guard<std::mutex> lk(t.mu);
     if (!t.on) return;
@@ -461,6 +474,11 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
           return set_err(DKV_ERR_INVALID, "page_table and page_table_host differ at [%d][%lld]", b,
                          (long long)j);
     }
+  }
+  if (stream_capturing(s)) {
+    // the captured copy node reads this image on every replay
+    std::lock_guard<std::mutex> lk(cache().mu);
+    e->captured = true;
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
@@ -701,7 +719,10 @@ dkv_status dkv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** 
 
 dkv_status dkv_host_free(void* host_ptr) {
   if (!host_ptr) return ok();
-  hipError_t e = hipHostFree(host_ptr);
+  // kernels queued on any stream may still read the block
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize before hipHostFree");
+  e = hipHostFree(host_ptr);
   if (e != hipSuccess) return hip_err(e, "hipHostFree");
   return ok();
 }

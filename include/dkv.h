@@ -156,6 +156,11 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
  * arguments; part_o / part_lse must hold at least S splits (num_splits_cap)
  * and the workspace (device memory) at least workspace_bytes.  Plans are
  * cached per distinct shape inside the library.
+ *
+ * Graph capture: the call may be captured into a HIP graph (stream in
+ * capture mode).  Make one ordinary call with the same arguments first so the
+ * plan is built outside the capture; the plan image a captured graph copies
+ * from is then kept for the life of the process.
  * ---------------------------------------------------------------------- */
 typedef struct dkv_plan_info {
   int64_t workspace_bytes; /* device workspace the call needs */
@@ -214,7 +219,8 @@ dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32
  * into the GPU's address space; *host_ptr is the CPU address, *dev_ptr the
  * address kernels use.  flags: DKV_HOST_COHERENT (fine-grained, default) or
  * DKV_HOST_NONCOHERENT (coarse-grained; GPU caches may hold lines during a
- * kernel).  Free with dkv_host_free(host_ptr) after all GPU work using it.
+ * kernel).  dkv_host_free(host_ptr) waits for all queued work on the
+ * current device, then releases the block.
  * ---------------------------------------------------------------------- */
 #define DKV_HOST_COHERENT 0u
 #define DKV_HOST_NONCOHERENT 1u
