@@ -130,7 +130,7 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
   const bool mixed = host_tok > 0 && dev_tok > 0;
   const int32_t ch = choose_chunk(host_tok * in.hkv, wh, mixed ? 4 : 2, 256, 16384, align, in.host_chunk);
-  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 8, 1024, 1 << 16, align, in.dev_chunk);
+  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 6, 1024, 1 << 16, align, in.dev_chunk);
 
   // ---- items
   std::vector<PlanItem> hitems, ditems;

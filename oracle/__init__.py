@@ -27,5 +27,6 @@ from .dkv_oracle import (  # noqa: F401
     decode_sequence,
     decode_sequence_split,
     decode_batch,
+    prefill_sequence,
     append_expected_rows,
 )

@@ -82,3 +82,15 @@ def merge_py(parts):
                 o[h][d] += w * po[h][d] / tot
         lse[h] = M + math.log(tot)
     return o, lse
+
+
+def prefill_py(q_rot, k, v, pos, scale):
+    """Causal prefill: q_rot [n][Hq][D] already rotated, row j at position pos[j]
+    attends to tokens 0..pos[j] of k, v [N][Hkv][D]."""
+    n = len(q_rot)
+    outs, lses = [], []
+    for j in range(n):
+        o, l = attention_py(q_rot[j], k[:pos[j] + 1], v[:pos[j] + 1], scale)
+        outs.append(o)
+        lses.append(l)
+    return outs, lses

@@ -276,3 +276,48 @@ def append_expected_rows(k_new, v_new, pos, theta: float, k_is_bits: bool = True
         v_bits = bf16_rne_bits(v_new)
     kr = rope_neox(k, np.full(k.shape[0], pos), theta)
     return bf16_rne_bits(kr), v_bits
+
+
+# ---------------------------------------------------------------- prefill
+
+def prefill_sequence(q_bits, k_raw_bits, v_bits, q_pos0: int, theta: float, scale: float,
+                     heads=None, rounded_keys: bool = True, row_block: int = 256):
+    """Causal attention of n new query tokens over a sequence's cache.
+
+    DirectKV README, introduction (one kernel projects, rotates and attends)
+    and Step 6 ("Prefill (all new KV)" cases).  Query row j sits at position
+    p_j = q_pos0 + j, is rotated there, and attends to cached tokens
+    0 .. p_j (its own key included).  q_bits [n, Hq, D]; k_raw_bits / v_bits
+    [N, Hkv, D] with N >= q_pos0 + n (keys before RoPE, rotated at their own
+    positions and stored as bf16 when ``rounded_keys``).
+    Returns o [n, len(heads), D], lse [n, len(heads)].
+    """
+    q = bf16_to_f64(q_bits)
+    n, Hq, D = q.shape
+    N, Hkv = k_raw_bits.shape[0], k_raw_bits.shape[1]
+    g = Hq // Hkv
+    heads = list(range(Hq)) if heads is None else list(heads)
+    assert q_pos0 + n <= N, "every query position must be in the cache"
+    pos = q_pos0 + np.arange(n)
+    q_rot = rope_neox(q, np.repeat(pos[:, None], Hq, axis=1), theta)
+    o = np.zeros((n, len(heads), D))
+    lse = np.zeros((n, len(heads)))
+    by_kv = {}
+    for j, h in enumerate(heads):
+        by_kv.setdefault(h // g, []).append((j, h))
+    last = q_pos0 + n
+    for kvh, hs in by_kv.items():
+        kk = _stored_keys(k_raw_bits[:last, kvh:kvh + 1, :], theta, rounded_keys)[:, 0, :]
+        vv = bf16_to_f64(v_bits[:last, kvh, :])
+        for r0 in range(0, n, row_block):
+            r1 = min(n, r0 + row_block)
+            for j, h in hs:
+                s = scale * (q_rot[r0:r1, h, :] @ kk.T)          # [rows, last]
+                mask = np.arange(last)[None, :] > pos[r0:r1, None]
+                s = np.where(mask, -np.inf, s)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                z = e.sum(axis=1, keepdims=True)
+                o[r0:r1, j, :] = (e / z) @ vv
+                lse[r0:r1, j] = (m + np.log(z))[:, 0]
+    return o, lse

@@ -384,3 +384,43 @@ def test_append_expected_rows():
     kv = O.project(x, w)[0].reshape(2, 8)
     k2, v2 = O.append_expected_rows(kv, kv, 0, 1e4, k_is_bits=False)
     assert np.array_equal(k2, O.bf16_rne_bits(kv)) and np.array_equal(v2, O.bf16_rne_bits(kv))
+
+
+# ------------------------------------------------------------------ prefill
+
+def test_prefill_single_row_equals_decode():
+    N, Hq, Hkv, D, th = 50, 8, 2, 16, 1e4
+    q, k, v = _tiny_inputs(31, N, Hq, Hkv, D)
+    o_d, l_d = O.decode_sequence(q, k, v, N - 1, th, 0.25)
+    o_p, l_p = O.prefill_sequence(q[None], k, v, N - 1, th, 0.25)
+    np.testing.assert_allclose(o_p[0], o_d, atol=1e-13)
+    np.testing.assert_allclose(l_p[0], l_d, atol=1e-13)
+
+
+def test_prefill_all_new_first_row_is_v0_and_rows_are_causal():
+    # all new KV (q_pos0 = 0): row 0 sees only token 0; changing later tokens
+    # leaves earlier rows unchanged
+    n, Hq, Hkv, D, th = 12, 4, 2, 8, 1e4
+    q = normal_bf16(32, 1, (n, Hq, D)); k = normal_bf16(32, 2, (n, Hkv, D)); v = normal_bf16(32, 3, (n, Hkv, D))
+    o, lse = O.prefill_sequence(q, k, v, 0, th, 0.35)
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], O.bf16_to_f64(v[0, h // 2]))
+    k2 = k.copy(); v2 = v.copy()
+    k2[7:] = normal_bf16(33, 2, (n - 7, Hkv, D)); v2[7:] = normal_bf16(33, 3, (n - 7, Hkv, D))
+    o2, l2 = O.prefill_sequence(q, k2, v2, 0, th, 0.35)
+    np.testing.assert_array_equal(o2[:7], o[:7])
+    assert np.abs(o2[7:] - o[7:]).max() > 1e-3
+
+
+def test_prefill_matches_scalar_twin_with_cached_prefix():
+    N0, n, Hq, Hkv, D, th = 5, 4, 4, 2, 8, 1e4
+    N = N0 + n
+    q = normal_bf16(34, 1, (n, Hq, D)); k = normal_bf16(34, 2, (N, Hkv, D)); v = normal_bf16(34, 3, (N, Hkv, D))
+    o, lse = O.prefill_sequence(q, k, v, N0, th, 0.3)
+    kf = O.bf16_to_f64(k); qf = O.bf16_to_f64(q)
+    kr = [[list(O.bf16_to_f64(O.bf16_rne_bits(np.array(BR.rope_neox_py(list(kf[t, j]), t, th)))))
+           for j in range(Hkv)] for t in range(N)]
+    qr = [[BR.rope_neox_py(list(qf[j, h]), N0 + j, th) for h in range(Hq)] for j in range(n)]
+    ob, lb = BR.prefill_py(qr, kr, O.bf16_to_f64(v).tolist(), [N0 + j for j in range(n)], 0.3)
+    np.testing.assert_allclose(o, ob, atol=1e-12)
+    np.testing.assert_allclose(lse, lb, atol=1e-12)
