@@ -403,6 +403,65 @@ def measure_long_sweep(dk, cfg, seed, flags, iters, bw_h, bw_d):
     return {"sweep": out, "best_split": best_split(out, bw_h, bw_d)}
 
 
+def measure_prefill(dk, cfg, seed, flags, steps, warmup):
+    """Causal prefill of new tokens: bulk append (RoPE + store into the tier),
+    prefill attention, merge.  Reported per offload ratio in cfg["ratios"]."""
+    import numpy as np
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    from synth import kv_raw, normal_bf16
+
+    hq, hkv, d, lens, news = cfg["hq"], cfg["hkv"], cfg["d"], cfg["lens"], cfg["new"]
+    B = cfg["batch"]
+    ks, vs = kv_raw(seed, lens, hkv, d)
+    q = torch.from_numpy(np.concatenate([normal_bf16(seed + b, 1, (n, hq, d)) for b, n in enumerate(news)])
+                         .view(np.int16)).cuda()
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    T = int(q_start[-1])
+    k_new = torch.from_numpy(np.concatenate([k[L - n:] for k, L, n in zip(ks, lens, news)]).view(np.int16)).cuda()
+    v_new = torch.from_numpy(np.concatenate([v[L - n:] for v, L, n in zip(vs, lens, news)]).view(np.int16)).cuda()
+    sidx = torch.from_numpy(np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(news)])).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(L - n, L, dtype=np.int32) for L, n in zip(lens, news)])).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    flops = 0
+    for L, n, p0 in zip(lens, news, q_pos0):
+        flops += 4 * hq * d * sum(p0 + j + 1 for j in range(n))
+    out = []
+    for r in cfg.get("ratios", [cfg["ratio"]]):
+        cache = contiguous_cache(hkv, d, lens, r, ks, vs, cfg["theta"], host_flags=flags)
+        bufs = dk.alloc_prefill_buffers(cache, B, hq, q_start, q_pos0, lens, r)
+        scale = 1.0 / math.sqrt(d)
+
+        def step():
+            dk.project_rope_append(cache, B, sl, r, sidx, pos, k_new=k_new, v_new=v_new,
+                                   rope_theta=cfg["theta"])
+            dk.prefill_attn_split(cache, q, q_start, q_pos0, lens, r, scale, cfg["theta"], bufs=bufs)
+            dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, T, hq, d, out_o=bufs.out_o,
+                         out_lse=bufs.out_lse)
+
+        gpu_warm(step)
+        dk.kernel_timing(True)
+        for k in dk.api.KERNELS:
+            dk.kernel_timing_read(k)
+        ms, _ = timed_loop(step, steps, warmup)
+        kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
+        dk.kernel_timing(False)
+        pf_ms = kt["prefill"][1] / max(1, kt["prefill"][0])
+        info = bufs.info
+        reads = info["host_bytes"] + info["dev_bytes"]
+        out.append({"ratio": r, "new_tokens": T, "ms_per_step": round(ms, 4),
+                    "prefill_kernel_ms": round(pf_ms, 4),
+                    "useful_tflops": round(flops / (pf_ms * 1e9), 2),
+                    "frac_bf16_mfma_peak": round(flops / (pf_ms * 1e9) / 2500.0, 4),
+                    "kv_reads_host_bytes": info["host_bytes"], "kv_reads_hbm_bytes": info["dev_bytes"],
+                    "kv_read_gbs": round(reads / (pf_ms * 1e6), 1),
+                    "kernel_ms": {k: round(v[1] / max(1, v[0]), 5) for k, v in kt.items()},
+                    "plan": {k: info[k] for k in ("num_splits", "host_wgs", "dev_wgs", "host_chunk", "dev_chunk")}})
+        cache.free()
+    return {"flops_per_step": flops, "per_ratio": out}
+
+
 def load_traffic(workload_name):
     p = os.path.join(ROOT, "profiles", f"attn_{workload_name}_traffic.json")
     if not os.path.exists(p):
@@ -427,7 +486,7 @@ def main():
     ap.add_argument("--sweep-iters", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--tune", default="", help="comma list of dkv_tuning fields, e.g. host_wgs=256")
-    ap.add_argument("--extra", default="tiny,opt_6_7b_b8,fused_ragged,llama3_8b_1m",
+    ap.add_argument("--extra", default="tiny,opt_6_7b_b8,fused_ragged,llama3_8b_1m,llama3_8b_prefill_2k",
                     help="other workloads measured after the headline ('' for none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: headline steps plus two calibration reads of known "
@@ -535,7 +594,9 @@ def main():
     for name in [x for x in args.extra.split(",") if x]:
         wcfg = workload(name, seed=args.seed)
         t0 = time.time()
-        if name == "llama3_8b_1m":
+        if "new" in wcfg:
+            workloads[name] = measure_prefill(dk, wcfg, args.seed, flags, 10, 3)
+        elif name == "llama3_8b_1m":
             bw_h = probe.get("host_zero_copy_gbs") or 50.0
             bw_d = probe.get("hbm_read_gbs") or 5000.0
             workloads[name] = measure_long_sweep(dk, wcfg, args.seed, flags, 10, bw_h, bw_d)
@@ -546,7 +607,7 @@ def main():
             ww["cache"].free()
             workloads[name] = res
         log(f"[bench] {name} measured in {time.time() - t0:.1f}s: "
-            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'graph_ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn', 'best_split')})}")
+            f"{json.dumps({k: v for k, v in workloads[name].items() if k in ('ms_per_step', 'graph_ms_per_step', 'eff_kv_gbs', 'attn_kv_gbs', 'frac_nominal_attn', 'best_split', 'per_ratio')})}")
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     StepGraph,
     KVCache,
     alloc_decode_buffers,
+    alloc_prefill_buffers,
     attn_trace,
     append_workspace_bytes,
     decode,
@@ -22,6 +23,9 @@ from .api import (  # noqa: F401
     kernel_timing_read,
     merge_lse,
     plan_inspect,
+    prefill,
+    prefill_attn_split,
+    prefill_plan,
     probe_read,
     project_rope_append,
     reset_tuning,

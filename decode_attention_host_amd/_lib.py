@@ -113,12 +113,16 @@ SIGNATURES = {
     "dkv_kernel_timing": (I32, [I32]),
     "dkv_kernel_timing_read": (I32, [I32, C.POINTER(I32), C.POINTER(F64)]),
     "dkv_attn_trace": (I32, [P, I32]),
+    "dkv_prefill_plan": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, C.POINTER(PlanInfo)]),
+    "dkv_prefill_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, P, F64, F32, F64, P, SZ, P, P,
+                                     P, I32, P]),
 }
 
 DKV_KERNEL_ATTN = 0
 DKV_KERNEL_ROPE_Q = 1
 DKV_KERNEL_MERGE = 2
 DKV_KERNEL_APPEND = 3
+DKV_KERNEL_PREFILL = 4
 
 _lib = None
 

@@ -7,6 +7,7 @@ path runs in libdkv's kernels.  Names follow the C functions:
   decode_plan          -> dkv_decode_plan
   decode_attn_split    -> dkv_decode_attn_split
   merge_lse            -> dkv_merge_lse
+  prefill_plan / prefill_attn_split -> dkv_prefill_plan / dkv_prefill_attn_split
   host_alloc / HostBuffer -> dkv_host_alloc / dkv_host_free
 """
 from __future__ import annotations
@@ -305,7 +306,8 @@ def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True
 
 
 KERNELS = {"attn": _lib.DKV_KERNEL_ATTN, "rope_q": _lib.DKV_KERNEL_ROPE_Q,
-           "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND}
+           "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND,
+           "prefill": _lib.DKV_KERNEL_PREFILL}
 
 
 def kernel_timing(enable: bool):
@@ -356,3 +358,61 @@ class StepGraph:
 
     def replay(self):
         self.graph.replay()
+
+
+def prefill_plan(cache: KVCache, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens,
+                 ratio: float) -> dict:
+    """dkv_prefill_plan (host int32 arrays)."""
+    d = cache.desc()
+    qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
+    info = PlanInfo()
+    check(lib().dkv_prefill_plan(C.byref(d), int(batch), int(num_q_heads), _ptr(qs), _ptr(qp), _ptr(sl),
+                                 float(ratio), C.byref(info)))
+    return info.as_dict()
+
+
+def alloc_prefill_buffers(cache: KVCache, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens,
+                          ratio: float, device="cuda") -> DecodeBuffers:
+    info = prefill_plan(cache, batch, num_q_heads, q_start, q_pos0, seq_lens, ratio)
+    T = int(np.asarray(q_start)[-1])
+    S = max(1, info["num_splits"])
+    D = cache.head_dim
+    return DecodeBuffers(
+        workspace=torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=device),
+        part_o=torch.empty((S, num_q_heads, D), dtype=torch.float32, device=device),
+        part_lse=torch.empty((S, num_q_heads), dtype=torch.float32, device=device),
+        split_offsets=torch.empty(T + 1, dtype=torch.int32, device=device),
+        out_o=torch.empty((max(T, 1), num_q_heads, D), dtype=torch.float32, device=device),
+        out_lse=torch.empty((max(T, 1), num_q_heads), dtype=torch.float32, device=device),
+        info=info,
+    )
+
+
+def prefill_attn_split(cache: KVCache, q: torch.Tensor, q_start, q_pos0, seq_lens, ratio: float,
+                       scale: float, rope_theta: float, *, bufs: DecodeBuffers | None = None,
+                       stream=None) -> DecodeBuffers:
+    """dkv_prefill_attn_split.  q [T,Hq,D] bf16 on the device; q_start [B+1],
+    q_pos0 [B], seq_lens [B] on the host."""
+    T, Hq, D = q.shape
+    qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
+    B = len(sl)
+    if bufs is None:
+        bufs = alloc_prefill_buffers(cache, B, Hq, qs, qp, sl, ratio, q.device)
+    d = cache.desc()
+    check(lib().dkv_prefill_attn_split(
+        C.byref(d), int(B), int(Hq), _ptr(q), _ptr(qs), _ptr(qp), _ptr(sl), float(ratio), float(scale),
+        float(rope_theta), _ptr(bufs.workspace), bufs.workspace.numel(), _ptr(bufs.part_o),
+        _ptr(bufs.part_lse), _ptr(bufs.split_offsets), int(bufs.part_o.shape[0]), _stream(stream)))
+    return bufs
+
+
+def prefill(cache: KVCache, q, q_start, q_pos0, seq_lens, ratio, scale, rope_theta, *, bufs=None,
+            stream=None):
+    """prefill_attn_split followed by merge_lse over the T query rows."""
+    T, Hq, D = q.shape
+    bufs = prefill_attn_split(cache, q, q_start, q_pos0, seq_lens, ratio, scale, rope_theta, bufs=bufs,
+                              stream=stream)
+    if T > 0:
+        merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, T, Hq, D, out_o=bufs.out_o,
+                  out_lse=bufs.out_lse, stream=stream)
+    return bufs.out_o[:T], bufs.out_lse[:T], bufs

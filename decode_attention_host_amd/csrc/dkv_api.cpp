@@ -156,6 +156,9 @@ dkv_status validate_ratio(double r) {
   return DKV_OK;
 }
 
+std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e);
+std::shared_ptr<PlanEntry> cache_find(const std::string& key);
+
 // Builds or fetches the plan for a decode call.
 dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int32_t* seq_lens,
                     double ratio, std::shared_ptr<PlanEntry>* out) {
@@ -193,15 +196,9 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
     }
     put(key, h);
   }
-  PlanCache& c = cache();
-  {
-    std::lock_guard<std::mutex> lk(c.mu);
-    auto it = c.map.find(key);
-    if (it != c.map.end()) {
-      c.lru.splice(c.lru.begin(), c.lru, it->second.second);
-      *out = it->second.first;
-      return DKV_OK;
-    }
+  if (auto hit = cache_find(key)) {
+    *out = hit;
+    return DKV_OK;
   }
   dkv::PlanInput in{};
   in.batch = batch; in.hq = hq; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
@@ -220,17 +217,26 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
   hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
   if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
   memcpy(e->pinned, blob.data(), e->bytes);
+  *out = cache_insert(key, e);
+  return DKV_OK;
+}
+
+size_t qrot_bytes(int32_t batch, int32_t hq, int32_t d) { return (size_t)batch * hq * d * 4; }
+
+// Stores a freshly built plan in the cache (or returns the entry another
+// thread stored first) and evicts unreferenced old entries.
+std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e) {
+  PlanCache& c = cache();
   std::vector<std::shared_ptr<PlanEntry>> evicted;
   {
     std::lock_guard<std::mutex> lk(c.mu);
     auto it = c.map.find(key);
-    if (it != c.map.end()) {  // another thread raced us: keep theirs
+    if (it != c.map.end()) {
       evicted.push_back(e);
       e = it->second.first;
     } else {
       c.lru.push_front(key);
       c.map.emplace(key, std::make_pair(e, c.lru.begin()));
-      // evict least recently used entries that no captured graph refers to
       auto lit = c.lru.end();
       while (c.map.size() > PlanCache::kCap && lit != c.lru.begin()) {
         --lit;
@@ -243,7 +249,6 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
     }
   }
   if (!evicted.empty()) {
-    // Evicted images may still feed queued uploads: wait for the device first.
     (void)hipDeviceSynchronize();
     for (auto& v : evicted)
       if (v.use_count() == 1 && v->pinned) {
@@ -251,11 +256,95 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
         v->pinned = nullptr;
       }
   }
-  *out = e;
+  return e;
+}
+
+std::shared_ptr<PlanEntry> cache_find(const std::string& key) {
+  PlanCache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  auto it = c.map.find(key);
+  if (it == c.map.end()) return nullptr;
+  c.lru.splice(c.lru.begin(), c.lru, it->second.second);
+  return it->second.first;
+}
+
+// Builds or fetches the plan of a prefill call.
+dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int32_t* q_start,
+                            const int32_t* q_pos0, const int32_t* seq_lens, double ratio,
+                            std::shared_ptr<PlanEntry>* out) {
+  if (batch < 1) return set_err(DKV_ERR_INVALID, "batch must be >= 1");
+  if (!seq_lens || !q_start || !q_pos0) return set_err(DKV_ERR_INVALID, "seq_lens, q_start and q_pos0 are required");
+  if (hq < 1 || hq % kv->num_kv_heads)
+    return set_err(DKV_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d", hq,
+                   kv->num_kv_heads);
+  const int g = hq / kv->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return set_err(DKV_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", g);
+  if (kv->page_size > 0 && !kv->page_table_host)
+    return set_err(DKV_ERR_INVALID, "paged layout needs page_table_host to plan");
+  uint64_t gen = 0;
+  const dkv_tuning t = tuning_snapshot(&gen);
+  int dev = 0;
+  int cus = t.num_cus;
+  if (cus <= 0) {
+    cus = device_cus(&dev);
+    if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
+  }
+  std::string key("prefill");
+  put(key, dev); put(key, cus); put(key, gen); put(key, batch); put(key, hq);
+  put(key, kv->num_kv_heads); put(key, kv->head_dim); put(key, kv->page_size); put(key, kv->max_pages);
+  put(key, kv->host_stride); put(key, kv->dev_stride); put(key, kv->host_rows); put(key, kv->dev_rows);
+  put(key, ratio);
+  key.append(reinterpret_cast<const char*>(seq_lens), sizeof(int32_t) * (size_t)batch);
+  key.append(reinterpret_cast<const char*>(q_start), sizeof(int32_t) * (size_t)(batch + 1));
+  key.append(reinterpret_cast<const char*>(q_pos0), sizeof(int32_t) * (size_t)batch);
+  if (kv->page_size > 0) {
+    uint64_t h = 1469598103934665603ull;
+    for (int b = 0; b < batch; ++b) {
+      const int64_t L = std::max(0, seq_lens[b]);
+      const int64_t npg = std::min<int64_t>((L + kv->page_size - 1) / kv->page_size, kv->max_pages);
+      h = fnv1a(kv->page_table_host + (int64_t)b * kv->max_pages, sizeof(int32_t) * npg, h);
+    }
+    put(key, h);
+  }
+  if (auto hit = cache_find(key)) {
+    *out = hit;
+    return DKV_OK;
+  }
+  dkv::PlanInput in{};
+  in.batch = batch; in.hq = hq; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
+  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
+  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
+  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
+  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host; in.ratio = ratio;
+  in.num_cus = cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  auto e = std::make_shared<PlanEntry>();
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_prefill_plan(in, q_start, q_pos0, &e->lay, &blob, &err))
+    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  e->bytes = blob.size();
+  hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
+  if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
+  memcpy(e->pinned, blob.data(), e->bytes);
+  *out = cache_insert(key, e);
   return DKV_OK;
 }
 
-size_t qrot_bytes(int32_t batch, int32_t hq, int32_t d) { return (size_t)batch * hq * d * 4; }
+void fill_info(const dkv::PlanLayout& L, size_t ws, dkv_plan_info* info) {
+  info->workspace_bytes = (int64_t)ws;
+  info->num_splits = L.num_splits;
+  info->host_items = L.n_host_items;
+  info->dev_items = L.n_dev_items;
+  info->host_wgs = L.host_wgs;
+  info->dev_wgs = L.dev_wgs;
+  info->host_chunk = L.host_chunk;
+  info->dev_chunk = L.dev_chunk;
+  info->host_bytes = L.host_bytes;
+  info->dev_bytes = L.dev_bytes;
+}
 
 // f_i = theta^(-2i/D) in IEEE double, the exponent formed as (-2 i) / D.
 dkv::RopeFreq rope_freq(double theta, int d) {
@@ -274,7 +363,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> pool;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[4];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[5];
 };
 
 Timing& timing() {
@@ -785,8 +874,8 @@ dkv_status dkv_kernel_timing(int32_t enable) {
 }
 
 dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms) {
-  if (kernel < 0 || kernel > 3 || !count || !total_ms)
-    return set_err(DKV_ERR_INVALID, "kernel id in [0,3] and outputs required");
+  if (kernel < 0 || kernel > 4 || !count || !total_ms)
+    return set_err(DKV_ERR_INVALID, "kernel id in [0,4] and outputs required");
   Timing& t = timing();
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;
   {
@@ -820,6 +909,95 @@ dkv_status dkv_attn_trace(void* dev_buffer, int32_t capacity_wgs) {
   std::lock_guard<std::mutex> lk(g_trace_mu);
   g_trace_buf = capacity_wgs > 0 ? static_cast<uint64_t*>(dev_buffer) : nullptr;
   g_trace_cap = capacity_wgs;
+  return ok();
+}
+
+dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                            const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                            double offload_ratio, dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  std::shared_ptr<PlanEntry> e;
+  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
+                        kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (st != DKV_OK) return st;
+  fill_info(e->lay, e->lay.blob_bytes + qrot_bytes(e->lay.n_rows, num_q_heads, kv->head_dim), info);
+  return ok();
+}
+
+dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                  const void* q, const int32_t* q_start, const int32_t* q_pos0,
+                                  const int32_t* seq_lens, double offload_ratio, float scale,
+                                  double rope_theta, void* workspace, size_t workspace_bytes,
+                                  float* part_o, float* part_lse, int32_t* split_offsets,
+                                  int32_t num_splits_cap, void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (!q || !part_o || !part_lse || !split_offsets || !workspace)
+    return set_err(DKV_ERR_INVALID, "q, part_o, part_lse, split_offsets and workspace are required");
+  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  std::shared_ptr<PlanEntry> e;
+  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
+                        kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  if (L.n_rows == 0) return ok();  // no query rows
+  const size_t need = L.blob_bytes + qrot_bytes(L.n_rows, num_q_heads, kv->head_dim);
+  if (workspace_bytes < need)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (num_splits_cap < L.num_splits)
+    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %d splits", num_splits_cap, L.num_splits);
+  hipStream_t s = (hipStream_t)stream;
+  if (stream_capturing(s)) {
+    std::lock_guard<std::mutex> lk(cache().mu);
+    e->captured = true;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_err(he, "plan upload");
+  float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
+  he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q),
+                                      reinterpret_cast<const int32_t*>(ws + L.rowpos_off), q_rot,
+                                      L.n_rows, num_q_heads, kv->head_dim,
+                                      rope_freq(rope_theta, kv->head_dim), scale_log2,
+                                      reinterpret_cast<const int32_t*>(ws + L.offsets_off),
+                                      split_offsets, stream);
+  t_rope.done();
+  if (he != hipSuccess) return hip_err(he, "rope_q launch");
+  dkv::PrefillArgs a{};
+  a.host_items = reinterpret_cast<const dkv::PrefillItem*>(ws + L.items_off);
+  a.dev_items = a.host_items + L.n_host_items;
+  a.plist = reinterpret_cast<const int32_t*>(ws + L.plist_off);
+  a.unit_counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
+  a.n_host_units = L.n_host_items * kv->num_kv_heads;
+  a.n_dev_units = L.n_dev_items * kv->num_kv_heads;
+  a.host_wgs = L.host_wgs;
+  a.dev_wgs = L.dev_wgs;
+  a.host_k = static_cast<const uint16_t*>(kv->host_k);
+  a.host_v = static_cast<const uint16_t*>(kv->host_v);
+  a.dev_k = static_cast<const uint16_t*>(kv->dev_k);
+  a.dev_v = static_cast<const uint16_t*>(kv->dev_v);
+  a.host_rows = kv->host_rows;
+  a.dev_rows = kv->dev_rows;
+  a.page_table = kv->page_size > 0 ? kv->page_table : nullptr;
+  a.max_pages = kv->max_pages;
+  a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : 0;
+  a.hq = num_q_heads;
+  a.hkv = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  TimedLaunch t_attn(DKV_KERNEL_PREFILL, s);
+  he = (hipError_t)dkv::launch_prefill(a, q_rot, stream);
+  t_attn.done();
+  if (he != hipSuccess) return hip_err(he, "prefill launch");
   return ok();
 }
 

@@ -33,6 +33,25 @@ struct PlanItem {
 };
 static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
 
+// Prefill work item: a block of consecutive query rows of one sequence (QB =
+// 64/G rows, all G heads of one KV head per unit) against a run of cached
+// tokens that lie in one tier.  The partial of block row r for this item is
+// split slot base + r * n_splits + split_idx.
+struct PrefillItem {
+  int32_t b;          // sequence
+  int32_t row0;       // global query row of the block's first row
+  int32_t n_rows;     // rows in the block (<= QB)
+  int32_t pos0;       // position of the block's first row
+  int32_t n_tok;      // tokens in the item
+  int32_t plist;      // paged: index of the first page in the page list
+  int32_t tok0;       // contiguous: logical position of the item's first token
+  int32_t split_idx;  // index of this item among its block's splits
+  int32_t n_splits;   // splits of the block
+  int32_t base;       // first split slot of the block
+  int64_t row_pool;   // contiguous: pool row of the item's first token
+};
+static_assert(sizeof(PrefillItem) == 48, "PrefillItem layout");
+
 // Host-side result of planning; the device image is `blob` (items, then the
 // page list, then split offsets), uploaded into the caller's workspace.
 struct PlanLayout {
@@ -52,6 +71,10 @@ struct PlanLayout {
   size_t counters_off = 0;       // two int32 counters, zero in the image
   size_t blob_bytes = 0;
   int32_t n_plist = 0;
+  size_t rowpos_off = 0;         // prefill: position of every query row [T]
+  int32_t n_rows = 0;            // prefill: T (query rows)
+  int64_t host_reads = 0;        // prefill: K+V bytes read from each tier,
+  int64_t dev_reads = 0;         //   counting re-reads by later row blocks
 };
 
 // Arguments of the split attention kernel.
@@ -143,12 +166,40 @@ struct ProjArgs {
   int32_t kslice;        // hidden / ksplit
 };
 
+// Arguments of the prefill kernel.
+struct PrefillArgs {
+  const PrefillItem* host_items;
+  const PrefillItem* dev_items;
+  const int32_t* plist;
+  int32_t* unit_counters;        // [2], zero at launch
+  int32_t n_host_units;
+  int32_t n_dev_units;
+  int32_t host_wgs;
+  int32_t dev_wgs;
+  const uint16_t* host_k;
+  const uint16_t* host_v;
+  const uint16_t* dev_k;
+  const uint16_t* dev_v;
+  int64_t host_rows;
+  int64_t dev_rows;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t page_shift;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t pad;
+  float* part_o;                 // [S][Hq][D]
+  float* part_lse;               // [S][Hq]
+};
+
 // Launchers (dkv_kernels.hip).  They return hipError_t as int.
 int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
                   const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream);
 int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
+int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_project(const ProjArgs& a, void* stream);
 int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
@@ -181,5 +232,12 @@ struct PlanInput {
 // Builds the plan and its device image; on failure returns false with `err`.
 bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
                 std::string* err);
+
+// Prefill plan: query rows of sequence b are q_start[b] .. q_start[b+1]-1,
+// row j of b at position q_pos0[b] + j; in.seq_lens are the cached lengths.
+// Device image: host items, dev items, page list, row positions [T], split
+// offsets [T+1], counters.
+bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
+                        PlanLayout* out, std::vector<uint8_t>* blob, std::string* err);
 
 }  // namespace dkv

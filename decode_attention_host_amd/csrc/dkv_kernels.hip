@@ -84,15 +84,18 @@ __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ plan_offsets,
                                                           int32_t* __restrict__ split_offsets,
                                                           int batch) {
-  const int b = blockIdx.y;
   const int half = d >> 1;
-  if (b == 0 && blockIdx.x == 0 && split_offsets)
+  if (blockIdx.x == 0 && split_offsets)
     for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
-  const double pos = (double)q_pos[b];
-  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < hq * half; idx += gridDim.x * blockDim.x) {
-    const int h = idx / half, i = idx - h * half;
+  const int64_t per_row = (int64_t)hq * half;
+  const int64_t total = (int64_t)batch * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(idx / per_row);
+    const int rem = (int)(idx - (int64_t)b * per_row);
+    const int h = rem / half, i = rem - h * half;
     double s, c;
-    sincos(pos * freq.f[i], &s, &c);
+    sincos((double)q_pos[b] * freq.f[i], &s, &c);
     const uint16_t* qh = q + ((size_t)b * hq + h) * d;
     const double xl = (double)bf16_to_f32(qh[i]);
     const double xh = (double)bf16_to_f32(qh[i + half]);
@@ -382,6 +385,283 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
     t[1] = wall_clock64();
     t[2] = host_role ? 1 : 0;
     t[3] = (uint64_t)units_done;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: causal attention of blocks of new query rows over the cache.
+//
+// A unit = (row block of QB = 64/G query rows of one sequence, run of cached
+// tokens in one tier, KV head); its 64 MFMA rows are the (head, row) pairs of
+// the group, 16 per wave.  Both contractions are dense here and run on
+// v_mfma_f32_16x16x32_bf16:
+//   S = Q.K^T   A = query rows (fp32 split into high/low bf16), B = K rows
+//   O += P.V    A = probabilities (high/low bf16 from LDS), B = V transposed
+//               into LDS while the tile is staged
+// Causal mask: token t is visible to a row at position p iff t <= p.
+// ---------------------------------------------------------------------------
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void prefill_split_kernel(PrefillArgs a,
+                                                                 const float* __restrict__ q_rot) {
+  constexpr int QB = 64 / G;
+  constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
+  constexpr int DT = D / 16;                   // 16-wide output-dim tiles of P.V
+  constexpr int KPITCH = D * 2 + 16;           // bytes per K row in LDS
+  constexpr int VT_PITCH = kTile + 8;          // bf16 per transposed V row
+  constexpr int P_PITCH = kTile + 8;           // bf16 per probability row
+  constexpr int CPR = D / 8;                   // 16-byte chunks per KV row
+  constexpr int NCK = kTile * CPR / kThreads;  // K chunks per thread
+  constexpr int NPV = kTile * CPR / 2 / kThreads;  // V row pairs per thread
+  static_assert(NPV >= 1, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t p_hi[4][16 * P_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lo[4][16 * P_PITCH];
+  __shared__ int tpos_lds[kTile];
+  __shared__ int s_next;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int j4 = lane >> 4;
+
+  const bool host_role = (int)blockIdx.x < a.host_wgs;
+  const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
+  const int nwg = host_role ? a.host_wgs : a.dev_wgs;
+  const int nunits = host_role ? a.n_host_units : a.n_dev_units;
+  const PrefillItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
+  const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
+  const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
+  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
+  int* counter = a.unit_counters + (host_role ? 1 : 0);
+
+  // pool row and logical position of token `tok` of an item (-1: not valid)
+  auto locate = [&](const PrefillItem& it, int tok, int64_t& row) -> int {
+    if (tok >= it.n_tok) return -1;
+    if (PAGED) {
+      const int lp = a.plist[it.plist + (tok >> a.page_shift)];
+      const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
+      const int off = tok & ((1 << a.page_shift) - 1);
+      row = ((int64_t)(e >> 1) << a.page_shift) | off;
+      if (e < 0 || ((e & 1) != 0) != host_role || row >= cap_rows) return -1;
+      return (lp << a.page_shift) + off;
+    }
+    row = it.row_pool + tok;
+    return it.tok0 + tok;
+  };
+
+  u32x4 kreg[NCK], vreg[NPV][2];
+  int treg = -1;
+  auto load_tile = [&](const PrefillItem& it, int kvh, int tile) {
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int r = chunk / CPR, col = chunk - (chunk / CPR) * CPR;
+      int64_t row = 0;
+      const bool ok = locate(it, tile * kTile + r, row) >= 0;
+      kreg[c] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                         kpool + (row * a.hkv + kvh) * D + col * 8))
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < NPV; ++q) {
+      const int pr = tid + q * kThreads;
+      const int rp = pr / CPR, col = pr - (pr / CPR) * CPR;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        int64_t row = 0;
+        const bool ok = locate(it, tile * kTile + 2 * rp + e, row) >= 0;
+        vreg[q][e] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                              vpool + (row * a.hkv + kvh) * D + col * 8))
+                        : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < kTile) {
+      int64_t row = 0;
+      treg = locate(it, tile * kTile + tid, row);
+    }
+  };
+
+  int u = wg;
+  PrefillItem it{};
+  int kvh = 0;
+  if (u < nunits) {
+    it = items[u / a.hkv];
+    kvh = u - (u / a.hkv) * a.hkv;
+    load_tile(it, kvh, 0);
+  }
+  while (u < nunits) {
+    const int ntiles = (it.n_tok + kTile - 1) / kTile;
+    // ---- query operand (A of S = Q.K^T): MFMA row n of this wave
+    bf16x8_t qa_hi[KS], qa_lo[KS];
+    {
+      const int rowi = wave * 16 + n;
+      const int h = rowi / QB, r = rowi - (rowi / QB) * QB;
+      const bool active = r < it.n_rows;
+      const float* qr = q_rot + ((size_t)(it.row0 + (active ? r : 0)) * a.hq + kvh * G + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d0 = ks * 32 + j4 * 8 + 2 * e;
+          const float x0 = active ? qr[d0] : 0.f, x1 = active ? qr[d0 + 1] : 0.f;
+          const uint32_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+          wh[e] = h0 | (h1 << 16);
+          wl[e] = f32_to_bf16(x0 - bf16_to_f32(h0)) | (f32_to_bf16(x1 - bf16_to_f32(h1)) << 16);
+        }
+        qa_hi[ks] = __builtin_bit_cast(bf16x8_t, (u32x4{wh[0], wh[1], wh[2], wh[3]}));
+        qa_lo[ks] = __builtin_bit_cast(bf16x8_t, (u32x4{wl[0], wl[1], wl[2], wl[3]}));
+      }
+    }
+    // C-layout rows of this lane: 4*j4 + i of the wave's 16
+    int rpos[4];
+    bool rvalid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rowi = wave * 16 + j4 * 4 + i;
+      const int r = rowi - (rowi / QB) * QB;
+      rvalid[i] = r < it.n_rows;
+      rpos[i] = it.pos0 + r;
+    }
+    float m_run[4], l_run[4];
+    floatx4 oacc[DT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    int next_u = nunits;
+    PrefillItem nit{};
+    int nkvh = 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+      __syncthreads();  // previous tile's readers are done
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int r = chunk / CPR, col = chunk - (chunk / CPR) * CPR;
+        *reinterpret_cast<u32x4*>(k_lds + r * KPITCH + col * 16) = kreg[c];
+      }
+#pragma unroll
+      for (int q = 0; q < NPV; ++q) {
+        const int pr = tid + q * kThreads;
+        const int rp = pr / CPR, col = pr - (pr / CPR) * CPR;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (vreg[q][0][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+          const uint32_t hi = (vreg[q][1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+          *reinterpret_cast<uint32_t*>(&vt_lds[(col * 8 + e) * VT_PITCH + 2 * rp]) = lo | (hi << 16);
+        }
+      }
+      if (tid < kTile) tpos_lds[tid] = treg;
+      const bool last = tile + 1 == ntiles;
+      if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
+      __syncthreads();
+      if (!last) {
+        load_tile(it, kvh, tile + 1);
+      } else {
+        next_u = s_next;
+        if (next_u < nunits) {
+          nit = items[next_u / a.hkv];
+          nkvh = next_u - (next_u / a.hkv) * a.hkv;
+          load_tile(nit, nkvh, 0);
+        }
+      }
+
+      // ---- S = Q.K^T for 16 rows x 64 tokens (four 16-token column tiles)
+      floatx4 sc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        sc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* krow = k_lds + (nt * 16 + n) * KPITCH + j4 * 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(krow + ks * 64));
+          sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[ks], kb, sc[nt], 0, 0, 0);
+          sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[ks], kb, sc[nt], 0, 0, 0);
+        }
+      }
+      // ---- causal mask and online softmax per row (row = 4*j4 + i)
+      int tp[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) tp[nt] = tpos_lds[nt * 16 + n];
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const bool vis = rvalid[i] && tp[nt] >= 0 && tp[nt] <= rpos[i];
+          sc[nt][i] = vis ? sc[nt][i] : -INFINITY;
+          mx = fmaxf(mx, sc[nt][i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        const float m_new = fmaxf(m_run[i], mx);
+        alpha[i] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[i] - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float pv = (sc[nt][i] == -INFINITY) ? 0.f : exp2f(sc[nt][i] - m_new);
+          ps += pv;
+          const uint32_t ph = f32_to_bf16(pv);
+          const int o = (j4 * 4 + i) * P_PITCH + nt * 16 + n;
+          p_hi[wave][o] = (uint16_t)ph;
+          p_lo[wave][o] = (uint16_t)f32_to_bf16(pv - bf16_to_f32(ph));
+        }
+        ps += __shfl_xor(ps, 1);
+        ps += __shfl_xor(ps, 2);
+        ps += __shfl_xor(ps, 4);
+        ps += __shfl_xor(ps, 8);
+        l_run[i] = l_run[i] * alpha[i] + ps;
+        m_run[i] = m_new;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- O += P.V: A = P rows (from LDS), B = V^T rows (from LDS)
+#pragma unroll
+      for (int kt = 0; kt < kTile / 32; ++kt) {
+        const int ko = kt * 32 + j4 * 8;
+        const bf16x8_t pa_hi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&p_hi[wave][n * P_PITCH + ko]));
+        const bf16x8_t pa_lo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&p_lo[wave][n * P_PITCH + ko]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&vt_lds[(dt * 16 + n) * VT_PITCH + ko]));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, oacc[dt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- write this unit's partial for every valid row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!rvalid[i]) continue;
+      const int rowi = wave * 16 + j4 * 4 + i;
+      const int h = rowi / QB, r = rowi - (rowi / QB) * QB;
+      const size_t slot = (size_t)it.base + (size_t)r * it.n_splits + it.split_idx;
+      const size_t head = slot * a.hq + kvh * G + h;
+      const bool empty = m_run[i] == -INFINITY;
+      const float inv = empty ? 0.f : 1.f / l_run[i];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.part_o[head * D + dt * 16 + n] = oacc[dt][i] * inv;
+      if (n == 0)
+        a.part_lse[head] = empty ? -INFINITY : (m_run[i] + log2f(l_run[i])) * 0.69314718055994530942f;
+    }
+    u = next_u;
+    it = nit;
+    kvh = nkvh;
   }
 }
 
@@ -713,8 +993,9 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
                   const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int bx = (hq * (d / 2) + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(rope_q_kernel, dim3(bx, batch), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
+  const int64_t total = (int64_t)batch * hq * (d / 2);
+  const int bx = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
+  hipLaunchKernelGGL(rope_q_kernel, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
                      scale_log2, plan_offsets, split_offsets, batch);
   return (int)hipGetLastError();
 }
@@ -724,6 +1005,35 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
   if (a.host_wgs + a.dev_wgs <= 0) return (int)hipSuccess;
   if (a.head_dim == 64) return (int)launch_attn_d<64>(a, q_rot, s);
   if (a.head_dim == 128) return (int)launch_attn_d<128>(a, q_rot, s);
+  return (int)hipErrorInvalidValue;
+}
+
+template <int D, int G>
+static hipError_t launch_prefill_dg(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
+  const int grid = a.host_wgs + a.dev_wgs;
+  if (a.page_table)
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+  else
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: return launch_prefill_dg<D, 1>(a, q_rot, s);
+    case 2: return launch_prefill_dg<D, 2>(a, q_rot, s);
+    case 4: return launch_prefill_dg<D, 4>(a, q_rot, s);
+    case 8: return launch_prefill_dg<D, 8>(a, q_rot, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.host_wgs + a.dev_wgs <= 0) return (int)hipSuccess;
+  if (a.head_dim == 64) return (int)launch_prefill_d<64>(a, q_rot, s);
+  if (a.head_dim == 128) return (int)launch_prefill_d<128>(a, q_rot, s);
   return (int)hipErrorInvalidValue;
 }
 

@@ -208,3 +208,199 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
 }
 
 }  // namespace dkv
+
+namespace dkv {
+
+// ---------------------------------------------------------------- prefill
+//
+// DirectKV README, Step 6 ("Prefill (all new KV)"): new tokens attend
+// causally to the cache.  A block of QB = 64/G consecutive query rows of one
+// sequence shares one stream of its KV prefix [0, last row's position]; that
+// prefix is cut by tier and into chunks, one work item per (block, chunk).
+bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
+                        PlanLayout* out, std::vector<uint8_t>* blob, std::string* err) {
+  *out = PlanLayout{};
+  const int B = in.batch;
+  if (B < 1) return fail(err, "batch must be >= 1 (got %lld)", B);
+  if (!in.seq_lens || !q_start || !q_pos0) return fail(err, "seq_lens, q_start and q_pos0 are required");
+  if (in.hkv < 1 || in.hq % in.hkv) return fail(err, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = in.hq / in.hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(err, "query group size %lld not built", G);
+  const int QB = 64 / G;
+  const bool paged = in.page_size > 0;
+  const int64_t P = paged ? in.page_size : 1;
+  const int64_t row_bytes = (int64_t)in.hkv * in.head_dim * 2;
+  if (q_start[0] != 0) return fail(err, "q_start[0] must be 0");
+
+  // ---- per-sequence placement (validated exactly as for decode)
+  std::vector<int64_t> nh(B, 0);
+  std::vector<std::vector<int32_t>> host_pages(paged ? B : 0), dev_pages(paged ? B : 0);
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = in.seq_lens[b];
+    const int64_t n = (int64_t)q_start[b + 1] - q_start[b];
+    if (n < 0) return fail(err, "q_start must be non-decreasing (sequence %lld)", b);
+    if (L < 1) return fail(err, "seq_lens[%lld] must be >= 1", b);
+    if (q_pos0[b] < 0 || (int64_t)q_pos0[b] + n > L)
+      return fail(err, "sequence %lld: query rows at positions %lld.. exceed the %lld cached tokens", b,
+                  q_pos0[b], L);
+    if (!paged) {
+      const int64_t h = (int64_t)std::floor(in.ratio * (double)L);
+      nh[b] = h;
+      if (h > 0 && (h > in.host_stride || (int64_t)b * in.host_stride + h > in.host_rows))
+        return fail(err, "sequence %lld: host rows needed beyond host_stride/host_rows", b);
+      if (L - h > 0 && (L - h > in.dev_stride || (int64_t)b * in.dev_stride + (L - h) > in.dev_rows))
+        return fail(err, "sequence %lld: device rows needed beyond dev_stride/dev_rows", b);
+    } else {
+      if (!in.page_table_host) return fail(err, "paged layout needs page_table_host");
+      const int64_t npg = ceil_div(L, P);
+      if (npg > in.max_pages) return fail(err, "sequence %lld needs %lld pages > max_pages", b, npg);
+      for (int64_t j = 0; j < npg; ++j) {
+        const int32_t e = in.page_table_host[(int64_t)b * in.max_pages + j];
+        if (e < 0) return fail(err, "page_table[%lld][%lld] is negative", b, j);
+        const bool host = (e & 1) != 0;
+        if (((int64_t)(e >> 1) + 1) * P > (host ? in.host_rows : in.dev_rows))
+          return fail(err, "page_table[%lld][%lld]: page beyond its tier's pool", b, j);
+        (host ? host_pages[b] : dev_pages[b]).push_back((int32_t)j);
+      }
+    }
+  }
+
+  // ---- row blocks and the tokens each reads per tier
+  struct Blk { int b, row0, n_rows, pos0; int64_t end; };
+  std::vector<Blk> blocks;
+  int64_t host_reads = 0, dev_reads = 0;
+  auto tier_tokens = [&](int b, int64_t E, bool host) -> int64_t {
+    if (!paged) return host ? std::min<int64_t>(nh[b], E) : std::max<int64_t>(0, E - nh[b]);
+    int64_t t = 0;
+    for (int32_t j : (host ? host_pages[b] : dev_pages[b])) {
+      if ((int64_t)j * P >= E) break;
+      t += std::min<int64_t>(P, E - (int64_t)j * P);
+    }
+    return t;
+  };
+  for (int b = 0; b < B; ++b) {
+    const int n = q_start[b + 1] - q_start[b];
+    for (int r0 = 0; r0 < n; r0 += QB) {
+      Blk k{b, q_start[b] + r0, std::min(QB, n - r0), q_pos0[b] + r0, 0};
+      k.end = (int64_t)k.pos0 + k.n_rows;  // tokens [0, end) are visible to some row
+      host_reads += tier_tokens(b, k.end, true);
+      dev_reads += tier_tokens(b, k.end, false);
+      blocks.push_back(k);
+    }
+  }
+
+  // ---- workgroup split (same rules as decode) and chunk sizes
+  const int32_t cus = std::max(1, in.num_cus);
+  const int32_t resident = cus * kSlotsPerCu;
+  const double bw_h = in.host_bw > 0 ? in.host_bw : 57.0;
+  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5300.0;
+  int32_t wh = 0, wd = 0;
+  if (host_reads > 0 && dev_reads > 0) {
+    const bool host_dominant = (double)host_reads / bw_h > 1.5 * (double)dev_reads / bw_d;
+    const int32_t want_h = in.host_wgs > 0 ? in.host_wgs : (host_dominant ? std::max(8, cus * 3 / 16) : std::max(4, cus / 16));
+    wh = std::min(std::max(want_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d))), resident / 2);
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
+  } else if (host_reads > 0) {
+    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 4);
+  } else {
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
+  }
+  const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
+  const int32_t ch = choose_chunk(host_reads * in.hkv, wh, 4, 256, 16384, align, in.host_chunk);
+  const int32_t cd = choose_chunk(dev_reads * in.hkv, wd, 6, 512, 1 << 16, align, in.dev_chunk);
+
+  // ---- items, split slots, row offsets and positions
+  const int64_t T = q_start[B];
+  std::vector<PrefillItem> hitems, ditems;
+  std::vector<int32_t> plist, rowpos(T), offsets(T + 1, 0);
+  int64_t slot = 0;
+  for (const Blk& k : blocks) {
+    std::vector<PrefillItem> items;
+    std::vector<bool> is_host;
+    for (int tier = 1; tier >= 0; --tier) {
+      const int64_t chunk = tier ? ch : cd;
+      if (!paged) {
+        const int64_t t0 = tier ? 0 : nh[k.b];
+        const int64_t t1 = tier ? std::min<int64_t>(nh[k.b], k.end) : k.end;
+        for (int64_t t = t0; t < t1; t += chunk) {
+          PrefillItem it{};
+          it.n_tok = (int32_t)std::min<int64_t>(chunk, t1 - t);
+          it.tok0 = (int32_t)t;
+          it.row_pool = tier ? (int64_t)k.b * in.host_stride + t : (int64_t)k.b * in.dev_stride + (t - nh[k.b]);
+          items.push_back(it);
+          is_host.push_back(tier == 1);
+        }
+      } else {
+        const std::vector<int32_t>& pages = tier ? host_pages[k.b] : dev_pages[k.b];
+        size_t npg = 0;
+        while (npg < pages.size() && (int64_t)pages[npg] * P < k.end) ++npg;
+        const size_t per = (size_t)(chunk / P);
+        for (size_t p0 = 0; p0 < npg; p0 += per) {
+          const size_t p1 = std::min(npg, p0 + per);
+          PrefillItem it{};
+          int64_t nt = 0;
+          for (size_t q = p0; q < p1; ++q) nt += std::min<int64_t>(P, k.end - (int64_t)pages[q] * P);
+          it.n_tok = (int32_t)nt;
+          it.plist = (int32_t)plist.size();
+          for (size_t q = p0; q < p1; ++q) plist.push_back(pages[q]);
+          items.push_back(it);
+          is_host.push_back(tier == 1);
+        }
+      }
+    }
+    const int32_t S_k = (int32_t)items.size();
+    for (int32_t s = 0; s < S_k; ++s) {
+      PrefillItem& it = items[s];
+      it.b = k.b;
+      it.row0 = k.row0;
+      it.n_rows = k.n_rows;
+      it.pos0 = k.pos0;
+      it.split_idx = s;
+      it.n_splits = S_k;
+      it.base = (int32_t)slot;
+      (is_host[s] ? hitems : ditems).push_back(it);
+    }
+    for (int r = 0; r < k.n_rows; ++r) {
+      offsets[k.row0 + r] = (int32_t)(slot + (int64_t)r * S_k);
+      rowpos[k.row0 + r] = k.pos0 + r;
+    }
+    slot += (int64_t)k.n_rows * S_k;
+    if (slot > INT32_MAX) return fail(err, "too many prefill splits");
+  }
+  offsets[T] = (int32_t)slot;
+  if ((int64_t)(hitems.size() + ditems.size()) * in.hkv > INT32_MAX) return fail(err, "too many work units");
+
+  out->n_host_items = (int32_t)hitems.size();
+  out->n_dev_items = (int32_t)ditems.size();
+  out->num_splits = (int32_t)slot;
+  out->batch = B;
+  out->n_rows = (int32_t)T;
+  out->host_wgs = hitems.empty() ? 0 : (int32_t)std::min<int64_t>(wh, (int64_t)hitems.size() * in.hkv);
+  out->dev_wgs = ditems.empty() ? 0 : (int32_t)std::min<int64_t>(wd, (int64_t)ditems.size() * in.hkv);
+  out->host_chunk = hitems.empty() ? 0 : ch;
+  out->dev_chunk = ditems.empty() ? 0 : cd;
+  out->host_reads = host_reads * row_bytes * 2;
+  out->dev_reads = dev_reads * row_bytes * 2;
+  out->host_bytes = out->host_reads;
+  out->dev_bytes = out->dev_reads;
+  out->n_plist = (int32_t)plist.size();
+  out->items_off = 0;
+  out->plist_off = (hitems.size() + ditems.size()) * sizeof(PrefillItem);
+  out->rowpos_off = round_up(out->plist_off + plist.size() * sizeof(int32_t), 16);
+  out->offsets_off = round_up(out->rowpos_off + T * sizeof(int32_t), 16);
+  out->counters_off = round_up(out->offsets_off + (T + 1) * sizeof(int32_t), 16);
+  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
+  if (blob) {
+    blob->assign(out->blob_bytes, 0);
+    uint8_t* p = blob->data();
+    if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(PrefillItem));
+    if (!ditems.empty())
+      memcpy(p + hitems.size() * sizeof(PrefillItem), ditems.data(), ditems.size() * sizeof(PrefillItem));
+    if (!plist.empty()) memcpy(p + out->plist_off, plist.data(), plist.size() * sizeof(int32_t));
+    if (T) memcpy(p + out->rowpos_off, rowpos.data(), T * sizeof(int32_t));
+    memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
+  }
+  return true;
+}
+
+}  // namespace dkv

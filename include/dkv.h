@@ -199,6 +199,39 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
                             int32_t page_cap, int32_t* split_offsets, dkv_plan_info* info);
 
 /* ------------------------------------------------------------------------
+ * Causal prefill attention over the split cache (DirectKV README,
+ * introduction: one kernel projects, rotates and attends; Step 6:
+ * "Prefill (all new KV)" correctness cases).
+ *
+ * New query rows are grouped per sequence: rows q_start[b] .. q_start[b+1]-1
+ * (host int32 [batch+1], q_start[0] = 0) belong to sequence b, and row j of b
+ * sits at position q_pos0[b] + j (host int32 [batch]).  Their keys and
+ * values must already be in the cache (dkv_project_rope_append with the
+ * same positions); seq_lens (host int32 [batch]) are the cached lengths and
+ * must cover every query position.  Each row is rotated by Neox RoPE at its
+ * position and attends to tokens 0 .. its position (causal):
+ *   s_t = scale * q_rot . k_t (t <= p),  o = softmax(s) V,  lse = ln sum e^s.
+ * q is [T][Hq][D] bf16 (device), T = q_start[batch].
+ *
+ * Output is split like dkv_decode_attn_split: the rows of a block of 64/G
+ * consecutive rows share runs of cached tokens, one per tier and chunk;
+ * each (row, run) writes a normalised partial, and split_offsets (device
+ * int32 [T+1]) gives each row's CSR range of splits.  dkv_merge_lse with
+ * batch = T then yields o [T][Hq][D] and lse [T][Hq].  dkv_prefill_plan gives
+ * the split count and workspace size.  Q.K^T and P.V run on MFMA.
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                            const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                            double offload_ratio, dkv_plan_info* info);
+
+dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                  const void* q, const int32_t* q_start, const int32_t* q_pos0,
+                                  const int32_t* seq_lens, double offload_ratio, float scale,
+                                  double rope_theta, void* workspace, size_t workspace_bytes,
+                                  float* part_o, float* part_lse, int32_t* split_offsets,
+                                  int32_t num_splits_cap, void* stream);
+
+/* ------------------------------------------------------------------------
  * LSE merge of partial results (the combine step implied by splitting one
  * sequence's KV over tiers and compute units: SplitKernel README, Key
  * Features; DirectKV README, Step 6, "SM-Parallel" kernel).
@@ -272,12 +305,14 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
  * kernel runs on.  dkv_kernel_timing_read waits for the recorded events,
  * returns how many launches were timed and their summed duration in ms, and
  * clears the record.  kernel: DKV_KERNEL_ATTN (split attention),
- * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND.
+ * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
+ * DKV_KERNEL_PREFILL (causal prefill attention).
  * ---------------------------------------------------------------------- */
 #define DKV_KERNEL_ATTN 0
 #define DKV_KERNEL_ROPE_Q 1
 #define DKV_KERNEL_MERGE 2
 #define DKV_KERNEL_APPEND 3
+#define DKV_KERNEL_PREFILL 4
 
 dkv_status dkv_kernel_timing(int32_t enable);
 

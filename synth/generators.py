@@ -155,6 +155,8 @@ CONFIGS = {
     "llama3_8b_1m": dict(batch=1, hq=32, hkv=8, d=128, lens=[1 << 20], ratio=1.0,
                          theta=5e5, layout="contig",
                          ratios=[0.0, 0.25, 0.5, 0.75, 0.9, 1.0]),
+    "llama3_8b_prefill_2k": dict(batch=1, hq=32, hkv=8, d=128, lens=[2048], new=[2048], ratio=1.0,
+                                 theta=5e5, layout="contig", ratios=[1.0, 0.0]),
     "fused_ragged": dict(batch=16, hq=32, hkv=8, d=128, lens_range=(1024, 65536),
                          ratio=0.8, theta=5e5, layout="paged", page=16, hidden=4096,
                          w_std=0.02),

@@ -1,0 +1,113 @@
+"""GPU parity of causal prefill over the split cache against the fp64 oracle.
+
+The new rows' keys and values are appended first (same positions); then each
+row attends causally to the cache.  Bar: max |do|, |dlse| <= 2e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import kv_raw, normal_bf16, paged_table, query
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def dk():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import decode_attention_host_amd as dk
+    dk.reset_tuning()
+    return dk
+
+
+def _prefill(dk, cache, qs, q_start, q_pos0, lens, ratio, theta, d):
+    import torch
+    q = torch.from_numpy(np.concatenate(qs, axis=0).view(np.int16)).cuda()
+    o, lse, bufs = dk.prefill(cache, q, q_start, q_pos0, lens, ratio, 1.0 / math.sqrt(d), theta)
+    torch.cuda.synchronize()
+    return o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), bufs
+
+
+def _check(o, lse, ro, rl, what):
+    eo, el = np.abs(o - ro).max(), np.abs(lse - rl).max()
+    print(f"{what}: max|do|={eo:.3g} max|dlse|={el:.3g}", flush=True)
+    assert eo <= TOL and el <= TOL, what
+
+
+CASES = [
+    # (lens, new rows per seq, hq, hkv, d, ratio, theta)
+    ([64], [64], 4, 2, 64, 1.0, 1e4),                  # all new KV, host tier
+    ([377], [77], 32, 8, 128, 0.5, 5e5),               # cached prefix split over both tiers
+    ([200, 33, 1000], [200, 1, 130], 8, 8, 128, 0.3, 1e4),  # MHA, ragged, an all-new sequence
+    ([300], [40], 16, 2, 64, 0.0, 1e4),                # g = 8, HBM only
+    ([130, 65], [65, 64], 8, 4, 128, 1.0, 5e5),        # g = 2, host only
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_prefill_contiguous(dk, case):
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, news, hq, hkv, d, r, th = CASES[case]
+    ks, vs = kv_raw(70 + case, lens, hkv, d)
+    qs = [normal_bf16(70 + case, 1, (n, hq, d)) for n in news]
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    o, lse, _ = _prefill(dk, cache, qs, q_start, q_pos0, lens, r, th, d)
+    for b in range(len(lens)):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], q_pos0[b], th, 1 / math.sqrt(d))
+        _check(o[q_start[b]:q_start[b + 1]], lse[q_start[b]:q_start[b + 1]], ro, rl, f"case {case} seq {b}")
+    cache.free()
+
+
+def test_prefill_paged_ragged(dk):
+    from decode_attention_host_amd.cache_build import paged_cache
+    lens, news, hq, hkv, d, th = [500, 17, 1200], [100, 17, 333], 32, 8, 128, 5e5
+    ks, vs = kv_raw(80, lens, hkv, d)
+    qs = [normal_bf16(80 + b, 1, (n, hq, d)) for b, n in enumerate(news)]
+    pt, nh, nd = paged_table(80, lens, 16, 0.8)
+    cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, th)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    o, lse, _ = _prefill(dk, cache, qs, q_start, q_pos0, lens, 0.0, th, d)
+    for b in range(3):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], q_pos0[b], th, 1 / math.sqrt(d))
+        _check(o[q_start[b]:q_start[b + 1]], lse[q_start[b]:q_start[b + 1]], ro, rl, f"paged seq {b}")
+    cache.free()
+
+
+def test_prefill_single_row_equals_decode(dk):
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, hq, hkv, d, r, th = [999], 32, 8, 128, 0.5, 5e5
+    ks, vs = kv_raw(81, lens, hkv, d)
+    qb = query(81, 1, hq, d)
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    o_p, l_p, _ = _prefill(dk, cache, [qb], np.array([0, 1], dtype=np.int32), [lens[0] - 1], lens, r, th, d)
+    q = torch.from_numpy(qb.view(np.int16)).cuda()
+    qpos = torch.tensor([lens[0] - 1], dtype=torch.int32, device="cuda")
+    o_d, l_d, _ = dk.decode(cache, q, qpos, lens, r, 1 / math.sqrt(d), th)
+    assert np.abs(o_p - o_d.cpu().numpy()).max() < 1e-5
+    assert np.abs(l_p - l_d.cpu().numpy()).max() < 1e-5
+    cache.free()
+
+
+def test_prefill_rows_deep_in_a_long_cache(dk):
+    # 48 rows at positions ~70000 over a 70048-token cache split host/HBM
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, n, hq, hkv, d, r, th = [70048], 48, 32, 8, 128, 0.6, 5e5
+    ks, vs = kv_raw(83, lens, hkv, d)
+    qb = normal_bf16(83, 1, (n, hq, d))
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    q_pos0 = lens[0] - n
+    o, lse, _ = _prefill(dk, cache, [qb], np.array([0, n], dtype=np.int32), [q_pos0], lens, r, th, d)
+    heads = [0, 5, 18, 31]
+    ro, rl = O.prefill_sequence(qb, ks[0], vs[0], q_pos0, th, 1 / math.sqrt(d), heads=heads)
+    _check(o[:, heads], lse[:, heads], ro, rl, "deep rows")
+    cache.free()
