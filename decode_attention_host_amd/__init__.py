@@ -26,6 +26,7 @@ from .api import (  # noqa: F401
     prefill,
     prefill_attn_split,
     prefill_plan,
+    prefill_plan_inspect,
     probe_read,
     project_rope_append,
     reset_tuning,

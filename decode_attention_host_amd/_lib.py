@@ -59,6 +59,7 @@ class PlanInfo(C.Structure):
         ("dev_chunk", C.c_int32),
         ("host_bytes", C.c_int64),
         ("dev_bytes", C.c_int64),
+        ("staged_bytes", C.c_int64),
     ]
 
     def as_dict(self):
@@ -72,7 +73,7 @@ class Tuning(C.Structure):
         ("dev_wgs", C.c_int32),
         ("host_chunk", C.c_int32),
         ("dev_chunk", C.c_int32),
-        ("reserved", C.c_int32),
+        ("stage_max_mib", C.c_int32),
         ("host_bw_gbs", C.c_double),
         ("dev_bw_gbs", C.c_double),
     ]
@@ -102,6 +103,8 @@ SIGNATURES = {
     "dkv_decode_plan": (I32, [C.POINTER(KvDesc), I32, I32, P, F64, C.POINTER(PlanInfo)]),
     "dkv_plan_inspect": (I32, [C.POINTER(KvDesc), I32, I32, P, F64, I32, P, I32, P, I32, P,
                                C.POINTER(PlanInfo)]),
+    "dkv_prefill_plan_inspect": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, I32, P, I32, P, I32, P, I32,
+                                       P, I32, C.POINTER(PlanInfo)]),
     "dkv_decode_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, F32, F64, P, SZ, P, P,
                                     P, I32, P]),
     "dkv_merge_lse": (I32, [P, P, P, I32, I32, I32, P, P, P]),
@@ -123,6 +126,7 @@ DKV_KERNEL_ROPE_Q = 1
 DKV_KERNEL_MERGE = 2
 DKV_KERNEL_APPEND = 3
 DKV_KERNEL_PREFILL = 4
+DKV_KERNEL_STAGE = 5
 
 _lib = None
 

@@ -212,6 +212,30 @@ def plan_inspect(cache_or_desc, batch: int, num_q_heads: int, seq_lens, ratio: f
     return items[:n], plist, offs, info.as_dict()
 
 
+def prefill_plan_inspect(cache_or_desc, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens,
+                         ratio: float, num_cus: int):
+    """dkv_prefill_plan_inspect: dict of items [n][11] int64, page pairs [m][2],
+    staging tiles [k][3] int64, split_offsets [T+1] and the plan info."""
+    d = cache_or_desc.desc() if isinstance(cache_or_desc, KVCache) else cache_or_desc
+    qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
+    info = PlanInfo()
+    args = (C.byref(d), int(batch), int(num_q_heads), _ptr(qs), _ptr(qp), _ptr(sl), float(ratio), int(num_cus))
+    check(lib().dkv_prefill_plan_inspect(*args, None, 0, None, 0, None, 0, None, 0, C.byref(info)))
+    n = info.host_items + info.dev_items
+    T = int(qs[-1])
+    items = np.zeros((max(n, 1), 11), dtype=np.int64)
+    # page pairs: at most (pages of the sequence) per item of a block
+    npg = 2 * (n * (int(max(sl)) // max(1, d.page_size) + 2) if d.page_size else 1)
+    pages = np.zeros(max(npg, 2), dtype=np.int32)
+    ntile = int(sum(int(x) for x in sl)) + len(sl)
+    tiles = np.zeros((max(ntile, 1), 3), dtype=np.int64)
+    offs = np.zeros(T + 1, dtype=np.int32)
+    check(lib().dkv_prefill_plan_inspect(*args, _ptr(items), n, _ptr(pages), len(pages), _ptr(tiles), ntile,
+                                         _ptr(offs), T + 1, C.byref(info)))
+    return {"items": items[:n], "pages": pages, "tiles": tiles[tiles[:, 2] > 0], "split_offsets": offs,
+            "info": info.as_dict()}
+
+
 @dataclass
 class DecodeBuffers:
     workspace: torch.Tensor
@@ -307,7 +331,7 @@ def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True
 
 KERNELS = {"attn": _lib.DKV_KERNEL_ATTN, "rope_q": _lib.DKV_KERNEL_ROPE_Q,
            "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND,
-           "prefill": _lib.DKV_KERNEL_PREFILL}
+           "prefill": _lib.DKV_KERNEL_PREFILL, "stage": _lib.DKV_KERNEL_STAGE}
 
 
 def kernel_timing(enable: bool):

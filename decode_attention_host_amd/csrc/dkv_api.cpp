@@ -320,6 +320,7 @@ dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, co
   in.num_cus = cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
   in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
   in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  in.stage_max_bytes = t.stage_max_mib < 0 ? 0 : (int64_t)(t.stage_max_mib == 0 ? 4096 : t.stage_max_mib) << 20;
   auto e = std::make_shared<PlanEntry>();
   std::vector<uint8_t> blob;
   std::string err;
@@ -333,6 +334,15 @@ dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, co
   return DKV_OK;
 }
 
+// Prefill workspace: plan image, rotated queries, then the HBM staging pool
+// (K rows, then V rows).
+size_t prefill_stage_off(const dkv::PlanLayout& L, int hq, int d) {
+  return (L.blob_bytes + qrot_bytes(L.n_rows, hq, d) + 255) / 256 * 256;
+}
+size_t prefill_ws_bytes(const dkv::PlanLayout& L, int hq, int hkv, int d) {
+  return prefill_stage_off(L, hq, d) + (size_t)L.stage_rows * hkv * d * 2 * 2;
+}
+
 void fill_info(const dkv::PlanLayout& L, size_t ws, dkv_plan_info* info) {
   info->workspace_bytes = (int64_t)ws;
   info->num_splits = L.num_splits;
@@ -344,6 +354,7 @@ void fill_info(const dkv::PlanLayout& L, size_t ws, dkv_plan_info* info) {
   info->dev_chunk = L.dev_chunk;
   info->host_bytes = L.host_bytes;
   info->dev_bytes = L.dev_bytes;
+  info->staged_bytes = L.staged_bytes;
 }
 
 // f_i = theta^(-2i/D) in IEEE double, the exponent formed as (-2 i) / D.
@@ -363,7 +374,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> pool;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[5];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[6];
 };
 
 Timing& timing() {
@@ -513,18 +524,60 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
   if (page_list)
     memcpy(page_list, blob.data() + L.plist_off, sizeof(int32_t) * std::min(L.n_plist, page_cap));
   if (split_offsets) memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * (batch + 1));
-  if (info) {
-    info->workspace_bytes = (int64_t)(L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim));
-    info->num_splits = L.num_splits;
-    info->host_items = L.n_host_items;
-    info->dev_items = L.n_dev_items;
-    info->host_wgs = L.host_wgs;
-    info->dev_wgs = L.dev_wgs;
-    info->host_chunk = L.host_chunk;
-    info->dev_chunk = L.dev_chunk;
-    info->host_bytes = L.host_bytes;
-    info->dev_bytes = L.dev_bytes;
+  if (info) fill_info(L, L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim), info);
+  return ok();
+}
+
+dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                    const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                                    double offload_ratio, int32_t num_cus, int64_t* items, int32_t items_cap,
+                                    int32_t* pages, int32_t pages_cap, int64_t* tiles, int32_t tiles_cap,
+                                    int32_t* split_offsets, int32_t offsets_cap, dkv_plan_info* info) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (num_cus < 1) return set_err(DKV_ERR_INVALID, "num_cus must be >= 1");
+  if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads)
+    return set_err(DKV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  const dkv_tuning t = tuning_snapshot(nullptr);
+  dkv::PlanInput in{};
+  in.batch = batch; in.hq = num_q_heads; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
+  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
+  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
+  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
+  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host;
+  in.ratio = kv->page_size == 0 ? offload_ratio : 0.0;
+  in.num_cus = num_cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  in.stage_max_bytes = t.stage_max_mib < 0 ? 0 : (int64_t)(t.stage_max_mib == 0 ? 4096 : t.stage_max_mib) << 20;
+  dkv::PlanLayout L;
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_prefill_plan(in, q_start, q_pos0, &L, &blob, &err))
+    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  const dkv::PrefillItem* it = reinterpret_cast<const dkv::PrefillItem*>(blob.data() + L.items_off);
+  const int n_items = L.n_host_items + L.n_dev_items;
+  if (items)
+    for (int i = 0; i < n_items && i < items_cap; ++i) {
+      int64_t* o = items + 11 * (size_t)i;
+      o[0] = it[i].pool; o[1] = it[i].b; o[2] = it[i].row0; o[3] = it[i].n_rows; o[4] = it[i].pos0;
+      o[5] = it[i].n_tok; o[6] = kv->page_size > 0 ? it[i].plist : it[i].row_pool; o[7] = it[i].tok0;
+      o[8] = it[i].split_idx; o[9] = it[i].n_splits; o[10] = it[i].base;
+    }
+  if (pages)
+    memcpy(pages, blob.data() + L.plist_off, sizeof(int32_t) * std::min(2 * L.n_plist, pages_cap));
+  if (tiles) {
+    const dkv::StageTile* tl = reinterpret_cast<const dkv::StageTile*>(blob.data() + L.stage_tiles_off);
+    for (int i = 0; i < L.n_stage_tiles && i < tiles_cap; ++i) {
+      tiles[3 * (size_t)i] = tl[i].src_row;
+      tiles[3 * (size_t)i + 1] = tl[i].dst_row;
+      tiles[3 * (size_t)i + 2] = tl[i].n_rows;
+    }
   }
+  if (split_offsets)
+    memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * std::min(L.n_rows + 1, offsets_cap));
+  if (info) fill_info(L, prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim), info);
   return ok();
 }
 
@@ -874,7 +927,7 @@ dkv_status dkv_kernel_timing(int32_t enable) {
 }
 
 dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms) {
-  if (kernel < 0 || kernel > 4 || !count || !total_ms)
+  if (kernel < 0 || kernel > DKV_KERNEL_STAGE || !count || !total_ms)
     return set_err(DKV_ERR_INVALID, "kernel id in [0,4] and outputs required");
   Timing& t = timing();
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;
@@ -923,7 +976,7 @@ dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
   st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
                         kv->page_size == 0 ? offload_ratio : 0.0, &e);
   if (st != DKV_OK) return st;
-  fill_info(e->lay, e->lay.blob_bytes + qrot_bytes(e->lay.n_rows, num_q_heads, kv->head_dim), info);
+  fill_info(e->lay, prefill_ws_bytes(e->lay, num_q_heads, kv->num_kv_heads, kv->head_dim), info);
   return ok();
 }
 
@@ -947,7 +1000,7 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   if (st != DKV_OK) return st;
   const dkv::PlanLayout& L = e->lay;
   if (L.n_rows == 0) return ok();  // no query rows
-  const size_t need = L.blob_bytes + qrot_bytes(L.n_rows, num_q_heads, kv->head_dim);
+  const size_t need = prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim);
   if (workspace_bytes < need)
     return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
   if (num_splits_cap < L.num_splits)
@@ -961,6 +1014,25 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
   if (he != hipSuccess) return hip_err(he, "plan upload");
   float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
+  const size_t pool_elems = (size_t)L.stage_rows * kv->num_kv_heads * kv->head_dim;
+  uint16_t* stage_k = reinterpret_cast<uint16_t*>(ws + prefill_stage_off(L, num_q_heads, kv->head_dim));
+  uint16_t* stage_v = stage_k + pool_elems;
+  if (L.n_stage_tiles > 0) {
+    dkv::StageArgs sa{};
+    sa.tiles = reinterpret_cast<const dkv::StageTile*>(ws + L.stage_tiles_off);
+    sa.n_tiles = L.n_stage_tiles;
+    sa.row_chunks = kv->num_kv_heads * kv->head_dim / 8;
+    sa.src_k = static_cast<const uint16_t*>(kv->host_k);
+    sa.src_v = static_cast<const uint16_t*>(kv->host_v);
+    sa.dst_k = stage_k;
+    sa.dst_v = stage_v;
+    int cus = tuning_snapshot(nullptr).num_cus;
+    if (cus <= 0) cus = device_cus(nullptr);
+    TimedLaunch t_stage(DKV_KERNEL_STAGE, s);
+    he = (hipError_t)dkv::launch_stage(sa, std::max(64, std::max(cus, 1) / 2), stream);
+    t_stage.done();
+    if (he != hipSuccess) return hip_err(he, "stage launch");
+  }
   const float scale_log2 = scale * 1.44269504088896340736f;
   TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
   he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q),
@@ -974,20 +1046,19 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   dkv::PrefillArgs a{};
   a.host_items = reinterpret_cast<const dkv::PrefillItem*>(ws + L.items_off);
   a.dev_items = a.host_items + L.n_host_items;
-  a.plist = reinterpret_cast<const int32_t*>(ws + L.plist_off);
+  a.pages = kv->page_size > 0 ? reinterpret_cast<const int32_t*>(ws + L.plist_off) : nullptr;
   a.unit_counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
-  a.n_host_units = L.n_host_items * kv->num_kv_heads;
-  a.n_dev_units = L.n_dev_items * kv->num_kv_heads;
+  a.n_host_items = L.n_host_items;
+  a.n_dev_items = L.n_dev_items;
   a.host_wgs = L.host_wgs;
   a.dev_wgs = L.dev_wgs;
+  a.dev_queues = L.dev_queues;
   a.host_k = static_cast<const uint16_t*>(kv->host_k);
   a.host_v = static_cast<const uint16_t*>(kv->host_v);
   a.dev_k = static_cast<const uint16_t*>(kv->dev_k);
   a.dev_v = static_cast<const uint16_t*>(kv->dev_v);
-  a.host_rows = kv->host_rows;
-  a.dev_rows = kv->dev_rows;
-  a.page_table = kv->page_size > 0 ? kv->page_table : nullptr;
-  a.max_pages = kv->max_pages;
+  a.stage_k = stage_k;
+  a.stage_v = stage_v;
   a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : 0;
   a.hq = num_q_heads;
   a.hkv = kv->num_kv_heads;

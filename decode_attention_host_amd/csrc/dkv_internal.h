@@ -33,24 +33,45 @@ struct PlanItem {
 };
 static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
 
-// Prefill work item: a block of consecutive query rows of one sequence (QB =
-// 64/G rows, all G heads of one KV head per unit) against a run of cached
-// tokens that lie in one tier.  The partial of block row r for this item is
-// split slot base + r * n_splits + split_idx.
+// Query-head rows per prefill workgroup: 4 waves x 32 rows (two 16-column
+// MFMA tiles each).  A row block holds kPrefillRows / G query rows.
+constexpr int kPrefillRows = 128;
+
+// Where a prefill item's tokens are read from.
+enum PrefillPool : int32_t { kPoolHost = 0, kPoolDev = 1, kPoolStaged = 2 };
+
+// Prefill work item: a block of consecutive query rows of one sequence (all G
+// heads of one KV head per unit) against a run of cached tokens that lie in
+// one pool.  The partial of block row r for this item is split slot
+// base + r * n_splits + split_idx.
 struct PrefillItem {
   int32_t b;          // sequence
   int32_t row0;       // global query row of the block's first row
-  int32_t n_rows;     // rows in the block (<= QB)
+  int32_t n_rows;     // rows in the block (<= kPrefillRows / G)
   int32_t pos0;       // position of the block's first row
   int32_t n_tok;      // tokens in the item
-  int32_t plist;      // paged: index of the first page in the page list
+  int32_t plist;      // paged: first (logical page, pool page) pair of the item
   int32_t tok0;       // contiguous: logical position of the item's first token
   int32_t split_idx;  // index of this item among its block's splits
   int32_t n_splits;   // splits of the block
   int32_t base;       // first split slot of the block
+  int32_t pool;       // PrefillPool
+  int32_t pad;
   int64_t row_pool;   // contiguous: pool row of the item's first token
+  int64_t pad2;
 };
-static_assert(sizeof(PrefillItem) == 48, "PrefillItem layout");
+static_assert(sizeof(PrefillItem) == 64, "PrefillItem layout");
+
+// One copy of host-tier rows into the HBM staging pool (prefill re-reads
+// them once per row block; staged, they cross the host link once).
+struct StageTile {
+  int64_t src_row;    // host pool row
+  int64_t dst_row;    // staging pool row
+  int32_t n_rows;
+  int32_t pad[3];
+};
+static_assert(sizeof(StageTile) == 32, "StageTile layout");
+constexpr int kStageTileRows = 64;
 
 // Host-side result of planning; the device image is `blob` (items, then the
 // page list, then split offsets), uploaded into the caller's workspace.
@@ -75,6 +96,11 @@ struct PlanLayout {
   int32_t n_rows = 0;            // prefill: T (query rows)
   int64_t host_reads = 0;        // prefill: K+V bytes read from each tier,
   int64_t dev_reads = 0;         //   counting re-reads by later row blocks
+  size_t stage_tiles_off = 0;    // prefill: StageTile list inside the blob
+  int32_t n_stage_tiles = 0;
+  int64_t stage_rows = 0;        // prefill: rows of the HBM staging pool
+  int64_t staged_bytes = 0;      // prefill: host K+V bytes copied once
+  int32_t dev_queues = 1;        // prefill: HBM work queues (1 or 8)
 };
 
 // Arguments of the split attention kernel.
@@ -167,30 +193,44 @@ struct ProjArgs {
 };
 
 // Arguments of the prefill kernel.
+// Prefill unit counters in the plan image: one per HBM queue, then the host's.
+constexpr int kPfMaxQueues = 8;
+constexpr int kPfHostCounter = kPfMaxQueues;
+
 struct PrefillArgs {
   const PrefillItem* host_items;
-  const PrefillItem* dev_items;
-  const int32_t* plist;
-  int32_t* unit_counters;        // [2], zero at launch
-  int32_t n_host_units;
-  int32_t n_dev_units;
+  const PrefillItem* dev_items;  // HBM and staged items
+  const int32_t* pages;          // paged: (logical page, pool page) pairs
+  int32_t* unit_counters;        // [kPfMaxQueues + 1], zero at launch
+  int32_t n_host_items;
+  int32_t n_dev_items;
   int32_t host_wgs;
-  int32_t dev_wgs;
+  int32_t dev_wgs;               // multiple of dev_queues
+  int32_t dev_queues;            // 1, or 8 when Hkv % 8 == 0 (one per XCD)
+  int32_t pad;
   const uint16_t* host_k;
   const uint16_t* host_v;
   const uint16_t* dev_k;
   const uint16_t* dev_v;
-  int64_t host_rows;
-  int64_t dev_rows;
-  const int32_t* page_table;
-  int32_t max_pages;
+  const uint16_t* stage_k;
+  const uint16_t* stage_v;
   int32_t page_shift;
   int32_t hq;
   int32_t hkv;
   int32_t head_dim;
-  int32_t pad;
   float* part_o;                 // [S][Hq][D]
   float* part_lse;               // [S][Hq]
+};
+
+// Arguments of the staging copy (host rows -> HBM staging pool).
+struct StageArgs {
+  const StageTile* tiles;
+  int32_t n_tiles;
+  int32_t row_chunks;            // 16-byte chunks per row (Hkv * D / 8)
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
 };
 
 // Launchers (dkv_kernels.hip).  They return hipError_t as int.
@@ -200,6 +240,7 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
 int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream);
+int launch_stage(const StageArgs& a, int nwg, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_project(const ProjArgs& a, void* stream);
 int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
@@ -227,6 +268,7 @@ struct PlanInput {
   int32_t dev_chunk;
   double host_bw;
   double dev_bw;
+  int64_t stage_max_bytes;        // prefill staging budget (< 0: never stage)
 };
 
 // Builds the plan and its device image; on failure returns false with `err`.
@@ -235,8 +277,8 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
 
 // Prefill plan: query rows of sequence b are q_start[b] .. q_start[b+1]-1,
 // row j of b at position q_pos0[b] + j; in.seq_lens are the cached lengths.
-// Device image: host items, dev items, page list, row positions [T], split
-// offsets [T+1], counters.
+// Device image: host items, dev/staged items, page pairs, stage tiles, row
+// positions [T], split offsets [T+1], counters.
 bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
                         PlanLayout* out, std::vector<uint8_t>* blob, std::string* err);
 

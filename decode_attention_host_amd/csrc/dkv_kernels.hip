@@ -391,33 +391,85 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
 // ---------------------------------------------------------------------------
 // Prefill: causal attention of blocks of new query rows over the cache.
 //
-// A unit = (row block of QB = 64/G query rows of one sequence, run of cached
-// tokens in one tier, KV head); its 64 MFMA rows are the (head, row) pairs of
-// the group, 16 per wave.  Both contractions are dense here and run on
-// v_mfma_f32_16x16x32_bf16:
-//   S = Q.K^T   A = query rows (fp32 split into high/low bf16), B = K rows
-//   O += P.V    A = probabilities (high/low bf16 from LDS), B = V transposed
-//               into LDS while the tile is staged
-// Causal mask: token t is visible to a row at position p iff t <= p.
+// A unit = (row block of kPrefillRows/G query rows of one sequence, run of
+// cached tokens in one pool, KV head).  Its 128 query-head rows are the
+// (row, head) pairs of the group, 32 per wave as two 16-column MFMA tiles.
+// Both contractions are dense and run on v_mfma_f32_16x16x32_bf16 in the
+// transposed form, so the probabilities never leave registers:
+//   S^T = K . Q^T   A = 16 keys x 32 dims (LDS), B = query columns (the fp32
+//                   rotated query split into high and low bf16 parts)
+//   O^T += V^T . P^T A = V transposed into LDS at staging time, B = the
+//                   probabilities (high and low bf16 parts) taken straight
+//                   from the S^T accumulators: accumulator lane group j holds
+//                   keys 4j..4j+3 of each 16-key tile, so a 32-key k-step
+//                   pairs two tiles and V^T is read in the same key order.
+// Causal mask: token t is visible to a row at position p iff t <= p; tiles
+// entirely below the block's first position skip the mask.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads) void prefill_split_kernel(PrefillArgs a,
-                                                                 const float* __restrict__ q_rot) {
-  constexpr int QB = 64 / G;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  const bf16x2_t v = {(__bf16)x, (__bf16)y};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// x = hi + lo with hi, lo bf16: pack (x0, x1) into hi and lo words.
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(x0, x1);
+  lo = pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+}
+
+#ifndef DKV_PF_NTW
+#define DKV_PF_NTW 1
+#endif
+constexpr int kPfNtw = DKV_PF_NTW;
+
+// Reductions over the four 16-lane groups of a wave (lanes n, n+16, n+32,
+// n+48), with the gfx950 lane-swap instructions: permlane16_swap pairs rows
+// 0-1 and 2-3, permlane32_swap the two halves.
+__device__ __forceinline__ float wave_max_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Headroom of the lazily updated softmax reference maximum (log2 units).
+constexpr float kRescaleSlack = 8.f;
+
+template <int NTW>
+constexpr int pf_threads() { return kPrefillRows / (16 * NTW) * 64; }
+
+// NTW: 16-column MFMA tiles (query-head rows / 16) per wave; the workgroup
+// holds kPrefillRows / (16 NTW) waves.  One tile per wave (8 waves, ~200
+// VGPRs, two waves per SIMD) measured faster than two per wave (4 waves, one
+// wave per SIMD) on the LLaMA-3-8B 2048-row prefill: 0.112 vs 0.134 ms.
+template <int D, int G, bool PAGED, int NTW>
+__global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a,
+                                                                          const float* __restrict__ q_rot) {
+  constexpr int NT = pf_threads<NTW>();
+  constexpr int QB = kPrefillRows / G;
   constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
-  constexpr int DT = D / 16;                   // 16-wide output-dim tiles of P.V
+  constexpr int DT = D / 16;                   // 16-row d tiles of O^T
   constexpr int KPITCH = D * 2 + 16;           // bytes per K row in LDS
-  constexpr int VT_PITCH = kTile + 8;          // bf16 per transposed V row
-  constexpr int P_PITCH = kTile + 8;           // bf16 per probability row
+  constexpr int VPB = kTile * 2 + 8;           // bytes per V^T row (one d, 64 keys)
   constexpr int CPR = D / 8;                   // 16-byte chunks per KV row
-  constexpr int NCK = kTile * CPR / kThreads;  // K chunks per thread
-  constexpr int NPV = kTile * CPR / 2 / kThreads;  // V row pairs per thread
-  static_assert(NPV >= 1, "tile shape");
+  constexpr int NCK = kTile * CPR / NT;        // K chunks per thread
+  constexpr int TPT = NCK;                     // V keys per thread (one 8-dim chunk)
+  constexpr int KQ = kTile / TPT;              // V key groups per tile
+  static_assert(TPT == 1 || TPT == 2 || TPT == 4, "tile shape");
+  static_assert(KQ * CPR == NT, "V staging covers the tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VT_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t p_hi[4][16 * P_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lo[4][16 * P_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[D * VPB];
   __shared__ int tpos_lds[kTile];
   __shared__ int s_next;
 
@@ -426,133 +478,172 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(PrefillArgs a,
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int j4 = lane >> 4;
+  // V staging: consecutive lanes take consecutive key groups of one 8-dim
+  // chunk, so the transposed LDS writes of a wave hit distinct banks
+  const int vq = tid % KQ;
+  const int vc = tid / KQ;
 
+  // Work queues: the host role has one; the HBM role has one per queue id
+  // (blockIdx mod dev_queues), each owning the KV heads congruent to it, so
+  // the workgroups that share an L2 share KV heads.
   const bool host_role = (int)blockIdx.x < a.host_wgs;
   const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
-  const int nwg = host_role ? a.host_wgs : a.dev_wgs;
-  const int nunits = host_role ? a.n_host_units : a.n_dev_units;
+  const int nq = host_role ? 1 : a.dev_queues;
+  const int q = wg % nq;
+  const int nwg = (host_role ? a.host_wgs : a.dev_wgs) / nq;
+  const int hpq = a.hkv / nq;  // KV heads per queue
+  const int nunits = (host_role ? a.n_host_items : a.n_dev_items) * hpq;
   const PrefillItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
-  const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
-  const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
-  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
-  int* counter = a.unit_counters + (host_role ? 1 : 0);
+  int* counter = a.unit_counters + (host_role ? kPfHostCounter : q);
 
-  // pool row and logical position of token `tok` of an item (-1: not valid)
-  auto locate = [&](const PrefillItem& it, int tok, int64_t& row) -> int {
+  struct Src {
+    const uint16_t* k;
+    const uint16_t* v;
+    bool nt;
+  };
+  auto src_of = [&](const PrefillItem& it) -> Src {
+    if (it.pool == kPoolHost) return Src{a.host_k, a.host_v, true};
+    if (it.pool == kPoolDev) return Src{a.dev_k, a.dev_v, false};
+    return Src{a.stage_k, a.stage_v, false};
+  };
+  // pool row of token `tok` of an item (tokens past the end read token 0)
+  auto row_of = [&](const PrefillItem& it, int tok) -> int64_t {
+    tok = tok < it.n_tok ? tok : 0;
+    if (PAGED) {
+      const int pg = tok >> a.page_shift;
+      return ((int64_t)a.pages[2 * (it.plist + pg) + 1] << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
+    }
+    return it.row_pool + tok;
+  };
+  auto pos_of = [&](const PrefillItem& it, int tok) -> int {
     if (tok >= it.n_tok) return -1;
     if (PAGED) {
-      const int lp = a.plist[it.plist + (tok >> a.page_shift)];
-      const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
-      const int off = tok & ((1 << a.page_shift) - 1);
-      row = ((int64_t)(e >> 1) << a.page_shift) | off;
-      if (e < 0 || ((e & 1) != 0) != host_role || row >= cap_rows) return -1;
-      return (lp << a.page_shift) + off;
+      const int pg = tok >> a.page_shift;
+      return (a.pages[2 * (it.plist + pg)] << a.page_shift) + (tok & ((1 << a.page_shift) - 1));
     }
-    row = it.row_pool + tok;
     return it.tok0 + tok;
   };
 
-  u32x4 kreg[NCK], vreg[NPV][2];
+  u32x4 kreg[NCK], vreg[TPT];
   int treg = -1;
-  auto load_tile = [&](const PrefillItem& it, int kvh, int tile) {
+  // Element offsets of this thread's K and V loads for tile 0 of a unit;
+  // tile t adds t * 64 rows.  Rows past the item's end are clamped to its
+  // first token: real data whose keys the mask removes (p = 0 exactly).
+  int64_t koff[NCK], voff[TPT];
+  auto set_offsets = [&](const PrefillItem& it, int kvh, int tile) {
+    const int t0 = tile * kTile;
 #pragma unroll
     for (int c = 0; c < NCK; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int r = chunk / CPR, col = chunk - (chunk / CPR) * CPR;
-      int64_t row = 0;
-      const bool ok = locate(it, tile * kTile + r, row) >= 0;
-      kreg[c] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                         kpool + (row * a.hkv + kvh) * D + col * 8))
-                   : u32x4{0u, 0u, 0u, 0u};
+      const int chunk = tid + c * NT;
+      koff[c] = (row_of(it, t0 + chunk / CPR) * a.hkv + kvh) * D + (chunk % CPR) * 8;
     }
 #pragma unroll
-    for (int q = 0; q < NPV; ++q) {
-      const int pr = tid + q * kThreads;
-      const int rp = pr / CPR, col = pr - (pr / CPR) * CPR;
+    for (int e = 0; e < TPT; ++e) voff[e] = (row_of(it, t0 + vq * TPT + e) * a.hkv + kvh) * D + vc * 8;
+  };
+  // Host rows stream once over the link (non-temporal); HBM and staged rows
+  // are re-read by later row blocks and stay cacheable.
+  auto load_tile = [&](const PrefillItem& it, const Src& sp, int kvh, int tile) {
+    const int t0 = tile * kTile;
+    // contiguous items step the offsets by whole tiles except where the
+    // tile runs past the item (clamping) ; paged items look up every tile
+    if (PAGED || tile == 0 || t0 + kTile > it.n_tok) {
+      set_offsets(it, kvh, tile);
+    } else {
+      const int64_t step = (int64_t)kTile * a.hkv * D;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        int64_t row = 0;
-        const bool ok = locate(it, tile * kTile + 2 * rp + e, row) >= 0;
-        vreg[q][e] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                              vpool + (row * a.hkv + kvh) * D + col * 8))
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int c = 0; c < NCK; ++c) koff[c] += step;
+#pragma unroll
+      for (int e = 0; e < TPT; ++e) voff[e] += step;
     }
-    if (tid < kTile) {
-      int64_t row = 0;
-      treg = locate(it, tile * kTile + tid, row);
+    if (sp.nt) {
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp.k + koff[c]));
+#pragma unroll
+      for (int e = 0; e < TPT; ++e) vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp.v + voff[e]));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) kreg[c] = *reinterpret_cast<const u32x4*>(sp.k + koff[c]);
+#pragma unroll
+      for (int e = 0; e < TPT; ++e) vreg[e] = *reinterpret_cast<const u32x4*>(sp.v + voff[e]);
     }
+    if (tid < kTile) treg = pos_of(it, t0 + tid);
   };
 
-  int u = wg;
+  int u = wg / nq;
   PrefillItem it{};
+  Src src{};
   int kvh = 0;
   if (u < nunits) {
-    it = items[u / a.hkv];
-    kvh = u - (u / a.hkv) * a.hkv;
-    load_tile(it, kvh, 0);
+    it = items[u / hpq];
+    kvh = q + nq * (u % hpq);
+    src = src_of(it);
+    load_tile(it, src, kvh, 0);
   }
   while (u < nunits) {
     const int ntiles = (it.n_tok + kTile - 1) / kTile;
-    // ---- query operand (A of S = Q.K^T): MFMA row n of this wave
-    bf16x8_t qa_hi[KS], qa_lo[KS];
-    {
-      const int rowi = wave * 16 + n;
-      const int h = rowi / QB, r = rowi - (rowi / QB) * QB;
-      const bool active = r < it.n_rows;
-      const float* qr = q_rot + ((size_t)(it.row0 + (active ? r : 0)) * a.hq + kvh * G + h) * D;
+    // ---- query operand (B of S^T): column n of tile nt = query-head row
+    //      rho = 16*(NTW*wave + nt) + n = (row rho/G, head rho%G)
+    uint32_t qb_hi[NTW][KS][4], qb_lo[NTW][KS][4];
+    int rpos[NTW];
+    bool rvalid[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int rho = (wave * NTW + nt) * 16 + n;
+      const int r = rho / G, h = rho % G;
+      rvalid[nt] = r < it.n_rows;
+      rpos[nt] = it.pos0 + r;
+      const float* qr = q_rot + ((size_t)(it.row0 + (rvalid[nt] ? r : 0)) * a.hq + kvh * G + h) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint32_t wh[4], wl[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d0 = ks * 32 + j4 * 8 + 2 * e;
-          const float x0 = active ? qr[d0] : 0.f, x1 = active ? qr[d0 + 1] : 0.f;
-          const uint32_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
-          wh[e] = h0 | (h1 << 16);
-          wl[e] = f32_to_bf16(x0 - bf16_to_f32(h0)) | (f32_to_bf16(x1 - bf16_to_f32(h1)) << 16);
-        }
-        qa_hi[ks] = __builtin_bit_cast(bf16x8_t, (u32x4{wh[0], wh[1], wh[2], wh[3]}));
-        qa_lo[ks] = __builtin_bit_cast(bf16x8_t, (u32x4{wl[0], wl[1], wl[2], wl[3]}));
+        const int d0 = ks * 32 + j4 * 8;
+        floatx4 x0 = *reinterpret_cast<const floatx4*>(qr + d0);
+        floatx4 x1 = *reinterpret_cast<const floatx4*>(qr + d0 + 4);
+        if (!rvalid[nt]) { x0 = floatx4{0.f, 0.f, 0.f, 0.f}; x1 = x0; }
+        split_bf16(x0[0], x0[1], qb_hi[nt][ks][0], qb_lo[nt][ks][0]);
+        split_bf16(x0[2], x0[3], qb_hi[nt][ks][1], qb_lo[nt][ks][1]);
+        split_bf16(x1[0], x1[1], qb_hi[nt][ks][2], qb_lo[nt][ks][2]);
+        split_bf16(x1[2], x1[3], qb_hi[nt][ks][3], qb_lo[nt][ks][3]);
       }
     }
-    // C-layout rows of this lane: 4*j4 + i of the wave's 16
-    int rpos[4];
-    bool rvalid[4];
+    // m_run: reference maximum of the scores (log2 units); it only moves when
+    // the running maximum exceeds it by more than kRescaleSlack, so most tiles
+    // skip rescaling O (probabilities then stay <= 2^kRescaleSlack).
+    float m_run[NTW], l_run[NTW];
+    floatx4 ot[NTW][DT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rowi = wave * 16 + j4 * 4 + i;
-      const int r = rowi - (rowi / QB) * QB;
-      rvalid[i] = r < it.n_rows;
-      rpos[i] = it.pos0 + r;
+    for (int nt = 0; nt < NTW; ++nt) {
+      m_run[nt] = -INFINITY;
+      l_run[nt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) ot[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    float m_run[4], l_run[4];
-    floatx4 oacc[DT];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     int next_u = nunits;
     PrefillItem nit{};
+    Src nsrc{};
     int nkvh = 0;
     for (int tile = 0; tile < ntiles; ++tile) {
       __syncthreads();  // previous tile's readers are done
 #pragma unroll
       for (int c = 0; c < NCK; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int r = chunk / CPR, col = chunk - (chunk / CPR) * CPR;
-        *reinterpret_cast<u32x4*>(k_lds + r * KPITCH + col * 16) = kreg[c];
+        const int chunk = tid + c * NT;
+        *reinterpret_cast<u32x4*>(k_lds + (chunk / CPR) * KPITCH + (chunk % CPR) * 16) = kreg[c];
       }
+      // V^T: row d = 8*vc + e holds keys vq*TPT .. vq*TPT + TPT-1
 #pragma unroll
-      for (int q = 0; q < NPV; ++q) {
-        const int pr = tid + q * kThreads;
-        const int rp = pr / CPR, col = pr - (pr / CPR) * CPR;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (vreg[q][0][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          const uint32_t hi = (vreg[q][1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(&vt_lds[(col * 8 + e) * VT_PITCH + 2 * rp]) = lo | (hi << 16);
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1, sh = (e & 1) * 16;
+        uint8_t* dst = vt_lds + (vc * 8 + e) * VPB + vq * TPT * 2;
+        if constexpr (TPT == 1) {
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((vreg[0][w] >> sh) & 0xffffu);
+        } else {
+          const uint32_t k01 = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[TPT > 1 ? 1 : 0][w] >> sh) & 0xffffu) << 16);
+          if constexpr (TPT == 4) {
+            const uint32_t k23 = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<u32x2*>(dst) = u32x2{k01, k23};
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = k01;
+          }
         }
       }
       if (tid < kTile) tpos_lds[tid] = treg;
@@ -560,108 +651,185 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(PrefillArgs a,
       if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
       __syncthreads();
       if (!last) {
-        load_tile(it, kvh, tile + 1);
+        load_tile(it, src, kvh, tile + 1);
       } else {
         next_u = s_next;
         if (next_u < nunits) {
-          nit = items[next_u / a.hkv];
-          nkvh = next_u - (next_u / a.hkv) * a.hkv;
-          load_tile(nit, nkvh, 0);
+          nit = items[next_u / hpq];
+          nkvh = q + nq * (next_u % hpq);
+          nsrc = src_of(nit);
+          load_tile(nit, nsrc, nkvh, 0);
         }
       }
 
-      // ---- S = Q.K^T for 16 rows x 64 tokens (four 16-token column tiles)
-      floatx4 sc[4];
+      // ---- S^T = K . Q^T: 64 keys (four 16-key tiles) x 16*NTW query columns;
+      //      high parts first, then low parts, so no MFMA waits on the one before
+      floatx4 st[4][NTW];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        sc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* krow = k_lds + (nt * 16 + n) * KPITCH + j4 * 16;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(krow + ks * 64));
-          sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[ks], kb, sc[nt], 0, 0, 0);
-          sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[ks], kb, sc[nt], 0, 0, 0);
+        for (int nt = 0; nt < NTW; ++nt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t kf[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          kf[mt] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const u32x4 qh = {qb_hi[nt][ks][0], qb_hi[nt][ks][1], qb_hi[nt][ks][2], qb_hi[nt][ks][3]};
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt], __builtin_bit_cast(bf16x8_t, qh), st[mt][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const u32x4 ql = {qb_lo[nt][ks][0], qb_lo[nt][ks][1], qb_lo[nt][ks][2], qb_lo[nt][ks][3]};
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt], __builtin_bit_cast(bf16x8_t, ql), st[mt][nt], 0, 0, 0);
         }
       }
-      // ---- causal mask and online softmax per row (row = 4*j4 + i)
-      int tp[4];
+      // ---- causal mask (keys past a row's position or past the item)
+      const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
+      if (need_mask) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) tp[nt] = tpos_lds[nt * 16 + n];
-      float alpha[4];
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 4; ++i) {
+            const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+              st[mt][nt][i] = (tp >= 0 && tp <= rpos[nt]) ? st[mt][nt][i] : -INFINITY;
+          }
+      }
+      // ---- online softmax per query column, P^T straight into B operands
+      float m_new[NTW];
+      bool grow = false;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const bool vis = rvalid[i] && tp[nt] >= 0 && tp[nt] <= rpos[i];
-          sc[nt][i] = vis ? sc[nt][i] : -INFINITY;
-          mx = fmaxf(mx, sc[nt][i]);
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[mt][nt][i]);
+        mx = wave_max_rows4(mx);  // over the four lane groups of column n
+        m_new[nt] = (mx > m_run[nt] + kRescaleSlack) ? mx : m_run[nt];
+        grow |= m_new[nt] != m_run[nt];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          // 1 if this column kept its reference (also while it is still -inf),
+          // 0 on its first finite maximum
+          const float alpha = m_new[nt] == m_run[nt] ? 1.f : exp2f(m_run[nt] - m_new[nt]);
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) ot[nt][dt] *= alpha;
+          m_run[nt] = m_new[nt];
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 1));
-        mx = fmaxf(mx, __shfl_xor(mx, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 4));
-        mx = fmaxf(mx, __shfl_xor(mx, 8));
-        const float m_new = fmaxf(m_run[i], mx);
-        alpha[i] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[i] - m_new);
+      }
+      uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+        float pv[4][4];
         float ps = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float pv = (sc[nt][i] == -INFINITY) ? 0.f : exp2f(sc[nt][i] - m_new);
-          ps += pv;
-          const uint32_t ph = f32_to_bf16(pv);
-          const int o = (j4 * 4 + i) * P_PITCH + nt * 16 + n;
-          p_hi[wave][o] = (uint16_t)ph;
-          p_lo[wave][o] = (uint16_t)f32_to_bf16(pv - bf16_to_f32(ph));
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[mt][i] = __builtin_amdgcn_exp2f(st[mt][nt][i] - m_use);  // -inf -> 0
+            ps += pv[mt][i];
+          }
+        l_run[nt] += ps;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          split_bf16(pv[2 * kt][0], pv[2 * kt][1], pb_hi[nt][kt][0], pb_lo[nt][kt][0]);
+          split_bf16(pv[2 * kt][2], pv[2 * kt][3], pb_hi[nt][kt][1], pb_lo[nt][kt][1]);
+          split_bf16(pv[2 * kt + 1][0], pv[2 * kt + 1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
+          split_bf16(pv[2 * kt + 1][2], pv[2 * kt + 1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
         }
-        ps += __shfl_xor(ps, 1);
-        ps += __shfl_xor(ps, 2);
-        ps += __shfl_xor(ps, 4);
-        ps += __shfl_xor(ps, 8);
-        l_run[i] = l_run[i] * alpha[i] + ps;
-        m_run[i] = m_new;
       }
+      // ---- O^T += V^T . P^T over two 32-key k-steps (high parts, then low)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha[i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-      // ---- O += P.V: A = P rows (from LDS), B = V^T rows (from LDS)
-#pragma unroll
-      for (int kt = 0; kt < kTile / 32; ++kt) {
-        const int ko = kt * 32 + j4 * 8;
-        const bf16x8_t pa_hi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&p_hi[wave][n * P_PITCH + ko]));
-        const bf16x8_t pa_lo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&p_lo[wave][n * P_PITCH + ko]));
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x8_t va[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(&vt_lds[(dt * 16 + n) * VT_PITCH + ko]));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, oacc[dt], 0, 0, 0);
+          const uint8_t* vrow = vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 4) * 2;
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 32);
+          va[dt] = __builtin_bit_cast(bf16x8_t, (u32x4{v0[0], v0[1], v1[0], v1[1]}));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const u32x4 ph = {pb_hi[nt][kt][0], pb_hi[nt][kt][1], pb_hi[nt][kt][2], pb_hi[nt][kt][3]};
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(bf16x8_t, ph), ot[nt][dt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const u32x4 pl = {pb_lo[nt][kt][0], pb_lo[nt][kt][1], pb_lo[nt][kt][2], pb_lo[nt][kt][3]};
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(bf16x8_t, pl), ot[nt][dt], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
 
     // ---- write this unit's partial for every valid row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!rvalid[i]) continue;
-      const int rowi = wave * 16 + j4 * 4 + i;
-      const int h = rowi / QB, r = rowi - (rowi / QB) * QB;
+    for (int nt = 0; nt < NTW; ++nt) {
+      const float l = wave_sum_rows4(l_run[nt]);
+      if (!rvalid[nt]) continue;
+      const int rho = (wave * NTW + nt) * 16 + n;
+      const int r = rho / G, h = rho % G;
       const size_t slot = (size_t)it.base + (size_t)r * it.n_splits + it.split_idx;
       const size_t head = slot * a.hq + kvh * G + h;
-      const bool empty = m_run[i] == -INFINITY;
-      const float inv = empty ? 0.f : 1.f / l_run[i];
+      const bool empty = m_run[nt] == -INFINITY;
+      const float inv = empty ? 0.f : 1.f / l;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) a.part_o[head * D + dt * 16 + n] = oacc[dt][i] * inv;
-      if (n == 0)
-        a.part_lse[head] = empty ? -INFINITY : (m_run[i] + log2f(l_run[i])) * 0.69314718055994530942f;
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<floatx4*>(a.part_o + head * D + dt * 16 + j4 * 4) = ot[nt][dt] * inv;
+      if (j4 == 0)
+        a.part_lse[head] = empty ? -INFINITY : (m_run[nt] + log2f(l)) * 0.69314718055994530942f;
     }
     u = next_u;
     it = nit;
+    src = nsrc;
     kvh = nkvh;
+  }
+}
+
+// Staging copy of host-tier rows into the HBM pool: tile after tile, 16-byte
+// non-temporal loads from the mapped host memory, eight in flight per lane.
+__global__ __launch_bounds__(kThreads) void stage_copy_kernel(StageArgs a) {
+  constexpr int U = 8;
+  for (int t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
+    const StageTile tl = a.tiles[t];
+    const int64_t per = (int64_t)tl.n_rows * a.row_chunks;  // chunks per tensor
+    const u32x4* src[2] = {reinterpret_cast<const u32x4*>(a.src_k) + tl.src_row * a.row_chunks,
+                           reinterpret_cast<const u32x4*>(a.src_v) + tl.src_row * a.row_chunks};
+    u32x4* dst[2] = {reinterpret_cast<u32x4*>(a.dst_k) + tl.dst_row * a.row_chunks,
+                     reinterpret_cast<u32x4*>(a.dst_v) + tl.dst_row * a.row_chunks};
+    for (int64_t c0 = threadIdx.x; c0 < 2 * per; c0 += (int64_t)kThreads * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t c = c0 + (int64_t)k * kThreads;
+        const int w = c >= per;
+        v[k] = c < 2 * per ? __builtin_nontemporal_load(src[w] + (c - w * per)) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t c = c0 + (int64_t)k * kThreads;
+        const int w = c >= per;
+        if (c < 2 * per) dst[w][c - w * per] = v[k];
+      }
+    }
   }
 }
 
@@ -751,6 +919,70 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
     out[tid] = o / Lsum;
     if (tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
   }
+}
+
+// Many (b, h) pairs with few splits each (prefill rows): one wave per pair,
+// each lane owns D/64 dims, splits folded in order with several loads in
+// flight.  A single split is returned exactly (weight exp(0) = 1, sum 1).
+constexpr int kMergeWaveThreads = 256;
+constexpr int64_t kMergeWaveMinPairs = 2048;
+
+template <int D>
+__global__ __launch_bounds__(kMergeWaveThreads) void merge_lse_wave_kernel(MergeArgs a) {
+  constexpr int E = D / 64;
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * (kMergeWaveThreads / 64) + (threadIdx.x >> 6);
+  if (bh >= (int64_t)a.batch * a.hq) return;
+  const int b = (int)(bh / a.hq), h = (int)(bh - (int64_t)b * a.hq);
+  const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
+  const float* lse = a.part_lse + h;
+  float m = -INFINITY;
+  for (int s = s0 + lane; s < s1; s += 64) m = fmaxf(m, lse[(size_t)s * a.hq]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float* out = a.out_o + (size_t)bh * D + lane * E;
+  if (m == -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = 0.f;
+    if (lane == 0 && a.out_lse) a.out_lse[bh] = -INFINITY;
+    return;
+  }
+  float l = 0.f;
+  for (int s = s0 + lane; s < s1; s += 64) {
+    const float x = lse[(size_t)s * a.hq];
+    l += (x == -INFINITY) ? 0.f : expf(x - m);
+  }
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  const float* po = a.part_o + (size_t)h * D + lane * E;
+  const size_t srow = (size_t)a.hq * D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  int s = s0;
+  for (; s + U <= s1; s += U) {
+    float x[U], v[U][E];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      x[k] = lse[(size_t)(s + k) * a.hq];
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = po[(size_t)(s + k) * srow + e];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const float w = (x[k] == -INFINITY) ? 0.f : expf(x[k] - m);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * v[k][e];
+    }
+  }
+  for (; s < s1; ++s) {
+    const float x = lse[(size_t)s * a.hq];
+    const float w = (x == -INFINITY) ? 0.f : expf(x - m);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += w * po[(size_t)s * srow + e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = acc[e] / l;
+  if (lane == 0 && a.out_lse) a.out_lse[bh] = m + logf(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -1011,10 +1243,11 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
 template <int D, int G>
 static hipError_t launch_prefill_dg(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
   const int grid = a.host_wgs + a.dev_wgs;
-  if (a.page_table)
-    hipLaunchKernelGGL((prefill_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+  if (grid <= 0) return hipSuccess;
+  if (a.pages)
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, true, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a, q_rot);
   else
-    hipLaunchKernelGGL((prefill_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, false, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a, q_rot);
   return hipGetLastError();
 }
 
@@ -1037,10 +1270,28 @@ int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream) {
   return (int)hipErrorInvalidValue;
 }
 
+int launch_stage(const StageArgs& a, int nwg, void* stream) {
+  if (a.n_tiles <= 0) return (int)hipSuccess;
+  nwg = std::max(1, std::min(nwg, a.n_tiles));
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(nwg), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
 int launch_merge(const MergeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t grid = (int64_t)a.batch * a.hq;
   if (grid > 0x7fffffff) return (int)hipErrorInvalidValue;
+  if (grid >= kMergeWaveMinPairs) {  // enough pairs to fill the chip one wave each
+    const int64_t per = kMergeWaveThreads / 64;
+    const unsigned wg = (unsigned)((grid + per - 1) / per);
+    if (a.head_dim == 64)
+      hipLaunchKernelGGL(merge_lse_wave_kernel<64>, dim3(wg), dim3(kMergeWaveThreads), 0, s, a);
+    else if (a.head_dim == 128)
+      hipLaunchKernelGGL(merge_lse_wave_kernel<128>, dim3(wg), dim3(kMergeWaveThreads), 0, s, a);
+    else
+      return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+  }
   if (a.head_dim == 64)
     hipLaunchKernelGGL(merge_lse_kernel<64>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
   else if (a.head_dim == 128)

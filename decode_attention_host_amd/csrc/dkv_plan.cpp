@@ -214,7 +214,7 @@ namespace dkv {
 // ---------------------------------------------------------------- prefill
 //
 // DirectKV README, Step 6 ("Prefill (all new KV)"): new tokens attend
-// causally to the cache.  A block of QB = 64/G consecutive query rows of one
+// causally to the cache.  A block of QB = 128/G consecutive query rows of one
 // sequence shares one stream of its KV prefix [0, last row's position]; that
 // prefix is cut by tier and into chunks, one work item per (block, chunk).
 bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
@@ -226,7 +226,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   if (in.hkv < 1 || in.hq % in.hkv) return fail(err, "num_q_heads must be a multiple of num_kv_heads");
   const int G = in.hq / in.hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(err, "query group size %lld not built", G);
-  const int QB = 64 / G;
+  const int QB = kPrefillRows / G;
   const bool paged = in.page_size > 0;
   const int64_t P = paged ? in.page_size : 1;
   const int64_t row_bytes = (int64_t)in.hkv * in.head_dim * 2;
@@ -235,6 +235,8 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   // ---- per-sequence placement (validated exactly as for decode)
   std::vector<int64_t> nh(B, 0);
   std::vector<std::vector<int32_t>> host_pages(paged ? B : 0), dev_pages(paged ? B : 0);
+  std::vector<int64_t> emax(B, 0);
+  std::vector<int32_t> nblk(B, 0);
   for (int b = 0; b < B; ++b) {
     const int64_t L = in.seq_lens[b];
     const int64_t n = (int64_t)q_start[b + 1] - q_start[b];
@@ -243,6 +245,8 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     if (q_pos0[b] < 0 || (int64_t)q_pos0[b] + n > L)
       return fail(err, "sequence %lld: query rows at positions %lld.. exceed the %lld cached tokens", b,
                   q_pos0[b], L);
+    emax[b] = n > 0 ? (int64_t)q_pos0[b] + n : 0;
+    nblk[b] = (int32_t)ceil_div(n, QB);
     if (!paged) {
       const int64_t h = (int64_t)std::floor(in.ratio * (double)L);
       nh[b] = h;
@@ -265,10 +269,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     }
   }
 
-  // ---- row blocks and the tokens each reads per tier
-  struct Blk { int b, row0, n_rows, pos0; int64_t end; };
-  std::vector<Blk> blocks;
-  int64_t host_reads = 0, dev_reads = 0;
+  // tokens of tier `host` below position E (pages of the tier are in logical order)
   auto tier_tokens = [&](int b, int64_t E, bool host) -> int64_t {
     if (!paged) return host ? std::min<int64_t>(nh[b], E) : std::max<int64_t>(0, E - nh[b]);
     int64_t t = 0;
@@ -278,12 +279,58 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     }
     return t;
   };
+  auto tier_pages_below = [&](int b, int64_t E, bool host) -> size_t {
+    const std::vector<int32_t>& pg = host ? host_pages[b] : dev_pages[b];
+    size_t k = 0;
+    while (k < pg.size() && (int64_t)pg[k] * P < E) ++k;
+    return k;
+  };
+
+  // ---- staging: host rows that two or more row blocks read are copied once
+  // into an HBM pool, within the byte budget, in sequence order.
+  const int64_t budget = in.stage_max_bytes;
+  std::vector<int64_t> stage_base(B, -1);
+  std::vector<StageTile> tiles;
+  int64_t stage_rows = 0;
+  for (int b = 0; b < B; ++b) {
+    if (budget <= 0 || nblk[b] < 2) continue;
+    const int64_t rows = paged ? (int64_t)tier_pages_below(b, emax[b], true) * P
+                               : std::min<int64_t>(nh[b], emax[b]);
+    if (rows <= 0 || (stage_rows + rows) * row_bytes * 2 > budget) continue;
+    stage_base[b] = stage_rows;
+    if (!paged) {
+      for (int64_t r = 0; r < rows; r += kStageTileRows) {
+        StageTile t{};
+        t.src_row = (int64_t)b * in.host_stride + r;
+        t.dst_row = stage_rows + r;
+        t.n_rows = (int32_t)std::min<int64_t>(kStageTileRows, rows - r);
+        tiles.push_back(t);
+      }
+    } else {
+      const int64_t np = rows / P;
+      for (int64_t i = 0; i < np; ++i) {
+        const int32_t e = in.page_table_host[(int64_t)b * in.max_pages + host_pages[b][i]];
+        StageTile t{};
+        t.src_row = (int64_t)(e >> 1) * P;
+        t.dst_row = stage_rows + i * P;
+        t.n_rows = (int32_t)P;
+        tiles.push_back(t);
+      }
+    }
+    stage_rows += rows;
+  }
+
+  // ---- row blocks and the tokens each reads per pool
+  struct Blk { int b, row0, n_rows, pos0; int64_t end; };
+  std::vector<Blk> blocks;
+  int64_t host_reads = 0, dev_reads = 0;
   for (int b = 0; b < B; ++b) {
     const int n = q_start[b + 1] - q_start[b];
     for (int r0 = 0; r0 < n; r0 += QB) {
       Blk k{b, q_start[b] + r0, std::min(QB, n - r0), q_pos0[b] + r0, 0};
       k.end = (int64_t)k.pos0 + k.n_rows;  // tokens [0, end) are visible to some row
-      host_reads += tier_tokens(b, k.end, true);
+      const int64_t th = tier_tokens(b, k.end, true);
+      (stage_base[b] >= 0 ? dev_reads : host_reads) += th;
       dev_reads += tier_tokens(b, k.end, false);
       blocks.push_back(k);
     }
@@ -307,18 +354,21 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   }
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
   const int32_t ch = choose_chunk(host_reads * in.hkv, wh, 4, 256, 16384, align, in.host_chunk);
-  const int32_t cd = choose_chunk(dev_reads * in.hkv, wd, 6, 512, 1 << 16, align, in.dev_chunk);
+  // A prefill token-head costs a full 128-row MFMA pass, so HBM units are
+  // long: fewer partials to write and merge, LPT order evens out the tail.
+  const int32_t cd = choose_chunk(dev_reads * in.hkv, wd, 2, 1024, 1 << 16, align, in.dev_chunk);
 
   // ---- items, split slots, row offsets and positions
   const int64_t T = q_start[B];
   std::vector<PrefillItem> hitems, ditems;
-  std::vector<int32_t> plist, rowpos(T), offsets(T + 1, 0);
+  std::vector<int32_t> pages, rowpos(T), offsets(T + 1, 0);
   int64_t slot = 0;
   for (const Blk& k : blocks) {
     std::vector<PrefillItem> items;
-    std::vector<bool> is_host;
+    const bool staged = stage_base[k.b] >= 0;
     for (int tier = 1; tier >= 0; --tier) {
-      const int64_t chunk = tier ? ch : cd;
+      const int32_t pool = tier ? (staged ? kPoolStaged : kPoolHost) : kPoolDev;
+      const int64_t chunk = pool == kPoolHost ? ch : cd;
       if (!paged) {
         const int64_t t0 = tier ? 0 : nh[k.b];
         const int64_t t1 = tier ? std::min<int64_t>(nh[k.b], k.end) : k.end;
@@ -326,25 +376,30 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
           PrefillItem it{};
           it.n_tok = (int32_t)std::min<int64_t>(chunk, t1 - t);
           it.tok0 = (int32_t)t;
-          it.row_pool = tier ? (int64_t)k.b * in.host_stride + t : (int64_t)k.b * in.dev_stride + (t - nh[k.b]);
+          it.pool = pool;
+          it.row_pool = pool == kPoolHost ? (int64_t)k.b * in.host_stride + t
+                      : pool == kPoolStaged ? stage_base[k.b] + t
+                                            : (int64_t)k.b * in.dev_stride + (t - nh[k.b]);
           items.push_back(it);
-          is_host.push_back(tier == 1);
         }
       } else {
-        const std::vector<int32_t>& pages = tier ? host_pages[k.b] : dev_pages[k.b];
-        size_t npg = 0;
-        while (npg < pages.size() && (int64_t)pages[npg] * P < k.end) ++npg;
+        const std::vector<int32_t>& pg = tier ? host_pages[k.b] : dev_pages[k.b];
+        const size_t npg = tier_pages_below(k.b, k.end, tier == 1);
         const size_t per = (size_t)(chunk / P);
         for (size_t p0 = 0; p0 < npg; p0 += per) {
           const size_t p1 = std::min(npg, p0 + per);
           PrefillItem it{};
           int64_t nt = 0;
-          for (size_t q = p0; q < p1; ++q) nt += std::min<int64_t>(P, k.end - (int64_t)pages[q] * P);
+          for (size_t q = p0; q < p1; ++q) nt += std::min<int64_t>(P, k.end - (int64_t)pg[q] * P);
           it.n_tok = (int32_t)nt;
-          it.plist = (int32_t)plist.size();
-          for (size_t q = p0; q < p1; ++q) plist.push_back(pages[q]);
+          it.plist = (int32_t)(pages.size() / 2);
+          it.pool = pool;
+          for (size_t q = p0; q < p1; ++q) {
+            const int32_t e = in.page_table_host[(int64_t)k.b * in.max_pages + pg[q]];
+            pages.push_back(pg[q]);
+            pages.push_back(pool == kPoolStaged ? (int32_t)(stage_base[k.b] / P + (int64_t)q) : (e >> 1));
+          }
           items.push_back(it);
-          is_host.push_back(tier == 1);
         }
       }
     }
@@ -358,7 +413,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
       it.split_idx = s;
       it.n_splits = S_k;
       it.base = (int32_t)slot;
-      (is_host[s] ? hitems : ditems).push_back(it);
+      (it.pool == kPoolHost ? hitems : ditems).push_back(it);
     }
     for (int r = 0; r < k.n_rows; ++r) {
       offsets[k.row0 + r] = (int32_t)(slot + (int64_t)r * S_k);
@@ -369,6 +424,12 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   }
   offsets[T] = (int32_t)slot;
   if ((int64_t)(hitems.size() + ditems.size()) * in.hkv > INT32_MAX) return fail(err, "too many work units");
+  if ((int64_t)pages.size() > INT32_MAX) return fail(err, "page list too long");
+  // longest items first: workgroups take units in list order, so the tail of
+  // the persistent loop is made of short units
+  auto longer = [](const PrefillItem& x, const PrefillItem& y) { return x.n_tok > y.n_tok; };
+  std::stable_sort(hitems.begin(), hitems.end(), longer);
+  std::stable_sort(ditems.begin(), ditems.end(), longer);
 
   out->n_host_items = (int32_t)hitems.size();
   out->n_dev_items = (int32_t)ditems.size();
@@ -376,27 +437,42 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   out->batch = B;
   out->n_rows = (int32_t)T;
   out->host_wgs = hitems.empty() ? 0 : (int32_t)std::min<int64_t>(wh, (int64_t)hitems.size() * in.hkv);
-  out->dev_wgs = ditems.empty() ? 0 : (int32_t)std::min<int64_t>(wd, (int64_t)ditems.size() * in.hkv);
+  out->dev_wgs = ditems.empty() ? 0 : (int32_t)std::min<int64_t>(std::max(wd, 1), (int64_t)ditems.size() * in.hkv);
+  // HBM queues per XCD (8 of them, workgroups dealt round-robin): queue q
+  // owns the KV heads h = q mod 8, so workgroups of one L2 re-read the same
+  // heads.  Both workgroup counts become multiples of 8 so that blockIdx
+  // mod 8 is the queue of every HBM-role workgroup.
+  out->dev_queues = 1;
+  if (in.hkv % kPfMaxQueues == 0 && out->dev_wgs >= kPfMaxQueues) {
+    out->dev_queues = kPfMaxQueues;
+    out->host_wgs = out->host_wgs / kPfMaxQueues * kPfMaxQueues + (out->host_wgs % kPfMaxQueues ? kPfMaxQueues : 0);
+    out->dev_wgs = out->dev_wgs / kPfMaxQueues * kPfMaxQueues;
+  }
   out->host_chunk = hitems.empty() ? 0 : ch;
   out->dev_chunk = ditems.empty() ? 0 : cd;
+  out->stage_rows = stage_rows;
+  out->staged_bytes = stage_rows * row_bytes * 2;
+  out->n_stage_tiles = (int32_t)tiles.size();
   out->host_reads = host_reads * row_bytes * 2;
   out->dev_reads = dev_reads * row_bytes * 2;
-  out->host_bytes = out->host_reads;
+  out->host_bytes = out->host_reads + out->staged_bytes;
   out->dev_bytes = out->dev_reads;
-  out->n_plist = (int32_t)plist.size();
+  out->n_plist = (int32_t)(pages.size() / 2);
   out->items_off = 0;
   out->plist_off = (hitems.size() + ditems.size()) * sizeof(PrefillItem);
-  out->rowpos_off = round_up(out->plist_off + plist.size() * sizeof(int32_t), 16);
+  out->stage_tiles_off = round_up(out->plist_off + pages.size() * sizeof(int32_t), 32);
+  out->rowpos_off = round_up(out->stage_tiles_off + tiles.size() * sizeof(StageTile), 16);
   out->offsets_off = round_up(out->rowpos_off + T * sizeof(int32_t), 16);
   out->counters_off = round_up(out->offsets_off + (T + 1) * sizeof(int32_t), 16);
-  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
+  out->blob_bytes = round_up(out->counters_off + (kPfMaxQueues + 1) * sizeof(int32_t), 256);
   if (blob) {
     blob->assign(out->blob_bytes, 0);
     uint8_t* p = blob->data();
     if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(PrefillItem));
     if (!ditems.empty())
       memcpy(p + hitems.size() * sizeof(PrefillItem), ditems.data(), ditems.size() * sizeof(PrefillItem));
-    if (!plist.empty()) memcpy(p + out->plist_off, plist.data(), plist.size() * sizeof(int32_t));
+    if (!pages.empty()) memcpy(p + out->plist_off, pages.data(), pages.size() * sizeof(int32_t));
+    if (!tiles.empty()) memcpy(p + out->stage_tiles_off, tiles.data(), tiles.size() * sizeof(StageTile));
     if (T) memcpy(p + out->rowpos_off, rowpos.data(), T * sizeof(int32_t));
     memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
   }

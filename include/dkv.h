@@ -173,6 +173,9 @@ typedef struct dkv_plan_info {
   int32_t dev_chunk;       /* tokens per HBM work item */
   int64_t host_bytes;      /* K+V bytes read from host memory per call */
   int64_t dev_bytes;       /* K+V bytes read from HBM per call */
+  int64_t staged_bytes;    /* prefill: host K+V bytes copied once into HBM and
+                              read from there (included in host_bytes; their
+                              re-reads are in dev_bytes); 0 for decode */
 } dkv_plan_info;
 
 dkv_status dkv_decode_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
@@ -213,16 +216,37 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
  *   s_t = scale * q_rot . k_t (t <= p),  o = softmax(s) V,  lse = ln sum e^s.
  * q is [T][Hq][D] bf16 (device), T = q_start[batch].
  *
- * Output is split like dkv_decode_attn_split: the rows of a block of 64/G
+ * Output is split like dkv_decode_attn_split: the rows of a block of 128/G
  * consecutive rows share runs of cached tokens, one per tier and chunk;
  * each (row, run) writes a normalised partial, and split_offsets (device
  * int32 [T+1]) gives each row's CSR range of splits.  dkv_merge_lse with
  * batch = T then yields o [T][Hq][D] and lse [T][Hq].  dkv_prefill_plan gives
  * the split count and workspace size.  Q.K^T and P.V run on MFMA.
+ *
+ * Host-tier rows that two or more row blocks of a sequence read are first
+ * copied once into an HBM staging pool inside the workspace (one read over
+ * the host link instead of one per block), within the staging budget of
+ * dkv_tuning.stage_max_mib; the workspace size includes that pool.
  * ---------------------------------------------------------------------- */
 dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                             const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
                             double offload_ratio, dkv_plan_info* info);
+
+/* Prefill planner introspection (no HIP calls; used by CPU tests): the plan
+ * dkv_prefill_plan would build for num_cus compute units.  Per item, 11
+ * int64 into items: pool (0 host, 1 HBM, 2 HBM staging copy of host rows),
+ * sequence, first query row, rows, first row's position, tokens, first
+ * (contiguous: pool row of the first token; paged: index of the first page
+ * pair), logical position of the first token (contiguous), split index,
+ * splits of the block, first split slot.  pages: (logical page, pool page)
+ * pairs of paged items.  tiles: 3 int64 per staging copy (host row, staging
+ * row, rows).  split_offsets: [T+1].  Arrays are filled up to their caps;
+ * info gives the counts (host_items + dev_items items). */
+dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                    const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                                    double offload_ratio, int32_t num_cus, int64_t* items, int32_t items_cap,
+                                    int32_t* pages, int32_t pages_cap, int64_t* tiles, int32_t tiles_cap,
+                                    int32_t* split_offsets, int32_t offsets_cap, dkv_plan_info* info);
 
 dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                                   const void* q, const int32_t* q_start, const int32_t* q_pos0,
@@ -273,7 +297,7 @@ typedef struct dkv_tuning {
   int32_t dev_wgs;       /* workgroups for the HBM tier (0: default) */
   int32_t host_chunk;    /* tokens per host work item, multiple of 64 (0: auto) */
   int32_t dev_chunk;     /* tokens per HBM work item, multiple of 64 (0: auto) */
-  int32_t reserved;
+  int32_t stage_max_mib;  /* prefill: HBM staging budget in MiB (0: 4096, < 0: never stage) */
   double host_bw_gbs;    /* host-link read bandwidth (0: 57) */
   double dev_bw_gbs;     /* HBM read bandwidth (0: 5300) */
 } dkv_tuning;
@@ -306,13 +330,15 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
  * returns how many launches were timed and their summed duration in ms, and
  * clears the record.  kernel: DKV_KERNEL_ATTN (split attention),
  * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
- * DKV_KERNEL_PREFILL (causal prefill attention).
+ * DKV_KERNEL_PREFILL (causal prefill attention), DKV_KERNEL_STAGE (prefill's
+ * copy of re-read host rows into HBM).
  * ---------------------------------------------------------------------- */
 #define DKV_KERNEL_ATTN 0
 #define DKV_KERNEL_ROPE_Q 1
 #define DKV_KERNEL_MERGE 2
 #define DKV_KERNEL_APPEND 3
 #define DKV_KERNEL_PREFILL 4
+#define DKV_KERNEL_STAGE 5
 
 dkv_status dkv_kernel_timing(int32_t enable);
 

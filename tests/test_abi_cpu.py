@@ -42,11 +42,37 @@ def test_every_declared_function_is_exported_and_bound(L):
     assert set(dkv_lib.SIGNATURES) == set(names)
 
 
-def test_struct_sizes_match_header_layout():
-    # dkv_kv_desc: 4 int32, 4 int64, 6 pointers; dkv_plan_info: 1 int64, 7 int32, 2 int64
-    assert C.sizeof(dkv_lib.KvDesc) == 4 * 4 + 4 * 8 + 6 * 8
-    assert C.sizeof(dkv_lib.PlanInfo) == 8 + 7 * 4 + 4 + 2 * 8  # padding after the int32 run
-    assert C.sizeof(dkv_lib.Tuning) == 6 * 4 + 2 * 8
+def _c_layout(struct, fields):
+    """sizeof and offsetof of a struct of include/dkv.h, from the C compiler."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler to read the header's layout")
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"dkv.h\"\nint main(void){\n"
+    src += f'printf("%zu\\n", sizeof({struct}));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        with open(os.path.join(d, "l.c"), "w") as fh:
+            fh.write(src)
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), os.path.join(d, "l.c"), "-o",
+                        os.path.join(d, "l")], check=True)
+        out = subprocess.run([os.path.join(d, "l")], check=True, capture_output=True, text=True).stdout
+    v = [int(x) for x in out.split()]
+    return v[0], v[1:]
+
+
+@pytest.mark.parametrize("struct,cls", [("dkv_kv_desc", "KvDesc"), ("dkv_plan_info", "PlanInfo"),
+                                        ("dkv_tuning", "Tuning"), ("dkv_bw_result", "BwResult")])
+def test_struct_layouts_match_header(struct, cls):
+    t = getattr(dkv_lib, cls)
+    names = [n for n, _ in t._fields_]
+    size, offs = _c_layout(struct, names)
+    assert C.sizeof(t) == size
+    assert [getattr(t, n).offset for n in names] == offs
 
 
 def test_version_and_last_error(L):

@@ -187,6 +187,34 @@ def test_merge_lse_against_oracle(dk):
             assert np.abs(o[b] - ro).max() < 1e-5 and np.abs(lse[b] - rl).max() < 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_lse_many_pairs(dk, d):
+    # >= 2048 (b, h) pairs takes the one-wave-per-pair merge
+    import torch
+    rng = np.random.default_rng(12)
+    B, hq = 300, 8
+    counts = rng.integers(0, 4, size=B)
+    counts[:4] = [0, 1, 70, 2]
+    S = int(counts.sum())
+    po = rng.standard_normal((S, hq, d)).astype(np.float32)
+    pl = (rng.standard_normal((S, hq)) * 5).astype(np.float32)
+    pl[rng.random((S, hq)) < 0.05] = -np.inf
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    o, lse = dk.merge_lse(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                          torch.from_numpy(offs).cuda(), B, hq, d)
+    o = o.cpu().numpy(); lse = lse.cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    fin = np.isfinite(pl[offs[1]])
+    assert np.array_equal(o[1][fin], po[offs[1]][fin])      # one split: returned exactly
+    for b in range(1, B):
+        ro, rl = O.merge_lse(po[offs[b]:offs[b + 1]].astype(np.float64),
+                             pl[offs[b]:offs[b + 1]].astype(np.float64))
+        assert np.abs(o[b] - ro).max() < 1e-5, b
+        assert np.array_equal(np.isneginf(lse[b]), np.isneginf(rl)), b
+        f = np.isfinite(rl)
+        assert np.abs(lse[b][f] - rl[f]).max(initial=0) < 1e-5, b
+
+
 # ----------------------------------------------------------------------- paged
 
 @pytest.mark.parametrize("lens,hq,hkv,d,frac", [

@@ -111,3 +111,50 @@ def test_prefill_rows_deep_in_a_long_cache(dk):
     ro, rl = O.prefill_sequence(qb, ks[0], vs[0], q_pos0, th, 1 / math.sqrt(d), heads=heads)
     _check(o[:, heads], lse[:, heads], ro, rl, "deep rows")
     cache.free()
+
+
+def test_prefill_staged_equals_direct(dk):
+    # host rows read by several row blocks: staged copy vs direct host reads
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, news, hq, hkv, d, r, th = [700, 300], [300, 300], 32, 8, 128, 0.8, 5e5
+    ks, vs = kv_raw(84, lens, hkv, d)
+    qs = [normal_bf16(84 + b, 1, (n, hq, d)) for b, n in enumerate(news)]
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    outs = []
+    try:
+        for mib in (0, -1):
+            dk.set_tuning(stage_max_mib=mib)
+            o, lse, bufs = _prefill(dk, cache, qs, q_start, q_pos0, lens, r, th, d)
+            print("stage_max_mib", mib, "staged bytes", bufs.info["staged_bytes"], flush=True)
+            assert (bufs.info["staged_bytes"] > 0) == (mib == 0)
+            outs.append((o, lse))
+    finally:
+        dk.reset_tuning()
+    assert np.abs(outs[0][0] - outs[1][0]).max() < 1e-5
+    assert np.abs(outs[0][1] - outs[1][1]).max() < 1e-5
+    for b in range(2):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], q_pos0[b], th, 1 / math.sqrt(d))
+        _check(outs[0][0][q_start[b]:q_start[b + 1]], outs[0][1][q_start[b]:q_start[b + 1]], ro, rl,
+               f"staged seq {b}")
+    cache.free()
+
+
+@pytest.mark.parametrize("ratio", [1.0, 0.0])
+def test_prefill_llama3_2k_full_size(dk, ratio):
+    # LLaMA-3-8B layer shape, 2048 new rows over an all-new cache: sampled rows
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    L, hq, hkv, d, th = 2048, 32, 8, 128, 5e5
+    ks, vs = kv_raw(0, [L], hkv, d)
+    qb = normal_bf16(0, 1, (L, hq, d))
+    cache = contiguous_cache(hkv, d, [L], ratio, ks, vs, th)
+    o, lse, bufs = _prefill(dk, cache, [qb], np.array([0, L], dtype=np.int32), [0], [L], ratio, th, d)
+    rows = [0, 1, 2, 63, 64, 127, 1000, 2047]
+    heads = [0, 3, 17, 31]
+    for r in rows:
+        ro, rl = O.prefill_sequence(qb[r:r + 1], ks[0][:r + 1], vs[0][:r + 1], r, th, 1 / math.sqrt(d),
+                                    heads=heads)
+        _check(o[r:r + 1, heads], lse[r:r + 1, heads], ro, rl, f"r={ratio} row {r}")
+    cache.free()
