@@ -448,13 +448,20 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
         kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
         dk.kernel_timing(False)
         pf_ms = kt["prefill"][1] / max(1, kt["prefill"][0])
+        st_ms = kt["stage"][1] / max(1, kt["stage"][0])
         info = bufs.info
         reads = info["host_bytes"] + info["dev_bytes"]
+        # MFMA work executed: Q.K and P.V each run twice (high and low bf16
+        # parts of the fp32 operand), so the executed rate is 2x the useful one
         out.append({"ratio": r, "new_tokens": T, "ms_per_step": round(ms, 4),
                     "prefill_kernel_ms": round(pf_ms, 4),
                     "useful_tflops": round(flops / (pf_ms * 1e9), 2),
-                    "frac_bf16_mfma_peak": round(flops / (pf_ms * 1e9) / 2500.0, 4),
+                    "frac_bf16_mfma_peak_useful": round(flops / (pf_ms * 1e9) / 2500.0, 4),
+                    "frac_bf16_mfma_peak_executed": round(2 * flops / (pf_ms * 1e9) / 2500.0, 4),
                     "kv_reads_host_bytes": info["host_bytes"], "kv_reads_hbm_bytes": info["dev_bytes"],
+                    "staged_bytes": info["staged_bytes"],
+                    "stage_kernel_ms": round(st_ms, 4),
+                    "stage_link_gbs": round(info["staged_bytes"] / (st_ms * 1e6), 1) if st_ms > 0 else None,
                     "kv_read_gbs": round(reads / (pf_ms * 1e6), 1),
                     "kernel_ms": {k: round(v[1] / max(1, v[0]), 5) for k, v in kt.items()},
                     "plan": {k: info[k] for k in ("num_splits", "host_wgs", "dev_wgs", "host_chunk", "dev_chunk")}})
