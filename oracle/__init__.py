@@ -29,4 +29,7 @@ from .dkv_oracle import (  # noqa: F401
     decode_batch,
     prefill_sequence,
     append_expected_rows,
+    linear,
+    linear_split_rows,
+    linear_split,
 )

@@ -94,3 +94,8 @@ def prefill_py(q_rot, k, v, pos, scale):
         outs.append(o)
         lses.append(l)
     return outs, lses
+
+
+def linear_py(x, w):
+    """x [M][K] times W^T for W [N][K] (nested lists) -> [M][N]."""
+    return [[dot_py(xm, wn) for wn in w] for xm in x]

@@ -321,3 +321,25 @@ def prefill_sequence(q_bits, k_raw_bits, v_bits, q_pos0: int, theta: float, scal
                 o[r0:r1, j, :] = (e / z) @ vv
                 lse[r0:r1, j] = (m + np.log(z))[:, 0]
     return o, lse
+
+
+# ---------------------------------------------------------------- offloaded linear
+
+def linear(x_bits, w_bits) -> np.ndarray:
+    """Offloaded linear layer, y = x W^T (SplitKernel README, Overview and Key
+    Features: weights fetched directly from the remote tier for an offloaded
+    linear).  Reading: W is stored like a PyTorch linear weight, [out][in]
+    bf16; x is [M][in] bf16; no bias; y [M][out] in float64."""
+    return bf16_to_f64(x_bits) @ bf16_to_f64(w_bits).T
+
+
+def linear_split_rows(ratio: float, out_features: int) -> int:
+    """Output rows of W held in host memory: the first floor(r * N) rows (the
+    same IEEE-double rule as the KV split; SplitKernel README, Usage:
+    placement and offloading-ratio utilities)."""
+    return contig_split_point(ratio, out_features)
+
+
+def linear_split(x_bits, w_host_bits, w_dev_bits) -> np.ndarray:
+    """y for W split by output rows: host rows first, then HBM rows."""
+    return np.concatenate([linear(x_bits, w_host_bits), linear(x_bits, w_dev_bits)], axis=1)

@@ -121,6 +121,42 @@ def test_projection_matches_scalar_twin_and_is_linear():
     assert np.array_equal(O.project(e, w)[0], w[3])
 
 
+# ------------------------------------------------------------------ offloaded linear
+
+def test_linear_matches_scalar_twin():
+    # catches a transposed or wrongly indexed weight (N != K here)
+    xb = normal_bf16(31, 1, (3, 8))
+    wb = normal_bf16(31, 2, (5, 8))
+    y = O.linear(xb, wb)
+    assert y.shape == (3, 5)
+    ref = BR.linear_py(O.bf16_to_f64(xb).tolist(), O.bf16_to_f64(wb).tolist())
+    np.testing.assert_allclose(y, ref, atol=1e-12)
+
+
+def test_linear_closed_forms():
+    one = bf16_bits_from_f32(np.ones((1, 6), np.float32))
+    # all-ones: every output is the inner dimension
+    assert np.array_equal(O.linear(one, bf16_bits_from_f32(np.ones((4, 6), np.float32))), np.full((1, 4), 6.0))
+    # identity weight returns x exactly; a basis input reads one column of W
+    xb = normal_bf16(32, 1, (2, 6))
+    eye = bf16_bits_from_f32(np.eye(6, dtype=np.float32))
+    assert np.array_equal(O.linear(xb, eye), O.bf16_to_f64(xb))
+    wb = normal_bf16(32, 2, (4, 6))
+    e = np.zeros((1, 6), np.float32); e[0, 2] = 1.0
+    assert np.array_equal(O.linear(bf16_bits_from_f32(e), wb)[0], O.bf16_to_f64(wb)[:, 2])
+
+
+def test_linear_split_rows_and_concat(golden):
+    for c in golden["split_point"]["cases"]:
+        assert O.linear_split_rows(c["r"], c["L"]) == c["n_host"]
+    xb = normal_bf16(33, 1, (3, 16))
+    wb = normal_bf16(33, 2, (10, 16))
+    for r in (0.0, 0.3, 0.7, 1.0):
+        nh = O.linear_split_rows(r, 10)
+        np.testing.assert_array_equal(O.linear_split(xb, wb[:nh], wb[nh:]), O.linear(xb, wb))
+    assert O.linear_split_rows(0.7, 10) == 7 and O.linear_split_rows(1.0, 10) == 10
+
+
 # ------------------------------------------------------------------ attention
 
 def test_attention_golden(golden):
