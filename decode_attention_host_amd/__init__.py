@@ -21,6 +21,9 @@ from .api import (  # noqa: F401
     get_tuning,
     kernel_timing,
     kernel_timing_read,
+    linear_plan,
+    linear_plan_inspect,
+    OffloadedLinear,
     merge_lse,
     plan_inspect,
     prefill,

@@ -107,6 +107,9 @@ SIGNATURES = {
                                        P, I32, C.POINTER(PlanInfo)]),
     "dkv_decode_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, F32, F64, P, SZ, P, P,
                                     P, I32, P]),
+    "dkv_linear_plan": (I32, [I32, I32, I32, F64, C.POINTER(PlanInfo)]),
+    "dkv_linear_split": (I32, [P, P, I32, I32, F64, P, I32, P, P, SZ, P]),
+    "dkv_linear_plan_inspect": (I32, [I32, I32, F64, I32, P, I32, C.POINTER(PlanInfo)]),
     "dkv_merge_lse": (I32, [P, P, P, I32, I32, I32, P, P, P]),
     "dkv_host_alloc": (I32, [SZ, C.c_uint32, C.POINTER(P), C.POINTER(P)]),
     "dkv_host_free": (I32, [P]),
@@ -127,6 +130,7 @@ DKV_KERNEL_MERGE = 2
 DKV_KERNEL_APPEND = 3
 DKV_KERNEL_PREFILL = 4
 DKV_KERNEL_STAGE = 5
+DKV_KERNEL_LINEAR = 6
 
 _lib = None
 

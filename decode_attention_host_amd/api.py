@@ -331,7 +331,8 @@ def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True
 
 KERNELS = {"attn": _lib.DKV_KERNEL_ATTN, "rope_q": _lib.DKV_KERNEL_ROPE_Q,
            "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND,
-           "prefill": _lib.DKV_KERNEL_PREFILL, "stage": _lib.DKV_KERNEL_STAGE}
+           "prefill": _lib.DKV_KERNEL_PREFILL, "stage": _lib.DKV_KERNEL_STAGE,
+           "linear": _lib.DKV_KERNEL_LINEAR}
 
 
 def kernel_timing(enable: bool):
@@ -440,3 +441,68 @@ def prefill(cache: KVCache, q, q_start, q_pos0, seq_lens, ratio, scale, rope_the
         merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, T, Hq, D, out_o=bufs.out_o,
                   out_lse=bufs.out_lse, stream=stream)
     return bufs.out_o[:T], bufs.out_lse[:T], bufs
+
+
+# ------------------------------------------------------------------ offloaded linear
+
+def linear_plan(m: int, out_features: int, in_features: int, ratio: float) -> dict:
+    """dkv_linear_plan."""
+    info = PlanInfo()
+    check(lib().dkv_linear_plan(int(m), int(out_features), int(in_features), float(ratio), C.byref(info)))
+    return info.as_dict()
+
+
+def linear_plan_inspect(out_features: int, in_features: int, ratio: float, num_cus: int):
+    """dkv_linear_plan_inspect: (items [n][6] int32, info)."""
+    info = PlanInfo()
+    check(lib().dkv_linear_plan_inspect(int(out_features), int(in_features), float(ratio), int(num_cus), None, 0,
+                                        C.byref(info)))
+    n = info.host_items + info.dev_items
+    items = np.zeros((max(n, 1), 6), dtype=np.int32)
+    check(lib().dkv_linear_plan_inspect(int(out_features), int(in_features), float(ratio), int(num_cus),
+                                        _ptr(items), n, C.byref(info)))
+    return items[:n], info.as_dict()
+
+
+class OffloadedLinear:
+    """A linear weight W [N][K] bf16 split by output rows: the first
+    floor(r N) rows in mapped host memory, the rest in an HBM tensor."""
+
+    def __init__(self, w_bits: np.ndarray, ratio: float, device="cuda", host_flags: int = DKV_HOST_COHERENT):
+        w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+        self.out_features, self.in_features = (int(v) for v in w_bits.shape)
+        self.ratio = float(ratio)
+        self.n_host = split_point(self.ratio, self.out_features)
+        K = self.in_features
+        self.host = None
+        if self.n_host > 0:
+            self.host = HostBuffer(self.n_host * K * 2, host_flags)
+            self.host.numpy(np.uint16, (self.n_host, K))[:] = w_bits[: self.n_host]
+        nd = self.out_features - self.n_host
+        self.dev = torch.from_numpy(w_bits[self.n_host:].view(np.int16).copy()).to(device) if nd > 0 else None
+        self._ws = None
+
+    def plan(self, m: int) -> dict:
+        return linear_plan(m, self.out_features, self.in_features, self.ratio)
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+        """y = x W^T for x [m][K] bf16 (int16 bits) on the device; returns y [m][N] fp32."""
+        m = int(x.shape[0])
+        if y is None:
+            y = torch.empty((m, self.out_features), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            need = max(256, self.plan(m)["workspace_bytes"])
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = self._ws
+        check(lib().dkv_linear_split(C.c_void_p(self.host.dev_ptr if self.host else 0),
+                                     _ptr(self.dev), self.out_features, self.in_features, self.ratio,
+                                     _ptr(x), m, _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+        return y
+
+    def free(self):
+        if self.host is not None:
+            self.host.free()
+            self.host = None
+        self.dev = None

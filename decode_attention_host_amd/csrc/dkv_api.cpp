@@ -374,7 +374,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> pool;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[6];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[7];
 };
 
 Timing& timing() {
@@ -423,6 +423,56 @@ struct TimedLaunch {
     e0 = nullptr;
   }
 };
+
+// Offloaded-linear plan: tuning fields as for decode, cached by shape.
+dkv::PlanInput linear_input(double ratio, int32_t cus, const dkv_tuning& t) {
+  dkv::PlanInput in{};
+  in.ratio = ratio;
+  in.num_cus = cus;
+  in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  return in;
+}
+
+dkv_status validate_linear(int32_t m, int32_t n, int32_t k, double ratio) {
+  if (m < 1 || n < 1 || k < 1) return set_err(DKV_ERR_INVALID, "m, out_features and in_features must be >= 1");
+  if (k % 8) return set_err(DKV_ERR_INVALID, "in_features must be a multiple of 8 (got %d)", k);
+  if ((int64_t)m * n > ((int64_t)1 << 40)) return set_err(DKV_ERR_INVALID, "m * out_features too large");
+  return validate_ratio(ratio);
+}
+
+dkv_status get_linear_plan(int32_t n, int32_t k, double ratio, std::shared_ptr<PlanEntry>* out) {
+  uint64_t gen = 0;
+  const dkv_tuning t = tuning_snapshot(&gen);
+  int dev = 0;
+  int cus = t.num_cus;
+  if (cus <= 0) {
+    cus = device_cus(&dev);
+    if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
+  }
+  std::string key("linear");
+  put(key, dev); put(key, cus); put(key, gen); put(key, n); put(key, k); put(key, ratio);
+  if (auto hit = cache_find(key)) {
+    *out = hit;
+    return DKV_OK;
+  }
+  auto e = std::make_shared<PlanEntry>();
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_linear_plan(linear_input(ratio, cus, t), dkv::kLinMaxTokens, n, k, &e->lay, &blob, &err))
+    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  e->bytes = blob.size();
+  hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
+  if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
+  memcpy(e->pinned, blob.data(), e->bytes);
+  *out = cache_insert(key, e);
+  return DKV_OK;
+}
+
+size_t linear_ws_bytes(const dkv::PlanLayout& L) {
+  return L.blob_bytes + (size_t)L.num_splits * dkv::kLinMaxTokens * dkv::kLinRows * 4;
+}
 
 }  // namespace
 
@@ -702,6 +752,93 @@ dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32
   return ok();
 }
 
+dkv_status dkv_linear_plan(int32_t m, int32_t out_features, int32_t in_features, double offload_ratio,
+                           dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_linear(m, out_features, in_features, offload_ratio);
+  if (st != DKV_OK) return st;
+  std::shared_ptr<PlanEntry> e;
+  st = get_linear_plan(out_features, in_features, offload_ratio, &e);
+  if (st != DKV_OK) return st;
+  fill_info(e->lay, linear_ws_bytes(e->lay), info);
+  return ok();
+}
+
+dkv_status dkv_linear_plan_inspect(int32_t out_features, int32_t in_features, double offload_ratio,
+                                   int32_t num_cus, int32_t* items, int32_t items_cap, dkv_plan_info* info) {
+  dkv_status st = validate_linear(1, out_features, in_features, offload_ratio);
+  if (st != DKV_OK) return st;
+  if (num_cus < 1) return set_err(DKV_ERR_INVALID, "num_cus must be >= 1");
+  dkv::PlanLayout L;
+  std::vector<uint8_t> blob;
+  std::string err;
+  if (!dkv::build_linear_plan(linear_input(offload_ratio, num_cus, tuning_snapshot(nullptr)), dkv::kLinMaxTokens,
+                              out_features, in_features, &L, &blob, &err))
+    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
+  const dkv::LinearItem* it = reinterpret_cast<const dkv::LinearItem*>(blob.data());
+  for (int i = 0; items && i < L.n_host_items + L.n_dev_items && i < items_cap; ++i) {
+    int32_t* o = items + 6 * (size_t)i;
+    o[0] = it[i].pool; o[1] = it[i].row0; o[2] = it[i].n_rows; o[3] = it[i].k0; o[4] = it[i].k1; o[5] = it[i].slot;
+  }
+  if (info) fill_info(L, linear_ws_bytes(L), info);
+  return ok();
+}
+
+dkv_status dkv_linear_split(const void* host_w, const void* dev_w, int32_t out_features, int32_t in_features,
+                            double offload_ratio, const void* x, int32_t m, float* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  dkv_status st = validate_linear(m, out_features, in_features, offload_ratio);
+  if (st != DKV_OK) return st;
+  if (!x || !y || !workspace) return set_err(DKV_ERR_INVALID, "x, y and workspace are required");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (((uintptr_t)x | (uintptr_t)host_w | (uintptr_t)dev_w) % 16)
+    return set_err(DKV_ERR_INVALID, "x and the weights must be 16-byte aligned");
+  std::shared_ptr<PlanEntry> e;
+  st = get_linear_plan(out_features, in_features, offload_ratio, &e);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  if (L.n_host_items > 0 && !host_w) return set_err(DKV_ERR_INVALID, "host_w is required for offload_ratio > 0");
+  if (L.n_dev_items > 0 && !dev_w) return set_err(DKV_ERR_INVALID, "dev_w is required for offload_ratio < 1");
+  if (workspace_bytes < linear_ws_bytes(L))
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, linear_ws_bytes(L));
+  hipStream_t s = (hipStream_t)stream;
+  if (stream_capturing(s)) {
+    std::lock_guard<std::mutex> lk(cache().mu);
+    e->captured = true;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  dkv::LinearArgs a{};
+  a.host_items = reinterpret_cast<const dkv::LinearItem*>(ws);
+  a.dev_items = a.host_items + L.n_host_items;
+  a.counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
+  a.n_host_items = L.n_host_items;
+  a.n_dev_items = L.n_dev_items;
+  a.host_wgs = L.host_wgs;
+  a.dev_wgs = L.dev_wgs;
+  a.n = out_features;
+  a.k = in_features;
+  a.n_host = (int32_t)(L.host_bytes / 2 / in_features);
+  a.host_w = static_cast<const uint16_t*>(host_w);
+  a.dev_w = static_cast<const uint16_t*>(dev_w);
+  a.part = L.num_splits > 0 ? reinterpret_cast<float*>(ws + L.blob_bytes) : nullptr;
+  a.blocks = reinterpret_cast<const dkv::LinearBlock*>(ws + L.plist_off);
+  a.n_blocks = L.n_plist;
+  // tokens in launches of up to 64; each launch re-uploads the plan image
+  // (its counters start at zero)
+  for (int32_t m0 = 0; m0 < m; m0 += dkv::kLinMaxTokens) {
+    hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
+    if (he != hipSuccess) return hip_err(he, "plan upload");
+    a.m = std::min(dkv::kLinMaxTokens, m - m0);
+    a.x = static_cast<const uint16_t*>(x) + (size_t)m0 * in_features;
+    a.y = y + (size_t)m0 * out_features;
+    TimedLaunch tl(DKV_KERNEL_LINEAR, s);
+    he = (hipError_t)dkv::launch_linear(a, stream);
+    tl.done();
+    if (he != hipSuccess) return hip_err(he, "linear launch");
+  }
+  return ok();
+}
+
 size_t dkv_append_workspace_bytes(int32_t n_new, int32_t hidden, int32_t kv_dim) {
   if (n_new <= 0 || hidden <= 0 || kv_dim <= 0) return 0;
   const int64_t n_pad = ((int64_t)n_new + 15) / 16 * 16;
@@ -927,7 +1064,7 @@ dkv_status dkv_kernel_timing(int32_t enable) {
 }
 
 dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms) {
-  if (kernel < 0 || kernel > DKV_KERNEL_STAGE || !count || !total_ms)
+  if (kernel < 0 || kernel > DKV_KERNEL_LINEAR || !count || !total_ms)
     return set_err(DKV_ERR_INVALID, "kernel id in [0,4] and outputs required");
   Timing& t = timing();
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;

@@ -73,6 +73,27 @@ struct StageTile {
 static_assert(sizeof(StageTile) == 32, "StageTile layout");
 constexpr int kStageTileRows = 64;
 
+// Offloaded linear: an item is up to kLinRows output rows of one tier and a
+// range [k0, k1) of the reduction dimension; slot < 0 writes y directly.
+constexpr int kLinRows = 64;
+constexpr int kLinMaxTokens = 64;  // tokens per launch (4 MFMA row tiles)
+struct LinearItem {
+  int32_t row0;
+  int32_t n_rows;
+  int32_t k0;
+  int32_t k1;
+  int32_t slot;
+  int32_t pool;    // kPoolHost / kPoolDev
+  int32_t pad[2];
+};
+static_assert(sizeof(LinearItem) == 32, "LinearItem layout");
+struct LinearBlock {  // partial slots base .. base + n_splits - 1 of rows row0 ..
+  int32_t row0;
+  int32_t n_rows;
+  int32_t base;
+  int32_t n_splits;
+};
+
 // Host-side result of planning; the device image is `blob` (items, then the
 // page list, then split offsets), uploaded into the caller's workspace.
 struct PlanLayout {
@@ -222,6 +243,28 @@ struct PrefillArgs {
   float* part_lse;               // [S][Hq]
 };
 
+struct LinearArgs {
+  const LinearItem* host_items;
+  const LinearItem* dev_items;
+  int32_t* counters;             // [2], zero at launch
+  int32_t n_host_items;
+  int32_t n_dev_items;
+  int32_t host_wgs;
+  int32_t dev_wgs;
+  int32_t m;                     // tokens in this launch (<= kLinMaxTokens)
+  int32_t n;                     // out_features
+  int32_t k;                     // in_features
+  int32_t n_host;                // rows of W in host memory
+  const uint16_t* host_w;        // [n_host][K]
+  const uint16_t* dev_w;         // [N - n_host][K]
+  const uint16_t* x;             // [m][K]
+  float* y;                      // [m][N]
+  float* part;                   // [S][kLinMaxTokens][kLinRows]
+  const LinearBlock* blocks;
+  int32_t n_blocks;
+  int32_t pad;
+};
+
 // Arguments of the staging copy (host rows -> HBM staging pool).
 struct StageArgs {
   const StageTile* tiles;
@@ -241,6 +284,7 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream);
 int launch_stage(const StageArgs& a, int nwg, void* stream);
+int launch_linear(const LinearArgs& a, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_project(const ProjArgs& a, void* stream);
 int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
@@ -281,5 +325,11 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
 // positions [T], split offsets [T+1], counters.
 bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
                         PlanLayout* out, std::vector<uint8_t>* blob, std::string* err);
+
+// Offloaded-linear plan (in.ratio, tuning fields and num_cus used).  Device
+// image: host items, dev items, row blocks (n_plist of them at plist_off),
+// counters.
+bool build_linear_plan(const PlanInput& in, int32_t M, int32_t N, int32_t K, PlanLayout* out,
+                       std::vector<uint8_t>* blob, std::string* err);
 
 }  // namespace dkv

@@ -804,6 +804,128 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   }
 }
 
+// ---------------------------------------------------------------------------
+// Offloaded linear y = x W^T with W [N][K] split by output rows between host
+// memory (read in place, non-temporal) and HBM.  Workgroup = 4 waves; an item
+// is up to 64 rows (16 per wave) x a K range.  Per 32-wide k-step the wave
+// issues v_mfma_f32_16x16x32_bf16 with B = 16 rows of W (each lane's 16 bytes
+// loaded straight from its row into the operand register) and A = 16 tokens
+// of x staged in LDS; MT row tiles cover up to 16*MT tokens with one W load.
+// The W loads of the next 256-wide K chunk are issued before the current
+// chunk's MFMAs so ~64 KB per workgroup are in flight.
+// ---------------------------------------------------------------------------
+constexpr int kLinKC = 256;  // K per LDS staging round (8 k-steps)
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
+  constexpr int XP = kLinKC * 2 + 16;  // bytes per staged token row
+  __shared__ __attribute__((aligned(16))) uint8_t x_lds[MT * 16 * XP];
+  __shared__ int s_next;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, j4 = lane >> 4;
+  const bool host_role = (int)blockIdx.x < a.host_wgs;
+  const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
+  const int nwg = host_role ? a.host_wgs : a.dev_wgs;
+  const int nunits = host_role ? a.n_host_items : a.n_dev_items;
+  const LinearItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
+  int* counter = a.counters + (host_role ? 1 : 0);
+  const uint16_t* __restrict__ wpool = host_role ? a.host_w : a.dev_w;
+  const int row_shift = host_role ? 0 : a.n_host;
+
+  u32x4 wf[2][8];
+  auto load_w = [&](const LinearItem& it, int kc, u32x4* dst) {
+    const int r = wave * 16 + n;
+    const int64_t row = (int64_t)(it.row0 - row_shift + (r < it.n_rows ? r : 0));
+    const uint16_t* base = wpool + row * a.k;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = kc + s * 32 + j4 * 8;
+      const bool ok = k < it.k1;
+      const u32x4* p = reinterpret_cast<const u32x4*>(base + (ok ? k : it.k0));
+      dst[s] = host_role ? __builtin_nontemporal_load(p) : *p;
+      if (!ok) dst[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  int u = wg;
+  LinearItem it{};
+  if (u < nunits) {
+    it = items[u];
+    load_w(it, it.k0, wf[0]);
+  }
+  int buf = 0;
+  while (u < nunits) {
+    floatx4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    int next_u = nunits;
+    LinearItem nit{};
+    for (int kc = it.k0; kc < it.k1; kc += kLinKC) {
+      __syncthreads();  // previous chunk's x readers are done
+      // stage x[0 .. 16 MT)[kc .. kc + 256) (zero past m or k1)
+      for (int c = tid; c < MT * 16 * (kLinKC / 8); c += kThreads) {
+        const int tok = c / (kLinKC / 8), kk = (c % (kLinKC / 8)) * 8;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (tok < a.m && kc + kk < it.k1) v = *reinterpret_cast<const u32x4*>(a.x + (size_t)tok * a.k + kc + kk);
+        *reinterpret_cast<u32x4*>(x_lds + tok * XP + kk * 2) = v;
+      }
+      const bool last = kc + kLinKC >= it.k1;
+      if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
+      __syncthreads();
+      if (!last) {
+        load_w(it, kc + kLinKC, wf[buf ^ 1]);
+      } else {
+        next_u = s_next;
+        if (next_u < nunits) {
+          nit = items[next_u];
+          load_w(nit, nit.k0, wf[buf ^ 1]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wf[buf][s]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const bf16x8_t xa = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4*>(x_lds + (t * 16 + n) * XP + (s * 32 + j4 * 8) * 2));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, acc[t], 0, 0, 0);
+        }
+      }
+      buf ^= 1;
+    }
+    // lane (n + 16 j4) holds y[token 16 t + 4 j4 + i][row n of this wave]
+    const int r = wave * 16 + n;
+    if (r < it.n_rows) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t * 16 + j4 * 4 + i;
+          if (tok >= a.m) continue;
+          if (it.slot < 0)
+            a.y[(size_t)tok * a.n + it.row0 + r] = acc[t][i];
+          else
+            a.part[((size_t)it.slot * kLinMaxTokens + tok) * kLinRows + r] = acc[t][i];
+        }
+    }
+    u = next_u;
+    it = nit;
+  }
+}
+
+// Sum of each row block's K-range partials, in slot order.
+__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(LinearArgs a) {
+  const int64_t total = (int64_t)a.n_blocks * a.m * kLinRows;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int r = (int)(i % kLinRows);
+    const int tok = (int)((i / kLinRows) % a.m);
+    const LinearBlock b = a.blocks[i / ((int64_t)kLinRows * a.m)];
+    if (r >= b.n_rows) continue;
+    float s = 0.f;
+    for (int j = 0; j < b.n_splits; ++j) s += a.part[((size_t)(b.base + j) * kLinMaxTokens + tok) * kLinRows + r];
+    a.y[(size_t)tok * a.n + b.row0 + r] = s;
+  }
+}
+
 // Staging copy of host-tier rows into the HBM pool: tile after tile, 16-byte
 // non-temporal loads from the mapped host memory, eight in flight per lane.
 __global__ __launch_bounds__(kThreads) void stage_copy_kernel(StageArgs a) {
@@ -1274,6 +1396,24 @@ int launch_stage(const StageArgs& a, int nwg, void* stream) {
   if (a.n_tiles <= 0) return (int)hipSuccess;
   nwg = std::max(1, std::min(nwg, a.n_tiles));
   hipLaunchKernelGGL(stage_copy_kernel, dim3(nwg), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_linear(const LinearArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = a.host_wgs + a.dev_wgs;
+  if (grid <= 0 || a.m < 1 || a.m > kLinMaxTokens) return (int)hipErrorInvalidValue;
+  if (a.m <= 16)
+    hipLaunchKernelGGL(linear_split_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.m <= 32)
+    hipLaunchKernelGGL(linear_split_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(linear_split_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.part == nullptr) return (int)e;
+  const int64_t total = (int64_t)a.n_blocks * a.m * kLinRows;
+  const int rg = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3(rg), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -46,6 +46,34 @@ int32_t choose_chunk(int64_t tier_token_heads, int32_t wgs, int32_t units_per_wg
   return (int32_t)round_up(c, align);
 }
 
+// Workgroups per tier for a launch whose tiers stream host_units and
+// dev_units (any common unit).  Measured on MI355X: 48-64 workgroups keep
+// PCIe 5.0 x16 full for a host tier alone; while HBM streams at the same
+// time, every extra host workgroup costs HBM throughput, so a balanced split
+// uses cus/16 (never below the bandwidth-proportional share of the resident
+// slots); HBM workgroups fill the remaining slots.
+void split_workgroups(const PlanInput& in, int64_t host_units, int64_t dev_units, int32_t* wh_out,
+                      int32_t* wd_out) {
+  const int32_t cus = std::max(1, in.num_cus);
+  const int32_t resident = cus * kSlotsPerCu;
+  const double bw_h = in.host_bw > 0 ? in.host_bw : 57.0;
+  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5300.0;
+  int32_t wh = 0, wd = 0;
+  if (host_units > 0 && dev_units > 0) {
+    const bool host_dominant = (double)host_units / bw_h > 1.5 * (double)dev_units / bw_d;
+    const int32_t want_h = in.host_wgs > 0 ? in.host_wgs : (host_dominant ? std::max(8, cus * 3 / 16) : std::max(4, cus / 16));
+    wh = std::max(want_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d)));
+    wh = std::min(wh, resident / 2);
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
+  } else if (host_units > 0) {
+    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 4);
+  } else if (dev_units > 0) {
+    wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
+  }
+  *wh_out = wh;
+  *wd_out = wd;
+}
+
 }  // namespace
 
 bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
@@ -104,28 +132,8 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
   }
 
   // ---- workgroup split between tiers
-  // Measured on MI355X: 48-64 workgroups keep PCIe 5.0 x16 full for a host
-  // tier alone; while HBM streams at the same time, every extra host
-  // workgroup costs HBM throughput, so a balanced split uses 16.
-  const int32_t cus = std::max(1, in.num_cus);
-  const int32_t resident = cus * kSlotsPerCu;
-  const double bw_h = in.host_bw > 0 ? in.host_bw : 57.0;
-  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5300.0;
-  const double t_h = (double)host_tok / bw_h;   // relative tier times
-  const double t_d = (double)dev_tok / bw_d;
   int32_t wh = 0, wd = 0;
-  if (host_tok > 0 && dev_tok > 0) {
-    const bool host_dominant = t_h > 1.5 * t_d;
-    const int32_t want_h = in.host_wgs > 0 ? in.host_wgs : (host_dominant ? std::max(8, cus * 3 / 16) : std::max(4, cus / 16));
-    // never below the bandwidth-proportional share of the resident slots
-    wh = std::max(want_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d)));
-    wh = std::min(wh, resident / 2);
-    wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
-  } else if (host_tok > 0) {
-    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 4);
-  } else {
-    wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
-  }
+  split_workgroups(in, host_tok, dev_tok, &wh, &wd);
 
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
   const bool mixed = host_tok > 0 && dev_tok > 0;
@@ -337,21 +345,8 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   }
 
   // ---- workgroup split (same rules as decode) and chunk sizes
-  const int32_t cus = std::max(1, in.num_cus);
-  const int32_t resident = cus * kSlotsPerCu;
-  const double bw_h = in.host_bw > 0 ? in.host_bw : 57.0;
-  const double bw_d = in.dev_bw > 0 ? in.dev_bw : 5300.0;
   int32_t wh = 0, wd = 0;
-  if (host_reads > 0 && dev_reads > 0) {
-    const bool host_dominant = (double)host_reads / bw_h > 1.5 * (double)dev_reads / bw_d;
-    const int32_t want_h = in.host_wgs > 0 ? in.host_wgs : (host_dominant ? std::max(8, cus * 3 / 16) : std::max(4, cus / 16));
-    wh = std::min(std::max(want_h, (int32_t)std::lround(resident * bw_h / (bw_h + bw_d))), resident / 2);
-    wd = in.dev_wgs > 0 ? in.dev_wgs : resident - wh;
-  } else if (host_reads > 0) {
-    wh = in.host_wgs > 0 ? in.host_wgs : std::max(8, cus / 4);
-  } else {
-    wd = in.dev_wgs > 0 ? in.dev_wgs : resident;
-  }
+  split_workgroups(in, host_reads, dev_reads, &wh, &wd);
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
   const int32_t ch = choose_chunk(host_reads * in.hkv, wh, 4, 256, 16384, align, in.host_chunk);
   // A prefill token-head costs a full 128-row MFMA pass, so HBM units are
@@ -475,6 +470,85 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     if (!tiles.empty()) memcpy(p + out->stage_tiles_off, tiles.data(), tiles.size() * sizeof(StageTile));
     if (T) memcpy(p + out->rowpos_off, rowpos.data(), T * sizeof(int32_t));
     memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------- linear
+//
+// SplitKernel README, Overview / Key Features: an offloaded linear layer reads
+// its weights directly from the remote tier.  W [N][K] is split by output
+// rows: rows [0, floor(r N)) in host memory, the rest in HBM.  An item is a
+// block of up to kLinRows rows of one tier and a range of the reduction
+// dimension; blocks split over K write partials that a reduce kernel sums
+// in a fixed order.
+bool build_linear_plan(const PlanInput& in, int32_t M, int32_t N, int32_t K, PlanLayout* out,
+                       std::vector<uint8_t>* blob, std::string* err) {
+  *out = PlanLayout{};
+  if (M < 1 || N < 1 || K < 1) return fail(err, "m, out_features and in_features must be >= 1");
+  if (K % 8) return fail(err, "in_features must be a multiple of 8 (got %lld)", K);
+  const int64_t nh = (int64_t)std::floor(in.ratio * (double)N);
+  const int64_t nd = N - nh;
+  const int64_t bh = ceil_div(nh, kLinRows), bd = ceil_div(nd, kLinRows);
+  int32_t wh = 0, wd = 0;
+  split_workgroups(in, nh * K, nd * K, &wh, &wd);
+  // K ranges per block: about two units per workgroup, ranges of >= 1024
+  auto splits = [&](int64_t blocks, int32_t wgs, int32_t tuned) -> int64_t {
+    if (blocks == 0) return 1;
+    if (tuned > 0) return std::max<int64_t>(1, ceil_div(K, round_up(tuned, 32)));
+    const int64_t c = ceil_div(2 * (int64_t)wgs, blocks);
+    return std::max<int64_t>(1, std::min<int64_t>(c, std::max<int64_t>(1, K / 1024)));
+  };
+  const int64_t ch = splits(bh, wh, in.host_chunk), cd = splits(bd, wd, in.dev_chunk);
+  const int64_t kh = round_up(ceil_div(K, ch), 32), kd = round_up(ceil_div(K, cd), 32);
+  const bool partial = ceil_div(K, kh) > 1 || ceil_div(K, kd) > 1;
+  std::vector<LinearItem> hitems, ditems;
+  std::vector<LinearBlock> blocks;
+  int64_t slot = 0;
+  for (int tier = 1; tier >= 0; --tier) {
+    const int64_t r0 = tier ? 0 : nh, r1 = tier ? nh : N;
+    const int64_t kc = tier ? kh : kd;
+    for (int64_t r = r0; r < r1; r += kLinRows) {
+      LinearBlock blk{};
+      blk.row0 = (int32_t)r;
+      blk.n_rows = (int32_t)std::min<int64_t>(kLinRows, r1 - r);
+      blk.base = (int32_t)slot;
+      for (int64_t k = 0; k < K; k += kc) {
+        LinearItem it{};
+        it.row0 = blk.row0;
+        it.n_rows = blk.n_rows;
+        it.k0 = (int32_t)k;
+        it.k1 = (int32_t)std::min<int64_t>(K, k + kc);
+        it.slot = partial ? (int32_t)slot++ : -1;
+        it.pool = tier ? kPoolHost : kPoolDev;
+        (tier ? hitems : ditems).push_back(it);
+        ++blk.n_splits;
+      }
+      blocks.push_back(blk);
+    }
+  }
+  if (slot > INT32_MAX / (kLinRows * kLinMaxTokens)) return fail(err, "too many linear partials");
+  out->n_host_items = (int32_t)hitems.size();
+  out->n_dev_items = (int32_t)ditems.size();
+  out->num_splits = (int32_t)slot;
+  out->host_wgs = hitems.empty() ? 0 : (int32_t)std::min<int64_t>(wh, (int64_t)hitems.size());
+  out->dev_wgs = ditems.empty() ? 0 : (int32_t)std::min<int64_t>(std::max(wd, 1), (int64_t)ditems.size());
+  out->host_chunk = hitems.empty() ? 0 : (int32_t)kh;
+  out->dev_chunk = ditems.empty() ? 0 : (int32_t)kd;
+  out->host_bytes = nh * K * 2;
+  out->dev_bytes = nd * K * 2;
+  out->n_plist = (int32_t)blocks.size();
+  out->items_off = 0;
+  out->plist_off = round_up((hitems.size() + ditems.size()) * sizeof(LinearItem), 16);
+  out->counters_off = round_up(out->plist_off + blocks.size() * sizeof(LinearBlock), 16);
+  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
+  if (blob) {
+    blob->assign(out->blob_bytes, 0);
+    uint8_t* p = blob->data();
+    if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(LinearItem));
+    if (!ditems.empty())
+      memcpy(p + hitems.size() * sizeof(LinearItem), ditems.data(), ditems.size() * sizeof(LinearItem));
+    if (!blocks.empty()) memcpy(p + out->plist_off, blocks.data(), blocks.size() * sizeof(LinearBlock));
   }
   return true;
 }

@@ -256,6 +256,36 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
                                   int32_t num_splits_cap, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Offloaded linear layer read in place from both tiers (SplitKernel README,
+ * Overview and Key Features: GPU kernels fetch offloaded weights directly from
+ * the remote tier; an offloaded linear primitive).
+ *
+ *   y[i][n] = sum_k x[i][k] * W[n][k],  i < m, n < out_features, k < in_features
+ *
+ * W is [out_features][in_features] bf16 (a PyTorch linear weight), split by
+ * output rows with the KV rule: rows [0, n_host), n_host = floor(r * N) in IEEE
+ * double, are host_w (mapped host memory, its device address; row-major
+ * [n_host][K]); rows [n_host, N) are dev_w (HBM, [N - n_host][K]).  Either may
+ * be NULL when it holds no rows.  x [m][K] bf16 and y [m][N] fp32 are device
+ * memory; no bias; fp32 accumulation on MFMA.  in_features must be a multiple
+ * of 8; x and the weights 16-byte aligned.  Both tiers stream at once, each on
+ * its own workgroups; tokens run in launches of up to 64.  dkv_linear_plan
+ * gives the workspace size (plan image plus K-split partials).
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_linear_plan(int32_t m, int32_t out_features, int32_t in_features, double offload_ratio,
+                           dkv_plan_info* info);
+
+dkv_status dkv_linear_split(const void* host_w, const void* dev_w, int32_t out_features, int32_t in_features,
+                            double offload_ratio, const void* x, int32_t m, float* y, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Linear planner introspection (no HIP calls; used by CPU tests): 6 int32 per
+ * item: pool (0 host, 1 HBM), first output row, rows, k0, k1, partial slot
+ * (-1: written to y directly).  info as for dkv_linear_plan. */
+dkv_status dkv_linear_plan_inspect(int32_t out_features, int32_t in_features, double offload_ratio,
+                                   int32_t num_cus, int32_t* items, int32_t items_cap, dkv_plan_info* info);
+
+/* ------------------------------------------------------------------------
  * LSE merge of partial results (the combine step implied by splitting one
  * sequence's KV over tiers and compute units: SplitKernel README, Key
  * Features; DirectKV README, Step 6, "SM-Parallel" kernel).
@@ -331,7 +361,7 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
  * clears the record.  kernel: DKV_KERNEL_ATTN (split attention),
  * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
  * DKV_KERNEL_PREFILL (causal prefill attention), DKV_KERNEL_STAGE (prefill's
- * copy of re-read host rows into HBM).
+ * copy of re-read host rows into HBM), DKV_KERNEL_LINEAR (offloaded linear).
  * ---------------------------------------------------------------------- */
 #define DKV_KERNEL_ATTN 0
 #define DKV_KERNEL_ROPE_Q 1
@@ -339,6 +369,7 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
 #define DKV_KERNEL_APPEND 3
 #define DKV_KERNEL_PREFILL 4
 #define DKV_KERNEL_STAGE 5
+#define DKV_KERNEL_LINEAR 6
 
 dkv_status dkv_kernel_timing(int32_t enable);
 

@@ -1,0 +1,85 @@
+"""GPU parity of the offloaded linear (W split by output rows between mapped
+host memory and HBM) against the fp64 oracle y = x W^T.
+
+Products of bf16 values are exact in fp32 and accumulate in fp32, so the bar
+is relative to the scale of the sum: |y - y_ref| <= 1e-5 * sqrt(K) * max|x||w|
+rows, with the 2e-3 absolute bar of the path as a ceiling.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import normal_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dk():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import decode_attention_host_amd as dk
+    dk.reset_tuning()
+    return dk
+
+
+def _run(dk, w, x, ratio):
+    import torch
+    lin = dk.OffloadedLinear(w, ratio)
+    y = lin(torch.from_numpy(x.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    out = y.cpu().numpy().astype(np.float64)
+    lin.free()
+    return out
+
+
+def _check(y, ref, K, what):
+    err = np.abs(y - ref).max()
+    tol = min(2e-3, 1e-5 * np.sqrt(K) * max(1.0, np.abs(ref).max() / np.sqrt(K)))
+    print(f"{what}: max|dy|={err:.3g} (tol {tol:.3g})", flush=True)
+    assert err <= tol, what
+
+
+CASES = [
+    # (m, N, K, ratio, w_std)
+    (1, 64, 64, 1.0, 1.0),
+    (1, 100, 264, 0.5, 1.0),        # ragged rows, K tail not a multiple of 32
+    (7, 1000, 1024, 0.3, 0.05),
+    (16, 4096, 4096, 0.0, 0.02),    # K split into partials
+    (17, 777, 2056, 0.9, 0.02),     # two token tiles
+    (64, 256, 512, 0.75, 1.0),      # four token tiles
+    (100, 300, 4096, 0.5, 0.02),    # two launches of tokens
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_linear_parity(dk, case):
+    m, N, K, r, std = CASES[case]
+    w = normal_bf16(90 + case, 5, (N, K), std=std)
+    x = normal_bf16(90 + case, 4, (m, K))
+    y = _run(dk, w, x, r)
+    _check(y, O.linear(x, w), K, f"case {case}")
+
+
+def test_linear_identity_weight_returns_x(dk):
+    from synth import bf16_bits_from_f32
+    K = 128
+    w = bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    x = normal_bf16(95, 4, (5, K))
+    y = _run(dk, w, x, 0.5)
+    assert np.array_equal(y, O.bf16_to_f64(x))
+
+
+def test_linear_ratios_agree_and_llama_mlp_full_size(dk):
+    # LLaMA-3-8B MLP up-projection shape, 16 tokens: every ratio gives the
+    # same result as r = 0 to fp32 summation-order noise; sampled rows vs oracle
+    N, K, m = 14336, 4096, 16
+    w = normal_bf16(96, 5, (N, K), std=0.02)
+    x = normal_bf16(96, 4, (m, K))
+    ys = {r: _run(dk, w, x, r) for r in (0.0, 0.5, 1.0)}
+    for r in (0.5, 1.0):
+        assert np.abs(ys[r] - ys[0.0]).max() < 1e-4
+    rows = np.random.default_rng(0).choice(N, 64, replace=False)
+    ref = O.linear(x, w[rows])
+    _check(ys[1.0][:, rows], ref, K, "llama mlp sampled rows r=1")
