@@ -469,6 +469,54 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
     return {"flops_per_step": flops, "per_ratio": out}
 
 
+def measure_linear(dk, cfg, seed, iters, bw_h, bw_d):
+    """Offloaded linear y = x W^T, W split by output rows; per (ratio, tokens):
+    median call time with a read-only cache flush between calls, effective
+    weight GB/s and the split roofline max(host_bytes/BW_h, hbm_bytes/BW_d)."""
+    import numpy as np
+    import torch
+    from synth import normal_bf16
+    N, K = cfg["out_features"], cfg["in_features"]
+    w = normal_bf16(seed, 5, (N, K), std=cfg["w_std"])
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    r_star = bw_h / (bw_h + bw_d)
+    out = []
+    for r in [0.0, r_star, 0.25, 0.5, 1.0]:
+        lin = dk.OffloadedLinear(w, r)
+        hb, db = lin.n_host * K * 2, (N - lin.n_host) * K * 2
+        for m in cfg["tokens"]:
+            x = torch.from_numpy(normal_bf16(seed, 4, (m, K)).view(np.int16)).cuda()
+            y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(256, lin.plan(m)["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+            gpu_warm(lambda: lin(x, y, ws), 0.2)
+            dk.kernel_timing(True)
+            dk.kernel_timing_read("linear")
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            sink = torch.empty(iters, dtype=torch.float32, device="cuda")
+            for i in range(iters):
+                torch.sum(flush, dim=0, out=sink[i])
+                ev[i][0].record()
+                lin(x, y, ws)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            n_k, k_ms = dk.kernel_timing_read("linear")
+            dk.kernel_timing(False)
+            times = sorted(a.elapsed_time(b) for a, b in ev)
+            med = statistics.median(times)
+            t_star = max(hb / (bw_h * 1e6), db / (bw_d * 1e6))
+            t_nom = max(hb / (PCIE_PEAK_GBS * 1e6), db / (HBM_PEAK_GBS * 1e6))
+            out.append({"ratio": round(r, 5), "tokens": m, "host_bytes": hb, "hbm_bytes": db,
+                        "ms_median": round(med, 4), "kernel_ms": round(k_ms / max(1, n_k), 4),
+                        "eff_weight_gbs": round((hb + db) / (med * 1e6), 1),
+                        "roofline_ms_measured": round(t_star, 4), "frac_measured": round(t_star / med, 3),
+                        "roofline_ms_nominal": round(t_nom, 4), "frac_nominal": round(t_nom / med, 3)})
+            log(f"[bench] linear r={r:.4f} m={m}: {med:.4f} ms, {out[-1]['eff_weight_gbs']} GB/s, "
+                f"frac(measured) {out[-1]['frac_measured']}")
+        lin.free()
+    del flush
+    return {"sweep": out}
+
+
 def load_traffic(workload_name):
     p = os.path.join(ROOT, "profiles", f"attn_{workload_name}_traffic.json")
     if not os.path.exists(p):
@@ -493,7 +541,8 @@ def main():
     ap.add_argument("--sweep-iters", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--tune", default="", help="comma list of dkv_tuning fields, e.g. host_wgs=256")
-    ap.add_argument("--extra", default="tiny,opt_6_7b_b8,fused_ragged,llama3_8b_1m,llama3_8b_prefill_2k",
+    ap.add_argument("--extra", default="tiny,opt_6_7b_b8,fused_ragged,llama3_8b_1m,llama3_8b_prefill_2k,"
+                                       "llama3_8b_mlp_up_linear",
                     help="other workloads measured after the headline ('' for none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: headline steps plus two calibration reads of known "
@@ -601,7 +650,11 @@ def main():
     for name in [x for x in args.extra.split(",") if x]:
         wcfg = workload(name, seed=args.seed)
         t0 = time.time()
-        if "new" in wcfg:
+        if wcfg.get("layout") == "linear":
+            bw_h = probe.get("host_zero_copy_gbs") or 50.0
+            bw_d = probe.get("hbm_read_gbs") or 5000.0
+            workloads[name] = measure_linear(dk, wcfg, args.seed, 20, bw_h, bw_d)
+        elif "new" in wcfg:
             workloads[name] = measure_prefill(dk, wcfg, args.seed, flags, 10, 3)
         elif name == "llama3_8b_1m":
             bw_h = probe.get("host_zero_copy_gbs") or 50.0

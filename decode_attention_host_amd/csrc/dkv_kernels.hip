@@ -807,21 +807,26 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 // ---------------------------------------------------------------------------
 // Offloaded linear y = x W^T with W [N][K] split by output rows between host
 // memory (read in place, non-temporal) and HBM.  Workgroup = 4 waves; an item
-// is up to 64 rows (16 per wave) x a K range.  Per 32-wide k-step the wave
-// issues v_mfma_f32_16x16x32_bf16 with B = 16 rows of W (each lane's 16 bytes
-// loaded straight from its row into the operand register) and A = 16 tokens
-// of x staged in LDS; MT row tiles cover up to 16*MT tokens with one W load.
-// The W loads of the next 256-wide K chunk are issued before the current
-// chunk's MFMAs so ~64 KB per workgroup are in flight.
+// is up to 64 rows (16 per wave) x a K range, walked in 256-wide chunks.  A
+// chunk of W (64 rows x 512 B) is loaded with every 32 lanes reading one row's
+// 512 contiguous bytes, prefetched into registers one chunk ahead, and staged
+// in LDS with x.  Per 32-wide k-step each wave issues
+// v_mfma_f32_16x16x32_bf16 with A = 16 tokens of x and B = its 16 rows of W,
+// both read from LDS; MT row tiles cover up to 16*MT tokens per W read.
 // ---------------------------------------------------------------------------
-constexpr int kLinKC = 256;  // K per LDS staging round (8 k-steps)
+constexpr int kLinKC = 256;  // K per chunk (8 k-steps)
 
 template <int MT>
 __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
-  constexpr int XP = kLinKC * 2 + 16;  // bytes per staged token row
+  constexpr int XP = kLinKC * 2 + 16;            // bytes per staged row (x token or W row)
+  constexpr int PASSES = kLinRows * kLinKC * 2 / 16 / kThreads;  // 16-byte W loads per thread per chunk
+  constexpr int RPP = kThreads / (kLinKC * 2 / 16);               // W rows per pass
   __shared__ __attribute__((aligned(16))) uint8_t x_lds[MT * 16 * XP];
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kLinRows * XP];
   __shared__ int s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, j4 = lane >> 4;
+  const int wr = tid / (kLinKC * 2 / 16);  // W staging: row within a pass
+  const int wc = tid % (kLinKC * 2 / 16);  //            16-byte column
   const bool host_role = (int)blockIdx.x < a.host_wgs;
   const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
   const int nwg = host_role ? a.host_wgs : a.dev_wgs;
@@ -831,18 +836,18 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
   const uint16_t* __restrict__ wpool = host_role ? a.host_w : a.dev_w;
   const int row_shift = host_role ? 0 : a.n_host;
 
-  u32x4 wf[2][8];
-  auto load_w = [&](const LinearItem& it, int kc, u32x4* dst) {
-    const int r = wave * 16 + n;
-    const int64_t row = (int64_t)(it.row0 - row_shift + (r < it.n_rows ? r : 0));
-    const uint16_t* base = wpool + row * a.k;
+  u32x4 wreg[PASSES];
+  // rows past the item read its first row, columns past k1 are zero
+  auto load_w = [&](const LinearItem& it, int kc) {
+    const int k = kc + wc * 8;
+    const bool kok = k < it.k1;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int k = kc + s * 32 + j4 * 8;
-      const bool ok = k < it.k1;
-      const u32x4* p = reinterpret_cast<const u32x4*>(base + (ok ? k : it.k0));
-      dst[s] = host_role ? __builtin_nontemporal_load(p) : *p;
-      if (!ok) dst[s] = u32x4{0u, 0u, 0u, 0u};
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = p * RPP + wr;
+      const int64_t row = (int64_t)(it.row0 - row_shift + (r < it.n_rows ? r : 0));
+      const u32x4* src = reinterpret_cast<const u32x4*>(wpool + row * a.k + (kok ? k : it.k0));
+      wreg[p] = host_role ? __builtin_nontemporal_load(src) : *src;
+      if (!kok) wreg[p] = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -850,9 +855,8 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
   LinearItem it{};
   if (u < nunits) {
     it = items[u];
-    load_w(it, it.k0, wf[0]);
+    load_w(it, it.k0);
   }
-  int buf = 0;
   while (u < nunits) {
     floatx4 acc[MT];
 #pragma unroll
@@ -860,8 +864,11 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
     int next_u = nunits;
     LinearItem nit{};
     for (int kc = it.k0; kc < it.k1; kc += kLinKC) {
-      __syncthreads();  // previous chunk's x readers are done
-      // stage x[0 .. 16 MT)[kc .. kc + 256) (zero past m or k1)
+      __syncthreads();  // previous chunk's readers are done
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p)
+        *reinterpret_cast<u32x4*>(w_lds + (p * RPP + wr) * XP + wc * 16) = wreg[p];
+      // x[0 .. 16 MT)[kc .. kc + 256) (zero past m or k1)
       for (int c = tid; c < MT * 16 * (kLinKC / 8); c += kThreads) {
         const int tok = c / (kLinKC / 8), kk = (c % (kLinKC / 8)) * 8;
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -872,17 +879,18 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
       if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
       __syncthreads();
       if (!last) {
-        load_w(it, kc + kLinKC, wf[buf ^ 1]);
+        load_w(it, kc + kLinKC);
       } else {
         next_u = s_next;
         if (next_u < nunits) {
           nit = items[next_u];
-          load_w(nit, nit.k0, wf[buf ^ 1]);
+          load_w(nit, nit.k0);
         }
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wf[buf][s]);
+      for (int s = 0; s < kLinKC / 32; ++s) {
+        const bf16x8_t wb = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4*>(w_lds + (wave * 16 + n) * XP + (s * 32 + j4 * 8) * 2));
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const bf16x8_t xa = __builtin_bit_cast(
@@ -890,7 +898,6 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, acc[t], 0, 0, 0);
         }
       }
-      buf ^= 1;
     }
     // lane (n + 16 j4) holds y[token 16 t + 4 j4 + i][row n of this wave]
     const int r = wave * 16 + n;

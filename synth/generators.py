@@ -142,9 +142,12 @@ def paged_table(seed: int, n_tokens, page: int, host_frac: float, max_pages: int
     return table, n_host_total, n_dev_total
 
 
-# The five workloads: shapes of LLaMA-3-8B / OPT-6.7B attention layers (DirectKV
+# The workloads: shapes of LLaMA-3-8B / OPT-6.7B attention layers (DirectKV
 # README, Artifact Evaluation "What is reproduced" table; SplitKernel README,
-# Overview and Key Features for the host/device split and offloading ratio).
+# Overview and Key Features for the host/device split and offloading ratio),
+# a 2048-row prefill of the LLaMA-3-8B layer, and the LLaMA-3-8B MLP
+# up-projection as the offloaded-linear workload (SplitKernel README, Key
+# Features: offloaded linear).
 CONFIGS = {
     "tiny": dict(batch=1, hq=4, hkv=2, d=64, lens=[512], ratio=1.0, theta=1e4,
                  layout="contig"),
@@ -157,6 +160,8 @@ CONFIGS = {
                          ratios=[0.0, 0.25, 0.5, 0.75, 0.9, 1.0]),
     "llama3_8b_prefill_2k": dict(batch=1, hq=32, hkv=8, d=128, lens=[2048], new=[2048], ratio=1.0,
                                  theta=5e5, layout="contig", ratios=[1.0, 0.0]),
+    "llama3_8b_mlp_up_linear": dict(out_features=14336, in_features=4096, tokens=[1, 16], w_std=0.02,
+                                    layout="linear"),
     "fused_ragged": dict(batch=16, hq=32, hkv=8, d=128, lens_range=(1024, 65536),
                          ratio=0.8, theta=5e5, layout="paged", page=16, hidden=4096,
                          w_std=0.02),
