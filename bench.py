@@ -54,9 +54,24 @@ def pcie_nominal_gbs(pci_bus_id: int | None):
 
 
 def kernel_src_sha():
+    """Hash of the split attention kernel's own source: its definition, its
+    launcher and the plan/argument structures it reads.  The stored traffic
+    figure of that kernel stays valid while this hash matches."""
+    import re
+    csrc = os.path.join(ROOT, "decode_attention_host_amd", "csrc")
+    k = open(os.path.join(csrc, "dkv_kernels.hip")).read()
+    h_src = open(os.path.join(csrc, "dkv_internal.h")).read()
+    a = k.index("__global__ __launch_bounds__(kThreads) void attn_split_kernel")
+    a = k.rindex("template", 0, a)
+    b = k.index("// ----", a)
+    parts = [k[a:b]]
+    parts += re.findall(r"static hipError_t launch_attn_d.*?\n}\n", k, re.S)
+    for struct in ("PlanItem", "AttnArgs"):
+        parts.append(re.search(r"struct %s \{.*?\n\};" % struct, h_src, re.S).group(0))
+    parts += re.findall(r"constexpr int k(?:Tile|Threads) = \d+;", h_src)
     h = hashlib.sha256()
-    for f in ("dkv_kernels.hip", "dkv_internal.h"):
-        h.update(open(os.path.join(ROOT, "decode_attention_host_amd", "csrc", f), "rb").read())
+    for x in parts:
+        h.update(x.encode())
     return h.hexdigest()[:16]
 
 
