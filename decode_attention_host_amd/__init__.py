@@ -28,6 +28,8 @@ from .api import (  # noqa: F401
     plan_inspect,
     prefill,
     prefill_attn_split,
+    prefill_fused,
+    prefill_fused_plan,
     prefill_plan,
     prefill_plan_inspect,
     probe_read,

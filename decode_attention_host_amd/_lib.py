@@ -103,8 +103,11 @@ SIGNATURES = {
     "dkv_decode_plan": (I32, [C.POINTER(KvDesc), I32, I32, P, F64, C.POINTER(PlanInfo)]),
     "dkv_plan_inspect": (I32, [C.POINTER(KvDesc), I32, I32, P, F64, I32, P, I32, P, I32, P,
                                C.POINTER(PlanInfo)]),
-    "dkv_prefill_plan_inspect": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, I32, P, I32, P, I32, P, I32,
-                                       P, I32, C.POINTER(PlanInfo)]),
+    "dkv_prefill_plan_inspect": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, I32, I32, P, I32, P, I32, P,
+                                       I32, P, I32, C.POINTER(PlanInfo)]),
+    "dkv_prefill_fused_plan": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, I32, C.POINTER(PlanInfo)]),
+    "dkv_prefill_fused": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, P, F64, F32, F64, P, I32, P, P, P, P, P, SZ,
+                                P, P, P]),
     "dkv_decode_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, F32, F64, P, SZ, P, P,
                                     P, I32, P]),
     "dkv_linear_plan": (I32, [I32, I32, I32, F64, C.POINTER(PlanInfo)]),

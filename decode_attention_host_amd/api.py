@@ -213,13 +213,14 @@ def plan_inspect(cache_or_desc, batch: int, num_q_heads: int, seq_lens, ratio: f
 
 
 def prefill_plan_inspect(cache_or_desc, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens,
-                         ratio: float, num_cus: int):
+                         ratio: float, num_cus: int, fused: bool = False):
     """dkv_prefill_plan_inspect: dict of items [n][11] int64, page pairs [m][2],
     staging tiles [k][3] int64, split_offsets [T+1] and the plan info."""
     d = cache_or_desc.desc() if isinstance(cache_or_desc, KVCache) else cache_or_desc
     qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
     info = PlanInfo()
-    args = (C.byref(d), int(batch), int(num_q_heads), _ptr(qs), _ptr(qp), _ptr(sl), float(ratio), int(num_cus))
+    args = (C.byref(d), int(batch), int(num_q_heads), _ptr(qs), _ptr(qp), _ptr(sl), float(ratio), int(bool(fused)),
+            int(num_cus))
     check(lib().dkv_prefill_plan_inspect(*args, None, 0, None, 0, None, 0, None, 0, C.byref(info)))
     n = info.host_items + info.dev_items
     T = int(qs[-1])
@@ -429,6 +430,41 @@ def prefill_attn_split(cache: KVCache, q: torch.Tensor, q_start, q_pos0, seq_len
         float(rope_theta), _ptr(bufs.workspace), bufs.workspace.numel(), _ptr(bufs.part_o),
         _ptr(bufs.part_lse), _ptr(bufs.split_offsets), int(bufs.part_o.shape[0]), _stream(stream)))
     return bufs
+
+
+def prefill_fused_plan(cache: KVCache, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens, ratio: float,
+                       hidden: int = 0) -> dict:
+    """dkv_prefill_fused_plan (host int32 arrays; hidden > 0 with projection)."""
+    d = cache.desc()
+    qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
+    info = PlanInfo()
+    check(lib().dkv_prefill_fused_plan(C.byref(d), int(batch), int(num_q_heads), _ptr(qs), _ptr(qp), _ptr(sl),
+                                       float(ratio), int(hidden), C.byref(info)))
+    return info.as_dict()
+
+
+def prefill_fused(cache: KVCache, q: torch.Tensor, q_start, q_pos0, seq_lens, ratio: float, scale: float,
+                  rope_theta: float, *, k_new=None, v_new=None, x=None, wk=None, wv=None, workspace=None,
+                  out_o=None, out_lse=None, stream=None):
+    """dkv_prefill_fused: append the T new rows (k_new/v_new [T,Hkv,D] bf16, or
+    x [T,hidden] with wk/wv) and attend causally; returns (o [T,Hq,D], lse [T,Hq])."""
+    T, Hq, D = q.shape
+    qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
+    B = len(qp)
+    hidden = int(x.shape[1]) if x is not None else 0
+    if workspace is None:
+        info = prefill_fused_plan(cache, B, Hq, qs, qp, sl, ratio, hidden)
+        workspace = torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=q.device)
+    if out_o is None:
+        out_o = torch.empty((max(T, 1), Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None:
+        out_lse = torch.empty((max(T, 1), Hq), dtype=torch.float32, device=q.device)
+    d = cache.desc()
+    check(lib().dkv_prefill_fused(C.byref(d), B, int(Hq), _ptr(q), _ptr(qs), _ptr(qp), _ptr(sl), float(ratio),
+                                  float(scale), float(rope_theta), _ptr(x), hidden, _ptr(wk), _ptr(wv),
+                                  _ptr(k_new), _ptr(v_new), _ptr(workspace), workspace.numel(), _ptr(out_o),
+                                  _ptr(out_lse), _stream(stream)))
+    return out_o[:T], out_lse[:T]
 
 
 def prefill(cache: KVCache, q, q_start, q_pos0, seq_lens, ratio, scale, rope_theta, *, bufs=None,

@@ -33,8 +33,11 @@ def _append_rows(cache: KVCache, batch: int, b: int, t0: int, k_raw: np.ndarray,
 
 
 def contiguous_cache(hkv: int, d: int, lens, ratio: float, k_raw, v_raw, theta: float,
-                     host_flags: int = DKV_HOST_COHERENT, host_stride=None, dev_stride=None) -> KVCache:
-    """Contiguous-split cache: k_raw[b] / v_raw[b] are uint16 [L_b, Hkv, D] (bf16 bits)."""
+                     host_flags: int = DKV_HOST_COHERENT, host_stride=None, dev_stride=None,
+                     upto=None) -> KVCache:
+    """Contiguous-split cache: k_raw[b] / v_raw[b] are uint16 [L_b, Hkv, D] (bf16 bits).
+    The placement follows the full lengths; tokens [0, upto[b]) are appended
+    (default: all of them)."""
     lens = [int(x) for x in lens]
     nh = [split_point(ratio, n) for n in lens]
     hs = max(nh) if host_stride is None else int(host_stride)
@@ -44,7 +47,9 @@ def contiguous_cache(hkv: int, d: int, lens, ratio: float, k_raw, v_raw, theta: 
                     host_stride=hs, dev_stride=ds, host_flags=host_flags)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     for b in range(B):
-        _append_rows(cache, B, b, 0, k_raw[b], v_raw[b], sl, ratio, theta)
+        n = lens[b] if upto is None else int(upto[b])
+        if n > 0:
+            _append_rows(cache, B, b, 0, k_raw[b][:n], v_raw[b][:n], sl, ratio, theta)
     torch.cuda.synchronize()
     return cache
 

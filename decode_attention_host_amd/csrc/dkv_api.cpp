@@ -271,7 +271,7 @@ std::shared_ptr<PlanEntry> cache_find(const std::string& key) {
 // Builds or fetches the plan of a prefill call.
 dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int32_t* q_start,
                             const int32_t* q_pos0, const int32_t* seq_lens, double ratio,
-                            std::shared_ptr<PlanEntry>* out) {
+                            std::shared_ptr<PlanEntry>* out, bool fresh = false) {
   if (batch < 1) return set_err(DKV_ERR_INVALID, "batch must be >= 1");
   if (!seq_lens || !q_start || !q_pos0) return set_err(DKV_ERR_INVALID, "seq_lens, q_start and q_pos0 are required");
   if (hq < 1 || hq % kv->num_kv_heads)
@@ -290,7 +290,7 @@ dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, co
     cus = device_cus(&dev);
     if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
   }
-  std::string key("prefill");
+  std::string key(fresh ? "prefill-fused" : "prefill");
   put(key, dev); put(key, cus); put(key, gen); put(key, batch); put(key, hq);
   put(key, kv->num_kv_heads); put(key, kv->head_dim); put(key, kv->page_size); put(key, kv->max_pages);
   put(key, kv->host_stride); put(key, kv->dev_stride); put(key, kv->host_rows); put(key, kv->dev_rows);
@@ -321,6 +321,7 @@ dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, co
   in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
   in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
   in.stage_max_bytes = t.stage_max_mib < 0 ? 0 : (int64_t)(t.stage_max_mib == 0 ? 4096 : t.stage_max_mib) << 20;
+  in.prefill_fresh = fresh ? 1 : 0;
   auto e = std::make_shared<PlanEntry>();
   std::vector<uint8_t> blob;
   std::string err;
@@ -341,6 +342,24 @@ size_t prefill_stage_off(const dkv::PlanLayout& L, int hq, int d) {
 }
 size_t prefill_ws_bytes(const dkv::PlanLayout& L, int hq, int hkv, int d) {
   return prefill_stage_off(L, hq, d) + (size_t)L.stage_rows * hkv * d * 2 * 2;
+}
+
+// Fused prefill workspace: the prefill workspace, then the fresh rows (K, V),
+// the partials, the split offsets and the projection scratch.
+struct FusedLayout {
+  size_t fresh_off, part_o_off, part_lse_off, offsets_off, proj_off, total;
+};
+FusedLayout fused_layout(const dkv::PlanLayout& L, int hq, int hkv, int d, int hidden) {
+  auto up = [](size_t a) { return (a + 255) / 256 * 256; };
+  FusedLayout f{};
+  const size_t rowb = (size_t)hkv * d * 2;
+  f.fresh_off = up(prefill_ws_bytes(L, hq, hkv, d));
+  f.part_o_off = up(f.fresh_off + 2 * rowb * (size_t)L.n_rows);
+  f.part_lse_off = up(f.part_o_off + (size_t)L.num_splits * hq * d * 4);
+  f.offsets_off = up(f.part_lse_off + (size_t)L.num_splits * hq * 4);
+  f.proj_off = up(f.offsets_off + ((size_t)L.n_rows + 1) * 4);
+  f.total = f.proj_off + (hidden > 0 ? dkv_append_workspace_bytes(L.n_rows, hidden, hkv * d) : 0);
+  return f;
 }
 
 void fill_info(const dkv::PlanLayout& L, size_t ws, dkv_plan_info* info) {
@@ -580,7 +599,7 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
 
 dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                                     const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
-                                    double offload_ratio, int32_t num_cus, int64_t* items, int32_t items_cap,
+                                    double offload_ratio, int32_t fused, int32_t num_cus, int64_t* items, int32_t items_cap,
                                     int32_t* pages, int32_t pages_cap, int64_t* tiles, int32_t tiles_cap,
                                     int32_t* split_offsets, int32_t offsets_cap, dkv_plan_info* info) {
   dkv_status st = validate_desc(kv);
@@ -601,6 +620,7 @@ dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_
   in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
   in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
   in.stage_max_bytes = t.stage_max_mib < 0 ? 0 : (int64_t)(t.stage_max_mib == 0 ? 4096 : t.stage_max_mib) << 20;
+  in.prefill_fresh = fused ? 1 : 0;
   dkv::PlanLayout L;
   std::vector<uint8_t> blob;
   std::string err;
@@ -612,7 +632,9 @@ dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_
     for (int i = 0; i < n_items && i < items_cap; ++i) {
       int64_t* o = items + 11 * (size_t)i;
       o[0] = it[i].pool; o[1] = it[i].b; o[2] = it[i].row0; o[3] = it[i].n_rows; o[4] = it[i].pos0;
-      o[5] = it[i].n_tok; o[6] = kv->page_size > 0 ? it[i].plist : it[i].row_pool; o[7] = it[i].tok0;
+      o[5] = it[i].n_tok;
+      o[6] = kv->page_size > 0 && it[i].pool != dkv::kPoolFresh ? it[i].plist : it[i].row_pool;
+      o[7] = it[i].tok0;
       o[8] = it[i].split_idx; o[9] = it[i].n_splits; o[10] = it[i].base;
     }
   if (pages)
@@ -627,7 +649,9 @@ dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_
   }
   if (split_offsets)
     memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * std::min(L.n_rows + 1, offsets_cap));
-  if (info) fill_info(L, prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim), info);
+  if (info)
+    fill_info(L, fused ? fused_layout(L, num_q_heads, kv->num_kv_heads, kv->head_dim, 0).total
+                       : prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim), info);
   return ok();
 }
 
@@ -1117,43 +1141,18 @@ dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
   return ok();
 }
 
-dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
-                                  const void* q, const int32_t* q_start, const int32_t* q_pos0,
-                                  const int32_t* seq_lens, double offload_ratio, float scale,
-                                  double rope_theta, void* workspace, size_t workspace_bytes,
-                                  float* part_o, float* part_lse, int32_t* split_offsets,
-                                  int32_t num_splits_cap, void* stream) {
-  dkv_status st = validate_desc(kv);
-  if (st != DKV_OK) return st;
-  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
-  if (!q || !part_o || !part_lse || !split_offsets || !workspace)
-    return set_err(DKV_ERR_INVALID, "q, part_o, part_lse, split_offsets and workspace are required");
-  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
-    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
-  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
-  std::shared_ptr<PlanEntry> e;
-  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
-                        kv->page_size == 0 ? offload_ratio : 0.0, &e);
-  if (st != DKV_OK) return st;
-  const dkv::PlanLayout& L = e->lay;
-  if (L.n_rows == 0) return ok();  // no query rows
-  const size_t need = prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim);
-  if (workspace_bytes < need)
-    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-  if (num_splits_cap < L.num_splits)
-    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %d splits", num_splits_cap, L.num_splits);
+// Staging copy, query rotation and the prefill kernel, after the plan image is
+// in the workspace.  fresh_k/fresh_v: the new rows (fused step) or NULL.
+static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, const void* q,
+                                 const dkv::PlanLayout& L, uint8_t* ws, float scale, double rope_theta,
+                                 const uint16_t* fresh_k, const uint16_t* fresh_v, float* part_o,
+                                 float* part_lse, int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (stream_capturing(s)) {
-    std::lock_guard<std::mutex> lk(cache().mu);
-    e->captured = true;
-  }
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
-  if (he != hipSuccess) return hip_err(he, "plan upload");
   float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
   const size_t pool_elems = (size_t)L.stage_rows * kv->num_kv_heads * kv->head_dim;
   uint16_t* stage_k = reinterpret_cast<uint16_t*>(ws + prefill_stage_off(L, num_q_heads, kv->head_dim));
   uint16_t* stage_v = stage_k + pool_elems;
+  hipError_t he;
   if (L.n_stage_tiles > 0) {
     dkv::StageArgs sa{};
     sa.tiles = reinterpret_cast<const dkv::StageTile*>(ws + L.stage_tiles_off);
@@ -1196,6 +1195,8 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   a.dev_v = static_cast<const uint16_t*>(kv->dev_v);
   a.stage_k = stage_k;
   a.stage_v = stage_v;
+  a.fresh_k = fresh_k;
+  a.fresh_v = fresh_v;
   a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : 0;
   a.hq = num_q_heads;
   a.hkv = kv->num_kv_heads;
@@ -1206,6 +1207,180 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   he = (hipError_t)dkv::launch_prefill(a, q_rot, stream);
   t_attn.done();
   if (he != hipSuccess) return hip_err(he, "prefill launch");
+  return DKV_OK;
+}
+
+dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                  const void* q, const int32_t* q_start, const int32_t* q_pos0,
+                                  const int32_t* seq_lens, double offload_ratio, float scale,
+                                  double rope_theta, void* workspace, size_t workspace_bytes,
+                                  float* part_o, float* part_lse, int32_t* split_offsets,
+                                  int32_t num_splits_cap, void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (!q || !part_o || !part_lse || !split_offsets || !workspace)
+    return set_err(DKV_ERR_INVALID, "q, part_o, part_lse, split_offsets and workspace are required");
+  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  std::shared_ptr<PlanEntry> e;
+  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
+                        kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  if (L.n_rows == 0) return ok();  // no query rows
+  const size_t need = prefill_ws_bytes(L, num_q_heads, kv->num_kv_heads, kv->head_dim);
+  if (workspace_bytes < need)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (num_splits_cap < L.num_splits)
+    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %d splits", num_splits_cap, L.num_splits);
+  hipStream_t s = (hipStream_t)stream;
+  if (stream_capturing(s)) {
+    std::lock_guard<std::mutex> lk(cache().mu);
+    e->captured = true;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_err(he, "plan upload");
+  st = prefill_stages(kv, num_q_heads, q, L, ws, scale, rope_theta, nullptr, nullptr, part_o, part_lse,
+                      split_offsets, stream);
+  return st == DKV_OK ? ok() : st;
+}
+
+dkv_status dkv_prefill_fused_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                                  double offload_ratio, int32_t hidden, dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  std::shared_ptr<PlanEntry> e;
+  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
+                        kv->page_size == 0 ? offload_ratio : 0.0, &e, true);
+  if (st != DKV_OK) return st;
+  fill_info(e->lay, fused_layout(e->lay, num_q_heads, kv->num_kv_heads, kv->head_dim, hidden).total, info);
+  return ok();
+}
+
+dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                             const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                             double offload_ratio, float scale, double rope_theta, const void* x,
+                             int32_t hidden, const void* wk, const void* wv, const void* k_new,
+                             const void* v_new, void* workspace, size_t workspace_bytes, float* out_o,
+                             float* out_lse, void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (!q || !out_o || !workspace) return set_err(DKV_ERR_INVALID, "q, out_o and workspace are required");
+  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  const int32_t kvd = kv->num_kv_heads * kv->head_dim;
+  const bool proj = x != nullptr;
+  if (proj) {
+    if (!wk || !wv) return set_err(DKV_ERR_INVALID, "projection mode needs wk and wv");
+    if (hidden < 256 || hidden % 256)
+      return set_err(DKV_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 256", hidden);
+    if ((2 * kvd) % 64) return set_err(DKV_ERR_UNSUPPORTED, "2*Hkv*D must be a multiple of 64");
+    if ((uintptr_t)x % 16 || (uintptr_t)wk % 16 || (uintptr_t)wv % 16)
+      return set_err(DKV_ERR_INVALID, "x, wk, wv must be 16-byte aligned");
+  } else {
+    if (!k_new || !v_new) return set_err(DKV_ERR_INVALID, "no-projection mode needs k_new and v_new");
+    if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
+      return set_err(DKV_ERR_INVALID, "k_new, v_new must be 16-byte aligned");
+  }
+  std::shared_ptr<PlanEntry> e;
+  st = get_prefill_plan(kv, batch, num_q_heads, q_start, q_pos0, seq_lens,
+                        kv->page_size == 0 ? offload_ratio : 0.0, &e, true);
+  if (st != DKV_OK) return st;
+  const dkv::PlanLayout& L = e->lay;
+  if (L.n_rows == 0) return ok();
+  const FusedLayout F = fused_layout(L, num_q_heads, kv->num_kv_heads, kv->head_dim, proj ? hidden : 0);
+  if (workspace_bytes < F.total)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, F.total);
+  hipStream_t s = (hipStream_t)stream;
+  if (stream_capturing(s)) {
+    std::lock_guard<std::mutex> lk(cache().mu);
+    e->captured = true;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_err(he, "plan upload");
+  uint16_t* fresh_k = reinterpret_cast<uint16_t*>(ws + F.fresh_off);
+  uint16_t* fresh_v = fresh_k + (size_t)L.n_rows * kvd;
+  // 1. new K/V (projection) -> cache slots and the fresh rows
+  dkv::AppendArgs a{};
+  a.batch = batch;
+  a.n_new = L.n_rows;
+  a.seq_lens = reinterpret_cast<const int32_t*>(ws + L.seqlens_off);
+  a.ratio = kv->page_size == 0 ? offload_ratio : 0.0;
+  a.seq_idx = reinterpret_cast<const int32_t*>(ws + L.rowseq_off);
+  a.pos = reinterpret_cast<const int32_t*>(ws + L.rowpos_off);
+  a.host_k = static_cast<uint16_t*>(kv->host_k);
+  a.host_v = static_cast<uint16_t*>(kv->host_v);
+  a.dev_k = static_cast<uint16_t*>(kv->dev_k);
+  a.dev_v = static_cast<uint16_t*>(kv->dev_v);
+  a.host_rows = kv->host_rows;
+  a.dev_rows = kv->dev_rows;
+  a.host_stride = kv->host_stride;
+  a.dev_stride = kv->dev_stride;
+  a.page_table = kv->page_table;
+  a.max_pages = kv->max_pages;
+  a.page_size = kv->page_size;
+  a.hkv = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.freq = rope_freq(rope_theta, kv->head_dim);
+  a.fresh_k = fresh_k;
+  a.fresh_v = fresh_v;
+  if (proj) {
+    dkv::ProjArgs p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.wk = static_cast<const uint16_t*>(wk);
+    p.wv = static_cast<const uint16_t*>(wv);
+    p.n_new = L.n_rows;
+    p.n_pad = (L.n_rows + 15) / 16 * 16;
+    p.hidden = hidden;
+    p.kv_dim = kvd;
+    p.ksplit = hidden / 256;
+    p.kslice = 256;
+    const int64_t part = (int64_t)p.ksplit * p.n_pad * 2 * kvd * 4;
+    p.partial = reinterpret_cast<float*>(ws + F.proj_off);
+    p.out = reinterpret_cast<float*>(ws + F.proj_off + ((part + 255) / 256) * 256);
+    he = (hipError_t)dkv::launch_project(p, stream);
+    if (he != hipSuccess) return hip_err(he, "projection launch");
+    a.kv_proj = p.out;
+  } else {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+  }
+  {
+    TimedLaunch tl(DKV_KERNEL_APPEND, s);
+    he = (hipError_t)dkv::launch_append(a, stream);
+    tl.done();
+    if (he != hipSuccess) return hip_err(he, "append launch");
+  }
+  // 2. staging of re-read prefix rows, query rotation, prefill attention
+  float* part_o = reinterpret_cast<float*>(ws + F.part_o_off);
+  float* part_lse = reinterpret_cast<float*>(ws + F.part_lse_off);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + F.offsets_off);
+  st = prefill_stages(kv, num_q_heads, q, L, ws, scale, rope_theta, fresh_k, fresh_v, part_o, part_lse, offs,
+                      stream);
+  if (st != DKV_OK) return st;
+  // 3. merge of each row's splits
+  dkv::MergeArgs m{};
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.split_offsets = offs;
+  m.batch = L.n_rows;
+  m.hq = num_q_heads;
+  m.head_dim = kv->head_dim;
+  m.out_o = out_o;
+  m.out_lse = out_lse;
+  TimedLaunch tm(DKV_KERNEL_MERGE, s);
+  he = (hipError_t)dkv::launch_merge(m, stream);
+  tm.done();
+  if (he != hipSuccess) return hip_err(he, "merge launch");
   return ok();
 }
 

@@ -38,7 +38,9 @@ static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
 constexpr int kPrefillRows = 128;
 
 // Where a prefill item's tokens are read from.
-enum PrefillPool : int32_t { kPoolHost = 0, kPoolDev = 1, kPoolStaged = 2 };
+// kPoolFresh: the new rows themselves, written to HBM by the fused step's
+// append next to their cache slots (row = the query row's index).
+enum PrefillPool : int32_t { kPoolHost = 0, kPoolDev = 1, kPoolStaged = 2, kPoolFresh = 3 };
 
 // Prefill work item: a block of consecutive query rows of one sequence (all G
 // heads of one KV head per unit) against a run of cached tokens that lie in
@@ -122,6 +124,8 @@ struct PlanLayout {
   int64_t stage_rows = 0;        // prefill: rows of the HBM staging pool
   int64_t staged_bytes = 0;      // prefill: host K+V bytes copied once
   int32_t dev_queues = 1;        // prefill: HBM work queues (1 or 8)
+  size_t rowseq_off = 0;         // prefill: sequence of every query row [T]
+  size_t seqlens_off = 0;        // prefill: cached lengths [B] (device copy)
 };
 
 // Arguments of the split attention kernel.
@@ -183,6 +187,8 @@ struct AppendArgs {
   const uint16_t* k_new;         // [n_new][Hkv][D] bf16, or NULL in projection mode
   const uint16_t* v_new;
   const float* kv_proj;          // projection mode: [n_new][2*Hkv*D] fp32 (K then V)
+  uint16_t* fresh_k;             // optional second copy of token i's K/V at row i
+  uint16_t* fresh_v;
   uint16_t* host_k;
   uint16_t* host_v;
   uint16_t* dev_k;
@@ -235,6 +241,8 @@ struct PrefillArgs {
   const uint16_t* dev_v;
   const uint16_t* stage_k;
   const uint16_t* stage_v;
+  const uint16_t* fresh_k;       // fused step: new rows [T][Hkv][D]
+  const uint16_t* fresh_v;
   int32_t page_shift;
   int32_t hq;
   int32_t hkv;
@@ -313,6 +321,7 @@ struct PlanInput {
   double host_bw;
   double dev_bw;
   int64_t stage_max_bytes;        // prefill staging budget (< 0: never stage)
+  int32_t prefill_fresh;          // prefill: new rows read from the fresh pool
 };
 
 // Builds the plan and its device image; on failure returns false with `err`.

@@ -74,8 +74,11 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
 
 // ---------------------------------------------------------------------------
 // Query rotation: q_rot[b][h][d] = scale*log2(e) * RoPE(q[b][h], q_pos[b])[d].
-// Angle pos * f_i and sin/cos in fp64 (f_i from the host table).  Block 0 also
-// copies the split offsets of the plan to the caller's array.
+// Angle pos * f_i and sin/cos in fp64 (f_i from the host table), computed once
+// per (row, pair i) and applied to `hpt` consecutive heads; many rows (prefill)
+// use all heads per thread, few rows (decode) a handful so that enough
+// threads run.  Block 0 also copies the split offsets of the plan to the
+// caller's array.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ q_pos,
@@ -83,25 +86,30 @@ __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __rest
                                                           RopeFreq freq, float scale_log2,
                                                           const int32_t* __restrict__ plan_offsets,
                                                           int32_t* __restrict__ split_offsets,
-                                                          int batch) {
+                                                          int batch, int hpt) {
   const int half = d >> 1;
   if (blockIdx.x == 0 && split_offsets)
     for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
-  const int64_t per_row = (int64_t)hq * half;
-  const int64_t total = (int64_t)batch * per_row;
+  const int groups = (hq + hpt - 1) / hpt;
+  const int64_t total = (int64_t)batch * groups * half;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int b = (int)(idx / per_row);
-    const int rem = (int)(idx - (int64_t)b * per_row);
-    const int h = rem / half, i = rem - h * half;
+    const int i = (int)(idx % half);
+    const int64_t bg = idx / half;
+    const int g = (int)(bg % groups);
+    const int b = (int)(bg / groups);
     double s, c;
     sincos((double)q_pos[b] * freq.f[i], &s, &c);
-    const uint16_t* qh = q + ((size_t)b * hq + h) * d;
-    const double xl = (double)bf16_to_f32(qh[i]);
-    const double xh = (double)bf16_to_f32(qh[i + half]);
-    float* o = q_rot + ((size_t)b * hq + h) * d;
-    o[i] = (float)(xl * c - xh * s) * scale_log2;
-    o[i + half] = (float)(xh * c + xl * s) * scale_log2;
+    const int h1 = min(hq, (g + 1) * hpt);
+#pragma unroll 4
+    for (int h = g * hpt; h < h1; ++h) {
+      const uint16_t* qh = q + ((size_t)b * hq + h) * d;
+      const double xl = (double)bf16_to_f32(qh[i]);
+      const double xh = (double)bf16_to_f32(qh[i + half]);
+      float* o = q_rot + ((size_t)b * hq + h) * d;
+      o[i] = (float)(xl * c - xh * s) * scale_log2;
+      o[i + half] = (float)(xh * c + xl * s) * scale_log2;
+    }
   }
 }
 
@@ -504,12 +512,14 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   auto src_of = [&](const PrefillItem& it) -> Src {
     if (it.pool == kPoolHost) return Src{a.host_k, a.host_v, true};
     if (it.pool == kPoolDev) return Src{a.dev_k, a.dev_v, false};
+    if (it.pool == kPoolFresh) return Src{a.fresh_k, a.fresh_v, false};
     return Src{a.stage_k, a.stage_v, false};
   };
-  // pool row of token `tok` of an item (tokens past the end read token 0)
+  // pool row of token `tok` of an item (tokens past the end read token 0);
+  // fresh rows are contiguous in either layout
   auto row_of = [&](const PrefillItem& it, int tok) -> int64_t {
     tok = tok < it.n_tok ? tok : 0;
-    if (PAGED) {
+    if (PAGED && it.pool != kPoolFresh) {
       const int pg = tok >> a.page_shift;
       return ((int64_t)a.pages[2 * (it.plist + pg) + 1] << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
     }
@@ -517,7 +527,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   };
   auto pos_of = [&](const PrefillItem& it, int tok) -> int {
     if (tok >= it.n_tok) return -1;
-    if (PAGED) {
+    if (PAGED && it.pool != kPoolFresh) {
       const int pg = tok >> a.page_shift;
       return (a.pages[2 * (it.plist + pg)] << a.page_shift) + (tok & ((1 << a.page_shift) - 1));
     }
@@ -546,7 +556,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     const int t0 = tile * kTile;
     // contiguous items step the offsets by whole tiles except where the
     // tile runs past the item (clamping) ; paged items look up every tile
-    if (PAGED || tile == 0 || t0 + kTile > it.n_tok) {
+    if ((PAGED && it.pool != kPoolFresh) || tile == 0 || t0 + kTile > it.n_tok) {
       set_offsets(it, kvh, tile);
     } else {
       const int64_t step = (int64_t)kTile * a.hkv * D;
@@ -1212,6 +1222,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     uint16_t* dst = sl.k + h * D;
     *reinterpret_cast<uint2*>(dst + p0) = make_uint2(yl[0], yl[1]);
     *reinterpret_cast<uint2*>(dst + half + p0) = make_uint2(yh[0], yh[1]);
+    if (a.fresh_k) {
+      uint16_t* fk = a.fresh_k + (size_t)i * kvd + h * D;
+      *reinterpret_cast<uint2*>(fk + p0) = make_uint2(yl[0], yl[1]);
+      *reinterpret_cast<uint2*>(fk + half + p0) = make_uint2(yh[0], yh[1]);
+    }
     // V: the same thread moves the matching 2 x 4 values of this head
     uint16_t* vd = sl.v + h * D;
     if (a.kv_proj) {
@@ -1224,10 +1239,22 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       }
       *reinterpret_cast<uint2*>(vd + p0) = make_uint2(w0[0], w0[1]);
       *reinterpret_cast<uint2*>(vd + half + p0) = make_uint2(w1[0], w1[1]);
+      if (a.fresh_v) {
+        uint16_t* fv = a.fresh_v + (size_t)i * kvd + h * D;
+        *reinterpret_cast<uint2*>(fv + p0) = make_uint2(w0[0], w0[1]);
+        *reinterpret_cast<uint2*>(fv + half + p0) = make_uint2(w1[0], w1[1]);
+      }
     } else {
       const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
-      *reinterpret_cast<uint2*>(vd + p0) = *reinterpret_cast<const uint2*>(vs + p0);
-      *reinterpret_cast<uint2*>(vd + half + p0) = *reinterpret_cast<const uint2*>(vs + half + p0);
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vs + p0);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vs + half + p0);
+      *reinterpret_cast<uint2*>(vd + p0) = v0;
+      *reinterpret_cast<uint2*>(vd + half + p0) = v1;
+      if (a.fresh_v) {
+        uint16_t* fv = a.fresh_v + (size_t)i * kvd + h * D;
+        *reinterpret_cast<uint2*>(fv + p0) = v0;
+        *reinterpret_cast<uint2*>(fv + half + p0) = v1;
+      }
     }
   }
 }
@@ -1354,10 +1381,13 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
                   const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int64_t total = (int64_t)batch * hq * (d / 2);
+  // heads per thread: all of them once rows alone give ~64K threads
+  const int64_t pairs = (int64_t)batch * (d / 2);
+  const int hpt = pairs >= 65536 ? hq : std::min(hq, 4);
+  const int64_t total = pairs * ((hq + hpt - 1) / hpt);
   const int bx = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
   hipLaunchKernelGGL(rope_q_kernel, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
-                     scale_log2, plan_offsets, split_offsets, batch);
+                     scale_log2, plan_offsets, split_offsets, batch, hpt);
   return (int)hipGetLastError();
 }
 

@@ -244,6 +244,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   std::vector<int64_t> nh(B, 0);
   std::vector<std::vector<int32_t>> host_pages(paged ? B : 0), dev_pages(paged ? B : 0);
   std::vector<int64_t> emax(B, 0);
+  std::vector<int64_t> pre(B, 0);    // tokens below pre[b] come from the tiers
   std::vector<int32_t> nblk(B, 0);
   for (int b = 0; b < B; ++b) {
     const int64_t L = in.seq_lens[b];
@@ -254,6 +255,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
       return fail(err, "sequence %lld: query rows at positions %lld.. exceed the %lld cached tokens", b,
                   q_pos0[b], L);
     emax[b] = n > 0 ? (int64_t)q_pos0[b] + n : 0;
+    pre[b] = in.prefill_fresh ? (int64_t)q_pos0[b] : L;
     nblk[b] = (int32_t)ceil_div(n, QB);
     if (!paged) {
       const int64_t h = (int64_t)std::floor(in.ratio * (double)L);
@@ -302,8 +304,8 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   int64_t stage_rows = 0;
   for (int b = 0; b < B; ++b) {
     if (budget <= 0 || nblk[b] < 2) continue;
-    const int64_t rows = paged ? (int64_t)tier_pages_below(b, emax[b], true) * P
-                               : std::min<int64_t>(nh[b], emax[b]);
+    const int64_t lim = std::min(emax[b], pre[b]);
+    const int64_t rows = paged ? (int64_t)tier_pages_below(b, lim, true) * P : std::min<int64_t>(nh[b], lim);
     if (rows <= 0 || (stage_rows + rows) * row_bytes * 2 > budget) continue;
     stage_base[b] = stage_rows;
     if (!paged) {
@@ -337,9 +339,10 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     for (int r0 = 0; r0 < n; r0 += QB) {
       Blk k{b, q_start[b] + r0, std::min(QB, n - r0), q_pos0[b] + r0, 0};
       k.end = (int64_t)k.pos0 + k.n_rows;  // tokens [0, end) are visible to some row
-      const int64_t th = tier_tokens(b, k.end, true);
+      const int64_t te = std::min(k.end, pre[b]);
+      const int64_t th = tier_tokens(b, te, true);
       (stage_base[b] >= 0 ? dev_reads : host_reads) += th;
-      dev_reads += tier_tokens(b, k.end, false);
+      dev_reads += tier_tokens(b, te, false) + std::max<int64_t>(0, k.end - pre[b]);
       blocks.push_back(k);
     }
   }
@@ -361,12 +364,21 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   for (const Blk& k : blocks) {
     std::vector<PrefillItem> items;
     const bool staged = stage_base[k.b] >= 0;
+    const int64_t te = std::min(k.end, pre[k.b]);  // end of the tier tokens
+    for (int64_t t = pre[k.b]; t < k.end; t += cd) {  // new rows: fresh pool
+      PrefillItem it{};
+      it.n_tok = (int32_t)std::min<int64_t>(cd, k.end - t);
+      it.tok0 = (int32_t)t;
+      it.pool = kPoolFresh;
+      it.row_pool = (int64_t)q_start[k.b] + (t - pre[k.b]);
+      items.push_back(it);
+    }
     for (int tier = 1; tier >= 0; --tier) {
       const int32_t pool = tier ? (staged ? kPoolStaged : kPoolHost) : kPoolDev;
       const int64_t chunk = pool == kPoolHost ? ch : cd;
       if (!paged) {
         const int64_t t0 = tier ? 0 : nh[k.b];
-        const int64_t t1 = tier ? std::min<int64_t>(nh[k.b], k.end) : k.end;
+        const int64_t t1 = tier ? std::min<int64_t>(nh[k.b], te) : te;
         for (int64_t t = t0; t < t1; t += chunk) {
           PrefillItem it{};
           it.n_tok = (int32_t)std::min<int64_t>(chunk, t1 - t);
@@ -379,13 +391,13 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
         }
       } else {
         const std::vector<int32_t>& pg = tier ? host_pages[k.b] : dev_pages[k.b];
-        const size_t npg = tier_pages_below(k.b, k.end, tier == 1);
+        const size_t npg = tier_pages_below(k.b, te, tier == 1);
         const size_t per = (size_t)(chunk / P);
         for (size_t p0 = 0; p0 < npg; p0 += per) {
           const size_t p1 = std::min(npg, p0 + per);
           PrefillItem it{};
           int64_t nt = 0;
-          for (size_t q = p0; q < p1; ++q) nt += std::min<int64_t>(P, k.end - (int64_t)pg[q] * P);
+          for (size_t q = p0; q < p1; ++q) nt += std::min<int64_t>(P, te - (int64_t)pg[q] * P);
           it.n_tok = (int32_t)nt;
           it.plist = (int32_t)(pages.size() / 2);
           it.pool = pool;
@@ -457,7 +469,9 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   out->plist_off = (hitems.size() + ditems.size()) * sizeof(PrefillItem);
   out->stage_tiles_off = round_up(out->plist_off + pages.size() * sizeof(int32_t), 32);
   out->rowpos_off = round_up(out->stage_tiles_off + tiles.size() * sizeof(StageTile), 16);
-  out->offsets_off = round_up(out->rowpos_off + T * sizeof(int32_t), 16);
+  out->rowseq_off = round_up(out->rowpos_off + T * sizeof(int32_t), 16);
+  out->seqlens_off = round_up(out->rowseq_off + T * sizeof(int32_t), 16);
+  out->offsets_off = round_up(out->seqlens_off + B * sizeof(int32_t), 16);
   out->counters_off = round_up(out->offsets_off + (T + 1) * sizeof(int32_t), 16);
   out->blob_bytes = round_up(out->counters_off + (kPfMaxQueues + 1) * sizeof(int32_t), 256);
   if (blob) {
@@ -469,6 +483,10 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
     if (!pages.empty()) memcpy(p + out->plist_off, pages.data(), pages.size() * sizeof(int32_t));
     if (!tiles.empty()) memcpy(p + out->stage_tiles_off, tiles.data(), tiles.size() * sizeof(StageTile));
     if (T) memcpy(p + out->rowpos_off, rowpos.data(), T * sizeof(int32_t));
+    int32_t* rs = reinterpret_cast<int32_t*>(p + out->rowseq_off);
+    for (int b = 0; b < B; ++b)
+      for (int32_t r = q_start[b]; r < q_start[b + 1]; ++r) rs[r] = b;
+    memcpy(p + out->seqlens_off, in.seq_lens, B * sizeof(int32_t));
     memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
   }
   return true;

@@ -233,18 +233,19 @@ dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
                             double offload_ratio, dkv_plan_info* info);
 
 /* Prefill planner introspection (no HIP calls; used by CPU tests): the plan
- * dkv_prefill_plan would build for num_cus compute units.  Per item, 11
- * int64 into items: pool (0 host, 1 HBM, 2 HBM staging copy of host rows),
+ * dkv_prefill_plan (fused = 0) or dkv_prefill_fused_plan (fused = 1) would
+ * build for num_cus compute units.  Per item, 11 int64 into items: pool (0
+ * host, 1 HBM, 2 HBM staging copy of host rows, 3 the fused step's new rows),
  * sequence, first query row, rows, first row's position, tokens, first
- * (contiguous: pool row of the first token; paged: index of the first page
- * pair), logical position of the first token (contiguous), split index,
+ * (contiguous layout or pool 3: pool row of the first token; paged: index of
+ * the first page pair), logical position of the first token, split index,
  * splits of the block, first split slot.  pages: (logical page, pool page)
  * pairs of paged items.  tiles: 3 int64 per staging copy (host row, staging
  * row, rows).  split_offsets: [T+1].  Arrays are filled up to their caps;
  * info gives the counts (host_items + dev_items items). */
 dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                                     const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
-                                    double offload_ratio, int32_t num_cus, int64_t* items, int32_t items_cap,
+                                    double offload_ratio, int32_t fused, int32_t num_cus, int64_t* items, int32_t items_cap,
                                     int32_t* pages, int32_t pages_cap, int64_t* tiles, int32_t tiles_cap,
                                     int32_t* split_offsets, int32_t offsets_cap, dkv_plan_info* info);
 
@@ -254,6 +255,33 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
                                   double rope_theta, void* workspace, size_t workspace_bytes,
                                   float* part_o, float* part_lse, int32_t* split_offsets,
                                   int32_t num_splits_cap, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused prefill step (DirectKV README, introduction: one kernel projects the
+ * new tokens' K/V, rotates them, appends them to the CPU-resident cache and
+ * attends; Step 6, "Prefill (all new KV)").
+ *
+ * Rows q_start[b] .. q_start[b+1]-1 of q are new tokens of sequence b at
+ * positions q_pos0[b] + j (host arrays as for dkv_prefill_attn_split;
+ * seq_lens are the lengths including the new tokens).  Their K/V come from
+ * k_new/v_new ([T][Hkv][D] bf16) or from x [T][hidden] times wk/wv as in
+ * dkv_project_rope_append.  The call appends them to their cache slots (host
+ * or HBM), keeps a second copy of the new rows in the workspace, and attends
+ * causally: cached tokens below q_pos0[b] come from the tiers (staged into HBM
+ * when several row blocks re-read host rows), the new rows from the copy.
+ * Output: out_o [T][Hq][D] fp32, out_lse [T][Hq] fp32 (or NULL).  Workspace
+ * size from dkv_prefill_fused_plan (hidden = 0 without projection).
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_prefill_fused_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                                  double offload_ratio, int32_t hidden, dkv_plan_info* info);
+
+dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                             const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
+                             double offload_ratio, float scale, double rope_theta, const void* x,
+                             int32_t hidden, const void* wk, const void* wv, const void* k_new,
+                             const void* v_new, void* workspace, size_t workspace_bytes, float* out_o,
+                             float* out_lse, void* stream);
 
 /* ------------------------------------------------------------------------
  * Offloaded linear layer read in place from both tiers (SplitKernel README,

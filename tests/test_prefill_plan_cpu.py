@@ -39,8 +39,10 @@ def desc(hkv, d, page=0, max_pages=0, host_rows=1 << 20, dev_rows=1 << 20, hs=1 
     return x
 
 
-def _check(plan, lens, news, hq, hkv, slot_of, stage_src):
-    """slot_of(b, t) -> (pool 0/1, row); stage_src: staging row -> host row."""
+def _check(plan, lens, news, hq, hkv, slot_of, stage_src, fused=False):
+    """slot_of(b, t) -> (pool 0/1, row); stage_src: staging row -> host row.
+    fused: tokens at or after a sequence's first new row come from pool 3 (the
+    new rows, in query-row order)."""
     items, offs, info = plan["items"], plan["split_offsets"], plan["info"]
     G = hq // hkv
     QB = QROWS // G
@@ -70,6 +72,12 @@ def _check(plan, lens, news, hq, hkv, slot_of, stage_src):
                     assert s not in slots
                     slots.add(s)
                 for k in range(ntok):
+                    if pool == 3:
+                        t, row = tok0 + k, first + k
+                        assert fused and t >= p0 and row == q_start[b] + (t - p0), (b, t)
+                        assert t not in seen
+                        seen[t] = 1
+                        continue
                     if plan["paged"]:
                         P = plan["P"]
                         lp, pp = plan["pages"][2 * (first + k // P)], plan["pages"][2 * (first + k // P) + 1]
@@ -77,6 +85,7 @@ def _check(plan, lens, news, hq, hkv, slot_of, stage_src):
                     else:
                         t, row = tok0 + k, first + k
                     assert t not in seen, (b, row0, t)
+                    assert not fused or t < p0, (b, t)
                     seen[t] = 1
                     tier, want = slot_of(b, t)
                     if pool == 2:
@@ -100,14 +109,15 @@ def _stage_map(plan):
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 64), (8, 4, 128)])
 @pytest.mark.parametrize("ratio", [0.0, 0.3, 1.0])
 @pytest.mark.parametrize("stage", [True, False])
-def test_prefill_plan_contiguous(L, hq, hkv, d, ratio, stage):
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_plan_contiguous(L, hq, hkv, d, ratio, stage, fused):
     lens, news = [64, 377, 33, 1000, 200], [64, 77, 1, 130, 200]
     hs = ds = 1024
     x = desc(hkv, d, host_rows=len(lens) * hs, dev_rows=len(lens) * ds, hs=hs, ds=ds)
     try:
         set_tuning(stage_max_mib=0 if stage else -1)
         plan = prefill_plan_inspect(x, len(lens), hq, np.concatenate([[0], np.cumsum(news)]),
-                                    [a - n for a, n in zip(lens, news)], lens, ratio, 16)
+                                    [a - n for a, n in zip(lens, news)], lens, ratio, 16, fused=fused)
     finally:
         reset_tuning()
     plan["paged"] = False
@@ -115,10 +125,12 @@ def test_prefill_plan_contiguous(L, hq, hkv, d, ratio, stage):
     def slot_of(b, t):
         return O.contig_slot(b, t, lens[b], ratio, hs, ds)
 
-    _check(plan, lens, news, hq, hkv, slot_of, _stage_map(plan))
+    _check(plan, lens, news, hq, hkv, slot_of, _stage_map(plan), fused)
     G = hq // hkv
     nblk = [-(-n // (QROWS // G)) for n in news]
-    staged_rows = sum(min(O.contig_split_point(ratio, a), a) for a, k in zip(lens, nblk) if k >= 2)
+    # staged: host rows below the first new row (fused) or below the last row
+    staged_rows = sum(min(O.contig_split_point(ratio, a), a - n if fused else a)
+                      for a, n, k in zip(lens, news, nblk) if k >= 2)
     assert plan["info"]["staged_bytes"] == (staged_rows * hkv * d * 4 if stage else 0)
     if stage:
         assert sum(int(t[2]) for t in plan["tiles"]) == staged_rows
@@ -127,14 +139,15 @@ def test_prefill_plan_contiguous(L, hq, hkv, d, ratio, stage):
 
 
 @pytest.mark.parametrize("stage", [True, False])
-def test_prefill_plan_paged(L, stage):
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_plan_paged(L, stage, fused):
     lens, news, hq, hkv, d = [500, 17, 1200, 40], [100, 17, 333, 1], 32, 8, 128
     pt, nh, nd = paged_table(80, lens, 16, 0.8)
     x = desc(hkv, d, page=16, max_pages=pt.shape[1], host_rows=nh * 16, dev_rows=nd * 16, pt=pt)
     try:
         set_tuning(stage_max_mib=0 if stage else -1)
         plan = prefill_plan_inspect(x, len(lens), hq, np.concatenate([[0], np.cumsum(news)]),
-                                    [a - n for a, n in zip(lens, news)], lens, 0.0, 16)
+                                    [a - n for a, n in zip(lens, news)], lens, 0.0, 16, fused=fused)
     finally:
         reset_tuning()
     plan["paged"], plan["P"] = True, 16
@@ -142,7 +155,7 @@ def test_prefill_plan_paged(L, stage):
     def slot_of(b, t):
         return O.paged_slot(pt, b, t, 16)
 
-    _check(plan, lens, news, hq, hkv, slot_of, _stage_map(plan))
+    _check(plan, lens, news, hq, hkv, slot_of, _stage_map(plan), fused)
     assert (plan["info"]["staged_bytes"] > 0) == stage   # sequences 0 and 2 span several blocks
 
 
