@@ -419,8 +419,10 @@ def measure_long_sweep(dk, cfg, seed, flags, iters, bw_h, bw_d):
 
 
 def measure_prefill(dk, cfg, seed, flags, steps, warmup):
-    """Causal prefill of new tokens: bulk append (RoPE + store into the tier),
-    prefill attention, merge.  Reported per offload ratio in cfg["ratios"]."""
+    """Causal prefill of new tokens, per offload ratio in cfg["ratios"]:
+    the fused step (append of the new rows into their tier plus an HBM copy,
+    prefill attention, merge: one library call) and the two-call path
+    (append; prefill attention over the cache; merge)."""
     import numpy as np
     import torch
     from decode_attention_host_amd.cache_build import contiguous_cache
@@ -428,6 +430,7 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
 
     hq, hkv, d, lens, news = cfg["hq"], cfg["hkv"], cfg["d"], cfg["lens"], cfg["new"]
     B = cfg["batch"]
+    th = cfg["theta"]
     ks, vs = kv_raw(seed, lens, hkv, d)
     q = torch.from_numpy(np.concatenate([normal_bf16(seed + b, 1, (n, hq, d)) for b, n in enumerate(news)])
                          .view(np.int16)).cuda()
@@ -439,22 +442,12 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
     sidx = torch.from_numpy(np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(news)])).cuda()
     pos = torch.from_numpy(np.concatenate([np.arange(L - n, L, dtype=np.int32) for L, n in zip(lens, news)])).cuda()
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
     flops = 0
     for L, n, p0 in zip(lens, news, q_pos0):
         flops += 4 * hq * d * sum(p0 + j + 1 for j in range(n))
-    out = []
-    for r in cfg.get("ratios", [cfg["ratio"]]):
-        cache = contiguous_cache(hkv, d, lens, r, ks, vs, cfg["theta"], host_flags=flags)
-        bufs = dk.alloc_prefill_buffers(cache, B, hq, q_start, q_pos0, lens, r)
-        scale = 1.0 / math.sqrt(d)
 
-        def step():
-            dk.project_rope_append(cache, B, sl, r, sidx, pos, k_new=k_new, v_new=v_new,
-                                   rope_theta=cfg["theta"])
-            dk.prefill_attn_split(cache, q, q_start, q_pos0, lens, r, scale, cfg["theta"], bufs=bufs)
-            dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, T, hq, d, out_o=bufs.out_o,
-                         out_lse=bufs.out_lse)
-
+    def timed(step):
         gpu_warm(step)
         dk.kernel_timing(True)
         for k in dk.api.KERNELS:
@@ -462,24 +455,49 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
         ms, _ = timed_loop(step, steps, warmup)
         kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
         dk.kernel_timing(False)
-        pf_ms = kt["prefill"][1] / max(1, kt["prefill"][0])
-        st_ms = kt["stage"][1] / max(1, kt["stage"][0])
-        info = bufs.info
-        reads = info["host_bytes"] + info["dev_bytes"]
+        return ms, {k: v[1] / max(1, v[0]) for k, v in kt.items() if v[0]}
+
+    out = []
+    for r in cfg.get("ratios", [cfg["ratio"]]):
+        # fused step over a cache holding only the prefix
+        cache = contiguous_cache(hkv, d, lens, r, ks, vs, th, host_flags=flags, upto=q_pos0)
+        info = dk.prefill_fused_plan(cache, B, hq, q_start, q_pos0, lens, r)
+        ws = torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+        oo = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+        ol = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+        f_ms, f_kt = timed(lambda: dk.prefill_fused(cache, q, q_start, q_pos0, lens, r, scale, th, k_new=k_new,
+                                                    v_new=v_new, workspace=ws, out_o=oo, out_lse=ol))
+        cache.free()
+        # two-call path over the full cache
+        cache = contiguous_cache(hkv, d, lens, r, ks, vs, th, host_flags=flags)
+        bufs = dk.alloc_prefill_buffers(cache, B, hq, q_start, q_pos0, lens, r)
+
+        def step():
+            dk.project_rope_append(cache, B, sl, r, sidx, pos, k_new=k_new, v_new=v_new, rope_theta=th)
+            dk.prefill_attn_split(cache, q, q_start, q_pos0, lens, r, scale, th, bufs=bufs)
+            dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, T, hq, d, out_o=bufs.out_o,
+                         out_lse=bufs.out_lse)
+
+        s_ms, s_kt = timed(step)
+        pf_ms = f_kt["prefill"]
         # MFMA work executed: Q.K and P.V each run twice (high and low bf16
         # parts of the fp32 operand), so the executed rate is 2x the useful one
-        out.append({"ratio": r, "new_tokens": T, "ms_per_step": round(ms, 4),
+        two = bufs.info
+        out.append({"ratio": r, "new_tokens": T,
+                    "fused_ms_per_step": round(f_ms, 4),
+                    "fused_kernel_ms": {k: round(v, 5) for k, v in f_kt.items()},
+                    "fused_kv_reads": {"host_bytes": info["host_bytes"], "hbm_bytes": info["dev_bytes"],
+                                       "staged_bytes": info["staged_bytes"]},
+                    "two_call_ms_per_step": round(s_ms, 4),
+                    "two_call_kernel_ms": {k: round(v, 5) for k, v in s_kt.items()},
+                    "two_call_kv_reads": {"host_bytes": two["host_bytes"], "hbm_bytes": two["dev_bytes"],
+                                          "staged_bytes": two["staged_bytes"]},
                     "prefill_kernel_ms": round(pf_ms, 4),
                     "useful_tflops": round(flops / (pf_ms * 1e9), 2),
                     "frac_bf16_mfma_peak_useful": round(flops / (pf_ms * 1e9) / 2500.0, 4),
                     "frac_bf16_mfma_peak_executed": round(2 * flops / (pf_ms * 1e9) / 2500.0, 4),
-                    "kv_reads_host_bytes": info["host_bytes"], "kv_reads_hbm_bytes": info["dev_bytes"],
-                    "staged_bytes": info["staged_bytes"],
-                    "stage_kernel_ms": round(st_ms, 4),
-                    "stage_link_gbs": round(info["staged_bytes"] / (st_ms * 1e6), 1) if st_ms > 0 else None,
-                    "kv_read_gbs": round(reads / (pf_ms * 1e6), 1),
-                    "kernel_ms": {k: round(v[1] / max(1, v[0]), 5) for k, v in kt.items()},
                     "plan": {k: info[k] for k in ("num_splits", "host_wgs", "dev_wgs", "host_chunk", "dev_chunk")}})
+        log(f"[bench] prefill r={r}: fused {f_ms:.4f} ms, two-call {s_ms:.4f} ms, prefill kernel {pf_ms:.4f} ms")
         cache.free()
     return {"flops_per_step": flops, "per_ratio": out}
 

@@ -1146,7 +1146,8 @@ dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
 static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, const void* q,
                                  const dkv::PlanLayout& L, uint8_t* ws, float scale, double rope_theta,
                                  const uint16_t* fresh_k, const uint16_t* fresh_v, float* part_o,
-                                 float* part_lse, int32_t* split_offsets, void* stream) {
+                                 float* part_lse, int32_t* split_offsets, void* stream,
+                                 const dkv::AppendArgs* writers = nullptr) {
   hipStream_t s = (hipStream_t)stream;
   float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
   const size_t pool_elems = (size_t)L.stage_rows * kv->num_kv_heads * kv->head_dim;
@@ -1203,6 +1204,11 @@ static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, con
   a.head_dim = kv->head_dim;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  if (writers) {
+    // a few workgroups keep the host link busy with the slot writes
+    a.app = *writers;
+    a.writer_wgs = (int32_t)std::min<int64_t>(64, std::max<int64_t>(1, writers->n_new / 8));
+  }
   TimedLaunch t_attn(DKV_KERNEL_PREFILL, s);
   he = (hipError_t)dkv::launch_prefill(a, q_rot, stream);
   t_attn.done();
@@ -1354,19 +1360,28 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
   }
+  // the HBM copy of the new rows first (attention reads it); the writes into
+  // their cache slots (PCIe writes when the slots are host-resident) are done
+  // by writer workgroups of the prefill launch, concurrently with attention
   {
+    dkv::AppendArgs af = a;
+    af.skip_slots = 1;
     TimedLaunch tl(DKV_KERNEL_APPEND, s);
-    he = (hipError_t)dkv::launch_append(a, stream);
+    he = (hipError_t)dkv::launch_append(af, stream);
     tl.done();
     if (he != hipSuccess) return hip_err(he, "append launch");
   }
-  // 2. staging of re-read prefix rows, query rotation, prefill attention
-  float* part_o = reinterpret_cast<float*>(ws + F.part_o_off);
-  float* part_lse = reinterpret_cast<float*>(ws + F.part_lse_off);
+  // 2. staging of re-read prefix rows, query rotation, prefill attention.
+  // With one split per row the split slot of row r is r and its normalised
+  // partial is the result: it is written to the output and no merge runs.
+  const bool direct = L.num_splits == L.n_rows && out_lse != nullptr;
+  float* part_o = direct ? out_o : reinterpret_cast<float*>(ws + F.part_o_off);
+  float* part_lse = direct ? out_lse : reinterpret_cast<float*>(ws + F.part_lse_off);
   int32_t* offs = reinterpret_cast<int32_t*>(ws + F.offsets_off);
   st = prefill_stages(kv, num_q_heads, q, L, ws, scale, rope_theta, fresh_k, fresh_v, part_o, part_lse, offs,
-                      stream);
+                      stream, &a);
   if (st != DKV_OK) return st;
+  if (direct) return ok();
   // 3. merge of each row's splits
   dkv::MergeArgs m{};
   m.part_o = part_o;

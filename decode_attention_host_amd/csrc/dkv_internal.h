@@ -189,6 +189,7 @@ struct AppendArgs {
   const float* kv_proj;          // projection mode: [n_new][2*Hkv*D] fp32 (K then V)
   uint16_t* fresh_k;             // optional second copy of token i's K/V at row i
   uint16_t* fresh_v;
+  int32_t skip_slots;            // 1: write only the second copy
   uint16_t* host_k;
   uint16_t* host_v;
   uint16_t* dev_k;
@@ -249,6 +250,9 @@ struct PrefillArgs {
   int32_t head_dim;
   float* part_o;                 // [S][Hq][D]
   float* part_lse;               // [S][Hq]
+  int32_t writer_wgs;            // fused step: workgroups copying the new rows
+  int32_t pad2;                  //   from fresh_k/v into their cache slots
+  AppendArgs app;                //   (placement of new row i, as for append)
 };
 
 struct LinearArgs {
@@ -293,7 +297,8 @@ int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream);
 int launch_stage(const StageArgs& a, int nwg, void* stream);
 int launch_linear(const LinearArgs& a, void* stream);
-int launch_append(const AppendArgs& a, void* stream);
+// max_wgs > 0 caps the grid (the kernel loops over the tokens).
+int launch_append(const AppendArgs& a, void* stream, int max_wgs = 0);
 int launch_project(const ProjArgs& a, void* stream);
 int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
                       void* stream);

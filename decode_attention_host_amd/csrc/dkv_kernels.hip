@@ -75,9 +75,8 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
 // ---------------------------------------------------------------------------
 // Query rotation: q_rot[b][h][d] = scale*log2(e) * RoPE(q[b][h], q_pos[b])[d].
 // Angle pos * f_i and sin/cos in fp64 (f_i from the host table), computed once
-// per (row, pair i) and applied to `hpt` consecutive heads; many rows (prefill)
-// use all heads per thread, few rows (decode) a handful so that enough
-// threads run.  Block 0 also copies the split offsets of the plan to the
+// per (row, pair i, group of `hpt` consecutive heads) and applied to the group;
+// hpt grows with the number of rows so that about 2^19 threads run.  Block 0 also copies the split offsets of the plan to the
 // caller's array.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
@@ -434,6 +433,50 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uin
 #endif
 constexpr int kPfNtw = DKV_PF_NTW;
 
+// Cache slot of new token i of an append (contiguous split or paged); shared
+// by the append kernel and the prefill kernel's writer role.
+struct Slot {
+  uint16_t* k;
+  uint16_t* v;
+  bool ok;
+};
+
+__device__ __forceinline__ Slot append_slot(const AppendArgs& a, int i) {
+  Slot s{nullptr, nullptr, false};
+  const int b = a.seq_idx[i];
+  const int p = a.pos[i];
+  if (b < 0 || b >= a.batch || p < 0) return s;
+  int64_t row;
+  bool host;
+  if (a.page_size == 0) {
+    const int L = a.seq_lens[b];
+    if (p >= L) return s;
+    const int64_t nh = (int64_t)floor(a.ratio * (double)L);
+    host = p < nh;
+    if (host) {
+      if (nh > a.host_stride) return s;
+      row = (int64_t)b * a.host_stride + p;
+    } else {
+      if (L - nh > a.dev_stride) return s;
+      row = (int64_t)b * a.dev_stride + (p - nh);
+    }
+  } else {
+    const int lp = p / a.page_size;
+    if (lp >= a.max_pages) return s;
+    const int32_t e = a.page_table[(int64_t)b * a.max_pages + lp];
+    if (e < 0) return s;
+    host = (e & 1) != 0;
+    row = (int64_t)(e >> 1) * a.page_size + (p % a.page_size);
+  }
+  const int64_t cap = host ? a.host_rows : a.dev_rows;
+  if (row < 0 || row >= cap) return s;
+  const int64_t off = row * (int64_t)a.hkv * a.head_dim;
+  s.k = (host ? a.host_k : a.dev_k) + off;
+  s.v = (host ? a.host_v : a.dev_v) + off;
+  s.ok = (host ? a.host_k : a.dev_k) != nullptr;
+  return s;
+}
+
 // Reductions over the four 16-lane groups of a wave (lanes n, n+16, n+32,
 // n+48), with the gfx950 lane-swap instructions: permlane16_swap pairs rows
 // 0-1 and 2-3, permlane32_swap the two halves.
@@ -494,8 +537,44 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   // Work queues: the host role has one; the HBM role has one per queue id
   // (blockIdx mod dev_queues), each owning the KV heads congruent to it, so
   // the workgroups that share an L2 share KV heads.
-  const bool host_role = (int)blockIdx.x < a.host_wgs;
-  const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
+  // Writer role (fused step only): the first writer_wgs workgroups copy the
+  // new rows from their HBM copy into their cache slots (PCIe writes when the
+  // slots are host-resident) while the other workgroups attend.
+  if ((int)blockIdx.x < a.writer_wgs) {
+    // (row, 16-byte chunk) pairs of the K and V rows, NT per pass, two passes
+    // in flight per thread
+    const int64_t chunks = (int64_t)a.hkv * D / 8;
+    const int64_t total = (int64_t)a.app.n_new * chunks;
+    const int64_t stride = (int64_t)a.writer_wgs * NT;
+    for (int64_t f0 = (int64_t)blockIdx.x * NT + tid; f0 < total; f0 += 2 * stride) {
+      u32x4 kv[2][2];
+      Slot sl[2];
+      int64_t c[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t f = f0 + j * stride;
+        sl[j] = Slot{nullptr, nullptr, false};
+        if (f < total) {
+          const int i = (int)(f / chunks);
+          c[j] = f - (int64_t)i * chunks;
+          sl[j] = append_slot(a.app, i);
+          const size_t src = (size_t)i * chunks * 8 + c[j] * 8;
+          kv[j][0] = *reinterpret_cast<const u32x4*>(a.fresh_k + src);
+          kv[j][1] = *reinterpret_cast<const u32x4*>(a.fresh_v + src);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (sl[j].ok) {
+          *reinterpret_cast<u32x4*>(sl[j].k + c[j] * 8) = kv[j][0];
+          *reinterpret_cast<u32x4*>(sl[j].v + c[j] * 8) = kv[j][1];
+        }
+    }
+    return;
+  }
+  const int bid = (int)blockIdx.x - a.writer_wgs;
+  const bool host_role = bid < a.host_wgs;
+  const int wg = host_role ? bid : bid - a.host_wgs;
   const int nq = host_role ? 1 : a.dev_queues;
   const int q = wg % nq;
   const int nwg = (host_role ? a.host_wgs : a.dev_wgs) / nq;
@@ -1129,47 +1208,6 @@ __global__ __launch_bounds__(kMergeWaveThreads) void merge_lse_wave_kernel(Merge
 // once to bf16, V stored as is.  Thread = (token, group of 8 rotation pairs);
 // it loops over the KV heads so each angle's sin/cos is computed once.
 // ---------------------------------------------------------------------------
-struct Slot {
-  uint16_t* k;
-  uint16_t* v;
-  bool ok;
-};
-
-__device__ __forceinline__ Slot append_slot(const AppendArgs& a, int i) {
-  Slot s{nullptr, nullptr, false};
-  const int b = a.seq_idx[i];
-  const int p = a.pos[i];
-  if (b < 0 || b >= a.batch || p < 0) return s;
-  int64_t row;
-  bool host;
-  if (a.page_size == 0) {
-    const int L = a.seq_lens[b];
-    if (p >= L) return s;
-    const int64_t nh = (int64_t)floor(a.ratio * (double)L);
-    host = p < nh;
-    if (host) {
-      if (nh > a.host_stride) return s;
-      row = (int64_t)b * a.host_stride + p;
-    } else {
-      if (L - nh > a.dev_stride) return s;
-      row = (int64_t)b * a.dev_stride + (p - nh);
-    }
-  } else {
-    const int lp = p / a.page_size;
-    if (lp >= a.max_pages) return s;
-    const int32_t e = a.page_table[(int64_t)b * a.max_pages + lp];
-    if (e < 0) return s;
-    host = (e & 1) != 0;
-    row = (int64_t)(e >> 1) * a.page_size + (p % a.page_size);
-  }
-  const int64_t cap = host ? a.host_rows : a.dev_rows;
-  if (row < 0 || row >= cap) return s;
-  const int64_t off = row * (int64_t)a.hkv * a.head_dim;
-  s.k = (host ? a.host_k : a.dev_k) + off;
-  s.v = (host ? a.host_v : a.dev_v) + off;
-  s.ok = (host ? a.host_k : a.dev_k) != nullptr;
-  return s;
-}
 
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   constexpr int QP = 4;  // rotation pairs per thread
@@ -1220,8 +1258,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
               (f64_to_bf16(xh[e1] * cs[e1] + xl[e1] * sn[e1]) << 16);
     }
     uint16_t* dst = sl.k + h * D;
-    *reinterpret_cast<uint2*>(dst + p0) = make_uint2(yl[0], yl[1]);
-    *reinterpret_cast<uint2*>(dst + half + p0) = make_uint2(yh[0], yh[1]);
+    if (!a.skip_slots) {
+      *reinterpret_cast<uint2*>(dst + p0) = make_uint2(yl[0], yl[1]);
+      *reinterpret_cast<uint2*>(dst + half + p0) = make_uint2(yh[0], yh[1]);
+    }
     if (a.fresh_k) {
       uint16_t* fk = a.fresh_k + (size_t)i * kvd + h * D;
       *reinterpret_cast<uint2*>(fk + p0) = make_uint2(yl[0], yl[1]);
@@ -1237,8 +1277,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         w0[e] = f32_to_bf16(vp[p0 + 2 * e]) | (f32_to_bf16(vp[p0 + 2 * e + 1]) << 16);
         w1[e] = f32_to_bf16(vp[half + p0 + 2 * e]) | (f32_to_bf16(vp[half + p0 + 2 * e + 1]) << 16);
       }
-      *reinterpret_cast<uint2*>(vd + p0) = make_uint2(w0[0], w0[1]);
-      *reinterpret_cast<uint2*>(vd + half + p0) = make_uint2(w1[0], w1[1]);
+      if (!a.skip_slots) {
+        *reinterpret_cast<uint2*>(vd + p0) = make_uint2(w0[0], w0[1]);
+        *reinterpret_cast<uint2*>(vd + half + p0) = make_uint2(w1[0], w1[1]);
+      }
       if (a.fresh_v) {
         uint16_t* fv = a.fresh_v + (size_t)i * kvd + h * D;
         *reinterpret_cast<uint2*>(fv + p0) = make_uint2(w0[0], w0[1]);
@@ -1248,8 +1290,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
       const uint2 v0 = *reinterpret_cast<const uint2*>(vs + p0);
       const uint2 v1 = *reinterpret_cast<const uint2*>(vs + half + p0);
-      *reinterpret_cast<uint2*>(vd + p0) = v0;
-      *reinterpret_cast<uint2*>(vd + half + p0) = v1;
+      if (!a.skip_slots) {
+        *reinterpret_cast<uint2*>(vd + p0) = v0;
+        *reinterpret_cast<uint2*>(vd + half + p0) = v1;
+      }
       if (a.fresh_v) {
         uint16_t* fv = a.fresh_v + (size_t)i * kvd + h * D;
         *reinterpret_cast<uint2*>(fv + p0) = v0;
@@ -1381,9 +1425,10 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
                   const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // heads per thread: all of them once rows alone give ~64K threads
+  // heads per thread: enough threads (~2^19) to hide load latency, sin/cos
+  // shared by the heads a thread covers
   const int64_t pairs = (int64_t)batch * (d / 2);
-  const int hpt = pairs >= 65536 ? hq : std::min(hq, 4);
+  const int hpt = (int)std::max<int64_t>(1, std::min<int64_t>(hq, pairs * hq >> 19));
   const int64_t total = pairs * ((hq + hpt - 1) / hpt);
   const int bx = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
   hipLaunchKernelGGL(rope_q_kernel, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
@@ -1401,7 +1446,7 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
 
 template <int D, int G>
 static hipError_t launch_prefill_dg(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
-  const int grid = a.host_wgs + a.dev_wgs;
+  const int grid = a.writer_wgs + a.host_wgs + a.dev_wgs;
   if (grid <= 0) return hipSuccess;
   if (a.pages)
     hipLaunchKernelGGL((prefill_split_kernel<D, G, true, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a, q_rot);
@@ -1478,11 +1523,12 @@ int launch_merge(const MergeArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_append(const AppendArgs& a, void* stream) {
+int launch_append(const AppendArgs& a, void* stream, int max_wgs) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t total = (int64_t)a.n_new * a.hkv * (a.head_dim / 8);
   const int64_t blocks = (total + kThreads - 1) / kThreads;
-  const int grid = (int)(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
+  const int cap = max_wgs > 0 ? std::min(max_wgs, 16384) : 16384;
+  const int grid = (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
   hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }

@@ -353,8 +353,10 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
   const int32_t ch = choose_chunk(host_reads * in.hkv, wh, 4, 256, 16384, align, in.host_chunk);
   // A prefill token-head costs a full 128-row MFMA pass, so HBM units are
-  // long: fewer partials to write and merge, LPT order evens out the tail.
-  const int32_t cd = choose_chunk(dev_reads * in.hkv, wd, 2, 1024, 1 << 16, align, in.dev_chunk);
+  // long: fewer partials to write and merge (none when every block fits one
+  // unit), longest-first order evens out the tail.  On the LLaMA-3-8B
+  // 2048-row case 2048-token units beat 1024 (0.105 vs 0.112 ms).
+  const int32_t cd = choose_chunk(dev_reads * in.hkv, wd, 2, 2048, 1 << 16, align, in.dev_chunk);
 
   // ---- items, split slots, row offsets and positions
   const int64_t T = q_start[B];

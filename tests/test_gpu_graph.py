@@ -103,3 +103,38 @@ def test_graph_replays_fused_paged(dk):
 
     _check_replays(dk, step, bufs)
     cache.free()
+
+
+def test_graph_replays_fused_prefill(dk):
+    # the fused prefill step forks the cache-slot writes onto a second stream
+    # and joins them back: the captured graph must replay it exactly
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, news, hq, hkv, d, r, th = [900, 300], [400, 300], 32, 8, 128, 0.7, 5e5
+    ks, vs = kv_raw(63, lens, hkv, d)
+    pre = [L - n for L, n in zip(lens, news)]
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th, upto=pre)
+    q = torch.from_numpy(np.concatenate([normal_bf16(63 + b, 1, (n, hq, d)) for b, n in enumerate(news)])
+                         .view(np.int16)).cuda()
+    kn = torch.from_numpy(np.concatenate([k[p:] for k, p in zip(ks, pre)]).view(np.int16)).cuda()
+    vn = torch.from_numpy(np.concatenate([v[p:] for v, p in zip(vs, pre)]).view(np.int16)).cuda()
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    T = int(q_start[-1])
+    info = dk.prefill_fused_plan(cache, 2, hq, q_start, pre, lens, r)
+    ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device="cuda")
+
+    class Bufs:
+        out_o = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+        out_lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        dk.prefill_fused(cache, q, q_start, pre, lens, r, 1 / math.sqrt(d), th, k_new=kn, v_new=vn,
+                         workspace=ws, out_o=Bufs.out_o, out_lse=Bufs.out_lse)
+
+    ref_o, ref_l = _check_replays(dk, step, Bufs)
+    ro, rl = O.prefill_sequence(np.concatenate([normal_bf16(63 + 1, 1, (news[1], hq, d))]), ks[1], vs[1], pre[1], th,
+                                1 / math.sqrt(d), heads=[0, 9, 31])
+    o = ref_o.cpu().numpy().astype(np.float64)[q_start[1]:, [0, 9, 31]]
+    l = ref_l.cpu().numpy().astype(np.float64)[q_start[1]:, [0, 9, 31]]
+    assert np.abs(o - ro).max() < 2e-3 and np.abs(l - rl).max() < 2e-3
+    cache.free()
