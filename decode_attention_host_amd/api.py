@@ -452,6 +452,9 @@ def prefill_fused(cache: KVCache, q: torch.Tensor, q_start, q_pos0, seq_lens, ra
     qs, qp, sl = _host_i32(q_start), _host_i32(q_pos0), _host_i32(seq_lens)
     B = len(qp)
     hidden = int(x.shape[1]) if x is not None else 0
+    if T == 0:
+        return (torch.empty((0, Hq, D), dtype=torch.float32, device=q.device),
+                torch.empty((0, Hq), dtype=torch.float32, device=q.device))
     if workspace is None:
         info = prefill_fused_plan(cache, B, Hq, qs, qp, sl, ratio, hidden)
         workspace = torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=q.device)

@@ -1225,6 +1225,8 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   dkv_status st = validate_desc(kv);
   if (st != DKV_OK) return st;
   if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (batch < 1 || !q_start) return set_err(DKV_ERR_INVALID, "batch >= 1 and q_start are required");
+  if (q_start[batch] == 0) return ok();  // no query rows: nothing is read or written
   if (!q || !part_o || !part_lse || !split_offsets || !workspace)
     return set_err(DKV_ERR_INVALID, "q, part_o, part_lse, split_offsets and workspace are required");
   if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
@@ -1278,6 +1280,8 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   dkv_status st = validate_desc(kv);
   if (st != DKV_OK) return st;
   if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
+  if (batch < 1 || !q_start) return set_err(DKV_ERR_INVALID, "batch >= 1 and q_start are required");
+  if (q_start[batch] == 0) return ok();  // no new rows: nothing is read or written
   if (!q || !out_o || !workspace) return set_err(DKV_ERR_INVALID, "q, out_o and workspace are required");
   if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
     return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");

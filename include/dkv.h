@@ -270,7 +270,8 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
  * causally: cached tokens below q_pos0[b] come from the tiers (staged into HBM
  * when several row blocks re-read host rows), the new rows from the copy.
  * Output: out_o [T][Hq][D] fp32, out_lse [T][Hq] fp32 (or NULL).  Workspace
- * size from dkv_prefill_fused_plan (hidden = 0 without projection).
+ * size from dkv_prefill_fused_plan (hidden = 0 without projection).  With
+ * T = 0 the call does nothing (and needs no buffers).
  * ---------------------------------------------------------------------- */
 dkv_status dkv_prefill_fused_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                                   const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,

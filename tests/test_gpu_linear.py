@@ -83,3 +83,12 @@ def test_linear_ratios_agree_and_llama_mlp_full_size(dk):
     rows = np.random.default_rng(0).choice(N, 64, replace=False)
     ref = O.linear(x, w[rows])
     _check(ys[1.0][:, rows], ref, K, "llama mlp sampled rows r=1")
+
+
+def test_linear_smallest_shapes(dk):
+    # one output row, K = 8 (a single 16-byte group, not a multiple of 32)
+    for N, K, m, r in [(1, 8, 1, 1.0), (1, 8, 3, 0.0), (2, 8, 1, 0.5), (65, 40, 2, 0.5)]:
+        w = normal_bf16(97, 5, (N, K))
+        x = normal_bf16(97, 4, (m, K))
+        y = _run(dk, w, x, r)
+        _check(y, O.linear(x, w), K, f"N={N} K={K} m={m} r={r}")

@@ -184,3 +184,40 @@ def test_fused_with_projection(dk):
         ro, rl = O.attention(q_rot[j], kst[:pos[j] + 1], vst[:pos[j] + 1], 1 / math.sqrt(d))
         _check(o[j], lse[j], ro, rl, f"projected row {j}")
     cache.free()
+
+
+def test_fused_edge_cases(dk):
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    hq, hkv, d, th, r = 8, 2, 64, 1e4, 0.5
+    lens = [50, 9]
+    ks, vs = kv_raw(140, lens, hkv, d)
+    # no query rows at all: nothing to do, no error
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    q0 = torch.empty((0, hq, d), dtype=torch.int16, device="cuda")
+    z = torch.empty((0, hkv, d), dtype=torch.int16, device="cuda")
+    o, l = dk.prefill_fused(cache, q0, [0, 0, 0], [50, 9], lens, r, 0.125, th, k_new=z, v_new=z)
+    assert o.shape[0] == 0
+    o2, l2, _ = dk.prefill(cache, q0, [0, 0, 0], [50, 9], lens, r, 0.125, th)
+    assert o2.shape[0] == 0
+    # one new row in the middle of a cache (rows after it stay invisible), and
+    # one row per sequence with the second sequence's row at position 0
+    news = [1, 1]
+    pre = [20, 0]
+    qs = [normal_bf16(141 + b, 1, (1, hq, d)) for b in range(2)]
+    q = torch.from_numpy(np.concatenate(qs).view(np.int16)).cuda()
+    kn = np.concatenate([ks[b][p:p + 1] for b, p in enumerate(pre)])
+    vn = np.concatenate([vs[b][p:p + 1] for b, p in enumerate(pre)])
+    o, l = dk.prefill_fused(cache, q, [0, 1, 2], pre, lens, r, 0.125, th,
+                            k_new=torch.from_numpy(kn.view(np.int16)).cuda(),
+                            v_new=torch.from_numpy(vn.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    o = o.cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    for b in range(2):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], pre[b], th, 0.125)
+        _check(o[b:b + 1], l[b:b + 1], ro, rl, f"edge seq {b}")
+    # position 0 sees only itself: every head's o is its KV head's V0 exactly
+    g = hq // hkv
+    assert np.array_equal(o[1], O.bf16_to_f64(vs[1][0])[np.arange(hq) // g])
+    cache.free()
