@@ -500,9 +500,11 @@ template <int NTW>
 constexpr int pf_threads() { return kPrefillRows / (16 * NTW) * 64; }
 
 // NTW: 16-column MFMA tiles (query-head rows / 16) per wave; the workgroup
-// holds kPrefillRows / (16 NTW) waves.  One tile per wave (8 waves, ~200
+// holds kPrefillRows / (16 NTW) waves.  One tile per wave (8 waves, ~210
 // VGPRs, two waves per SIMD) measured faster than two per wave (4 waves, one
-// wave per SIMD) on the LLaMA-3-8B 2048-row prefill: 0.112 vs 0.134 ms.
+// wave per SIMD) on the LLaMA-3-8B 2048-row prefill: 0.105 vs 0.131 ms, also
+// when the two-per-wave form interleaves one group's softmax with the other
+// group's MFMAs; 64-row workgroups (two per CU) gave 0.111 ms.
 template <int D, int G, bool PAGED, int NTW>
 __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a,
                                                                           const float* __restrict__ q_rot) {
@@ -751,77 +753,69 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
         }
       }
 
-      // ---- S^T = K . Q^T: 64 keys (four 16-key tiles) x 16*NTW query columns;
-      //      high parts first, then low parts, so no MFMA waits on the one before
+      // ---- per-tile compute, in pieces per 16-column group nt:
+      //   S^T = K . Q^T (64 keys x 16 columns), causal mask, softmax with the
+      //   lazily moved reference maximum, P^T into B operands, O^T += V^T . P^T.
+      // High-part MFMAs of all tiles are issued before the low-part ones so no
+      // MFMA waits on the one before it.
       floatx4 st[4][NTW];
+      uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
+      const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
+      auto load_k = [&](bf16x8_t (&kf)[KS][4]) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < 4; ++mt)
+            kf[ks][mt] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
+      };
+      auto s_mfma = [&](int nt, const bf16x8_t (&kf)[KS][4]) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8_t kf[4];
+        for (int mt = 0; mt < 4; ++mt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          kf[mt] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+        for (int ks = 0; ks < KS; ++ks) {
           const u32x4 qh = {qb_hi[nt][ks][0], qb_hi[nt][ks][1], qb_hi[nt][ks][2], qb_hi[nt][ks][3]};
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt], __builtin_bit_cast(bf16x8_t, qh), st[mt][nt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, qh),
+                                                                 st[mt][nt], 0, 0, 0);
           const u32x4 ql = {qb_lo[nt][ks][0], qb_lo[nt][ks][1], qb_lo[nt][ks][2], qb_lo[nt][ks][3]};
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt], __builtin_bit_cast(bf16x8_t, ql), st[mt][nt], 0, 0, 0);
+            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, ql),
+                                                                 st[mt][nt], 0, 0, 0);
         }
-      }
-      // ---- causal mask (keys past a row's position or past the item)
-      const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
-      if (need_mask) {
+      };
+      // causal mask and the reference-maximum update of column group nt
+      auto mask_rescale = [&](int nt) {
+        if (need_mask) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+            for (int i = 0; i < 4; ++i) {
+              const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
               st[mt][nt][i] = (tp >= 0 && tp <= rpos[nt]) ? st[mt][nt][i] : -INFINITY;
-          }
-      }
-      // ---- online softmax per query column, P^T straight into B operands
-      float m_new[NTW];
-      bool grow = false;
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[mt][nt][i]);
         mx = wave_max_rows4(mx);  // over the four lane groups of column n
-        m_new[nt] = (mx > m_run[nt] + kRescaleSlack) ? mx : m_run[nt];
-        grow |= m_new[nt] != m_run[nt];
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+        const float m_new = (mx > m_run[nt] + kRescaleSlack) ? mx : m_run[nt];
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run[nt]) != 0) {  // wave-uniform
           // 1 if this column kept its reference (also while it is still -inf),
           // 0 on its first finite maximum
-          const float alpha = m_new[nt] == m_run[nt] ? 1.f : exp2f(m_run[nt] - m_new[nt]);
+          const float alpha = m_new == m_run[nt] ? 1.f : exp2f(m_run[nt] - m_new);
           l_run[nt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) ot[nt][dt] *= alpha;
-          m_run[nt] = m_new[nt];
+          m_run[nt] = m_new;
         }
-      }
-      uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
+      };
+      // probabilities of column group nt, split into high/low bf16 B operands
+      auto probs = [&](int nt) {
         const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
         float pv[4][4];
         float ps = 0.f;
@@ -840,34 +834,48 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
           split_bf16(pv[2 * kt + 1][0], pv[2 * kt + 1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
           split_bf16(pv[2 * kt + 1][2], pv[2 * kt + 1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
         }
-      }
-      // ---- O^T += V^T . P^T over two 32-key k-steps (high parts, then low)
+      };
+      // V^T operands of both 32-key k-steps
+      auto load_v = [&](bf16x8_t (&va)[2][DT]) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8_t va[DT];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint8_t* vrow = vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 4) * 2;
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 32);
-          va[dt] = __builtin_bit_cast(bf16x8_t, (u32x4{v0[0], v0[1], v1[0], v1[1]}));
-        }
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint8_t* vrow = vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 4) * 2;
+            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
+            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 32);
+            va[kt][dt] = __builtin_bit_cast(bf16x8_t, (u32x4{v0[0], v0[1], v1[0], v1[1]}));
+          }
+      };
+      auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT]) {
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+        for (int kt = 0; kt < 2; ++kt) {
           const u32x4 ph = {pb_hi[nt][kt][0], pb_hi[nt][kt][1], pb_hi[nt][kt][2], pb_hi[nt][kt][3]};
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(bf16x8_t, ph), ot[nt][dt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, ph),
+                                                                 ot[nt][dt], 0, 0, 0);
           const u32x4 pl = {pb_lo[nt][kt][0], pb_lo[nt][kt][1], pb_lo[nt][kt][2], pb_lo[nt][kt][3]};
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(bf16x8_t, pl), ot[nt][dt], 0, 0, 0);
+            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, pl),
+                                                                 ot[nt][dt], 0, 0, 0);
         }
-      }
+      };
+      bf16x8_t kf[KS][4];
+      load_k(kf);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) s_mfma(nt, kf);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) mask_rescale(nt);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) probs(nt);
+      bf16x8_t va[2][DT];
+      load_v(va);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) pv_mfma(nt, va);
     }
+
 
     // ---- write this unit's partial for every valid row
 #pragma unroll
