@@ -493,6 +493,16 @@ __device__ __forceinline__ float wave_sum_rows4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Key order inside a V^T row: within each 32-key step, lane group j of an
+// MFMA operand takes keys 4j..4j+3 and 16+4j..16+4j+3 (the keys its S^T
+// accumulators hold), so those eight keys are stored next to each other and
+// the operand is one 16-byte LDS read.  Keys of one aligned quad stay
+// contiguous.
+__device__ __forceinline__ int vt_slot(int key) {
+  const int q = (key & 31) >> 2;
+  return (key & ~31) + ((q & 3) << 3) + ((q >> 2) << 2) + (key & 3);
+}
+
 // Headroom of the lazily updated softmax reference maximum (log2 units).
 constexpr float kRescaleSlack = 8.f;
 
@@ -513,7 +523,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
   constexpr int DT = D / 16;                   // 16-row d tiles of O^T
   constexpr int KPITCH = D * 2 + 16;           // bytes per K row in LDS
-  constexpr int VPB = kTile * 2 + 8;           // bytes per V^T row (one d, 64 keys)
+  constexpr int VPB = kTile * 2 + 16;          // bytes per V^T row (one d, 64 keys)
   constexpr int CPR = D / 8;                   // 16-byte chunks per KV row
   constexpr int NCK = kTile * CPR / NT;        // K chunks per thread
   constexpr int TPT = NCK;                     // V keys per thread (one 8-dim chunk)
@@ -724,7 +734,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1, sh = (e & 1) * 16;
-        uint8_t* dst = vt_lds + (vc * 8 + e) * VPB + vq * TPT * 2;
+        uint8_t* dst = vt_lds + (vc * 8 + e) * VPB + vt_slot(vq * TPT) * 2;
         if constexpr (TPT == 1) {
           *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((vreg[0][w] >> sh) & 0xffffu);
         } else {
@@ -841,10 +851,8 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const uint8_t* vrow = vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 4) * 2;
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 32);
-            va[kt][dt] = __builtin_bit_cast(bf16x8_t, (u32x4{v0[0], v0[1], v1[0], v1[1]}));
+            va[kt][dt] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4*>(vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 8) * 2));
           }
       };
       auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT]) {
