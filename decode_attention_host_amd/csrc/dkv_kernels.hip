@@ -503,6 +503,21 @@ __device__ __forceinline__ int vt_slot(int key) {
   return (key & ~31) + ((q & 3) << 3) + ((q >> 2) << 2) + (key & 3);
 }
 
+// A plan item at a workgroup-uniform address, read through the constant
+// address space: scalar loads, counted apart from the vector loads in flight,
+// so fetching the next unit's item does not wait for the tile loads.
+__device__ __forceinline__ PrefillItem load_item_uniform(const PrefillItem* p) {
+  static_assert(sizeof(PrefillItem) == 64, "item size");
+  typedef __attribute__((address_space(4))) const u32x4 ConstVec;
+  const ConstVec* w = (const ConstVec*)p;
+  struct Raw {
+    u32x4 v[4];
+  } t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.v[i] = w[i];
+  return __builtin_bit_cast(PrefillItem, t);
+}
+
 // Headroom of the lazily updated softmax reference maximum (log2 units).
 constexpr float kRescaleSlack = 8.f;
 
@@ -592,19 +607,18 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   const int nwg = (host_role ? a.host_wgs : a.dev_wgs) / nq;
   const int hpq = a.hkv / nq;  // KV heads per queue
   const int nunits = (host_role ? a.n_host_items : a.n_dev_items) * hpq;
-  const PrefillItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
+  const PrefillItem* items = host_role ? a.host_items : a.dev_items;
   int* counter = a.unit_counters + (host_role ? kPfHostCounter : q);
 
   struct Src {
     const uint16_t* k;
     const uint16_t* v;
-    bool nt;
   };
   auto src_of = [&](const PrefillItem& it) -> Src {
-    if (it.pool == kPoolHost) return Src{a.host_k, a.host_v, true};
-    if (it.pool == kPoolDev) return Src{a.dev_k, a.dev_v, false};
-    if (it.pool == kPoolFresh) return Src{a.fresh_k, a.fresh_v, false};
-    return Src{a.stage_k, a.stage_v, false};
+    if (it.pool == kPoolHost) return Src{a.host_k, a.host_v};
+    if (it.pool == kPoolDev) return Src{a.dev_k, a.dev_v};
+    if (it.pool == kPoolFresh) return Src{a.fresh_k, a.fresh_v};
+    return Src{a.stage_k, a.stage_v};
   };
   // pool row of token `tok` of an item (tokens past the end read token 0);
   // fresh rows are contiguous in either layout
@@ -625,11 +639,19 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     return it.tok0 + tok;
   };
 
-  u32x4 kreg[NCK], vreg[TPT];
-  int treg = -1;
-  // Element offsets of this thread's K and V loads for tile 0 of a unit;
-  // tile t adds t * 64 rows.  Rows past the item's end are clamped to its
-  // first token: real data whose keys the mask removes (p = 0 exactly).
+  // Tiles stream through two register sets: while a tile is computed out of
+  // LDS, the loads of the next two tiles are in flight (prefetch distance
+  // two).  Each set carries the unit and tile index its data belongs to.
+  struct TileRegs {
+    u32x4 k[NCK];
+    u32x4 v[TPT];
+    int tpos;
+    int u;     // unit, nunits when the stream has ended
+    int tile;  // tile index inside the unit
+  };
+  // Element offsets of this thread's K and V loads for the prefetch cursor's
+  // current tile.  Rows past the item's end are clamped to its first token:
+  // real data whose keys the mask removes (p = 0 exactly).
   int64_t koff[NCK], voff[TPT];
   auto set_offsets = [&](const PrefillItem& it, int kvh, int tile) {
     const int t0 = tile * kTile;
@@ -641,52 +663,98 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 #pragma unroll
     for (int e = 0; e < TPT; ++e) voff[e] = (row_of(it, t0 + vq * TPT + e) * a.hkv + kvh) * D + vc * 8;
   };
-  // Host rows stream once over the link (non-temporal); HBM and staged rows
-  // are re-read by later row blocks and stay cacheable.
-  auto load_tile = [&](const PrefillItem& it, const Src& sp, int kvh, int tile) {
+  // Loads of the prefetch cursor's next tile into r.  Every call issues the
+  // same loads, so the count of loads in flight per step is fixed and the
+  // wait before a set is staged covers that set alone: once the stream has
+  // ended the addresses fall back to the first bytes of q_rot (the tags mark
+  // such a set as empty).
+  auto load_tile = [&](TileRegs& r, bool live, const PrefillItem& it, const Src& sp, int kvh, int tile) {
     const int t0 = tile * kTile;
-    // contiguous items step the offsets by whole tiles except where the
-    // tile runs past the item (clamping) ; paged items look up every tile
-    if ((PAGED && it.pool != kPoolFresh) || tile == 0 || t0 + kTile > it.n_tok) {
-      set_offsets(it, kvh, tile);
-    } else {
-      const int64_t step = (int64_t)kTile * a.hkv * D;
+    if (live) {
+      // contiguous items step the offsets by whole tiles except where the
+      // tile runs past the item (clamping) ; paged items look up every tile
+      if ((PAGED && it.pool != kPoolFresh) || tile == 0 || t0 + kTile > it.n_tok) {
+        set_offsets(it, kvh, tile);
+      } else {
+        const int64_t step = (int64_t)kTile * a.hkv * D;
 #pragma unroll
-      for (int c = 0; c < NCK; ++c) koff[c] += step;
+        for (int c = 0; c < NCK; ++c) koff[c] += step;
 #pragma unroll
-      for (int e = 0; e < TPT; ++e) voff[e] += step;
+        for (int e = 0; e < TPT; ++e) voff[e] += step;
+      }
     }
-    if (sp.nt) {
+    const uint16_t* dummy = reinterpret_cast<const uint16_t*>(q_rot);
 #pragma unroll
-      for (int c = 0; c < NCK; ++c) kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp.k + koff[c]));
+    for (int c = 0; c < NCK; ++c)
+      r.k[c] = *reinterpret_cast<const u32x4*>(live ? sp.k + koff[c] : dummy + c * 8);
 #pragma unroll
-      for (int e = 0; e < TPT; ++e) vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp.v + voff[e]));
-    } else {
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) kreg[c] = *reinterpret_cast<const u32x4*>(sp.k + koff[c]);
-#pragma unroll
-      for (int e = 0; e < TPT; ++e) vreg[e] = *reinterpret_cast<const u32x4*>(sp.v + voff[e]);
-    }
-    if (tid < kTile) treg = pos_of(it, t0 + tid);
+    for (int e = 0; e < TPT; ++e)
+      r.v[e] = *reinterpret_cast<const u32x4*>(live ? sp.v + voff[e] : dummy + (NCK + e) * 8);
+    r.tpos = (live && tid < kTile) ? pos_of(it, t0 + tid) : -1;
   };
 
-  int u = wg / nq;
-  PrefillItem it{};
-  Src src{};
-  int kvh = 0;
-  if (u < nunits) {
-    it = items[u / hpq];
-    kvh = q + nq * (u % hpq);
-    src = src_of(it);
-    load_tile(it, src, kvh, 0);
+  // ---- prefetch cursor: the unit and tile whose loads are issued next.
+  // A workgroup's first unit is wg / nq; later ones come from the queue's
+  // counter (claimed by thread 0, read by all after a barrier).
+  int pu = wg / nq;
+  PrefillItem pit{};
+  Src psrc{};
+  int pkvh = 0, ptile = 0, pntiles = 0;
+  auto open_unit = [&]() {
+    if (pu < nunits) {
+      pit = load_item_uniform(items + pu / hpq);
+      pkvh = q + nq * (pu % hpq);
+      psrc = src_of(pit);
+      ptile = 0;
+      pntiles = (pit.n_tok + kTile - 1) / kTile;
+    }
+  };
+  auto needs_claim = [&]() { return pu < nunits && ptile == pntiles; };  // workgroup-uniform
+  auto claim = [&](bool c) {  // between two barriers
+    if (c && tid == 0) s_next = nwg + atomicAdd(counter, 1);
+  };
+  auto after_claim = [&](bool c) {  // after the barrier that follows claim()
+    if (c) {
+      pu = __builtin_amdgcn_readfirstlane(s_next);
+      open_unit();
+    }
+  };
+  auto issue = [&](TileRegs& r) {
+    const bool live = pu < nunits;
+    load_tile(r, live, pit, psrc, pkvh, ptile);
+    r.u = live ? pu : nunits;
+    r.tile = live ? ptile++ : 0;
+  };
+
+  TileRegs ra, rb;
+  open_unit();
+  issue(ra);
+  {
+    const bool c = needs_claim();
+    claim(c);
+    __syncthreads();
+    after_claim(c);
+    issue(rb);
   }
-  while (u < nunits) {
-    const int ntiles = (it.n_tok + kTile - 1) / kTile;
-    // ---- query operand (B of S^T): column n of tile nt = query-head row
-    //      rho = 16*(NTW*wave + nt) + n = (row rho/G, head rho%G)
-    uint32_t qb_hi[NTW][KS][4], qb_lo[NTW][KS][4];
-    int rpos[NTW];
-    bool rvalid[NTW];
+
+  // ---- compute cursor: the unit whose tiles are being reduced
+  PrefillItem it{};
+  int kvh = 0, ntiles = 0;
+  // query operand (B of S^T): column n of tile nt = query-head row
+  // rho = 16*(NTW*wave + nt) + n = (row rho/G, head rho%G)
+  uint32_t qb_hi[NTW][KS][4], qb_lo[NTW][KS][4];
+  int rpos[NTW];
+  bool rvalid[NTW];
+  // m_run: reference maximum of the scores (log2 units); it only moves when
+  // the running maximum exceeds it by more than kRescaleSlack, so most tiles
+  // skip rescaling O (probabilities then stay <= 2^kRescaleSlack).
+  float m_run[NTW], l_run[NTW];
+  floatx4 ot[NTW][DT];
+
+  auto begin_unit = [&](int u) {
+    it = load_item_uniform(items + u / hpq);
+    kvh = q + nq * (u % hpq);
+    ntiles = (it.n_tok + kTile - 1) / kTile;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int rho = (wave * NTW + nt) * 16 + n;
@@ -705,187 +773,15 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
         split_bf16(x1[0], x1[1], qb_hi[nt][ks][2], qb_lo[nt][ks][2]);
         split_bf16(x1[2], x1[3], qb_hi[nt][ks][3], qb_lo[nt][ks][3]);
       }
-    }
-    // m_run: reference maximum of the scores (log2 units); it only moves when
-    // the running maximum exceeds it by more than kRescaleSlack, so most tiles
-    // skip rescaling O (probabilities then stay <= 2^kRescaleSlack).
-    float m_run[NTW], l_run[NTW];
-    floatx4 ot[NTW][DT];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
       m_run[nt] = -INFINITY;
       l_run[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) ot[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+  };
 
-    int next_u = nunits;
-    PrefillItem nit{};
-    Src nsrc{};
-    int nkvh = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-      __syncthreads();  // previous tile's readers are done
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) {
-        const int chunk = tid + c * NT;
-        *reinterpret_cast<u32x4*>(k_lds + (chunk / CPR) * KPITCH + (chunk % CPR) * 16) = kreg[c];
-      }
-      // V^T: row d = 8*vc + e holds keys vq*TPT .. vq*TPT + TPT-1
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        uint8_t* dst = vt_lds + (vc * 8 + e) * VPB + vt_slot(vq * TPT) * 2;
-        if constexpr (TPT == 1) {
-          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((vreg[0][w] >> sh) & 0xffffu);
-        } else {
-          const uint32_t k01 = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[TPT > 1 ? 1 : 0][w] >> sh) & 0xffffu) << 16);
-          if constexpr (TPT == 4) {
-            const uint32_t k23 = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<u32x2*>(dst) = u32x2{k01, k23};
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = k01;
-          }
-        }
-      }
-      if (tid < kTile) tpos_lds[tid] = treg;
-      const bool last = tile + 1 == ntiles;
-      if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
-      __syncthreads();
-      if (!last) {
-        load_tile(it, src, kvh, tile + 1);
-      } else {
-        next_u = s_next;
-        if (next_u < nunits) {
-          nit = items[next_u / hpq];
-          nkvh = q + nq * (next_u % hpq);
-          nsrc = src_of(nit);
-          load_tile(nit, nsrc, nkvh, 0);
-        }
-      }
-
-      // ---- per-tile compute, in pieces per 16-column group nt:
-      //   S^T = K . Q^T (64 keys x 16 columns), causal mask, softmax with the
-      //   lazily moved reference maximum, P^T into B operands, O^T += V^T . P^T.
-      // High-part MFMAs of all tiles are issued before the low-part ones so no
-      // MFMA waits on the one before it.
-      floatx4 st[4][NTW];
-      uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
-      const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
-      auto load_k = [&](bf16x8_t (&kf)[KS][4]) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            kf[ks][mt] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
-      };
-      auto s_mfma = [&](int nt, const bf16x8_t (&kf)[KS][4]) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 qh = {qb_hi[nt][ks][0], qb_hi[nt][ks][1], qb_hi[nt][ks][2], qb_hi[nt][ks][3]};
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, qh),
-                                                                 st[mt][nt], 0, 0, 0);
-          const u32x4 ql = {qb_lo[nt][ks][0], qb_lo[nt][ks][1], qb_lo[nt][ks][2], qb_lo[nt][ks][3]};
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, ql),
-                                                                 st[mt][nt], 0, 0, 0);
-        }
-      };
-      // causal mask and the reference-maximum update of column group nt
-      auto mask_rescale = [&](int nt) {
-        if (need_mask) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
-              st[mt][nt][i] = (tp >= 0 && tp <= rpos[nt]) ? st[mt][nt][i] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[mt][nt][i]);
-        mx = wave_max_rows4(mx);  // over the four lane groups of column n
-        const float m_new = (mx > m_run[nt] + kRescaleSlack) ? mx : m_run[nt];
-        if (__builtin_amdgcn_ballot_w64(m_new != m_run[nt]) != 0) {  // wave-uniform
-          // 1 if this column kept its reference (also while it is still -inf),
-          // 0 on its first finite maximum
-          const float alpha = m_new == m_run[nt] ? 1.f : exp2f(m_run[nt] - m_new);
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) ot[nt][dt] *= alpha;
-          m_run[nt] = m_new;
-        }
-      };
-      // probabilities of column group nt, split into high/low bf16 B operands
-      auto probs = [&](int nt) {
-        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-        float pv[4][4];
-        float ps = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[mt][i] = __builtin_amdgcn_exp2f(st[mt][nt][i] - m_use);  // -inf -> 0
-            ps += pv[mt][i];
-          }
-        l_run[nt] += ps;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          split_bf16(pv[2 * kt][0], pv[2 * kt][1], pb_hi[nt][kt][0], pb_lo[nt][kt][0]);
-          split_bf16(pv[2 * kt][2], pv[2 * kt][3], pb_hi[nt][kt][1], pb_lo[nt][kt][1]);
-          split_bf16(pv[2 * kt + 1][0], pv[2 * kt + 1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
-          split_bf16(pv[2 * kt + 1][2], pv[2 * kt + 1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
-        }
-      };
-      // V^T operands of both 32-key k-steps
-      auto load_v = [&](bf16x8_t (&va)[2][DT]) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            va[kt][dt] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4*>(vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 8) * 2));
-          }
-      };
-      auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT]) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const u32x4 ph = {pb_hi[nt][kt][0], pb_hi[nt][kt][1], pb_hi[nt][kt][2], pb_hi[nt][kt][3]};
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, ph),
-                                                                 ot[nt][dt], 0, 0, 0);
-          const u32x4 pl = {pb_lo[nt][kt][0], pb_lo[nt][kt][1], pb_lo[nt][kt][2], pb_lo[nt][kt][3]};
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, pl),
-                                                                 ot[nt][dt], 0, 0, 0);
-        }
-      };
-      bf16x8_t kf[KS][4];
-      load_k(kf);
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) s_mfma(nt, kf);
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) mask_rescale(nt);
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) probs(nt);
-      bf16x8_t va[2][DT];
-      load_v(va);
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) pv_mfma(nt, va);
-    }
-
-
-    // ---- write this unit's partial for every valid row
+  // ---- this unit's partial for every valid row
+  auto end_unit = [&]() {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const float l = wave_sum_rows4(l_run[nt]);
@@ -902,10 +798,176 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
       if (j4 == 0)
         a.part_lse[head] = empty ? -INFINITY : (m_run[nt] + log2f(l)) * 0.69314718055994530942f;
     }
-    u = next_u;
-    it = nit;
-    src = nsrc;
-    kvh = nkvh;
+  };
+
+  // One tile: stage set r in LDS, refill r with the tile two ahead, reduce.
+  // A set past the end of the stream is staged and refilled (with the same
+  // loads as any other) but not reduced.
+  auto step = [&](TileRegs& r) {
+    const int tile = r.tile;
+    const bool work = r.u < nunits;
+    if (work && tile == 0) begin_unit(r.u);
+    __syncthreads();  // previous tile's readers are done
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      const int chunk = tid + c * NT;
+      *reinterpret_cast<u32x4*>(k_lds + (chunk / CPR) * KPITCH + (chunk % CPR) * 16) = r.k[c];
+    }
+    // V^T: row d = 8*vc + e holds keys vq*TPT .. vq*TPT + TPT-1
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      uint8_t* dst = vt_lds + (vc * 8 + e) * VPB + vt_slot(vq * TPT) * 2;
+      if constexpr (TPT == 1) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((r.v[0][w] >> sh) & 0xffffu);
+      } else {
+        const uint32_t k01 = ((r.v[0][w] >> sh) & 0xffffu) | (((r.v[TPT > 1 ? 1 : 0][w] >> sh) & 0xffffu) << 16);
+        if constexpr (TPT == 4) {
+          const uint32_t k23 = ((r.v[2][w] >> sh) & 0xffffu) | (((r.v[3][w] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<u32x2*>(dst) = u32x2{k01, k23};
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = k01;
+        }
+      }
+    }
+    if (tid < kTile) tpos_lds[tid] = r.tpos;
+    const bool c = needs_claim();
+    claim(c);
+    __syncthreads();
+    after_claim(c);
+    issue(r);
+
+    if (!work) return;
+
+    // ---- per-tile compute, in pieces per 16-column group nt:
+    //   S^T = K . Q^T (64 keys x 16 columns), causal mask, softmax with the
+    //   lazily moved reference maximum, P^T into B operands, O^T += V^T . P^T.
+    // High-part MFMAs of all tiles are issued before the low-part ones so no
+    // MFMA waits on the one before it.
+    floatx4 st[4][NTW];
+    uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
+    const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
+    auto load_k = [&](bf16x8_t (&kf)[KS][4]) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          kf[ks][mt] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
+    };
+    auto s_mfma = [&](int nt, const bf16x8_t (&kf)[KS][4]) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 qh = {qb_hi[nt][ks][0], qb_hi[nt][ks][1], qb_hi[nt][ks][2], qb_hi[nt][ks][3]};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, qh),
+                                                               st[mt][nt], 0, 0, 0);
+        const u32x4 ql = {qb_lo[nt][ks][0], qb_lo[nt][ks][1], qb_lo[nt][ks][2], qb_lo[nt][ks][3]};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, ql),
+                                                               st[mt][nt], 0, 0, 0);
+      }
+    };
+    // causal mask and the reference-maximum update of column group nt
+    auto mask_rescale = [&](int nt) {
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
+            st[mt][nt][i] = (tp >= 0 && tp <= rpos[nt]) ? st[mt][nt][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[mt][nt][i]);
+      mx = wave_max_rows4(mx);  // over the four lane groups of column n
+      const float m_new = (mx > m_run[nt] + kRescaleSlack) ? mx : m_run[nt];
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[nt]) != 0) {  // wave-uniform
+        // 1 if this column kept its reference (also while it is still -inf),
+        // 0 on its first finite maximum
+        const float alpha = m_new == m_run[nt] ? 1.f : exp2f(m_run[nt] - m_new);
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) ot[nt][dt] *= alpha;
+        m_run[nt] = m_new;
+      }
+    };
+    // probabilities of column group nt, split into high/low bf16 B operands
+    auto probs = [&](int nt) {
+      const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+      float pv[4][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[mt][i] = __builtin_amdgcn_exp2f(st[mt][nt][i] - m_use);  // -inf -> 0
+          ps += pv[mt][i];
+        }
+      l_run[nt] += ps;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        split_bf16(pv[2 * kt][0], pv[2 * kt][1], pb_hi[nt][kt][0], pb_lo[nt][kt][0]);
+        split_bf16(pv[2 * kt][2], pv[2 * kt][3], pb_hi[nt][kt][1], pb_lo[nt][kt][1]);
+        split_bf16(pv[2 * kt + 1][0], pv[2 * kt + 1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
+        split_bf16(pv[2 * kt + 1][2], pv[2 * kt + 1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
+      }
+    };
+    // V^T operands of both 32-key k-steps
+    auto load_v = [&](bf16x8_t (&va)[2][DT]) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          va[kt][dt] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4*>(vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 8) * 2));
+        }
+    };
+    auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT]) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const u32x4 ph = {pb_hi[nt][kt][0], pb_hi[nt][kt][1], pb_hi[nt][kt][2], pb_hi[nt][kt][3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, ph),
+                                                               ot[nt][dt], 0, 0, 0);
+        const u32x4 pl = {pb_lo[nt][kt][0], pb_lo[nt][kt][1], pb_lo[nt][kt][2], pb_lo[nt][kt][3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, pl),
+                                                               ot[nt][dt], 0, 0, 0);
+      }
+    };
+    bf16x8_t kf[KS][4];
+    load_k(kf);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) s_mfma(nt, kf);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) mask_rescale(nt);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) probs(nt);
+    bf16x8_t va[2][DT];
+    load_v(va);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) pv_mfma(nt, va);
+
+    if (tile + 1 == ntiles) end_unit();
+  };
+  // The two sets alternate; the stream ends when a set carries no unit.  The
+  // loop has one exit and both steps run on every pass, so on every path the
+  // other set's loads were issued after this set's: the wait before staging
+  // a set leaves the other set's loads in flight.
+  while (ra.u < nunits) {
+    step(ra);
+    step(rb);
   }
 }
 
