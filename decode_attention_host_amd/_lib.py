@@ -76,6 +76,8 @@ class Tuning(C.Structure):
         ("stage_max_mib", C.c_int32),
         ("host_bw_gbs", C.c_double),
         ("dev_bw_gbs", C.c_double),
+        ("writer_wgs", C.c_int32),
+        ("reserved", C.c_int32),
     ]
 
 

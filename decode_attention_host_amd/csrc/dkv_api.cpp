@@ -513,9 +513,10 @@ dkv_status dkv_set_tuning(const dkv_tuning* t) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   if (t) {
     if (t->num_cus < 0 || t->host_wgs < 0 || t->dev_wgs < 0 || t->host_chunk < 0 ||
-        t->dev_chunk < 0 || !(t->host_bw_gbs >= 0) || !(t->dev_bw_gbs >= 0))
+        t->dev_chunk < 0 || !(t->host_bw_gbs >= 0) || !(t->dev_bw_gbs >= 0) || t->writer_wgs < 0)
       return set_err(DKV_ERR_INVALID, "tuning fields must be >= 0");
-    if (t->host_wgs > 65535 || t->dev_wgs > 65535)
+    if (t->reserved != 0) return set_err(DKV_ERR_INVALID, "tuning.reserved must be 0");
+    if (t->host_wgs > 65535 || t->dev_wgs > 65535 || t->writer_wgs > 65535)
       return set_err(DKV_ERR_INVALID, "workgroup counts must be <= 65535");
     g_tune = *t;
   } else {
@@ -1207,7 +1208,9 @@ static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, con
   if (writers) {
     // a few workgroups keep the host link busy with the slot writes
     a.app = *writers;
-    a.writer_wgs = (int32_t)std::min<int64_t>(64, std::max<int64_t>(1, writers->n_new / 8));
+    const int32_t tuned = tuning_snapshot(nullptr).writer_wgs;
+    a.writer_wgs = tuned > 0 ? std::min<int32_t>(tuned, std::max<int32_t>(1, writers->n_new))
+                             : (int32_t)std::min<int64_t>(64, std::max<int64_t>(1, writers->n_new / 8));
   }
   TimedLaunch t_attn(DKV_KERNEL_PREFILL, s);
   he = (hipError_t)dkv::launch_prefill(a, q_rot, stream);

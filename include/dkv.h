@@ -359,6 +359,9 @@ typedef struct dkv_tuning {
   int32_t stage_max_mib;  /* prefill: HBM staging budget in MiB (0: 4096, < 0: never stage) */
   double host_bw_gbs;    /* host-link read bandwidth (0: 57) */
   double dev_bw_gbs;     /* HBM read bandwidth (0: 5300) */
+  int32_t writer_wgs;    /* fused prefill: workgroups writing the new rows into
+                            their cache slots (0: auto) */
+  int32_t reserved;      /* must be 0 */
 } dkv_tuning;
 
 dkv_status dkv_set_tuning(const dkv_tuning* tuning); /* NULL restores defaults */

@@ -168,6 +168,15 @@ def test_validation_errors_before_any_hip_call(L):
     # tuning
     t = dkv_lib.Tuning(); t.host_wgs = -1
     assert L.dkv_set_tuning(C.byref(t)) == dkv_lib.DKV_ERR_INVALID
+    t = dkv_lib.Tuning(); t.writer_wgs = -1
+    assert L.dkv_set_tuning(C.byref(t)) == dkv_lib.DKV_ERR_INVALID
+    t = dkv_lib.Tuning(); t.reserved = 1
+    assert L.dkv_set_tuning(C.byref(t)) == dkv_lib.DKV_ERR_INVALID
+    t = dkv_lib.Tuning(); t.writer_wgs = 16
+    assert L.dkv_set_tuning(C.byref(t)) == dkv_lib.DKV_OK
+    got = dkv_lib.Tuning()
+    assert L.dkv_get_tuning(C.byref(got)) == dkv_lib.DKV_OK and got.writer_wgs == 16
+    assert L.dkv_set_tuning(None) == dkv_lib.DKV_OK
 
 
 def test_append_workspace_size(L):
