@@ -36,6 +36,8 @@ static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
 // Query-head rows per prefill workgroup: 4 waves x 32 rows (two 16-column
 // MFMA tiles each).  A row block holds kPrefillRows / G query rows.
 constexpr int kPrefillRows = 128;
+// Keys per prefill tile (one LDS staging step).
+constexpr int kPfTile = 128;
 
 // Where a prefill item's tokens are read from.
 // kPoolFresh: the new rows themselves, written to HBM by the fused step's

@@ -534,6 +534,11 @@ template <int D, int G, bool PAGED, int NTW>
 __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a,
                                                                           const float* __restrict__ q_rot) {
   constexpr int NT = pf_threads<NTW>();
+  constexpr int PT = kPfTile;                  // keys per tile
+  constexpr int HT = PT / 64;                  // 64-key halves per tile
+  constexpr int NSET = PT == 64 ? 2 : 1;       // register sets in flight
+  constexpr int MT = PT / 16;                  // 16-key blocks per tile
+  constexpr int KT = PT / 32;                  // 32-key k-steps of P.V per tile
   constexpr int QB = kPrefillRows / G;
   constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
   constexpr int DT = D / 16;                   // 16-row d tiles of O^T
@@ -542,17 +547,17 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   // 64-bank LDS, which serves them at ~245 B/clk per CU on MI355X against
   // ~126 B/clk with a 16-byte pad (measured).
   constexpr int KPITCH = D * 2 + 32;           // bytes per K row in LDS
-  constexpr int VPB = kTile * 2 + 32;          // bytes per V^T row (one d, 64 keys)
+  constexpr int VPB = PT * 2 + 32;             // bytes per V^T row (one d, PT keys)
   constexpr int CPR = D / 8;                   // 16-byte chunks per KV row
-  constexpr int NCK = kTile * CPR / NT;        // K chunks per thread
+  constexpr int NCK = PT * CPR / NT;           // K chunks per thread
   constexpr int TPT = NCK;                     // V keys per thread (one 8-dim chunk)
-  constexpr int KQ = kTile / TPT;              // V key groups per tile
+  constexpr int KQ = PT / TPT;                 // V key groups per tile
   static_assert(TPT == 1 || TPT == 2 || TPT == 4, "tile shape");
   static_assert(KQ * CPR == NT, "V staging covers the tile");
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[PT * KPITCH];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[D * VPB];
-  __shared__ int tpos_lds[kTile];
+  __shared__ int tpos_lds[PT];
   __shared__ int s_next;
 
   const int tid = threadIdx.x;
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   // real data whose keys the mask removes (p = 0 exactly).
   int64_t koff[NCK], voff[TPT];
   auto set_offsets = [&](const PrefillItem& it, int kvh, int tile) {
-    const int t0 = tile * kTile;
+    const int t0 = tile * PT;
 #pragma unroll
     for (int c = 0; c < NCK; ++c) {
       const int chunk = tid + c * NT;
@@ -673,14 +678,14 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   // ended the addresses fall back to the first bytes of q_rot (the tags mark
   // such a set as empty).
   auto load_tile = [&](TileRegs& r, bool live, const PrefillItem& it, const Src& sp, int kvh, int tile) {
-    const int t0 = tile * kTile;
+    const int t0 = tile * PT;
     if (live) {
       // contiguous items step the offsets by whole tiles except where the
       // tile runs past the item (clamping) ; paged items look up every tile
-      if ((PAGED && it.pool != kPoolFresh) || tile == 0 || t0 + kTile > it.n_tok) {
+      if ((PAGED && it.pool != kPoolFresh) || tile == 0 || t0 + PT > it.n_tok) {
         set_offsets(it, kvh, tile);
       } else {
-        const int64_t step = (int64_t)kTile * a.hkv * D;
+        const int64_t step = (int64_t)PT * a.hkv * D;
 #pragma unroll
         for (int c = 0; c < NCK; ++c) koff[c] += step;
 #pragma unroll
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 #pragma unroll
     for (int e = 0; e < TPT; ++e)
       r.v[e] = *reinterpret_cast<const u32x4*>(live ? sp.v + voff[e] : dummy + (NCK + e) * 8);
-    r.tpos = (live && tid < kTile) ? pos_of(it, t0 + tid) : -1;
+    r.tpos = (live && tid < PT) ? pos_of(it, t0 + tid) : -1;
   };
 
   // ---- prefetch cursor: the unit and tile whose loads are issued next.
@@ -710,7 +715,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
       pkvh = q + nq * (pu % hpq);
       psrc = src_of(pit);
       ptile = 0;
-      pntiles = (pit.n_tok + kTile - 1) / kTile;
+      pntiles = (pit.n_tok + PT - 1) / PT;
     }
   };
   auto needs_claim = [&]() { return pu < nunits && ptile == pntiles; };  // workgroup-uniform
@@ -733,7 +738,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   TileRegs ra, rb;
   open_unit();
   issue(ra);
-  {
+  if constexpr (NSET == 2) {
     const bool c = needs_claim();
     claim(c);
     __syncthreads();
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   auto begin_unit = [&](int u) {
     it = load_item_uniform(items + u / hpq);
     kvh = q + nq * (u % hpq);
-    ntiles = (it.n_tok + kTile - 1) / kTile;
+    ntiles = (it.n_tok + PT - 1) / PT;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int rho = (wave * NTW + nt) * 16 + n;
@@ -834,7 +839,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
         }
       }
     }
-    if (tid < kTile) tpos_lds[tid] = r.tpos;
+    if (tid < PT) tpos_lds[tid] = r.tpos;
     const bool c = needs_claim();
     claim(c);
     __syncthreads();
@@ -848,39 +853,41 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     //   lazily moved reference maximum, P^T into B operands, O^T += V^T . P^T.
     // High-part MFMAs of all tiles are issued before the low-part ones so no
     // MFMA waits on the one before it.
-    floatx4 st[4][NTW];
-    uint32_t pb_hi[NTW][2][4], pb_lo[NTW][2][4];
-    const bool need_mask = (tile + 1) * kTile > it.n_tok || tpos_lds[kTile - 1] > it.pos0;
-    auto load_k = [&](bf16x8_t (&kf)[KS][4]) {
+    floatx4 st[MT][NTW];
+    uint32_t pb_hi[NTW][KT][4], pb_lo[NTW][KT][4];
+    const bool need_mask = (tile + 1) * PT > it.n_tok || tpos_lds[PT - 1] > it.pos0;
+    // K operands of the 64 keys of half h
+    auto load_k = [&](bf16x8_t (&kf)[KS][4], int h) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           kf[ks][mt] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4*>(k_lds + (mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
+              bf16x8_t,
+              *reinterpret_cast<const u32x4*>(k_lds + (h * 64 + mt * 16 + n) * KPITCH + ks * 64 + j4 * 16));
     };
-    auto s_mfma = [&](int nt, const bf16x8_t (&kf)[KS][4]) {
+    auto s_mfma = [&](int nt, const bf16x8_t (&kf)[KS][4], int h) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) st[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt) st[4 * h + mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 qh = {qb_hi[nt][ks][0], qb_hi[nt][ks][1], qb_hi[nt][ks][2], qb_hi[nt][ks][3]};
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, qh),
-                                                               st[mt][nt], 0, 0, 0);
+          st[4 * h + mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[ks][mt], __builtin_bit_cast(bf16x8_t, qh), st[4 * h + mt][nt], 0, 0, 0);
         const u32x4 ql = {qb_lo[nt][ks][0], qb_lo[nt][ks][1], qb_lo[nt][ks][2], qb_lo[nt][ks][3]};
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], __builtin_bit_cast(bf16x8_t, ql),
-                                                               st[mt][nt], 0, 0, 0);
+          st[4 * h + mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[ks][mt], __builtin_bit_cast(bf16x8_t, ql), st[4 * h + mt][nt], 0, 0, 0);
       }
     };
     // causal mask and the reference-maximum update of column group nt
     auto mask_rescale = [&](int nt) {
       if (need_mask) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tp = tpos_lds[mt * 16 + j4 * 4 + i];
@@ -889,7 +896,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[mt][nt][i]);
       mx = wave_max_rows4(mx);  // over the four lane groups of column n
@@ -907,61 +914,69 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     // probabilities of column group nt, split into high/low bf16 B operands
     auto probs = [&](int nt) {
       const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-      float pv[4][4];
       float ps = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int kt = 0; kt < KT; ++kt) {
+        float pv[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[mt][i] = __builtin_amdgcn_exp2f(st[mt][nt][i] - m_use);  // -inf -> 0
-          ps += pv[mt][i];
-        }
-      l_run[nt] += ps;
+        for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        split_bf16(pv[2 * kt][0], pv[2 * kt][1], pb_hi[nt][kt][0], pb_lo[nt][kt][0]);
-        split_bf16(pv[2 * kt][2], pv[2 * kt][3], pb_hi[nt][kt][1], pb_lo[nt][kt][1]);
-        split_bf16(pv[2 * kt + 1][0], pv[2 * kt + 1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
-        split_bf16(pv[2 * kt + 1][2], pv[2 * kt + 1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
+          for (int i = 0; i < 4; ++i) {
+            pv[m2][i] = __builtin_amdgcn_exp2f(st[2 * kt + m2][nt][i] - m_use);  // -inf -> 0
+            ps += pv[m2][i];
+          }
+        split_bf16(pv[0][0], pv[0][1], pb_hi[nt][kt][0], pb_lo[nt][kt][0]);
+        split_bf16(pv[0][2], pv[0][3], pb_hi[nt][kt][1], pb_lo[nt][kt][1]);
+        split_bf16(pv[1][0], pv[1][1], pb_hi[nt][kt][2], pb_lo[nt][kt][2]);
+        split_bf16(pv[1][2], pv[1][3], pb_hi[nt][kt][3], pb_lo[nt][kt][3]);
       }
+      l_run[nt] += ps;
     };
-    // V^T operands of both 32-key k-steps
-    auto load_v = [&](bf16x8_t (&va)[2][DT]) {
+    // V^T operands of the two 32-key k-steps of half h
+    auto load_v = [&](bf16x8_t (&va)[2][DT], int h) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          va[kt][dt] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4*>(vt_lds + (dt * 16 + n) * VPB + (kt * 32 + j4 * 8) * 2));
+          va[k2][dt] = __builtin_bit_cast(
+              bf16x8_t,
+              *reinterpret_cast<const u32x4*>(vt_lds + (dt * 16 + n) * VPB + ((2 * h + k2) * 32 + j4 * 8) * 2));
         }
     };
-    auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT]) {
+    auto pv_mfma = [&](int nt, const bf16x8_t (&va)[2][DT], int h) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int kt = 2 * h + k2;
         const u32x4 ph = {pb_hi[nt][kt][0], pb_hi[nt][kt][1], pb_hi[nt][kt][2], pb_hi[nt][kt][3]};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, ph),
+          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[k2][dt], __builtin_bit_cast(bf16x8_t, ph),
                                                                ot[nt][dt], 0, 0, 0);
         const u32x4 pl = {pb_lo[nt][kt][0], pb_lo[nt][kt][1], pb_lo[nt][kt][2], pb_lo[nt][kt][3]};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kt][dt], __builtin_bit_cast(bf16x8_t, pl),
+          ot[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[k2][dt], __builtin_bit_cast(bf16x8_t, pl),
                                                                ot[nt][dt], 0, 0, 0);
       }
     };
-    bf16x8_t kf[KS][4];
-    load_k(kf);
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) s_mfma(nt, kf);
+    for (int h = 0; h < HT; ++h) {
+      bf16x8_t kf[KS][4];
+      load_k(kf, h);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) s_mfma(nt, kf, h);
+    }
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) mask_rescale(nt);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) probs(nt);
-    bf16x8_t va[2][DT];
-    load_v(va);
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) pv_mfma(nt, va);
+    for (int h = 0; h < HT; ++h) {
+      bf16x8_t va[2][DT];
+      load_v(va, h);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) pv_mfma(nt, va, h);
+    }
 
     if (tile + 1 == ntiles) end_unit();
   };
@@ -969,9 +984,13 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   // loop has one exit and both steps run on every pass, so on every path the
   // other set's loads were issued after this set's: the wait before staging
   // a set leaves the other set's loads in flight.
-  while (ra.u < nunits) {
-    step(ra);
-    step(rb);
+  if constexpr (NSET == 2) {
+    while (ra.u < nunits) {
+      step(ra);
+      step(rb);
+    }
+  } else {
+    while (ra.u < nunits) step(ra);
   }
 }
 

@@ -350,7 +350,7 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
   // ---- workgroup split (same rules as decode) and chunk sizes
   int32_t wh = 0, wd = 0;
   split_workgroups(in, host_reads, dev_reads, &wh, &wd);
-  const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
+  const int32_t align = (int32_t)std::max<int64_t>(kPfTile, P);  // whole prefill tiles per item
   const int32_t ch = choose_chunk(host_reads * in.hkv, wh, 4, 256, 16384, align, in.host_chunk);
   // A prefill token-head costs a full 128-row MFMA pass, so HBM units are
   // long: fewer partials to write and merge (none when every block fits one
