@@ -525,11 +525,12 @@ template <int NTW>
 constexpr int pf_threads() { return kPrefillRows / (16 * NTW) * 64; }
 
 // NTW: 16-column MFMA tiles (query-head rows / 16) per wave; the workgroup
-// holds kPrefillRows / (16 NTW) waves.  One tile per wave (8 waves, ~210
-// VGPRs, two waves per SIMD) measured faster than two per wave (4 waves, one
-// wave per SIMD) on the LLaMA-3-8B 2048-row prefill: 0.105 vs 0.131 ms, also
-// when the two-per-wave form interleaves one group's softmax with the other
-// group's MFMAs; 64-row workgroups (two per CU) gave 0.111 ms.
+// holds kPrefillRows / (16 NTW) waves.  With 64-key tiles, one column tile
+// per wave (8 waves, two per SIMD) measured faster than two per wave (4
+// waves, one per SIMD) on the LLaMA-3-8B 2048-row prefill: 0.105 vs 0.131 ms,
+// also when the two-per-wave form interleaves one group's softmax with the
+// other group's MFMAs; 64-row workgroups (two per CU) gave 0.111 ms.  With
+// 128-key tiles one column tile per wave takes 254 VGPRs.
 template <int D, int G, bool PAGED, int NTW>
 __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a,
                                                                           const float* __restrict__ q_rot) {
