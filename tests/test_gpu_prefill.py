@@ -158,3 +158,45 @@ def test_prefill_llama3_2k_full_size(dk, ratio):
                                     heads=heads)
         _check(o[r:r + 1, heads], lse[r:r + 1, heads], ro, rl, f"r={ratio} row {r}")
     cache.free()
+
+
+def test_prefill_many_small_items(dk):
+    # tuned 128-token chunks: every row block is cut into several items per
+    # tier (partials merged per row), and the ratio puts the tier boundary
+    # inside a tile
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, news, hq, hkv, d, r, th = [3000, 1500], [200, 130], 32, 8, 128, 0.37, 5e5
+    ks, vs = kv_raw(85, lens, hkv, d)
+    qs = [normal_bf16(85 + b, 1, (n, hq, d)) for b, n in enumerate(news)]
+    cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    try:
+        dk.set_tuning(host_chunk=128, dev_chunk=128, stage_max_mib=-1)
+        o, lse, bufs = _prefill(dk, cache, qs, q_start, q_pos0, lens, r, th, d)
+        print("plan", bufs.info, flush=True)
+        assert bufs.info["num_splits"] > 4 * sum(news)
+    finally:
+        dk.reset_tuning()
+    for b in range(2):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], q_pos0[b], th, 1 / math.sqrt(d))
+        _check(o[q_start[b]:q_start[b + 1]], lse[q_start[b]:q_start[b + 1]], ro, rl, f"small items seq {b}")
+    cache.free()
+
+
+@pytest.mark.parametrize("page", [32, 128, 256])
+def test_prefill_paged_page_sizes(dk, page):
+    # pages smaller than, equal to and larger than a 128-key tile
+    from decode_attention_host_amd.cache_build import paged_cache
+    lens, news, hq, hkv, d, th = [700, 300], [90, 300], 16, 4, 128, 1e4
+    ks, vs = kv_raw(86, lens, hkv, d)
+    qs = [normal_bf16(86 + b, 1, (n, hq, d)) for b, n in enumerate(news)]
+    pt, nh, nd = paged_table(86, lens, page, 0.6)
+    cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, th, page=page)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q_pos0 = [L - n for L, n in zip(lens, news)]
+    o, lse, _ = _prefill(dk, cache, qs, q_start, q_pos0, lens, 0.0, th, d)
+    for b in range(2):
+        ro, rl = O.prefill_sequence(qs[b], ks[b], vs[b], q_pos0[b], th, 1 / math.sqrt(d))
+        _check(o[q_start[b]:q_start[b + 1]], lse[q_start[b]:q_start[b + 1]], ro, rl, f"page {page} seq {b}")
+    cache.free()
