@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     linear_plan,
     linear_plan_inspect,
     OffloadedLinear,
+    PagedKVAllocator,
     merge_lse,
     plan_inspect,
     prefill,

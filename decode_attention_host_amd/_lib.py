@@ -85,6 +85,20 @@ class BwResult(C.Structure):
     _fields_ = [("read_gbs", C.c_double), ("read_ms", C.c_double), ("dma_gbs", C.c_double)]
 
 
+class PagerStats(C.Structure):
+    _fields_ = [
+        ("free_host_pages", C.c_int32),
+        ("free_dev_pages", C.c_int32),
+        ("used_host_pages", C.c_int32),
+        ("used_dev_pages", C.c_int32),
+        ("spilled_pages", C.c_int32),
+        ("reserved", C.c_int32),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
 P = C.c_void_p
 I32 = C.c_int32
 I64 = C.c_int64
@@ -116,6 +130,12 @@ SIGNATURES = {
     "dkv_linear_split": (I32, [P, P, I32, I32, F64, P, I32, P, P, SZ, P]),
     "dkv_linear_plan_inspect": (I32, [I32, I32, F64, I32, P, I32, C.POINTER(PlanInfo)]),
     "dkv_merge_lse": (I32, [P, P, P, I32, I32, I32, P, P, P]),
+    "dkv_pager_create": (I32, [I32, I32, I32, I32, I32, F64, C.POINTER(P)]),
+    "dkv_pager_destroy": (I32, [P]),
+    "dkv_pager_reserve": (I32, [P, I32, I64]),
+    "dkv_pager_release": (I32, [P, I32]),
+    "dkv_pager_table": (I32, [P, C.POINTER(PI32), C.POINTER(PI32)]),
+    "dkv_pager_stats_get": (I32, [P, C.POINTER(PagerStats)]),
     "dkv_host_alloc": (I32, [SZ, C.c_uint32, C.POINTER(P), C.POINTER(P)]),
     "dkv_host_free": (I32, [P]),
     "dkv_set_tuning": (I32, [C.POINTER(Tuning)]),

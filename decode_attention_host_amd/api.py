@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import KvDesc, PlanInfo, Tuning, BwResult, check, lib
+from ._lib import KvDesc, PagerStats, PlanInfo, Tuning, BwResult, check, lib
 
 DKV_HOST_COHERENT = _lib.DKV_HOST_COHERENT
 DKV_HOST_NONCOHERENT = _lib.DKV_HOST_NONCOHERENT
@@ -132,6 +132,27 @@ class KVCache:
         self.max_pages = int(pt.shape[1])
         self.page_table = torch.from_numpy(pt).to("cuda")
 
+    def update_page_table(self, page_table):
+        """Overwrite the page table in place (same shape): host copy now, device
+        copy by a copy queued on the current stream after earlier work."""
+        pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+        if self.page_table is None or pt.shape != self.page_table_host.shape:
+            raise ValueError("update_page_table needs a table of the current shape")
+        np.copyto(self.page_table_host, pt)
+        self.page_table.copy_(torch.from_numpy(pt))
+
+    def with_page_table(self, page_table) -> "KVCache":
+        """A view that shares this cache's pools and has its own page table
+        (for a batch made of some of the sequences).  Freeing a view does not
+        free the pools."""
+        import copy
+        v = copy.copy(self)
+        v.page_table = None
+        v.page_table_host = None
+        v.set_page_table(page_table)
+        v._is_view = True
+        return v
+
     def host_view(self, which: str) -> np.ndarray:
         """uint16 numpy view [host_rows][Hkv][D] of a host pool ('k' or 'v')."""
         buf = self.host_k if which == "k" else self.host_v
@@ -156,9 +177,75 @@ class KVCache:
         return d
 
     def free(self):
+        if getattr(self, "_is_view", False):
+            return
         for b in (self.host_k, self.host_v):
             if b is not None:
                 b.free()
+
+
+class PagedKVAllocator:
+    """Paged KV pools managed by the native allocator (dkv_pager_*).
+
+    ``pools`` is a paged KVCache over all ``max_seqs`` sequence slots: append
+    through it with seq_idx = slot.  ``reserve`` / ``release`` change the
+    allocator's table and copy it to ``pools``; ``batch(slots)`` is a view
+    over the same pools whose page table rows are the given slots, for an
+    attention call over those sequences.
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, *, n_host_pages: int, n_dev_pages: int,
+                 max_seqs: int, max_pages: int, host_fraction: float, page_size: int = 16,
+                 host_flags: int = DKV_HOST_COHERENT):
+        h = C.c_void_p()
+        check(lib().dkv_pager_create(int(n_host_pages), int(n_dev_pages), int(page_size), int(max_seqs),
+                                     int(max_pages), float(host_fraction), C.byref(h)))
+        self._h = h
+        tbl, npg = _lib.PI32(), _lib.PI32()
+        check(lib().dkv_pager_table(h, C.byref(tbl), C.byref(npg)))
+        self._table = np.ctypeslib.as_array(tbl, shape=(int(max_seqs), int(max_pages)))
+        self._npages = np.ctypeslib.as_array(npg, shape=(int(max_seqs),))
+        self.page_size = int(page_size)
+        self.host_fraction = float(host_fraction)
+        self.pools = KVCache(num_kv_heads, head_dim, host_rows=int(n_host_pages) * self.page_size,
+                             dev_rows=int(n_dev_pages) * self.page_size, page_size=self.page_size,
+                             page_table=self._table.copy(), host_flags=host_flags)
+
+    def reserve(self, seq: int, n_tokens: int, sync: bool = True):
+        """Pages for tokens [0, n_tokens) of slot ``seq`` (all or nothing)."""
+        check(lib().dkv_pager_reserve(self._h, int(seq), int(n_tokens)))
+        if sync:
+            self.sync()
+
+    def release(self, seq: int, sync: bool = True):
+        check(lib().dkv_pager_release(self._h, int(seq)))
+        if sync:
+            self.sync()
+
+    def sync(self):
+        """Copy the allocator's table into ``pools`` (host and device copies)."""
+        self.pools.update_page_table(self._table)
+
+    def table(self) -> np.ndarray:
+        return self._table.copy()
+
+    def pages_of(self, seq: int) -> int:
+        return int(self._npages[int(seq)])
+
+    def stats(self) -> dict:
+        st = PagerStats()
+        check(lib().dkv_pager_stats_get(self._h, C.byref(st)))
+        return st.as_dict()
+
+    def batch(self, slots) -> KVCache:
+        return self.pools.with_page_table(self._table[np.asarray(list(slots), dtype=np.int64)])
+
+    def close(self):
+        if self._h is not None:
+            check(lib().dkv_pager_destroy(self._h))
+            self._h = None
+            self._table = self._npages = None
+            self.pools.free()
 
 
 def append_workspace_bytes(n_new: int, hidden: int, kv_dim: int) -> int:

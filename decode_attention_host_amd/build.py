@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdkv.so")
 
-SOURCES = ["dkv_api.cpp", "dkv_plan.cpp", "dkv_kernels.hip"]
+SOURCES = ["dkv_api.cpp", "dkv_plan.cpp", "dkv_pager.cpp", "dkv_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

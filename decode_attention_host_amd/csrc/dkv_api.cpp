@@ -44,6 +44,14 @@ dkv_status hip_err(hipError_t e, const char* what) {
   return set_err(DKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+// The thread's last-error message, shared with the other translation units.
+dkv_status dkv::error(dkv_status st, const char* msg) { return set_err(st, "%s", msg); }
+dkv_status dkv::success() { return ok(); }
+
+namespace {
+
 bool debug_validate() {
   static const bool on = [] {
     const char* v = getenv("DKV_DEBUG_VALIDATE");

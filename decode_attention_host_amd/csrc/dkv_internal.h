@@ -8,6 +8,8 @@
 #include <string>
 #include <vector>
 
+#include "dkv.h"
+
 namespace dkv {
 
 // Rotary frequencies f_i = theta^(-2i/D), i < D/2, computed once on the host
@@ -347,5 +349,10 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
 // counters.
 bool build_linear_plan(const PlanInput& in, int32_t M, int32_t N, int32_t K, PlanLayout* out,
                        std::vector<uint8_t>* blob, std::string* err);
+
+// Sets the calling thread's last-error message (dkv_last_error) and returns
+// st; success() clears it and returns DKV_OK.
+dkv_status error(dkv_status st, const char* msg);
+dkv_status success();
 
 }  // namespace dkv

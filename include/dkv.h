@@ -330,6 +330,53 @@ dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32
                          float* out_o, float* out_lse, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Paged KV allocator (DirectKV README, introduction: the KV pool kept in
+ * CPU-pinned memory; SplitKernel README, Overview: a cache split between
+ * host and device memory by an offload ratio).
+ *
+ * Host-side bookkeeping for the paged layout of dkv_kv_desc: a host pool of
+ * n_host_pages pages and an HBM pool of n_dev_pages pages (page_size rows
+ * each, the caller allocates the pools), one LIFO free list per pool, and the
+ * page table [max_seqs][max_pages] (entry phys << 1 | tier, tier 1 = host;
+ * -1 = unused) that dkv_kv_desc.page_table(_host) describe.  No GPU calls:
+ * the caller copies the table (dkv_pager_table) to its device copy after a
+ * change and before kernels read it.
+ *
+ * Placement: logical page j of a sequence goes to the host pool iff
+ * floor(f*(j+1)) > floor(f*j), f = host_fraction in [0, 1], so that exactly
+ * floor(f*n) of its first n pages are host-resident at every length n.  If
+ * the chosen pool is empty the page goes to the other pool (counted in
+ * spilled_pages).
+ *
+ * dkv_pager_reserve(seq, n_tokens) gives sequence seq pages for tokens
+ * [0, n_tokens) (never shrinks); it is all-or-nothing: with too few free
+ * pages in both pools it changes nothing and returns DKV_ERR_NOMEM, and
+ * n_tokens beyond max_pages*page_size returns DKV_ERR_INVALID.
+ * dkv_pager_release(seq) returns all of seq's pages to their pools.  The
+ * pointer from dkv_pager_table stays valid until dkv_pager_destroy.  Calls on
+ * one pager must not overlap; distinct pagers are independent.
+ * ---------------------------------------------------------------------- */
+typedef struct dkv_pager dkv_pager;
+
+typedef struct dkv_pager_stats {
+  int32_t free_host_pages;
+  int32_t free_dev_pages;
+  int32_t used_host_pages;
+  int32_t used_dev_pages;
+  int32_t spilled_pages;  /* pages placed in the other pool since creation */
+  int32_t reserved;
+} dkv_pager_stats;
+
+dkv_status dkv_pager_create(int32_t n_host_pages, int32_t n_dev_pages, int32_t page_size,
+                            int32_t max_seqs, int32_t max_pages, double host_fraction, dkv_pager** out);
+dkv_status dkv_pager_destroy(dkv_pager* pager);
+dkv_status dkv_pager_reserve(dkv_pager* pager, int32_t seq, int64_t n_tokens);
+dkv_status dkv_pager_release(dkv_pager* pager, int32_t seq);
+/* *table: [max_seqs][max_pages] int32; *pages_of_seq (may be NULL): [max_seqs] */
+dkv_status dkv_pager_table(const dkv_pager* pager, const int32_t** table, const int32_t** pages_of_seq);
+dkv_status dkv_pager_stats_get(const dkv_pager* pager, dkv_pager_stats* stats);
+
+/* ------------------------------------------------------------------------
  * Host-pinned memory for the host tier (DirectKV README, introduction:
  * CPU-pinned KV pool).  Allocates `bytes` of page-locked host memory mapped
  * into the GPU's address space; *host_ptr is the CPU address, *dev_ptr the

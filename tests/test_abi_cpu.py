@@ -66,7 +66,8 @@ def _c_layout(struct, fields):
 
 
 @pytest.mark.parametrize("struct,cls", [("dkv_kv_desc", "KvDesc"), ("dkv_plan_info", "PlanInfo"),
-                                        ("dkv_tuning", "Tuning"), ("dkv_bw_result", "BwResult")])
+                                        ("dkv_tuning", "Tuning"), ("dkv_bw_result", "BwResult"),
+                                        ("dkv_pager_stats", "PagerStats")])
 def test_struct_layouts_match_header(struct, cls):
     t = getattr(dkv_lib, cls)
     names = [n for n, _ in t._fields_]
