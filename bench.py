@@ -576,6 +576,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--ratio", type=float, default=None,
+                    help="offload ratio for the main workload instead of its own (profiling runs)")
     ap.add_argument("--host-flags", choices=["coherent", "noncoherent"], default="coherent")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -603,6 +605,8 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = workload(args.workload, seed=args.seed)
+    if args.ratio is not None:
+        cfg["ratio"] = float(args.ratio)
     if args.tune:
         kw = {}
         for item in args.tune.split(","):
@@ -625,8 +629,10 @@ def main():
         dst = torch.empty_like(src)
         src.fill_(3)
         dst.copy_(src)
-        dk.probe_read(cache.host_k.dev_ptr, 64 << 20, 64, nontemporal=True, iters=1)
+        if cache.host_k is not None and cache.host_rows * cfg["hkv"] * cfg["d"] * 2 >= (64 << 20):
+            dk.probe_read(cache.host_k.dev_ptr, 64 << 20, 64, nontemporal=True, iters=1)
         torch.cuda.synchronize()
+        gpu_warm(step, 0.5)
         ms, _ = timed_loop(step, args.steps, args.warmup)
         log(f"[bench] profile run: {args.steps} steps, {ms:.4f} ms/step")
         cache.free()
