@@ -537,7 +537,6 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   constexpr int NT = pf_threads<NTW>();
   constexpr int PT = kPfTile;                  // keys per tile
   constexpr int HT = PT / 64;                  // 64-key halves per tile
-  constexpr int NSET = PT == 64 ? 2 : 1;       // register sets in flight
   constexpr int MT = PT / 16;                  // 16-key blocks per tile
   constexpr int KT = PT / 32;                  // 32-key k-steps of P.V per tile
   constexpr int QB = kPrefillRows / G;
@@ -649,9 +648,9 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     return it.tok0 + tok;
   };
 
-  // Tiles stream through two register sets: while a tile is computed out of
-  // LDS, the loads of the next two tiles are in flight (prefetch distance
-  // two).  Each set carries the unit and tile index its data belongs to.
+  // A thread's share of the next tile is loaded into registers while the
+  // current tile is reduced out of LDS; the registers carry the unit and tile
+  // index their data belongs to.
   struct TileRegs {
     u32x4 k[NCK];
     u32x4 v[TPT];
@@ -674,10 +673,9 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     for (int e = 0; e < TPT; ++e) voff[e] = (row_of(it, t0 + vq * TPT + e) * a.hkv + kvh) * D + vc * 8;
   };
   // Loads of the prefetch cursor's next tile into r.  Every call issues the
-  // same loads, so the count of loads in flight per step is fixed and the
-  // wait before a set is staged covers that set alone: once the stream has
+  // same loads, so no path through a step lacks them: once the stream has
   // ended the addresses fall back to the first bytes of q_rot (the tags mark
-  // such a set as empty).
+  // such a tile as empty).
   auto load_tile = [&](TileRegs& r, bool live, const PrefillItem& it, const Src& sp, int kvh, int tile) {
     const int t0 = tile * PT;
     if (live) {
@@ -736,16 +734,9 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     r.tile = live ? ptile++ : 0;
   };
 
-  TileRegs ra, rb;
+  TileRegs ra;
   open_unit();
   issue(ra);
-  if constexpr (NSET == 2) {
-    const bool c = needs_claim();
-    claim(c);
-    __syncthreads();
-    after_claim(c);
-    issue(rb);
-  }
 
   // ---- compute cursor: the unit whose tiles are being reduced
   PrefillItem it{};
@@ -810,9 +801,9 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
     }
   };
 
-  // One tile: stage set r in LDS, refill r with the tile two ahead, reduce.
-  // A set past the end of the stream is staged and refilled (with the same
-  // loads as any other) but not reduced.
+  // One tile: stage r in LDS, refill r with the next tile, reduce.  A tile
+  // past the end of the stream is staged and refilled (with the same loads as
+  // any other) but not reduced.
   auto step = [&](TileRegs& r) {
     const int tile = r.tile;
     const bool work = r.u < nunits;
@@ -981,18 +972,8 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 
     if (tile + 1 == ntiles) end_unit();
   };
-  // The two sets alternate; the stream ends when a set carries no unit.  The
-  // loop has one exit and both steps run on every pass, so on every path the
-  // other set's loads were issued after this set's: the wait before staging
-  // a set leaves the other set's loads in flight.
-  if constexpr (NSET == 2) {
-    while (ra.u < nunits) {
-      step(ra);
-      step(rb);
-    }
-  } else {
-    while (ra.u < nunits) step(ra);
-  }
+  // the stream ends when the registers carry no unit
+  while (ra.u < nunits) step(ra);
 }
 
 // ---------------------------------------------------------------------------
