@@ -79,6 +79,9 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
 // hpt grows with the number of rows so that about 2^19 threads run.  Block 0 also copies the split offsets of the plan to the
 // caller's array.
 // ---------------------------------------------------------------------------
+// VP consecutive rotation pairs per thread: the loads are VP bf16 wide and
+// the stores VP floats wide (VP = 4 when the pointers allow it).
+template <int VP>
 __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ q_pos,
                                                           float* __restrict__ q_rot, int hq, int d,
@@ -87,27 +90,56 @@ __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __rest
                                                           int32_t* __restrict__ split_offsets,
                                                           int batch, int hpt) {
   const int half = d >> 1;
+  const int hv = half / VP;  // pair groups per head
   if (blockIdx.x == 0 && split_offsets)
     for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
   const int groups = (hq + hpt - 1) / hpt;
-  const int64_t total = (int64_t)batch * groups * half;
+  const int64_t total = (int64_t)batch * groups * hv;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(idx % half);
-    const int64_t bg = idx / half;
+    const int i0 = (int)(idx % hv) * VP;
+    const int64_t bg = idx / hv;
     const int g = (int)(bg % groups);
     const int b = (int)(bg / groups);
-    double s, c;
-    sincos((double)q_pos[b] * freq.f[i], &s, &c);
+    double s[VP], c[VP];
+#pragma unroll
+    for (int v = 0; v < VP; ++v) sincos((double)q_pos[b] * freq.f[i0 + v], &s[v], &c[v]);
     const int h1 = min(hq, (g + 1) * hpt);
-#pragma unroll 4
+#pragma unroll 2
     for (int h = g * hpt; h < h1; ++h) {
       const uint16_t* qh = q + ((size_t)b * hq + h) * d;
-      const double xl = (double)bf16_to_f32(qh[i]);
-      const double xh = (double)bf16_to_f32(qh[i + half]);
       float* o = q_rot + ((size_t)b * hq + h) * d;
-      o[i] = (float)(xl * c - xh * s) * scale_log2;
-      o[i + half] = (float)(xh * c + xl * s) * scale_log2;
+      uint16_t xl16[VP], xh16[VP];
+      if constexpr (VP == 4) {
+        const uint2 l = *reinterpret_cast<const uint2*>(qh + i0);
+        const uint2 u = *reinterpret_cast<const uint2*>(qh + i0 + half);
+        xl16[0] = l.x & 0xffffu; xl16[1] = l.x >> 16; xl16[2] = l.y & 0xffffu; xl16[3] = l.y >> 16;
+        xh16[0] = u.x & 0xffffu; xh16[1] = u.x >> 16; xh16[2] = u.y & 0xffffu; xh16[3] = u.y >> 16;
+      } else {
+#pragma unroll
+        for (int v = 0; v < VP; ++v) {
+          xl16[v] = qh[i0 + v];
+          xh16[v] = qh[i0 + v + half];
+        }
+      }
+      float lo[VP], hi[VP];
+#pragma unroll
+      for (int v = 0; v < VP; ++v) {
+        const double xl = (double)bf16_to_f32(xl16[v]);
+        const double xh = (double)bf16_to_f32(xh16[v]);
+        lo[v] = (float)(xl * c[v] - xh * s[v]) * scale_log2;
+        hi[v] = (float)(xh * c[v] + xl * s[v]) * scale_log2;
+      }
+      if constexpr (VP == 4) {
+        *reinterpret_cast<floatx4*>(o + i0) = floatx4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<floatx4*>(o + i0 + half) = floatx4{hi[0], hi[1], hi[2], hi[3]};
+      } else {
+#pragma unroll
+        for (int v = 0; v < VP; ++v) {
+          o[i0 + v] = lo[v];
+          o[i0 + v + half] = hi[v];
+        }
+      }
     }
   }
 }
@@ -1508,14 +1540,22 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
                   const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
                   int32_t* split_offsets, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // heads per thread: enough threads (~2^19) to hide load latency, sin/cos
-  // shared by the heads a thread covers
+  // four pairs per thread when q (8 B) and q_rot (16 B) are aligned for the
+  // wide accesses
+  const bool wide = (d / 2) % 4 == 0 && ((uintptr_t)q & 7) == 0 && ((uintptr_t)q_rot & 15) == 0;
+  const int vp = wide ? 4 : 1;
+  // heads per thread: enough threads (~2^19 pairs' worth) to hide load
+  // latency, sin/cos shared by the heads a thread covers
   const int64_t pairs = (int64_t)batch * (d / 2);
   const int hpt = (int)std::max<int64_t>(1, std::min<int64_t>(hq, pairs * hq >> 19));
-  const int64_t total = pairs * ((hq + hpt - 1) / hpt);
+  const int64_t total = pairs / vp * ((hq + hpt - 1) / hpt);
   const int bx = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
-  hipLaunchKernelGGL(rope_q_kernel, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
-                     scale_log2, plan_offsets, split_offsets, batch, hpt);
+  if (wide)
+    hipLaunchKernelGGL(rope_q_kernel<4>, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
+                       scale_log2, plan_offsets, split_offsets, batch, hpt);
+  else
+    hipLaunchKernelGGL(rope_q_kernel<1>, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
+                       scale_log2, plan_offsets, split_offsets, batch, hpt);
   return (int)hipGetLastError();
 }
 
