@@ -296,7 +296,7 @@ def cpu_baseline(cfg, w, budget_s):
         O.decode_sequence(w["qb"][b], w["ks"][b], w["vs"][b], lens[b] - 1, cfg["theta"], scale)
         done_bytes += lens[b] * cfg["hkv"] * d * 4
         seqs += 1
-        if time.perf_counter() - t0 >= budget_s or seqs >= 4 * B:
+        if time.perf_counter() - t0 >= budget_s:  # whole calls until the budget is spent
             break
     dt = time.perf_counter() - t0
     if limiter is not None:
