@@ -343,10 +343,11 @@ dkv_status get_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, co
   return DKV_OK;
 }
 
-// Prefill workspace: plan image, rotated queries, then the HBM staging pool
-// (K rows, then V rows).
+// Prefill workspace: plan image, the rows' rotation table ((cos, sin) fp64
+// per row and pair), then the HBM staging pool (K rows, then V rows).
+size_t rope_table_bytes(int32_t n_rows, int d) { return (size_t)n_rows * (d / 2) * 16; }
 size_t prefill_stage_off(const dkv::PlanLayout& L, int hq, int d) {
-  return (L.blob_bytes + qrot_bytes(L.n_rows, hq, d) + 255) / 256 * 256;
+  return (L.blob_bytes + rope_table_bytes(L.n_rows, d) + 255) / 256 * 256;
 }
 size_t prefill_ws_bytes(const dkv::PlanLayout& L, int hq, int hkv, int d) {
   return prefill_stage_off(L, hq, d) + (size_t)L.stage_rows * hkv * d * 2 * 2;
@@ -1152,13 +1153,15 @@ dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
 
 // Staging copy, query rotation and the prefill kernel, after the plan image is
 // in the workspace.  fresh_k/fresh_v: the new rows (fused step) or NULL.
+// rope_table_ready: the rotation table (and the split offsets) were written
+// earlier in the call.
 static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, const void* q,
                                  const dkv::PlanLayout& L, uint8_t* ws, float scale, double rope_theta,
                                  const uint16_t* fresh_k, const uint16_t* fresh_v, float* part_o,
                                  float* part_lse, int32_t* split_offsets, void* stream,
-                                 const dkv::AppendArgs* writers = nullptr) {
+                                 const dkv::AppendArgs* writers = nullptr, bool rope_table_ready = false) {
   hipStream_t s = (hipStream_t)stream;
-  float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
+  double* rope_cs = reinterpret_cast<double*>(ws + L.blob_bytes);
   const size_t pool_elems = (size_t)L.stage_rows * kv->num_kv_heads * kv->head_dim;
   uint16_t* stage_k = reinterpret_cast<uint16_t*>(ws + prefill_stage_off(L, num_q_heads, kv->head_dim));
   uint16_t* stage_v = stage_k + pool_elems;
@@ -1180,15 +1183,15 @@ static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, con
     if (he != hipSuccess) return hip_err(he, "stage launch");
   }
   const float scale_log2 = scale * 1.44269504088896340736f;
-  TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
-  he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q),
-                                      reinterpret_cast<const int32_t*>(ws + L.rowpos_off), q_rot,
-                                      L.n_rows, num_q_heads, kv->head_dim,
-                                      rope_freq(rope_theta, kv->head_dim), scale_log2,
-                                      reinterpret_cast<const int32_t*>(ws + L.offsets_off),
-                                      split_offsets, stream);
-  t_rope.done();
-  if (he != hipSuccess) return hip_err(he, "rope_q launch");
+  if (!rope_table_ready) {
+    TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
+    he = (hipError_t)dkv::launch_rope_table(reinterpret_cast<const int32_t*>(ws + L.rowpos_off), L.n_rows,
+                                            kv->head_dim, rope_freq(rope_theta, kv->head_dim), rope_cs,
+                                            reinterpret_cast<const int32_t*>(ws + L.offsets_off),
+                                            split_offsets, stream);
+    t_rope.done();
+    if (he != hipSuccess) return hip_err(he, "rope table launch");
+  }
   dkv::PrefillArgs a{};
   a.host_items = reinterpret_cast<const dkv::PrefillItem*>(ws + L.items_off);
   a.dev_items = a.host_items + L.n_host_items;
@@ -1220,8 +1223,11 @@ static dkv_status prefill_stages(const dkv_kv_desc* kv, int32_t num_q_heads, con
     a.writer_wgs = tuned > 0 ? std::min<int32_t>(tuned, std::max<int32_t>(1, writers->n_new))
                              : (int32_t)std::min<int64_t>(64, std::max<int64_t>(1, writers->n_new / 8));
   }
+  a.q = static_cast<const uint16_t*>(q);
+  a.rope_cs = rope_cs;
+  a.scale_log2 = scale_log2;
   TimedLaunch t_attn(DKV_KERNEL_PREFILL, s);
-  he = (hipError_t)dkv::launch_prefill(a, q_rot, stream);
+  he = (hipError_t)dkv::launch_prefill(a, stream);
   t_attn.done();
   if (he != hipSuccess) return hip_err(he, "prefill launch");
   return DKV_OK;
@@ -1240,6 +1246,7 @@ dkv_status dkv_prefill_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t 
   if (q_start[batch] == 0) return ok();  // no query rows: nothing is read or written
   if (!q || !part_o || !part_lse || !split_offsets || !workspace)
     return set_err(DKV_ERR_INVALID, "q, part_o, part_lse, split_offsets and workspace are required");
+  if ((uintptr_t)q % 16) return set_err(DKV_ERR_INVALID, "q must be 16-byte aligned");
   if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
     return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
   if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -1294,6 +1301,7 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   if (batch < 1 || !q_start) return set_err(DKV_ERR_INVALID, "batch >= 1 and q_start are required");
   if (q_start[batch] == 0) return ok();  // no new rows: nothing is read or written
   if (!q || !out_o || !workspace) return set_err(DKV_ERR_INVALID, "q, out_o and workspace are required");
+  if ((uintptr_t)q % 16) return set_err(DKV_ERR_INVALID, "q must be 16-byte aligned");
   if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
     return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
   if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -1330,6 +1338,18 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   if (he != hipSuccess) return hip_err(he, "plan upload");
   uint16_t* fresh_k = reinterpret_cast<uint16_t*>(ws + F.fresh_off);
   uint16_t* fresh_v = fresh_k + (size_t)L.n_rows * kvd;
+  // 0. the rows' rotation angles, shared by the key append and the queries
+  const bool direct = L.num_splits == L.n_rows && out_lse != nullptr;
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + F.offsets_off);
+  double* rope_cs = reinterpret_cast<double*>(ws + L.blob_bytes);
+  {
+    TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
+    he = (hipError_t)dkv::launch_rope_table(reinterpret_cast<const int32_t*>(ws + L.rowpos_off), L.n_rows,
+                                            kv->head_dim, rope_freq(rope_theta, kv->head_dim), rope_cs,
+                                            reinterpret_cast<const int32_t*>(ws + L.offsets_off), offs, stream);
+    t_rope.done();
+    if (he != hipSuccess) return hip_err(he, "rope table launch");
+  }
   // 1. new K/V (projection) -> cache slots and the fresh rows
   dkv::AppendArgs a{};
   a.batch = batch;
@@ -1352,6 +1372,7 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   a.hkv = kv->num_kv_heads;
   a.head_dim = kv->head_dim;
   a.freq = rope_freq(rope_theta, kv->head_dim);
+  a.rope_cs = rope_cs;
   a.fresh_k = fresh_k;
   a.fresh_v = fresh_v;
   if (proj) {
@@ -1389,12 +1410,10 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   // 2. staging of re-read prefix rows, query rotation, prefill attention.
   // With one split per row the split slot of row r is r and its normalised
   // partial is the result: it is written to the output and no merge runs.
-  const bool direct = L.num_splits == L.n_rows && out_lse != nullptr;
   float* part_o = direct ? out_o : reinterpret_cast<float*>(ws + F.part_o_off);
   float* part_lse = direct ? out_lse : reinterpret_cast<float*>(ws + F.part_lse_off);
-  int32_t* offs = reinterpret_cast<int32_t*>(ws + F.offsets_off);
   st = prefill_stages(kv, num_q_heads, q, L, ws, scale, rope_theta, fresh_k, fresh_v, part_o, part_lse, offs,
-                      stream, &a);
+                      stream, &a, true);
   if (st != DKV_OK) return st;
   if (direct) return ok();
   // 3. merge of each row's splits

@@ -208,6 +208,7 @@ struct AppendArgs {
   int32_t hkv;
   int32_t head_dim;
   RopeFreq freq;
+  const double* rope_cs;         // optional [n_new][D/2] (cos, sin) of token i's angles
 };
 
 struct ProjArgs {
@@ -257,6 +258,10 @@ struct PrefillArgs {
   int32_t writer_wgs;            // fused step: workgroups copying the new rows
   int32_t pad2;                  //   from fresh_k/v into their cache slots
   AppendArgs app;                //   (placement of new row i, as for append)
+  const uint16_t* q;             // query rows [T][Hq][D] bf16 (unrotated)
+  const double* rope_cs;         // [T][D/2] (cos, sin) of each row's angles
+  float scale_log2;              // scale * log2(e), folded into the rotated q
+  int32_t pad3;
 };
 
 struct LinearArgs {
@@ -298,7 +303,12 @@ int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int bat
                   int32_t* split_offsets, void* stream);
 int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
-int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream);
+int launch_prefill(const PrefillArgs& a, void* stream);
+// (cos, sin) in fp64 of the rotation angles of every prefill row:
+// cs[row][i] for angle rowpos[row] * freq.f[i], i < d / 2; block 0 also copies
+// plan_offsets[0 .. n_rows] to split_offsets (if not NULL).
+int launch_rope_table(const int32_t* rowpos, int n_rows, int d, const RopeFreq& freq, double* cs,
+                      const int32_t* plan_offsets, int32_t* split_offsets, void* stream);
 int launch_stage(const StageArgs& a, int nwg, void* stream);
 int launch_linear(const LinearArgs& a, void* stream);
 // max_wgs > 0 caps the grid (the kernel loops over the tokens).

@@ -144,6 +144,25 @@ __global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __rest
   }
 }
 
+// (cos, sin) of every prefill row's rotation angles, fp64, computed once per
+// call; the prefill kernel rotates its query columns with them.
+__global__ __launch_bounds__(kThreads) void rope_table_kernel(const int32_t* __restrict__ rowpos, int n_rows,
+                                                              int half, RopeFreq freq, double2* __restrict__ cs,
+                                                              const int32_t* __restrict__ plan_offsets,
+                                                              int32_t* __restrict__ split_offsets) {
+  if (blockIdx.x == 0 && split_offsets)
+    for (int i = threadIdx.x; i <= n_rows; i += blockDim.x) split_offsets[i] = plan_offsets[i];
+  const int64_t total = (int64_t)n_rows * half;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / half;
+    const int i = (int)(idx - row * half);
+    double sn, c;
+    sincos((double)rowpos[row] * freq.f[i], &sn, &c);
+    cs[idx] = make_double2(c, sn);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split decode attention.
 // ---------------------------------------------------------------------------
@@ -564,8 +583,7 @@ constexpr int pf_threads() { return kPrefillRows / (16 * NTW) * 64; }
 // other group's MFMAs; 64-row workgroups (two per CU) gave 0.111 ms.  With
 // 128-key tiles one column tile per wave takes 254 VGPRs.
 template <int D, int G, bool PAGED, int NTW>
-__global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a,
-                                                                          const float* __restrict__ q_rot) {
+__global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(PrefillArgs a) {
   constexpr int NT = pf_threads<NTW>();
   constexpr int PT = kPfTile;                  // keys per tile
   constexpr int HT = PT / 64;                  // 64-key halves per tile
@@ -706,8 +724,8 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   };
   // Loads of the prefetch cursor's next tile into r.  Every call issues the
   // same loads, so no path through a step lacks them: once the stream has
-  // ended the addresses fall back to the first bytes of q_rot (the tags mark
-  // such a tile as empty).
+  // ended the addresses fall back to the first bytes of the query rows (the
+  // tags mark such a tile as empty).
   auto load_tile = [&](TileRegs& r, bool live, const PrefillItem& it, const Src& sp, int kvh, int tile) {
     const int t0 = tile * PT;
     if (live) {
@@ -723,7 +741,7 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
         for (int e = 0; e < TPT; ++e) voff[e] += step;
       }
     }
-    const uint16_t* dummy = reinterpret_cast<const uint16_t*>(q_rot);
+    const uint16_t* dummy = a.q;
 #pragma unroll
     for (int c = 0; c < NCK; ++c)
       r.k[c] = *reinterpret_cast<const u32x4*>(live ? sp.k + koff[c] : dummy + c * 8);
@@ -794,17 +812,30 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
       const int r = rho / G, h = rho % G;
       rvalid[nt] = r < it.n_rows;
       rpos[nt] = it.pos0 + r;
-      const float* qr = q_rot + ((size_t)(it.row0 + (rvalid[nt] ? r : 0)) * a.hq + kvh * G + h) * D;
+      // rotate the column's query (Neox pairs d, d + D/2) with the row's fp64
+      // (cos, sin), round once to fp32, fold in scale * log2(e)
+      const size_t row = (size_t)it.row0 + (rvalid[nt] ? r : 0);
+      const uint16_t* qr = a.q + (row * a.hq + kvh * G + h) * D;
+      const double2* cs = reinterpret_cast<const double2*>(a.rope_cs) + row * (D / 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = ks * 32 + j4 * 8;
-        floatx4 x0 = *reinterpret_cast<const floatx4*>(qr + d0);
-        floatx4 x1 = *reinterpret_cast<const floatx4*>(qr + d0 + 4);
-        if (!rvalid[nt]) { x0 = floatx4{0.f, 0.f, 0.f, 0.f}; x1 = x0; }
-        split_bf16(x0[0], x0[1], qb_hi[nt][ks][0], qb_lo[nt][ks][0]);
-        split_bf16(x0[2], x0[3], qb_hi[nt][ks][1], qb_lo[nt][ks][1]);
-        split_bf16(x1[0], x1[1], qb_hi[nt][ks][2], qb_lo[nt][ks][2]);
-        split_bf16(x1[2], x1[3], qb_hi[nt][ks][3], qb_lo[nt][ks][3]);
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        const int d0 = ks * 32 + j4 * 8;  // dims d0 .. d0+7 and their partners d0+D/2 ..
+        const u32x4 lo16 = *reinterpret_cast<const u32x4*>(qr + d0);
+        const u32x4 hi16 = *reinterpret_cast<const u32x4*>(qr + d0 + D / 2);
+        float yl[8], yh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double2 t = cs[d0 + e];
+          const double xl = (double)bf16_to_f32((uint16_t)((lo16[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+          const double xh = (double)bf16_to_f32((uint16_t)((hi16[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+          yl[e] = rvalid[nt] ? (float)(xl * t.x - xh * t.y) * a.scale_log2 : 0.f;
+          yh[e] = rvalid[nt] ? (float)(xh * t.x + xl * t.y) * a.scale_log2 : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          split_bf16(yl[2 * e], yl[2 * e + 1], qb_hi[nt][ks][e], qb_lo[nt][ks][e]);
+          split_bf16(yh[2 * e], yh[2 * e + 1], qb_hi[nt][ks + KS / 2][e], qb_lo[nt][ks + KS / 2][e]);
+        }
       }
       m_run[nt] = -INFINITY;
       l_run[nt] = 0.f;
@@ -1361,8 +1392,18 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       xh[3] = (double)bf16_to_f32(hi.y >> 16);
     }
     double cs[QP], sn[QP];
+    if (a.rope_cs) {  // the angles of token i, computed once for all its heads
+      const double2* t = reinterpret_cast<const double2*>(a.rope_cs) + (size_t)i * half + p0;
 #pragma unroll
-    for (int e = 0; e < QP; ++e) sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
+      for (int e = 0; e < QP; ++e) {
+        const double2 v = t[e];
+        cs[e] = v.x;
+        sn[e] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < QP; ++e) sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
+    }
     uint32_t yl[QP / 2], yh[QP / 2];
 #pragma unroll
     for (int e = 0; e < QP / 2; ++e) {
@@ -1568,33 +1609,42 @@ int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
 }
 
 template <int D, int G>
-static hipError_t launch_prefill_dg(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
+static hipError_t launch_prefill_dg(const PrefillArgs& a, hipStream_t s) {
   const int grid = a.writer_wgs + a.host_wgs + a.dev_wgs;
   if (grid <= 0) return hipSuccess;
   if (a.pages)
-    hipLaunchKernelGGL((prefill_split_kernel<D, G, true, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a, q_rot);
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, true, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_split_kernel<D, G, false, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a, q_rot);
+    hipLaunchKernelGGL((prefill_split_kernel<D, G, false, kPfNtw>), dim3(grid), dim3(pf_threads<kPfNtw>()), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const PrefillArgs& a, const float* q_rot, hipStream_t s) {
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_prefill_dg<D, 1>(a, q_rot, s);
-    case 2: return launch_prefill_dg<D, 2>(a, q_rot, s);
-    case 4: return launch_prefill_dg<D, 4>(a, q_rot, s);
-    case 8: return launch_prefill_dg<D, 8>(a, q_rot, s);
+    case 1: return launch_prefill_dg<D, 1>(a, s);
+    case 2: return launch_prefill_dg<D, 2>(a, s);
+    case 4: return launch_prefill_dg<D, 4>(a, s);
+    case 8: return launch_prefill_dg<D, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-int launch_prefill(const PrefillArgs& a, const float* q_rot, void* stream) {
+int launch_prefill(const PrefillArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.host_wgs + a.dev_wgs <= 0) return (int)hipSuccess;
-  if (a.head_dim == 64) return (int)launch_prefill_d<64>(a, q_rot, s);
-  if (a.head_dim == 128) return (int)launch_prefill_d<128>(a, q_rot, s);
+  if (a.head_dim == 64) return (int)launch_prefill_d<64>(a, s);
+  if (a.head_dim == 128) return (int)launch_prefill_d<128>(a, s);
   return (int)hipErrorInvalidValue;
+}
+
+int launch_rope_table(const int32_t* rowpos, int n_rows, int d, const RopeFreq& freq, double* cs,
+                      const int32_t* plan_offsets, int32_t* split_offsets, void* stream) {
+  const int64_t total = (int64_t)n_rows * (d / 2);
+  const int bx = (int)std::max<int64_t>(1, std::min<int64_t>((total + kThreads - 1) / kThreads, 16384));
+  hipLaunchKernelGGL(rope_table_kernel, dim3(bx), dim3(kThreads), 0, (hipStream_t)stream, rowpos, n_rows, d / 2,
+                     freq, reinterpret_cast<double2*>(cs), plan_offsets, split_offsets);
+  return (int)hipGetLastError();
 }
 
 int launch_stage(const StageArgs& a, int nwg, void* stream) {

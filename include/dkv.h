@@ -214,7 +214,7 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
  * must cover every query position.  Each row is rotated by Neox RoPE at its
  * position and attends to tokens 0 .. its position (causal):
  *   s_t = scale * q_rot . k_t (t <= p),  o = softmax(s) V,  lse = ln sum e^s.
- * q is [T][Hq][D] bf16 (device), T = q_start[batch].
+ * q is [T][Hq][D] bf16 (device, 16-byte aligned), T = q_start[batch].
  *
  * Output is split like dkv_decode_attn_split: the rows of a block of 128/G
  * consecutive rows share runs of cached tokens, one per tier and chunk;
