@@ -1338,18 +1338,9 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   if (he != hipSuccess) return hip_err(he, "plan upload");
   uint16_t* fresh_k = reinterpret_cast<uint16_t*>(ws + F.fresh_off);
   uint16_t* fresh_v = fresh_k + (size_t)L.n_rows * kvd;
-  // 0. the rows' rotation angles, shared by the key append and the queries
   const bool direct = L.num_splits == L.n_rows && out_lse != nullptr;
   int32_t* offs = reinterpret_cast<int32_t*>(ws + F.offsets_off);
   double* rope_cs = reinterpret_cast<double*>(ws + L.blob_bytes);
-  {
-    TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
-    he = (hipError_t)dkv::launch_rope_table(reinterpret_cast<const int32_t*>(ws + L.rowpos_off), L.n_rows,
-                                            kv->head_dim, rope_freq(rope_theta, kv->head_dim), rope_cs,
-                                            reinterpret_cast<const int32_t*>(ws + L.offsets_off), offs, stream);
-    t_rope.done();
-    if (he != hipSuccess) return hip_err(he, "rope table launch");
-  }
   // 1. new K/V (projection) -> cache slots and the fresh rows
   dkv::AppendArgs a{};
   a.batch = batch;
@@ -1372,7 +1363,6 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   a.hkv = kv->num_kv_heads;
   a.head_dim = kv->head_dim;
   a.freq = rope_freq(rope_theta, kv->head_dim);
-  a.rope_cs = rope_cs;
   a.fresh_k = fresh_k;
   a.fresh_v = fresh_v;
   if (proj) {
@@ -1396,14 +1386,16 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
   }
-  // the HBM copy of the new rows first (attention reads it); the writes into
-  // their cache slots (PCIe writes when the slots are host-resident) are done
-  // by writer workgroups of the prefill launch, concurrently with attention
+  // the HBM copy of the new rows first (attention reads it), with the rows'
+  // rotation table (the queries use it); the writes into their cache slots
+  // (PCIe writes when the slots are host-resident) are done by writer
+  // workgroups of the prefill launch, concurrently with attention
   {
     dkv::AppendArgs af = a;
     af.skip_slots = 1;
     TimedLaunch tl(DKV_KERNEL_APPEND, s);
-    he = (hipError_t)dkv::launch_append(af, stream);
+    he = (hipError_t)dkv::launch_append_rows(af, rope_cs, reinterpret_cast<const int32_t*>(ws + L.offsets_off),
+                                             offs, stream);
     tl.done();
     if (he != hipSuccess) return hip_err(he, "append launch");
   }

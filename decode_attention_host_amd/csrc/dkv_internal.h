@@ -208,7 +208,6 @@ struct AppendArgs {
   int32_t hkv;
   int32_t head_dim;
   RopeFreq freq;
-  const double* rope_cs;         // optional [n_new][D/2] (cos, sin) of token i's angles
 };
 
 struct ProjArgs {
@@ -313,6 +312,12 @@ int launch_stage(const StageArgs& a, int nwg, void* stream);
 int launch_linear(const LinearArgs& a, void* stream);
 // max_wgs > 0 caps the grid (the kernel loops over the tokens).
 int launch_append(const AppendArgs& a, void* stream, int max_wgs = 0);
+// Fused prefill step: the new rows' keys (rotated) and values into fresh_k /
+// fresh_v (and their slots unless skip_slots), and their rotation table
+// [n_new][D/2] (cos, sin) in fp64; block 0 also copies plan_offsets[0 ..
+// n_new] to split_offsets.
+int launch_append_rows(const AppendArgs& a, double* table, const int32_t* plan_offsets,
+                       int32_t* split_offsets, void* stream);
 int launch_project(const ProjArgs& a, void* stream);
 int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
                       void* stream);

@@ -1355,6 +1355,89 @@ __global__ __launch_bounds__(kMergeWaveThreads) void merge_lse_wave_kernel(Merge
 // it loops over the KV heads so each angle's sin/cos is computed once.
 // ---------------------------------------------------------------------------
 
+// Fused prefill step: the rotation table of the new rows and their keys and
+// values.  One thread per (row, group of QP pairs): it computes the pairs'
+// (cos, sin) once, stores them in the table (the prefill kernel rotates the
+// queries with them) and rotates that slice of the row's key for every KV
+// head.  Rows go to the HBM copy (fresh_k/fresh_v) and, unless skip_slots,
+// to their cache slots; projection mode reads kv_proj as append_kernel does.
+__global__ __launch_bounds__(kThreads) void append_rows_kernel(AppendArgs a, double2* __restrict__ table,
+                                                               const int32_t* __restrict__ plan_offsets,
+                                                               int32_t* __restrict__ split_offsets) {
+  constexpr int QP = 4;  // rotation pairs per thread
+  if (blockIdx.x == 0 && split_offsets)
+    for (int i = threadIdx.x; i <= a.n_new; i += blockDim.x) split_offsets[i] = plan_offsets[i];
+  const int D = a.head_dim, half = D / 2, groups = half / QP;
+  const int kvd = a.hkv * D;
+  const int64_t total = (int64_t)a.n_new * groups;
+  for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total;
+       gidx += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(gidx / groups);
+    const int p0 = (int)(gidx - (int64_t)i * groups) * QP;
+    const double pos = (double)a.pos[i];
+    double cs[QP], sn[QP];
+#pragma unroll
+    for (int e = 0; e < QP; ++e) {
+      sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
+      table[(size_t)i * half + p0 + e] = make_double2(cs[e], sn[e]);
+    }
+    const Slot sl = a.skip_slots ? Slot{nullptr, nullptr, false} : append_slot(a, i);
+    for (int h = 0; h < a.hkv; ++h) {
+      double xl[QP], xh[QP];
+      uint2 v0, v1;
+      if (a.kv_proj) {
+        const float* kp = a.kv_proj + (size_t)i * 2 * kvd + h * D;
+        const float* vp = kp + kvd;
+#pragma unroll
+        for (int e = 0; e < QP; ++e) {
+          xl[e] = (double)kp[p0 + e];
+          xh[e] = (double)kp[half + p0 + e];
+        }
+        v0 = make_uint2(f32_to_bf16(vp[p0]) | (f32_to_bf16(vp[p0 + 1]) << 16),
+                        f32_to_bf16(vp[p0 + 2]) | (f32_to_bf16(vp[p0 + 3]) << 16));
+        v1 = make_uint2(f32_to_bf16(vp[half + p0]) | (f32_to_bf16(vp[half + p0 + 1]) << 16),
+                        f32_to_bf16(vp[half + p0 + 2]) | (f32_to_bf16(vp[half + p0 + 3]) << 16));
+      } else {
+        const uint16_t* kp = a.k_new + (size_t)i * kvd + h * D;
+        const uint16_t* vs = a.v_new + (size_t)i * kvd + h * D;
+        const uint2 lo = *reinterpret_cast<const uint2*>(kp + p0);
+        const uint2 hi = *reinterpret_cast<const uint2*>(kp + half + p0);
+        v0 = *reinterpret_cast<const uint2*>(vs + p0);
+        v1 = *reinterpret_cast<const uint2*>(vs + half + p0);
+        xl[0] = (double)bf16_to_f32(lo.x & 0xffffu);
+        xl[1] = (double)bf16_to_f32(lo.x >> 16);
+        xl[2] = (double)bf16_to_f32(lo.y & 0xffffu);
+        xl[3] = (double)bf16_to_f32(lo.y >> 16);
+        xh[0] = (double)bf16_to_f32(hi.x & 0xffffu);
+        xh[1] = (double)bf16_to_f32(hi.x >> 16);
+        xh[2] = (double)bf16_to_f32(hi.y & 0xffffu);
+        xh[3] = (double)bf16_to_f32(hi.y >> 16);
+      }
+      uint32_t yl[QP / 2], yh[QP / 2];
+#pragma unroll
+      for (int e = 0; e < QP / 2; ++e) {
+        const int e0 = 2 * e, e1 = 2 * e + 1;
+        yl[e] = f64_to_bf16(xl[e0] * cs[e0] - xh[e0] * sn[e0]) |
+                (f64_to_bf16(xl[e1] * cs[e1] - xh[e1] * sn[e1]) << 16);
+        yh[e] = f64_to_bf16(xh[e0] * cs[e0] + xl[e0] * sn[e0]) |
+                (f64_to_bf16(xh[e1] * cs[e1] + xl[e1] * sn[e1]) << 16);
+      }
+      uint16_t* fk = a.fresh_k + (size_t)i * kvd + h * D;
+      uint16_t* fv = a.fresh_v + (size_t)i * kvd + h * D;
+      *reinterpret_cast<uint2*>(fk + p0) = make_uint2(yl[0], yl[1]);
+      *reinterpret_cast<uint2*>(fk + half + p0) = make_uint2(yh[0], yh[1]);
+      *reinterpret_cast<uint2*>(fv + p0) = v0;
+      *reinterpret_cast<uint2*>(fv + half + p0) = v1;
+      if (sl.ok) {
+        *reinterpret_cast<uint2*>(sl.k + h * D + p0) = make_uint2(yl[0], yl[1]);
+        *reinterpret_cast<uint2*>(sl.k + h * D + half + p0) = make_uint2(yh[0], yh[1]);
+        *reinterpret_cast<uint2*>(sl.v + h * D + p0) = v0;
+        *reinterpret_cast<uint2*>(sl.v + h * D + half + p0) = v1;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   constexpr int QP = 4;  // rotation pairs per thread
   const int D = a.head_dim, half = D / 2, groups = half / QP;
@@ -1392,18 +1475,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       xh[3] = (double)bf16_to_f32(hi.y >> 16);
     }
     double cs[QP], sn[QP];
-    if (a.rope_cs) {  // the angles of token i, computed once for all its heads
-      const double2* t = reinterpret_cast<const double2*>(a.rope_cs) + (size_t)i * half + p0;
 #pragma unroll
-      for (int e = 0; e < QP; ++e) {
-        const double2 v = t[e];
-        cs[e] = v.x;
-        sn[e] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < QP; ++e) sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
-    }
+    for (int e = 0; e < QP; ++e) sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
     uint32_t yl[QP / 2], yh[QP / 2];
 #pragma unroll
     for (int e = 0; e < QP / 2; ++e) {
@@ -1703,6 +1776,15 @@ int launch_append(const AppendArgs& a, void* stream, int max_wgs) {
   const int cap = max_wgs > 0 ? std::min(max_wgs, 16384) : 16384;
   const int grid = (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
   hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_append_rows(const AppendArgs& a, double* table, const int32_t* plan_offsets,
+                       int32_t* split_offsets, void* stream) {
+  const int64_t total = (int64_t)a.n_new * (a.head_dim / 8);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kThreads - 1) / kThreads, 16384));
+  hipLaunchKernelGGL(append_rows_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a,
+                     reinterpret_cast<double2*>(table), plan_offsets, split_offsets);
   return (int)hipGetLastError();
 }
 
