@@ -596,7 +596,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this path runs on one GPU: bench.py measures N=1 only; "
-                          "the multi-GPU sharding is described in DESIGN.md, not built"}), flush=True)
+                          "sharding over several GPUs is a design note, not built"}), flush=True)
         sys.exit(2)
 
     import torch
