@@ -1356,33 +1356,37 @@ __global__ __launch_bounds__(kMergeWaveThreads) void merge_lse_wave_kernel(Merge
 // ---------------------------------------------------------------------------
 
 // Fused prefill step: the rotation table of the new rows and their keys and
-// values.  One thread per (row, group of QP pairs): it computes the pairs'
-// (cos, sin) once, stores them in the table (the prefill kernel rotates the
-// queries with them) and rotates that slice of the row's key for every KV
-// head.  Rows go to the HBM copy (fresh_k/fresh_v) and, unless skip_slots,
+// values.  One thread per (row, group of QP pairs, hpt KV heads): it computes
+// the pairs' (cos, sin) once, stores them in the table (first head chunk;
+// the prefill kernel rotates the queries with them) and rotates that slice of
+// the row's key for its heads.  Rows go to the HBM copy (fresh_k/fresh_v) and, unless skip_slots,
 // to their cache slots; projection mode reads kv_proj as append_kernel does.
 __global__ __launch_bounds__(kThreads) void append_rows_kernel(AppendArgs a, double2* __restrict__ table,
                                                                const int32_t* __restrict__ plan_offsets,
-                                                               int32_t* __restrict__ split_offsets) {
+                                                               int32_t* __restrict__ split_offsets, int hpt) {
   constexpr int QP = 4;  // rotation pairs per thread
   if (blockIdx.x == 0 && split_offsets)
     for (int i = threadIdx.x; i <= a.n_new; i += blockDim.x) split_offsets[i] = plan_offsets[i];
   const int D = a.head_dim, half = D / 2, groups = half / QP;
   const int kvd = a.hkv * D;
-  const int64_t total = (int64_t)a.n_new * groups;
+  const int hchunks = (a.hkv + hpt - 1) / hpt;  // threads per (row, pair group)
+  const int64_t total = (int64_t)a.n_new * groups * hchunks;
   for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total;
        gidx += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(gidx / groups);
-    const int p0 = (int)(gidx - (int64_t)i * groups) * QP;
+    const int64_t ig = gidx / hchunks;
+    const int hc = (int)(gidx - ig * hchunks);
+    const int i = (int)(ig / groups);
+    const int p0 = (int)(ig - (int64_t)i * groups) * QP;
     const double pos = (double)a.pos[i];
     double cs[QP], sn[QP];
 #pragma unroll
     for (int e = 0; e < QP; ++e) {
       sincos(pos * a.freq.f[p0 + e], &sn[e], &cs[e]);
-      table[(size_t)i * half + p0 + e] = make_double2(cs[e], sn[e]);
+      if (hc == 0) table[(size_t)i * half + p0 + e] = make_double2(cs[e], sn[e]);
     }
     const Slot sl = a.skip_slots ? Slot{nullptr, nullptr, false} : append_slot(a, i);
-    for (int h = 0; h < a.hkv; ++h) {
+    const int h1 = min(a.hkv, (hc + 1) * hpt);
+    for (int h = hc * hpt; h < h1; ++h) {
       double xl[QP], xh[QP];
       uint2 v0, v1;
       if (a.kv_proj) {
@@ -1781,10 +1785,13 @@ int launch_append(const AppendArgs& a, void* stream, int max_wgs) {
 
 int launch_append_rows(const AppendArgs& a, double* table, const int32_t* plan_offsets,
                        int32_t* split_offsets, void* stream) {
-  const int64_t total = (int64_t)a.n_new * (a.head_dim / 8);
+  // heads per thread: at most 2, so that a few thousand rows still give
+  // every CU several waves (the angles are computed once per thread)
+  const int hpt = std::min(a.hkv, 2);
+  const int64_t total = (int64_t)a.n_new * (a.head_dim / 8) * ((a.hkv + hpt - 1) / hpt);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kThreads - 1) / kThreads, 16384));
   hipLaunchKernelGGL(append_rows_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a,
-                     reinterpret_cast<double2*>(table), plan_offsets, split_offsets);
+                     reinterpret_cast<double2*>(table), plan_offsets, split_offsets, hpt);
   return (int)hipGetLastError();
 }
 
