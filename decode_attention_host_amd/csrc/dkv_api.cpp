@@ -1386,13 +1386,27 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
   }
+  // Does any new row land in a host slot?  Those writes cross the link and
+  // are done by writer workgroups of the prefill launch, concurrently with
+  // attention; when every slot is in HBM the append writes them itself.
+  bool host_slots = false;
+  for (int b = 0; b < batch && !host_slots; ++b) {
+    const int64_t p0 = q_pos0[b], p1 = p0 + (q_start[b + 1] - q_start[b]);
+    if (p1 <= p0) continue;
+    if (kv->page_size == 0) {
+      host_slots = p0 < (int64_t)std::floor(a.ratio * (double)seq_lens[b]);
+    } else {
+      for (int64_t pg = p0 / kv->page_size; pg <= (p1 - 1) / kv->page_size && !host_slots; ++pg) {
+        const int32_t e = pg < kv->max_pages ? kv->page_table_host[(int64_t)b * kv->max_pages + pg] : -1;
+        host_slots = e >= 0 && (e & 1);
+      }
+    }
+  }
   // the HBM copy of the new rows first (attention reads it), with the rows'
-  // rotation table (the queries use it); the writes into their cache slots
-  // (PCIe writes when the slots are host-resident) are done by writer
-  // workgroups of the prefill launch, concurrently with attention
+  // rotation table (the queries use it)
   {
     dkv::AppendArgs af = a;
-    af.skip_slots = 1;
+    af.skip_slots = host_slots ? 1 : 0;
     TimedLaunch tl(DKV_KERNEL_APPEND, s);
     he = (hipError_t)dkv::launch_append_rows(af, rope_cs, reinterpret_cast<const int32_t*>(ws + L.offsets_off),
                                              offs, stream);
@@ -1405,7 +1419,7 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
   float* part_o = direct ? out_o : reinterpret_cast<float*>(ws + F.part_o_off);
   float* part_lse = direct ? out_lse : reinterpret_cast<float*>(ws + F.part_lse_off);
   st = prefill_stages(kv, num_q_heads, q, L, ws, scale, rope_theta, fresh_k, fresh_v, part_o, part_lse, offs,
-                      stream, &a, true);
+                      stream, host_slots ? &a : nullptr, true);
   if (st != DKV_OK) return st;
   if (direct) return ok();
   // 3. merge of each row's splits

@@ -119,13 +119,16 @@ def test_fused_equals_two_call_path(dk):
     c1.free(); c2.free()
 
 
-def test_fused_paged_ragged(dk):
+@pytest.mark.parametrize("host_frac", [0.8, 0.0])
+def test_fused_paged_ragged(dk, host_frac):
+    # 0.8: some new rows land in host pages (written by the prefill launch's
+    # writer workgroups); 0.0: every page is in HBM (the append writes them)
     import torch
     from decode_attention_host_amd.cache_build import paged_cache
     lens, news, hq, hkv, d, th = [500, 17, 1200], [100, 17, 333], 32, 8, 128, 5e5
     ks, vs = kv_raw(120, lens, hkv, d)
     qs = [normal_bf16(120 + b, 1, (n, hq, d)) for b, n in enumerate(news)]
-    pt, nh, nd = paged_table(120, lens, 16, 0.8)
+    pt, nh, nd = paged_table(120, lens, 16, host_frac)
     pre = [L - n for L, n in zip(lens, news)]
     cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, th, upto=pre)
     kn, vn = _new_rows(ks, vs, lens, news)
