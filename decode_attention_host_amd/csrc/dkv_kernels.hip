@@ -1,12 +1,20 @@
 // dkv_kernels.hip - gfx950 kernels of the zero-copy split decode attention path.
 //
-//   rope_q_kernel       rotate each query head (Neox RoPE, fp64 angle) once per call
-//   attn_split_kernel   stream K/V tiles of one tier into LDS, Q.K on MFMA,
-//                       online softmax, P.V on the vector ALUs, write (o, lse)
-//   merge_lse_kernel    combine per-split partials by log-sum-exp
-//   append_kernel       Neox RoPE of new keys (fp64) + bf16 store into the cache slot
-//   proj_kernel         new-token K/V projection on MFMA (split over the hidden dim)
-//   probe_read_kernel   streaming-read bandwidth probe with the attention load pattern
+//   rope_q_kernel         rotate each query head (Neox RoPE, fp64 angle) once per call
+//   attn_split_kernel     stream K/V tiles of one tier into LDS, Q.K on MFMA,
+//                         online softmax, P.V on the vector ALUs, write (o, lse)
+//   merge_lse_kernel      combine per-split partials by log-sum-exp (one workgroup
+//   merge_lse_wave_kernel   per pair for few long lists, one wave per pair for many)
+//   append_kernel         Neox RoPE of new keys (fp64) + bf16 store into the cache slot
+//   proj_kernel           new-token K/V projection on MFMA (split over the hidden dim)
+//   proj_reduce_kernel    sum of the projection's hidden-dim partials
+//   rope_table_kernel     (cos, sin) of every prefill row's angles, fp64
+//   append_rows_kernel    fused prefill step: append of the new rows + their rotation table
+//   prefill_split_kernel  causal prefill attention over both tiers, both products on MFMA
+//   stage_copy_kernel     copy of host-tier rows that prefill re-reads into HBM
+//   linear_split_kernel   y = x W^T with W split by rows between host memory and HBM
+//   linear_reduce_kernel  sum of the linear's K-range partials
+//   probe_read_kernel     streaming-read bandwidth probe with the attention load pattern
 //
 // Method sources (page, section): DirectKV README, introduction (fused projection,
 // Neox RoPE and attention reading KV from CPU-pinned buffers) and Attribution

@@ -50,6 +50,7 @@ CASES = [
     (17, 777, 2056, 0.9, 0.02),     # two token tiles
     (64, 256, 512, 0.75, 1.0),      # four token tiles
     (100, 300, 4096, 0.5, 0.02),    # two launches of tokens
+    (5, 200, 3000, 0.0, 0.5),       # K split into ranges of 1504 and 1496: both end inside a chunk
 ]
 
 
