@@ -23,6 +23,15 @@ pytestmark = pytest.mark.gpu
 HBM_PEAK_GBS = 8000.0
 
 
+@pytest.fixture(scope="module")
+def dk():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import decode_attention_host_amd as dk
+    dk.reset_tuning()
+    return dk
+
+
 def link_nominal_gbs():
     """PCIe link speed x width of the visible GPU from sysfs (128b/130b), per
     direction; 64 GB/s (5.0 x16) when sysfs does not say."""
