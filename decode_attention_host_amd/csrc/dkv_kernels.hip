@@ -184,6 +184,21 @@ struct AttnShape {
   static constexpr int kDimsPerLane = D / 64;            // P.V output dims per lane
 };
 
+// A plan item read through the scalar cache (constant address space): the
+// fields land in SGPRs, so taking them over as the current item waits for
+// this load alone and not for the tile loads issued after it.
+__device__ __forceinline__ PlanItem load_plan_item_uniform(const PlanItem* p) {
+  static_assert(sizeof(PlanItem) == 32, "item size");
+  typedef __attribute__((address_space(4))) const u32x4 ConstVec;
+  const ConstVec* w = (const ConstVec*)p;
+  struct Raw {
+    u32x4 v[2];
+  } t;
+  t.v[0] = w[0];
+  t.v[1] = w[1];
+  return __builtin_bit_cast(PlanItem, t);
+}
+
 template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const float* __restrict__ q_rot) {
   using S = AttnShape<D>;
@@ -225,6 +240,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
 
   u32x4 kreg[NC], vreg[NC];
   auto load_tile = [&](const PlanItem& it, int kvh, int tile) {
+    // paged: every chunk's page-list entry, then every page-table entry, then
+    // the K/V loads, so a tile costs two lookup round trips, not two per chunk
+    // each waiting behind the previous chunk's K/V loads
+    // (tokens past the item look up its last token's page: every lookup is
+    // in bounds and none waits for a select on its result)
+    int32_t pte[NC];
+    if (PAGED) {
+      int lp[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int tok = min(tile * kTile + (tid + c * kThreads) / S::kChunksPerRow, it.n_tok - 1);
+        lp[c] = a.plist[it.plist + (tok >> a.page_shift)];
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) pte[c] = a.page_table[(int64_t)it.b * a.max_pages + lp[c]];
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int chunk = tid + c * kThreads;
@@ -234,13 +265,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
       bool valid = tok < it.n_tok;
       int64_t row = 0;
       if (PAGED) {
-        if (valid) {
-          const int lp = a.plist[it.plist + (tok >> a.page_shift)];
-          const int32_t e = a.page_table[(int64_t)it.b * a.max_pages + lp];
-          const int64_t phys = (int64_t)(e >> 1);
-          row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
-          valid = e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
-        }
+        const int32_t e = pte[c];
+        const int64_t phys = (int64_t)(e >> 1);
+        row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
+        valid = valid && e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
       } else {
         row = it.row0 + tok;
       }
@@ -276,15 +304,26 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
     {
       const int hsel = n & 7;
       const bool active = hsel < G;
+      // Every lane loads its 8 dims per k-step with two 16-byte loads, all
+      // issued before any is used (inactive lanes read head 0's row and are
+      // zeroed afterwards): one round trip per unit instead of one per pair
+      // of dims, which cost about 7 us per unit with HBM streaming.  q_rot
+      // sits in the 256-byte aligned workspace.
       const float* qr = q_rot + ((size_t)it.b * a.hq + kvh * G + (active ? hsel : 0)) * D;
+      floatx4 qv[KS][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = ks * 32 + j4 * 8;
+        const floatx4* p = reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8);
+        qv[ks][0] = p[0];
+        qv[ks][1] = p[1];
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = active ? qr[d0 + 2 * e] : 0.f;
-          const float x1 = active ? qr[d0 + 2 * e + 1] : 0.f;
+          const float x0 = active ? qv[ks][e >> 1][(e & 1) * 2] : 0.f;
+          const float x1 = active ? qv[ks][e >> 1][(e & 1) * 2 + 1] : 0.f;
           uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
           if (n >= 8) {  // low part: residual after the high part
             b0 = f32_to_bf16(x0 - bf16_to_f32(b0));
@@ -326,9 +365,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
       if (!last) {
         load_tile(it, kvh, tile + 1);
       } else {
-        next_u = s_next;
+        next_u = __builtin_amdgcn_readfirstlane(s_next);
         if (next_u < nunits) {
-          nit = items[next_u / a.hkv];
+          nit = load_plan_item_uniform(items + next_u / a.hkv);
           nkvh = next_u - (next_u / a.hkv) * a.hkv;
           load_tile(nit, nkvh, 0);
         }
