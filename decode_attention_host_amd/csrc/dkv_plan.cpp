@@ -142,36 +142,51 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
   // 0.032 ms as 512 units of 512 against 0.038 ms as 256 units of 1024 on
   // MI355X (the unit's fixed cost is one round trip for its query operand).
   const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 6, 512, 1 << 16, align, in.dev_chunk);
+  // Guided tail for long HBM ranges: the last part of every sequence's HBM
+  // range is cut into quarter-size units that go to the end of the work list,
+  // about two per workgroup, so the workgroups run out of work nearly together
+  // (units of a few thousand tokens otherwise leave them finishing up to one
+  // unit apart).
+  const int64_t cs = round_up(cd / 4, align);
+  const bool guided = in.dev_chunk <= 0 && cs >= 512 && dev_tok * in.hkv >= (int64_t)cd * wd * 4;
+  const double tail_frac = guided ? std::min(0.5, 2.0 * wd * cs / ((double)dev_tok * in.hkv)) : 0.0;
 
   // ---- items
-  std::vector<PlanItem> hitems, ditems;
+  std::vector<PlanItem> hitems, ditems, dtail;
   std::vector<int32_t> plist;
   std::vector<int32_t> offsets(B + 1, 0);
   int32_t slot = 0;
   for (int b = 0; b < B; ++b) {
     offsets[b] = slot;
     for (int tier = 1; tier >= 0; --tier) {
-      std::vector<PlanItem>& dst = tier ? hitems : ditems;
-      const int64_t chunk = tier ? ch : cd;
       if (!paged) {
         const int64_t nh = n_host[b];
         const int64_t begin = tier ? 0 : nh;
         const int64_t end = tier ? nh : (int64_t)in.seq_lens[b];
-        for (int64_t t0 = begin; t0 < end; t0 += chunk) {
+        // tokens [split, end) of the HBM range form the guided tail
+        const int64_t split = tier ? end : end - ((int64_t)((end - begin) * tail_frac) / align) * align;
+        for (int64_t t0 = begin; t0 < end;) {
+          const bool tail = t0 >= split;
+          const int64_t chunk = tier ? ch : (tail ? cs : cd);
           PlanItem it{};
           it.b = b;
           it.slot = slot++;
-          it.n_tok = (int32_t)std::min<int64_t>(chunk, end - t0);
+          it.n_tok = (int32_t)std::min<int64_t>(chunk, (tail ? end : split) - t0);
           it.plist = 0;
           it.row0 = tier ? (int64_t)b * in.host_stride + t0 : (int64_t)b * in.dev_stride + (t0 - nh);
-          dst.push_back(it);
+          (tier ? hitems : (tail ? dtail : ditems)).push_back(it);
+          t0 += it.n_tok;
         }
       } else {
         const std::vector<int32_t>& pages = tier ? host_pages[b] : dev_pages[b];
         const int64_t L = in.seq_lens[b];
-        const int64_t per = chunk / P;
-        for (size_t k0 = 0; k0 < pages.size(); k0 += per) {
-          const size_t k1 = std::min(pages.size(), k0 + (size_t)per);
+        const size_t npg = pages.size();
+        const size_t split = tier ? npg : npg - (size_t)((double)npg * tail_frac) / (size_t)(align / P) *
+                                                  (size_t)(align / P);
+        for (size_t k0 = 0; k0 < npg;) {
+          const bool tail = k0 >= split;
+          const int64_t per = (tier ? ch : (tail ? cs : cd)) / P;
+          const size_t k1 = std::min(tail ? npg : split, k0 + (size_t)per);
           int64_t ntok = 0;
           for (size_t k = k0; k < k1; ++k) ntok += std::min<int64_t>(P, L - (int64_t)pages[k] * P);
           PlanItem it{};
@@ -181,12 +196,14 @@ bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob
           it.plist = (int32_t)plist.size();
           it.row0 = 0;
           for (size_t k = k0; k < k1; ++k) plist.push_back(pages[k]);
-          dst.push_back(it);
+          (tier ? hitems : (tail ? dtail : ditems)).push_back(it);
+          k0 = k1;
         }
       }
     }
   }
   offsets[B] = slot;
+  ditems.insert(ditems.end(), dtail.begin(), dtail.end());
 
   out->n_host_items = (int32_t)hitems.size();
   out->n_dev_items = (int32_t)ditems.size();

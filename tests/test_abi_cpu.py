@@ -276,3 +276,67 @@ def test_planner_rejects_layout_overflow(L):
         plan_inspect(xp, 1, 32, [20], 0.0, 8)   # second page unmapped
     with pytest.raises(dkv_lib.DkvError):
         plan_inspect(xp, 1, 32, [40], 0.0, 8)   # 3 pages > max_pages
+
+
+def _ranges_cover(items, lens, ratio, hs, ds):
+    # item token ranges tile [0, L_b) of every sequence exactly once
+    per = {b: [] for b in range(len(lens))}
+    for tier, b, slot, ntok, first in items:
+        nh = O.contig_split_point(ratio, lens[b])
+        t0 = first - b * hs if tier else first - b * ds + nh
+        per[int(b)].append((int(t0), int(ntok), int(tier)))
+    for b, rs in per.items():
+        rs.sort()
+        t = 0
+        nh = O.contig_split_point(ratio, lens[b])
+        for t0, n, tier in rs:
+            assert t0 == t and n >= 1 and tier == (1 if t0 < nh else 0) and (t0 + n <= nh or t0 >= nh)
+            t += n
+        assert t == lens[b]
+
+
+def test_planner_guided_tail_contiguous(L):
+    # long HBM ranges: the last part of each sequence is cut into smaller
+    # units that come last in the HBM work list; coverage is unchanged
+    lens = [1 << 20, 200000]
+    hs = ds = 1 << 20
+    x = desc(hkv=8, d=128, host_rows=0, dev_rows=2 * ds, hs=hs, ds=ds)
+    items, _, offs, info = inspect(L, x, 2, 32, lens, 0.0, cus=256)
+    _ranges_cover(items, lens, 0.0, hs, ds)
+    assert info["num_splits"] == len(items) == offs[-1]
+    for b in range(len(lens)):
+        assert sorted(int(s) for _, bb, s, _, _ in items if bb == b) == list(range(offs[b], offs[b + 1]))
+    ntok = items[:, 3]
+    big = int(info["dev_chunk"])
+    small = ntok < big // 2
+    assert small.any() and (~small).any()
+    first_small = int(np.argmax(small))
+    assert small[first_small:].all()                    # the small units come last
+    assert int(ntok[small].max()) <= (big // 4 + 63) // 64 * 64
+    # about two small units per HBM workgroup
+    n_small_units = int(small.sum()) * 8
+    assert info["dev_wgs"] <= n_small_units <= 4 * info["dev_wgs"]
+
+
+def test_planner_guided_tail_paged(L):
+    lens = [1 << 20]
+    npg = (1 << 20) // 16
+    perm = np.random.default_rng(1).permutation(npg).astype(np.int32)
+    pt = (perm << 1)[None, :].copy()
+    x = desc(hkv=8, d=128, page=16, max_pages=npg, host_rows=16, dev_rows=npg * 16, pt=pt)
+    items, plist, offs, info = inspect(L, x, 1, 32, lens, 0.0, cus=256)
+    covered = np.zeros(npg, dtype=np.int32)
+    for tier, b, slot, ntok, first in items:
+        assert tier == 0 and ntok % 16 == 0
+        covered[plist[first:first + ntok // 16]] += 1
+    assert (covered == 1).all()
+    ntok = items[:, 3]
+    small = ntok < int(info["dev_chunk"]) // 2
+    assert small.any() and small[int(np.argmax(small)):].all()
+
+
+def test_planner_no_guided_tail_when_units_are_small(L):
+    lens = [32768]
+    x = desc(hkv=8, d=128, host_rows=0, dev_rows=1 << 15, hs=1 << 15, ds=1 << 15)
+    items, _, offs, info = inspect(L, x, 1, 32, lens, 0.0, cus=256)
+    assert set(int(n) for n in items[:, 3]) == {int(info["dev_chunk"])}
