@@ -229,7 +229,6 @@ dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int3
   return DKV_OK;
 }
 
-size_t qrot_bytes(int32_t batch, int32_t hq, int32_t d) { return (size_t)batch * hq * d * 4; }
 
 // Stores a freshly built plan in the cache (or returns the entry another
 // thread stored first) and evicts unreferenced old entries.
@@ -551,7 +550,7 @@ dkv_status dkv_decode_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_h
   st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
   if (st != DKV_OK) return st;
   const dkv::PlanLayout& L = e->lay;
-  info->workspace_bytes = (int64_t)(L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim));
+  info->workspace_bytes = (int64_t)L.blob_bytes;
   info->num_splits = L.num_splits;
   info->host_items = L.n_host_items;
   info->dev_items = L.n_dev_items;
@@ -603,7 +602,7 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
   if (page_list)
     memcpy(page_list, blob.data() + L.plist_off, sizeof(int32_t) * std::min(L.n_plist, page_cap));
   if (split_offsets) memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * (batch + 1));
-  if (info) fill_info(L, L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim), info);
+  if (info) fill_info(L, L.blob_bytes, info);
   return ok();
 }
 
@@ -683,7 +682,7 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
   if (st != DKV_OK) return st;
   const dkv::PlanLayout& L = e->lay;
-  const size_t need = L.blob_bytes + qrot_bytes(batch, num_q_heads, kv->head_dim);
+  const size_t need = L.blob_bytes;
   if (workspace_bytes < need)
     return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
   if (num_splits_cap < L.num_splits)
@@ -709,16 +708,7 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
   if (he != hipSuccess) return hip_err(he, "plan upload");
-  float* q_rot = reinterpret_cast<float*>(ws + L.blob_bytes);
   const float scale_log2 = scale * 1.44269504088896340736f;
-  TimedLaunch t_rope(DKV_KERNEL_ROPE_Q, s);
-  he = (hipError_t)dkv::launch_rope_q(static_cast<const uint16_t*>(q), q_pos, q_rot, batch,
-                                      num_q_heads, kv->head_dim, rope_freq(rope_theta, kv->head_dim),
-                                      scale_log2,
-                                      reinterpret_cast<const int32_t*>(ws + L.offsets_off),
-                                      split_offsets, stream);
-  t_rope.done();
-  if (he != hipSuccess) return hip_err(he, "rope_q launch");
   dkv::AttnArgs a{};
   a.host_items = reinterpret_cast<const dkv::PlanItem*>(ws + L.items_off);
   a.dev_items = a.host_items + L.n_host_items;
@@ -749,13 +739,14 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   a.theta = rope_theta;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  a.freq = rope_freq(rope_theta, kv->head_dim);
   {
     std::lock_guard<std::mutex> lk(g_trace_mu);
     a.wg_trace = g_trace_buf;
     a.wg_trace_cap = g_trace_cap;
   }
   TimedLaunch t_attn(DKV_KERNEL_ATTN, s);
-  he = (hipError_t)dkv::launch_attn_with_q(a, q_rot, stream);
+  he = (hipError_t)dkv::launch_attn(a, stream);
   t_attn.done();
   if (he != hipSuccess) return hip_err(he, "attention launch");
   return ok();

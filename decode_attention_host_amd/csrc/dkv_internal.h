@@ -139,7 +139,7 @@ struct AttnArgs {
   const int32_t* plist;          // paged: logical page indices
   const int32_t* plan_offsets;   // [batch+1] split offsets (in the workspace)
   int32_t* unit_counters;        // [2] dynamic unit counters (HBM, host), zero at launch
-  int32_t* split_offsets;        // [batch+1] caller copy (written by block 0)
+  int32_t* split_offsets;        // [batch+1] caller copy (written by block 0), or NULL
   int32_t n_host_units;          // host items x Hkv
   int32_t n_dev_units;           // dev items x Hkv
   int32_t host_wgs;
@@ -167,6 +167,7 @@ struct AttnArgs {
   uint64_t* wg_trace;            // optional [grid][4]: start, end, role, units (wall clock)
   int32_t wg_trace_cap;
   int32_t pad1;
+  RopeFreq freq;                 // f_i = theta^(-2i/D), i < D/2
 };
 
 struct MergeArgs {
@@ -297,10 +298,7 @@ struct StageArgs {
 };
 
 // Launchers (dkv_kernels.hip).  They return hipError_t as int.
-int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
-                  const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
-                  int32_t* split_offsets, void* stream);
-int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream);
+int launch_attn(const AttnArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
 // (cos, sin) in fp64 of the rotation angles of every prefill row:

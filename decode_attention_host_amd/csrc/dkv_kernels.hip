@@ -1,8 +1,8 @@
 // dkv_kernels.hip - gfx950 kernels of the zero-copy split decode attention path.
 //
-//   rope_q_kernel         rotate each query head (Neox RoPE, fp64 angle) once per call
-//   attn_split_kernel     stream K/V tiles of one tier into LDS, Q.K on MFMA,
-//                         online softmax, P.V on the vector ALUs, write (o, lse)
+//   attn_split_kernel     rotate the unit's query heads (Neox RoPE, fp64 angle), stream
+//                         K/V tiles of one tier into LDS, Q.K on MFMA, online softmax,
+//                         P.V on the vector ALUs, write (o, lse)
 //   merge_lse_kernel      combine per-split partials by log-sum-exp (one workgroup
 //   merge_lse_wave_kernel   per pair for few long lists, one wave per pair for many)
 //   append_kernel         Neox RoPE of new keys (fp64) + bf16 store into the cache slot
@@ -80,78 +80,6 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
   return sign | em;
 }
 
-// ---------------------------------------------------------------------------
-// Query rotation: q_rot[b][h][d] = scale*log2(e) * RoPE(q[b][h], q_pos[b])[d].
-// Angle pos * f_i and sin/cos in fp64 (f_i from the host table), computed once
-// per (row, pair i, group of `hpt` consecutive heads) and applied to the group;
-// hpt grows with the number of rows so that about 2^19 threads run.  Block 0 also copies the split offsets of the plan to the
-// caller's array.
-// ---------------------------------------------------------------------------
-// VP consecutive rotation pairs per thread: the loads are VP bf16 wide and
-// the stores VP floats wide (VP = 4 when the pointers allow it).
-template <int VP>
-__global__ __launch_bounds__(kThreads) void rope_q_kernel(const uint16_t* __restrict__ q,
-                                                          const int32_t* __restrict__ q_pos,
-                                                          float* __restrict__ q_rot, int hq, int d,
-                                                          RopeFreq freq, float scale_log2,
-                                                          const int32_t* __restrict__ plan_offsets,
-                                                          int32_t* __restrict__ split_offsets,
-                                                          int batch, int hpt) {
-  const int half = d >> 1;
-  const int hv = half / VP;  // pair groups per head
-  if (blockIdx.x == 0 && split_offsets)
-    for (int i = threadIdx.x; i <= batch; i += blockDim.x) split_offsets[i] = plan_offsets[i];
-  const int groups = (hq + hpt - 1) / hpt;
-  const int64_t total = (int64_t)batch * groups * hv;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int i0 = (int)(idx % hv) * VP;
-    const int64_t bg = idx / hv;
-    const int g = (int)(bg % groups);
-    const int b = (int)(bg / groups);
-    double s[VP], c[VP];
-#pragma unroll
-    for (int v = 0; v < VP; ++v) sincos((double)q_pos[b] * freq.f[i0 + v], &s[v], &c[v]);
-    const int h1 = min(hq, (g + 1) * hpt);
-#pragma unroll 2
-    for (int h = g * hpt; h < h1; ++h) {
-      const uint16_t* qh = q + ((size_t)b * hq + h) * d;
-      float* o = q_rot + ((size_t)b * hq + h) * d;
-      uint16_t xl16[VP], xh16[VP];
-      if constexpr (VP == 4) {
-        const uint2 l = *reinterpret_cast<const uint2*>(qh + i0);
-        const uint2 u = *reinterpret_cast<const uint2*>(qh + i0 + half);
-        xl16[0] = l.x & 0xffffu; xl16[1] = l.x >> 16; xl16[2] = l.y & 0xffffu; xl16[3] = l.y >> 16;
-        xh16[0] = u.x & 0xffffu; xh16[1] = u.x >> 16; xh16[2] = u.y & 0xffffu; xh16[3] = u.y >> 16;
-      } else {
-#pragma unroll
-        for (int v = 0; v < VP; ++v) {
-          xl16[v] = qh[i0 + v];
-          xh16[v] = qh[i0 + v + half];
-        }
-      }
-      float lo[VP], hi[VP];
-#pragma unroll
-      for (int v = 0; v < VP; ++v) {
-        const double xl = (double)bf16_to_f32(xl16[v]);
-        const double xh = (double)bf16_to_f32(xh16[v]);
-        lo[v] = (float)(xl * c[v] - xh * s[v]) * scale_log2;
-        hi[v] = (float)(xh * c[v] + xl * s[v]) * scale_log2;
-      }
-      if constexpr (VP == 4) {
-        *reinterpret_cast<floatx4*>(o + i0) = floatx4{lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<floatx4*>(o + i0 + half) = floatx4{hi[0], hi[1], hi[2], hi[3]};
-      } else {
-#pragma unroll
-        for (int v = 0; v < VP; ++v) {
-          o[i0 + v] = lo[v];
-          o[i0 + v + half] = hi[v];
-        }
-      }
-    }
-  }
-}
-
 // (cos, sin) of every prefill row's rotation angles, fp64, computed once per
 // call; the prefill kernel rotates its query columns with them.
 __global__ __launch_bounds__(kThreads) void rope_table_kernel(const int32_t* __restrict__ rowpos, int n_rows,
@@ -200,7 +128,7 @@ __device__ __forceinline__ PlanItem load_plan_item_uniform(const PlanItem* p) {
 }
 
 template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const float* __restrict__ q_rot) {
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   using S = AttnShape<D>;
   constexpr int NC = S::kChunksPerThread;
   constexpr int KS = S::kKSteps;
@@ -213,6 +141,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
   __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
   __shared__ float a_lds[4][8];
+  __shared__ __attribute__((aligned(16))) float q_lds[G][D];  // the unit's rotated query heads
   __shared__ int s_next;
 
   const int tid = threadIdx.x;
@@ -220,6 +149,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
   const int wave = tid >> 6;
   const int n = lane & 15;     // MFMA column / row-in-tile
   const int j4 = lane >> 4;    // 0..3
+
+  if (blockIdx.x == 0 && a.split_offsets)
+    for (int i = tid; i <= a.batch; i += kThreads) a.split_offsets[i] = a.plan_offsets[i];
 
   // Role: the first host_wgs workgroups stream the host tier, the rest HBM.
   const bool host_role = (int)blockIdx.x < a.host_wgs;
@@ -316,31 +248,40 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, const 
     ++units_done;
     const int ntiles = (it.n_tok + kTile - 1) / kTile;
 
+    // ---- the unit's G query heads rotated at q_pos[b] (Neox pairs i, i + D/2;
+    // angle pos * f_i, sin and cos in fp64; rounded once to fp32 with
+    // scale * log2(e) folded in), one pair per thread, staged in LDS.  The
+    // previous unit's readers of q_lds passed several barriers since.
+    {
+      const int pos = a.q_pos[it.b];
+      const uint16_t* qh = a.q + ((size_t)it.b * a.hq + (size_t)kvh * G) * D;
+      for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
+        const int h = idx / (D / 2), i = idx - h * (D / 2);
+        double sn, cs;
+        sincos((double)pos * a.freq.f[i], &sn, &cs);
+        const double xl = (double)bf16_to_f32(qh[h * D + i]);
+        const double xh = (double)bf16_to_f32(qh[h * D + i + D / 2]);
+        q_lds[h][i] = (float)(xl * cs - xh * sn) * a.scale_log2;
+        q_lds[h][i + D / 2] = (float)(xh * cs + xl * sn) * a.scale_log2;
+      }
+      __syncthreads();
+    }
     // ---- query operand: columns h (high bf16 part) and h+8 (low part)
     bf16x8_t qb[KS];
     {
       const int hsel = n & 7;
       const bool active = hsel < G;
-      // Every lane loads its 8 dims per k-step with two 16-byte loads, all
-      // issued before any is used (inactive lanes read head 0's row and are
-      // zeroed afterwards): one round trip per unit instead of one per pair
-      // of dims, which cost about 7 us per unit with HBM streaming.  q_rot
-      // sits in the 256-byte aligned workspace.
-      const float* qr = q_rot + ((size_t)it.b * a.hq + kvh * G + (active ? hsel : 0)) * D;
-      floatx4 qv[KS][2];
+      const float* qr = &q_lds[active ? hsel : 0][0];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const floatx4* p = reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8);
-        qv[ks][0] = p[0];
-        qv[ks][1] = p[1];
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        const floatx4 lo4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8);
+        const floatx4 hi4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8 + 4);
+        const float x8[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = active ? qv[ks][e >> 1][(e & 1) * 2] : 0.f;
-          const float x1 = active ? qv[ks][e >> 1][(e & 1) * 2 + 1] : 0.f;
+          const float x0 = active ? x8[2 * e] : 0.f;
+          const float x1 = active ? x8[2 * e + 1] : 0.f;
           uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
           if (n >= 8) {  // low part: residual after the high part
             b0 = f32_to_bf16(x0 - bf16_to_f32(b0));
@@ -1730,54 +1671,31 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __res
 // Launchers
 // ---------------------------------------------------------------------------
 template <int D, int G>
-static hipError_t launch_attn_dg(const AttnArgs& a, const float* q_rot, hipStream_t s) {
-  const int grid = a.host_wgs + a.dev_wgs;
+static hipError_t launch_attn_dg(const AttnArgs& a, hipStream_t s) {
+  // at least one workgroup: block 0 also writes the caller's split offsets
+  const int grid = std::max(1, a.host_wgs + a.dev_wgs);
   if (a.page_shift >= 0 && a.page_table)
-    hipLaunchKernelGGL((attn_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+    hipLaunchKernelGGL((attn_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a, q_rot);
+    hipLaunchKernelGGL((attn_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_attn_d(const AttnArgs& a, const float* q_rot, hipStream_t s) {
+static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_attn_dg<D, 1>(a, q_rot, s);
-    case 2: return launch_attn_dg<D, 2>(a, q_rot, s);
-    case 4: return launch_attn_dg<D, 4>(a, q_rot, s);
-    case 8: return launch_attn_dg<D, 8>(a, q_rot, s);
+    case 1: return launch_attn_dg<D, 1>(a, s);
+    case 2: return launch_attn_dg<D, 2>(a, s);
+    case 4: return launch_attn_dg<D, 4>(a, s);
+    case 8: return launch_attn_dg<D, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-int launch_rope_q(const uint16_t* q, const int32_t* q_pos, float* q_rot, int batch, int hq, int d,
-                  const RopeFreq& freq, float scale_log2, const int32_t* plan_offsets,
-                  int32_t* split_offsets, void* stream) {
+int launch_attn(const AttnArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // four pairs per thread when q (8 B) and q_rot (16 B) are aligned for the
-  // wide accesses
-  const bool wide = (d / 2) % 4 == 0 && ((uintptr_t)q & 7) == 0 && ((uintptr_t)q_rot & 15) == 0;
-  const int vp = wide ? 4 : 1;
-  // heads per thread: enough threads (~2^19 pairs' worth) to hide load
-  // latency, sin/cos shared by the heads a thread covers
-  const int64_t pairs = (int64_t)batch * (d / 2);
-  const int hpt = (int)std::max<int64_t>(1, std::min<int64_t>(hq, pairs * hq >> 19));
-  const int64_t total = pairs / vp * ((hq + hpt - 1) / hpt);
-  const int bx = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
-  if (wide)
-    hipLaunchKernelGGL(rope_q_kernel<4>, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
-                       scale_log2, plan_offsets, split_offsets, batch, hpt);
-  else
-    hipLaunchKernelGGL(rope_q_kernel<1>, dim3(bx), dim3(kThreads), 0, s, q, q_pos, q_rot, hq, d, freq,
-                       scale_log2, plan_offsets, split_offsets, batch, hpt);
-  return (int)hipGetLastError();
-}
-
-int launch_attn_with_q(const AttnArgs& a, const float* q_rot, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (a.host_wgs + a.dev_wgs <= 0) return (int)hipSuccess;
-  if (a.head_dim == 64) return (int)launch_attn_d<64>(a, q_rot, s);
-  if (a.head_dim == 128) return (int)launch_attn_d<128>(a, q_rot, s);
+  if (a.head_dim == 64) return (int)launch_attn_d<64>(a, s);
+  if (a.head_dim == 128) return (int)launch_attn_d<128>(a, s);
   return (int)hipErrorInvalidValue;
 }
 

@@ -438,7 +438,8 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
  * kernel runs on.  dkv_kernel_timing_read waits for the recorded events,
  * returns how many launches were timed and their summed duration in ms, and
  * clears the record.  kernel: DKV_KERNEL_ATTN (split attention),
- * DKV_KERNEL_ROPE_Q (query rotation), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
+ * DKV_KERNEL_ROPE_Q (the two-call prefill's rotation table; decode rotates its
+ * queries inside the attention kernel), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
  * DKV_KERNEL_PREFILL (causal prefill attention), DKV_KERNEL_STAGE (prefill's
  * copy of re-read host rows into HBM), DKV_KERNEL_LINEAR (offloaded linear).
  * ---------------------------------------------------------------------- */
