@@ -454,11 +454,13 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
         flops += 4 * hq * d * sum(p0 + j + 1 for j in range(n))
 
     def timed(step):
+        # median of five timed loops: a step of ~0.1 ms leaves the GPU idle
+        # through any host-side stall of a few ms inside a single loop
         gpu_warm(step)
         dk.kernel_timing(True)
         for k in dk.api.KERNELS:
             dk.kernel_timing_read(k)
-        ms, _ = timed_loop(step, steps, warmup)
+        ms = statistics.median(timed_loop(step, steps, warmup)[0] for _ in range(5))
         kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
         dk.kernel_timing(False)
         return ms, {k: v[1] / max(1, v[0]) for k, v in kt.items() if v[0]}
