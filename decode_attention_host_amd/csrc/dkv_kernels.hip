@@ -1254,19 +1254,23 @@ __device__ __forceinline__ float block_reduce_n(float v, bool is_max, float* sm)
   return v;
 }
 
-// Workgroup = (b, h), 1024 threads: D/4 lanes each own 4 dims (one 16-byte
-// load per split), 4096/D groups of lanes fold every group-th split with
-// several loads in flight, then the groups combine through LDS.
+// Workgroup = (b, h, slice of DS), 1024 threads: D/(4 DS) lanes each own 4
+// of the slice's dims (one 16-byte load per split), the rest of the threads
+// form groups that fold every group-th split with several loads in flight,
+// then the groups combine through LDS.  With few (b, h) pairs (one sequence)
+// the dims are sliced over DS workgroups so that more CUs read the partials;
+// each slice recomputes the maximum and the sum from the lse list.
 constexpr int kMergeThreads = 1024;
 
-template <int D>
+template <int D, int DS>
 __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
-  constexpr int LANES = D / 4;
+  constexpr int DW = D / DS;  // dims of this workgroup
+  constexpr int LANES = DW / 4;
   constexpr int NG = kMergeThreads / LANES;
   constexpr int U = 4;
   __shared__ float sm_red[kMergeThreads / 64];
-  __shared__ __attribute__((aligned(16))) float sm_o[NG][D];
-  const int bh = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) float sm_o[NG][DW];
+  const int bh = blockIdx.x / DS, slice = blockIdx.x - bh * DS;
   const int b = bh / a.hq, h = bh - b * a.hq;
   const int tid = threadIdx.x;
   const int s0 = a.split_offsets[b], s1 = a.split_offsets[b + 1];
@@ -1274,10 +1278,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
   float m = -INFINITY;
   for (int s = s0 + tid; s < s1; s += kMergeThreads) m = fmaxf(m, lse[(size_t)s * a.hq]);
   const float M = block_reduce_n<kMergeThreads>(m, true, sm_red);
-  float* out = a.out_o + ((size_t)b * a.hq + h) * D;
+  float* out = a.out_o + ((size_t)b * a.hq + h) * D + slice * DW;
   if (M == -INFINITY) {  // no finite split
-    if (tid < D) out[tid] = 0.f;
-    if (tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = -INFINITY;
+    if (tid < DW) out[tid] = 0.f;
+    if (slice == 0 && tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = -INFINITY;
     return;
   }
   float l = 0.f;
@@ -1287,7 +1291,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
   }
   const float Lsum = block_reduce_n<kMergeThreads>(l, false, sm_red);
   const int g = tid / LANES, d4 = (tid - g * LANES) * 4;
-  const float* po = a.part_o + (size_t)h * D + d4;
+  const float* po = a.part_o + (size_t)h * D + slice * DW + d4;
   const size_t srow = (size_t)a.hq * D;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   int s = s0 + g;
@@ -1313,12 +1317,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
   }
   *reinterpret_cast<float4*>(&sm_o[g][d4]) = acc;
   __syncthreads();
-  if (tid < D) {
+  // combine the NG groups in two passes: every thread first sums PER groups
+  // of one dim, then DW threads sum the kMergeThreads / DW results
+  constexpr int R = kMergeThreads / DW, PER = NG / R;
+  static_assert(NG % R == 0, "merge combine");
+  {
+    const int col = tid % DW, gs = tid / DW;
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o += sm_o[gs * PER + k][col];
+    __syncthreads();
+    sm_o[gs][col] = o;
+    __syncthreads();
+  }
+  if (tid < DW) {
     float o = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < NG; ++k) o += sm_o[k][tid];
+    for (int k = 0; k < R; ++k) o += sm_o[k][tid];
     out[tid] = o / Lsum;
-    if (tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
+    if (slice == 0 && tid == 0 && a.out_lse) a.out_lse[(size_t)b * a.hq + h] = M + logf(Lsum);
   }
 }
 
@@ -1778,12 +1795,21 @@ int launch_merge(const MergeArgs& a, void* stream) {
       return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
   }
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL(merge_lse_kernel<64>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_lse_kernel<128>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
-  else
+  // fewer pairs than CUs: slice the dims (32 per workgroup)
+  const bool sliced = grid < 256;
+  if (a.head_dim == 64) {
+    if (sliced)
+      hipLaunchKernelGGL((merge_lse_kernel<64, 2>), dim3((unsigned)(grid * 2)), dim3(kMergeThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_lse_kernel<64, 1>), dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
+  } else if (a.head_dim == 128) {
+    if (sliced)
+      hipLaunchKernelGGL((merge_lse_kernel<128, 4>), dim3((unsigned)(grid * 4)), dim3(kMergeThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_lse_kernel<128, 1>), dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a);
+  } else {
     return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

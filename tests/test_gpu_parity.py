@@ -165,11 +165,13 @@ def test_split_offsets_and_partials_are_consistent(dk):
 
 # ----------------------------------------------------------------------- merge
 
-def test_merge_lse_against_oracle(dk):
+@pytest.mark.parametrize("B,hq,d", [(3, 8, 128), (3, 8, 64), (40, 8, 128)])
+def test_merge_lse_against_oracle(dk, B, hq, d):
+    # fewer than 256 (b, h) pairs: dims sliced over several workgroups per
+    # pair; 320 pairs: one workgroup per pair
     import torch
     rng = np.random.default_rng(11)
-    B, hq, d = 3, 8, 128
-    counts = [1, 5, 37]
+    counts = [1, 5, 37] + [int(c) for c in rng.integers(1, 90, size=B - 3)]
     S = sum(counts)
     po = rng.standard_normal((S, hq, d)).astype(np.float32)
     pl = (rng.standard_normal((S, hq)) * 5).astype(np.float32)
