@@ -61,7 +61,7 @@ def kernel_src_sha():
     csrc = os.path.join(ROOT, "decode_attention_host_amd", "csrc")
     k = open(os.path.join(csrc, "dkv_kernels.hip")).read()
     h_src = open(os.path.join(csrc, "dkv_internal.h")).read()
-    a = k.index("__global__ __launch_bounds__(kThreads) void attn_split_kernel")
+    a = re.search(r"__global__ __launch_bounds__\([^)]*\) void attn_split_kernel", k).start()
     a = k.rindex("template", 0, a)
     b = k.index("// ----", a)
     parts = [k[a:b]]
