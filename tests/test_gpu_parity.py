@@ -240,6 +240,24 @@ def test_paged_parity_and_equals_contiguous(dk, lens, hq, hkv, d, frac):
     cache.free(); c2.free()
 
 
+@pytest.mark.parametrize("page,d", [(1, 128), (8, 128), (32, 128), (256, 128), (8, 64), (32, 64)])
+def test_paged_page_sizes(dk, page, d):
+    # pages shorter than a chunk's rows (16 at D = 128, 32 at D = 64: per-lane
+    # lookups) and as long or longer (workgroup-uniform scalar lookups),
+    # ragged lengths over both tiers
+    lens = [1, 255, 700, 1301]
+    hq, hkv = 16, 4
+    ks, vs = _raw(23, lens, hkv, d)
+    qb = _q(23, len(lens), hq, d)
+    pt, nh, nd = paged_table(5 + page, lens, page, 0.6)
+    from decode_attention_host_amd.cache_build import paged_cache
+    cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, 5e5, page=page)
+    o, lse, _ = _run_decode(dk, cache, qb, lens, 0.0, 5e5)
+    o_ref, l_ref = _oracle(qb, ks, vs, lens, 5e5)
+    _assert_close(o, lse, o_ref, l_ref)
+    cache.free()
+
+
 # ----------------------------------------------------------------------- append indexing
 
 def _pool_bits(cache, tier, which):
