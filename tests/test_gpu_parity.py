@@ -85,6 +85,9 @@ CASES = [
     ([4096], 32, 8, 128, 0.0, 5e5),              # HBM only
     ([4096], 32, 8, 128, 1.0, 5e5),              # host only
     ([5000, 63, 64], 16, 4, 64, 0.9, 1e4),
+    ([3000, 10], 16, 2, 64, 0.4, 1e4),           # g = 8, D = 64
+    ([1500], 8, 8, 64, 0.6, 1e4),                # MHA, D = 64
+    ([2500, 700], 16, 8, 128, 0.2, 5e5),         # g = 2, D = 128
 ]
 
 
