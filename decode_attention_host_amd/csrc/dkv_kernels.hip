@@ -1607,18 +1607,30 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   const int col0 = blockIdx.x * kProjCols;
   const int ks = blockIdx.y;            // hidden slice
   const int k0 = ks * kProjK;
-  // ---- stage W[k0 .. k0+kProjK)[col0 .. col0+64) transposed
-  for (int c = tid; c < kProjK * (kProjCols / 8); c += kThreads) {
+  // ---- stage W[k0 .. k0+kProjK)[col0 .. col0+64) transposed; every load of
+  // the thread is issued before the first is used (one round trip, not one
+  // per load)
+  constexpr int WPT = kProjK * (kProjCols / 8) / kThreads;  // 16-byte loads per thread
+  static_assert(WPT * kThreads == kProjK * (kProjCols / 8), "staging split");
+  u32x4 w[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int c = tid + i * kThreads;
     const int kr = c / (kProjCols / 8);
-    const int cc = (c - kr * (kProjCols / 8)) * 8;
-    const int gcol = col0 + cc;
+    const int gcol = col0 + (c - kr * (kProjCols / 8)) * 8;
     const uint16_t* src = (gcol < a.kv_dim) ? a.wk + (size_t)(k0 + kr) * a.kv_dim + gcol
                                             : a.wv + (size_t)(k0 + kr) * a.kv_dim + (gcol - a.kv_dim);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+    w[i] = *reinterpret_cast<const u32x4*>(src);
+  }
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int c = tid + i * kThreads;
+    const int kr = c / (kProjCols / 8);
+    const int cc = (c - kr * (kProjCols / 8)) * 8;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      wt[cc + 2 * e][kr] = (uint16_t)(w[e] & 0xffffu);
-      wt[cc + 2 * e + 1][kr] = (uint16_t)(w[e] >> 16);
+      wt[cc + 2 * e][kr] = (uint16_t)(w[i][e] & 0xffffu);
+      wt[cc + 2 * e + 1][kr] = (uint16_t)(w[i][e] >> 16);
     }
   }
   __syncthreads();
@@ -1628,11 +1640,15 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
     floatx4 c = {0.f, 0.f, 0.f, 0.f};
     const int row = m0 + n;
     const bool rv = row < a.n_new;
+    // x rows past n_new read row 0 and are zeroed when used
     const uint16_t* xr = a.x + (size_t)(rv ? row : 0) * a.hidden + k0 + j4 * 8;
-#pragma unroll 4
-    for (int kk = 0; kk < kProjK; kk += 32) {
-      u32x4 av = rv ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(&wt[ctile + n][kk + j4 * 8]);
+    u32x4 xv[kProjK / 32];
+#pragma unroll
+    for (int s = 0; s < kProjK / 32; ++s) xv[s] = *reinterpret_cast<const u32x4*>(xr + s * 32);
+#pragma unroll
+    for (int s = 0; s < kProjK / 32; ++s) {
+      const u32x4 av = rv ? xv[s] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(&wt[ctile + n][s * 32 + j4 * 8]);
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                   __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
     }
@@ -1654,6 +1670,9 @@ __global__ __launch_bounds__(kThreads) void proj_reduce_kernel(ProjArgs a) {
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(idx / ncols), c = (int)(idx - (int64_t)r * ncols);
     float s = 0.f;
+    // unrolled so that several slices' loads are in flight; sums stay in
+    // slice order
+#pragma unroll 8
     for (int k = 0; k < a.ksplit; ++k) s += a.partial[((size_t)k * a.n_pad + r) * ncols + c];
     a.out[idx] = s;
   }
