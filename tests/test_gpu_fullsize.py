@@ -88,6 +88,14 @@ def test_llama3_8b_1m_ratios_sampled_heads(dk):
         _check(o[0, heads], lse[0, heads], ro, rl, f"llama3_8b_1m r={r}")
     host_full.free()
     dev_full.free()
+    # the same tokens in permuted 16-token pages, all in HBM: the long HBM
+    # range takes the planner's guided tail on the paged path
+    from decode_attention_host_amd.cache_build import paged_cache
+    pt, nh, nd = paged_table(1, [L], 16, 0.0)
+    paged = paged_cache(hkv, d, [L], pt, nh, nd, ks, vs, th)
+    o, lse = _decode(dk, paged, qb, [L], 0.0, th)
+    _check(o[0, heads], lse[0, heads], ro, rl, "llama3_8b_1m paged, HBM")
+    paged.free()
 
 
 def test_fused_ragged_full_sampled_sequences(dk):
