@@ -198,6 +198,54 @@ def timed_loop(step, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def flushed_steps(dk, step, iters, flush):
+    """Per-step times of `iters` steps with a read-only cache flush between
+    them, and the library's per-kernel timing over the same steps."""
+    import torch
+    gpu_warm(step, 0.3)
+    dk.kernel_timing(True)
+    for k in dk.api.KERNELS:
+        dk.kernel_timing_read(k)
+    # steps back to back with a flush between them; the host runs ahead, so
+    # each event pair brackets GPU work only
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    sink = torch.empty(iters, dtype=torch.float32, device="cuda")
+    for i in range(iters):
+        torch.sum(flush, dim=0, out=sink[i])
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev]
+    kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
+    dk.kernel_timing(False)
+    return times, kt
+
+
+def paged_hbm_point(dk, cfg, w, iters, contiguous_ms):
+    """The same tokens in a paged cache of permuted 16-token pages, all in HBM."""
+    import torch
+    from decode_attention_host_amd.cache_build import paged_cache
+    from synth import paged_table
+    L, hq, hkv, d = cfg["lens"][0], cfg["hq"], cfg["hkv"], cfg["d"]
+    pt, nh, nd = paged_table(1, [L], 16, 0.0)
+    cache = paged_cache(hkv, d, [L], pt, nh, nd, w["ks"], w["vs"], cfg["theta"])
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    bufs = dk.alloc_decode_buffers(cache, 1, hq, [L], 0.0)
+    times, kt = flushed_steps(dk, make_step(dk, cfg, w, cache, 0.0, bufs), iters, flush)
+    med = statistics.median(times)
+    db = L * hkv * d * 2 * 2
+    out = {"page": 16, "pages": "permuted, all in HBM", "ms_median": round(med, 4),
+           "eff_gbs": round(db / (med * 1e6), 2),
+           "kernel_ms": {k: round(v[1] / max(1, v[0]), 5) for k, v in kt.items()},
+           "vs_contiguous": round(contiguous_ms / med, 3) if contiguous_ms else None}
+    log(f"[bench] paged HBM: {med:.3f} ms ({out['vs_contiguous']} of the contiguous speed)")
+    del flush
+    cache.free()
+    return out
+
+
 def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
     """Per-ratio latency from full host and device copies of the same cache."""
     import torch
@@ -218,24 +266,7 @@ def ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d):
         nh = view.n_host
         bufs = dk.alloc_decode_buffers(view, 1, hq, [L], r)
         step = make_step(dk, cfg, w, view, r, bufs)
-        gpu_warm(step, 0.3)
-        dk.kernel_timing(True)
-        for k in dk.api.KERNELS:
-            dk.kernel_timing_read(k)
-        # steps back to back with a flush between them; the host runs ahead, so
-        # each event pair brackets GPU work only
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(iters)]
-        sink = torch.empty(iters, dtype=torch.float32, device="cuda")
-        for i in range(iters):
-            torch.sum(flush, dim=0, out=sink[i])
-            ev[i][0].record()
-            step()
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        times = [a.elapsed_time(b) for a, b in ev]
-        kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
-        dk.kernel_timing(False)
+        times, kt = flushed_steps(dk, step, iters, flush)
         med = statistics.median(times)
         hb, db = nh * row, (L - nh) * row
         t_star = max(hb / (bw_h * 1e6), db / (bw_d * 1e6))
@@ -420,8 +451,9 @@ def measure_long_sweep(dk, cfg, seed, flags, iters, bw_h, bw_d):
     r_star = bw_h / (bw_h + bw_d)
     ratios = [0.0, r_star, 0.25, 0.5, 0.75, 0.9, 1.0]
     out = ratio_sweep(dk, cfg, w, ratios, iters, bw_h, bw_d)
+    paged = paged_hbm_point(dk, cfg, w, iters, next((x["ms_median"] for x in out if x["ratio"] == 0.0), None))
     host_full.free()
-    return {"sweep": out, "best_split": best_split(out, bw_h, bw_d)}
+    return {"sweep": out, "best_split": best_split(out, bw_h, bw_d), "paged_hbm": paged}
 
 
 def measure_prefill(dk, cfg, seed, flags, steps, warmup):
