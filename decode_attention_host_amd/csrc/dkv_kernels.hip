@@ -596,7 +596,6 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
   constexpr int HT = PT / 64;                  // 64-key halves per tile
   constexpr int MT = PT / 16;                  // 16-key blocks per tile
   constexpr int KT = PT / 32;                  // 32-key k-steps of P.V per tile
-  constexpr int QB = kPrefillRows / G;
   constexpr int KS = D / 32;                   // k-steps of Q.K over the head dim
   constexpr int DT = D / 16;                   // 16-row d tiles of O^T
   // Row pitches padded by 32 bytes: the MFMA operand reads (16 rows x 16 B at
