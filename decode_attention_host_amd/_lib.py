@@ -8,7 +8,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdkv.so")
+# DKV_LIB names another build of the same library (e.g. the host-sanitizer
+# build); the binding still raises if that file is missing.
+LIB_PATH = os.environ.get("DKV_LIB") or os.path.join(HERE, "libdkv.so")
 
 DKV_OK = 0
 DKV_ERR_INVALID = 1

@@ -40,9 +40,19 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libdkv.so; returns its path."""
+# Host-only sanitizer build: the C++ runtime (planner, pager, argument checks)
+# compiled by g++ with AddressSanitizer and UBSan; the kernels as usual.
+SAN_LIB = os.path.join(HERE, "libdkv_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined"]
+
+
+def build(verbose: bool = False, host_sanitize: bool = False) -> str:
+    """Compile every source and link libdkv.so; returns its path.  With
+    host_sanitize the host C++ is built with AddressSanitizer and UBSan into
+    libdkv_san.so instead (load it with DKV_LIB and the sanitizer runtimes
+    preloaded; CPU tests only)."""
     tmp = tempfile.mkdtemp(prefix="dkv_build_")
+    lib = SAN_LIB if host_sanitize else LIB
     try:
         objs = []
         for src in SOURCES:
@@ -50,6 +60,9 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmp, src + ".o")
             if src.endswith(".hip"):
                 cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
+            elif host_sanitize:
+                cmd = ["g++", "-fPIC", "-std=c++17", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}", *SAN_FLAGS,
+                       "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
             else:
                 cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
             if verbose:
@@ -58,15 +71,17 @@ def build(verbose: bool = False) -> str:
             objs.append(obj)
         out_tmp = os.path.join(tmp, "libdkv.so")
         cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp]
+        if host_sanitize:
+            cmd.insert(4, "-fsanitize=address,undefined")
         if verbose:
             print(" ".join(cmd), flush=True)
         _run(cmd)
-        shutil.move(out_tmp, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
+        shutil.move(out_tmp, lib + ".tmp")
+        os.replace(lib + ".tmp", lib)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, host_sanitize="--host-sanitize" in sys.argv[1:]))
