@@ -17,7 +17,6 @@ from .dkv_oracle import (  # noqa: F401
     rope_inv_freq,
     rope_neox,
     project,
-    softmax_weights,
     attention,
     attention_subset,
     merge_lse,

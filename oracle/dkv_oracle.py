@@ -99,14 +99,6 @@ def project(x, w) -> np.ndarray:
 
 # ---------------------------------------------------------------- attention
 
-def softmax_weights(q_h, k_h, scale: float):
-    """Scores s_t = scale * q . k_t and weights e^(s_t - m) / Z for one head."""
-    s = scale * (np.asarray(k_h, dtype=np.float64) @ np.asarray(q_h, dtype=np.float64))
-    m = s.max()
-    e = np.exp(s - m)
-    return e / e.sum(), s
-
-
 def attention(q_rot, k, v, scale: float):
     """Softmax attention of every query head over all N tokens.
 

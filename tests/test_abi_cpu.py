@@ -209,7 +209,8 @@ def _check_contig_cover(items, offs, lens, ratio, hs, ds):
 @pytest.mark.parametrize("ratio", [0.0, 0.25, 0.5, 0.9, 1.0])
 def test_planner_contiguous_coverage(L, ratio):
     lens = [1, 63, 64, 65, 1000, 4097]
-    hs = ds = 8192
+    # unequal strides: a host/device stride swap in the planner moves rows
+    hs, ds = 8192, 4099
     x = desc(hkv=2, d=64, host_rows=len(lens) * hs, dev_rows=len(lens) * ds, hs=hs, ds=ds)
     items, _, offs, info = inspect(L, x, len(lens), 8, lens, ratio, cus=8)
     _check_contig_cover(items, offs, lens, ratio, hs, ds)

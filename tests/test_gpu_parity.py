@@ -316,7 +316,8 @@ def test_append_writes_only_target_rows_contiguous(dk):
     import torch
     hkv, d, theta, ratio = 2, 64, 1e4, 0.5
     lens = [10, 7]
-    hs, ds = 8, 8
+    # unequal strides: a host/device stride swap in the slot rule moves rows
+    hs, ds = 8, 13
     cache = dk.KVCache(hkv, d, host_rows=2 * hs, dev_rows=2 * ds, host_stride=hs, dev_stride=ds)
     cache.host_view("k")[...] = 0x1111
     cache.host_view("v")[...] = 0x2222

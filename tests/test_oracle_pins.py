@@ -166,12 +166,6 @@ def test_attention_golden(golden):
         np.testing.assert_allclose(lse, c["lse"], atol=1e-13, err_msg=c["why"])
 
 
-def test_softmax_weights_sum_to_one():
-    rng = np.random.default_rng(9)
-    w, s = O.softmax_weights(rng.standard_normal(64), rng.standard_normal((300, 64)), 0.125)
-    assert abs(w.sum() - 1.0) < 1e-14 and np.all(w > 0)
-
-
 def test_single_token_returns_v0_exactly():
     rng = np.random.default_rng(10)
     q = rng.standard_normal((4, 64)); k = rng.standard_normal((1, 2, 64)); v = rng.standard_normal((1, 2, 64))
@@ -304,19 +298,32 @@ def test_paged_slot_golden(golden):
 
 
 def test_contig_slots_are_injective_and_cover():
+    # unequal strides (host 16, device 21 rows per sequence) so that a swap of
+    # the two strides, or of the tiers they belong to, changes the rows
     lens = [5, 1, 9, 16]
+    hs, ds = 16, 21
     for r in (0.0, 0.3, 0.5, 1.0):
         seen = set()
         for b, L in enumerate(lens):
             nh = O.contig_split_point(r, L)
             for t in range(L):
-                tier, row = O.contig_slot(b, t, L, r, 16, 16)
+                tier, row = O.contig_slot(b, t, L, r, hs, ds)
                 # brute-force statement of the layout
                 assert tier == (1 if t < nh else 0)
-                assert row == (b * 16 + t if tier else b * 16 + t - nh)
+                assert row == (b * hs + t if tier else b * ds + t - nh)
                 assert (tier, row) not in seen
                 seen.add((tier, row))
         assert len(seen) == sum(lens)
+
+
+def test_contig_slot_golden_unequal_strides():
+    # sequence 2 of a cache with 10 host rows and 7 device rows per sequence,
+    # L = 10, r = 0.7 (7 host tokens, see the split-point golden case):
+    # token 6 is host row 2*10 + 6 = 26; token 7 is the first device token,
+    # device row 2*7 + 0 = 14; token 9 is device row 2*7 + 2 = 16
+    assert O.contig_slot(2, 6, 10, 0.7, 10, 7) == (1, 26)
+    assert O.contig_slot(2, 7, 10, 0.7, 10, 7) == (0, 14)
+    assert O.contig_slot(2, 9, 10, 0.7, 10, 7) == (0, 16)
 
 
 def test_paged_table_slots_injective_and_ratio():
@@ -377,6 +384,32 @@ def test_decode_sequence_matches_scalar_pipeline():
     ob, lb = BR.attention_py(qr, kr, vf.tolist(), 1 / math.sqrt(D))
     np.testing.assert_allclose(o, ob, atol=1e-12)
     np.testing.assert_allclose(lse, lb, atol=1e-12)
+
+
+def test_decode_batch_matches_scalar_pipeline_per_sequence():
+    # a ragged batch (1, 3 and 6 cached tokens) with each query at its own
+    # position: every sequence is re-stated with the scalar twin (keys rotated
+    # at their positions and rounded to bf16, query rotated at q_pos[b]); a
+    # mix-up of sequences, lengths or positions fails
+    Hq, Hkv, D, theta, scale = 4, 2, 8, 1e4, 0.3
+    lens = [1, 3, 6]
+    qpos = [0, 2, 5]
+    qb = normal_bf16(41, 1, (len(lens), Hq, D))
+    caches = [(normal_bf16(41 + b, 2, (L, Hkv, D)), normal_bf16(41 + b, 3, (L, Hkv, D)))
+              for b, L in enumerate(lens)]
+    o, lse = O.decode_batch(qb, caches, qpos, theta, scale)
+    assert o.shape == (3, Hq, D) and lse.shape == (3, Hq)
+    for b, (kb, vb) in enumerate(caches):
+        kf = O.bf16_to_f64(kb); vf = O.bf16_to_f64(vb); qf = O.bf16_to_f64(qb[b])
+        kr = [[list(O.bf16_to_f64(O.bf16_rne_bits(np.array(BR.rope_neox_py(list(kf[t, j]), t, theta)))))
+               for j in range(Hkv)] for t in range(lens[b])]
+        qr = [BR.rope_neox_py(list(qf[h]), qpos[b], theta) for h in range(Hq)]
+        ob, lb = BR.attention_py(qr, kr, vf.tolist(), scale)
+        np.testing.assert_allclose(o[b], ob, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lb, atol=1e-12)
+    # the single-token sequence returns its value exactly
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], O.bf16_to_f64(caches[0][1][0, h // 2]))
 
 
 def test_decode_shift_invariance_without_rounding():

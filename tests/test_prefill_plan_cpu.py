@@ -112,7 +112,7 @@ def _stage_map(plan):
 @pytest.mark.parametrize("fused", [False, True])
 def test_prefill_plan_contiguous(L, hq, hkv, d, ratio, stage, fused):
     lens, news = [64, 377, 33, 1000, 200], [64, 77, 1, 130, 200]
-    hs = ds = 1024
+    hs, ds = 1024, 1001  # unequal: a host/device stride swap moves rows
     x = desc(hkv, d, host_rows=len(lens) * hs, dev_rows=len(lens) * ds, hs=hs, ds=ds)
     try:
         set_tuning(stage_max_mib=0 if stage else -1)
