@@ -109,7 +109,7 @@ def make_step(dk, cfg, w, cache, ratio, bufs):
     def step():
         dk.project_rope_append(cache, B, w["seq_lens_dev"], ratio, w["sidx"], w["qpos"],
                                k_new=w["k_new"], v_new=w["v_new"], rope_theta=cfg["theta"])
-        dk.decode_attn_split(cache, w["q"], w["qpos"], lens, ratio, scale, cfg["theta"], bufs=bufs)
+        dk.decode_attn_split(cache, w["q"], w["qpos"], w["seq_lens_dev"], ratio, scale, cfg["theta"], bufs=bufs)
         dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, B, hq, d, out_o=bufs.out_o,
                      out_lse=bufs.out_lse)
     return step
@@ -405,12 +405,13 @@ def measure_fused_paged(dk, cfg, seed, flags, steps, warmup):
     sidx = torch.arange(B, dtype=torch.int32, device="cuda")
     ws = torch.empty(dk.append_workspace_bytes(B, hid, hkv * d), dtype=torch.uint8, device="cuda")
     bufs = dk.alloc_decode_buffers(cache, B, hq, ntok, 0.0)
+    ntok_dev = torch.tensor(ntok, dtype=torch.int32, device="cuda")
     scale = 1.0 / math.sqrt(d)
 
     def step():
         dk.project_rope_append(cache, B, None, 0.0, sidx, pos, x=x, wk=wk, wv=wv,
                                rope_theta=cfg["theta"], workspace=ws)
-        dk.decode_attn_split(cache, q, pos, ntok, 0.0, scale, cfg["theta"], bufs=bufs)
+        dk.decode_attn_split(cache, q, pos, ntok_dev, 0.0, scale, cfg["theta"], bufs=bufs)
         dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, B, hq, d, out_o=bufs.out_o,
                      out_lse=bufs.out_lse)
 

@@ -128,6 +128,10 @@ SIGNATURES = {
                                 P, P, P]),
     "dkv_decode_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, F32, F64, P, SZ, P, P,
                                     P, I32, P]),
+    "dkv_decode_step_plan": (I32, [C.POINTER(KvDesc), I32, I32, F64, I32, C.POINTER(PlanInfo)]),
+    "dkv_decode_step": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, P, P, I32, P, P, P, P, F64, F32, F64, P, SZ,
+                              P, P, P]),
+    "dkv_decode_errors": (I32, [C.POINTER(KvDesc), P, I32, C.POINTER(I32)]),
     "dkv_linear_plan": (I32, [I32, I32, I32, F64, C.POINTER(PlanInfo)]),
     "dkv_linear_split": (I32, [P, P, I32, I32, F64, P, I32, P, P, SZ, P]),
     "dkv_linear_plan_inspect": (I32, [I32, I32, F64, I32, P, I32, C.POINTER(PlanInfo)]),
@@ -158,6 +162,7 @@ DKV_KERNEL_APPEND = 3
 DKV_KERNEL_PREFILL = 4
 DKV_KERNEL_STAGE = 5
 DKV_KERNEL_LINEAR = 6
+DKV_KERNEL_TIERS = 7
 
 _lib = None
 

@@ -272,8 +272,9 @@ def project_rope_append(cache: KVCache, batch: int, seq_lens, ratio: float, seq_
 
 
 def decode_plan(cache: KVCache, batch: int, num_q_heads: int, seq_lens, ratio: float) -> dict:
+    """dkv_decode_plan; ``seq_lens`` (host, or None) adds the items those lengths give."""
     d = cache.desc()
-    sl = _host_i32(seq_lens)
+    sl = None if seq_lens is None else _host_i32(seq_lens)
     info = PlanInfo()
     check(lib().dkv_decode_plan(C.byref(d), int(batch), int(num_q_heads), _ptr(sl), float(ratio),
                                 C.byref(info)))
@@ -324,6 +325,16 @@ def prefill_plan_inspect(cache_or_desc, batch: int, num_q_heads: int, q_start, q
             "info": info.as_dict()}
 
 
+def _dev_i32(a, device="cuda"):
+    """int32 lengths/positions on the device: a device tensor is passed through
+    (it must be int32); a host sequence is copied (convenience for tests)."""
+    if isinstance(a, torch.Tensor):
+        if a.dtype != torch.int32 or not a.is_cuda:
+            raise ValueError("expected a device int32 tensor")
+        return a.contiguous()
+    return torch.tensor(np.asarray(a, dtype=np.int32), dtype=torch.int32, device=device)
+
+
 @dataclass
 class DecodeBuffers:
     workspace: torch.Tensor
@@ -337,11 +348,15 @@ class DecodeBuffers:
 
 def alloc_decode_buffers(cache: KVCache, batch: int, num_q_heads: int, seq_lens, ratio: float,
                          device="cuda") -> DecodeBuffers:
-    info = decode_plan(cache, batch, num_q_heads, seq_lens, ratio)
+    """Buffers of the split form for this shape: partials for the split bound of
+    the shape (any lengths that fit the pools), a zero-filled workspace.
+    ``seq_lens`` (host, optional) only adds the item counts to ``info``."""
+    sl = None if seq_lens is None or isinstance(seq_lens, torch.Tensor) else seq_lens
+    info = decode_plan(cache, batch, num_q_heads, sl, ratio)
     S = max(1, info["num_splits"])
     D = cache.head_dim
     return DecodeBuffers(
-        workspace=torch.empty(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=device),
+        workspace=torch.zeros(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=device),
         part_o=torch.empty((S, num_q_heads, D), dtype=torch.float32, device=device),
         part_lse=torch.empty((S, num_q_heads), dtype=torch.float32, device=device),
         split_offsets=torch.empty(batch + 1, dtype=torch.int32, device=device),
@@ -354,12 +369,13 @@ def alloc_decode_buffers(cache: KVCache, batch: int, num_q_heads: int, seq_lens,
 def decode_attn_split(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_lens, ratio: float,
                       scale: float, rope_theta: float, *, bufs: DecodeBuffers | None = None,
                       stream=None) -> DecodeBuffers:
-    """dkv_decode_attn_split.  q [B,Hq,D] bf16 and q_pos [B] int32 on the device;
-    seq_lens on the host.  Returns the buffers holding part_o/part_lse/split_offsets."""
+    """dkv_decode_attn_split.  q [B,Hq,D] bf16, q_pos [B] and seq_lens [B] int32
+    on the device (a host list of lengths is copied).  Returns the buffers
+    holding part_o/part_lse/split_offsets."""
     B, Hq, D = q.shape
-    sl = _host_i32(seq_lens)
     if bufs is None:
-        bufs = alloc_decode_buffers(cache, B, Hq, sl, ratio, q.device)
+        bufs = alloc_decode_buffers(cache, B, Hq, seq_lens, ratio, q.device)
+    sl = _dev_i32(seq_lens, q.device)
     d = cache.desc()
     check(lib().dkv_decode_attn_split(
         C.byref(d), int(B), int(Hq), _ptr(q), _ptr(q_pos), _ptr(sl), float(ratio), float(scale),
@@ -392,6 +408,53 @@ def decode(cache: KVCache, q, q_pos, seq_lens, ratio, scale, rope_theta, *, bufs
     return bufs.out_o, bufs.out_lse, bufs
 
 
+def decode_step_plan(cache: KVCache, batch: int, num_q_heads: int, ratio: float, hidden: int = 0) -> dict:
+    """dkv_decode_step_plan."""
+    d = cache.desc()
+    info = PlanInfo()
+    check(lib().dkv_decode_step_plan(C.byref(d), int(batch), int(num_q_heads), float(ratio), int(hidden),
+                                     C.byref(info)))
+    return info.as_dict()
+
+
+def decode_step_workspace(cache: KVCache, batch: int, num_q_heads: int, ratio: float, hidden: int = 0,
+                          device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for dkv_decode_step (every call leaves it zeroed)."""
+    info = decode_step_plan(cache, batch, num_q_heads, ratio, hidden)
+    return torch.zeros(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=device)
+
+
+def decode_step(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_lens: torch.Tensor, ratio: float,
+                scale: float, rope_theta: float, *, pos_new=None, k_new=None, v_new=None, x=None, wk=None,
+                wv=None, workspace: torch.Tensor | None = None, out_o=None, out_lse=None, stream=None):
+    """dkv_decode_step: append each sequence's new token (k_new/v_new [B,Hkv,D]
+    bf16, or x [B,hidden] with wk/wv) at pos_new (default seq_lens), attend over
+    seq_lens + 1 tokens and merge, in one launch.  Returns (o [B,Hq,D], lse [B,Hq])."""
+    B, Hq, D = q.shape
+    hidden = int(x.shape[1]) if x is not None else 0
+    sl = _dev_i32(seq_lens, q.device)
+    if workspace is None:
+        workspace = decode_step_workspace(cache, B, Hq, ratio, hidden, q.device)
+    if out_o is None:
+        out_o = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    d = cache.desc()
+    check(lib().dkv_decode_step(
+        C.byref(d), int(B), int(Hq), _ptr(q), _ptr(q_pos), _ptr(sl), _ptr(pos_new), _ptr(x), hidden, _ptr(wk),
+        _ptr(wv), _ptr(k_new), _ptr(v_new), float(ratio), float(scale), float(rope_theta), _ptr(workspace),
+        workspace.numel(), _ptr(out_o), _ptr(out_lse), _stream(stream)))
+    return out_o, out_lse
+
+
+def decode_errors(cache: KVCache, workspace: torch.Tensor, clear: bool = True) -> int:
+    """dkv_decode_errors: layout error flags the decode kernels left in ``workspace``."""
+    d = cache.desc()
+    f = C.c_int32()
+    check(lib().dkv_decode_errors(C.byref(d), _ptr(workspace), int(bool(clear)), C.byref(f)))
+    return f.value
+
+
 def set_tuning(**kw):
     t = Tuning()
     for k, v in kw.items():
@@ -420,7 +483,7 @@ def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True
 KERNELS = {"attn": _lib.DKV_KERNEL_ATTN, "rope_q": _lib.DKV_KERNEL_ROPE_Q,
            "merge": _lib.DKV_KERNEL_MERGE, "append": _lib.DKV_KERNEL_APPEND,
            "prefill": _lib.DKV_KERNEL_PREFILL, "stage": _lib.DKV_KERNEL_STAGE,
-           "linear": _lib.DKV_KERNEL_LINEAR}
+           "linear": _lib.DKV_KERNEL_LINEAR, "tiers": _lib.DKV_KERNEL_TIERS}
 
 
 def kernel_timing(enable: bool):

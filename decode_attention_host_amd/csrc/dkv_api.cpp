@@ -167,69 +167,6 @@ dkv_status validate_ratio(double r) {
 std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e);
 std::shared_ptr<PlanEntry> cache_find(const std::string& key);
 
-// Builds or fetches the plan for a decode call.
-dkv_status get_plan(const dkv_kv_desc* kv, int32_t batch, int32_t hq, const int32_t* seq_lens,
-                    double ratio, std::shared_ptr<PlanEntry>* out) {
-  if (batch < 1) return set_err(DKV_ERR_INVALID, "batch must be >= 1");
-  if (!seq_lens) return set_err(DKV_ERR_INVALID, "seq_lens is NULL");
-  if (hq < 1 || hq % kv->num_kv_heads)
-    return set_err(DKV_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
-                   hq, kv->num_kv_heads);
-  const int g = hq / kv->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8)
-    return set_err(DKV_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", g);
-  if (kv->page_size > 0 && !kv->page_table_host)
-    return set_err(DKV_ERR_INVALID, "paged layout needs page_table_host to plan");
-  uint64_t gen = 0;
-  const dkv_tuning t = tuning_snapshot(&gen);
-  int dev = 0;
-  int cus = t.num_cus;
-  if (cus <= 0) {
-    cus = device_cus(&dev);
-    if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
-  }
-  std::string key;
-  key.reserve(128 + 4 * batch);
-  put(key, dev); put(key, cus); put(key, gen); put(key, batch); put(key, hq);
-  put(key, kv->num_kv_heads); put(key, kv->head_dim); put(key, kv->page_size); put(key, kv->max_pages);
-  put(key, kv->host_stride); put(key, kv->dev_stride); put(key, kv->host_rows); put(key, kv->dev_rows);
-  put(key, ratio);
-  key.append(reinterpret_cast<const char*>(seq_lens), sizeof(int32_t) * (size_t)batch);
-  if (kv->page_size > 0) {
-    uint64_t h = 1469598103934665603ull;
-    for (int b = 0; b < batch; ++b) {
-      const int64_t L = std::max(0, seq_lens[b]);
-      const int64_t npg = std::min<int64_t>((L + kv->page_size - 1) / kv->page_size, kv->max_pages);
-      h = fnv1a(kv->page_table_host + (int64_t)b * kv->max_pages, sizeof(int32_t) * npg, h);
-    }
-    put(key, h);
-  }
-  if (auto hit = cache_find(key)) {
-    *out = hit;
-    return DKV_OK;
-  }
-  dkv::PlanInput in{};
-  in.batch = batch; in.hq = hq; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
-  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
-  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
-  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
-  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host; in.ratio = ratio;
-  in.num_cus = cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
-  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
-  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
-  auto e = std::make_shared<PlanEntry>();
-  std::vector<uint8_t> blob;
-  std::string err;
-  if (!dkv::build_plan(in, &e->lay, &blob, &err)) return set_err(DKV_ERR_INVALID, "%s", err.c_str());
-  e->bytes = blob.size();
-  hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
-  if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
-  memcpy(e->pinned, blob.data(), e->bytes);
-  *out = cache_insert(key, e);
-  return DKV_OK;
-}
-
-
 // Stores a freshly built plan in the cache (or returns the entry another
 // thread stored first) and evicts unreferenced old entries.
 std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e) {
@@ -401,7 +338,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> pool;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[7];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[8];
 };
 
 Timing& timing() {
@@ -501,6 +438,172 @@ size_t linear_ws_bytes(const dkv::PlanLayout& L) {
   return L.blob_bytes + (size_t)L.num_splits * dkv::kLinMaxTokens * dkv::kLinRows * 4;
 }
 
+// ---------------------------------------------------------------- decode shape
+//
+// A decode call has no host plan: the launch shape (workgroups per tier and KV
+// head, item-length rules) follows from its arguments, and the kernel derives
+// the items from the lengths in device memory.  The workspace holds the item
+// queues and counters (zero between calls: every call leaves them zeroed),
+// the paged layout's tier lists, and the fused form's run partials.
+struct DecodeShape {
+  dkv::DecodeTemplate t{};
+  int32_t g = 0;
+  int32_t max_slots = 0;
+  int64_t max_splits = 0;
+  size_t counters_off = 0, group_off = 0, tiers_off = 0, lists_off = 0, run_o_off = 0, run_lse_off = 0,
+         proj_off = 0, total = 0;
+};
+
+dkv::PlanInput decode_input(const dkv_kv_desc* kv, int32_t batch, int32_t hq, double ratio, int32_t cus,
+                            const dkv_tuning& t) {
+  dkv::PlanInput in{};
+  in.batch = batch; in.hq = hq; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
+  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
+  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
+  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
+  in.page_table_host = kv->page_table_host; in.ratio = ratio;
+  in.num_cus = cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
+  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
+  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
+  return in;
+}
+
+dkv_status decode_shape(const dkv_kv_desc* kv, int32_t batch, int32_t hq, double ratio, bool fused, int32_t hidden,
+                        int32_t num_cus, DecodeShape* out) {
+  if (batch < 1 || batch > dkv::kDecodeMaxBatch)
+    return set_err(DKV_ERR_UNSUPPORTED, "batch %d outside 1..%d", batch, dkv::kDecodeMaxBatch);
+  if (hq < 1 || hq % kv->num_kv_heads)
+    return set_err(DKV_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d", hq,
+                   kv->num_kv_heads);
+  const int g = hq / kv->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return set_err(DKV_ERR_UNSUPPORTED, "query group size %d not built (1, 2, 4, 8)", g);
+  if (kv->page_size == 0 && validate_ratio(ratio) != DKV_OK) return DKV_ERR_INVALID;
+  const dkv_tuning tu = tuning_snapshot(nullptr);
+  int cus = num_cus > 0 ? num_cus : tu.num_cus;
+  if (cus <= 0) {
+    cus = device_cus(nullptr);
+    if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
+  }
+  const bool paged = kv->page_size > 0;
+  const bool host_tier = kv->host_rows > 0 && (paged || ratio > 0.0);
+  const bool dev_tier = kv->dev_rows > 0 && (paged || ratio < 1.0);
+  if (!host_tier && !dev_tier) return set_err(DKV_ERR_INVALID, "no tier can hold tokens (pool rows and ratio)");
+  const double frac = paged ? (double)kv->host_rows / (double)(kv->host_rows + kv->dev_rows) : ratio;
+  DecodeShape d;
+  d.t = dkv::decode_template(decode_input(kv, batch, hq, ratio, cus, tu), host_tier, dev_tier, frac);
+  d.g = g;
+  d.max_slots = d.t.team_h + 2 * d.t.team_d + 1;
+  d.max_splits = dkv::decode_max_splits(d.t, batch, kv->host_rows, kv->dev_rows);
+  auto up = [](size_t a) { return (a + 255) / 256 * 256; };
+  const size_t hkv = (size_t)kv->num_kv_heads, D = (size_t)kv->head_dim, B = (size_t)batch;
+  d.counters_off = 0;
+  d.group_off = up((2 * hkv + 2) * 4);
+  d.tiers_off = up(d.group_off + (fused ? B * hkv * 2 * 4 : 0));
+  d.lists_off = up(d.tiers_off + (paged ? B * 4 * 4 : 0));
+  d.run_o_off = up(d.lists_off + (paged ? 2 * B * (size_t)kv->max_pages * 4 : 0));
+  d.run_lse_off = up(d.run_o_off + (fused ? B * hkv * d.max_slots * g * D * 4 : 0));
+  d.proj_off = up(d.run_lse_off + (fused ? B * hkv * d.max_slots * g * 4 : 0));
+  d.total = d.proj_off +
+            (fused && hidden > 0 ? dkv_append_workspace_bytes(batch, hidden, kv->num_kv_heads * kv->head_dim) : 0);
+  *out = d;
+  return DKV_OK;
+}
+
+dkv::DecodeArgs decode_args(const dkv_kv_desc* kv, const DecodeShape& d, int32_t batch, int32_t hq, const void* q,
+                            const int32_t* q_pos, const int32_t* seq_lens, double ratio, float scale,
+                            double rope_theta, void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  dkv::DecodeArgs a{};
+  a.host_k = static_cast<uint16_t*>(kv->host_k);
+  a.host_v = static_cast<uint16_t*>(kv->host_v);
+  a.dev_k = static_cast<uint16_t*>(kv->dev_k);
+  a.dev_v = static_cast<uint16_t*>(kv->dev_v);
+  a.host_rows = kv->host_rows;
+  a.dev_rows = kv->dev_rows;
+  a.host_stride = kv->host_stride;
+  a.dev_stride = kv->dev_stride;
+  a.page_table = kv->page_size > 0 ? kv->page_table : nullptr;
+  a.max_pages = kv->max_pages;
+  a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : -1;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_pos = q_pos;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = kv->num_kv_heads;
+  a.head_dim = kv->head_dim;
+  a.ratio = kv->page_size > 0 ? 0.0 : ratio;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  a.tmpl = d.t;
+  a.counters = reinterpret_cast<int32_t*>(ws + d.counters_off);
+  a.group_cnt = reinterpret_cast<int32_t*>(ws + d.group_off);
+  a.tier_counts = reinterpret_cast<const int32_t*>(ws + d.tiers_off);
+  a.tier_pages = reinterpret_cast<const int32_t*>(ws + d.lists_off);
+  a.run_o = reinterpret_cast<float*>(ws + d.run_o_off);
+  a.run_lse = reinterpret_cast<float*>(ws + d.run_lse_off);
+  a.max_slots = d.max_slots;
+  a.freq = rope_freq(rope_theta, kv->head_dim);
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  a.wg_trace = g_trace_buf;
+  a.wg_trace_cap = g_trace_cap;
+  return a;
+}
+
+// DKV_DEBUG_VALIDATE: the lengths (and the page table) read back and checked
+// against the layout before anything is launched.
+dkv_status decode_debug_check(const dkv_kv_desc* kv, int32_t batch, const int32_t* seq_lens, double ratio,
+                              int new_tokens, hipStream_t s) {
+  std::vector<int32_t> sl(batch);
+  hipError_t he = hipStreamSynchronize(s);
+  if (he == hipSuccess) he = hipMemcpy(sl.data(), seq_lens, 4 * (size_t)batch, hipMemcpyDeviceToHost);
+  if (he != hipSuccess) return hip_err(he, "debug copy of seq_lens");
+  std::vector<int32_t> pt;
+  if (kv->page_size > 0) {
+    pt.resize((size_t)batch * kv->max_pages);
+    he = hipMemcpy(pt.data(), kv->page_table, pt.size() * 4, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_err(he, "debug copy of page_table");
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = sl[b];
+    if (L < 0) return set_err(DKV_ERR_INVALID, "seq_lens[%d] = %lld is negative", b, (long long)L);
+    const int64_t placed = L + new_tokens;
+    if (kv->page_size == 0) {
+      int64_t nh, nd, ph;
+      dkv::contig_tiers(ratio, L, placed, &nh, &nd, &ph);
+      if (ph > 0 && (ph > kv->host_stride || (int64_t)b * kv->host_stride + ph > kv->host_rows))
+        return set_err(DKV_ERR_INVALID, "sequence %d: host rows needed beyond host_stride/host_rows", b);
+      if (placed - ph > 0 &&
+          (placed - ph > kv->dev_stride || (int64_t)b * kv->dev_stride + (placed - ph) > kv->dev_rows))
+        return set_err(DKV_ERR_INVALID, "sequence %d: device rows needed beyond dev_stride/dev_rows", b);
+    } else {
+      const int64_t npg = (placed + kv->page_size - 1) / kv->page_size;
+      if (npg > kv->max_pages) return set_err(DKV_ERR_INVALID, "sequence %d needs %lld pages > max_pages", b,
+                                              (long long)npg);
+      for (int64_t j = 0; j < npg; ++j) {
+        const int32_t e = pt[(size_t)b * kv->max_pages + j];
+        const bool host = (e & 1) != 0;
+        if (e < 0 || ((int64_t)(e >> 1) + 1) * kv->page_size > (host ? kv->host_rows : kv->dev_rows))
+          return set_err(DKV_ERR_INVALID, "page_table[%d][%lld] = %d: unmapped or beyond its pool", b,
+                         (long long)j, e);
+      }
+    }
+  }
+  return DKV_OK;
+}
+
+dkv_status validate_decode_common(const dkv_kv_desc* kv, const void* q, const int32_t* q_pos,
+                                  const int32_t* seq_lens, float scale, double rope_theta, const void* workspace) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (!q || !q_pos || !seq_lens || !workspace)
+    return set_err(DKV_ERR_INVALID, "q, q_pos, seq_lens and workspace are required");
+  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
+    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  return DKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,21 +648,26 @@ dkv_status dkv_decode_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_h
   if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
   dkv_status st = validate_desc(kv);
   if (st != DKV_OK) return st;
-  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
-  std::shared_ptr<PlanEntry> e;
-  st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  DecodeShape d;
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, false, 0, 0, &d);
   if (st != DKV_OK) return st;
-  const dkv::PlanLayout& L = e->lay;
-  info->workspace_bytes = (int64_t)L.blob_bytes;
-  info->num_splits = L.num_splits;
-  info->host_items = L.n_host_items;
-  info->dev_items = L.n_dev_items;
-  info->host_wgs = L.host_wgs;
-  info->dev_wgs = L.dev_wgs;
-  info->host_chunk = L.host_chunk;
-  info->dev_chunk = L.dev_chunk;
-  info->host_bytes = L.host_bytes;
-  info->dev_bytes = L.dev_bytes;
+  *info = dkv_plan_info{};
+  info->workspace_bytes = (int64_t)d.total;
+  info->num_splits = (int32_t)std::min<int64_t>(d.max_splits, INT32_MAX);
+  info->host_wgs = d.t.team_h * kv->num_kv_heads;
+  info->dev_wgs = d.t.team_d * kv->num_kv_heads;
+  if (seq_lens) {
+    dkv_plan_info exact{};
+    st = dkv_plan_inspect(kv, batch, num_q_heads, seq_lens, offload_ratio, 0, nullptr, 0, nullptr, 0, nullptr,
+                          &exact);
+    if (st != DKV_OK) return st;
+    info->host_items = exact.host_items;
+    info->dev_items = exact.dev_items;
+    info->host_chunk = exact.host_chunk;
+    info->dev_chunk = exact.dev_chunk;
+    info->host_bytes = exact.host_bytes;
+    info->dev_bytes = exact.dev_bytes;
+  }
   return ok();
 }
 
@@ -569,43 +677,76 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
                             int32_t page_cap, int32_t* split_offsets, dkv_plan_info* info) {
   dkv_status st = validate_desc(kv);
   if (st != DKV_OK) return st;
-  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
-  if (batch < 1 || !seq_lens) return set_err(DKV_ERR_INVALID, "batch >= 1 and seq_lens required");
-  if (num_cus < 1) return set_err(DKV_ERR_INVALID, "num_cus must be >= 1");
-  if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads)
-    return set_err(DKV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
-  const dkv_tuning t = tuning_snapshot(nullptr);
-  dkv::PlanInput in{};
-  in.batch = batch; in.hq = num_q_heads; in.hkv = kv->num_kv_heads; in.head_dim = kv->head_dim;
-  in.page_size = kv->page_size; in.max_pages = kv->max_pages;
-  in.host_stride = kv->host_stride; in.dev_stride = kv->dev_stride;
-  in.host_rows = kv->host_rows; in.dev_rows = kv->dev_rows;
-  in.seq_lens = seq_lens; in.page_table_host = kv->page_table_host;
-  in.ratio = kv->page_size == 0 ? offload_ratio : 0.0;
-  in.num_cus = num_cus; in.host_wgs = t.host_wgs; in.dev_wgs = t.dev_wgs;
-  in.host_chunk = t.host_chunk; in.dev_chunk = t.dev_chunk;
-  in.host_bw = t.host_bw_gbs; in.dev_bw = t.dev_bw_gbs;
-  dkv::PlanLayout L;
-  std::vector<uint8_t> blob;
-  std::string err;
-  if (!dkv::build_plan(in, &L, &blob, &err)) return set_err(DKV_ERR_INVALID, "%s", err.c_str());
-  const dkv::PlanItem* it = reinterpret_cast<const dkv::PlanItem*>(blob.data() + L.items_off);
-  const int n_items = L.n_host_items + L.n_dev_items;
-  if (items)
-    for (int i = 0; i < n_items && i < items_cap; ++i) {
-      items[5 * i + 0] = i < L.n_host_items ? 1 : 0;
-      items[5 * i + 1] = it[i].b;
-      items[5 * i + 2] = it[i].slot;
-      items[5 * i + 3] = it[i].n_tok;
-      items[5 * i + 4] = kv->page_size > 0 ? it[i].plist : it[i].row0;
+  if (!seq_lens) return set_err(DKV_ERR_INVALID, "seq_lens is required");
+  if (num_cus < 0) return set_err(DKV_ERR_INVALID, "num_cus must be >= 0");
+  if (kv->page_size > 0 && !kv->page_table_host)
+    return set_err(DKV_ERR_INVALID, "paged layout needs page_table_host to inspect");
+  DecodeShape d;
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, false, 0, num_cus, &d);
+  if (st != DKV_OK) return st;
+  const dkv::PlanInput in = decode_input(kv, batch, num_q_heads, offload_ratio, 1, tuning_snapshot(nullptr));
+  std::vector<int64_t> nh(batch), nd(batch);
+  std::vector<std::vector<int32_t>> hp(batch), dp(batch);
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return set_err(DKV_ERR_INVALID, "seq_lens[%d] is negative", b);
+    if (kv->page_size == 0) {
+      int64_t ph;
+      dkv::contig_tiers(offload_ratio, seq_lens[b], seq_lens[b], &nh[b], &nd[b], &ph);
+      if (ph > 0 && (ph > kv->host_stride || (int64_t)b * kv->host_stride + ph > kv->host_rows))
+        return set_err(DKV_ERR_INVALID, "sequence %d: host rows needed beyond host_stride/host_rows", b);
+      if (seq_lens[b] - ph > 0 && (seq_lens[b] - ph > kv->dev_stride ||
+                                   (int64_t)b * kv->dev_stride + (seq_lens[b] - ph) > kv->dev_rows))
+        return set_err(DKV_ERR_INVALID, "sequence %d: device rows needed beyond dev_stride/dev_rows", b);
+    } else if (!dkv::decode_tiers_host(in, b, seq_lens[b], &hp[b], &dp[b], &nh[b], &nd[b])) {
+      return set_err(DKV_ERR_INVALID, "sequence %d: page table entry unmapped or beyond its pool", b);
     }
-  if (page_list)
-    memcpy(page_list, blob.data() + L.plist_off, sizeof(int32_t) * std::min(L.n_plist, page_cap));
-  if (split_offsets) memcpy(split_offsets, blob.data() + L.offsets_off, sizeof(int32_t) * (batch + 1));
-  if (info) fill_info(L, L.blob_bytes, info);
+  }
+  std::vector<dkv::DecodeHostItem> list;
+  std::vector<int32_t> offs;
+  dkv::DecodeSizes z{};
+  dkv::decode_enumerate(d.t, batch, nh.data(), nd.data(), &list, &offs, &z);
+  int32_t n_host = 0, n_page = 0;
+  int64_t host_tok = 0, dev_tok = 0;
+  for (int b = 0; b < batch; ++b) {
+    host_tok += nh[b];
+    dev_tok += nd[b];
+  }
+  for (size_t i = 0; i < list.size(); ++i) {
+    const dkv::DecodeHostItem& it = list[i];
+    n_host += it.host;
+    int64_t first;
+    if (kv->page_size == 0) {
+      first = (int64_t)it.b * (it.host ? kv->host_stride : kv->dev_stride) + it.k0;
+    } else {
+      // logical pages of the item, appended to page_list
+      const std::vector<int32_t>& pg = it.host ? hp[it.b] : dp[it.b];
+      first = n_page;
+      const int64_t p0 = it.k0 / kv->page_size, p1 = (it.k0 + it.n_tok + kv->page_size - 1) / kv->page_size;
+      for (int64_t k = p0; k < p1; ++k, ++n_page)
+        if (page_list && n_page < page_cap) page_list[n_page] = pg[k];
+    }
+    if (items && (int64_t)i < items_cap) {
+      int64_t* o = items + 5 * i;
+      o[0] = it.host; o[1] = it.b; o[2] = it.slot; o[3] = it.n_tok; o[4] = first;
+    }
+  }
+  if (split_offsets) memcpy(split_offsets, offs.data(), sizeof(int32_t) * (batch + 1));
+  if (info) {
+    const int64_t row_bytes = (int64_t)kv->num_kv_heads * kv->head_dim * 2;
+    *info = dkv_plan_info{};
+    info->workspace_bytes = (int64_t)d.total;
+    info->num_splits = offs[batch];
+    info->host_items = n_host;
+    info->dev_items = (int32_t)list.size() - n_host;
+    info->host_wgs = d.t.team_h * kv->num_kv_heads;
+    info->dev_wgs = d.t.team_d * kv->num_kv_heads;
+    info->host_chunk = n_host ? z.ch : 0;
+    info->dev_chunk = (int32_t)list.size() > n_host ? z.cd : 0;
+    info->host_bytes = host_tok * row_bytes * 2;
+    info->dev_bytes = dev_tok * row_bytes * 2;
+  }
   return ok();
 }
-
 dkv_status dkv_prefill_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                                     const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
                                     double offload_ratio, int32_t fused, int32_t num_cus, int64_t* items, int32_t items_cap,
@@ -670,85 +811,146 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
                                  void* workspace, size_t workspace_bytes, float* part_o,
                                  float* part_lse, int32_t* split_offsets, int32_t num_splits_cap,
                                  void* stream) {
-  dkv_status st = validate_desc(kv);
+  dkv_status st = validate_decode_common(kv, q, q_pos, seq_lens, scale, rope_theta, workspace);
   if (st != DKV_OK) return st;
-  if (kv->page_size == 0 && validate_ratio(offload_ratio) != DKV_OK) return DKV_ERR_INVALID;
-  if (!q || !q_pos || !part_o || !part_lse || !split_offsets || !workspace)
-    return set_err(DKV_ERR_INVALID, "q, q_pos, part_o, part_lse, split_offsets and workspace are required");
-  if (!(std::isfinite(scale)) || !(std::isfinite(rope_theta)) || rope_theta <= 0.0)
-    return set_err(DKV_ERR_INVALID, "scale must be finite and rope_theta > 0");
-  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
-  std::shared_ptr<PlanEntry> e;
-  st = get_plan(kv, batch, num_q_heads, seq_lens, kv->page_size == 0 ? offload_ratio : 0.0, &e);
+  if (!part_o || !part_lse || !split_offsets)
+    return set_err(DKV_ERR_INVALID, "part_o, part_lse and split_offsets are required");
+  DecodeShape d;
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, false, 0, 0, &d);
   if (st != DKV_OK) return st;
-  const dkv::PlanLayout& L = e->lay;
-  const size_t need = L.blob_bytes;
-  if (workspace_bytes < need)
-    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-  if (num_splits_cap < L.num_splits)
-    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %d splits", num_splits_cap, L.num_splits);
+  if (workspace_bytes < d.total)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, d.total);
+  if ((int64_t)num_splits_cap < d.max_splits)
+    return set_err(DKV_ERR_INVALID, "num_splits_cap %d < %lld (the split bound of this shape)", num_splits_cap,
+                   (long long)d.max_splits);
   hipStream_t s = (hipStream_t)stream;
-  if (debug_validate() && kv->page_size > 0) {
-    std::vector<int32_t> pt((size_t)batch * kv->max_pages);
-    hipError_t he = hipMemcpy(pt.data(), kv->page_table, pt.size() * 4, hipMemcpyDeviceToHost);
-    if (he != hipSuccess) return hip_err(he, "debug copy of page_table");
-    for (int b = 0; b < batch; ++b) {
-      const int64_t npg = ((int64_t)seq_lens[b] + kv->page_size - 1) / kv->page_size;
-      for (int64_t j = 0; j < npg; ++j)
-        if (pt[(size_t)b * kv->max_pages + j] != kv->page_table_host[(size_t)b * kv->max_pages + j])
-          return set_err(DKV_ERR_INVALID, "page_table and page_table_host differ at [%d][%lld]", b,
-                         (long long)j);
-    }
+  if (debug_validate()) {
+    st = decode_debug_check(kv, batch, seq_lens, offload_ratio, 0, s);
+    if (st != DKV_OK) return st;
   }
-  if (stream_capturing(s)) {
-    // the captured copy node reads this image on every replay
-    std::lock_guard<std::mutex> lk(cache().mu);
-    e->captured = true;
-  }
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
-  if (he != hipSuccess) return hip_err(he, "plan upload");
-  const float scale_log2 = scale * 1.44269504088896340736f;
-  dkv::AttnArgs a{};
-  a.host_items = reinterpret_cast<const dkv::PlanItem*>(ws + L.items_off);
-  a.dev_items = a.host_items + L.n_host_items;
-  a.plist = reinterpret_cast<const int32_t*>(ws + L.plist_off);
-  a.plan_offsets = reinterpret_cast<const int32_t*>(ws + L.offsets_off);
-  a.unit_counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
-  a.split_offsets = split_offsets;
-  a.n_host_units = L.n_host_items * kv->num_kv_heads;
-  a.n_dev_units = L.n_dev_items * kv->num_kv_heads;
-  a.host_wgs = L.host_wgs;
-  a.dev_wgs = L.dev_wgs;
-  a.host_k = static_cast<const uint16_t*>(kv->host_k);
-  a.host_v = static_cast<const uint16_t*>(kv->host_v);
-  a.dev_k = static_cast<const uint16_t*>(kv->dev_k);
-  a.dev_v = static_cast<const uint16_t*>(kv->dev_v);
-  a.host_rows = kv->host_rows;
-  a.dev_rows = kv->dev_rows;
-  a.page_table = kv->page_size > 0 ? kv->page_table : nullptr;
-  a.max_pages = kv->max_pages;
-  a.page_shift = kv->page_size > 0 ? log2i(kv->page_size) : -1;
-  a.q = static_cast<const uint16_t*>(q);
-  a.q_pos = q_pos;
-  a.batch = batch;
-  a.hq = num_q_heads;
-  a.hkv = kv->num_kv_heads;
-  a.head_dim = kv->head_dim;
-  a.scale_log2 = scale_log2;
-  a.theta = rope_theta;
+  dkv::DecodeArgs a = decode_args(kv, d, batch, num_q_heads, q, q_pos, seq_lens, offload_ratio, scale, rope_theta,
+                                  workspace);
+  a.fused = 0;
   a.part_o = part_o;
   a.part_lse = part_lse;
-  a.freq = rope_freq(rope_theta, kv->head_dim);
-  {
-    std::lock_guard<std::mutex> lk(g_trace_mu);
-    a.wg_trace = g_trace_buf;
-    a.wg_trace_cap = g_trace_cap;
+  a.split_offsets = split_offsets;
+  hipError_t he;
+  if (kv->page_size > 0) {
+    TimedLaunch t_tiers(DKV_KERNEL_TIERS, s);
+    he = (hipError_t)dkv::launch_decode_tiers(a, const_cast<int32_t*>(a.tier_counts),
+                                              const_cast<int32_t*>(a.tier_pages), stream);
+    t_tiers.done();
+    if (he != hipSuccess) return hip_err(he, "tier lists launch");
   }
   TimedLaunch t_attn(DKV_KERNEL_ATTN, s);
-  he = (hipError_t)dkv::launch_attn(a, stream);
+  he = (hipError_t)dkv::launch_decode(a, stream);
   t_attn.done();
   if (he != hipSuccess) return hip_err(he, "attention launch");
+  return ok();
+}
+
+dkv_status dkv_decode_step_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, double offload_ratio,
+                                int32_t hidden, dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (hidden < 0) return set_err(DKV_ERR_INVALID, "hidden must be >= 0");
+  DecodeShape d;
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, true, hidden, 0, &d);
+  if (st != DKV_OK) return st;
+  *info = dkv_plan_info{};
+  info->workspace_bytes = (int64_t)d.total;
+  info->num_splits = d.max_slots;
+  info->host_wgs = d.t.team_h * kv->num_kv_heads;
+  info->dev_wgs = d.t.team_d * kv->num_kv_heads;
+  return ok();
+}
+
+dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                           const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new, const void* x,
+                           int32_t hidden, const void* wk, const void* wv, const void* k_new, const void* v_new,
+                           double offload_ratio, float scale, double rope_theta, void* workspace,
+                           size_t workspace_bytes, float* out_o, float* out_lse, void* stream) {
+  dkv_status st = validate_decode_common(kv, q, q_pos, seq_lens, scale, rope_theta, workspace);
+  if (st != DKV_OK) return st;
+  if (!out_o) return set_err(DKV_ERR_INVALID, "out_o is required");
+  const bool proj = x != nullptr;
+  const bool append = proj || k_new != nullptr || v_new != nullptr;
+  const int32_t kvd = kv->num_kv_heads * kv->head_dim;
+  if (proj) {
+    if (!wk || !wv) return set_err(DKV_ERR_INVALID, "projection mode needs wk and wv");
+    if (hidden < 256 || hidden % 256)
+      return set_err(DKV_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 256", hidden);
+    if ((2 * kvd) % 64) return set_err(DKV_ERR_UNSUPPORTED, "2*Hkv*D must be a multiple of 64");
+    if ((uintptr_t)x % 16 || (uintptr_t)wk % 16 || (uintptr_t)wv % 16)
+      return set_err(DKV_ERR_INVALID, "x, wk, wv must be 16-byte aligned");
+  } else if (append && (!k_new || !v_new)) {
+    return set_err(DKV_ERR_INVALID, "appending needs both k_new and v_new (or x with wk and wv)");
+  }
+  DecodeShape d;
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, true, proj ? hidden : 0, 0, &d);
+  if (st != DKV_OK) return st;
+  if (workspace_bytes < d.total)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, d.total);
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_validate()) {
+    st = decode_debug_check(kv, batch, seq_lens, offload_ratio, append ? 1 : 0, s);
+    if (st != DKV_OK) return st;
+  }
+  dkv::DecodeArgs a = decode_args(kv, d, batch, num_q_heads, q, q_pos, seq_lens, offload_ratio, scale, rope_theta,
+                                  workspace);
+  a.fused = 1;
+  a.new_tokens = append ? 1 : 0;
+  a.out_o = out_o;
+  a.out_lse = out_lse;
+  a.pos_new = pos_new;
+  hipError_t he;
+  if (proj) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace) + d.proj_off;
+    dkv::ProjArgs p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.wk = static_cast<const uint16_t*>(wk);
+    p.wv = static_cast<const uint16_t*>(wv);
+    p.n_new = batch;
+    p.n_pad = (batch + 15) / 16 * 16;
+    p.hidden = hidden;
+    p.kv_dim = kvd;
+    p.ksplit = hidden / 256;
+    p.kslice = 256;
+    const int64_t part = (int64_t)p.ksplit * p.n_pad * 2 * kvd * 4;
+    p.partial = reinterpret_cast<float*>(ws);
+    p.out = reinterpret_cast<float*>(ws + ((part + 255) / 256) * 256);
+    TimedLaunch t_proj(DKV_KERNEL_APPEND, s);
+    he = (hipError_t)dkv::launch_project(p, stream);
+    t_proj.done();
+    if (he != hipSuccess) return hip_err(he, "projection launch");
+    a.kv_proj = p.out;
+  } else if (append) {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+  }
+  if (kv->page_size > 0) {
+    TimedLaunch t_tiers(DKV_KERNEL_TIERS, s);
+    he = (hipError_t)dkv::launch_decode_tiers(a, const_cast<int32_t*>(a.tier_counts),
+                                              const_cast<int32_t*>(a.tier_pages), stream);
+    t_tiers.done();
+    if (he != hipSuccess) return hip_err(he, "tier lists launch");
+  }
+  TimedLaunch t_attn(DKV_KERNEL_ATTN, s);
+  he = (hipError_t)dkv::launch_decode(a, stream);
+  t_attn.done();
+  if (he != hipSuccess) return hip_err(he, "decode step launch");
+  return ok();
+}
+
+dkv_status dkv_decode_errors(const dkv_kv_desc* kv, const void* workspace, int32_t clear, int32_t* flags) {
+  if (!kv || !workspace || !flags) return set_err(DKV_ERR_INVALID, "kv, workspace and flags are required");
+  hipError_t he = hipDeviceSynchronize();
+  const int32_t* w = static_cast<const int32_t*>(workspace) + dkv::decode_error_word(kv->num_kv_heads);
+  if (he == hipSuccess) he = hipMemcpy(flags, w, 4, hipMemcpyDeviceToHost);
+  if (he == hipSuccess && clear) he = hipMemset(const_cast<int32_t*>(w), 0, 4);
+  if (he == hipSuccess) he = hipDeviceSynchronize();
+  if (he != hipSuccess) return hip_err(he, "reading the decode error word");
   return ok();
 }
 
@@ -1089,7 +1291,7 @@ dkv_status dkv_kernel_timing(int32_t enable) {
 }
 
 dkv_status dkv_kernel_timing_read(int32_t kernel, int32_t* count, double* total_ms) {
-  if (kernel < 0 || kernel > DKV_KERNEL_LINEAR || !count || !total_ms)
+  if (kernel < 0 || kernel > DKV_KERNEL_TIERS || !count || !total_ms)
     return set_err(DKV_ERR_INVALID, "kernel id in [0,4] and outputs required");
   Timing& t = timing();
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;

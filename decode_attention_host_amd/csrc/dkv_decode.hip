@@ -1,0 +1,985 @@
+// dkv_decode.hip - gfx950 decode kernels: split decode attention over a KV
+// cache held partly in host-pinned memory (read in place over the host link)
+// and partly in HBM, with the work split derived on the device.
+//
+//   decode_tiers_kernel  paged layout: each sequence's pages sorted by tier
+//                        (physical page numbers in logical order) and its
+//                        tokens per tier, for the sequence lengths of this call
+//   decode_kernel        rotate the query heads (Neox RoPE, fp64 angle), stream
+//                        K/V tiles of one tier into LDS, Q.K on MFMA, online
+//                        softmax, P.V on the vector ALUs; either one normalised
+//                        partial per work item (split form) or, fused, one
+//                        partial per workgroup run merged by log-sum-exp in the
+//                        same launch, after appending each sequence's new token
+//
+// Method sources (page, section): DirectKV README, introduction (one kernel
+// projects the new token's K/V, rotates keys with Neox RoPE and attends over
+// KV read from CPU-pinned buffers) and Attribution (online softmax over KV
+// streamed from CPU memory with no GPU staging buffer); SplitKernel README,
+// Overview and Key Features (direct access of the remote tier into on-chip
+// memory; attention over a host/device partitioned KV cache; both tiers'
+// bandwidth used at once).
+//
+// Design for CDNA4:
+//   * No host plan.  Every workgroup reads the lengths (and, paged, the tier
+//     counts) from device memory and derives the same items (dkv_decomp.h), so
+//     a call captured in a graph stays valid while the cache grows, and a step
+//     needs no host work beyond argument checks.
+//   * Teams.  A workgroup serves one KV head in one tier; the items of a tier
+//     are taken in order from the team's queue (first by index, then by an
+//     atomic counter), so every workgroup sees its sequences in increasing
+//     order and its rotated query changes only with the sequence.
+//   * Fused form.  A workgroup keeps its online-softmax state across
+//     consecutive items of one sequence and writes one partial per run; the
+//     last run of a (sequence, KV head) to finish merges them.  Partials are
+//     written and read with agent-coherent (sc1) buffer accesses and the
+//     completion counter is bumped after the stores are acknowledged, which
+//     orders them across XCDs without an L2 write-back.
+//   * Tiles: 64 tokens of one KV head, D/32 coalesced 16-byte loads of K and
+//     of V per thread (non-temporal: the KV is read once), staged in LDS with a
+//     16-byte row pad; the next tile is in flight while one is computed.
+//   * Q.K^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims from LDS, B =
+//     the group's rotated queries, each fp32 query split into high and low bf16
+//     parts in columns h and h+8 (~16 bits of the query, fp32 accumulation).
+//   * P.V on the vector ALUs (two output dims per lane at D = 128).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dkv_decomp.h"
+#include "dkv_device.h"
+#include "dkv_internal.h"
+
+namespace dkv {
+
+template <int D>
+struct AttnShape {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kPitch = kRowBytes + 16;          // LDS row pitch (bytes)
+  static constexpr int kChunksPerRow = D / 8;            // 16-byte chunks per row
+  static constexpr int kChunksPerThread = kTile * kChunksPerRow / kThreads;  // D/32
+  static constexpr int kKSteps = D / 32;                 // MFMA k-steps per key
+  static constexpr int kDimsPerLane = D / 64;            // P.V output dims per lane
+};
+
+// Buffer accesses that are coherent across XCDs: cache policy sc1 makes a
+// store write through to the device-coherent level and a load read from it,
+// so no L2 write-back or invalidate is needed around them.
+constexpr int kCoherent = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, int byte_off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void coherent_store1(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ floatx4 coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
+}
+
+// Waits until this thread's stores are acknowledged (written at the coherent
+// level for the sc1 stores above).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Paged layout: per sequence, the physical pages of each tier in logical order
+// and the tokens each tier holds among the sequence's first seq_lens[b].
+// One 1024-thread workgroup per sequence; each round takes 16 consecutive
+// page entries per thread (all loads issued before any is used) and places
+// them with a block-wide scan.  Entries that are negative or beyond their
+// tier's pool are left out (and flagged in the workspace).
+// ---------------------------------------------------------------------------
+constexpr int kTierThreads = 1024;
+constexpr int kTierPer = 16;
+
+__global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a, int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ pages) {
+  constexpr int NW = kTierThreads / 64;
+  __shared__ int32_t s_wh[NW], s_wd[NW];
+  __shared__ int32_t s_base[2];
+  __shared__ int32_t s_last;  // tier of the sequence's final page: 1 host, 0 HBM, -1 none
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = 1 << a.page_shift;
+  int64_t A = a.seq_lens[b];
+  if (A < 0) A = 0;
+  int64_t npg = (A + P - 1) >> a.page_shift;
+  int err = 0;
+  if (npg > a.max_pages) {
+    err |= kDecodeErrPage;
+    npg = a.max_pages;
+    A = npg * P;
+  }
+  const int32_t* __restrict__ row = a.page_table + (int64_t)b * a.max_pages;
+  int32_t* __restrict__ hl = pages + (int64_t)b * a.max_pages;
+  int32_t* __restrict__ dl = pages + ((int64_t)a.batch + b) * a.max_pages;
+  const int64_t host_pages_cap = a.host_k ? (a.host_rows >> a.page_shift) : 0;
+  const int64_t dev_pages_cap = a.dev_k ? (a.dev_rows >> a.page_shift) : 0;
+  if (tid == 0) {
+    s_base[0] = 0;
+    s_base[1] = 0;
+    s_last = -1;
+  }
+  __syncthreads();
+  for (int64_t j0 = 0; j0 < npg; j0 += (int64_t)kTierThreads * kTierPer) {
+    const int64_t jt = j0 + (int64_t)tid * kTierPer;
+    int32_t e[kTierPer];
+#pragma unroll
+    for (int k = 0; k < kTierPer; ++k) e[k] = (jt + k < npg) ? row[jt + k] : -1;
+    uint32_t hm = 0, dm = 0;
+    int ch = 0, cd = 0;
+#pragma unroll
+    for (int k = 0; k < kTierPer; ++k) {
+      if (jt + k >= npg) continue;
+      const int32_t x = e[k];
+      const bool host = (x & 1) != 0;
+      const bool ok = x >= 0 && (int64_t)(x >> 1) < (host ? host_pages_cap : dev_pages_cap);
+      if (!ok) {
+        err |= kDecodeErrPage;
+        continue;
+      }
+      if (host) {
+        hm |= 1u << k;
+        ++ch;
+      } else {
+        dm |= 1u << k;
+        ++cd;
+      }
+      if (jt + k == npg - 1) s_last = host ? 1 : 0;
+    }
+    int ih = ch, id = cd;  // inclusive scans within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int th = __shfl_up(ih, o), td = __shfl_up(id, o);
+      if (lane >= o) {
+        ih += th;
+        id += td;
+      }
+    }
+    if (lane == 63) {
+      s_wh[wave] = ih;
+      s_wd[wave] = id;
+    }
+    __syncthreads();
+    int ph = s_base[0], pd = s_base[1];
+    for (int w = 0; w < wave; ++w) {
+      ph += s_wh[w];
+      pd += s_wd[w];
+    }
+    ph += ih - ch;
+    pd += id - cd;
+#pragma unroll
+    for (int k = 0; k < kTierPer; ++k) {
+      if (hm & (1u << k)) hl[ph++] = e[k] >> 1;
+      if (dm & (1u << k)) dl[pd++] = e[k] >> 1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int th = 0, td = 0;
+      for (int w = 0; w < NW; ++w) {
+        th += s_wh[w];
+        td += s_wd[w];
+      }
+      s_base[0] += th;
+      s_base[1] += td;
+    }
+    __syncthreads();
+  }
+  if (err) atomicOr(&a.counters[decode_error_word(a.hkv)], err);
+  if (tid == 0) {
+    const int64_t deficit = npg > 0 ? P - (A - (npg - 1) * P) : 0;
+    const int64_t nh = (int64_t)s_base[0] * P - (s_last == 1 ? deficit : 0);
+    const int64_t nd = (int64_t)s_base[1] * P - (s_last == 0 ? deficit : 0);
+    counts[4 * b + 0] = s_base[0];
+    counts[4 * b + 1] = s_base[1];
+    counts[4 * b + 2] = (int32_t)nh;
+    counts[4 * b + 3] = (int32_t)nd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel.
+// ---------------------------------------------------------------------------
+
+// One work item as the kernel sees it.
+struct DItem {
+  int32_t b;      // sequence
+  int32_t n_tok;  // tokens
+  int32_t slot;   // split form: partial slot
+  int32_t pad;
+  int64_t k0;     // first ordinal of the item in its tier
+};
+
+// Per-sequence prefix arrays of the current call (LDS), built by wave 0.
+struct DecodeLds {
+  int32_t ph[kDecodeMaxBatch + 1];   // host items before sequence b
+  int32_t pm[kDecodeMaxBatch + 1];   // HBM items (before the tail) before b
+  int32_t pt[kDecodeMaxBatch + 1];   // HBM tail items before b
+  int32_t off[kDecodeMaxBatch + 1];  // split slots before b
+  int32_t nh[kDecodeMaxBatch];       // host tokens attended
+  int32_t nd[kDecodeMaxBatch];       // HBM tokens attended
+  int32_t t0[kDecodeMaxBatch];       // first tail ordinal of the HBM range
+  DecodeSizes z;
+};
+
+// Largest b in [0, B) with arr[b] <= i (arr non-decreasing, arr[0] = 0, i < arr[B]).
+__device__ __forceinline__ int seq_of(const int32_t* arr, int B, int i) {
+  int lo = 0, hi = B;  // arr[lo] <= i < arr[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (arr[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ DItem item_at(const DecodeLds& L, int B, bool host, int i) {
+  DItem it{};
+  if (host) {
+    const int b = seq_of(L.ph, B, i);
+    const int c = i - L.ph[b];
+    it.b = b;
+    it.k0 = (int64_t)c * L.z.ch;
+    it.n_tok = (int32_t)min((int64_t)L.z.ch, (int64_t)L.nh[b] - it.k0);
+    it.slot = L.off[b] + c;
+  } else {
+    const int M = L.pm[B];
+    if (i < M) {
+      const int b = seq_of(L.pm, B, i);
+      const int c = i - L.pm[b];
+      it.b = b;
+      it.k0 = (int64_t)c * L.z.cd;
+      it.n_tok = (int32_t)min((int64_t)L.z.cd, (int64_t)L.t0[b] - it.k0);
+      it.slot = L.off[b] + (L.ph[b + 1] - L.ph[b]) + c;
+    } else {
+      const int i2 = i - M;
+      const int b = seq_of(L.pt, B, i2);
+      const int c = i2 - L.pt[b];
+      it.b = b;
+      it.k0 = (int64_t)L.t0[b] + (int64_t)c * L.z.cs;
+      it.n_tok = (int32_t)min((int64_t)L.z.cs, (int64_t)L.nd[b] - it.k0);
+      it.slot = L.off[b] + (L.ph[b + 1] - L.ph[b]) + (L.pm[b + 1] - L.pm[b]) + c;
+    }
+  }
+  return it;
+}
+
+// Inclusive scan of v over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ long long wave_sum64(long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Wave 0 reads the lengths, derives each sequence's tier tokens and items and
+// writes the prefix arrays; the caller synchronises the workgroup afterwards.
+template <bool PAGED>
+__device__ void build_prefix(const DecodeArgs& a, DecodeLds& L) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.batch;
+  long long th = 0, td = 0;
+  int err = 0;
+  for (int b = lane; b < B; b += 64) {
+    int64_t nh, nd;
+    if (PAGED) {
+      nh = a.tier_counts[4 * b + 2];
+      nd = a.tier_counts[4 * b + 3];
+    } else {
+      int64_t Lb = a.seq_lens[b];
+      if (Lb < 0) Lb = 0;
+      int64_t placed_host;
+      contig_tiers(a.ratio, Lb, Lb + a.new_tokens, &nh, &nd, &placed_host);
+      const int64_t placed_dev = Lb + a.new_tokens - placed_host;
+      const bool bad = (placed_host > 0 && (placed_host > a.host_stride || !a.host_k ||
+                                            (int64_t)b * a.host_stride + placed_host > a.host_rows)) ||
+                       (placed_dev > 0 && (placed_dev > a.dev_stride || !a.dev_k ||
+                                           (int64_t)b * a.dev_stride + placed_dev > a.dev_rows));
+      if (bad) {  // rows beyond the layout: the sequence is not read (and is flagged)
+        err |= kDecodeErrLayout;
+        nh = 0;
+        nd = 0;
+      }
+    }
+    L.nh[b] = (int32_t)nh;
+    L.nd[b] = (int32_t)nd;
+    th += nh;
+    td += nd;
+  }
+  th = wave_sum64(th);
+  td = wave_sum64(td);
+  const DecodeSizes z = decode_sizes(a.tmpl, th, td);
+  int ch = 0, cm = 0, ct = 0, cs = 0;  // running totals of earlier chunks of 64 sequences
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    DecodeSeqItems s{};
+    if (b < B) s = decode_seq_items(z, a.tmpl.align, L.nh[b], L.nd[b]);
+    const int nsp = s.uh + s.um + s.ut;
+    const int ih = wave_incl_scan(s.uh), im = wave_incl_scan(s.um), it = wave_incl_scan(s.ut),
+              is = wave_incl_scan(nsp);
+    if (b < B) {
+      L.ph[b] = ch + ih - s.uh;
+      L.pm[b] = cm + im - s.um;
+      L.pt[b] = ct + it - s.ut;
+      L.off[b] = cs + is - nsp;
+      L.t0[b] = (int32_t)s.t0;
+    }
+    ch += __shfl(ih, 63);
+    cm += __shfl(im, 63);
+    ct += __shfl(it, 63);
+    cs += __shfl(is, 63);
+  }
+  if (lane == 0) {
+    L.ph[B] = ch;
+    L.pm[B] = cm;
+    L.pt[B] = ct;
+    L.off[B] = cs;
+    L.z = z;
+  }
+  if (err) atomicOr(&a.counters[decode_error_word(a.hkv)], err);
+}
+
+template <int D, int G, bool PAGED, bool FUSED>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  using S = AttnShape<D>;
+  constexpr int NC = S::kChunksPerThread;
+  constexpr int KS = S::kKSteps;
+  constexpr int DPL = S::kDimsPerLane;
+  static_assert(G >= 1 && G <= 8, "group size");
+  static_assert(4 * G * (D + 2) * 4 <= kTile * S::kPitch, "epilogue scratch");
+  static_assert(G * D * 4 <= kTile * S::kPitch, "run partial scratch");
+
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * S::kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
+  __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
+  __shared__ float a_lds[4][8];
+  __shared__ __attribute__((aligned(16))) float q_lds[G][D];  // rotated query heads of q_b
+  __shared__ __attribute__((aligned(16))) float o_lds[G][D];  // a partial being written
+  __shared__ float l_lds[G];
+  __shared__ DecodeLds L;
+  __shared__ int s_next;
+  __shared__ int s_slot;
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;     // MFMA column / row-in-tile
+  const int j4 = lane >> 4;    // 0..3
+  const int B = a.batch;
+
+  const bool traced = a.wg_trace && (int)blockIdx.x < a.wg_trace_cap && tid == 0;
+  const uint64_t t_start = traced ? wall_clock64() : 0;
+
+  if (wave == 0) build_prefix<PAGED>(a, L);
+  __syncthreads();
+
+  // Role and team: host-tier workgroups first, each team one KV head.
+  const DecodeTemplate& T = a.tmpl;
+  const bool host_role = (int)blockIdx.x < a.hkv * T.team_h;
+  const int r_idx = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.hkv * T.team_h;
+  const int team = host_role ? T.team_h : T.team_d;
+  const int kvh = r_idx / team;
+  const int jt = r_idx - kvh * team;
+  const int n_items = host_role ? L.ph[B] : L.pm[B] + L.pt[B];
+  const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
+  const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
+  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
+  const int64_t stride = host_role ? a.host_stride : a.dev_stride;
+  const int32_t* __restrict__ tier_list =
+      PAGED ? a.tier_pages + (host_role ? 0 : (int64_t)B * a.max_pages) : nullptr;
+  int* qctr = a.counters + (host_role ? 0 : a.hkv) + kvh;
+
+  if (!FUSED && blockIdx.x == 0 && a.split_offsets)
+    for (int i = tid; i <= B; i += kThreads) a.split_offsets[i] = L.off[i];
+
+  // Rotated query heads of sequence b for this KV head into q_lds: one Neox pair
+  // per thread, angle q_pos[b] * f_i with sin and cos in fp64, rounded once to
+  // fp32 with scale * log2(e) folded in.
+  int q_b = -1;
+  auto rotate_q = [&](int b) {
+    __syncthreads();  // earlier readers of q_lds are done
+    const int pos = a.q_pos[b];
+    const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * D;
+    for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
+      const int h = idx / (D / 2), i = idx - h * (D / 2);
+      double sn, cs;
+      sincos((double)pos * a.freq.f[i], &sn, &cs);
+      const double xl = (double)bf16_to_f32(qh[h * D + i]);
+      const double xh = (double)bf16_to_f32(qh[h * D + i + D / 2]);
+      q_lds[h][i] = (float)(xl * cs - xh * sn) * a.scale_log2;
+      q_lds[h][i + D / 2] = (float)(xh * cs + xl * sn) * a.scale_log2;
+    }
+    __syncthreads();
+    q_b = b;
+  };
+
+  // Runs of partials (fused form): completion bookkeeping per (sequence, KV head).
+  auto group_total = [&](int b) -> int {
+    return (L.ph[b + 1] - L.ph[b]) + (L.pm[b + 1] - L.pm[b]) + (L.pt[b + 1] - L.pt[b]) + a.new_tokens;
+  };
+
+  // Fused form: merge every run partial of (b, kvh); this workgroup finished
+  // it last.  Per head, the maximum and the sum of exp(lse - max) come from a
+  // pass over the lse values; the outputs then fold the runs in chunks whose
+  // weights are staged in LDS (the K tile buffer), with the threads of each
+  // float4 of the output splitting the runs of a chunk between them.
+  auto merge_group = [&](int b) {
+    const int g = b * a.hkv + kvh;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.run_o + (size_t)g * a.max_slots * G * D);
+    const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.run_lse + (size_t)g * a.max_slots * G);
+    if (tid == 0)
+      s_slot = __hip_atomic_load(&a.group_cnt[2 * g + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ns = min(s_slot, a.max_slots);
+    for (int h = wave; h < G; h += 4) {
+      float m = -INFINITY;
+      for (int s = lane; s < ns; s += 64) m = fmaxf(m, coherent_load1(rl, (s * G + h) * 4));
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      float w = 0.f;
+      for (int s = lane; s < ns; s += 64) {
+        const float x = coherent_load1(rl, (s * G + h) * 4);
+        w += (x == -INFINITY) ? 0.f : expf(x - m);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) w += __shfl_xor(w, o);
+      if (lane == 0) {
+        l_lds[h] = (m == -INFINITY) ? -INFINITY : m + logf(w);
+        a_lds[0][h] = m;
+        a_lds[1][h] = w;
+      }
+    }
+    __syncthreads();
+    constexpr int NCH = G * D / 4;                        // float4 chunks of the outputs (<= 256)
+    constexpr int NSG = kThreads / NCH;                   // threads per chunk
+    constexpr int CAP = (kTile * S::kPitch) / (G * 4);    // runs whose weights fit the K buffer
+    static_assert(NCH <= kThreads && NSG >= 1, "merge layout");
+    float* wl = reinterpret_cast<float*>(k_lds);          // [CAP][G] weights of a chunk of runs
+    float* red = reinterpret_cast<float*>(v_lds);         // [NSG][G*D]
+    const int c = tid % NCH, sg = tid / NCH;
+    const int hc = (c * 4) / D;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += CAP) {
+      const int s1 = min(ns, s0 + CAP);
+      for (int idx = tid; idx < (s1 - s0) * G; idx += kThreads) {
+        const int h = idx % G;
+        const float x = coherent_load1(rl, ((s0 * G) + idx) * 4), m = a_lds[0][h];
+        wl[idx] = (m == -INFINITY || x == -INFINITY) ? 0.f : expf(x - m) / a_lds[1][h];
+      }
+      __syncthreads();
+      if (sg < NSG) {
+        int s = s0 + sg;
+        constexpr int U = 8;
+        for (; s + (U - 1) * NSG < s1; s += U * NSG) {
+          floatx4 o[U];
+#pragma unroll
+          for (int k = 0; k < U; ++k) o[k] = coherent_load4(ro, ((s + k * NSG) * G * D + c * 4) * 4);
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            const float w = wl[(s + k * NSG - s0) * G + hc];
+            if (w != 0.f) acc += w * o[k];
+          }
+        }
+        for (; s < s1; s += NSG) {
+          const floatx4 o = coherent_load4(ro, (s * G * D + c * 4) * 4);
+          const float w = wl[(s - s0) * G + hc];
+          if (w != 0.f) acc += w * o;
+        }
+      }
+      __syncthreads();
+    }
+    if (sg < NSG) *reinterpret_cast<floatx4*>(red + sg * G * D + c * 4) = acc;
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      float o = 0.f;
+#pragma unroll
+      for (int k = 0; k < NSG; ++k) o += red[k * G * D + idx];
+      const int h = idx / D, d = idx - h * D;
+      a.out_o[((size_t)b * a.hq + kvh * G + h) * D + d] = (l_lds[h] == -INFINITY) ? 0.f : o;
+    }
+    if (tid < G && a.out_lse) a.out_lse[(size_t)b * a.hq + kvh * G + tid] = l_lds[tid];
+    if (tid == 0) {
+      __hip_atomic_store(&a.group_cnt[2 * g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.group_cnt[2 * g + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  };
+
+  // Fused form: write the run partial held in o_lds / l_lds for sequence b,
+  // count its items and merge if it completes the group.
+  auto flush_run = [&](int b, int items) {
+    const int g = b * a.hkv + kvh;
+    if (tid == 0) s_slot = atomicAdd(&a.group_cnt[2 * g + 1], 1);
+    __syncthreads();
+    const int slot = s_slot;
+    if (slot < a.max_slots) {
+      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.run_o + ((size_t)g * a.max_slots + slot) * G * D);
+      const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.run_lse + ((size_t)g * a.max_slots + slot) * G);
+      for (int c = tid; c < G * D / 4; c += kThreads)
+        coherent_store4(ro, c * 16, *reinterpret_cast<const floatx4*>(&o_lds[0][0] + c * 4));
+      if (tid < G) coherent_store1(rl, tid * 4, l_lds[tid]);
+    } else if (tid == 0) {
+      atomicOr(&a.counters[decode_error_word(a.hkv)], kDecodeErrCapacity);
+    }
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+      const int done = atomicAdd(&a.group_cnt[2 * g], items) + items;
+      s_flag = done == group_total(b);
+    }
+    __syncthreads();
+    if (s_flag) merge_group(b);
+  };
+
+  // Fused form, appended token: rotate its key at pos_new[b] (fp64, one bf16
+  // rounding), store K and V in the token's cache slot, and write the
+  // one-token partial of (b, kvh): o = v, lse = its scaled score.
+  auto new_token = [&](int b) {
+    if (q_b != b) rotate_q(b);
+    const int p = a.pos_new ? a.pos_new[b] : a.seq_lens[b];
+    float* kr = reinterpret_cast<float*>(k_lds);  // rotated key (bf16 values) [D]
+    float* vr = kr + D;                           // value [D]
+    const int kvd = a.hkv * D;
+    // slot of (b, p)
+    uint16_t* sk = nullptr;
+    uint16_t* sv = nullptr;
+    if (p >= 0) {
+      if (PAGED) {
+        const int lp = p >> a.page_shift;
+        if (lp < a.max_pages) {
+          const int32_t e = a.page_table[(int64_t)b * a.max_pages + lp];
+          const bool host = (e & 1) != 0;
+          const int64_t row = ((int64_t)(e >> 1) << a.page_shift) | (p & ((1 << a.page_shift) - 1));
+          if (e >= 0 && row < (host ? a.host_rows : a.dev_rows) && (host ? a.host_k : a.dev_k)) {
+            sk = (host ? a.host_k : a.dev_k) + row * kvd + kvh * D;
+            sv = (host ? a.host_v : a.dev_v) + row * kvd + kvh * D;
+          }
+        }
+      } else {
+        int64_t Lb = a.seq_lens[b];
+        if (Lb < 0) Lb = 0;
+        int64_t nh, nd, ph;
+        contig_tiers(a.ratio, Lb, Lb + 1, &nh, &nd, &ph);
+        const bool host = p < ph;
+        if (p <= Lb) {
+          const int64_t row = host ? (int64_t)b * a.host_stride + p : (int64_t)b * a.dev_stride + (p - ph);
+          const bool fits = host ? (ph <= a.host_stride && row < a.host_rows && a.host_k)
+                                 : (Lb + 1 - ph <= a.dev_stride && row < a.dev_rows && a.dev_k);
+          if (fits) {
+            sk = (host ? a.host_k : a.dev_k) + row * kvd + kvh * D;
+            sv = (host ? a.host_v : a.dev_v) + row * kvd + kvh * D;
+          }
+        }
+      }
+    }
+    if (!sk && tid == 0) atomicOr(&a.counters[decode_error_word(a.hkv)], kDecodeErrSlot);
+    if (tid < D / 2) {
+      const int i = tid;
+      double xl, xh;
+      if (a.kv_proj) {
+        const float* kp = a.kv_proj + (size_t)b * 2 * kvd + kvh * D;
+        xl = (double)kp[i];
+        xh = (double)kp[i + D / 2];
+      } else {
+        const uint16_t* kp = a.k_new + (size_t)b * kvd + kvh * D;
+        xl = (double)bf16_to_f32(kp[i]);
+        xh = (double)bf16_to_f32(kp[i + D / 2]);
+      }
+      double sn, cs;
+      sincos((double)p * a.freq.f[i], &sn, &cs);
+      const uint32_t yl = f64_to_bf16(xl * cs - xh * sn);
+      const uint32_t yh = f64_to_bf16(xh * cs + xl * sn);
+      kr[i] = bf16_to_f32(yl);
+      kr[i + D / 2] = bf16_to_f32(yh);
+      if (sk) {
+        sk[i] = (uint16_t)yl;
+        sk[i + D / 2] = (uint16_t)yh;
+      }
+    } else if (tid < D) {
+      const int i = tid - D / 2;
+      for (int d = i; d < D; d += D / 2) {
+        uint32_t vb;
+        if (a.kv_proj) vb = f32_to_bf16(a.kv_proj[(size_t)b * 2 * kvd + kvd + kvh * D + d]);
+        else vb = a.v_new[(size_t)b * kvd + kvh * D + d];
+        vr[d] = bf16_to_f32(vb);
+        if (sv) sv[d] = (uint16_t)vb;
+      }
+    }
+    __syncthreads();
+    // scores: 32 lanes per head
+    {
+      const int h = tid >> 5, l32 = tid & 31;
+      float s = 0.f;
+      if (h < G)
+        for (int d = l32; d < D; d += 32) s = fmaf(q_lds[h][d], kr[d], s);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (h < G && l32 == 0) l_lds[h] = s * 0.69314718055994530942f;  // log2 units -> natural log
+    }
+    for (int idx = tid; idx < G * D; idx += kThreads) o_lds[idx / D][idx % D] = vr[idx % D];
+    __syncthreads();
+    flush_run(b, 1);
+  };
+
+  int units_done = 0;
+
+  // appended tokens of this workgroup (fused form): team kvh of the HBM tier,
+  // or of the host tier when there is none; the last workgroups of the team
+  // take them, which have the fewest items
+  if (FUSED && a.new_tokens) {
+    const bool mine_role = T.team_d > 0 ? !host_role : host_role;
+    if (mine_role)
+      for (int b = team - 1 - jt; b < B; b += team) new_token(b);
+  }
+
+  u32x4 kreg[NC], vreg[NC];
+  // Paged: the physical page of each chunk of a tile, from the tier list.
+  // Chunk c covers rows [c*RPC, (c+1)*RPC) of the tile; with pages of at least
+  // RPC rows all threads look up the same entries, through the scalar cache.
+  auto lookup = [&](const DItem& it, int tile, int32_t* pte) {
+    constexpr int RPC = kThreads / S::kChunksPerRow;
+    const int32_t* pl = tier_list + (int64_t)it.b * a.max_pages;
+    if ((1 << a.page_shift) >= RPC) {
+      typedef __attribute__((address_space(4))) const int32_t ConstInt;
+      const ConstInt* cl = (const ConstInt*)pl;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        pte[c] = cl[(it.k0 + min(tile * kTile + c * RPC, it.n_tok - 1)) >> a.page_shift];
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int tok = min(tile * kTile + (tid + c * kThreads) / S::kChunksPerRow, it.n_tok - 1);
+        pte[c] = pl[(it.k0 + tok) >> a.page_shift];
+      }
+    }
+  };
+  auto load_tile = [&](const DItem& it, int tile, const int32_t* pte) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int r = chunk / S::kChunksPerRow;
+      const int col = chunk - r * S::kChunksPerRow;
+      const int tok = tile * kTile + r;
+      bool valid = tok < it.n_tok;
+      int64_t row;
+      if (PAGED) {
+        const int64_t k = it.k0 + tok;
+        row = ((int64_t)pte[c] << a.page_shift) | (k & ((1 << a.page_shift) - 1));
+        valid = valid && row < cap_rows;
+      } else {
+        row = (int64_t)it.b * stride + it.k0 + tok;
+      }
+      const int64_t off = (row * a.hkv + kvh) * D + col * 8;
+      if (valid) {
+        // KV is read once per step: non-temporal loads on both tiers
+        kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
+        vreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
+      } else {
+        kreg[c] = u32x4{0u, 0u, 0u, 0u};
+        vreg[c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  int i = jt;
+  DItem it{};
+  int32_t pte[NC] = {};
+  if (i < n_items) {
+    it = item_at(L, B, host_role, i);
+    if (PAGED) lookup(it, 0, pte);
+    load_tile(it, 0, pte);
+  }
+  bool run_open = false;  // fused: online-softmax state carries a run of sequence run_b
+  int run_b = -1, run_items = 0;
+  float m_run = -INFINITY;  // per lane: state of head (n & 7)
+  float l_run = 0.f;
+  float acc[G][DPL];
+  bf16x8_t qb[KS];
+  while (i < n_items) {
+    ++units_done;
+    const int ntiles = (it.n_tok + kTile - 1) / kTile;
+    if (!run_open) {
+      if (q_b != it.b) rotate_q(it.b);
+      // query operand: columns h (high bf16 part) and h+8 (low part)
+      const int hsel = n & 7;
+      const bool active = hsel < G;
+      const float* qr = &q_lds[active ? hsel : 0][0];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const floatx4 lo4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8);
+        const floatx4 hi4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8 + 4);
+        const float x8[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = active ? x8[2 * e] : 0.f;
+          const float x1 = active ? x8[2 * e + 1] : 0.f;
+          uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
+          if (n >= 8) {  // low part: residual after the high part
+            b0 = f32_to_bf16(x0 - bf16_to_f32(b0));
+            b1 = f32_to_bf16(x1 - bf16_to_f32(b1));
+          }
+          w[e] = b0 | (b1 << 16);
+        }
+        u32x4 wv = {w[0], w[1], w[2], w[3]};
+        qb[ks] = __builtin_bit_cast(bf16x8_t, wv);
+      }
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+      run_open = true;
+      run_b = it.b;
+      run_items = 0;
+    }
+
+    int next_i = n_items;
+    DItem nit{};
+    for (int tile = 0; tile < ntiles; ++tile) {
+      __syncthreads();  // previous tile's readers are done
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int r = chunk / S::kChunksPerRow;
+        const int col = chunk - r * S::kChunksPerRow;
+        *reinterpret_cast<u32x4*>(k_lds + r * S::kPitch + col * 16) = kreg[c];
+        *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
+      }
+      const bool last = tile + 1 == ntiles;
+      if (last && tid == 0) s_next = team + atomicAdd(qctr, 1);
+      __syncthreads();
+      // keep one tile in flight: the next tile of this item, or the first
+      // tile of the next item while this item's last tile is computed
+      if (!last) {
+        if (PAGED) lookup(it, tile + 1, pte);
+        load_tile(it, tile + 1, pte);
+      } else {
+        next_i = __builtin_amdgcn_readfirstlane(s_next);
+        if (next_i < n_items) {
+          nit = item_at(L, B, host_role, next_i);
+          if (PAGED) lookup(nit, 0, pte);
+          load_tile(nit, 0, pte);
+        }
+      }
+
+      // ---- scores for this wave's 16 tokens: rows = tokens, columns = heads
+      floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = k_lds + (wave * 16 + n) * S::kPitch + j4 * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + ks * 64);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qb[ks], sc, 0, 0, 0);
+      }
+      const int tok0 = tile * kTile + wave * 16 + j4 * 4;
+      float s[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = sc[q] + __shfl_xor(sc[q], 8);
+        s[q] = (tok0 + q < it.n_tok) ? v : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p[q] = (s[q] == -INFINITY) ? 0.f : exp2f(s[q] - m_new);
+        ps += p[q];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      if (n < G) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p_lds[wave][j4 * 4 + q][n] = p[q];
+        if (j4 == 0) a_lds[wave][n] = alpha;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- P.V: lane owns dims lane*DPL .. lane*DPL+DPL-1
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = a_lds[wave][h];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
+      }
+      const uint8_t* vbase = v_lds + (wave * 16) * S::kPitch + lane * DPL * 2;
+#pragma unroll 4
+      for (int t = 0; t < 16; ++t) {
+        float vv[DPL];
+        if (DPL == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vbase + t * S::kPitch);
+          vv[0] = __uint_as_float(w << 16);
+          vv[DPL - 1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint16_t*>(vbase + t * S::kPitch);
+          vv[0] = __uint_as_float(w << 16);
+        }
+        float pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pp[h] = p_lds[wave][t][h];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pp[h], vv[e], acc[h][e]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    ++run_items;
+
+    // ---- end of an item (split form) or of a run (fused form): combine the
+    // four waves and write the partial
+    const bool flush = !FUSED || next_i >= n_items || nit.b != run_b;
+    if (flush) {
+      __syncthreads();
+      float* sm_m = reinterpret_cast<float*>(k_lds);   // [4][G]
+      float* sm_l = sm_m + 4 * G;                      // [4][G]
+      float* sm_acc = sm_l + 4 * G;                    // [4][G][D]
+      if (lane < G) {
+        sm_m[wave * G + lane] = m_run;
+        sm_l[wave * G + lane] = l_run;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) sm_acc[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
+      __syncthreads();
+      for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * G + h]);
+        float o = 0.f, lsum = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float mw = sm_m[w * G + h];
+            const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            lsum += sw * sm_l[w * G + h];
+            o += sw * sm_acc[(w * G + h) * D + d];
+          }
+          o = o / lsum;
+        }
+        const float lse = (M == -INFINITY) ? -INFINITY : (M + log2f(lsum)) * 0.69314718055994530942f;
+        if (FUSED) {
+          o_lds[h][d] = o;
+          if (d == 0) l_lds[h] = lse;
+        } else {
+          const int hq_idx = kvh * G + h;
+          a.part_o[((size_t)it.slot * a.hq + hq_idx) * D + d] = o;
+          if (d == 0) a.part_lse[(size_t)it.slot * a.hq + hq_idx] = lse;
+        }
+      }
+      if (FUSED) {
+        __syncthreads();
+        flush_run(run_b, run_items);
+      }
+      run_open = false;
+    }
+    // the next item's first tile is already in registers
+    i = next_i;
+    it = nit;
+  }
+
+  // Fused form: groups with nothing to merge (no tokens and no appended token).
+  if (FUSED && !a.new_tokens && blockIdx.x == 0) {
+    for (int b = 0; b < B; ++b)
+      if (L.ph[b + 1] == L.ph[b] && L.pm[b + 1] == L.pm[b] && L.pt[b + 1] == L.pt[b])
+        for (int idx = tid; idx < a.hq * D; idx += kThreads) {
+          a.out_o[(size_t)b * a.hq * D + idx] = 0.f;
+          if (idx < a.hq && a.out_lse) a.out_lse[(size_t)b * a.hq + idx] = -INFINITY;
+        }
+  }
+
+  // Last workgroup out clears the item queues for the next call on this workspace.
+  __syncthreads();
+  if (tid == 0) {
+    wait_stores();
+    const int ec = decode_exit_counter(a.hkv);
+    const int done = atomicAdd(&a.counters[ec], 1) + 1;
+    if (done == (int)gridDim.x) {
+      for (int k = 0; k < 2 * a.hkv; ++k)
+        __hip_atomic_store(&a.counters[k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.counters[ec], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (traced) {
+    uint64_t* t = a.wg_trace + 4 * (size_t)blockIdx.x;
+    t[0] = t_start;
+    t[1] = wall_clock64();
+    t[2] = host_role ? 1 : 0;
+    t[3] = (uint64_t)units_done;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+int launch_decode_tiers(const DecodeArgs& a, int32_t* tier_counts, int32_t* tier_pages, void* stream) {
+  if (a.batch < 1) return (int)hipSuccess;
+  hipLaunchKernelGGL(decode_tiers_kernel, dim3(a.batch), dim3(kTierThreads), 0, (hipStream_t)stream, a,
+                     tier_counts, tier_pages);
+  return (int)hipGetLastError();
+}
+
+template <int D, int G, bool FUSED>
+static hipError_t launch_decode_dgf(const DecodeArgs& a, hipStream_t s) {
+  const int grid = a.hkv * (a.tmpl.team_h + a.tmpl.team_d);
+  if (grid < 1) return hipErrorInvalidValue;
+  if (a.page_shift >= 0)
+    hipLaunchKernelGGL((decode_kernel<D, G, true, FUSED>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G, false, FUSED>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t s) {
+  return a.fused ? launch_decode_dgf<D, G, true>(a, s) : launch_decode_dgf<D, G, false>(a, s);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: return launch_decode_dg<D, 1>(a, s);
+    case 2: return launch_decode_dg<D, 2>(a, s);
+    case 4: return launch_decode_dg<D, 4>(a, s);
+    case 8: return launch_decode_dg<D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.head_dim == 64) return (int)launch_decode_d<64>(a, s);
+  if (a.head_dim == 128) return (int)launch_decode_d<128>(a, s);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace dkv

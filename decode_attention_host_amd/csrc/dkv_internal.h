@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "dkv.h"
+#include "dkv_decomp.h"
 
 namespace dkv {
 
@@ -22,18 +23,6 @@ struct RopeFreq {
 constexpr int kTile = 64;
 // Threads per attention / merge / append workgroup.
 constexpr int kThreads = 256;
-
-// One work item: a run of tokens of one sequence that all live in one tier.
-// The attention kernel processes every item once per KV head ("unit").
-struct PlanItem {
-  int32_t b;      // sequence
-  int32_t slot;   // split slot (row of part_o / part_lse)
-  int32_t n_tok;  // tokens in the item (>= 1)
-  int32_t plist;  // paged: index of the item's first entry in the page list
-  int64_t row0;   // contiguous: pool row of the item's first token
-  int64_t pad;
-};
-static_assert(sizeof(PlanItem) == 32, "PlanItem layout");
 
 // Query-head rows per prefill workgroup: 4 waves x 32 rows (two 16-column
 // MFMA tiles each).  A row block holds kPrefillRows / G query rows.
@@ -132,43 +121,66 @@ struct PlanLayout {
   size_t seqlens_off = 0;        // prefill: cached lengths [B] (device copy)
 };
 
-// Arguments of the split attention kernel.
-struct AttnArgs {
-  const PlanItem* host_items;
-  const PlanItem* dev_items;
-  const int32_t* plist;          // paged: logical page indices
-  const int32_t* plan_offsets;   // [batch+1] split offsets (in the workspace)
-  int32_t* unit_counters;        // [2] dynamic unit counters (HBM, host), zero at launch
-  int32_t* split_offsets;        // [batch+1] caller copy (written by block 0), or NULL
-  int32_t n_host_units;          // host items x Hkv
-  int32_t n_dev_units;           // dev items x Hkv
-  int32_t host_wgs;
-  int32_t dev_wgs;
-  const uint16_t* host_k;
-  const uint16_t* host_v;
-  const uint16_t* dev_k;
-  const uint16_t* dev_v;
+// Arguments of the decode kernel (dkv_decode.hip).  Every work item is
+// derived in the kernel from the lengths in device memory (dkv_decomp.h).
+struct DecodeArgs {
+  // tiers
+  uint16_t* host_k;              // mapped host-pinned pools (device addresses)
+  uint16_t* host_v;
+  uint16_t* dev_k;               // HBM pools
+  uint16_t* dev_v;
   int64_t host_rows;
   int64_t dev_rows;
-  const int32_t* page_table;
+  int64_t host_stride;           // contiguous layout: rows per sequence
+  int64_t dev_stride;
+  const int32_t* page_table;     // paged layout: [batch][max_pages]
   int32_t max_pages;
-  int32_t page_shift;            // log2(page_size) (paged)
-  const uint16_t* q;             // [batch][Hq][D]
+  int32_t page_shift;            // log2(page size), -1 for the contiguous layout
+  // the call
+  const uint16_t* q;             // [batch][Hq][D] bf16
   const int32_t* q_pos;          // [batch]
+  const int32_t* seq_lens;       // [batch] cached tokens attended (device)
   int32_t batch;
   int32_t hq;
   int32_t hkv;
   int32_t head_dim;
+  double ratio;                  // contiguous: offload ratio
   float scale_log2;              // scale * log2(e)
-  float pad0;
-  double theta;
+  int32_t fused;                 // 1: merge in the kernel (last finisher per sequence and KV head)
+  DecodeTemplate tmpl;
+  // workspace
+  int32_t* counters;             // [2 Hkv] item queues (host heads, then HBM heads), exit count, error flags
+  int32_t* group_cnt;            // fused: [batch * Hkv][2] items done, partials written
+  const int32_t* tier_counts;    // paged: [batch][4] host pages, HBM pages, host tokens, HBM tokens
+  const int32_t* tier_pages;     // paged: [2][batch][max_pages] physical pages, host tier then HBM
+  // split form: one normalised partial per item
   float* part_o;                 // [S][Hq][D]
   float* part_lse;               // [S][Hq]
-  uint64_t* wg_trace;            // optional [grid][4]: start, end, role, units (wall clock)
+  int32_t* split_offsets;        // [batch + 1] (written by workgroup 0)
+  // fused form
+  float* run_o;                  // [batch * Hkv][max_slots][G][D] partials of workgroup runs
+  float* run_lse;                // [batch * Hkv][max_slots][G]
+  int32_t max_slots;
+  int32_t new_tokens;            // 1: each sequence first appends a token at pos_new[b]
+  float* out_o;                  // [batch][Hq][D]
+  float* out_lse;                // [batch][Hq] or NULL
+  const int32_t* pos_new;        // [batch] position of the appended token (NULL: seq_lens[b])
+  const uint16_t* k_new;         // [batch][Hkv][D] bf16, or NULL with kv_proj
+  const uint16_t* v_new;
+  const float* kv_proj;          // [batch][2 Hkv D] fp32 projection (K then V), or NULL
+  uint64_t* wg_trace;            // optional [grid][4]: start, end, role, items (wall clock)
   int32_t wg_trace_cap;
   int32_t pad1;
   RopeFreq freq;                 // f_i = theta^(-2i/D), i < D/2
 };
+
+// Counter words of the decode workspace (int32 offsets from `counters`).
+DKV_HD constexpr int decode_exit_counter(int hkv) { return 2 * hkv; }
+DKV_HD constexpr int decode_error_word(int hkv) { return 2 * hkv + 1; }
+constexpr int kDecodeErrLayout = 1;     // a contiguous sequence's rows exceed its stride or pool
+constexpr int kDecodeErrPage = 2;       // a page entry is negative or beyond its tier's pool
+constexpr int kDecodeErrSlot = 4;       // an appended token has no valid cache slot
+constexpr int kDecodeErrCapacity = 8;   // a partial slot beyond the workspace (never expected)
 
 struct MergeArgs {
   const float* part_o;
@@ -298,7 +310,10 @@ struct StageArgs {
 };
 
 // Launchers (dkv_kernels.hip).  They return hipError_t as int.
-int launch_attn(const AttnArgs& a, void* stream);
+// Decode: the paged layout's per-sequence tier lists and counts, then the
+// decode kernel (grid = Hkv * (team_h + team_d)).
+int launch_decode_tiers(const DecodeArgs& a, int32_t* tier_counts, int32_t* tier_pages, void* stream);
+int launch_decode(const DecodeArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
 // (cos, sin) in fp64 of the rotation angles of every prefill row:
@@ -346,9 +361,29 @@ struct PlanInput {
   int32_t prefill_fresh;          // prefill: new rows read from the fresh pool
 };
 
-// Builds the plan and its device image; on failure returns false with `err`.
-bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
-                std::string* err);
+// Decode launch shape (dkv_plan.cpp): workgroups per tier and KV head and the
+// item-length rules; host_tier / dev_tier say which tiers can hold tokens and
+// host_frac the expected host share of them.  No sequence lengths involved.
+DecodeTemplate decode_template(const PlanInput& in, bool host_tier, bool dev_tier, double host_frac);
+
+// Host twin of decode_tiers_kernel for one sequence (plan introspection):
+// the logical pages of each tier in order (the kernel lists their physical
+// pages) and the tokens each tier holds among the first `attended`; false when
+// an entry was left out.
+bool decode_tiers_host(const PlanInput& in, int64_t b, int64_t attended, std::vector<int32_t>* host_pages,
+                       std::vector<int32_t>* dev_pages, int64_t* nh, int64_t* nd);
+
+// Every item of a call in queue order (host items, HBM items, HBM tail items)
+// and the split offsets [B+1], from each sequence's tier tokens.
+struct DecodeHostItem {
+  int32_t host;   // 1 host tier, 0 HBM
+  int32_t b;
+  int32_t slot;
+  int32_t n_tok;
+  int64_t k0;     // first ordinal in the tier
+};
+void decode_enumerate(const DecodeTemplate& t, int B, const int64_t* nh, const int64_t* nd,
+                      std::vector<DecodeHostItem>* items, std::vector<int32_t>* offsets, DecodeSizes* z);
 
 // Prefill plan: query rows of sequence b are q_start[b] .. q_start[b+1]-1,
 // row j of b at position q_pos0[b] + j; in.seq_lens are the cached lengths.

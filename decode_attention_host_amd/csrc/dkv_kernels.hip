@@ -42,43 +42,9 @@
 #include <algorithm>
 
 #include "dkv_internal.h"
+#include "dkv_device.h"
 
 namespace dkv {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// float -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// double -> bf16 bits with one rounding (nearest, ties to even).
-__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
-  uint64_t u = (uint64_t)__double_as_longlong(x);
-  const uint32_t sign = (uint32_t)(u >> 63) << 15;
-  const int e = (int)((u >> 52) & 0x7ff);
-  if (e == 0x7ff) return sign | ((u << 12) ? 0x7fc0u : 0x7f80u);
-  const double ax = fabs(x);
-  if (ax < 0x1p-126) {
-    // subnormal bf16 grid: quantum 2^-133
-    const double q = rint(ax * 0x1p133);  // 0 .. 128 (128 = smallest normal)
-    return sign | (uint32_t)q;
-  }
-  const uint64_t mant = u & ((1ull << 52) - 1);
-  uint64_t keep = mant >> 45;
-  const uint64_t rest = mant & ((1ull << 45) - 1);
-  const uint64_t half = 1ull << 44;
-  uint32_t em = (uint32_t)((e - 1023 + 127) << 7) | (uint32_t)keep;
-  if (rest > half || (rest == half && (keep & 1))) em += 1;  // may carry into the exponent
-  if (em >= 0x7f80u) em = 0x7f80u;                           // overflow -> inf
-  return sign | em;
-}
 
 // (cos, sin) of every prefill row's rotation angles, fp64, computed once per
 // call; the prefill kernel rotates its query columns with them.
@@ -96,361 +62,6 @@ __global__ __launch_bounds__(kThreads) void rope_table_kernel(const int32_t* __r
     double sn, c;
     sincos((double)rowpos[row] * freq.f[i], &sn, &c);
     cs[idx] = make_double2(c, sn);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split decode attention.
-// ---------------------------------------------------------------------------
-template <int D>
-struct AttnShape {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kPitch = kRowBytes + 16;          // LDS row pitch (bytes)
-  static constexpr int kChunksPerRow = D / 8;            // 16-byte chunks per row
-  static constexpr int kChunksPerThread = kTile * kChunksPerRow / kThreads;  // D/32
-  static constexpr int kKSteps = D / 32;                 // MFMA k-steps per key
-  static constexpr int kDimsPerLane = D / 64;            // P.V output dims per lane
-};
-
-// A plan item read through the scalar cache (constant address space): the
-// fields land in SGPRs, so taking them over as the current item waits for
-// this load alone and not for the tile loads issued after it.
-__device__ __forceinline__ PlanItem load_plan_item_uniform(const PlanItem* p) {
-  static_assert(sizeof(PlanItem) == 32, "item size");
-  typedef __attribute__((address_space(4))) const u32x4 ConstVec;
-  const ConstVec* w = (const ConstVec*)p;
-  struct Raw {
-    u32x4 v[2];
-  } t;
-  t.v[0] = w[0];
-  t.v[1] = w[1];
-  return __builtin_bit_cast(PlanItem, t);
-}
-
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
-  using S = AttnShape<D>;
-  constexpr int NC = S::kChunksPerThread;
-  constexpr int KS = S::kKSteps;
-  constexpr int DPL = S::kDimsPerLane;
-  static_assert(G >= 1 && G <= 8, "group size");
-  // per-wave state dump at the end of a unit must fit in the K tile buffer
-  static_assert(4 * G * (D + 2) * 4 <= kTile * S::kPitch, "epilogue scratch");
-
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * S::kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
-  __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
-  __shared__ float a_lds[4][8];
-  __shared__ __attribute__((aligned(16))) float q_lds[G][D];  // the unit's rotated query heads
-  __shared__ int s_next;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 15;     // MFMA column / row-in-tile
-  const int j4 = lane >> 4;    // 0..3
-
-  if (blockIdx.x == 0 && a.split_offsets)
-    for (int i = tid; i <= a.batch; i += kThreads) a.split_offsets[i] = a.plan_offsets[i];
-
-  // Role: the first host_wgs workgroups stream the host tier, the rest HBM.
-  const bool host_role = (int)blockIdx.x < a.host_wgs;
-  const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
-  const int nwg = host_role ? a.host_wgs : a.dev_wgs;
-  const int nunits = host_role ? a.n_host_units : a.n_dev_units;
-  const PlanItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
-  const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
-  const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
-  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
-  // Units [0, nwg) go to workgroups by index; each later unit goes to the
-  // workgroup that finishes first (per-role counter, zeroed by the plan upload).
-  int* counter = a.unit_counters + (host_role ? 1 : 0);
-
-  const bool traced = a.wg_trace && (int)blockIdx.x < a.wg_trace_cap && tid == 0;
-  const uint64_t t_start = traced ? wall_clock64() : 0;
-  int units_done = 0;
-
-  u32x4 kreg[NC], vreg[NC];
-  // Paged: the page-table entries of a tile's chunks.  Every page-list entry
-  // is loaded, then every page-table entry (tokens past the item look up its
-  // last token's page, so every lookup is in bounds and none waits for a
-  // select on its result).  Chunk c covers rows [c*RPC, (c+1)*RPC) of the
-  // tile; with pages of at least RPC rows those rows share one page, the
-  // lookups are workgroup-uniform and go through the scalar cache, where
-  // neighbouring entries share lines (1M tokens in HBM, permuted 16-token
-  // pages: 0.92 ms against 0.99 ms with vector lookups; looking one tile
-  // further ahead than the loads measured no faster).
-  auto lookup = [&](const PlanItem& it, int tile, int32_t* pte) {
-    constexpr int RPC = kThreads / S::kChunksPerRow;
-    if ((1 << a.page_shift) >= RPC) {
-      typedef __attribute__((address_space(4))) const int32_t ConstInt;
-      const ConstInt* pl = (const ConstInt*)(a.plist + it.plist);
-      const ConstInt* ptab = (const ConstInt*)(a.page_table + (int64_t)it.b * a.max_pages);
-      int lp[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) lp[c] = pl[min(tile * kTile + c * RPC, it.n_tok - 1) >> a.page_shift];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) pte[c] = ptab[lp[c]];
-    } else {
-      int lp[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int tok = min(tile * kTile + (tid + c * kThreads) / S::kChunksPerRow, it.n_tok - 1);
-        lp[c] = a.plist[it.plist + (tok >> a.page_shift)];
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) pte[c] = a.page_table[(int64_t)it.b * a.max_pages + lp[c]];
-    }
-  };
-  auto load_tile = [&](const PlanItem& it, int kvh, int tile, const int32_t* pte) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int r = chunk / S::kChunksPerRow;
-      const int col = chunk - r * S::kChunksPerRow;
-      const int tok = tile * kTile + r;
-      bool valid = tok < it.n_tok;
-      int64_t row = 0;
-      if (PAGED) {
-        const int32_t e = pte[c];
-        const int64_t phys = (int64_t)(e >> 1);
-        row = (phys << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
-        valid = valid && e >= 0 && ((e & 1) != 0) == host_role && row < cap_rows;
-      } else {
-        row = it.row0 + tok;
-      }
-      const int64_t off = (row * a.hkv + kvh) * D + col * 8;
-      if (valid) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(kpool + off);
-        const u32x4* vp = reinterpret_cast<const u32x4*>(vpool + off);
-        // KV is read once per step: non-temporal loads on both tiers (on
-        // MI355X they also stream HBM faster than ordinary loads)
-        kreg[c] = __builtin_nontemporal_load(kp);
-        vreg[c] = __builtin_nontemporal_load(vp);
-      } else {
-        kreg[c] = u32x4{0u, 0u, 0u, 0u};
-        vreg[c] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-
-  int u = wg;
-  PlanItem it{};
-  int kvh = 0;
-  int32_t pte[NC] = {};
-  if (u < nunits) {
-    it = items[u / a.hkv];
-    kvh = u - (u / a.hkv) * a.hkv;
-    if (PAGED) lookup(it, 0, pte);
-    load_tile(it, kvh, 0, pte);
-  }
-  while (u < nunits) {
-    ++units_done;
-    const int ntiles = (it.n_tok + kTile - 1) / kTile;
-
-    // ---- the unit's G query heads rotated at q_pos[b] (Neox pairs i, i + D/2;
-    // angle pos * f_i, sin and cos in fp64; rounded once to fp32 with
-    // scale * log2(e) folded in), one pair per thread, staged in LDS.  The
-    // previous unit's readers of q_lds passed several barriers since.
-    {
-      const int pos = a.q_pos[it.b];
-      const uint16_t* qh = a.q + ((size_t)it.b * a.hq + (size_t)kvh * G) * D;
-      for (int idx = tid; idx < G * (D / 2); idx += kThreads) {
-        const int h = idx / (D / 2), i = idx - h * (D / 2);
-        double sn, cs;
-        sincos((double)pos * a.freq.f[i], &sn, &cs);
-        const double xl = (double)bf16_to_f32(qh[h * D + i]);
-        const double xh = (double)bf16_to_f32(qh[h * D + i + D / 2]);
-        q_lds[h][i] = (float)(xl * cs - xh * sn) * a.scale_log2;
-        q_lds[h][i + D / 2] = (float)(xh * cs + xl * sn) * a.scale_log2;
-      }
-      __syncthreads();
-    }
-    // ---- query operand: columns h (high bf16 part) and h+8 (low part)
-    bf16x8_t qb[KS];
-    {
-      const int hsel = n & 7;
-      const bool active = hsel < G;
-      const float* qr = &q_lds[active ? hsel : 0][0];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const floatx4 lo4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8);
-        const floatx4 hi4 = *reinterpret_cast<const floatx4*>(qr + ks * 32 + j4 * 8 + 4);
-        const float x8[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = active ? x8[2 * e] : 0.f;
-          const float x1 = active ? x8[2 * e + 1] : 0.f;
-          uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
-          if (n >= 8) {  // low part: residual after the high part
-            b0 = f32_to_bf16(x0 - bf16_to_f32(b0));
-            b1 = f32_to_bf16(x1 - bf16_to_f32(b1));
-          }
-          w[e] = b0 | (b1 << 16);
-        }
-        u32x4 wv = {w[0], w[1], w[2], w[3]};
-        qb[ks] = __builtin_bit_cast(bf16x8_t, wv);
-      }
-    }
-
-    float m_run = -INFINITY;  // per lane: state of head (n & 7)
-    float l_run = 0.f;
-    float acc[G][DPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-
-    int next_u = nunits;
-    PlanItem nit{};
-    int nkvh = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-      __syncthreads();  // previous tile's readers are done
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int r = chunk / S::kChunksPerRow;
-        const int col = chunk - r * S::kChunksPerRow;
-        *reinterpret_cast<u32x4*>(k_lds + r * S::kPitch + col * 16) = kreg[c];
-        *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
-      }
-      const bool last = tile + 1 == ntiles;
-      if (last && tid == 0) s_next = nwg + atomicAdd(counter, 1);
-      __syncthreads();
-      // keep one tile in flight: the next tile of this unit, or the first
-      // tile of the next unit while this unit's last tile is computed
-      if (!last) {
-        if (PAGED) lookup(it, tile + 1, pte);
-        load_tile(it, kvh, tile + 1, pte);
-      } else {
-        next_u = __builtin_amdgcn_readfirstlane(s_next);
-        if (next_u < nunits) {
-          nit = load_plan_item_uniform(items + next_u / a.hkv);
-          nkvh = next_u - (next_u / a.hkv) * a.hkv;
-          if (PAGED) lookup(nit, 0, pte);
-          load_tile(nit, nkvh, 0, pte);
-        }
-      }
-
-
-      // ---- scores for this wave's 16 tokens: rows = tokens, columns = heads
-      floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = k_lds + (wave * 16 + n) * S::kPitch + j4 * 16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + ks * 64);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qb[ks], sc,
-                                                     0, 0, 0);
-      }
-      const int tok0 = tile * kTile + wave * 16 + j4 * 4;
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = sc[i] + __shfl_xor(sc[i], 8);
-        s[i] = (tok0 + i < it.n_tok) ? v : -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-      float p[4], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = (s[i] == -INFINITY) ? 0.f : exp2f(s[i] - m_new);
-        ps += p[i];
-      }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      if (n < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p_lds[wave][j4 * 4 + i][n] = p[i];
-        if (j4 == 0) a_lds[wave][n] = alpha;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-      // ---- P.V: lane owns dims lane*DPL .. lane*DPL+DPL-1
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = a_lds[wave][h];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
-      }
-      const uint8_t* vbase = v_lds + (wave * 16) * S::kPitch + lane * DPL * 2;
-#pragma unroll 4
-      for (int t = 0; t < 16; ++t) {
-        float vv[DPL];
-        if (DPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(vbase + t * S::kPitch);
-          vv[0] = __uint_as_float(w << 16);
-          vv[DPL - 1] = __uint_as_float(w & 0xffff0000u);
-        } else {
-          const uint32_t w = *reinterpret_cast<const uint16_t*>(vbase + t * S::kPitch);
-          vv[0] = __uint_as_float(w << 16);
-        }
-        float pp[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pp[h] = p_lds[wave][t][h];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pp[h], vv[e], acc[h][e]);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-
-    // ---- combine the four waves of this unit and write the partial
-    __syncthreads();
-    float* sm_m = reinterpret_cast<float*>(k_lds);   // [4][G]
-    float* sm_l = sm_m + 4 * G;                      // [4][G]
-    float* sm_acc = sm_l + 4 * G;                    // [4][G][D]
-    if (lane < G) {
-      sm_m[wave * G + lane] = m_run;
-      sm_l[wave * G + lane] = l_run;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) sm_acc[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int h = idx / D, d = idx - h * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * G + h]);
-      float o = 0.f, lsum = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float mw = sm_m[w * G + h];
-          const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-          lsum += sw * sm_l[w * G + h];
-          o += sw * sm_acc[(w * G + h) * D + d];
-        }
-        o = o / lsum;
-      }
-      const int hq_idx = kvh * G + h;
-      a.part_o[((size_t)it.slot * a.hq + hq_idx) * D + d] = o;
-      if (d == 0)
-        a.part_lse[(size_t)it.slot * a.hq + hq_idx] =
-            (M == -INFINITY) ? -INFINITY : (M + log2f(lsum)) * 0.69314718055994530942f;
-    }
-    // the next unit's first tile is already in registers
-    u = next_u;
-    it = nit;
-    kvh = nkvh;
-  }
-  if (traced) {
-    uint64_t* t = a.wg_trace + 4 * (size_t)blockIdx.x;
-    t[0] = t_start;
-    t[1] = wall_clock64();
-    t[2] = host_role ? 1 : 0;
-    t[3] = (uint64_t)units_done;
   }
 }
 
@@ -1704,35 +1315,6 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __res
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int G>
-static hipError_t launch_attn_dg(const AttnArgs& a, hipStream_t s) {
-  // at least one workgroup: block 0 also writes the caller's split offsets
-  const int grid = std::max(1, a.host_wgs + a.dev_wgs);
-  if (a.page_shift >= 0 && a.page_table)
-    hipLaunchKernelGGL((attn_split_kernel<D, G, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
-  switch (a.hq / a.hkv) {
-    case 1: return launch_attn_dg<D, 1>(a, s);
-    case 2: return launch_attn_dg<D, 2>(a, s);
-    case 4: return launch_attn_dg<D, 4>(a, s);
-    case 8: return launch_attn_dg<D, 8>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-int launch_attn(const AttnArgs& a, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (a.head_dim == 64) return (int)launch_attn_d<64>(a, s);
-  if (a.head_dim == 128) return (int)launch_attn_d<128>(a, s);
-  return (int)hipErrorInvalidValue;
-}
-
 template <int D, int G>
 static hipError_t launch_prefill_dg(const PrefillArgs& a, hipStream_t s) {
   const int grid = a.writer_wgs + a.host_wgs + a.dev_wgs;

@@ -76,163 +76,109 @@ void split_workgroups(const PlanInput& in, int64_t host_units, int64_t dev_units
 
 }  // namespace
 
-bool build_plan(const PlanInput& in, PlanLayout* out, std::vector<uint8_t>* blob,
-                std::string* err) {
-  *out = PlanLayout{};
-  const int B = in.batch;
-  if (B < 1) return fail(err, "batch must be >= 1 (got %lld)", B);
-  if (!in.seq_lens) return fail(err, "seq_lens is NULL");
-  const bool paged = in.page_size > 0;
-  const int64_t P = paged ? in.page_size : 1;
-  const int64_t row_bytes = (int64_t)in.hkv * in.head_dim * 2;
-
-  // ---- tokens per tier per sequence
-  std::vector<int64_t> n_host(B), n_dev(B);
-  std::vector<std::vector<int32_t>> host_pages(paged ? B : 0), dev_pages(paged ? B : 0);
-  int64_t host_tok = 0, dev_tok = 0;
-  for (int b = 0; b < B; ++b) {
-    const int64_t L = in.seq_lens[b];
-    if (L < 1) return fail(err, "seq_lens[%lld] = %lld: every sequence needs >= 1 token", b, L);
-    if (!paged) {
-      const int64_t nh = (int64_t)std::floor(in.ratio * (double)L);
-      n_host[b] = nh;
-      n_dev[b] = L - nh;
-      if (nh > 0 && (nh > in.host_stride || (int64_t)b * in.host_stride + nh > in.host_rows))
-        return fail(err, "sequence %lld: host rows needed beyond host_stride/host_rows (n_host %lld)",
-                    b, nh);
-      if (L - nh > 0 &&
-          (L - nh > in.dev_stride || (int64_t)b * in.dev_stride + (L - nh) > in.dev_rows))
-        return fail(err, "sequence %lld: device rows needed beyond dev_stride/dev_rows (n_dev %lld)",
-                    b, L - nh);
-    } else {
-      if (!in.page_table_host) return fail(err, "paged layout needs page_table_host");
-      const int64_t npg = ceil_div(L, P);
-      if (npg > in.max_pages)
-        return fail(err, "sequence %lld needs %lld pages > max_pages %lld", b, npg, in.max_pages);
-      int64_t nh = 0, nd = 0;
-      for (int64_t j = 0; j < npg; ++j) {
-        const int32_t e = in.page_table_host[(int64_t)b * in.max_pages + j];
-        if (e < 0) return fail(err, "page_table[%lld][%lld] = %lld is negative", b, j, e);
-        const int64_t phys = (int64_t)(e >> 1);
-        const int64_t ntok = (j == npg - 1) ? L - j * P : P;
-        const bool host = (e & 1) != 0;
-        const int64_t cap = host ? in.host_rows : in.dev_rows;
-        if ((phys + 1) * P > cap)
-          return fail(err, "page_table[%lld][%lld]: page %lld beyond its tier's pool", b, j, phys);
-        (host ? host_pages[b] : dev_pages[b]).push_back((int32_t)j);
-        (host ? nh : nd) += ntok;
-      }
-      n_host[b] = nh;
-      n_dev[b] = nd;
-    }
-    if (n_host[b] > 0 && (!in.host_rows)) return fail(err, "host tier used but host_rows is 0");
-    if (n_dev[b] > 0 && (!in.dev_rows)) return fail(err, "device tier used but dev_rows is 0");
-    host_tok += n_host[b];
-    dev_tok += n_dev[b];
-  }
-
-  // ---- workgroup split between tiers
+// ---------------------------------------------------------------- decode
+//
+// The decode kernel derives its items on the device (dkv_decomp.h); the host
+// only fixes the shape of the launch: workgroups per tier and per KV head, and
+// the item-length rules.  Nothing here depends on the sequence lengths.
+DecodeTemplate decode_template(const PlanInput& in, bool host_tier, bool dev_tier, double host_frac) {
+  DecodeTemplate t{};
+  t.hkv = std::max(1, in.hkv);
+  const int32_t cus = std::max(1, in.num_cus);
+  const int32_t resident = cus * kSlotsPerCu;
+  // the same workgroup split as the other split kernels, with an expected
+  // host share in place of the byte counts
   int32_t wh = 0, wd = 0;
-  split_workgroups(in, host_tok, dev_tok, &wh, &wd);
+  const double f = std::min(1.0, std::max(0.0, host_frac));
+  split_workgroups(in, host_tier ? (int64_t)std::llround(f * 1e9) : 0,
+                   dev_tier ? (int64_t)std::llround((1.0 - f) * 1e9) : 0, &wh, &wd);
+  if (host_tier && wh < 1) wh = 1;
+  if (dev_tier && wd < 1) wd = 1;
+  t.team_h = host_tier ? (int32_t)ceil_div(wh, t.hkv) : 0;
+  t.team_d = dev_tier ? (int32_t)std::max<int64_t>(1, (in.dev_wgs > 0 ? ceil_div(wd, t.hkv)
+                                                                        : (resident - t.team_h * t.hkv) / t.hkv))
+                      : 0;
+  const bool mixed = host_tier && dev_tier;
+  t.upw_h = mixed ? 4 : 2;
+  t.upw_d = 6;
+  // host items as short as one tile when the tier is small (a PCIe round trip
+  // per tile: many short items in flight beat a few long ones); HBM items of
+  // at least 512 tokens (the 32k-token layer from HBM: 0.032 ms as 512-token
+  // units against 0.038 ms as 1024-token units on MI355X)
+  t.floor_h = kTile;
+  t.floor_d = 512;
+  t.align = (int32_t)std::max<int64_t>(kTile, in.page_size > 0 ? in.page_size : 1);
+  t.guided = 1;
+  t.tuned_h = in.host_chunk > 0 ? (int32_t)round_up(in.host_chunk, t.align) : 0;
+  t.tuned_d = in.dev_chunk > 0 ? (int32_t)round_up(in.dev_chunk, t.align) : 0;
+  return t;
+}
 
-  const int32_t align = (int32_t)std::max<int64_t>(kTile, P);
-  const bool mixed = host_tok > 0 && dev_tok > 0;
-  const int32_t ch = choose_chunk(host_tok * in.hkv, wh, mixed ? 4 : 2, 256, 16384, align, in.host_chunk);
-  // HBM units of >= 512 tokens: a 32k-token layer from HBM runs its kernel in
-  // 0.032 ms as 512 units of 512 against 0.038 ms as 256 units of 1024 on
-  // MI355X (the unit's fixed cost is one round trip for its query operand).
-  const int32_t cd = choose_chunk(dev_tok * in.hkv, wd, 6, 512, 1 << 16, align, in.dev_chunk);
-  // Guided tail for long HBM ranges: the last part of every sequence's HBM
-  // range is cut into quarter-size units that go to the end of the work list,
-  // about two per workgroup, so the workgroups run out of work nearly together
-  // (units of a few thousand tokens otherwise leave them finishing up to one
-  // unit apart).
-  const int64_t cs = round_up(cd / 4, align);
-  const bool guided = in.dev_chunk <= 0 && cs >= 512 && dev_tok * in.hkv >= (int64_t)cd * wd * 4;
-  const double tail_frac = guided ? std::min(0.5, 2.0 * wd * cs / ((double)dev_tok * in.hkv)) : 0.0;
-
-  // ---- items
-  std::vector<PlanItem> hitems, ditems, dtail;
-  std::vector<int32_t> plist;
-  std::vector<int32_t> offsets(B + 1, 0);
-  int32_t slot = 0;
-  for (int b = 0; b < B; ++b) {
-    offsets[b] = slot;
-    for (int tier = 1; tier >= 0; --tier) {
-      if (!paged) {
-        const int64_t nh = n_host[b];
-        const int64_t begin = tier ? 0 : nh;
-        const int64_t end = tier ? nh : (int64_t)in.seq_lens[b];
-        // tokens [split, end) of the HBM range form the guided tail
-        const int64_t split = tier ? end : end - ((int64_t)((end - begin) * tail_frac) / align) * align;
-        for (int64_t t0 = begin; t0 < end;) {
-          const bool tail = t0 >= split;
-          const int64_t chunk = tier ? ch : (tail ? cs : cd);
-          PlanItem it{};
-          it.b = b;
-          it.slot = slot++;
-          it.n_tok = (int32_t)std::min<int64_t>(chunk, (tail ? end : split) - t0);
-          it.plist = 0;
-          it.row0 = tier ? (int64_t)b * in.host_stride + t0 : (int64_t)b * in.dev_stride + (t0 - nh);
-          (tier ? hitems : (tail ? dtail : ditems)).push_back(it);
-          t0 += it.n_tok;
-        }
-      } else {
-        const std::vector<int32_t>& pages = tier ? host_pages[b] : dev_pages[b];
-        const int64_t L = in.seq_lens[b];
-        const size_t npg = pages.size();
-        const size_t split = tier ? npg : npg - (size_t)((double)npg * tail_frac) / (size_t)(align / P) *
-                                                  (size_t)(align / P);
-        for (size_t k0 = 0; k0 < npg;) {
-          const bool tail = k0 >= split;
-          const int64_t per = (tier ? ch : (tail ? cs : cd)) / P;
-          const size_t k1 = std::min(tail ? npg : split, k0 + (size_t)per);
-          int64_t ntok = 0;
-          for (size_t k = k0; k < k1; ++k) ntok += std::min<int64_t>(P, L - (int64_t)pages[k] * P);
-          PlanItem it{};
-          it.b = b;
-          it.slot = slot++;
-          it.n_tok = (int32_t)ntok;
-          it.plist = (int32_t)plist.size();
-          it.row0 = 0;
-          for (size_t k = k0; k < k1; ++k) plist.push_back(pages[k]);
-          (tier ? hitems : (tail ? dtail : ditems)).push_back(it);
-          k0 = k1;
-        }
-      }
+bool decode_tiers_host(const PlanInput& in, int64_t b, int64_t attended, std::vector<int32_t>* host_pages,
+                       std::vector<int32_t>* dev_pages, int64_t* nh, int64_t* nd) {
+  const int64_t P = in.page_size;
+  int64_t A = std::max<int64_t>(0, attended);
+  int64_t npg = ceil_div(A, P);
+  bool ok = true;
+  if (npg > in.max_pages) {
+    ok = false;
+    npg = in.max_pages;
+    A = npg * P;
+  }
+  host_pages->clear();
+  dev_pages->clear();
+  int last = -1;
+  for (int64_t j = 0; j < npg; ++j) {
+    const int32_t e = in.page_table_host[b * in.max_pages + j];
+    const bool host = (e & 1) != 0;
+    const int64_t cap = host ? (in.host_rows / P) : (in.dev_rows / P);
+    if (e < 0 || (int64_t)(e >> 1) >= cap) {
+      ok = false;
+      continue;
     }
+    (host ? host_pages : dev_pages)->push_back((int32_t)j);
+    if (j == npg - 1) last = host ? 1 : 0;
   }
-  offsets[B] = slot;
-  ditems.insert(ditems.end(), dtail.begin(), dtail.end());
+  const int64_t deficit = npg > 0 ? P - (A - (npg - 1) * P) : 0;
+  *nh = (int64_t)host_pages->size() * P - (last == 1 ? deficit : 0);
+  *nd = (int64_t)dev_pages->size() * P - (last == 0 ? deficit : 0);
+  return ok;
+}
 
-  out->n_host_items = (int32_t)hitems.size();
-  out->n_dev_items = (int32_t)ditems.size();
-  out->num_splits = slot;
-  out->batch = B;
-  out->host_wgs = hitems.empty() ? 0 : std::min<int64_t>(wh, (int64_t)hitems.size() * in.hkv);
-  out->dev_wgs = ditems.empty() ? 0 : std::min<int64_t>(wd, (int64_t)ditems.size() * in.hkv);
-  out->host_chunk = hitems.empty() ? 0 : ch;
-  out->dev_chunk = ditems.empty() ? 0 : cd;
-  out->host_bytes = host_tok * row_bytes * 2;
-  out->dev_bytes = dev_tok * row_bytes * 2;
-  out->n_plist = (int32_t)plist.size();
-  out->items_off = 0;
-  out->plist_off = (hitems.size() + ditems.size()) * sizeof(PlanItem);
-  out->offsets_off = round_up(out->plist_off + plist.size() * sizeof(int32_t), 16);
-  out->counters_off = round_up(out->offsets_off + (B + 1) * sizeof(int32_t), 16);
-  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
-  if ((int64_t)(hitems.size() + ditems.size()) * in.hkv > INT32_MAX)
-    return fail(err, "too many work units");
-  if (blob) {
-    blob->assign(out->blob_bytes, 0);
-    uint8_t* p = blob->data();
-    if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(PlanItem));
-    if (!ditems.empty())
-      memcpy(p + hitems.size() * sizeof(PlanItem), ditems.data(), ditems.size() * sizeof(PlanItem));
-    if (!plist.empty()) memcpy(p + out->plist_off, plist.data(), plist.size() * sizeof(int32_t));
-    memcpy(p + out->offsets_off, offsets.data(), offsets.size() * sizeof(int32_t));
+void decode_enumerate(const DecodeTemplate& t, int B, const int64_t* nh, const int64_t* nd,
+                      std::vector<DecodeHostItem>* items, std::vector<int32_t>* offsets, DecodeSizes* zout) {
+  int64_t th = 0, td = 0;
+  for (int b = 0; b < B; ++b) {
+    th += nh[b];
+    td += nd[b];
   }
-  return true;
+  const DecodeSizes z = decode_sizes(t, th, td);
+  if (zout) *zout = z;
+  std::vector<DecodeSeqItems> s(B);
+  offsets->assign(B + 1, 0);
+  for (int b = 0; b < B; ++b) {
+    s[b] = decode_seq_items(z, t.align, nh[b], nd[b]);
+    (*offsets)[b + 1] = (*offsets)[b] + decode_seq_splits(s[b]);
+  }
+  items->clear();
+  // host items, then HBM items before the tail, then the tail (the order the
+  // kernel's queues hand them out)
+  for (int b = 0; b < B; ++b)
+    for (int c = 0; c < s[b].uh; ++c) {
+      const int64_t k0 = (int64_t)c * z.ch;
+      items->push_back({1, b, (*offsets)[b] + c, (int32_t)std::min<int64_t>(z.ch, nh[b] - k0), k0});
+    }
+  for (int b = 0; b < B; ++b)
+    for (int c = 0; c < s[b].um; ++c) {
+      const int64_t k0 = (int64_t)c * z.cd;
+      items->push_back({0, b, (*offsets)[b] + s[b].uh + c, (int32_t)std::min<int64_t>(z.cd, s[b].t0 - k0), k0});
+    }
+  for (int b = 0; b < B; ++b)
+    for (int c = 0; c < s[b].ut; ++c) {
+      const int64_t k0 = s[b].t0 + (int64_t)c * z.cs;
+      items->push_back(
+          {0, b, (*offsets)[b] + s[b].uh + s[b].um + c, (int32_t)std::min<int64_t>(z.cs, nd[b] - k0), k0});
+    }
 }
 
 }  // namespace dkv

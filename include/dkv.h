@@ -66,9 +66,10 @@ int32_t dkv_version(void);
  *
  *  page_size > 0 (a power of two), paged.  page_table[b*max_pages + t/page]
  *    = phys << 1 | tier (tier 1 = host pools, 0 = device pools) and the row
- *    is phys*page_size + t % page_size.  page_table lives in device memory;
- *    page_table_host is an identical host copy used to plan the per-tier work
- *    (the planner reads tiers from it; kernels read the device copy).
+ *    is phys*page_size + t % page_size.  page_table lives in device memory
+ *    and is what every kernel reads; page_table_host, an identical host copy,
+ *    is needed only by the prefill planners and by plan introspection (decode
+ *    calls derive their work from the device copy).
  *
  *  host_k/host_v are device addresses of host-pinned memory (zero-copy);
  *  dev_k/dev_v are HBM.  host_rows / dev_rows are the pool capacities in rows
@@ -140,31 +141,44 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
  *
  * One query token per sequence: q [batch][Hq][D] bf16 (device), rotated
  * in-kernel by Neox RoPE at q_pos[b] (device int32 [batch]).  Query head h
- * reads KV head h / (Hq/Hkv).  Sequence b attends to its seq_lens[b] cached
- * tokens (host int32 [batch], each >= 1; keys already rotated by the append):
+ * reads KV head h / (Hq/Hkv).  Sequence b attends to its first seq_lens[b]
+ * cached tokens (device int32 [batch], each >= 0; keys already rotated by the
+ * append):
  *   s_t = scale * q_rot . k_t,  o = sum_t softmax(s)_t v_t,  lse = ln sum_t e^s_t.
  *
- * The tokens of each sequence are cut into work items that each lie in one
- * tier (host or HBM) and one KV head.  Items of the two tiers run at the same
- * time on disjoint sets of workgroups; each item writes a normalised partial
- * (part_o [S][Hq][D] fp32, part_lse [S][Hq] fp32, natural log) in the split
- * slots of its sequence, and split_offsets (device int32 [batch+1]) receives
- * the CSR bounds: sequence b owns splits [split_offsets[b], split_offsets[b+1]).
+ * No host planning per call: the kernel reads seq_lens (and, paged, the page
+ * table) in device memory and cuts each sequence's tokens into work items
+ * that each lie in one tier; items of the two tiers run at the same time on
+ * disjoint sets of workgroups, each bound to one KV head.  Every item writes a
+ * normalised partial (part_o [S][Hq][D] fp32, part_lse [S][Hq] fp32, natural
+ * log) in the split slots of its sequence, and split_offsets (device int32
+ * [batch+1]) receives the CSR bounds: sequence b owns splits
+ * [split_offsets[b], split_offsets[b+1]) (empty for seq_lens[b] = 0).
  * dkv_merge_lse turns the partials into the final output.
  *
- * dkv_decode_plan returns the split count S and the workspace size for these
- * arguments; part_o / part_lse must hold at least S splits (num_splits_cap)
- * and the workspace (device memory) at least workspace_bytes.  Plans are
- * cached per distinct shape inside the library.
+ * dkv_decode_plan gives, for the call's shape (not its lengths), the
+ * workspace size and S, the most splits any lengths that fit the pools can
+ * produce: part_o / part_lse must hold num_splits_cap >= S splits.  With
+ * seq_lens (host int32 [batch], optional) it also reports the items, item
+ * lengths and bytes per tier those lengths give.
  *
- * Graph capture: the call may be captured into a HIP graph (stream in
- * capture mode).  Make one ordinary call with the same arguments first so the
- * plan is built outside the capture; the plan image a captured graph copies
- * from is then kept for the life of the process.
+ * Workspace (device memory, 256-byte aligned): zero-filled before its first
+ * use; every call leaves its counters at zero again, so it is reused as is.
+ * Calls that share a workspace must not overlap (they race).  The call
+ * allocates nothing and never synchronises, so it may be captured into a HIP
+ * graph: each replay reads the lengths and positions present in device
+ * memory at that time, so one graph serves a cache that grows.
+ *
+ * Sequences whose rows fall outside the layout (contiguous: beyond host_stride,
+ * dev_stride or a pool; paged: negative or out-of-pool page entries, more pages
+ * than max_pages) are not read and set a flag that dkv_decode_errors reports;
+ * DKV_DEBUG_VALIDATE=1 checks them on the host before launching instead
+ * (synchronous).
  * ---------------------------------------------------------------------- */
 typedef struct dkv_plan_info {
   int64_t workspace_bytes; /* device workspace the call needs */
-  int32_t num_splits;      /* S: rows of part_o / part_lse */
+  int32_t num_splits;      /* decode: split bound S (step: partial slots per sequence
+                              and KV head); prefill: splits of the plan */
   int32_t host_items;      /* work items in the host tier (per KV head) */
   int32_t dev_items;       /* work items in the HBM tier (per KV head) */
   int32_t host_wgs;        /* workgroups streaming the host tier */
@@ -188,18 +202,65 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
                                  float* part_o, float* part_lse, int32_t* split_offsets,
                                  int32_t num_splits_cap, void* stream);
 
-/* Plan introspection with no GPU work: runs the planner for `num_cus`
- * compute units (current tuning otherwise) and copies the plan out to host
- * memory.  items receives up to items_cap rows of 5 int64 values
- * (tier [1 host, 0 HBM], b, slot, n_tok, first) where `first` is the pool row
- * of the item's first token (contiguous) or its index into page_list (paged);
+/* Plan introspection with no GPU work: the items the decode kernel derives
+ * for these host lengths (seq_lens host int32 [batch]) when planned for
+ * `num_cus` compute units (0: tuning or current device).  items receives up
+ * to items_cap rows of 5 int64 values (tier [1 host, 0 HBM], b, slot, n_tok,
+ * first) in queue order (host items first) where `first` is the pool row of
+ * the item's first token (contiguous) or its index into page_list (paged);
  * page_list receives up to page_cap logical page indices; split_offsets
- * receives batch+1 values.  Any output pointer may be NULL.  Host tier items
- * come first.  info as for dkv_decode_plan. */
+ * receives batch+1 values.  Any output pointer may be NULL.  info as for
+ * dkv_decode_plan, with num_splits the exact count. */
 dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                             const int32_t* seq_lens, double offload_ratio, int32_t num_cus,
                             int64_t* items, int32_t items_cap, int32_t* page_list,
                             int32_t page_cap, int32_t* split_offsets, dkv_plan_info* info);
+
+/* ------------------------------------------------------------------------
+ * Fused decode step in one launch (DirectKV README, introduction: one kernel
+ * projects the new token's K/V, rotates the key with Neox RoPE, appends it to
+ * the CPU-resident cache and attends; Attribution: online softmax over KV
+ * streamed from CPU memory).
+ *
+ * Sequence b holds seq_lens[b] cached tokens (device int32 [batch]).  When a
+ * new token is given (k_new/v_new [batch][Hkv][D] bf16, or x [batch][hidden]
+ * bf16 with wk/wv [hidden][Hkv*D] bf16 as in dkv_project_rope_append), it is
+ * appended at position pos_new[b] (device int32 [batch]; NULL: seq_lens[b])
+ * into its slot of a cache of seq_lens[b] + 1 tokens (contiguous: split point
+ * floor(r * (seq_lens[b] + 1)); paged: the page table entry), with its key
+ * rotated at that position in fp64 and rounded once to bf16, and the query
+ * attends to the seq_lens[b] cached tokens plus the new one (read from
+ * registers, as stored).  With no new token (k_new = v_new = x = NULL) the
+ * query attends to the cached tokens only.  The partials of each (sequence,
+ * KV head) are merged by log-sum-exp inside the same launch (the last
+ * workgroup to finish one merges it): out_o [batch][Hq][D] fp32, out_lse
+ * [batch][Hq] fp32 (or NULL).  A sequence with nothing to attend gets
+ * out_o = 0 and out_lse = -inf.
+ *
+ * One kernel launch (plus the paged layout's tier lists and, with x, the
+ * projection).  Workspace from dkv_decode_step_plan (hidden = 0 without
+ * projection), same rules as for dkv_decode_attn_split: zero before its first
+ * use, left zeroed, no allocation, capturable, valid while lengths grow.
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_decode_step_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
+                                double offload_ratio, int32_t hidden, dkv_plan_info* info);
+
+dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                           const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new,
+                           const void* x, int32_t hidden, const void* wk, const void* wv,
+                           const void* k_new, const void* v_new, double offload_ratio, float scale,
+                           double rope_theta, void* workspace, size_t workspace_bytes, float* out_o,
+                           float* out_lse, void* stream);
+
+/* Layout errors the decode kernels flagged in this workspace since it was
+ * last cleared (bit 1: contiguous rows beyond a stride or pool, 2: page entry
+ * unmapped or beyond its pool, 4: appended token without a slot, 8: partial
+ * slots exhausted).  Synchronises the device; clear != 0 resets the flags. */
+#define DKV_DECODE_ERR_LAYOUT 1
+#define DKV_DECODE_ERR_PAGE 2
+#define DKV_DECODE_ERR_SLOT 4
+#define DKV_DECODE_ERR_CAPACITY 8
+dkv_status dkv_decode_errors(const dkv_kv_desc* kv, const void* workspace, int32_t clear, int32_t* flags);
 
 /* ------------------------------------------------------------------------
  * Causal prefill attention over the split cache (DirectKV README,
@@ -441,7 +502,8 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
  * DKV_KERNEL_ROPE_Q (the two-call prefill's rotation table; decode rotates its
  * queries inside the attention kernel), DKV_KERNEL_MERGE, DKV_KERNEL_APPEND,
  * DKV_KERNEL_PREFILL (causal prefill attention), DKV_KERNEL_STAGE (prefill's
- * copy of re-read host rows into HBM), DKV_KERNEL_LINEAR (offloaded linear).
+ * copy of re-read host rows into HBM), DKV_KERNEL_LINEAR (offloaded linear),
+ * DKV_KERNEL_TIERS (the paged decode's per-tier page lists).
  * ---------------------------------------------------------------------- */
 #define DKV_KERNEL_ATTN 0
 #define DKV_KERNEL_ROPE_Q 1
@@ -450,6 +512,7 @@ dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t no
 #define DKV_KERNEL_PREFILL 4
 #define DKV_KERNEL_STAGE 5
 #define DKV_KERNEL_LINEAR 6
+#define DKV_KERNEL_TIERS 7
 
 dkv_status dkv_kernel_timing(int32_t enable);
 

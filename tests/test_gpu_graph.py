@@ -64,7 +64,7 @@ def test_graph_replays_contiguous_split(dk):
 
     def step():
         dk.project_rope_append(cache, 2, sl, r, sidx, qpos, k_new=k_new, v_new=v_new, rope_theta=th)
-        dk.decode_attn_split(cache, q, qpos, lens, r, 1 / math.sqrt(d), th, bufs=bufs)
+        dk.decode_attn_split(cache, q, qpos, sl, r, 1 / math.sqrt(d), th, bufs=bufs)
         dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, 2, hq, d, out_o=bufs.out_o,
                      out_lse=bufs.out_lse)
 
@@ -93,11 +93,12 @@ def test_graph_replays_fused_paged(dk):
     sidx = torch.arange(B, dtype=torch.int32, device="cuda")
     ws = torch.empty(dk.append_workspace_bytes(B, hid, hkv * d), dtype=torch.uint8, device="cuda")
     bufs = dk.alloc_decode_buffers(cache, B, hq, ntok, 0.0)
+    ntok_dev = torch.tensor(ntok, dtype=torch.int32, device="cuda")
 
     def step():
         dk.project_rope_append(cache, B, None, 0.0, sidx, pos, x=x, wk=wk, wv=wv, rope_theta=th,
                                workspace=ws)
-        dk.decode_attn_split(cache, q, pos, ntok, 0.0, 1 / math.sqrt(d), th, bufs=bufs)
+        dk.decode_attn_split(cache, q, pos, ntok_dev, 0.0, 1 / math.sqrt(d), th, bufs=bufs)
         dk.merge_lse(bufs.part_o, bufs.part_lse, bufs.split_offsets, B, hq, d, out_o=bufs.out_o,
                      out_lse=bufs.out_lse)
 
@@ -106,8 +107,9 @@ def test_graph_replays_fused_paged(dk):
 
 
 def test_graph_replays_fused_prefill(dk):
-    # the fused prefill step forks the cache-slot writes onto a second stream
-    # and joins them back: the captured graph must replay it exactly
+    # the fused prefill step (append of the new rows, staging, prefill launch
+    # with writer workgroups for the cache slots, merge): the captured graph
+    # must replay it exactly
     import torch
     from decode_attention_host_amd.cache_build import contiguous_cache
     lens, news, hq, hkv, d, r, th = [900, 300], [400, 300], 32, 8, 128, 0.7, 5e5
