@@ -397,16 +397,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const bool host_role = (int)blockIdx.x < a.hkv * T.team_h;
   const int r_idx = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.hkv * T.team_h;
   const int team = host_role ? T.team_h : T.team_d;
-  const int kvh = r_idx / team;
-  const int jt = r_idx - kvh * team;
+  // Fused form: workgroups are bound to one KV head ("team") and take the
+  // items of their tier in order, so they can carry a run across items.
+  // Split form: one queue per tier whose units are (item, KV head) with the
+  // KV head fastest, so the heads of a token range are read together.
+  int kvh = FUSED ? r_idx / team : 0;
+  const int jt = FUSED ? r_idx - kvh * team : r_idx;
   const int n_items = host_role ? L.ph[B] : L.pm[B] + L.pt[B];
+  const int n_units = FUSED ? n_items : n_items * a.hkv;
+  const int first_stride = FUSED ? team : team * a.hkv;
   const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
   const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
   const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
   const int64_t stride = host_role ? a.host_stride : a.dev_stride;
   const int32_t* __restrict__ tier_list =
       PAGED ? a.tier_pages + (host_role ? 0 : (int64_t)B * a.max_pages) : nullptr;
-  int* qctr = a.counters + (host_role ? 0 : a.hkv) + kvh;
+  int* qctr = a.counters + (host_role ? 0 : a.hkv) + kvh;  // split form: kvh = 0
 
   if (!FUSED && blockIdx.x == 0 && a.split_offsets)
     for (int i = tid; i <= B; i += kThreads) a.split_offsets[i] = L.off[i];
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // Rotated query heads of sequence b for this KV head into q_lds: one Neox pair
   // per thread, angle q_pos[b] * f_i with sin and cos in fp64, rounded once to
   // fp32 with scale * log2(e) folded in.
-  int q_b = -1;
+  int q_b = -1, q_kvh = -1;
   auto rotate_q = [&](int b) {
     __syncthreads();  // earlier readers of q_lds are done
     const int pos = a.q_pos[b];
@@ -430,6 +436,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
     q_b = b;
+    q_kvh = kvh;
   };
 
   // Runs of partials (fused form): completion bookkeeping per (sequence, KV head).
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // rounding), store K and V in the token's cache slot, and write the
   // one-token partial of (b, kvh): o = v, lse = its scaled score.
   auto new_token = [&](int b) {
-    if (q_b != b) rotate_q(b);
+    if (q_b != b || q_kvh != kvh) rotate_q(b);
     const int p = a.pos_new ? a.pos_new[b] : a.seq_lens[b];
     float* kr = reinterpret_cast<float*>(k_lds);  // rotated key (bf16 values) [D]
     float* vr = kr + D;                           // value [D]
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
   };
-  auto load_tile = [&](const DItem& it, int tile, const int32_t* pte) {
+  auto load_tile = [&](const DItem& it, int kv, int tile, const int32_t* pte) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int chunk = tid + c * kThreads;
@@ -688,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       } else {
         row = (int64_t)it.b * stride + it.k0 + tok;
       }
-      const int64_t off = (row * a.hkv + kvh) * D + col * 8;
+      const int64_t off = (row * a.hkv + kv) * D + col * 8;
       if (valid) {
         // KV is read once per step: non-temporal loads on both tiers
         kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
@@ -700,13 +707,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   };
 
+  // unit u: the item (and, split form, the KV head) it stands for
+  auto unit_item = [&](int u, int* kv) -> DItem {
+    if (FUSED) return item_at(L, B, host_role, u);
+    const int item = u / a.hkv;
+    *kv = u - item * a.hkv;
+    return item_at(L, B, host_role, item);
+  };
   int i = jt;
   DItem it{};
   int32_t pte[NC] = {};
-  if (i < n_items) {
-    it = item_at(L, B, host_role, i);
+  if (i < n_units) {
+    it = unit_item(i, &kvh);
     if (PAGED) lookup(it, 0, pte);
-    load_tile(it, 0, pte);
+    load_tile(it, kvh, 0, pte);
   }
   bool run_open = false;  // fused: online-softmax state carries a run of sequence run_b
   int run_b = -1, run_items = 0;
@@ -714,11 +728,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   float l_run = 0.f;
   float acc[G][DPL];
   bf16x8_t qb[KS];
-  while (i < n_items) {
+  while (i < n_units) {
     ++units_done;
     const int ntiles = (it.n_tok + kTile - 1) / kTile;
     if (!run_open) {
-      if (q_b != it.b) rotate_q(it.b);
+      if (q_b != it.b || q_kvh != kvh) rotate_q(it.b);
       // query operand: columns h (high bf16 part) and h+8 (low part)
       const int hsel = n & 7;
       const bool active = hsel < G;
@@ -754,7 +768,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       run_items = 0;
     }
 
-    int next_i = n_items;
+    int next_i = n_units;
+    int nkvh = kvh;
     DItem nit{};
     for (int tile = 0; tile < ntiles; ++tile) {
       __syncthreads();  // previous tile's readers are done
@@ -767,19 +782,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
       }
       const bool last = tile + 1 == ntiles;
-      if (last && tid == 0) s_next = team + atomicAdd(qctr, 1);
+      if (last && tid == 0) s_next = first_stride + atomicAdd(qctr, 1);
       __syncthreads();
       // keep one tile in flight: the next tile of this item, or the first
       // tile of the next item while this item's last tile is computed
       if (!last) {
         if (PAGED) lookup(it, tile + 1, pte);
-        load_tile(it, tile + 1, pte);
+        load_tile(it, kvh, tile + 1, pte);
       } else {
         next_i = __builtin_amdgcn_readfirstlane(s_next);
-        if (next_i < n_items) {
-          nit = item_at(L, B, host_role, next_i);
+        if (next_i < n_units) {
+          nit = unit_item(next_i, &nkvh);
           if (PAGED) lookup(nit, 0, pte);
-          load_tile(nit, 0, pte);
+          load_tile(nit, nkvh, 0, pte);
         }
       }
 
@@ -855,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ---- end of an item (split form) or of a run (fused form): combine the
     // four waves and write the partial
-    const bool flush = !FUSED || next_i >= n_items || nit.b != run_b;
+    const bool flush = !FUSED || next_i >= n_units || nit.b != run_b;
     if (flush) {
       __syncthreads();
       float* sm_m = reinterpret_cast<float*>(k_lds);   // [4][G]
@@ -905,6 +920,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // the next item's first tile is already in registers
     i = next_i;
     it = nit;
+    kvh = nkvh;
   }
 
   // Fused form: groups with nothing to merge (no tokens and no appended token).
