@@ -146,7 +146,7 @@ SIGNATURES = {
     "dkv_host_free": (I32, [P]),
     "dkv_set_tuning": (I32, [C.POINTER(Tuning)]),
     "dkv_get_tuning": (I32, [C.POINTER(Tuning)]),
-    "dkv_probe_read": (I32, [P, SZ, I32, I32, I32, P, P, C.POINTER(BwResult), P]),
+    "dkv_probe_read": (I32, [P, P, SZ, I32, I32, I32, P, P, C.POINTER(BwResult), P]),
     "dkv_kernel_timing": (I32, [I32]),
     "dkv_kernel_timing_read": (I32, [I32, C.POINTER(I32), C.POINTER(F64)]),
     "dkv_attn_trace": (I32, [P, I32]),

@@ -473,9 +473,16 @@ def get_tuning() -> dict:
 
 
 def probe_read(src_dev_ptr: int, nbytes: int, nwg: int, nontemporal: bool = True, iters: int = 5,
-               dma_dst=None, dma_src_host=None, stream=None) -> dict:
+               dma_dst=None, dma_src_host=None, stream=None, blocked: bool = False, src2_dev_ptr=None,
+               segments: bool = False) -> dict:
+    """dkv_probe_read: best of ``iters`` passes; ``blocked`` gives each workgroup
+    one contiguous slice instead of a grid-stride walk, ``segments`` one 256-byte
+    segment of every 2 KiB row of a slice; ``src2_dev_ptr`` adds a second buffer
+    of ``nbytes`` read at the same time (the rate counts both)."""
     r = BwResult()
-    check(lib().dkv_probe_read(C.c_void_p(int(src_dev_ptr)), int(nbytes), int(nwg), int(bool(nontemporal)),
+    mode = int(bool(nontemporal)) | (4 if segments else (2 if blocked else 0))
+    src2 = C.c_void_p(int(src2_dev_ptr)) if src2_dev_ptr else None
+    check(lib().dkv_probe_read(C.c_void_p(int(src_dev_ptr)), src2, int(nbytes), int(nwg), mode,
                                int(iters), _ptr(dma_dst), _ptr(dma_src_host), C.byref(r), _stream(stream)))
     return {"read_gbs": r.read_gbs, "read_ms": r.read_ms, "dma_gbs": r.dma_gbs}
 

@@ -1233,51 +1233,67 @@ dkv_status dkv_host_free(void* host_ptr) {
   return ok();
 }
 
-dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t nontemporal,
+dkv_status dkv_probe_read(const void* src, const void* src2, size_t bytes, int32_t nwg, int32_t mode,
                           int32_t iters, void* dma_dst, const void* dma_src_host,
                           dkv_bw_result* out, void* stream) {
   if (!src || !out) return set_err(DKV_ERR_INVALID, "src and out are required");
   if (bytes < 16 || bytes % 16) return set_err(DKV_ERR_INVALID, "bytes must be a positive multiple of 16");
-  if (nwg < 1 || nwg > 65535 || iters < 1) return set_err(DKV_ERR_INVALID, "nwg in [1,65535], iters >= 1");
-  if ((uintptr_t)src % 16) return set_err(DKV_ERR_INVALID, "src must be 16-byte aligned");
+  if (nwg < 1 || nwg > 65535 || iters < 1 || iters > 1000)
+    return set_err(DKV_ERR_INVALID, "nwg in [1,65535], iters in [1,1000]");
+  if (mode < 0 || mode > 7 || (mode & 6) == 6) return set_err(DKV_ERR_INVALID, "mode: bit 0, and bit 1 or bit 2");
+  if ((mode & 4) && (bytes % 2048 || nwg % ((src2 ? 2 : 1) * 8)))
+    return set_err(DKV_ERR_INVALID, "segment mode needs 2 KiB rows and 8 workgroups per buffer");
+  if ((uintptr_t)src % 16 || (uintptr_t)src2 % 16) return set_err(DKV_ERR_INVALID, "sources must be 16-byte aligned");
+  if (src2 && nwg % 2) return set_err(DKV_ERR_INVALID, "two buffers need an even workgroup count");
+  const double total_bytes = (double)bytes * (src2 ? 2 : 1);
   hipStream_t s = (hipStream_t)stream;
   float* sink = nullptr;
   hipError_t e = hipMalloc(&sink, 256);
   if (e != hipSuccess) return hip_err(e, "probe sink");
-  hipEvent_t e0, e1;
-  (void)hipEventCreate(&e0);
-  (void)hipEventCreate(&e1);
+  std::vector<hipEvent_t> ev(2 * (size_t)iters, nullptr);
+  for (auto& x : ev)
+    if (e == hipSuccess) e = hipEventCreate(&x);
   dkv_status st = DKV_OK;
-  e = (hipError_t)dkv::launch_probe_read(src, bytes, nwg, nontemporal, sink, stream);  // warm-up
-  if (e == hipSuccess) e = hipEventRecord(e0, s);
-  for (int i = 0; i < iters && e == hipSuccess; ++i)
-    e = (hipError_t)dkv::launch_probe_read(src, bytes, nwg, nontemporal, sink, stream);
-  if (e == hipSuccess) e = hipEventRecord(e1, s);
-  if (e == hipSuccess) e = hipEventSynchronize(e1);
-  float ms = 0.f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  // best of `iters` timed passes, each bracketed by its own events
+  auto timed = [&](auto launch, double* best_ms, double* avg_ms) -> hipError_t {
+    hipError_t r = launch();  // warm-up
+    for (int i = 0; i < iters && r == hipSuccess; ++i) {
+      r = hipEventRecord(ev[2 * i], s);
+      if (r == hipSuccess) r = launch();
+      if (r == hipSuccess) r = hipEventRecord(ev[2 * i + 1], s);
+    }
+    if (r == hipSuccess) r = hipEventSynchronize(ev[2 * iters - 1]);
+    double best = 1e30, sum = 0.0;
+    for (int i = 0; i < iters && r == hipSuccess; ++i) {
+      float ms = 0.f;
+      r = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+      best = std::min(best, (double)ms);
+      sum += ms;
+    }
+    *best_ms = best;
+    *avg_ms = sum / iters;
+    return r;
+  };
+  double best = 0.0, avg = 0.0;
+  if (e == hipSuccess)
+    e = timed([&] { return (hipError_t)dkv::launch_probe_read(src, src2, bytes, nwg, mode, sink, stream); }, &best,
+              &avg);
   if (e != hipSuccess) {
     st = hip_err(e, "probe kernel");
   } else {
-    out->read_ms = ms / iters;
-    out->read_gbs = (double)bytes / (out->read_ms * 1e6);
+    out->read_ms = best;
+    out->read_gbs = total_bytes / (best * 1e6);
     out->dma_gbs = 0.0;
     if (dma_dst && dma_src_host) {
-      e = hipMemcpyAsync(dma_dst, dma_src_host, bytes, hipMemcpyHostToDevice, s);
-      if (e == hipSuccess) e = hipEventRecord(e0, s);
-      for (int i = 0; i < iters && e == hipSuccess; ++i)
-        e = hipMemcpyAsync(dma_dst, dma_src_host, bytes, hipMemcpyHostToDevice, s);
-      if (e == hipSuccess) e = hipEventRecord(e1, s);
-      if (e == hipSuccess) e = hipEventSynchronize(e1);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+      e = timed([&] { return hipMemcpyAsync(dma_dst, dma_src_host, bytes, hipMemcpyHostToDevice, s); }, &best, &avg);
       if (e != hipSuccess)
         st = hip_err(e, "probe DMA");
       else
-        out->dma_gbs = (double)bytes / ((ms / iters) * 1e6);
+        out->dma_gbs = (double)bytes / (best * 1e6);
     }
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
+  for (auto& x : ev)
+    if (x) (void)hipEventDestroy(x);
   (void)hipFree(sink);
   if (st != DKV_OK) return st;
   return ok();

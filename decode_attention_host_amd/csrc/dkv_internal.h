@@ -332,7 +332,9 @@ int launch_append(const AppendArgs& a, void* stream, int max_wgs = 0);
 int launch_append_rows(const AppendArgs& a, double* table, const int32_t* plan_offsets,
                        int32_t* split_offsets, void* stream);
 int launch_project(const ProjArgs& a, void* stream);
-int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
+// mode: bit 0 non-temporal loads, bit 1 blocked (one contiguous slice per workgroup)
+// src2 (optional): a second buffer of `bytes`, read by the odd workgroups
+int launch_probe_read(const void* src, const void* src2, size_t bytes, int nwg, int mode, float* sink,
                       void* stream);
 
 // Planner (dkv_plan.cpp), no HIP calls.

@@ -1289,25 +1289,74 @@ __global__ __launch_bounds__(kThreads) void proj_reduce_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming read probe: 16 B per lane per load, coalesced, grid-stride.
+// Streaming read probe: 16 B per lane per load, coalesced, U loads in flight
+// per thread.  Grid-stride: consecutive workgroups read neighbouring 4 KiB
+// blocks.  Blocked: each workgroup streams its own contiguous slice, as the
+// attention kernel streams a work item.  Segments: the buffer is rows of
+// kProbeRow bytes cut into kProbeSeg-byte segments, and a workgroup streams one
+// segment of every row of its slice (the attention kernel's reads of one KV
+// head: 256 bytes of each 2 KiB token row of the LLaMA-3-8B layer).
 // ---------------------------------------------------------------------------
-template <bool NT>
+constexpr int kProbeRow = 2048;
+constexpr int kProbeSeg = 256;
+
+template <bool NT, int MODE>
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ src,
-                                                             int64_t n16, float* sink) {
+                                                             const u32x4* __restrict__ src2, int64_t n16,
+                                                             float* sink) {
   constexpr int U = 8;  // 16-byte loads in flight per thread
+  // with a second buffer, odd workgroups read it and even ones the first
+  const int nb = src2 ? 2 : 1;
+  int wg = (int)blockIdx.x / nb, nwg = (int)gridDim.x / nb;
+  const u32x4* __restrict__ p = (src2 && (blockIdx.x & 1)) ? src2 : src;
   uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + (U - 1) * stride < n16; i += U * stride) {
-    u32x4 v[U];
+  if (MODE == 2) {
+    constexpr int SPR = kProbeRow / kProbeSeg;   // segments per row
+    constexpr int CPS = kProbeSeg / 16;          // 16-byte chunks per segment
+    constexpr int RPI = kThreads / CPS;          // rows per load instruction
+    const int seg = wg % SPR;
+    wg /= SPR;
+    nwg = max(1, nwg / SPR);
+    const int64_t rows = n16 * 16 / kProbeRow;
+    const int64_t per = (rows + nwg - 1) / nwg;
+    const int64_t r0 = (int64_t)wg * per, r1 = min(rows, r0 + per);
+    const int rr = threadIdx.x / CPS, cc = threadIdx.x % CPS;
+    auto at = [&](int64_t row) { return p + row * (kProbeRow / 16) + seg * CPS + cc; };
+    int64_t r = r0 + rr;
+    for (; r + (U - 1) * RPI < r1; r += U * RPI) {
+      u32x4 v[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) v[k] = NT ? __builtin_nontemporal_load(src + i + k * stride) : src[i + k * stride];
+      for (int k = 0; k < U; ++k) v[k] = NT ? __builtin_nontemporal_load(at(r + k * RPI)) : *at(r + k * RPI);
 #pragma unroll
-    for (int k = 0; k < U; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = NT ? __builtin_nontemporal_load(src + i) : src[i];
-    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      for (int k = 0; k < U; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    for (; r < r1; r += RPI) {
+      const u32x4 v = NT ? __builtin_nontemporal_load(at(r)) : *at(r);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  } else {
+    int64_t i, end, stride;
+    if (MODE == 1) {
+      const int64_t per = (n16 + nwg - 1) / nwg;
+      i = (int64_t)wg * per + threadIdx.x;
+      end = min(n16, (int64_t)(wg + 1) * per);
+      stride = blockDim.x;
+    } else {
+      i = (int64_t)wg * blockDim.x + threadIdx.x;
+      end = n16;
+      stride = (int64_t)nwg * blockDim.x;
+    }
+    for (; i + (U - 1) * stride < end; i += U * stride) {
+      u32x4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) v[k] = NT ? __builtin_nontemporal_load(p + i + k * stride) : p[i + k * stride];
+#pragma unroll
+      for (int k = 0; k < U; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    for (; i < end; i += stride) {
+      const u32x4 v = NT ? __builtin_nontemporal_load(p + i) : p[i];
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
   }
   if (acc == 0x9e3779b9u) sink[0] = (float)acc;  // keeps the loads alive
 }
@@ -1446,16 +1495,25 @@ int launch_project(const ProjArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_probe_read(const void* src, size_t bytes, int nwg, int nontemporal, float* sink,
+int launch_probe_read(const void* src, const void* src2, size_t bytes, int nwg, int mode, float* sink,
                       void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t n16 = (int64_t)(bytes / 16);
-  if (nontemporal)
-    hipLaunchKernelGGL(probe_read_kernel<true>, dim3(nwg), dim3(kThreads), 0, s,
-                       (const u32x4*)src, n16, sink);
-  else
-    hipLaunchKernelGGL(probe_read_kernel<false>, dim3(nwg), dim3(kThreads), 0, s,
-                       (const u32x4*)src, n16, sink);
+  const u32x4* p = (const u32x4*)src;
+  const u32x4* p2 = (const u32x4*)src2;
+  const bool nt = mode & 1;
+  const int layout = (mode & 4) ? 2 : ((mode & 2) ? 1 : 0);
+#define DKV_PROBE(NTV, M) hipLaunchKernelGGL((probe_read_kernel<NTV, M>), dim3(nwg), dim3(kThreads), 0, s, p, p2, n16, sink)
+  if (nt) {
+    if (layout == 0) DKV_PROBE(true, 0);
+    else if (layout == 1) DKV_PROBE(true, 1);
+    else DKV_PROBE(true, 2);
+  } else {
+    if (layout == 0) DKV_PROBE(false, 0);
+    else if (layout == 1) DKV_PROBE(false, 1);
+    else DKV_PROBE(false, 2);
+  }
+#undef DKV_PROBE
   return (int)hipGetLastError();
 }
 

@@ -476,20 +476,30 @@ dkv_status dkv_set_tuning(const dkv_tuning* tuning); /* NULL restores defaults *
 dkv_status dkv_get_tuning(dkv_tuning* tuning);
 
 /* ------------------------------------------------------------------------
- * Bandwidth probe: reads `bytes` of memory with a streaming kernel that has
- * the same load pattern as the attention kernel (16 B per lane, coalesced)
- * and reports GB/s.  src is a device address (HBM or mapped host memory),
- * nwg the number of workgroups (<= 65535), iters the timed repetitions.
- * Also a DMA copy rate for host->device hipMemcpyAsync of the same block when
- * dma_dst is non-NULL (device buffer of `bytes`).  Blocks until done.
+ * Bandwidth probe: reads `bytes` of memory with a streaming kernel (16 B per
+ * lane, coalesced, 8 loads in flight per thread) and reports the best of
+ * `iters` timed passes (1..1000), each bracketed by its own HIP events.  src
+ * is a device address (HBM or mapped host memory), nwg the number of
+ * workgroups (<= 65535).  src2 (optional, NULL for one buffer): a second
+ * buffer of `bytes` read at the same time by the odd workgroups (as the
+ * attention kernel streams the K and V pools together); the rate counts both.
+ * mode: bit 0 non-temporal loads; bit 1 blocked (each workgroup streams one
+ * contiguous slice, as the attention kernel streams a work item) instead of
+ * grid-stride; bit 2 segments (instead of bit 1: the buffer is rows of 2 KiB,
+ * and each workgroup streams one 256-byte segment of every row of its slice,
+ * as the attention kernel reads one KV head of the LLaMA-3-8B row; `bytes` a
+ * multiple of 2 KiB, nwg a multiple of 8 per buffer).  Also the best host->device
+ * hipMemcpyAsync rate of the same block when dma_dst is non-NULL (device
+ * buffer of `bytes`).  Blocks until done.  Measurement helper: it allocates a
+ * 256-byte sink and its events.
  * ---------------------------------------------------------------------- */
 typedef struct dkv_bw_result {
-  double read_gbs;   /* kernel read rate */
-  double read_ms;    /* average kernel time */
-  double dma_gbs;    /* hipMemcpyAsync rate (0 if not measured) */
+  double read_gbs;   /* kernel read rate of the best pass */
+  double read_ms;    /* kernel time of the best pass */
+  double dma_gbs;    /* hipMemcpyAsync rate of the best pass (0 if not measured) */
 } dkv_bw_result;
 
-dkv_status dkv_probe_read(const void* src, size_t bytes, int32_t nwg, int32_t nontemporal,
+dkv_status dkv_probe_read(const void* src, const void* src2, size_t bytes, int32_t nwg, int32_t mode,
                           int32_t iters, void* dma_dst, const void* dma_src_host,
                           dkv_bw_result* out, void* stream);
 
