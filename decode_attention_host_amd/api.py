@@ -447,6 +447,23 @@ def decode_step(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_lens: 
     return out_o, out_lse
 
 
+def decode_step_static(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_lens: torch.Tensor, ratio: float,
+                       scale: float, rope_theta: float, *, out_o: torch.Tensor, out_lse: torch.Tensor | None = None,
+                       pos_new=None, k_new=None, v_new=None, x=None, wk=None, wv=None, stream=None):
+    """dkv_decode_step_static: decode_step on the library's static scratch (no
+    workspace, no allocation: the caller passes the outputs)."""
+    B, Hq, D = q.shape
+    hidden = int(x.shape[1]) if x is not None else 0
+    if not isinstance(seq_lens, torch.Tensor):
+        raise ValueError("seq_lens must be a device int32 tensor (this entry point allocates nothing)")
+    d = cache.desc()
+    check(lib().dkv_decode_step_static(
+        C.byref(d), int(B), int(Hq), _ptr(q), _ptr(q_pos), _ptr(seq_lens), _ptr(pos_new), _ptr(x), hidden, _ptr(wk),
+        _ptr(wv), _ptr(k_new), _ptr(v_new), float(ratio), float(scale), float(rope_theta), _ptr(out_o),
+        _ptr(out_lse), _stream(stream)))
+    return out_o, out_lse
+
+
 def decode_errors(cache: KVCache, workspace: torch.Tensor, clear: bool = True) -> int:
     """dkv_decode_errors: layout error flags the decode kernels left in ``workspace``."""
     d = cache.desc()

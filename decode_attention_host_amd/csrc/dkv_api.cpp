@@ -498,7 +498,7 @@ dkv_status decode_shape(const dkv_kv_desc* kv, int32_t batch, int32_t hq, double
   auto up = [](size_t a) { return (a + 255) / 256 * 256; };
   const size_t hkv = (size_t)kv->num_kv_heads, D = (size_t)kv->head_dim, B = (size_t)batch;
   d.counters_off = 0;
-  d.group_off = up((2 * hkv + 2) * 4);
+  d.group_off = up((size_t)dkv::decode_counter_words((int)hkv) * 4);
   d.tiers_off = up(d.group_off + (fused ? B * hkv * 2 * 4 : 0));
   d.lists_off = up(d.tiers_off + (paged ? B * 4 * 4 : 0));
   d.run_o_off = up(d.lists_off + (paged ? 2 * B * (size_t)kv->max_pages * 4 : 0));
@@ -866,11 +866,14 @@ dkv_status dkv_decode_step_plan(const dkv_kv_desc* kv, int32_t batch, int32_t nu
   return ok();
 }
 
-dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
-                           const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new, const void* x,
-                           int32_t hidden, const void* wk, const void* wv, const void* k_new, const void* v_new,
-                           double offload_ratio, float scale, double rope_theta, void* workspace,
-                           size_t workspace_bytes, float* out_o, float* out_lse, void* stream) {
+// The fused decode step on a given workspace (the caller's, or the static
+// scratch for the allocation-free entry point).
+static dkv_status decode_step_impl(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                                   const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new,
+                                   const void* x, int32_t hidden, const void* wk, const void* wv,
+                                   const void* k_new, const void* v_new, double offload_ratio, float scale,
+                                   double rope_theta, void* workspace, size_t workspace_bytes, float* out_o,
+                                   float* out_lse, void* stream, bool static_scratch = false) {
   dkv_status st = validate_decode_common(kv, q, q_pos, seq_lens, scale, rope_theta, workspace);
   if (st != DKV_OK) return st;
   if (!out_o) return set_err(DKV_ERR_INVALID, "out_o is required");
@@ -890,8 +893,12 @@ dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_h
   DecodeShape d;
   st = decode_shape(kv, batch, num_q_heads, offload_ratio, true, proj ? hidden : 0, 0, &d);
   if (st != DKV_OK) return st;
-  if (workspace_bytes < d.total)
+  if (workspace_bytes < d.total) {
+    if (static_scratch)
+      return set_err(DKV_ERR_UNSUPPORTED, "this shape needs %zu bytes of scratch, beyond the static %zu bytes",
+                     d.total, workspace_bytes);
     return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, d.total);
+  }
   hipStream_t s = (hipStream_t)stream;
   if (debug_validate()) {
     st = decode_debug_check(kv, batch, seq_lens, offload_ratio, append ? 1 : 0, s);
@@ -943,10 +950,32 @@ dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_h
   return ok();
 }
 
+dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                           const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new, const void* x,
+                           int32_t hidden, const void* wk, const void* wv, const void* k_new, const void* v_new,
+                           double offload_ratio, float scale, double rope_theta, void* workspace,
+                           size_t workspace_bytes, float* out_o, float* out_lse, void* stream) {
+  return decode_step_impl(kv, batch, num_q_heads, q, q_pos, seq_lens, pos_new, x, hidden, wk, wv, k_new, v_new,
+                          offload_ratio, scale, rope_theta, workspace, workspace_bytes, out_o, out_lse, stream);
+}
+
+dkv_status dkv_decode_step_static(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                                  const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new,
+                                  const void* x, int32_t hidden, const void* wk, const void* wv, const void* k_new,
+                                  const void* v_new, double offload_ratio, float scale, double rope_theta,
+                                  float* out_o, float* out_lse, void* stream) {
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  hipError_t he = (hipError_t)dkv::decode_static_scratch(&scratch, &bytes);
+  if (he != hipSuccess) return hip_err(he, "address of the static decode scratch");
+  return decode_step_impl(kv, batch, num_q_heads, q, q_pos, seq_lens, pos_new, x, hidden, wk, wv, k_new, v_new,
+                          offload_ratio, scale, rope_theta, scratch, bytes, out_o, out_lse, stream, true);
+}
+
 dkv_status dkv_decode_errors(const dkv_kv_desc* kv, const void* workspace, int32_t clear, int32_t* flags) {
   if (!kv || !workspace || !flags) return set_err(DKV_ERR_INVALID, "kv, workspace and flags are required");
   hipError_t he = hipDeviceSynchronize();
-  const int32_t* w = static_cast<const int32_t*>(workspace) + dkv::decode_error_word(kv->num_kv_heads);
+  const int32_t* w = static_cast<const int32_t*>(workspace) + dkv::decode_error_word();
   if (he == hipSuccess) he = hipMemcpy(flags, w, 4, hipMemcpyDeviceToHost);
   if (he == hipSuccess && clear) he = hipMemset(const_cast<int32_t*>(w), 0, 4);
   if (he == hipSuccess) he = hipDeviceSynchronize();

@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dkv_decomp.h"
 #include "dkv_device.h"
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
     }
     __syncthreads();
   }
-  if (err) atomicOr(&a.counters[decode_error_word(a.hkv)], err);
+  if (err) atomicOr(&a.counters[decode_error_word()], err);
   if (tid == 0) {
     const int64_t deficit = npg > 0 ? P - (A - (npg - 1) * P) : 0;
     const int64_t nh = (int64_t)s_base[0] * P - (s_last == 1 ? deficit : 0);
@@ -354,7 +355,7 @@ __device__ void build_prefix(const DecodeArgs& a, DecodeLds& L) {
     L.off[B] = cs;
     L.z = z;
   }
-  if (err) atomicOr(&a.counters[decode_error_word(a.hkv)], err);
+  if (err) atomicOr(&a.counters[decode_error_word()], err);
 }
 
 template <int D, int G, bool PAGED, bool FUSED>
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int64_t stride = host_role ? a.host_stride : a.dev_stride;
   const int32_t* __restrict__ tier_list =
       PAGED ? a.tier_pages + (host_role ? 0 : (int64_t)B * a.max_pages) : nullptr;
-  int* qctr = a.counters + (host_role ? 0 : a.hkv) + kvh;  // split form: kvh = 0
+  int* qctr = a.counters + decode_queue(a.hkv, host_role, kvh);  // split form: kvh = 0
 
   if (!FUSED && blockIdx.x == 0 && a.split_offsets)
     for (int i = tid; i <= B; i += kThreads) a.split_offsets[i] = L.off[i];
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         coherent_store4(ro, c * 16, *reinterpret_cast<const floatx4*>(&o_lds[0][0] + c * 4));
       if (tid < G) coherent_store1(rl, tid * 4, l_lds[tid]);
     } else if (tid == 0) {
-      atomicOr(&a.counters[decode_error_word(a.hkv)], kDecodeErrCapacity);
+      atomicOr(&a.counters[decode_error_word()], kDecodeErrCapacity);
     }
     wait_stores();
     __syncthreads();
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-    if (!sk && tid == 0) atomicOr(&a.counters[decode_error_word(a.hkv)], kDecodeErrSlot);
+    if (!sk && tid == 0) atomicOr(&a.counters[decode_error_word()], kDecodeErrSlot);
     if (tid < D / 2) {
       const int i = tid;
       double xl, xh;
@@ -937,10 +938,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (tid == 0) {
     wait_stores();
-    const int ec = decode_exit_counter(a.hkv);
+    const int ec = decode_exit_counter();
     const int done = atomicAdd(&a.counters[ec], 1) + 1;
     if (done == (int)gridDim.x) {
-      for (int k = 0; k < 2 * a.hkv; ++k)
+      for (int k = decode_queue(a.hkv, true, 0); k < decode_counter_words(a.hkv); ++k)
         __hip_atomic_store(&a.counters[k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.counters[ec], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -952,6 +953,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     t[2] = host_role ? 1 : 0;
     t[3] = (uint64_t)units_done;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate device memory (the
+// allocation-free decode step): a file-scope device array, one copy on every
+// GPU the library runs on, zero when the code object loads.  Every completed
+// call leaves its counters at zero again (and rewrites everything else it
+// reads), so calls of any shape follow each other on it; calls that overlap
+// on one GPU race.  Host code never uses the array's name as an address: the
+// per-device address comes from hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kDecodeStaticScratchBytes];
+
+int decode_static_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  *bytes = kDecodeStaticScratchBytes;
+  return (int)hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -149,7 +149,7 @@ struct DecodeArgs {
   int32_t fused;                 // 1: merge in the kernel (last finisher per sequence and KV head)
   DecodeTemplate tmpl;
   // workspace
-  int32_t* counters;             // [2 Hkv] item queues (host heads, then HBM heads), exit count, error flags
+  int32_t* counters;             // error flags, exit count, [2 Hkv] item queues (decode_queue)
   int32_t* group_cnt;            // fused: [batch * Hkv][2] items done, partials written
   const int32_t* tier_counts;    // paged: [batch][4] host pages, HBM pages, host tokens, HBM tokens
   const int32_t* tier_pages;     // paged: [2][batch][max_pages] physical pages, host tier then HBM
@@ -174,9 +174,14 @@ struct DecodeArgs {
   RopeFreq freq;                 // f_i = theta^(-2i/D), i < D/2
 };
 
-// Counter words of the decode workspace (int32 offsets from `counters`).
-DKV_HD constexpr int decode_exit_counter(int hkv) { return 2 * hkv; }
-DKV_HD constexpr int decode_error_word(int hkv) { return 2 * hkv + 1; }
+// Counter words of the decode workspace (int32 offsets from `counters`): the
+// error flags first, at a place no other shape uses for a counter (they are
+// sticky, while every counter returns to zero at the end of each call), then
+// the exit count, then the item queues (host KV heads, then HBM KV heads).
+DKV_HD constexpr int decode_error_word() { return 0; }
+DKV_HD constexpr int decode_exit_counter() { return 1; }
+DKV_HD constexpr int decode_queue(int hkv, bool host, int kvh) { return 2 + (host ? 0 : hkv) + kvh; }
+DKV_HD constexpr int decode_counter_words(int hkv) { return 2 + 2 * hkv; }
 constexpr int kDecodeErrLayout = 1;     // a contiguous sequence's rows exceed its stride or pool
 constexpr int kDecodeErrPage = 2;       // a page entry is negative or beyond its tier's pool
 constexpr int kDecodeErrSlot = 4;       // an appended token has no valid cache slot
@@ -314,6 +319,11 @@ struct StageArgs {
 // decode kernel (grid = Hkv * (team_h + team_d)).
 int launch_decode_tiers(const DecodeArgs& a, int32_t* tier_counts, int32_t* tier_pages, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
+// The static decode scratch of the current device (dkv_decode.hip): its
+// device address (from hipGetSymbolAddress, once per device) and size.
+constexpr size_t kDecodeStaticScratchBytes = DKV_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+int decode_static_scratch(void** ptr, size_t* bytes);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
 // (cos, sin) in fp64 of the rotation angles of every prefill row:

@@ -252,6 +252,27 @@ dkv_status dkv_decode_step(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_h
                            double rope_theta, void* workspace, size_t workspace_bytes, float* out_o,
                            float* out_lse, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The fused decode step for callers that cannot allocate device memory
+ * (code under graph capture that must not allocate, serving loops and
+ * harnesses that forbid hipMalloc): dkv_decode_step with the library's own
+ * scratch in place of the caller's workspace.  The scratch is a static device
+ * array of DKV_STATIC_SCRATCH_BYTES on every GPU the library runs on (held
+ * until the process ends); a shape whose workspace (dkv_decode_step_plan)
+ * exceeds it is rejected with DKV_ERR_UNSUPPORTED.  The call allocates
+ * nothing.  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (different streams, or threads) race and must not be issued.
+ * dkv_decode_errors reads its flags with the array's address, which this
+ * ABI does not expose; DKV_DEBUG_VALIDATE checks layouts on the host instead.
+ * ---------------------------------------------------------------------- */
+#define DKV_STATIC_SCRATCH_BYTES (64u << 20)
+
+dkv_status dkv_decode_step_static(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads, const void* q,
+                                  const int32_t* q_pos, const int32_t* seq_lens, const int32_t* pos_new,
+                                  const void* x, int32_t hidden, const void* wk, const void* wv,
+                                  const void* k_new, const void* v_new, double offload_ratio, float scale,
+                                  double rope_theta, float* out_o, float* out_lse, void* stream);
+
 /* Layout errors the decode kernels flagged in this workspace since it was
  * last cleared (bit 1: contiguous rows beyond a stride or pool, 2: page entry
  * unmapped or beyond its pool, 4: appended token without a slot, 8: partial
