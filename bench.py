@@ -351,6 +351,62 @@ def best_split(sweep, bw_h, bw_d):
             "r0_ms_median": r0["ms_median"] if r0 else None}
 
 
+def measure_staged(dk, cfg, seed, flags, ratios, chunks, iters, bw_h, bw_d):
+    """The staged-prefetch comparator against the zero-copy path on the same
+    cache (SplitKernel README, Overview: the conventional design copies the
+    offloaded data into GPU memory before computing): attention only (no
+    append), flushed steps.  Staging writes the host-tier bytes into HBM and
+    reads them back, so it adds 2x those bytes of HBM traffic and holds a ring
+    of 2 x chunk rows of K and V."""
+    import numpy as np
+    import torch
+    from decode_attention_host_amd.cache_build import SplitView, contiguous_cache
+    from synth import kv_raw, query
+    L, hq, hkv, d, th = cfg["lens"][0], cfg["hq"], cfg["hkv"], cfg["d"], cfg["theta"]
+    ks, vs = kv_raw(seed, [L], hkv, d)
+    host_full = contiguous_cache(hkv, d, [L], 1.0, ks, vs, th, host_flags=flags)
+    dev_full = contiguous_cache(hkv, d, [L], 0.0, ks, vs, th)
+    del ks, vs
+    q = torch.from_numpy(query(seed, 1, hq, d).view(np.int16)).cuda()
+    qpos = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
+    sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    row = hkv * d * 2 * 2
+    out = []
+    for r in ratios:
+        view = SplitView(host_full, dev_full, L, r)
+        bufs = dk.alloc_decode_buffers(view, 1, hq, [L], r)
+        zc = flushed_steps(dk, lambda: dk.decode(view, q, qpos, sl, r, scale, th, bufs=bufs), iters, flush)
+        nh = view.n_host
+        hb, db = nh * row, (L - nh) * row
+        t_star = max(hb / (bw_h * 1e6), db / (bw_d * 1e6))
+        rec = {"ratio": round(r, 5), "host_bytes": hb, "hbm_bytes": db, "roofline_ms_measured": round(t_star, 5),
+               "zero_copy_ms": zc["ms_median"], "zero_copy_kernel_ms": zc["kernel_ms"], "staged": []}
+        for chunk in chunks:
+            info = dk.decode_staged_plan(view, hq, L, r, chunk)
+            ws = torch.zeros(max(256, info["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+            oo = torch.empty((hq, d), dtype=torch.float32, device="cuda")
+            ol = torch.empty((hq,), dtype=torch.float32, device="cuda")
+            f = flushed_steps(dk, lambda: dk.decode_staged(view, q, qpos, L, r, scale, th, chunk, workspace=ws,
+                                                             out_o=oo, out_lse=ol), iters, flush)
+            diff = float((oo - bufs.out_o[0]).abs().max())
+            rec["staged"].append({"chunk_tokens": chunk, "chunks": info["host_items"], "ms_median": f["ms_median"],
+                                  "ms_p90": f["ms_p90"], "vs_zero_copy": round(f["ms_median"] / zc["ms_median"], 4),
+                                  "ring_bytes": 2 * chunk * row, "staging_hbm_bytes": 2 * info["staged_bytes"],
+                                  "hbm_traffic_factor": round((db + 2 * info["staged_bytes"]) / max(1, db), 3)
+                                  if db else None,
+                                  "max_abs_diff_vs_zero_copy": diff})
+            del ws
+            log(f"[bench] staged {cfg['name']} r={r:.4f} chunk={chunk}: {f['ms_median']:.4f} ms vs zero-copy "
+                f"{zc['ms_median']:.4f} ms")
+        out.append(rec)
+    del flush
+    host_full.free()
+    dev_full.free()
+    return out
+
+
 def measure_fused_paged(dk, cfg, seed, flags, steps, warmup):
     """Ragged batch over a paged cache: the new token projected from its hidden
     state (x Wk, x Wv), rotated and appended at L_b, then attention over L_b + 1."""
@@ -669,7 +725,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--tune", default="", help="comma list of dkv_tuning fields, e.g. host_wgs=256")
     ap.add_argument("--extra", default="tiny,llama3_8b_32k,opt_6_7b_b8,fused_ragged,llama3_8b_prefill_2k,"
-                                       "llama3_8b_mlp_up_linear",
+                                       "llama3_8b_mlp_up_linear,staged_prefetch",
                     help="other workloads measured after the headline ('' for none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: headline steps plus two calibration reads of known "
@@ -807,8 +863,17 @@ def main():
 
     workloads = {}
     for name in [x for x in args.extra.split(",") if x]:
-        wcfg = workload(name, seed=args.seed)
         t0 = time.time()
+        if name == "staged_prefetch":
+            r_star = bw_h / (bw_h + bw_d)
+            workloads[name] = {
+                "llama3_8b_32k": measure_staged(dk, workload("llama3_8b_32k", seed=args.seed), args.seed, flags,
+                                                [r_star, 0.25, 1.0], [2048, 8192], 10, bw_h, bw_d),
+                "llama3_8b_1m": measure_staged(dk, workload("llama3_8b_1m", seed=args.seed), args.seed, flags,
+                                               [r_star, 0.25, 1.0], [4096, 16384, 65536], 5, bw_h, bw_d)}
+            log(f"[bench] {name} measured in {time.time() - t0:.1f}s")
+            continue
+        wcfg = workload(name, seed=args.seed)
         if wcfg.get("layout") == "linear":
             workloads[name] = measure_linear(dk, wcfg, args.seed, 20, bw_h, bw_d)
         elif "new" in wcfg:

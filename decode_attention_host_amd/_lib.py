@@ -134,6 +134,8 @@ SIGNATURES = {
     "dkv_decode_errors": (I32, [C.POINTER(KvDesc), P, I32, C.POINTER(I32)]),
     "dkv_decode_step_static": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, P, P, I32, P, P, P, P, F64, F32, F64,
                                      P, P, P]),
+    "dkv_decode_staged_plan": (I32, [C.POINTER(KvDesc), I32, I64, F64, I32, C.POINTER(PlanInfo)]),
+    "dkv_decode_staged": (I32, [C.POINTER(KvDesc), I32, P, P, I64, F64, F32, F64, I32, P, SZ, P, P, P]),
     "dkv_linear_plan": (I32, [I32, I32, I32, F64, C.POINTER(PlanInfo)]),
     "dkv_linear_split": (I32, [P, P, I32, I32, F64, P, I32, P, P, SZ, P]),
     "dkv_linear_plan_inspect": (I32, [I32, I32, F64, I32, P, I32, C.POINTER(PlanInfo)]),

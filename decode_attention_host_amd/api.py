@@ -464,6 +464,36 @@ def decode_step_static(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq
     return out_o, out_lse
 
 
+def decode_staged_plan(cache: KVCache, num_q_heads: int, seq_len: int, ratio: float, chunk_tokens: int) -> dict:
+    """dkv_decode_staged_plan."""
+    d = cache.desc()
+    info = PlanInfo()
+    check(lib().dkv_decode_staged_plan(C.byref(d), int(num_q_heads), int(seq_len), float(ratio), int(chunk_tokens),
+                                       C.byref(info)))
+    return info.as_dict()
+
+
+def decode_staged(cache: KVCache, q: torch.Tensor, q_pos: torch.Tensor, seq_len: int, ratio: float, scale: float,
+                  rope_theta: float, chunk_tokens: int, *, workspace: torch.Tensor | None = None, out_o=None,
+                  out_lse=None, stream=None):
+    """dkv_decode_staged (one sequence): the host tier copied chunk by chunk
+    into an HBM ring by the DMA engine and attended from there; returns
+    (o [Hq, D], lse [Hq])."""
+    _, Hq, D = q.shape
+    if workspace is None:
+        info = decode_staged_plan(cache, Hq, seq_len, ratio, chunk_tokens)
+        workspace = torch.zeros(max(256, info["workspace_bytes"]), dtype=torch.uint8, device=q.device)
+    if out_o is None:
+        out_o = torch.empty((Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None:
+        out_lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    d = cache.desc()
+    check(lib().dkv_decode_staged(C.byref(d), int(Hq), _ptr(q), _ptr(q_pos), int(seq_len), float(ratio),
+                                  float(scale), float(rope_theta), int(chunk_tokens), _ptr(workspace),
+                                  workspace.numel(), _ptr(out_o), _ptr(out_lse), _stream(stream)))
+    return out_o, out_lse
+
+
 def decode_errors(cache: KVCache, workspace: torch.Tensor, clear: bool = True) -> int:
     """dkv_decode_errors: layout error flags the decode kernels left in ``workspace``."""
     d = cache.desc()

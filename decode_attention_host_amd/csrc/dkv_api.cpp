@@ -52,6 +52,8 @@ dkv_status dkv::success() { return ok(); }
 
 namespace {
 
+constexpr int kMaxCopyDevices = 64;
+
 bool debug_validate() {
   static const bool on = [] {
     const char* v = getenv("DKV_DEBUG_VALIDATE");
@@ -604,6 +606,67 @@ dkv_status validate_decode_common(const dkv_kv_desc* kv, const void* q, const in
   return DKV_OK;
 }
 
+// ---------------------------------------------------------------- staged prefetch
+//
+// The conventional design the zero-copy path is compared with (SplitKernel
+// README, Overview: prefetching offloaded data into GPU memory costs HBM
+// traffic and capacity and leaves pipeline bubbles): the host tier is copied
+// by the DMA engine, chunk by chunk, into a two-slot HBM ring on a copy
+// stream; each staged chunk is attended from HBM (one launch of the fused
+// decode kernel, no new token) while the next chunk is copied; the HBM tier is
+// attended alongside; the per-chunk results are merged by log-sum-exp.
+
+struct StagedLayout {
+  int64_t nh = 0, nd = 0;        // host / HBM tokens of the sequence
+  int32_t chunk = 0, n_chunks = 0, n_rows = 0;
+  DecodeShape step;              // workspace of the per-chunk decode launches
+  size_t ring_off = 0, ring_slot_bytes = 0, part_o_off = 0, part_lse_off = 0, ints_off = 0, total = 0;
+};
+
+dkv_status staged_layout(const dkv_kv_desc* kv, int32_t hq, int64_t seq_len, double ratio, int32_t chunk,
+                         StagedLayout* out) {
+  if (kv->page_size != 0) return set_err(DKV_ERR_UNSUPPORTED, "the staged comparator takes the contiguous layout");
+  if (seq_len < 1 || seq_len > INT32_MAX) return set_err(DKV_ERR_INVALID, "seq_len must be in [1, 2^31)");
+  if (chunk < 64 || chunk % 64) return set_err(DKV_ERR_INVALID, "chunk_tokens must be a positive multiple of 64");
+  if (validate_ratio(ratio) != DKV_OK) return DKV_ERR_INVALID;
+  StagedLayout L;
+  int64_t ph;
+  dkv::contig_tiers(ratio, seq_len, seq_len, &L.nh, &L.nd, &ph);
+  if (L.nh > kv->host_stride || L.nh > kv->host_rows || L.nd > kv->dev_stride || L.nd > kv->dev_rows)
+    return set_err(DKV_ERR_INVALID, "the sequence's rows exceed the layout");
+  L.chunk = chunk;
+  L.n_chunks = (int32_t)((L.nh + chunk - 1) / chunk);
+  L.n_rows = L.n_chunks + (L.nd > 0 ? 1 : 0);
+  // every per-chunk launch reads an HBM-only view of `chunk` rows
+  dkv_kv_desc view = *kv;
+  view.host_k = view.host_v = nullptr;
+  view.host_rows = view.host_stride = 0;
+  view.dev_rows = view.dev_stride = std::max<int64_t>(chunk, L.nd);
+  view.dev_k = view.dev_v = reinterpret_cast<void*>(256);  // shape only
+  dkv_status st = decode_shape(&view, 1, hq, 0.0, true, 0, 0, &L.step);
+  if (st != DKV_OK) return st;
+  auto up = [](size_t a) { return (a + 255) / 256 * 256; };
+  const size_t row_bytes = (size_t)kv->num_kv_heads * kv->head_dim * 2;
+  L.ring_slot_bytes = up((size_t)chunk * row_bytes);
+  L.ring_off = up(L.step.total);
+  L.part_o_off = L.ring_off + 4 * L.ring_slot_bytes;  // two slots of K and of V
+  L.part_lse_off = up(L.part_o_off + (size_t)std::max(1, L.n_rows) * hq * kv->head_dim * 4);
+  L.ints_off = up(L.part_lse_off + (size_t)std::max(1, L.n_rows) * hq * 4);
+  L.total = up(L.ints_off + (size_t)(L.n_rows + 3) * 4);
+  *out = L;
+  return DKV_OK;
+}
+
+struct CopyEngine {
+  std::mutex mu;
+  hipStream_t stream[kMaxCopyDevices] = {};
+  hipEvent_t ev[kMaxCopyDevices][4] = {};
+};
+CopyEngine& copy_engine() {
+  static CopyEngine* c = new CopyEngine();
+  return *c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -981,6 +1044,116 @@ dkv_status dkv_decode_errors(const dkv_kv_desc* kv, const void* workspace, int32
   if (he == hipSuccess) he = hipDeviceSynchronize();
   if (he != hipSuccess) return hip_err(he, "reading the decode error word");
   return ok();
+}
+
+dkv_status dkv_decode_staged_plan(const dkv_kv_desc* kv, int32_t num_q_heads, int64_t seq_len, double offload_ratio,
+                                  int32_t chunk_tokens, dkv_plan_info* info) {
+  if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  StagedLayout L;
+  st = staged_layout(kv, num_q_heads, seq_len, offload_ratio, chunk_tokens, &L);
+  if (st != DKV_OK) return st;
+  const int64_t row_bytes = (int64_t)kv->num_kv_heads * kv->head_dim * 2;
+  *info = dkv_plan_info{};
+  info->workspace_bytes = (int64_t)L.total;
+  info->num_splits = L.n_rows;
+  info->host_items = L.n_chunks;
+  info->host_chunk = L.chunk;
+  info->host_bytes = L.nh * row_bytes * 2;
+  info->dev_bytes = L.nd * row_bytes * 2;
+  info->staged_bytes = L.nh * row_bytes * 2;
+  return ok();
+}
+
+dkv_status dkv_decode_staged(const dkv_kv_desc* kv, int32_t num_q_heads, const void* q, const int32_t* q_pos,
+                             int64_t seq_len, double offload_ratio, float scale, double rope_theta,
+                             int32_t chunk_tokens, void* workspace, size_t workspace_bytes, float* out_o,
+                             float* out_lse, void* stream) {
+  dkv_status st = validate_desc(kv);
+  if (st != DKV_OK) return st;
+  if (!q || !q_pos || !workspace || !out_o)
+    return set_err(DKV_ERR_INVALID, "q, q_pos, workspace and out_o are required");
+  if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  StagedLayout L;
+  st = staged_layout(kv, num_q_heads, seq_len, offload_ratio, chunk_tokens, &L);
+  if (st != DKV_OK) return st;
+  if (workspace_bytes < L.total)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_err(he, "current device");
+  if (dev < 0 || dev >= kMaxCopyDevices) return set_err(DKV_ERR_UNSUPPORTED, "device index %d", dev);
+  hipStream_t s = (hipStream_t)stream;
+  CopyEngine& ce = copy_engine();
+  std::lock_guard<std::mutex> lk(ce.mu);
+  if (!ce.stream[dev]) {  // the copy stream and its events, once per device (default priority)
+    he = hipStreamCreateWithFlags(&ce.stream[dev], hipStreamNonBlocking);
+    for (int k = 0; k < 4 && he == hipSuccess; ++k) he = hipEventCreateWithFlags(&ce.ev[dev][k], hipEventDisableTiming);
+    if (he != hipSuccess) return hip_err(he, "copy stream");
+  }
+  hipStream_t cs = ce.stream[dev];
+  hipEvent_t* copied = &ce.ev[dev][0];  // [2]
+  hipEvent_t* freed = &ce.ev[dev][2];   // [2]
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int hq = num_q_heads, D = kv->head_dim;
+  const size_t row_bytes = (size_t)kv->num_kv_heads * D * 2;
+  float* part_o = reinterpret_cast<float*>(ws + L.part_o_off);
+  float* part_lse = reinterpret_cast<float*>(ws + L.part_lse_off);
+  int32_t* ints = reinterpret_cast<int32_t*>(ws + L.ints_off);  // [n_rows] lengths, then offsets {0, n_rows}
+  std::vector<int32_t> host_ints(L.n_rows + 2);
+  for (int i = 0; i < L.n_chunks; ++i)
+    host_ints[i] = (int32_t)std::min<int64_t>(L.chunk, L.nh - (int64_t)i * L.chunk);
+  if (L.nd > 0) host_ints[L.n_chunks] = (int32_t)L.nd;
+  host_ints[L.n_rows] = 0;
+  host_ints[L.n_rows + 1] = L.n_rows;
+  he = hipMemcpyAsync(ints, host_ints.data(), host_ints.size() * 4, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_err(he, "chunk lengths upload");
+  // the ring is free once earlier work on the stream is done
+  he = hipEventRecord(freed[0], s);
+  if (he == hipSuccess) he = hipEventRecord(freed[1], s);
+  if (he != hipSuccess) return hip_err(he, "ring events");
+  auto view_of = [&](void* k, void* v, int64_t rows, int64_t stride) {
+    dkv_kv_desc w = *kv;
+    w.host_k = w.host_v = nullptr;
+    w.host_rows = w.host_stride = 0;
+    w.dev_k = k;
+    w.dev_v = v;
+    w.dev_rows = rows;
+    w.dev_stride = stride;
+    return w;
+  };
+  // the HBM tier, on the compute stream, while the first chunk is copied
+  if (L.nd > 0) {
+    const dkv_kv_desc w = view_of(kv->dev_k, kv->dev_v, L.nd, L.nd);
+    st = dkv_decode_step(&w, 1, hq, q, q_pos, ints + L.n_chunks, nullptr, nullptr, 0, nullptr, nullptr, nullptr,
+                         nullptr, 0.0, scale, rope_theta, ws, L.ring_off, part_o + (size_t)L.n_chunks * hq * D,
+                         part_lse + (size_t)L.n_chunks * hq, stream);
+    if (st != DKV_OK) return st;
+  }
+  for (int i = 0; i < L.n_chunks; ++i) {
+    const int slot = i & 1;
+    uint8_t* rk = ws + L.ring_off + (size_t)(2 * slot) * L.ring_slot_bytes;
+    uint8_t* rv = rk + L.ring_slot_bytes;
+    const size_t bytes = (size_t)host_ints[i] * row_bytes;
+    const size_t src_off = (size_t)i * L.chunk * row_bytes;
+    he = hipStreamWaitEvent(cs, freed[slot], 0);
+    if (he == hipSuccess)
+      he = hipMemcpyAsync(rk, static_cast<const uint8_t*>(kv->host_k) + src_off, bytes, hipMemcpyDefault, cs);
+    if (he == hipSuccess)
+      he = hipMemcpyAsync(rv, static_cast<const uint8_t*>(kv->host_v) + src_off, bytes, hipMemcpyDefault, cs);
+    if (he == hipSuccess) he = hipEventRecord(copied[slot], cs);
+    if (he == hipSuccess) he = hipStreamWaitEvent(s, copied[slot], 0);
+    if (he != hipSuccess) return hip_err(he, "staging copy");
+    const dkv_kv_desc w = view_of(rk, rv, L.chunk, L.chunk);
+    st = dkv_decode_step(&w, 1, hq, q, q_pos, ints + i, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0.0,
+                         scale, rope_theta, ws, L.ring_off, part_o + (size_t)i * hq * D, part_lse + (size_t)i * hq,
+                         stream);
+    if (st != DKV_OK) return st;
+    he = hipEventRecord(freed[slot], s);
+    if (he != hipSuccess) return hip_err(he, "ring events");
+  }
+  return dkv_merge_lse(part_o, part_lse, ints + L.n_rows, 1, hq, D, out_o, out_lse, stream);
 }
 
 dkv_status dkv_merge_lse(const float* part_o, const float* part_lse, const int32_t* split_offsets,

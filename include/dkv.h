@@ -397,6 +397,32 @@ dkv_status dkv_linear_plan_inspect(int32_t out_features, int32_t in_features, do
                                    int32_t num_cus, int32_t* items, int32_t items_cap, dkv_plan_info* info);
 
 /* ------------------------------------------------------------------------
+ * Staged-prefetch decode: the conventional design the zero-copy path is
+ * measured against (SplitKernel README, Overview: prefetching offloaded data
+ * into GPU memory costs extra HBM traffic and capacity, pipeline bubbles and
+ * unused aggregate bandwidth).  For one sequence (batch 1) of seq_len tokens
+ * in the contiguous-split layout, the host tier's floor(r * seq_len) tokens
+ * are copied by the DMA engine (hipMemcpyAsync on a library copy stream,
+ * created once per device at default priority) in chunks of chunk_tokens
+ * rows into a two-slot HBM ring in the workspace; each staged chunk is
+ * attended from HBM by one launch of the fused decode kernel (no new token)
+ * while the next one is copied, the HBM tier alongside, and the per-chunk
+ * results are merged by log-sum-exp into out_o [Hq][D] / out_lse [Hq].
+ * q [Hq][D] bf16 and q_pos [1] are device memory; the keys in the cache are
+ * already rotated.  dkv_decode_staged_plan gives the workspace size (the
+ * per-chunk decode scratch, the ring, the partials), staged_bytes the bytes
+ * copied into HBM and host_items the chunk count.  The workspace must be
+ * zero-filled before its first use (left zeroed).  Calls must not overlap.
+ * ---------------------------------------------------------------------- */
+dkv_status dkv_decode_staged_plan(const dkv_kv_desc* kv, int32_t num_q_heads, int64_t seq_len,
+                                  double offload_ratio, int32_t chunk_tokens, dkv_plan_info* info);
+
+dkv_status dkv_decode_staged(const dkv_kv_desc* kv, int32_t num_q_heads, const void* q, const int32_t* q_pos,
+                             int64_t seq_len, double offload_ratio, float scale, double rope_theta,
+                             int32_t chunk_tokens, void* workspace, size_t workspace_bytes, float* out_o,
+                             float* out_lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * LSE merge of partial results (the combine step implied by splitting one
  * sequence's KV over tiers and compute units: SplitKernel README, Key
  * Features; DirectKV README, Step 6, "SM-Parallel" kernel).
