@@ -694,14 +694,18 @@ def cpu_baseline(cfg, raw, budget_s):
             "ms_per_step_extrapolated": round(dt / done * hkv * 1e3, 1)}
 
 
-def load_traffic(workload_name):
+def load_traffic(workload_name, ratio, form):
+    """HBM + host-link bytes per launch of the decode kernel from the stored
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes of this workload, offload ratio
+    and step form, or None when none is stored or the kernel sources changed
+    since."""
     p = os.path.join(ROOT, "profiles", f"decode_{workload_name}_traffic.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("kernel_src_sha") != kernel_src_sha():
+    if t.get("kernel_src_sha") != kernel_src_sha() or t.get("offload_ratio") != ratio:
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t.get("forms", {}).get(form, {}).get("traffic_bytes_per_launch")
 
 
 def main():
@@ -729,7 +733,8 @@ def main():
                     help="other workloads measured after the headline ('' for none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: headline steps plus two calibration reads of known "
-                         "size (a 256 MiB HBM copy and a 64 MiB zero-copy read of the host pool)")
+                         "size (a 256 MiB HBM copy and a 1 GiB zero-copy read of the host pool, or "
+                         "all of it when smaller)")
     args = ap.parse_args()
     args.form_fixed = args.form is not None
     if args.form is None:
@@ -772,8 +777,10 @@ def main():
         src.fill_(3)
         dst.copy_(src)
         cache = st.cache
-        if cache.host_k is not None and cache.host_rows * hkv * d * 2 >= (64 << 20):
-            dk.probe_read(cache.host_k.dev_ptr, 64 << 20, 64, nontemporal=True, iters=1)
+        host_bytes = cache.host_rows * hkv * d * 2 if cache.host_k is not None else 0
+        if host_bytes >= (64 << 20):
+            dk.probe_read(cache.host_k.dev_ptr, min(host_bytes, 1 << 30) // (1 << 20) << 20, 64,
+                          nontemporal=True, iters=1)
         torch.cuda.synchronize()
         gpu_warm(step, 0.5)
         ms, _ = timed_loop(step, args.steps, args.warmup)
@@ -829,7 +836,7 @@ def main():
         meas_dma = None
     roofline = {"bound": "hbm" if not host_dominant else "host_link", "achieved": round(achieved, 3),
                 "peak": peak, "unit": "GB/s", "frac": round(achieved / peak, 4),
-                "traffic": load_traffic(cfg["name"]),
+                "traffic": load_traffic(cfg["name"], ratio, form),
                 "kernel": "decode_kernel (one-launch step: append + attention + merge)" if form == "fused"
                 else "decode_kernel (split attention)",
                 "kernel_ms": round(attn_ms, 5),

@@ -25,10 +25,13 @@
 //     counts) from device memory and derives the same items (dkv_decomp.h), so
 //     a call captured in a graph stays valid while the cache grows, and a step
 //     needs no host work beyond argument checks.
-//   * Teams.  A workgroup serves one KV head in one tier; the items of a tier
-//     are taken in order from the team's queue (first by index, then by an
-//     atomic counter), so every workgroup sees its sequences in increasing
-//     order and its rotated query changes only with the sequence.
+//   * Queues.  Each tier has its own queue of units, taken in order (first by
+//     index, then by an atomic counter), so a workgroup sees its sequences in
+//     increasing order.  Split form: a unit is (item, KV head) with the KV
+//     head fastest, so the workgroups of a tier stream neighbouring rows of
+//     the same token range at once (DRAM page locality).  Fused form: a team of
+//     workgroups serves one KV head in one tier and takes that head's items,
+//     so a workgroup can carry its softmax state from one item to the next.
 //   * Fused form.  A workgroup keeps its online-softmax state across
 //     consecutive items of one sequence and writes one partial per run; the
 //     last run of a (sequence, KV head) to finish merges them.  Partials are

@@ -1,8 +1,6 @@
-// dkv_kernels.hip - gfx950 kernels of the zero-copy split decode attention path.
+// dkv_kernels.hip - gfx950 kernels of the prefill, linear and helper paths
+// (the decode attention kernels are in dkv_decode.hip).
 //
-//   attn_split_kernel     rotate the unit's query heads (Neox RoPE, fp64 angle), stream
-//                         K/V tiles of one tier into LDS, Q.K on MFMA, online softmax,
-//                         P.V on the vector ALUs, write (o, lse)
 //   merge_lse_kernel      combine per-split partials by log-sum-exp (one workgroup
 //   merge_lse_wave_kernel   per pair for few long lists, one wave per pair for many)
 //   append_kernel         Neox RoPE of new keys (fp64) + bf16 store into the cache slot
@@ -14,7 +12,8 @@
 //   stage_copy_kernel     copy of host-tier rows that prefill re-reads into HBM
 //   linear_split_kernel   y = x W^T with W split by rows between host memory and HBM
 //   linear_reduce_kernel  sum of the linear's K-range partials
-//   probe_read_kernel     streaming-read bandwidth probe with the attention load pattern
+//   probe_read_kernel     streaming-read bandwidth probe (grid-stride, blocked, or
+//                         row segments like the attention tiles)
 //
 // Method sources (page, section): DirectKV README, introduction (fused projection,
 // Neox RoPE and attention reading KV from CPU-pinned buffers) and Attribution
@@ -23,16 +22,12 @@
 // tier into on-chip memory; attention over a host/device partitioned KV cache).
 //
 // Design notes for CDNA4:
-//   * 64-lane waves, 256-thread workgroups (4 waves).  A tile is 64 tokens of one
-//     KV head: each thread moves D/32 16-byte chunks of K and of V per tile with
-//     coalesced loads (host-tier loads are non-temporal), stores them into LDS,
-//     and each wave then owns 16 of the 64 tokens.
-//   * Q.K^T runs on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims from LDS,
-//     B = the group's query heads; each rotated query (fp32) is split into a
-//     high and a low bf16 part placed in columns h and h+8, so the product keeps
-//     ~16 bits of the query and fp32 accumulation.
-//   * P.V runs on the vector ALUs with one or two output dims per lane: values
-//     are exact bf16, weights fp32, accumulation fp32.
+//   * 64-lane waves, 256-thread workgroups (4 waves).  Prefill tiles are 64
+//     keys of one KV head: each thread moves D/32 16-byte chunks of K and of V
+//     per tile with coalesced loads (host-tier loads are non-temporal) into LDS.
+//   * Both prefill products run on v_mfma_f32_16x16x32_bf16; operands that are
+//     not exact in bf16 (rotated queries, softmax weights) are split into a high
+//     and a low bf16 part so the product keeps ~16 bits and fp32 accumulation.
 //   * Host-role and HBM-role workgroups are disjoint (blockIdx below / above the
 //     host workgroup count) so both tiers stream concurrently.
 #include <hip/hip_runtime.h>
