@@ -38,6 +38,23 @@ def _decode(dk, cache, qb, lens, ratio, theta, q_pos=None):
     return o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
+def _step(dk, cache, qb, ks, vs, lens, ratio, theta):
+    """The one-launch fused step the bench times: each sequence's newest token
+    (position L_b - 1, the bits already cached) appended again, then attention
+    over all L_b tokens and the merge, in one launch."""
+    import torch
+    B, hq, d = qb.shape
+    q = torch.from_numpy(qb.view(np.int16)).cuda()
+    cached = torch.tensor([n - 1 for n in lens], dtype=torch.int32, device="cuda")
+    k_new = torch.from_numpy(np.stack([k[-1] for k in ks]).view(np.int16)).cuda()
+    v_new = torch.from_numpy(np.stack([v[-1] for v in vs]).view(np.int16)).cuda()
+    ws = dk.decode_step_workspace(cache, B, hq, ratio)
+    o, lse = dk.decode_step(cache, q, cached.clone(), cached, ratio, 1.0 / math.sqrt(d), theta,
+                            k_new=k_new, v_new=v_new, workspace=ws)
+    torch.cuda.synchronize()
+    return o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
 def _check(o, lse, ref_o, ref_l, what):
     eo = np.abs(o - ref_o).max()
     el = np.abs(lse - ref_l).max()
@@ -45,16 +62,23 @@ def _check(o, lse, ref_o, ref_l, what):
     assert eo <= TOL and el <= TOL, what
 
 
-def test_llama3_8b_32k_all_heads(dk):
+@pytest.mark.parametrize("ratio", [None, 0.25, 0.0079])
+def test_llama3_8b_32k_all_heads(dk, ratio):
+    """The headline 32k layer at its own ratio (all host), at a quarter offloaded
+    and at the 1M layer's best-split share r* (0.79%: 258 host tokens), split
+    form and fused step."""
     from decode_attention_host_amd.cache_build import contiguous_cache
     cfg = workload("llama3_8b_32k")
     L, hkv, hq, d, th = cfg["lens"][0], cfg["hkv"], cfg["hq"], cfg["d"], cfg["theta"]
+    r = cfg["ratio"] if ratio is None else ratio
     ks, vs = kv_raw(0, [L], hkv, d)
     qb = query(0, 1, hq, d)
-    cache = contiguous_cache(hkv, d, [L], cfg["ratio"], ks, vs, th)
-    o, lse = _decode(dk, cache, qb, [L], cfg["ratio"], th)
+    cache = contiguous_cache(hkv, d, [L], r, ks, vs, th)
     ro, rl = O.decode_sequence(qb[0], ks[0], vs[0], L - 1, th, 1 / math.sqrt(d))
-    _check(o[0], lse[0], ro, rl, "llama3_8b_32k")
+    o, lse = _decode(dk, cache, qb, [L], r, th)
+    _check(o[0], lse[0], ro, rl, f"llama3_8b_32k r={r} split form")
+    o, lse = _step(dk, cache, qb, ks, vs, [L], r, th)
+    _check(o[0], lse[0], ro, rl, f"llama3_8b_32k r={r} fused step")
     cache.free()
 
 
@@ -66,9 +90,11 @@ def test_opt_6_7b_b8_all_heads(dk):
     qb = query(0, cfg["batch"], hq, d)
     cache = contiguous_cache(hkv, d, lens, r, ks, vs, th)
     o, lse = _decode(dk, cache, qb, lens, r, th)
+    fo, fl = _step(dk, cache, qb, ks, vs, lens, r, th)
     for b in range(cfg["batch"]):
         ro, rl = O.decode_sequence(qb[b], ks[b], vs[b], lens[b] - 1, th, 1 / math.sqrt(d))
-        _check(o[b], lse[b], ro, rl, f"opt_6_7b_b8 seq {b}")
+        _check(o[b], lse[b], ro, rl, f"opt_6_7b_b8 seq {b} split form")
+        _check(fo[b], fl[b], ro, rl, f"opt_6_7b_b8 seq {b} fused step")
     cache.free()
 
 
@@ -82,10 +108,14 @@ def test_llama3_8b_1m_ratios_sampled_heads(dk):
     dev_full = contiguous_cache(hkv, d, [L], 0.0, ks, vs, th)
     heads = [0, 13, 31]  # KV heads 0, 3, 7
     ro, rl = O.decode_sequence(qb[0], ks[0], vs[0], L - 1, th, 1 / math.sqrt(d), heads=heads)
-    for r in (0.0, 0.75, 1.0):
+    # r* = BW_h / (BW_h + BW_d) with the measured 57.5 GB/s link and 7.2 TB/s
+    # HBM read (0.79%), half of it, and three larger shares; both step forms
+    for r in (0.0, 0.0040, 0.0079, 0.75, 1.0):
         view = SplitView(host_full, dev_full, L, r)
         o, lse = _decode(dk, view, qb, [L], r, th)
-        _check(o[0, heads], lse[0, heads], ro, rl, f"llama3_8b_1m r={r}")
+        _check(o[0, heads], lse[0, heads], ro, rl, f"llama3_8b_1m r={r} split form")
+        o, lse = _step(dk, view, qb, ks, vs, [L], r, th)
+        _check(o[0, heads], lse[0, heads], ro, rl, f"llama3_8b_1m r={r} fused step")
     host_full.free()
     dev_full.free()
     # the same tokens in permuted 16-token pages, all in HBM: the long HBM
@@ -117,6 +147,16 @@ def test_fused_ragged_full_sampled_sequences(dk):
                            wv=torch.from_numpy(wv.view(np.int16)).cuda(), rope_theta=th)
     qb = query(0, B, hq, d)
     o, lse = _decode(dk, cache, qb, ntok, 0.0, th)
+    # the fused step: projection of the same hidden states, the same slots
+    # written again, attention over L_b + 1 tokens and the merge in one launch
+    cached = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = dk.decode_step_workspace(cache, B, hq, 0.0, hid)
+    fo, fl = dk.decode_step(cache, torch.from_numpy(qb.view(np.int16)).cuda(), cached.clone(), cached, 0.0,
+                            1.0 / math.sqrt(d), th, x=torch.from_numpy(x.view(np.int16)).cuda(),
+                            wk=torch.from_numpy(wk.view(np.int16)).cuda(),
+                            wv=torch.from_numpy(wv.view(np.int16)).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    fo, fl = fo.cpu().numpy().astype(np.float64), fl.cpu().numpy().astype(np.float64)
     kk = O.project(O.bf16_to_f64(x), O.bf16_to_f64(wk)).reshape(B, hkv, d)
     vv = O.project(O.bf16_to_f64(x), O.bf16_to_f64(wv)).reshape(B, hkv, d)
     order = np.argsort(lens)
@@ -131,4 +171,5 @@ def test_fused_ragged_full_sampled_sequences(dk):
             q_rot = O.rope_neox(O.bf16_to_f64(qb[b][heads]), np.full(4, lens[b]), th)
             ro, rl = O.attention(q_rot, kst, vst, 1 / math.sqrt(d))
             _check(o[b, heads], lse[b, heads], ro, rl, f"fused_ragged seq {b} (L={lens[b]}) kv head {kvh}")
+            _check(fo[b, heads], fl[b, heads], ro, rl, f"fused_ragged seq {b} kv head {kvh}, fused step")
     cache.free()
