@@ -119,21 +119,30 @@ def kernel_times(dk, step, iters):
 
 def flushed_steps(dk, step, iters, flush):
     """Per-step times of `iters` steps with a read-only cache flush between
-    them (median, p10, p90) and the per-kernel times over the same steps."""
+    them (median, p10, p90), then the per-kernel times over a second pass of
+    the same steps (the library's event pair around each launch would
+    otherwise add to the step times)."""
     import torch
     gpu_warm(step, 0.2)
+    sink = torch.empty(iters, dtype=torch.float32, device="cuda")
+
+    def run(ev):
+        for i in range(iters):
+            torch.sum(flush, dim=0, out=sink[i])
+            if ev:
+                ev[i][0].record()
+            step()
+            if ev:
+                ev[i][1].record()
+        torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    run(ev)
+    t = sorted(a.elapsed_time(b) for a, b in ev)
     dk.kernel_timing(True)
     for k in dk.api.KERNELS:
         dk.kernel_timing_read(k)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    sink = torch.empty(iters, dtype=torch.float32, device="cuda")
-    for i in range(iters):
-        torch.sum(flush, dim=0, out=sink[i])
-        ev[i][0].record()
-        step()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in ev)
+    run(None)
     kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
     dk.kernel_timing(False)
     return {"ms_median": round(statistics.median(t), 5), "ms_p10": round(t[len(t) // 10], 5),
@@ -569,14 +578,11 @@ def measure_prefill(dk, cfg, seed, flags, steps, warmup):
     def timed(step):
         # median of five timed loops: a step of ~0.1 ms leaves the GPU idle
         # through any host-side stall of a few ms inside a single loop
+        # (step times without the library's per-launch event pairs; kernel
+        # times from one more loop with them)
         gpu_warm(step)
-        dk.kernel_timing(True)
-        for k in dk.api.KERNELS:
-            dk.kernel_timing_read(k)
         ms = statistics.median(timed_loop(step, steps, warmup)[0] for _ in range(5))
-        kt = {k: dk.kernel_timing_read(k) for k in dk.api.KERNELS}
-        dk.kernel_timing(False)
-        return ms, {k: v[1] / max(1, v[0]) for k, v in kt.items() if v[0]}
+        return ms, kernel_times(dk, step, steps)
 
     out = []
     for r in cfg.get("ratios", [cfg["ratio"]]):
@@ -637,7 +643,7 @@ def measure_linear(dk, cfg, seed, iters, bw_h, bw_d):
         for m in cfg["tokens"]:
             x = torch.from_numpy(normal_bf16(seed, 4, (m, K)).view(np.int16)).cuda()
             y = torch.empty((m, N), dtype=torch.float32, device="cuda")
-            ws = torch.empty(max(256, lin.plan(m)["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+            ws = lin.workspace(m)
             f = flushed_steps(dk, lambda: lin(x, y, ws), iters, flush)
             med = f["ms_median"]
             t_star = max(hb / (bw_h * 1e6), db / (bw_d * 1e6))

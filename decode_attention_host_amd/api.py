@@ -728,6 +728,11 @@ class OffloadedLinear:
     def plan(self, m: int) -> dict:
         return linear_plan(m, self.out_features, self.in_features, self.ratio)
 
+    def workspace(self, m: int, device="cuda") -> torch.Tensor:
+        """A zero-filled workspace for calls of up to m tokens (every call
+        leaves its counters at zero again)."""
+        return torch.zeros(max(256, self.plan(m)["workspace_bytes"]), dtype=torch.uint8, device=device)
+
     def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
         """y = x W^T for x [m][K] bf16 (int16 bits) on the device; returns y [m][N] fp32."""
@@ -737,7 +742,7 @@ class OffloadedLinear:
         if workspace is None:
             need = max(256, self.plan(m)["workspace_bytes"])
             if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=x.device)   # every call leaves it zeroed
             workspace = self._ws
         check(lib().dkv_linear_split(C.c_void_p(self.host.dev_ptr if self.host else 0),
                                      _ptr(self.dev), self.out_features, self.in_features, self.ratio,

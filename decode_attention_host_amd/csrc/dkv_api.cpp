@@ -390,7 +390,7 @@ struct TimedLaunch {
   }
 };
 
-// Offloaded-linear plan: tuning fields as for decode, cached by shape.
+// Offloaded-linear planner input: tuning fields as for decode.
 dkv::PlanInput linear_input(double ratio, int32_t cus, const dkv_tuning& t) {
   dkv::PlanInput in{};
   in.ratio = ratio;
@@ -408,36 +408,32 @@ dkv_status validate_linear(int32_t m, int32_t n, int32_t k, double ratio) {
   return validate_ratio(ratio);
 }
 
-dkv_status get_linear_plan(int32_t n, int32_t k, double ratio, std::shared_ptr<PlanEntry>* out) {
-  uint64_t gen = 0;
-  const dkv_tuning t = tuning_snapshot(&gen);
-  int dev = 0;
-  int cus = t.num_cus;
+// The linear call's shape: no plan image, the kernel derives its items.
+dkv_status get_linear_shape(int32_t n, int32_t k, double ratio, int32_t cus_override, dkv::LinearShape* z) {
+  const dkv_tuning t = tuning_snapshot(nullptr);
+  int cus = cus_override > 0 ? cus_override : t.num_cus;
   if (cus <= 0) {
+    int dev = 0;
     cus = device_cus(&dev);
     if (cus <= 0) return set_err(DKV_ERR_HIP, "cannot query the current device's CU count");
   }
-  std::string key("linear");
-  put(key, dev); put(key, cus); put(key, gen); put(key, n); put(key, k); put(key, ratio);
-  if (auto hit = cache_find(key)) {
-    *out = hit;
-    return DKV_OK;
-  }
-  auto e = std::make_shared<PlanEntry>();
-  std::vector<uint8_t> blob;
   std::string err;
-  if (!dkv::build_linear_plan(linear_input(ratio, cus, t), dkv::kLinMaxTokens, n, k, &e->lay, &blob, &err))
-    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
-  e->bytes = blob.size();
-  hipError_t he = hipHostMalloc(&e->pinned, e->bytes, hipHostMallocDefault);
-  if (he != hipSuccess) return set_err(DKV_ERR_NOMEM, "plan staging: %s", hipGetErrorString(he));
-  memcpy(e->pinned, blob.data(), e->bytes);
-  *out = cache_insert(key, e);
+  if (!dkv::linear_shape(linear_input(ratio, cus, t), n, k, z, &err)) return set_err(DKV_ERR_INVALID, "%s", err.c_str());
   return DKV_OK;
 }
 
-size_t linear_ws_bytes(const dkv::PlanLayout& L) {
-  return L.blob_bytes + (size_t)L.num_splits * dkv::kLinMaxTokens * dkv::kLinRows * 4;
+void fill_linear_info(const dkv::LinearShape& z, dkv_plan_info* info) {
+  *info = dkv_plan_info{};
+  info->workspace_bytes = (int64_t)z.ws_bytes;
+  info->num_splits = z.num_splits;
+  info->host_items = z.n_host_items;
+  info->dev_items = z.n_dev_items;
+  info->host_wgs = z.host_wgs;
+  info->dev_wgs = z.dev_wgs;
+  info->host_chunk = z.n_host_items ? z.kc_host : 0;
+  info->dev_chunk = z.n_dev_items ? z.kc_dev : 0;
+  info->host_bytes = z.host_bytes;
+  info->dev_bytes = z.dev_bytes;
 }
 
 // ---------------------------------------------------------------- decode shape
@@ -1186,10 +1182,10 @@ dkv_status dkv_linear_plan(int32_t m, int32_t out_features, int32_t in_features,
   if (!info) return set_err(DKV_ERR_INVALID, "info is NULL");
   dkv_status st = validate_linear(m, out_features, in_features, offload_ratio);
   if (st != DKV_OK) return st;
-  std::shared_ptr<PlanEntry> e;
-  st = get_linear_plan(out_features, in_features, offload_ratio, &e);
+  dkv::LinearShape z;
+  st = get_linear_shape(out_features, in_features, offload_ratio, 0, &z);
   if (st != DKV_OK) return st;
-  fill_info(e->lay, linear_ws_bytes(e->lay), info);
+  fill_linear_info(z, info);
   return ok();
 }
 
@@ -1198,18 +1194,16 @@ dkv_status dkv_linear_plan_inspect(int32_t out_features, int32_t in_features, do
   dkv_status st = validate_linear(1, out_features, in_features, offload_ratio);
   if (st != DKV_OK) return st;
   if (num_cus < 1) return set_err(DKV_ERR_INVALID, "num_cus must be >= 1");
-  dkv::PlanLayout L;
-  std::vector<uint8_t> blob;
-  std::string err;
-  if (!dkv::build_linear_plan(linear_input(offload_ratio, num_cus, tuning_snapshot(nullptr)), dkv::kLinMaxTokens,
-                              out_features, in_features, &L, &blob, &err))
-    return set_err(DKV_ERR_INVALID, "%s", err.c_str());
-  const dkv::LinearItem* it = reinterpret_cast<const dkv::LinearItem*>(blob.data());
-  for (int i = 0; items && i < L.n_host_items + L.n_dev_items && i < items_cap; ++i) {
+  dkv::LinearShape z;
+  st = get_linear_shape(out_features, in_features, offload_ratio, num_cus, &z);
+  if (st != DKV_OK) return st;
+  std::vector<dkv::LinearItem> it;
+  dkv::linear_items(z, out_features, in_features, &it);
+  for (int i = 0; items && i < (int)it.size() && i < items_cap; ++i) {
     int32_t* o = items + 6 * (size_t)i;
     o[0] = it[i].pool; o[1] = it[i].row0; o[2] = it[i].n_rows; o[3] = it[i].k0; o[4] = it[i].k1; o[5] = it[i].slot;
   }
-  if (info) fill_info(L, linear_ws_bytes(L), info);
+  if (info) fill_linear_info(z, info);
   return ok();
 }
 
@@ -1222,46 +1216,41 @@ dkv_status dkv_linear_split(const void* host_w, const void* dev_w, int32_t out_f
   if ((uintptr_t)workspace % 256) return set_err(DKV_ERR_INVALID, "workspace must be 256-byte aligned");
   if (((uintptr_t)x | (uintptr_t)host_w | (uintptr_t)dev_w) % 16)
     return set_err(DKV_ERR_INVALID, "x and the weights must be 16-byte aligned");
-  std::shared_ptr<PlanEntry> e;
-  st = get_linear_plan(out_features, in_features, offload_ratio, &e);
+  dkv::LinearShape z;
+  st = get_linear_shape(out_features, in_features, offload_ratio, 0, &z);
   if (st != DKV_OK) return st;
-  const dkv::PlanLayout& L = e->lay;
-  if (L.n_host_items > 0 && !host_w) return set_err(DKV_ERR_INVALID, "host_w is required for offload_ratio > 0");
-  if (L.n_dev_items > 0 && !dev_w) return set_err(DKV_ERR_INVALID, "dev_w is required for offload_ratio < 1");
-  if (workspace_bytes < linear_ws_bytes(L))
-    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, linear_ws_bytes(L));
+  if (z.n_host_items > 0 && !host_w) return set_err(DKV_ERR_INVALID, "host_w is required for offload_ratio > 0");
+  if (z.n_dev_items > 0 && !dev_w) return set_err(DKV_ERR_INVALID, "dev_w is required for offload_ratio < 1");
+  if (workspace_bytes < z.ws_bytes)
+    return set_err(DKV_ERR_INVALID, "workspace too small: %zu < %zu bytes", workspace_bytes, z.ws_bytes);
   hipStream_t s = (hipStream_t)stream;
-  if (stream_capturing(s)) {
-    std::lock_guard<std::mutex> lk(cache().mu);
-    e->captured = true;
-  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   dkv::LinearArgs a{};
-  a.host_items = reinterpret_cast<const dkv::LinearItem*>(ws);
-  a.dev_items = a.host_items + L.n_host_items;
-  a.counters = reinterpret_cast<int32_t*>(ws + L.counters_off);
-  a.n_host_items = L.n_host_items;
-  a.n_dev_items = L.n_dev_items;
-  a.host_wgs = L.host_wgs;
-  a.dev_wgs = L.dev_wgs;
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.n_host_items = z.n_host_items;
+  a.n_dev_items = z.n_dev_items;
+  a.host_wgs = z.host_wgs;
+  a.dev_wgs = z.dev_wgs;
   a.n = out_features;
   a.k = in_features;
-  a.n_host = (int32_t)(L.host_bytes / 2 / in_features);
+  a.n_host = z.n_host;
+  a.bh = z.bh;
+  a.kc_host = z.kc_host;
+  a.kc_dev = z.kc_dev;
+  a.sp_host = z.sp_host;
+  a.sp_dev = z.sp_dev;
+  a.p_host = z.sp_host > 1 ? z.n_host_items : 0;
   a.host_w = static_cast<const uint16_t*>(host_w);
   a.dev_w = static_cast<const uint16_t*>(dev_w);
-  a.part = L.num_splits > 0 ? reinterpret_cast<float*>(ws + L.blob_bytes) : nullptr;
-  a.blocks = reinterpret_cast<const dkv::LinearBlock*>(ws + L.plist_off);
-  a.n_blocks = L.n_plist;
-  // tokens in launches of up to 64; each launch re-uploads the plan image
-  // (its counters start at zero)
+  a.part = z.num_splits > 0 ? reinterpret_cast<float*>(ws + z.part_off) : nullptr;
+  // tokens in launches of up to 64, one launch each (every launch leaves the
+  // workspace counters at zero)
   for (int32_t m0 = 0; m0 < m; m0 += dkv::kLinMaxTokens) {
-    hipError_t he = hipMemcpyAsync(ws, e->pinned, e->bytes, hipMemcpyHostToDevice, s);
-    if (he != hipSuccess) return hip_err(he, "plan upload");
     a.m = std::min(dkv::kLinMaxTokens, m - m0);
     a.x = static_cast<const uint16_t*>(x) + (size_t)m0 * in_features;
     a.y = y + (size_t)m0 * out_features;
     TimedLaunch tl(DKV_KERNEL_LINEAR, s);
-    he = (hipError_t)dkv::launch_linear(a, stream);
+    hipError_t he = (hipError_t)dkv::launch_linear(a, stream);
     tl.done();
     if (he != hipSuccess) return hip_err(he, "linear launch");
   }

@@ -1,6 +1,6 @@
 // dkv_device.h - device helpers shared by the gfx950 kernel files: bf16
-// conversions with one rounding, vector types, and the cache slot of an
-// appended token.
+// conversions with one rounding, vector types, and buffer accesses coherent
+// across XCDs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,5 +45,31 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
   if (em >= 0x7f80u) em = 0x7f80u;                           // overflow -> inf
   return sign | em;
 }
+
+// Buffer accesses that are coherent across XCDs: cache policy sc1 makes a
+// store write through to the device-coherent level and a load read from it,
+// so no L2 write-back or invalidate is needed around them.
+constexpr int kCoherent = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, int byte_off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void coherent_store1(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ floatx4 coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
+}
+
+// Waits until this thread's stores are acknowledged (written at the coherent
+// level for the sc1 stores above).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace dkv

@@ -82,11 +82,28 @@ struct LinearItem {
   int32_t pad[2];
 };
 static_assert(sizeof(LinearItem) == 32, "LinearItem layout");
-struct LinearBlock {  // partial slots base .. base + n_splits - 1 of rows row0 ..
-  int32_t row0;
-  int32_t n_rows;
-  int32_t base;
-  int32_t n_splits;
+
+// The items of a linear call follow from this shape alone (the kernel derives
+// them; the planner lists them for introspection).  Host tier first: row block
+// j of a tier covers rows r0 + 64 j .. (r0 = 0 host, n_host HBM) and is cut
+// into sp K ranges of kc (the last one shorter); item i of a tier is block
+// i / sp, range i % sp.  In a tier with sp > 1 item i writes partial slot i
+// (host) or p_host + i (HBM; p_host = host items if the host tier is split,
+// else 0), and the last range of a block to finish sums its slots in order
+// into y; with sp = 1 an item writes y directly.
+struct LinearShape {
+  int32_t n_host = 0;         // output rows in host memory
+  int32_t bh = 0, bd = 0;     // row blocks per tier
+  int32_t kc_host = 0, kc_dev = 0;
+  int32_t sp_host = 1, sp_dev = 1;
+  int32_t host_wgs = 0, dev_wgs = 0;
+  int32_t n_host_items = 0, n_dev_items = 0;
+  int32_t num_splits = 0;     // partial slots (0: no K split)
+  int64_t host_bytes = 0, dev_bytes = 0;
+  // workspace: [4 + bh + bd] int32 counters (zero between calls), then the
+  // partials [num_splits][kLinMaxTokens][kLinRows] fp32
+  size_t part_off = 0;
+  size_t ws_bytes = 0;
 };
 
 // Host-side result of planning; the device image is `blob` (items, then the
@@ -282,9 +299,8 @@ struct PrefillArgs {
 };
 
 struct LinearArgs {
-  const LinearItem* host_items;
-  const LinearItem* dev_items;
-  int32_t* counters;             // [2], zero at launch
+  int32_t* counters;             // [0] HBM queue, [1] host queue, [2] exit, [3] unused, [4 + block]
+                                 // ranges done per row block; zero at launch, left zero
   int32_t n_host_items;
   int32_t n_dev_items;
   int32_t host_wgs;
@@ -293,14 +309,15 @@ struct LinearArgs {
   int32_t n;                     // out_features
   int32_t k;                     // in_features
   int32_t n_host;                // rows of W in host memory
+  int32_t bh;                    // host row blocks
+  int32_t kc_host, kc_dev;       // K per item
+  int32_t sp_host, sp_dev;       // items per row block
+  int32_t p_host;                // partial slots of the host tier (0 when it is not split)
   const uint16_t* host_w;        // [n_host][K]
   const uint16_t* dev_w;         // [N - n_host][K]
   const uint16_t* x;             // [m][K]
   float* y;                      // [m][N]
   float* part;                   // [S][kLinMaxTokens][kLinRows]
-  const LinearBlock* blocks;
-  int32_t n_blocks;
-  int32_t pad;
 };
 
 // Arguments of the staging copy (host rows -> HBM staging pool).
@@ -404,11 +421,10 @@ void decode_enumerate(const DecodeTemplate& t, int B, const int64_t* nh, const i
 bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32_t* q_pos0,
                         PlanLayout* out, std::vector<uint8_t>* blob, std::string* err);
 
-// Offloaded-linear plan (in.ratio, tuning fields and num_cus used).  Device
-// image: host items, dev items, row blocks (n_plist of them at plist_off),
-// counters.
-bool build_linear_plan(const PlanInput& in, int32_t M, int32_t N, int32_t K, PlanLayout* out,
-                       std::vector<uint8_t>* blob, std::string* err);
+// Offloaded-linear shape (in.ratio, tuning fields and num_cus used), and its
+// items in kernel order (for introspection).
+bool linear_shape(const PlanInput& in, int32_t N, int32_t K, LinearShape* out, std::string* err);
+void linear_items(const LinearShape& z, int32_t N, int32_t K, std::vector<LinearItem>* items);
 
 // Sets the calling thread's last-error message (dkv_last_error) and returns
 // st; success() clears it and returns DKV_OK.

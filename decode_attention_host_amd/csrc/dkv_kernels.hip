@@ -11,7 +11,6 @@
 //   prefill_split_kernel  causal prefill attention over both tiers, both products on MFMA
 //   stage_copy_kernel     copy of host-tier rows that prefill re-reads into HBM
 //   linear_split_kernel   y = x W^T with W split by rows between host memory and HBM
-//   linear_reduce_kernel  sum of the linear's K-range partials
 //   probe_read_kernel     streaming-read bandwidth probe (grid-stride, blocked, or
 //                         row segments like the attention tiles)
 //
@@ -665,11 +664,43 @@ __global__ __launch_bounds__(pf_threads<NTW>()) void prefill_split_kernel(Prefil
 // in flight across the MFMAs, 0.035 ms when each chunk's loads were waited
 // for right after issue; 512-wide chunks were no faster (0.026 ms).  The
 // host tier runs at the link rate either way.
+//
+// No host plan: item i of a tier is derived from the call's shape (row block
+// i / sp, K range i % sp).  When K is split, each range writes its partial
+// with agent-coherent stores, and the last range of a row block to finish
+// (per-block counter) sums the block's partials in slot order into y.  The
+// last workgroup to exit sets the queue and block counters back to zero, so
+// the workspace needs no upload or clear between calls.
 // ---------------------------------------------------------------------------
 constexpr int kLinKC = 256;  // K per chunk (8 k-steps)
 
+struct LinItem {
+  int row0, n_rows, k0, k1;
+  int slot;   // partial slot, < 0: y written directly
+  int blk;    // row block over both tiers (index of its counter)
+  int sp;     // K ranges of the block
+  int first;  // the block's first partial slot
+};
+
+__device__ __forceinline__ LinItem linear_item(const LinearArgs& a, bool host, int i) {
+  const int sp = host ? a.sp_host : a.sp_dev, kc = host ? a.kc_host : a.kc_dev;
+  const int blk = i / sp, s = i - blk * sp;
+  const int r0 = host ? 0 : a.n_host, r1 = host ? a.n_host : a.n;
+  LinItem it;
+  it.row0 = r0 + blk * kLinRows;
+  it.n_rows = min(kLinRows, r1 - it.row0);
+  it.k0 = s * kc;
+  it.k1 = min(a.k, it.k0 + kc);
+  it.slot = sp > 1 ? (host ? i : a.p_host + i) : -1;
+  it.blk = host ? blk : a.bh + blk;
+  it.sp = sp;
+  it.first = it.slot - s;
+  return it;
+}
+
 template <int MT, bool HOST>
-__device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds, uint8_t* w_lds, int* s_next_p) {
+__device__ __forceinline__ void linear_stream(const LinearArgs& a, uint8_t* x_lds, uint8_t* w_lds, int* s_next_p,
+                                              int* s_last_p) {
   constexpr int XP = kLinKC * 2 + 16;                   // bytes per staged row (x token or W row)
   constexpr int CPR = kLinKC * 2 / 16;                  // 16-byte columns per staged row
   constexpr int PASSES = kLinRows * CPR / kThreads;     // 16-byte W loads per thread per chunk
@@ -684,17 +715,17 @@ __device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds
   const int wg = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.host_wgs;
   const int nwg = host_role ? a.host_wgs : a.dev_wgs;
   const int nunits = host_role ? a.n_host_items : a.n_dev_items;
-  const LinearItem* __restrict__ items = host_role ? a.host_items : a.dev_items;
   int* counter = a.counters + (host_role ? 1 : 0);
   const uint16_t* __restrict__ wpool = host_role ? a.host_w : a.dev_w;
   const int row_shift = host_role ? 0 : a.n_host;
+  const __amdgpu_buffer_rsrc_t part_rsrc = coherent_rsrc(a.part);
 
   u32x4 wreg[PASSES], xreg[XPASSES];
   // Columns past k1 read the item's first column for W and are zeroed when
   // staged (a select right after the load would wait for it); x tokens past
   // m and columns past k1 are not loaded and stay zero.
   bool wz = false;
-  auto load_chunk = [&](const LinearItem& it, int kc) {
+  auto load_chunk = [&](const LinItem& it, int kc) {
     const int k = kc + wc * 8;
     const bool kok = k < it.k1;
     wz = !kok;
@@ -714,9 +745,9 @@ __device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds
   };
 
   int u = wg;
-  LinearItem it{};
+  LinItem it{};
   if (u < nunits) {
-    it = items[u];
+    it = linear_item(a, host_role, u);
     load_chunk(it, it.k0);
   }
   while (u < nunits) {
@@ -724,7 +755,7 @@ __device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
     int next_u = nunits;
-    LinearItem nit{};
+    LinItem nit{};
     for (int kc = it.k0; kc < it.k1; kc += kLinKC) {
       __syncthreads();  // previous chunk's readers are done
 #pragma unroll
@@ -738,14 +769,14 @@ __device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds
       __syncthreads();
       // one call site for the next chunk's loads, so that they land in the
       // same registers on both paths and stay in flight through the MFMAs
-      LinearItem lit = it;
+      LinItem lit = it;
       int lkc = kc + kLinKC;
       bool more = true;
       if (last) {
         next_u = s_next;
         more = next_u < nunits;
         if (more) {
-          nit = items[next_u];
+          nit = linear_item(a, host_role, next_u);
           lit = nit;
           lkc = nit.k0;
         }
@@ -775,8 +806,32 @@ __device__ __forceinline__ void linear_items(const LinearArgs& a, uint8_t* x_lds
           if (it.slot < 0)
             a.y[(size_t)tok * a.n + it.row0 + r] = acc[t][i];
           else
-            a.part[((size_t)it.slot * kLinMaxTokens + tok) * kLinRows + r] = acc[t][i];
+            coherent_store1(part_rsrc, ((it.slot * kLinMaxTokens + tok) * kLinRows + r) * 4, acc[t][i]);
         }
+    }
+    if (it.slot >= 0) {
+      // the last K range of this row block to finish sums the block's
+      // partials, in slot order, into y
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) {
+        int* done = a.counters + 4 + it.blk;
+        const int prev = atomicAdd(done, 1);
+        const bool fin = prev == it.sp - 1;
+        if (fin) __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last_p = fin;
+      }
+      __syncthreads();
+      if (*s_last_p) {
+        for (int e = tid; e < a.m * kLinRows; e += kThreads) {
+          const int rr = e % kLinRows, tok = e / kLinRows;
+          if (rr >= it.n_rows) continue;
+          float sum = 0.f;
+          for (int j = 0; j < it.sp; ++j)
+            sum += coherent_load1(part_rsrc, (((it.first + j) * kLinMaxTokens + tok) * kLinRows + rr) * 4);
+          a.y[(size_t)tok * a.n + it.row0 + rr] = sum;
+        }
+      }
     }
     u = next_u;
     it = nit;
@@ -788,24 +843,17 @@ __global__ __launch_bounds__(kThreads) void linear_split_kernel(LinearArgs a) {
   constexpr int XP = kLinKC * 2 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t x_lds[MT * 16 * XP];
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kLinRows * XP];
-  __shared__ int s_next;
+  __shared__ int s_next, s_last;
   if ((int)blockIdx.x < a.host_wgs)
-    linear_items<MT, true>(a, x_lds, w_lds, &s_next);
+    linear_stream<MT, true>(a, x_lds, w_lds, &s_next, &s_last);
   else
-    linear_items<MT, false>(a, x_lds, w_lds, &s_next);
-}
-
-// Sum of each row block's K-range partials, in slot order.
-__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(LinearArgs a) {
-  const int64_t total = (int64_t)a.n_blocks * a.m * kLinRows;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
-    const int r = (int)(i % kLinRows);
-    const int tok = (int)((i / kLinRows) % a.m);
-    const LinearBlock b = a.blocks[i / ((int64_t)kLinRows * a.m)];
-    if (r >= b.n_rows) continue;
-    float s = 0.f;
-    for (int j = 0; j < b.n_splits; ++j) s += a.part[((size_t)(b.base + j) * kLinMaxTokens + tok) * kLinRows + r];
-    a.y[(size_t)tok * a.n + b.row0 + r] = s;
+    linear_stream<MT, false>(a, x_lds, w_lds, &s_next, &s_last);
+  // the last workgroup out sets the queues back to zero (every workgroup
+  // has taken its last item before it gets here)
+  if (threadIdx.x == 0 && atomicAdd(a.counters + 2, 1) == (int)gridDim.x - 1) {
+    __hip_atomic_store(a.counters + 0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.counters + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.counters + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1415,11 +1463,6 @@ int launch_linear(const LinearArgs& a, void* stream) {
     hipLaunchKernelGGL(linear_split_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(linear_split_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.part == nullptr) return (int)e;
-  const int64_t total = (int64_t)a.n_blocks * a.m * kLinRows;
-  const int rg = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, 4096);
-  hipLaunchKernelGGL(linear_reduce_kernel, dim3(rg), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

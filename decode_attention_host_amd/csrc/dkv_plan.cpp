@@ -466,82 +466,74 @@ bool build_prefill_plan(const PlanInput& in, const int32_t* q_start, const int32
 // its weights directly from the remote tier.  W [N][K] is split by output
 // rows: rows [0, floor(r N)) in host memory, the rest in HBM.  An item is a
 // block of up to kLinRows rows of one tier and a range of the reduction
-// dimension; blocks split over K write partials that a reduce kernel sums
-// in a fixed order.
-bool build_linear_plan(const PlanInput& in, int32_t M, int32_t N, int32_t K, PlanLayout* out,
-                       std::vector<uint8_t>* blob, std::string* err) {
-  *out = PlanLayout{};
-  if (M < 1 || N < 1 || K < 1) return fail(err, "m, out_features and in_features must be >= 1");
+// dimension.  With at least a quarter as many row blocks as workgroups K
+// stays whole (no partials); with fewer, K is cut so that a tier has about
+// two items per workgroup, ranges of at least 1024, and the ranges of a block
+// are summed by the last of them to finish, in the same launch.  Measured on
+// MI355X for the 14336 x 4096 MLP up-projection from HBM (224 row blocks),
+// 1 token, one call after a cache flush: 0.031 ms unsplit on 224 workgroups,
+// 0.035 ms in 2 ranges, 0.036 in 4, 0.044 in 8.
+bool linear_shape(const PlanInput& in, int32_t N, int32_t K, LinearShape* out, std::string* err) {
+  *out = LinearShape{};
+  if (N < 1 || K < 1) return fail(err, "out_features and in_features must be >= 1");
   if (K % 8) return fail(err, "in_features must be a multiple of 8 (got %lld)", K);
   const int64_t nh = (int64_t)std::floor(in.ratio * (double)N);
   const int64_t nd = N - nh;
   const int64_t bh = ceil_div(nh, kLinRows), bd = ceil_div(nd, kLinRows);
   int32_t wh = 0, wd = 0;
   split_workgroups(in, nh * K, nd * K, &wh, &wd);
-  // K ranges per block: about two units per workgroup, ranges of >= 1024.
-  // With at least a quarter as many row blocks as workgroups K is not split:
-  // no partials and no reduce launch (the MLP up-projection's 224 HBM blocks
-  // on 512 workgroups: 0.043 ms per 1-token call unsplit against 0.051 ms
-  // split four ways on MI355X).
-  auto splits = [&](int64_t blocks, int32_t wgs, int32_t tuned) -> int64_t {
-    if (blocks == 0) return 1;
-    if (tuned > 0) return std::max<int64_t>(1, ceil_div(K, round_up(tuned, 32)));
-    if (4 * blocks >= (int64_t)wgs) return 1;
-    const int64_t c = ceil_div(2 * (int64_t)wgs, blocks);
-    return std::max<int64_t>(1, std::min<int64_t>(c, std::max<int64_t>(1, K / 1024)));
+  auto kchunk = [&](int64_t blocks, int32_t wgs, int32_t tuned) -> int64_t {
+    if (tuned > 0) return std::min<int64_t>(round_up(tuned, 32), round_up(K, 32));
+    if (blocks == 0 || 4 * blocks >= (int64_t)wgs) return round_up(K, 32);
+    const int64_t c = std::min<int64_t>(ceil_div(2 * (int64_t)wgs, blocks), std::max<int64_t>(1, K / 1024));
+    return round_up(ceil_div(K, c), 32);
   };
-  const int64_t ch = splits(bh, wh, in.host_chunk), cd = splits(bd, wd, in.dev_chunk);
-  const int64_t kh = round_up(ceil_div(K, ch), 32), kd = round_up(ceil_div(K, cd), 32);
-  const bool partial = ceil_div(K, kh) > 1 || ceil_div(K, kd) > 1;
-  std::vector<LinearItem> hitems, ditems;
-  std::vector<LinearBlock> blocks;
-  int64_t slot = 0;
-  for (int tier = 1; tier >= 0; --tier) {
-    const int64_t r0 = tier ? 0 : nh, r1 = tier ? nh : N;
-    const int64_t kc = tier ? kh : kd;
-    for (int64_t r = r0; r < r1; r += kLinRows) {
-      LinearBlock blk{};
-      blk.row0 = (int32_t)r;
-      blk.n_rows = (int32_t)std::min<int64_t>(kLinRows, r1 - r);
-      blk.base = (int32_t)slot;
-      for (int64_t k = 0; k < K; k += kc) {
-        LinearItem it{};
-        it.row0 = blk.row0;
-        it.n_rows = blk.n_rows;
-        it.k0 = (int32_t)k;
-        it.k1 = (int32_t)std::min<int64_t>(K, k + kc);
-        it.slot = partial ? (int32_t)slot++ : -1;
-        it.pool = tier ? kPoolHost : kPoolDev;
-        (tier ? hitems : ditems).push_back(it);
-        ++blk.n_splits;
-      }
-      blocks.push_back(blk);
-    }
-  }
-  if (slot > INT32_MAX / (kLinRows * kLinMaxTokens)) return fail(err, "too many linear partials");
-  out->n_host_items = (int32_t)hitems.size();
-  out->n_dev_items = (int32_t)ditems.size();
-  out->num_splits = (int32_t)slot;
-  out->host_wgs = hitems.empty() ? 0 : (int32_t)std::min<int64_t>(wh, (int64_t)hitems.size());
-  out->dev_wgs = ditems.empty() ? 0 : (int32_t)std::min<int64_t>(std::max(wd, 1), (int64_t)ditems.size());
-  out->host_chunk = hitems.empty() ? 0 : (int32_t)kh;
-  out->dev_chunk = ditems.empty() ? 0 : (int32_t)kd;
+  const int64_t kh = kchunk(bh, wh, in.host_chunk), kd = kchunk(bd, wd, in.dev_chunk);
+  const int64_t sh = ceil_div(K, kh), sd = ceil_div(K, kd);
+  const int64_t ih = bh * sh, id = bd * sd;
+  // a tier whose blocks are not split writes y directly
+  const int64_t ph = sh > 1 ? ih : 0, pd = sd > 1 ? id : 0;
+  const bool partial = ph + pd > 0;
+  // partial byte offsets are 32-bit buffer offsets
+  if (ph + pd > INT32_MAX / (kLinRows * kLinMaxTokens * 4)) return fail(err, "too many linear K ranges");
+  if (ih + id > INT32_MAX / 2) return fail(err, "too many linear items");
+  out->n_host = (int32_t)nh;
+  out->bh = (int32_t)bh;
+  out->bd = (int32_t)bd;
+  out->kc_host = (int32_t)kh;
+  out->kc_dev = (int32_t)kd;
+  out->sp_host = (int32_t)sh;
+  out->sp_dev = (int32_t)sd;
+  out->n_host_items = (int32_t)ih;
+  out->n_dev_items = (int32_t)id;
+  out->host_wgs = ih == 0 ? 0 : (int32_t)std::min<int64_t>(wh, ih);
+  out->dev_wgs = id == 0 ? 0 : (int32_t)std::min<int64_t>(std::max(wd, 1), id);
+  out->num_splits = partial ? (int32_t)(ph + pd) : 0;
   out->host_bytes = nh * K * 2;
   out->dev_bytes = nd * K * 2;
-  out->n_plist = (int32_t)blocks.size();
-  out->items_off = 0;
-  out->plist_off = round_up((hitems.size() + ditems.size()) * sizeof(LinearItem), 16);
-  out->counters_off = round_up(out->plist_off + blocks.size() * sizeof(LinearBlock), 16);
-  out->blob_bytes = round_up(out->counters_off + 4 * sizeof(int32_t), 256);
-  if (blob) {
-    blob->assign(out->blob_bytes, 0);
-    uint8_t* p = blob->data();
-    if (!hitems.empty()) memcpy(p, hitems.data(), hitems.size() * sizeof(LinearItem));
-    if (!ditems.empty())
-      memcpy(p + hitems.size() * sizeof(LinearItem), ditems.data(), ditems.size() * sizeof(LinearItem));
-    if (!blocks.empty()) memcpy(p + out->plist_off, blocks.data(), blocks.size() * sizeof(LinearBlock));
-  }
+  out->part_off = (size_t)round_up((4 + bh + bd) * (int64_t)sizeof(int32_t), 256);
+  out->ws_bytes = out->part_off + (size_t)out->num_splits * kLinMaxTokens * kLinRows * 4;
   return true;
+}
+
+void linear_items(const LinearShape& z, int32_t N, int32_t K, std::vector<LinearItem>* items) {
+  items->clear();
+  int32_t slot = 0;
+  for (int tier = 1; tier >= 0; --tier) {
+    const int64_t r0 = tier ? 0 : z.n_host, r1 = tier ? z.n_host : N;
+    const int64_t kc = tier ? z.kc_host : z.kc_dev;
+    for (int64_t r = r0; r < r1; r += kLinRows)
+      for (int64_t k = 0; k < K; k += kc) {
+        LinearItem it{};
+        it.row0 = (int32_t)r;
+        it.n_rows = (int32_t)std::min<int64_t>(kLinRows, r1 - r);
+        it.k0 = (int32_t)k;
+        it.k1 = (int32_t)std::min<int64_t>(K, k + kc);
+        it.slot = (tier ? z.sp_host : z.sp_dev) > 1 ? slot++ : -1;
+        it.pool = tier ? kPoolHost : kPoolDev;
+        items->push_back(it);
+      }
+  }
 }
 
 }  // namespace dkv

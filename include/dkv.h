@@ -380,8 +380,14 @@ dkv_status dkv_prefill_fused(const dkv_kv_desc* kv, int32_t batch, int32_t num_q
  * be NULL when it holds no rows.  x [m][K] bf16 and y [m][N] fp32 are device
  * memory; no bias; fp32 accumulation on MFMA.  in_features must be a multiple
  * of 8; x and the weights 16-byte aligned.  Both tiers stream at once, each on
- * its own workgroups; tokens run in launches of up to 64.  dkv_linear_plan
- * gives the workspace size (plan image plus K-split partials).
+ * its own workgroups; tokens run in launches of up to 64.  There is no host
+ * plan: the kernel derives its items (row blocks of 64 rows x K ranges) from
+ * the call's shape, and when K is split the last range of a row block to
+ * finish sums the block's partials in the same launch.  dkv_linear_plan gives
+ * the workspace size (counters plus K-split partials).  The workspace must be
+ * zero-filled before its first use; every call leaves its counters at zero,
+ * so a call needs no upload and can be captured in a graph.  Calls sharing a
+ * workspace must not overlap.
  * ---------------------------------------------------------------------- */
 dkv_status dkv_linear_plan(int32_t m, int32_t out_features, int32_t in_features, double offload_ratio,
                            dkv_plan_info* info);

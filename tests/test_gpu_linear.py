@@ -51,6 +51,7 @@ CASES = [
     (64, 256, 512, 0.75, 1.0),      # four token tiles
     (100, 300, 4096, 0.5, 0.02),    # two launches of tokens
     (5, 200, 3000, 0.0, 0.5),       # K split into ranges of 1504 and 1496: both end inside a chunk
+    (9, 8192, 4096, 0.01, 0.02),    # host tier split over K (2 blocks x 4 ranges), HBM tier whole
 ]
 
 
@@ -93,3 +94,59 @@ def test_linear_smallest_shapes(dk):
         x = normal_bf16(97, 4, (m, K))
         y = _run(dk, w, x, r)
         _check(y, O.linear(x, w), K, f"N={N} K={K} m={m} r={r}")
+
+
+def test_linear_workspace_reused_and_left_zeroed(dk):
+    """K split over both tiers (tuned ranges), partials summed in the launch:
+    calls of 100 tokens (two launches), 3 and 64 tokens on one workspace must
+    each match the oracle and leave the workspace counters at zero."""
+    import torch
+    N, K = 300, 2056
+    w = normal_bf16(98, 5, (N, K), std=0.05)
+    try:
+        dk.set_tuning(host_chunk=256, dev_chunk=512)
+        lin = dk.OffloadedLinear(w, 0.4)
+        info = lin.plan(100)
+        assert info["num_splits"] == info["host_items"] + info["dev_items"] > 0
+        ws = lin.workspace(100)
+        for m in (100, 3, 64):
+            x = normal_bf16(98 + m, 4, (m, K))
+            y = lin(torch.from_numpy(x.view(np.int16)).cuda(), workspace=ws)
+            torch.cuda.synchronize()
+            _check(y.cpu().numpy().astype(np.float64), O.linear(x, w), K, f"reused workspace m={m}")
+            assert int(torch.count_nonzero(ws[:256])) == 0, "counters not left at zero"
+        lin.free()
+    finally:
+        dk.reset_tuning()
+
+
+@pytest.mark.parametrize("tune", [{}, {"dev_chunk": 512, "host_chunk": 1024}])
+def test_linear_graph_replays_match_eager(dk, tune):
+    """A linear call captured in a HIP graph (no host plan: nothing is
+    uploaded per call) replays to the eager result bit for bit, with eager
+    calls on the same workspace between replays."""
+    import torch
+    N, K, m = 1000, 4096, 5
+    w = normal_bf16(99, 5, (N, K), std=0.02)
+    try:
+        if tune:
+            dk.set_tuning(**tune)
+        lin = dk.OffloadedLinear(w, 0.25)
+        ws = lin.workspace(m)
+        x = torch.from_numpy(normal_bf16(99, 4, (m, K)).view(np.int16)).cuda()
+        y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        lin(x, y, ws)
+        torch.cuda.synchronize()
+        eager = y.clone()
+        g = dk.StepGraph(lambda: lin(x, y, ws))
+        for i in range(4):
+            y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager), f"replay {i}"
+            lin(x, workspace=ws)
+            torch.cuda.synchronize()
+        _check(eager.cpu().numpy().astype(np.float64), O.linear(normal_bf16(99, 4, (m, K)), w), K, "graph case")
+        lin.free()
+    finally:
+        dk.reset_tuning()

@@ -22,7 +22,9 @@ def test_linear_plan_covers_rows_and_k(N, K, ratio):
     cover = np.zeros(N, dtype=np.int64)   # total k covered per row
     slots = [int(s) for s in items[:, 5] if s >= 0]
     assert len(slots) == len(set(slots)) == info["num_splits"]
-    assert (len(slots) == 0) or (len(slots) == len(items))
+    for pool in (0, 1):   # a tier's items all write partials (K split) or none do
+        tier = items[items[:, 0] == pool]
+        assert np.all(tier[:, 5] >= 0) or np.all(tier[:, 5] < 0)
     for pool, r0, nr, k0, k1, slot in items:
         assert 1 <= nr <= 64 and 0 <= k0 < k1 <= K and k0 % 32 == 0
         rows = np.arange(r0, r0 + nr)
