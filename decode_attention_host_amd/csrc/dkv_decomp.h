@@ -9,8 +9,10 @@
 // memory and HBM); a tier's tokens are numbered in tier order ("ordinals":
 // contiguous layout, the tier's rows in order; paged layout, the tier's pages
 // in logical order).  An item is a run of ordinals of one sequence in one
-// tier.  Workgroups are bound to one KV head ("team") and walk the items of
-// their tier in order, so every item is processed once per KV head.
+// tier, processed once per KV head.  Each tier has `team` workgroups per KV
+// head: the fused form binds each to one KV head and walks that head's items
+// in order; the split form walks (item, KV head) units in order, KV head
+// fastest, over all of the tier's workgroups.
 // SplitKernel README, Overview: both tiers stream at the same time; Key
 // Features: attention over a host/device partitioned KV cache.
 #pragma once

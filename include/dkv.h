@@ -148,8 +148,9 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
  *
  * No host planning per call: the kernel reads seq_lens (and, paged, the page
  * table) in device memory and cuts each sequence's tokens into work items
- * that each lie in one tier; items of the two tiers run at the same time on
- * disjoint sets of workgroups, each bound to one KV head.  Every item writes a
+ * that each lie in one tier; the two tiers run at the same time on disjoint
+ * sets of workgroups, each taking (item, KV head) units of its tier from a
+ * queue in the workspace.  Every (item, KV head) writes a
  * normalised partial (part_o [S][Hq][D] fp32, part_lse [S][Hq] fp32, natural
  * log) in the split slots of its sequence, and split_offsets (device int32
  * [batch+1]) receives the CSR bounds: sequence b owns splits
