@@ -92,11 +92,24 @@ int device_cus(int* dev_out) {
 }
 
 // ---------------------------------------------------------------- plan cache
+// A prefill plan: its device image in pinned host memory, the source of every
+// upload.  The image is freed with the last reference; uploads from it may
+// still be queued then, so the device is synchronised first (this happens
+// only on eviction, never on a cache hit).
 struct PlanEntry {
   dkv::PlanLayout lay;
-  void* pinned = nullptr;  // immutable device image, source of every upload
+  void* pinned = nullptr;
   size_t bytes = 0;
   bool captured = false;   // referenced by a captured graph: never evicted
+  PlanEntry() = default;
+  PlanEntry(const PlanEntry&) = delete;
+  PlanEntry& operator=(const PlanEntry&) = delete;
+  ~PlanEntry() {
+    if (pinned) {
+      (void)hipDeviceSynchronize();
+      (void)hipHostFree(pinned);
+    }
+  }
 };
 
 // True while `s` is capturing a graph (its work is recorded, not run).
@@ -194,14 +207,9 @@ std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<
       }
     }
   }
-  if (!evicted.empty()) {
-    (void)hipDeviceSynchronize();
-    for (auto& v : evicted)
-      if (v.use_count() == 1 && v->pinned) {
-        (void)hipHostFree(v->pinned);
-        v->pinned = nullptr;
-      }
-  }
+  // evicted images are freed (after a device synchronisation) by the last
+  // reference: here, or at the end of a call that still holds one
+  evicted.clear();
   return e;
 }
 
