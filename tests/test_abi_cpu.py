@@ -341,3 +341,22 @@ def test_planner_no_guided_tail_when_units_are_small(L):
     x = desc(hkv=8, d=128, host_rows=0, dev_rows=1 << 15, hs=1 << 15, ds=1 << 15)
     items, _, offs, info = inspect(L, x, 1, 32, lens, 0.0, cus=256)
     assert set(int(n) for n in items[:, 3]) == {int(info["dev_chunk"])}
+
+
+def test_decode_batch_bound(L):
+    # the decode kernel derives items for up to 512 sequences (per-sequence
+    # prefixes in LDS): 512 plans, 513 is refused before any HIP call
+    x = desc(hkv=2, d=64, host_rows=513 * 1024, dev_rows=513 * 1024, hs=1024, ds=1024)
+    lens = np.full(513, 100, dtype=np.int32)
+    from decode_attention_host_amd.api import set_tuning, reset_tuning
+    try:
+        set_tuning(num_cus=256)
+        info = dkv_lib.PlanInfo()
+        assert L.dkv_decode_plan(C.byref(x), 512, 8, lens.ctypes.data, 0.5, C.byref(info)) == dkv_lib.DKV_OK
+        assert info.num_splits >= 512
+        assert L.dkv_decode_plan(C.byref(x), 513, 8, lens.ctypes.data, 0.5, C.byref(info)) == \
+            dkv_lib.DKV_ERR_UNSUPPORTED
+        assert L.dkv_decode_step_plan(C.byref(x), 512, 8, 0.5, 0, C.byref(info)) == dkv_lib.DKV_OK
+        assert L.dkv_decode_step_plan(C.byref(x), 513, 8, 0.5, 0, C.byref(info)) == dkv_lib.DKV_ERR_UNSUPPORTED
+    finally:
+        reset_tuning()

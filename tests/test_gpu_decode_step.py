@@ -153,6 +153,33 @@ def test_step_paged_parity_and_append(dk, lens, hq, hkv, d, frac):
     cache.free()
 
 
+def test_max_batch_512_both_forms(dk):
+    """The largest batch the decode kernel takes (512 sequences, lengths 0..200
+    tokens, some empty, paged with pages split 50/50 between the tiers): the
+    fused step appends each new token and attends; then the split form
+    attends over the grown cache.  Every sequence against the oracle."""
+    import torch
+    from decode_attention_host_amd.cache_build import paged_cache
+    B, hq, hkv, d, theta = 512, 8, 2, 64, 1e4
+    lens = [int(x) for x in np.random.default_rng(512).integers(0, 201, B)]
+    lens[3] = lens[200] = 0
+    full = [L + 1 for L in lens]
+    ks, vs = kv_raw(512, full, hkv, d)
+    qb = query(512, B, hq, d)
+    pt, nh, nd = paged_table(512, full, 16, 0.5)
+    cache = paged_cache(hkv, d, full, pt, nh, nd, ks, vs, theta, upto=lens)
+    o, lse = dk.decode_step(cache, _bits(qb), _dev(lens), _dev(lens), 0.0, 1 / math.sqrt(d), theta,
+                            k_new=_bits(np.stack([k[L] for k, L in zip(ks, lens)])),
+                            v_new=_bits(np.stack([v[L] for v, L in zip(vs, lens)])))
+    torch.cuda.synchronize()
+    ro, rl = _oracle_step(qb, ks, vs, lens, theta)
+    _check(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl, "512 fused step")
+    so, sl, _ = dk.decode(cache, _bits(qb), _dev(lens), full, 0.0, 1 / math.sqrt(d), theta)
+    torch.cuda.synchronize()
+    _check(so.cpu().numpy().astype(np.float64), sl.cpu().numpy().astype(np.float64), ro, rl, "512 split form")
+    cache.free()
+
+
 def test_step_without_new_token_equals_split_form(dk):
     # no new token: the fused launch attends to the cached tokens only and must
     # agree with the split form (attention + merge) and the oracle
