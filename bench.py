@@ -343,6 +343,37 @@ def ratio_sweep(dk, cfg, seed, flags, ratios, iters, bw_h, bw_d, raw=None):
     return out
 
 
+def paged_hbm_point(dk, cfg, seed, ks, vs, iters, flush, bw_d, sweep):
+    """The same tokens in a paged cache of 16-token pages, all in HBM, at
+    seeded permuted physical pages: both forms timed like the sweep, against
+    the contiguous r = 0 point."""
+    import numpy as np
+    import torch
+    from decode_attention_host_amd.cache_build import paged_cache
+    from synth import paged_table, query
+    L, hq, hkv, d = cfg["lens"][0], cfg["hq"], cfg["hkv"], cfg["d"]
+    pt, nh, nd = paged_table(seed + 1, [L], 16, 0.0)
+    cache = paged_cache(hkv, d, [L], pt, nh, nd, ks, vs, cfg["theta"])
+    q = torch.from_numpy(query(seed, 1, hq, d).view(np.int16)).cuda()
+    k_new = torch.from_numpy(np.ascontiguousarray(ks[0][-1:]).view(np.int16)).cuda()
+    v_new = torch.from_numpy(np.ascontiguousarray(vs[0][-1:]).view(np.int16)).cuda()
+    st = DecodeSteps(dk, cfg, cache, 0.0, q, k_new, v_new, [L])
+    db = st.info()["dev_bytes"]
+    rec = {"layout": "paged, 16-token pages permuted in HBM", "hbm_bytes": db,
+           "roofline_ms_measured": round(db / (bw_d * 1e6), 5)}
+    for form in ("fused", "split"):
+        rec[form] = flushed_steps(dk, getattr(st, form), iters, flush)
+    rec["best_form"] = min(("fused", "split"), key=lambda k: rec[k]["ms_median"])
+    rec["ms_median"] = rec[rec["best_form"]]["ms_median"]
+    r0 = next((e for e in sweep if e["ratio"] == 0.0), None)
+    if r0:
+        rec["vs_contiguous_r0"] = round(r0["ms_median"] / rec["ms_median"], 3)
+    log(f"[bench] {cfg['name']} paged in HBM: fused {rec['fused']['ms_median']:.4f} ms, "
+        f"split {rec['split']['ms_median']:.4f} ms, vs contiguous r=0 {rec.get('vs_contiguous_r0')}")
+    cache.free()
+    return rec
+
+
 def best_split(sweep, bw_h, bw_d):
     """Fastest measured point vs the combined roofline total / (BW_h + BW_d)."""
     best = min(sweep, key=lambda e: e["ms_median"])
@@ -861,6 +892,9 @@ def main():
         ratios = [0.0, r_star / 2, r_star, 0.25, 0.5, 0.75, 0.9, 1.0]
         pts = ratio_sweep(dk, cfg, args.seed, flags, ratios, args.sweep_iters, bw_h, bw_d, raw=raw)
         sweep = {"r_star": round(r_star, 5), "points": pts, "best_split": best_split(pts, bw_h, bw_d)}
+        flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        sweep["paged_hbm"] = paged_hbm_point(dk, cfg, args.seed, raw[0], raw[1], args.sweep_iters, flush, bw_d, pts)
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline:

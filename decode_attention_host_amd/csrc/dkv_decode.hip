@@ -72,13 +72,18 @@ struct AttnShape {
 // ---------------------------------------------------------------------------
 // Paged layout: per sequence, the physical pages of each tier in logical order
 // and the tokens each tier holds among the sequence's first seq_lens[b].
-// One 1024-thread workgroup per sequence; each round takes 16 consecutive
-// page entries per thread (all loads issued before any is used) and places
-// them with a block-wide scan.  Entries that are negative or beyond their
-// tier's pool are left out (and flagged in the workspace).
+// Grid (chunks, batch): workgroup (c, b) places page entries [c CH, (c+1) CH)
+// of sequence b, CH = 1024 threads x 16 entries.  It first counts the valid
+// host and HBM entries before its chunk (strided loads, many in flight), so
+// the chunks of a long sequence run side by side with no dependency between
+// workgroups; then each thread takes 16 consecutive entries (all loads issued
+// before any is used) and places them with a block-wide scan.  Entries that
+// are negative or beyond their tier's pool are left out (and flagged by the
+// chunk that holds them).  The last chunk writes the sequence's counts.
 // ---------------------------------------------------------------------------
 constexpr int kTierThreads = 1024;
 constexpr int kTierPer = 16;
+constexpr int kTierChunk = kTierThreads * kTierPer;
 
 __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a, int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ pages) {
@@ -86,7 +91,8 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
   __shared__ int32_t s_wh[NW], s_wd[NW];
   __shared__ int32_t s_base[2];
   __shared__ int32_t s_last;  // tier of the sequence's final page: 1 host, 0 HBM, -1 none
-  const int b = blockIdx.x;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = 1 << a.page_shift;
   int64_t A = a.seq_lens[b];
@@ -98,88 +104,123 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
     npg = a.max_pages;
     A = npg * P;
   }
+  const int64_t last_chunk = npg > 0 ? (npg - 1) / kTierChunk : 0;
+  if (c > last_chunk) return;  // workgroup-uniform
+  if (c > 0) err = 0;          // the length is flagged once
   const int32_t* __restrict__ row = a.page_table + (int64_t)b * a.max_pages;
   int32_t* __restrict__ hl = pages + (int64_t)b * a.max_pages;
   int32_t* __restrict__ dl = pages + ((int64_t)a.batch + b) * a.max_pages;
   const int64_t host_pages_cap = a.host_k ? (a.host_rows >> a.page_shift) : 0;
   const int64_t dev_pages_cap = a.dev_k ? (a.dev_rows >> a.page_shift) : 0;
+  auto valid = [&](int32_t x) {
+    const bool host = (x & 1) != 0;
+    return x >= 0 && (int64_t)(x >> 1) < (host ? host_pages_cap : dev_pages_cap);
+  };
+
+  // valid host / HBM entries before this chunk
+  const int64_t j0 = (int64_t)c * kTierChunk;
+  int ch0 = 0, cd0 = 0;
+  constexpr int U = 8;
+  for (int64_t j = tid; j < j0; j += (int64_t)kTierThreads * U) {
+    int32_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = j + (int64_t)u * kTierThreads;
+      e[u] = idx < j0 ? row[idx] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (valid(e[u])) {
+        if (e[u] & 1) ++ch0;
+        else ++cd0;
+      }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    ch0 += __shfl_xor(ch0, o);
+    cd0 += __shfl_xor(cd0, o);
+  }
+  if (lane == 0) {
+    s_wh[wave] = ch0;
+    s_wd[wave] = cd0;
+  }
+  if (tid == 0) s_last = -1;
+  __syncthreads();
   if (tid == 0) {
-    s_base[0] = 0;
-    s_base[1] = 0;
-    s_last = -1;
+    int th = 0, td = 0;
+    for (int w = 0; w < NW; ++w) {
+      th += s_wh[w];
+      td += s_wd[w];
+    }
+    s_base[0] = th;
+    s_base[1] = td;
   }
   __syncthreads();
-  for (int64_t j0 = 0; j0 < npg; j0 += (int64_t)kTierThreads * kTierPer) {
-    const int64_t jt = j0 + (int64_t)tid * kTierPer;
-    int32_t e[kTierPer];
+
+  // this chunk: 16 consecutive entries per thread, placed by a block scan
+  const int64_t jt = j0 + (int64_t)tid * kTierPer;
+  int32_t e[kTierPer];
 #pragma unroll
-    for (int k = 0; k < kTierPer; ++k) e[k] = (jt + k < npg) ? row[jt + k] : -1;
-    uint32_t hm = 0, dm = 0;
-    int ch = 0, cd = 0;
+  for (int k = 0; k < kTierPer; ++k) e[k] = (jt + k < npg) ? row[jt + k] : -1;
+  uint32_t hm = 0, dm = 0;
+  int ch = 0, cd = 0;
 #pragma unroll
-    for (int k = 0; k < kTierPer; ++k) {
-      if (jt + k >= npg) continue;
-      const int32_t x = e[k];
-      const bool host = (x & 1) != 0;
-      const bool ok = x >= 0 && (int64_t)(x >> 1) < (host ? host_pages_cap : dev_pages_cap);
-      if (!ok) {
-        err |= kDecodeErrPage;
-        continue;
-      }
-      if (host) {
-        hm |= 1u << k;
-        ++ch;
-      } else {
-        dm |= 1u << k;
-        ++cd;
-      }
-      if (jt + k == npg - 1) s_last = host ? 1 : 0;
+  for (int k = 0; k < kTierPer; ++k) {
+    if (jt + k >= npg) continue;
+    const int32_t x = e[k];
+    if (!valid(x)) {
+      err |= kDecodeErrPage;
+      continue;
     }
-    int ih = ch, id = cd;  // inclusive scans within the wave
+    const bool host = (x & 1) != 0;
+    if (host) {
+      hm |= 1u << k;
+      ++ch;
+    } else {
+      dm |= 1u << k;
+      ++cd;
+    }
+    if (jt + k == npg - 1) s_last = host ? 1 : 0;
+  }
+  int ih = ch, id = cd;  // inclusive scans within the wave
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int th = __shfl_up(ih, o), td = __shfl_up(id, o);
-      if (lane >= o) {
-        ih += th;
-        id += td;
-      }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int th = __shfl_up(ih, o), td = __shfl_up(id, o);
+    if (lane >= o) {
+      ih += th;
+      id += td;
     }
-    if (lane == 63) {
-      s_wh[wave] = ih;
-      s_wd[wave] = id;
-    }
-    __syncthreads();
-    int ph = s_base[0], pd = s_base[1];
-    for (int w = 0; w < wave; ++w) {
-      ph += s_wh[w];
-      pd += s_wd[w];
-    }
-    ph += ih - ch;
-    pd += id - cd;
+  }
+  __syncthreads();  // s_wh / s_wd of the count phase are read
+  if (lane == 63) {
+    s_wh[wave] = ih;
+    s_wd[wave] = id;
+  }
+  __syncthreads();
+  int ph = s_base[0], pd = s_base[1];
+  for (int w = 0; w < wave; ++w) {
+    ph += s_wh[w];
+    pd += s_wd[w];
+  }
+  ph += ih - ch;
+  pd += id - cd;
 #pragma unroll
-    for (int k = 0; k < kTierPer; ++k) {
-      if (hm & (1u << k)) hl[ph++] = e[k] >> 1;
-      if (dm & (1u << k)) dl[pd++] = e[k] >> 1;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int th = 0, td = 0;
-      for (int w = 0; w < NW; ++w) {
-        th += s_wh[w];
-        td += s_wd[w];
-      }
-      s_base[0] += th;
-      s_base[1] += td;
-    }
-    __syncthreads();
+  for (int k = 0; k < kTierPer; ++k) {
+    if (hm & (1u << k)) hl[ph++] = e[k] >> 1;
+    if (dm & (1u << k)) dl[pd++] = e[k] >> 1;
   }
   if (err) atomicOr(&a.counters[decode_error_word()], err);
-  if (tid == 0) {
+  if (c == last_chunk && tid == 0) {
+    int th = s_base[0], td = s_base[1];
+    for (int w = 0; w < NW; ++w) {
+      th += s_wh[w];
+      td += s_wd[w];
+    }
     const int64_t deficit = npg > 0 ? P - (A - (npg - 1) * P) : 0;
-    const int64_t nh = (int64_t)s_base[0] * P - (s_last == 1 ? deficit : 0);
-    const int64_t nd = (int64_t)s_base[1] * P - (s_last == 0 ? deficit : 0);
-    counts[4 * b + 0] = s_base[0];
-    counts[4 * b + 1] = s_base[1];
+    const int64_t nh = (int64_t)th * P - (s_last == 1 ? deficit : 0);
+    const int64_t nd = (int64_t)td * P - (s_last == 0 ? deficit : 0);
+    counts[4 * b + 0] = th;
+    counts[4 * b + 1] = td;
     counts[4 * b + 2] = (int32_t)nh;
     counts[4 * b + 3] = (int32_t)nd;
   }
@@ -387,7 +428,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int first_stride = FUSED ? team : team * a.hkv;
   const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
   const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
-  const int64_t cap_rows = host_role ? a.host_rows : a.dev_rows;
   const int64_t stride = host_role ? a.host_stride : a.dev_stride;
   const int32_t* __restrict__ tier_list =
       PAGED ? a.tier_pages + (host_role ? 0 : (int64_t)B * a.max_pages) : nullptr;
@@ -638,24 +678,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   u32x4 kreg[NC], vreg[NC];
-  // Paged: the physical page of each chunk of a tile, from the tier list.
-  // Chunk c covers rows [c*RPC, (c+1)*RPC) of the tile; with pages of at least
-  // RPC rows all threads look up the same entries, through the scalar cache.
+  // Paged: the physical page of each of this thread's chunks of a tile, from
+  // the tier list, issued right before the tile's loads.  One form for every
+  // page size (vector loads, lanes of a page share a line): a runtime choice
+  // between scalar and vector lookups left loads of one branch pending on
+  // registers the other reuses, which made the compiler wait for the whole
+  // tile in flight before every tile's compute.
   auto lookup = [&](const DItem& it, int tile, int32_t* pte) {
-    constexpr int RPC = kThreads / S::kChunksPerRow;
     const int32_t* pl = tier_list + (int64_t)it.b * a.max_pages;
-    if ((1 << a.page_shift) >= RPC) {
-      typedef __attribute__((address_space(4))) const int32_t ConstInt;
-      const ConstInt* cl = (const ConstInt*)pl;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        pte[c] = cl[(it.k0 + min(tile * kTile + c * RPC, it.n_tok - 1)) >> a.page_shift];
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int tok = min(tile * kTile + (tid + c * kThreads) / S::kChunksPerRow, it.n_tok - 1);
-        pte[c] = pl[(it.k0 + tok) >> a.page_shift];
-      }
+    for (int c = 0; c < NC; ++c) {
+      const int tok = min(tile * kTile + (tid + c * kThreads) / S::kChunksPerRow, it.n_tok - 1);
+      pte[c] = pl[(it.k0 + tok) >> a.page_shift];
     }
   };
   auto load_tile = [&](const DItem& it, int kv, int tile, const int32_t* pte) {
@@ -664,25 +698,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int chunk = tid + c * kThreads;
       const int r = chunk / S::kChunksPerRow;
       const int col = chunk - r * S::kChunksPerRow;
-      const int tok = tile * kTile + r;
-      bool valid = tok < it.n_tok;
+      // rows past the item's end load its last token again (real data whose
+      // scores the mask removes, so p = 0 exactly): every load is issued
+      // unconditionally and none waits for another
+      const int tok = min(tile * kTile + r, it.n_tok - 1);
       int64_t row;
       if (PAGED) {
         const int64_t k = it.k0 + tok;
         row = ((int64_t)pte[c] << a.page_shift) | (k & ((1 << a.page_shift) - 1));
-        valid = valid && row < cap_rows;
       } else {
         row = (int64_t)it.b * stride + it.k0 + tok;
       }
       const int64_t off = (row * a.hkv + kv) * D + col * 8;
-      if (valid) {
-        // KV is read once per step: non-temporal loads on both tiers
-        kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
-        vreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
-      } else {
-        kreg[c] = u32x4{0u, 0u, 0u, 0u};
-        vreg[c] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // KV is read once per step: non-temporal loads on both tiers
+      kreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
+      vreg[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
     }
   };
 
@@ -968,7 +998,8 @@ int decode_static_scratch(void** ptr, size_t* bytes) {
 // ---------------------------------------------------------------------------
 int launch_decode_tiers(const DecodeArgs& a, int32_t* tier_counts, int32_t* tier_pages, void* stream) {
   if (a.batch < 1) return (int)hipSuccess;
-  hipLaunchKernelGGL(decode_tiers_kernel, dim3(a.batch), dim3(kTierThreads), 0, (hipStream_t)stream, a,
+  const int chunks = (int)std::max<int64_t>(1, ((int64_t)a.max_pages + kTierChunk - 1) / kTierChunk);
+  hipLaunchKernelGGL(decode_tiers_kernel, dim3(chunks, a.batch), dim3(kTierThreads), 0, (hipStream_t)stream, a,
                      tier_counts, tier_pages);
   return (int)hipGetLastError();
 }
