@@ -726,10 +726,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int i = jt;
   DItem it{};
   int32_t pte[NC] = {};
+  // paged: pte holds the pages of the next tile to load (looked up one tile
+  // ahead of its loads; past an item's last tile it repeats the last one)
   if (i < n_units) {
     it = unit_item(i, &kvh);
     if (PAGED) lookup(it, 0, pte);
     load_tile(it, kvh, 0, pte);
+    if (PAGED) lookup(it, min(1, (it.n_tok - 1) / kTile), pte);
   }
   bool run_open = false;  // fused: online-softmax state carries a run of sequence run_b
   int run_b = -1, run_items = 0;
@@ -796,14 +799,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       // keep one tile in flight: the next tile of this item, or the first
       // tile of the next item while this item's last tile is computed
       if (!last) {
-        if (PAGED) lookup(it, tile + 1, pte);
         load_tile(it, kvh, tile + 1, pte);
+        if (PAGED) lookup(it, min(tile + 2, ntiles - 1), pte);
       } else {
         next_i = __builtin_amdgcn_readfirstlane(s_next);
         if (next_i < n_units) {
           nit = unit_item(next_i, &nkvh);
           if (PAGED) lookup(nit, 0, pte);
           load_tile(nit, nkvh, 0, pte);
+          if (PAGED) lookup(nit, min(1, (nit.n_tok - 1) / kTile), pte);
         }
       }
 
