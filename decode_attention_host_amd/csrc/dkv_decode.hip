@@ -121,19 +121,39 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
   const int64_t j0 = (int64_t)c * kTierChunk;
   int ch0 = 0, cd0 = 0;
   constexpr int U = 8;
-  for (int64_t j = tid; j < j0; j += (int64_t)kTierThreads * U) {
-    int32_t e[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t idx = j + (int64_t)u * kTierThreads;
-      e[u] = idx < j0 ? row[idx] : -1;
+  auto count = [&](int32_t x) {
+    if (valid(x)) {
+      if (x & 1) ++ch0;
+      else ++cd0;
     }
+  };
+  if (((uintptr_t)row & 15) == 0) {
+    // 16-byte loads (j0 is a multiple of 4 entries), U per thread in flight
+    const u32x4* row4 = reinterpret_cast<const u32x4*>(row);
+    const int64_t n4 = j0 >> 2;
+    for (int64_t j = tid; j < n4; j += (int64_t)kTierThreads * U) {
+      u32x4 e[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (valid(e[u])) {
-        if (e[u] & 1) ++ch0;
-        else ++cd0;
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = j + (int64_t)u * kTierThreads;
+        e[u] = idx < n4 ? row4[idx] : u32x4{~0u, ~0u, ~0u, ~0u};
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) count((int32_t)e[u][q]);
+    }
+  } else {
+    for (int64_t j = tid; j < j0; j += (int64_t)kTierThreads * U) {
+      int32_t e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = j + (int64_t)u * kTierThreads;
+        e[u] = idx < j0 ? row[idx] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) count(e[u]);
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -157,44 +177,40 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
   }
   __syncthreads();
 
-  // this chunk: 16 consecutive entries per thread, placed by a block scan
-  const int64_t jt = j0 + (int64_t)tid * kTierPer;
+  // this chunk: wave w takes entries [w*64*16, (w+1)*64*16) of it in 16
+  // rounds of 64 consecutive entries (lane = entry: coalesced loads and, per
+  // tier, consecutive stores); per-wave counts, one scan over the waves, then
+  // each round places its entries by ballot.
+  constexpr int WPE = 64 * kTierPer;  // entries per wave
+  const int64_t jw = j0 + (int64_t)wave * WPE + lane;
   int32_t e[kTierPer];
 #pragma unroll
-  for (int k = 0; k < kTierPer; ++k) e[k] = (jt + k < npg) ? row[jt + k] : -1;
-  uint32_t hm = 0, dm = 0;
-  int ch = 0, cd = 0;
+  for (int k = 0; k < kTierPer; ++k) e[k] = (jw + 64 * k < npg) ? row[jw + 64 * k] : -1;
+  uint32_t hm = 0, dm = 0;  // per lane: rounds whose entry is a valid host / HBM page
 #pragma unroll
   for (int k = 0; k < kTierPer; ++k) {
-    if (jt + k >= npg) continue;
+    const int64_t j = jw + 64 * k;
+    if (j >= npg) continue;
     const int32_t x = e[k];
     if (!valid(x)) {
       err |= kDecodeErrPage;
       continue;
     }
     const bool host = (x & 1) != 0;
-    if (host) {
-      hm |= 1u << k;
-      ++ch;
-    } else {
-      dm |= 1u << k;
-      ++cd;
-    }
-    if (jt + k == npg - 1) s_last = host ? 1 : 0;
+    if (host) hm |= 1u << k;
+    else dm |= 1u << k;
+    if (j == npg - 1) s_last = host ? 1 : 0;
   }
-  int ih = ch, id = cd;  // inclusive scans within the wave
+  int ch = __builtin_popcount(hm), cd = __builtin_popcount(dm);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int th = __shfl_up(ih, o), td = __shfl_up(id, o);
-    if (lane >= o) {
-      ih += th;
-      id += td;
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    ch += __shfl_xor(ch, o);
+    cd += __shfl_xor(cd, o);
   }
   __syncthreads();  // s_wh / s_wd of the count phase are read
-  if (lane == 63) {
-    s_wh[wave] = ih;
-    s_wd[wave] = id;
+  if (lane == 0) {
+    s_wh[wave] = ch;
+    s_wd[wave] = cd;
   }
   __syncthreads();
   int ph = s_base[0], pd = s_base[1];
@@ -202,12 +218,14 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
     ph += s_wh[w];
     pd += s_wd[w];
   }
-  ph += ih - ch;
-  pd += id - cd;
 #pragma unroll
   for (int k = 0; k < kTierPer; ++k) {
-    if (hm & (1u << k)) hl[ph++] = e[k] >> 1;
-    if (dm & (1u << k)) dl[pd++] = e[k] >> 1;
+    const uint64_t bh = __ballot((hm >> k) & 1u), bd = __ballot((dm >> k) & 1u);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if ((hm >> k) & 1u) hl[ph + __popcll(bh & below)] = e[k] >> 1;
+    if ((dm >> k) & 1u) dl[pd + __popcll(bd & below)] = e[k] >> 1;
+    ph += __popcll(bh);
+    pd += __popcll(bd);
   }
   if (err) atomicOr(&a.counters[decode_error_word()], err);
   if (c == last_chunk && tid == 0) {
