@@ -284,6 +284,49 @@ def test_layout_violation_is_flagged_not_read(dk):
     cache.free()
 
 
+def test_paged_tier_lists_over_several_chunks(dk):
+    """A sequence of 20000 one-token pages spans two chunks of the tier-list
+    kernel (16384 page entries each): its attention must match the oracle;
+    with one page entry of the second chunk unmapped, that token is left out
+    (the oracle without it) and the page error is flagged."""
+    import torch
+    from decode_attention_host_amd.cache_build import paged_cache
+    lens, hq, hkv, d, th = [20000, 3000], 8, 2, 64, 1e4
+    ks, vs = kv_raw(87, lens, hkv, d)
+    qb = query(87, 2, hq, d)
+    pt, nh, nd = paged_table(87, lens, 1, 0.5)
+    cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, th, page=1)
+    ws = dk.decode_step_workspace(cache, 2, hq, 0.0)
+    qpos = [L - 1 for L in lens]
+    o, lse = dk.decode_step(cache, _bits(qb), _dev(qpos), _dev(lens), 0.0, 1 / math.sqrt(d), th, workspace=ws)
+    torch.cuda.synchronize()
+    assert dk.decode_errors(cache, ws) == 0
+    for b in range(2):
+        ro, rl = O.decode_sequence(qb[b], ks[b], vs[b], qpos[b], th, 1 / math.sqrt(d))
+        _check(o[b].cpu().numpy().astype(np.float64), lse[b].cpu().numpy().astype(np.float64), ro, rl,
+               f"paged 1-token pages, seq {b}")
+    # unmap token 17000 of sequence 0 (second chunk of its row)
+    drop = 17000
+    pt_bad = pt.copy()
+    pt_bad[0, drop] = -1
+    cache.update_page_table(pt_bad)
+    o, lse = dk.decode_step(cache, _bits(qb), _dev(qpos), _dev(lens), 0.0, 1 / math.sqrt(d), th, workspace=ws)
+    torch.cuda.synchronize()
+    assert dk.decode_errors(cache, ws) & 2
+    keep = np.ones(lens[0], dtype=bool)
+    keep[drop] = False
+    kst = O.bf16_to_f64(O.bf16_rne_bits(O.rope_neox(O.bf16_to_f64(ks[0]), np.arange(lens[0])[:, None], th)))
+    vst = O.bf16_to_f64(vs[0])
+    g = hq // hkv
+    q_rot = O.rope_neox(O.bf16_to_f64(qb[0]), np.full(hq, qpos[0]), th)
+    for kvh in range(hkv):
+        heads = list(range(kvh * g, (kvh + 1) * g))
+        ro, rl = O.attention(q_rot[heads], kst[keep][:, kvh:kvh + 1], vst[keep][:, kvh:kvh + 1], 1 / math.sqrt(d))
+        _check(o[0, heads].cpu().numpy().astype(np.float64), lse[0, heads].cpu().numpy().astype(np.float64), ro, rl,
+               f"token {drop} unmapped, kv head {kvh}")
+    cache.free()
+
+
 # ----------------------------------------------------------------- growing decode loop
 
 CHECK_STEPS = (1, 50, 100)
