@@ -113,3 +113,47 @@ def test_kernel_timing_fits_inside_the_call(dk):
     finally:
         dk.kernel_timing(False)
         cache.free()
+
+
+@pytest.mark.parametrize("form", ["split", "fused"])
+def test_workgroup_trace_accounts_for_every_unit(dk, form):
+    """dkv_attn_trace: every workgroup of a decode launch records its role,
+    a start no later than its end, and its units; the units of each role add up
+    to the work the host enumeration of the same call lists (items x KV heads)."""
+    hq, hkv, d, lens, ratio, theta = 32, 8, 128, [9000, 3000], 0.4, 5e5
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    ks = [normal_bf16(4, 1 + b, (L, hkv, d)) for b, L in enumerate(lens)]
+    vs = [normal_bf16(4, 5 + b, (L, hkv, d)) for b, L in enumerate(lens)]
+    q = torch.from_numpy(normal_bf16(4, 0, (2, hq, d)).view(np.int16)).cuda()
+    cache = contiguous_cache(hkv, d, lens, ratio, ks, vs, theta)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    items, _, _, info = dk.plan_inspect(cache.desc(), 2, hq, lens, ratio, cus)
+    n_host = int((items[:, 0] == 1).sum())
+    n_dev = int((items[:, 0] == 0).sum())
+    grid = 4096
+    buf = torch.zeros((grid, 4), dtype=torch.int64, device="cuda")
+    try:
+        qpos = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+        dk.attn_trace(buf)
+        if form == "split":
+            dk.decode(cache, q, qpos, lens, ratio, 1 / math.sqrt(d), theta)
+        else:
+            ws = dk.decode_step_workspace(cache, 2, hq, ratio)
+            dk.decode_step(cache, q, qpos, torch.tensor(lens, dtype=torch.int32, device="cuda"), ratio,
+                           1 / math.sqrt(d), theta, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        dk.attn_trace(None)
+        cache.free()
+    t = buf.cpu().numpy()
+    used = t[t[:, 0] != 0]
+    print(f"{form}: {len(used)} workgroups traced, host items {n_host}, HBM items {n_dev}", flush=True)
+    assert len(used) == info["host_wgs"] + info["dev_wgs"]
+    assert np.all(used[:, 1] >= used[:, 0])
+    host = used[used[:, 2] == 1]
+    dev = used[used[:, 2] == 0]
+    assert len(host) == info["host_wgs"] and len(dev) == info["dev_wgs"]
+    # every (item, KV head) is processed once: the items the host enumeration
+    # lists per KV head, times the KV heads
+    assert int(host[:, 3].sum()) == n_host * hkv
+    assert int(dev[:, 3].sum()) == n_dev * hkv
