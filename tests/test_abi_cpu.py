@@ -360,3 +360,31 @@ def test_decode_batch_bound(L):
         assert L.dkv_decode_step_plan(C.byref(x), 513, 8, 0.5, 0, C.byref(info)) == dkv_lib.DKV_ERR_UNSUPPORTED
     finally:
         reset_tuning()
+
+
+def test_staged_plan_layout_and_validation(L):
+    """dkv_decode_staged_plan (host only): chunks of the host tier, bytes
+    staged into HBM, a workspace that holds the two-slot ring; paged layouts,
+    chunk sizes off the 64-token grid and rows beyond the layout are refused."""
+    from decode_attention_host_amd.api import set_tuning, reset_tuning
+    hkv, d, hq = 8, 128, 32
+    row = hkv * d * 2
+    try:
+        set_tuning(num_cus=256)
+        x = desc(hkv=hkv, d=d, host_rows=1 << 16, dev_rows=1 << 16, hs=1 << 16, ds=1 << 16)
+        info = dkv_lib.PlanInfo()
+        for L_, r, chunk in [(5000, 0.6, 1024), (3000, 1.0, 64), (777, 0.0, 256), (40000, 0.25, 4096)]:
+            assert L.dkv_decode_staged_plan(C.byref(x), hq, L_, r, chunk, C.byref(info)) == dkv_lib.DKV_OK
+            nh = O.contig_split_point(r, L_)
+            assert info.host_items == -(-nh // chunk)
+            assert info.staged_bytes == nh * row * 2
+            assert info.host_bytes == nh * row * 2 and info.dev_bytes == (L_ - nh) * row * 2
+            assert info.workspace_bytes >= 4 * chunk * row  # two ring slots of K and of V
+        assert L.dkv_decode_staged_plan(C.byref(x), hq, 5000, 0.5, 100, C.byref(info)) == dkv_lib.DKV_ERR_INVALID
+        assert L.dkv_decode_staged_plan(C.byref(x), hq, 0, 0.5, 1024, C.byref(info)) == dkv_lib.DKV_ERR_INVALID
+        assert L.dkv_decode_staged_plan(C.byref(x), hq, 1 << 20, 0.5, 1024, C.byref(info)) == dkv_lib.DKV_ERR_INVALID
+        pt = np.zeros((1, 4), dtype=np.int32)
+        xp = desc(hkv=hkv, d=d, page=16, max_pages=4, host_rows=64, dev_rows=64, pt=pt)
+        assert L.dkv_decode_staged_plan(C.byref(xp), hq, 64, 0.5, 64, C.byref(info)) == dkv_lib.DKV_ERR_UNSUPPORTED
+    finally:
+        reset_tuning()
