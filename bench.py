@@ -325,8 +325,13 @@ def ratio_sweep(dk, cfg, seed, flags, ratios, iters, bw_h, bw_d, raw=None):
                "roofline_ms_measured": round(t_star, 5), "roofline_ms_nominal": round(t_nom, 5),
                "plan": {k: info[k] for k in ("host_wgs", "dev_wgs", "host_chunk", "dev_chunk",
                                              "host_items", "dev_items")}}
+        # cold (cache flushed before each step): 50 steps where a step is
+        # short, `iters` otherwise; warm: the same count back to back
+        n_it = max(iters, 50) if r < 0.5 else iters
         for form in ("fused", "split"):
-            f = flushed_steps(dk, getattr(st, form), iters, flush)
+            f = flushed_steps(dk, getattr(st, form), n_it, flush)
+            f["steps"] = n_it
+            f["warm_ms"] = round(timed_loop(getattr(st, form), n_it, 3)[0], 5)
             f["eff_gbs"] = round((hb + db) / (f["ms_median"] * 1e6), 2)
             f["frac_measured"] = round(t_star / f["ms_median"], 3)
             f["frac_nominal"] = round(t_nom / f["ms_median"], 3)
