@@ -448,15 +448,16 @@ void fill_linear_info(const dkv::LinearShape& z, dkv_plan_info* info) {
 //
 // A decode call has no host plan: the launch shape (workgroups per tier and KV
 // head, item-length rules) follows from its arguments, and the kernel derives
-// the items from the lengths in device memory.  The workspace holds the item
+// the items from the lengths in device memory.  The workspace holds the unit
 // queues and counters (zero between calls: every call leaves them zeroed),
-// the paged layout's tier lists, and the fused form's run partials.
+// the paged layout's tier lists, and the fused form's partials (one slot per
+// item and one per appended token of each sequence) with their merge counts.
 struct DecodeShape {
   dkv::DecodeTemplate t{};
   int32_t g = 0;
-  int32_t max_slots = 0;
-  int64_t max_splits = 0;
-  size_t counters_off = 0, group_off = 0, tiers_off = 0, lists_off = 0, run_o_off = 0, run_lse_off = 0,
+  int32_t max_slots = 0;   // fused: partial slots in the workspace
+  int64_t max_splits = 0;  // split bound over any lengths that fit the pools
+  size_t counters_off = 0, group_off = 0, tiers_off = 0, lists_off = 0, part_o_off = 0, part_lse_off = 0,
          proj_off = 0, total = 0;
 };
 
@@ -475,7 +476,7 @@ dkv::PlanInput decode_input(const dkv_kv_desc* kv, int32_t batch, int32_t hq, do
 }
 
 dkv_status decode_shape(const dkv_kv_desc* kv, int32_t batch, int32_t hq, double ratio, bool fused, int32_t hidden,
-                        int32_t num_cus, DecodeShape* out) {
+                        int32_t num_cus, DecodeShape* out, bool static_layout = false) {
   if (batch < 1 || batch > dkv::kDecodeMaxBatch)
     return set_err(DKV_ERR_UNSUPPORTED, "batch %d outside 1..%d", batch, dkv::kDecodeMaxBatch);
   if (hq < 1 || hq % kv->num_kv_heads)
@@ -499,17 +500,29 @@ dkv_status decode_shape(const dkv_kv_desc* kv, int32_t batch, int32_t hq, double
   DecodeShape d;
   d.t = dkv::decode_template(decode_input(kv, batch, hq, ratio, cus, tu), host_tier, dev_tier, frac);
   d.g = g;
-  d.max_slots = d.t.team_h + 2 * d.t.team_d + 1;
   d.max_splits = dkv::decode_max_splits(d.t, batch, kv->host_rows, kv->dev_rows);
+  const int64_t slots = d.max_splits + batch;
+  // the kernel addresses the fused partials with 31-bit byte offsets
+  if (fused && slots * hq * (int64_t)kv->head_dim * 4 > INT32_MAX)
+    return set_err(DKV_ERR_UNSUPPORTED, "fused step: %lld partial slots x %d heads x %d dims exceed 2 GiB",
+                   (long long)slots, hq, kv->head_dim);
+  d.max_slots = fused ? (int32_t)slots : 0;
   auto up = [](size_t a) { return (a + 255) / 256 * 256; };
   const size_t hkv = (size_t)kv->num_kv_heads, D = (size_t)kv->head_dim, B = (size_t)batch;
+  const size_t S = (size_t)d.max_slots;
   d.counters_off = 0;
-  d.group_off = up((size_t)dkv::decode_counter_words((int)hkv) * 4);
-  d.tiers_off = up(d.group_off + (fused ? B * hkv * 2 * 4 : 0));
+  d.group_off = up((size_t)dkv::decode_counter_words() * 4);
+  d.tiers_off = up(d.group_off + (fused ? (S + B) * hkv * 4 : 0));
+  if (static_layout) {  // counters in the static scratch's fixed counter area
+    if (d.tiers_off > dkv::kDecodeStaticCounterBytes)
+      return set_err(DKV_ERR_UNSUPPORTED, "this shape needs %zu bytes of counters, beyond the static %zu bytes",
+                     d.tiers_off, dkv::kDecodeStaticCounterBytes);
+    d.tiers_off = dkv::kDecodeStaticCounterBytes;
+  }
   d.lists_off = up(d.tiers_off + (paged ? B * 4 * 4 : 0));
-  d.run_o_off = up(d.lists_off + (paged ? 2 * B * (size_t)kv->max_pages * 4 : 0));
-  d.run_lse_off = up(d.run_o_off + (fused ? B * hkv * d.max_slots * g * D * 4 : 0));
-  d.proj_off = up(d.run_lse_off + (fused ? B * hkv * d.max_slots * g * 4 : 0));
+  d.part_o_off = up(d.lists_off + (paged ? 2 * B * (size_t)kv->max_pages * 4 : 0));
+  d.part_lse_off = up(d.part_o_off + (fused ? S * (size_t)hq * D * 4 : 0));
+  d.proj_off = up(d.part_lse_off + (fused ? S * (size_t)hq * 4 : 0));
   d.total = d.proj_off +
             (fused && hidden > 0 ? dkv_append_workspace_bytes(batch, hidden, kv->num_kv_heads * kv->head_dim) : 0);
   *out = d;
@@ -546,8 +559,8 @@ dkv::DecodeArgs decode_args(const dkv_kv_desc* kv, const DecodeShape& d, int32_t
   a.group_cnt = reinterpret_cast<int32_t*>(ws + d.group_off);
   a.tier_counts = reinterpret_cast<const int32_t*>(ws + d.tiers_off);
   a.tier_pages = reinterpret_cast<const int32_t*>(ws + d.lists_off);
-  a.run_o = reinterpret_cast<float*>(ws + d.run_o_off);
-  a.run_lse = reinterpret_cast<float*>(ws + d.run_lse_off);
+  a.part_o = reinterpret_cast<float*>(ws + d.part_o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + d.part_lse_off);
   a.max_slots = d.max_slots;
   a.freq = rope_freq(rope_theta, kv->head_dim);
   std::lock_guard<std::mutex> lk(g_trace_mu);
@@ -901,6 +914,7 @@ dkv_status dkv_decode_attn_split(const dkv_kv_desc* kv, int32_t batch, int32_t n
   a.part_o = part_o;
   a.part_lse = part_lse;
   a.split_offsets = split_offsets;
+  a.max_slots = num_splits_cap;
   hipError_t he;
   if (kv->page_size > 0) {
     TimedLaunch t_tiers(DKV_KERNEL_TIERS, s);
@@ -958,7 +972,7 @@ static dkv_status decode_step_impl(const dkv_kv_desc* kv, int32_t batch, int32_t
     return set_err(DKV_ERR_INVALID, "appending needs both k_new and v_new (or x with wk and wv)");
   }
   DecodeShape d;
-  st = decode_shape(kv, batch, num_q_heads, offload_ratio, true, proj ? hidden : 0, 0, &d);
+  st = decode_shape(kv, batch, num_q_heads, offload_ratio, true, proj ? hidden : 0, 0, &d, static_scratch);
   if (st != DKV_OK) return st;
   if (workspace_bytes < d.total) {
     if (static_scratch)

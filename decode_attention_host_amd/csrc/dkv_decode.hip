@@ -7,10 +7,10 @@
 //                        tokens per tier, for the sequence lengths of this call
 //   decode_kernel        rotate the query heads (Neox RoPE, fp64 angle), stream
 //                        K/V tiles of one tier into LDS, Q.K on MFMA, online
-//                        softmax, P.V on the vector ALUs; either one normalised
-//                        partial per work item (split form) or, fused, one
-//                        partial per workgroup run merged by log-sum-exp in the
-//                        same launch, after appending each sequence's new token
+//                        softmax, P.V on the vector ALUs, one normalised
+//                        partial per (work item, KV head); fused, the
+//                        partials are merged by log-sum-exp in the same
+//                        launch, after each sequence's new token is appended
 //
 // Method sources (page, section): DirectKV README, introduction (one kernel
 // projects the new token's K/V, rotates keys with Neox RoPE and attends over
@@ -25,19 +25,21 @@
 //     counts) from device memory and derives the same items (dkv_decomp.h), so
 //     a call captured in a graph stays valid while the cache grows, and a step
 //     needs no host work beyond argument checks.
-//   * Queues.  Each tier has its own queue of units, taken in order (first by
-//     index, then by an atomic counter), so a workgroup sees its sequences in
-//     increasing order.  Split form: a unit is (item, KV head) with the KV
-//     head fastest, so the workgroups of a tier stream neighbouring rows of
-//     the same token range at once (DRAM page locality).  Fused form: a team of
-//     workgroups serves one KV head in one tier and takes that head's items,
-//     so a workgroup can carry its softmax state from one item to the next.
-//   * Fused form.  A workgroup keeps its online-softmax state across
-//     consecutive items of one sequence and writes one partial per run; the
-//     last run of a (sequence, KV head) to finish merges them.  Partials are
-//     written and read with agent-coherent (sc1) buffer accesses and the
-//     completion counter is bumped after the stores are acknowledged, which
-//     orders them across XCDs without an L2 write-back.
+//   * Queues.  Each tier has one queue of (item, KV head) units with the KV
+//     head fastest, taken in order (first by index, then by an atomic
+//     counter), so the workgroups of a tier stream neighbouring rows of the
+//     same token range at once (DRAM page locality).  Fused form: the
+//     appended tokens, one unit per (sequence, KV head), follow the HBM
+//     tier's attention units in its queue, so the first workgroups to run out
+//     of attention take them.
+//   * Fused form.  Each unit's partial goes to its slot in the workspace; a
+//     sequence's slots (its appended token, then its items) form groups of
+//     kMergeGroup.  The last unit of a group to finish merges the group into
+//     its first slot, and the last group of a (sequence, KV head) merges the
+//     group results into the output, so no workgroup folds more than a few
+//     dozen partials.  Partials are written and read with agent-coherent
+//     (sc1) buffer accesses and each count is bumped after the stores are
+//     acknowledged, which orders them across XCDs without an L2 write-back.
 //   * Tiles: 64 tokens of one KV head, D/32 coalesced 16-byte loads of K and
 //     of V per thread (non-temporal: the KV is read once), staged in LDS with a
 //     16-byte row pad; the next tile is in flight while one is computed.
@@ -248,6 +250,10 @@ __global__ __launch_bounds__(kTierThreads) void decode_tiers_kernel(DecodeArgs a
 // Decode kernel.
 // ---------------------------------------------------------------------------
 
+// Fused form: partial slots per merge group (a group's last unit to finish
+// folds them; the last group of a (sequence, KV head) folds the groups).
+constexpr int kMergeGroup = 16;
+
 // One work item as the kernel sees it.
 struct DItem {
   int32_t b;      // sequence
@@ -403,18 +409,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int DPL = S::kDimsPerLane;
   static_assert(G >= 1 && G <= 8, "group size");
   static_assert(4 * G * (D + 2) * 4 <= kTile * S::kPitch, "epilogue scratch");
-  static_assert(G * D * 4 <= kTile * S::kPitch, "run partial scratch");
+  static_assert(2 * D * 4 <= kTile * S::kPitch, "appended token scratch");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kTile * S::kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kTile * S::kPitch];
   __shared__ __attribute__((aligned(16))) float p_lds[4][16][8];
   __shared__ float a_lds[4][8];
   __shared__ __attribute__((aligned(16))) float q_lds[G][D];  // rotated query heads of q_b
-  __shared__ __attribute__((aligned(16))) float o_lds[G][D];  // a partial being written
-  __shared__ float l_lds[G];
   __shared__ DecodeLds L;
   __shared__ int s_next;
-  __shared__ int s_slot;
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
@@ -430,27 +433,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   if (wave == 0) build_prefix<PAGED>(a, L);
   __syncthreads();
 
-  // Role and team: host-tier workgroups first, each team one KV head.
+  // Role: host-tier workgroups first.  One queue per tier whose units are
+  // (item, KV head) with the KV head fastest, so the heads of a token range
+  // are read together.
   const DecodeTemplate& T = a.tmpl;
   const bool host_role = (int)blockIdx.x < a.hkv * T.team_h;
   const int r_idx = host_role ? (int)blockIdx.x : (int)blockIdx.x - a.hkv * T.team_h;
-  const int team = host_role ? T.team_h : T.team_d;
-  // Fused form: workgroups are bound to one KV head ("team") and take the
-  // items of their tier in order, so they can carry a run across items.
-  // Split form: one queue per tier whose units are (item, KV head) with the
-  // KV head fastest, so the heads of a token range are read together.
-  int kvh = FUSED ? r_idx / team : 0;
-  const int jt = FUSED ? r_idx - kvh * team : r_idx;
+  const int role_wgs = a.hkv * (host_role ? T.team_h : T.team_d);
   const int n_items = host_role ? L.ph[B] : L.pm[B] + L.pt[B];
-  const int n_units = FUSED ? n_items : n_items * a.hkv;
-  const int first_stride = FUSED ? team : team * a.hkv;
+  // the call's partial slots must fit the arrays it was given; otherwise
+  // nothing is computed and the call is flagged (the host's bound on the slot
+  // count makes this unreachable for lengths that fit the pools)
+  const bool fits = L.off[B] + (FUSED ? B * a.new_tokens : 0) <= a.max_slots;
+  const int n_units = fits ? n_items * a.hkv : 0;
   const uint16_t* __restrict__ kpool = host_role ? a.host_k : a.dev_k;
   const uint16_t* __restrict__ vpool = host_role ? a.host_v : a.dev_v;
   const int64_t stride = host_role ? a.host_stride : a.dev_stride;
   const int32_t* __restrict__ tier_list =
       PAGED ? a.tier_pages + (host_role ? 0 : (int64_t)B * a.max_pages) : nullptr;
-  int* qctr = a.counters + decode_queue(a.hkv, host_role, kvh);  // split form: kvh = 0
+  int* qctr = a.counters + decode_queue(host_role);
+  int kvh = 0;
 
+  if (!fits && blockIdx.x == 0 && tid == 0) atomicOr(&a.counters[decode_error_word()], kDecodeErrCapacity);
   if (!FUSED && blockIdx.x == 0 && a.split_offsets)
     for (int i = tid; i <= B; i += kThreads) a.split_offsets[i] = L.off[i];
 
@@ -476,127 +480,163 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     q_kvh = kvh;
   };
 
-  // Runs of partials (fused form): completion bookkeeping per (sequence, KV head).
-  auto group_total = [&](int b) -> int {
-    return (L.ph[b + 1] - L.ph[b]) + (L.pm[b + 1] - L.pm[b]) + (L.pt[b + 1] - L.pt[b]) + a.new_tokens;
+  // Fused form.  Sequence b owns slots [seq_first(b), seq_first(b) +
+  // seq_slots(b)): first its appended token's, then one per item.  Partials
+  // are [slot][Hq][D] (lse [slot][Hq]); offsets fit 31 bits (checked on the
+  // host).
+  auto seq_slots = [&](int b) -> int {
+    return (L.off[b + 1] - L.off[b]) + a.new_tokens;
   };
+  auto seq_first = [&](int b) -> int { return L.off[b] + b * a.new_tokens; };
 
-  // Fused form: merge every run partial of (b, kvh); this workgroup finished
-  // it last.  Per head, the maximum and the sum of exp(lse - max) come from a
-  // pass over the lse values; the outputs then fold the runs in chunks whose
-  // weights are staged in LDS (the K tile buffer), with the threads of each
-  // float4 of the output splitting the runs of a chunk between them.
-  auto merge_group = [&](int b) {
-    const int g = b * a.hkv + kvh;
-    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.run_o + (size_t)g * a.max_slots * G * D);
-    const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.run_lse + (size_t)g * a.max_slots * G);
-    if (tid == 0)
-      s_slot = __hip_atomic_load(&a.group_cnt[2 * g + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int ns = min(s_slot, a.max_slots);
-    for (int h = wave; h < G; h += 4) {
-      float m = -INFINITY;
-      for (int s = lane; s < ns; s += 64) m = fmaxf(m, coherent_load1(rl, (s * G + h) * 4));
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      float w = 0.f;
-      for (int s = lane; s < ns; s += 64) {
-        const float x = coherent_load1(rl, (s * G + h) * 4);
-        w += (x == -INFINITY) ? 0.f : expf(x - m);
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) w += __shfl_xor(w, o);
-      if (lane == 0) {
-        l_lds[h] = (m == -INFINITY) ? -INFINITY : m + logf(w);
-        a_lds[0][h] = m;
-        a_lds[1][h] = w;
-      }
-    }
-    __syncthreads();
-    constexpr int NCH = G * D / 4;                        // float4 chunks of the outputs (<= 256)
-    constexpr int NSG = kThreads / NCH;                   // threads per chunk
-    constexpr int CAP = (kTile * S::kPitch) / (G * 4);    // runs whose weights fit the K buffer
-    static_assert(NCH <= kThreads && NSG >= 1, "merge layout");
-    float* wl = reinterpret_cast<float*>(k_lds);          // [CAP][G] weights of a chunk of runs
-    float* red = reinterpret_cast<float*>(v_lds);         // [NSG][G*D]
+  // Fold n partials of (b, kvh), at slots s0, s0 + step, ..., by log-sum-exp
+  // into slot dst or, with dst < 0, into the output.  The lse values of up to
+  // CAPN partials at a time are staged in LDS (the K tile buffer); pass 1
+  // gives each head's maximum and sum of exp(lse - max), pass 2 turns the
+  // staged values into weights and folds the outputs, the threads of each
+  // float4 of the output splitting the partials between them.
+  auto merge = [&](int b, int s0, int step, int n, int dst) {
+    const __amdgpu_buffer_rsrc_t pr_o = coherent_rsrc(a.part_o);
+    const __amdgpu_buffer_rsrc_t pr_l = coherent_rsrc(a.part_lse);
+    constexpr int CAPN = (kTile * S::kPitch) / (G * 4);
+    constexpr int NCH = G * D / 4;           // float4 chunks of a partial (<= 256)
+    constexpr int NSG = kThreads / NCH;      // threads per chunk
+    static_assert(NCH <= kThreads && NSG * NCH == kThreads, "merge layout");
+    static_assert(NSG * G * D * 4 <= kTile * S::kPitch, "merge reduction scratch");
+    constexpr int U = 8;                     // loads in flight per thread
+    float* wl = reinterpret_cast<float*>(k_lds);   // [CAPN][G]
+    float* red = reinterpret_cast<float*>(v_lds);  // [NSG][G * D]
+    const int hq0 = kvh * G;
     const int c = tid % NCH, sg = tid / NCH;
     const int hc = (c * 4) / D;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ns; s0 += CAP) {
-      const int s1 = min(ns, s0 + CAP);
-      for (int idx = tid; idx < (s1 - s0) * G; idx += kThreads) {
-        const int h = idx % G;
-        const float x = coherent_load1(rl, ((s0 * G) + idx) * 4), m = a_lds[0][h];
-        wl[idx] = (m == -INFINITY || x == -INFINITY) ? 0.f : expf(x - m) / a_lds[1][h];
+    auto o_off = [&](int k) { return (((s0 + k * step) * a.hq + hq0) * D + c * 4) * 4; };
+    auto stage = [&](int c0, int cn) {
+      for (int idx = tid; idx < cn * G; idx += kThreads) {
+        const int k = idx / G, h = idx - k * G;
+        wl[idx] = coherent_load1(pr_l, ((s0 + (c0 + k) * step) * a.hq + hq0 + h) * 4);
       }
+    };
+    __syncthreads();  // earlier users of the tile buffers and a_lds are done
+    for (int c0 = 0; c0 < n; c0 += CAPN) {
+      const int cn = min(CAPN, n - c0);
+      if (c0 > 0) __syncthreads();
+      stage(c0, cn);
       __syncthreads();
-      if (sg < NSG) {
-        int s = s0 + sg;
-        constexpr int U = 8;
-        for (; s + (U - 1) * NSG < s1; s += U * NSG) {
-          floatx4 o[U];
+      for (int h = wave; h < G; h += 4) {
+        float m = -INFINITY;
+        for (int k = lane; k < cn; k += 64) m = fmaxf(m, wl[k * G + h]);
 #pragma unroll
-          for (int k = 0; k < U; ++k) o[k] = coherent_load4(ro, ((s + k * NSG) * G * D + c * 4) * 4);
-#pragma unroll
-          for (int k = 0; k < U; ++k) {
-            const float w = wl[(s + k * NSG - s0) * G + hc];
-            if (w != 0.f) acc += w * o[k];
-          }
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float w = 0.f;
+        for (int k = lane; k < cn; k += 64) {
+          const float x = wl[k * G + h];
+          w += (x == -INFINITY) ? 0.f : expf(x - m);
         }
-        for (; s < s1; s += NSG) {
-          const floatx4 o = coherent_load4(ro, (s * G * D + c * 4) * 4);
-          const float w = wl[(s - s0) * G + hc];
-          if (w != 0.f) acc += w * o;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) w += __shfl_xor(w, o);
+        if (lane == 0) {
+          const float mp = c0 > 0 ? a_lds[0][h] : -INFINITY;
+          const float wp = c0 > 0 ? a_lds[1][h] : 0.f;
+          const float M = fmaxf(mp, m);
+          a_lds[0][h] = M;
+          a_lds[1][h] = (M == -INFINITY) ? 0.f
+                                          : (mp == -INFINITY ? 0.f : wp * expf(mp - M)) +
+                                                (m == -INFINITY ? 0.f : w * expf(m - M));
         }
       }
       __syncthreads();
     }
-    if (sg < NSG) *reinterpret_cast<floatx4*>(red + sg * G * D + c * 4) = acc;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < n; c0 += CAPN) {
+      const int cn = min(CAPN, n - c0);
+      if (n > CAPN) {  // restage this chunk (pass 1 left the last one)
+        __syncthreads();
+        stage(c0, cn);
+        __syncthreads();
+      }
+      for (int idx = tid; idx < cn * G; idx += kThreads) {
+        const int h = idx % G;
+        const float x = wl[idx], M = a_lds[0][h];
+        wl[idx] = (M == -INFINITY || x == -INFINITY) ? 0.f : expf(x - M) / a_lds[1][h];
+      }
+      __syncthreads();
+      int k = sg;
+      for (; k + (U - 1) * NSG < cn; k += U * NSG) {
+        floatx4 o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) o[u] = coherent_load4(pr_o, o_off(c0 + k + u * NSG));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = wl[(k + u * NSG) * G + hc];
+          if (w != 0.f) acc += w * o[u];
+        }
+      }
+      for (; k < cn; k += NSG) {
+        const floatx4 o = coherent_load4(pr_o, o_off(c0 + k));
+        const float w = wl[k * G + hc];
+        if (w != 0.f) acc += w * o;
+      }
+    }
+    *reinterpret_cast<floatx4*>(red + sg * G * D + c * 4) = acc;
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += kThreads) {
       float o = 0.f;
 #pragma unroll
       for (int k = 0; k < NSG; ++k) o += red[k * G * D + idx];
-      const int h = idx / D, d = idx - h * D;
-      a.out_o[((size_t)b * a.hq + kvh * G + h) * D + d] = (l_lds[h] == -INFINITY) ? 0.f : o;
+      const int h = idx / D;
+      if (a_lds[0][h] == -INFINITY) o = 0.f;
+      if (dst < 0) a.out_o[((size_t)b * a.hq + hq0) * D + idx] = o;
+      else coherent_store1(pr_o, ((dst * a.hq + hq0) * D + idx) * 4, o);
     }
-    if (tid < G && a.out_lse) a.out_lse[(size_t)b * a.hq + kvh * G + tid] = l_lds[tid];
-    if (tid == 0) {
-      __hip_atomic_store(&a.group_cnt[2 * g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.group_cnt[2 * g + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < G) {
+      const float M = a_lds[0][tid];
+      const float lse = (M == -INFINITY) ? -INFINITY : M + logf(a_lds[1][tid]);
+      if (dst < 0) {
+        if (a.out_lse) a.out_lse[(size_t)b * a.hq + hq0 + tid] = lse;
+      } else {
+        coherent_store1(pr_l, (dst * a.hq + hq0 + tid) * 4, lse);
+      }
     }
-    __syncthreads();
   };
 
-  // Fused form: write the run partial held in o_lds / l_lds for sequence b,
-  // count its items and merge if it completes the group.
-  auto flush_run = [&](int b, int items) {
-    const int g = b * a.hkv + kvh;
-    if (tid == 0) s_slot = atomicAdd(&a.group_cnt[2 * g + 1], 1);
-    __syncthreads();
-    const int slot = s_slot;
-    if (slot < a.max_slots) {
-      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.run_o + ((size_t)g * a.max_slots + slot) * G * D);
-      const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.run_lse + ((size_t)g * a.max_slots + slot) * G);
-      for (int c = tid; c < G * D / 4; c += kThreads)
-        coherent_store4(ro, c * 16, *reinterpret_cast<const floatx4*>(&o_lds[0][0] + c * 4));
-      if (tid < G) coherent_store1(rl, tid * 4, l_lds[tid]);
-    } else if (tid == 0) {
-      atomicOr(&a.counters[decode_error_word()], kDecodeErrCapacity);
+  // Fused form: the partial at relative slot rel of (b, kvh) is written and
+  // acknowledged.  Count it in its group; the group's last arrival merges the
+  // group into the group's first slot (or, for a single group, into the
+  // output) and counts the group; the last group merges the group results.
+  auto arrive = [&](int b, int rel) {
+    const int S_b = seq_slots(b), first = seq_first(b);
+    const int gk = rel / kMergeGroup;
+    const int gs = first + gk * kMergeGroup;
+    const int gn = min(kMergeGroup, S_b - gk * kMergeGroup);
+    const int ng = (S_b + kMergeGroup - 1) / kMergeGroup;
+    int* c1 = a.group_cnt + (size_t)gs * a.hkv + kvh;
+    int* c2 = a.group_cnt + (size_t)a.max_slots * a.hkv + (size_t)b * a.hkv + kvh;
+    if (gn > 1) {  // a group of one slot is its own result
+      if (tid == 0) s_flag = atomicAdd(c1, 1) + 1 == gn;
+      __syncthreads();
+      if (!s_flag) return;
+      if (tid == 0) __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-      const int done = atomicAdd(&a.group_cnt[2 * g], items) + items;
-      s_flag = done == group_total(b);
+    if (ng == 1) {
+      merge(b, gs, 1, gn, -1);
+      return;
+    }
+    if (gn > 1) {
+      merge(b, gs, 1, gn, gs);
+      wait_stores();
     }
     __syncthreads();
-    if (s_flag) merge_group(b);
+    if (tid == 0) s_flag = atomicAdd(c2, 1) + 1 == ng;
+    __syncthreads();
+    if (!s_flag) return;
+    if (tid == 0) __hip_atomic_store(c2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge(b, first, kMergeGroup, ng, -1);
   };
 
-  // Fused form, appended token: rotate its key at pos_new[b] (fp64, one bf16
-  // rounding), store K and V in the token's cache slot, and write the
-  // one-token partial of (b, kvh): o = v, lse = its scaled score.
+  // Fused form, appended token of (b, kvh): rotate its key at pos_new[b]
+  // (fp64, one bf16 rounding), store K and V in the token's cache slot, and
+  // write its one-token partial (o = v, lse = its scaled score) into the
+  // sequence's first slot.
   auto new_token = [&](int b) {
     if (q_b != b || q_kvh != kvh) rotate_q(b);
     const int p = a.pos_new ? a.pos_new[b] : a.seq_lens[b];
@@ -626,9 +666,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const bool host = p < ph;
         if (p <= Lb) {
           const int64_t row = host ? (int64_t)b * a.host_stride + p : (int64_t)b * a.dev_stride + (p - ph);
-          const bool fits = host ? (ph <= a.host_stride && row < a.host_rows && a.host_k)
-                                 : (Lb + 1 - ph <= a.dev_stride && row < a.dev_rows && a.dev_k);
-          if (fits) {
+          const bool fits_row = host ? (ph <= a.host_stride && row < a.host_rows && a.host_k)
+                                     : (Lb + 1 - ph <= a.dev_stride && row < a.dev_rows && a.dev_k);
+          if (fits_row) {
             sk = (host ? a.host_k : a.dev_k) + row * kvd + kvh * D;
             sv = (host ? a.host_v : a.dev_v) + row * kvd + kvh * D;
           }
@@ -669,6 +709,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
+    const int slot = seq_first(b);
+    const __amdgpu_buffer_rsrc_t pr_o = coherent_rsrc(a.part_o);
+    const __amdgpu_buffer_rsrc_t pr_l = coherent_rsrc(a.part_lse);
     // scores: 32 lanes per head
     {
       const int h = tid >> 5, l32 = tid & 31;
@@ -677,23 +720,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int d = l32; d < D; d += 32) s = fmaf(q_lds[h][d], kr[d], s);
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      if (h < G && l32 == 0) l_lds[h] = s * 0.69314718055994530942f;  // log2 units -> natural log
+      if (h < G && l32 == 0)  // log2 units -> natural log
+        coherent_store1(pr_l, (slot * a.hq + kvh * G + h) * 4, s * 0.69314718055994530942f);
     }
-    for (int idx = tid; idx < G * D; idx += kThreads) o_lds[idx / D][idx % D] = vr[idx % D];
+    for (int idx = tid; idx < G * D; idx += kThreads)
+      coherent_store1(pr_o, ((slot * a.hq + kvh * G) * D + idx) * 4, vr[idx % D]);
+    wait_stores();
     __syncthreads();
-    flush_run(b, 1);
+    arrive(b, 0);
   };
 
   int units_done = 0;
-
-  // appended tokens of this workgroup (fused form): team kvh of the HBM tier,
-  // or of the host tier when there is none; the last workgroups of the team
-  // take them, which have the fewest items
-  if (FUSED && a.new_tokens) {
-    const bool mine_role = T.team_d > 0 ? !host_role : host_role;
-    if (mine_role)
-      for (int b = team - 1 - jt; b < B; b += team) new_token(b);
-  }
+  // Appended tokens (fused form): one (sequence, KV head) pair each, queued
+  // after the attention units of the HBM tier (of the host tier when there is
+  // no HBM tier), so the first workgroups to run out of units take them.
+  const int n_new = (FUSED && a.new_tokens && fits && (T.team_d > 0 ? !host_role : host_role)) ? B * a.hkv : 0;
 
   u32x4 kreg[NC], vreg[NC];
   // Paged: the physical page of each of this thread's chunks of a tile, from
@@ -734,14 +775,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // unit u: the item (and, split form, the KV head) it stands for
+  // unit u: its item and KV head
   auto unit_item = [&](int u, int* kv) -> DItem {
-    if (FUSED) return item_at(L, B, host_role, u);
     const int item = u / a.hkv;
     *kv = u - item * a.hkv;
     return item_at(L, B, host_role, item);
   };
-  int i = jt;
+  int i = r_idx;
   DItem it{};
   int32_t pte[NC] = {};
   // paged: pte holds the pages of the next tile to load (looked up one tile
@@ -752,17 +792,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     load_tile(it, kvh, 0, pte);
     if (PAGED) lookup(it, min(1, (it.n_tok - 1) / kTile), pte);
   }
-  bool run_open = false;  // fused: online-softmax state carries a run of sequence run_b
-  int run_b = -1, run_items = 0;
-  float m_run = -INFINITY;  // per lane: state of head (n & 7)
-  float l_run = 0.f;
   float acc[G][DPL];
   bf16x8_t qb[KS];
   while (i < n_units) {
     ++units_done;
     const int ntiles = (it.n_tok + kTile - 1) / kTile;
-    if (!run_open) {
-      if (q_b != it.b || q_kvh != kvh) rotate_q(it.b);
+    if (q_b != it.b || q_kvh != kvh) rotate_q(it.b);
+    {
       // query operand: columns h (high bf16 part) and h+8 (low part)
       const int hsel = n & 7;
       const bool active = hsel < G;
@@ -787,17 +823,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         u32x4 wv = {w[0], w[1], w[2], w[3]};
         qb[ks] = __builtin_bit_cast(bf16x8_t, wv);
       }
-      m_run = -INFINITY;
-      l_run = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-      run_open = true;
-      run_b = it.b;
-      run_items = 0;
     }
-
+    float m_run = -INFINITY;  // per lane: state of head (n & 7)
+    float l_run = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
     int next_i = n_units;
     int nkvh = kvh;
     DItem nit{};
@@ -812,7 +844,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
       }
       const bool last = tile + 1 == ntiles;
-      if (last && tid == 0) s_next = first_stride + atomicAdd(qctr, 1);
+      if (last && tid == 0) s_next = role_wgs + atomicAdd(qctr, 1);
       __syncthreads();
       // keep one tile in flight: the next tile of this item, or the first
       // tile of the next item while this item's last tile is computed
@@ -897,13 +929,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-    ++run_items;
 
-    // ---- end of an item (split form) or of a run (fused form): combine the
-    // four waves and write the partial
-    const bool flush = !FUSED || next_i >= n_units || nit.b != run_b;
-    if (flush) {
-      __syncthreads();
+    // ---- end of the unit: combine the four waves and write its partial
+    __syncthreads();
+    {
       float* sm_m = reinterpret_cast<float*>(k_lds);   // [4][G]
       float* sm_l = sm_m + 4 * G;                      // [4][G]
       float* sm_acc = sm_l + 4 * G;                    // [4][G][D]
@@ -916,6 +945,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) sm_acc[(wave * G + h) * D + lane * DPL + e] = acc[h][e];
       __syncthreads();
+      const int slot = FUSED ? it.slot + (it.b + 1) * a.new_tokens : it.slot;
       for (int idx = tid; idx < G * D; idx += kThreads) {
         const int h = idx / D, d = idx - h * D;
         float M = -INFINITY;
@@ -933,31 +963,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           o = o / lsum;
         }
         const float lse = (M == -INFINITY) ? -INFINITY : (M + log2f(lsum)) * 0.69314718055994530942f;
+        const int hq_idx = kvh * G + h;
         if (FUSED) {
-          o_lds[h][d] = o;
-          if (d == 0) l_lds[h] = lse;
+          coherent_store1(coherent_rsrc(a.part_o), ((slot * a.hq + hq_idx) * D + d) * 4, o);
+          if (d == 0) coherent_store1(coherent_rsrc(a.part_lse), (slot * a.hq + hq_idx) * 4, lse);
         } else {
-          const int hq_idx = kvh * G + h;
-          a.part_o[((size_t)it.slot * a.hq + hq_idx) * D + d] = o;
-          if (d == 0) a.part_lse[(size_t)it.slot * a.hq + hq_idx] = lse;
+          a.part_o[((size_t)slot * a.hq + hq_idx) * D + d] = o;
+          if (d == 0) a.part_lse[(size_t)slot * a.hq + hq_idx] = lse;
         }
       }
       if (FUSED) {
+        wait_stores();
         __syncthreads();
-        flush_run(run_b, run_items);
+        arrive(it.b, a.new_tokens + it.slot - L.off[it.b]);
       }
-      run_open = false;
     }
     // the next item's first tile is already in registers
     i = next_i;
     it = nit;
     kvh = nkvh;
   }
+  // appended tokens: queue indices [n_units, n_units + n_new)
+  if constexpr (FUSED) {
+    while (i < n_units + n_new) {
+      const int pr = i - n_units;
+      kvh = pr % a.hkv;
+      new_token(pr / a.hkv);
+      if (tid == 0) s_next = role_wgs + atomicAdd(qctr, 1);
+      __syncthreads();
+      i = __builtin_amdgcn_readfirstlane(s_next);
+    }
+  }
 
-  // Fused form: groups with nothing to merge (no tokens and no appended token).
-  if (FUSED && !a.new_tokens && blockIdx.x == 0) {
+  // Fused form: sequences with nothing to merge (no tokens and no appended token).
+  if (FUSED && !a.new_tokens && fits && blockIdx.x == 0) {
     for (int b = 0; b < B; ++b)
-      if (L.ph[b + 1] == L.ph[b] && L.pm[b + 1] == L.pm[b] && L.pt[b + 1] == L.pt[b])
+      if (L.off[b + 1] == L.off[b])
         for (int idx = tid; idx < a.hq * D; idx += kThreads) {
           a.out_o[(size_t)b * a.hq * D + idx] = 0.f;
           if (idx < a.hq && a.out_lse) a.out_lse[(size_t)b * a.hq + idx] = -INFINITY;
@@ -971,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int ec = decode_exit_counter();
     const int done = atomicAdd(&a.counters[ec], 1) + 1;
     if (done == (int)gridDim.x) {
-      for (int k = decode_queue(a.hkv, true, 0); k < decode_counter_words(a.hkv); ++k)
+      for (int k = decode_queue(true); k < decode_counter_words(); ++k)
         __hip_atomic_store(&a.counters[k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.counters[ec], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -988,9 +1029,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Static scratch for callers that cannot allocate device memory (the
 // allocation-free decode step): a file-scope device array, one copy on every
-// GPU the library runs on, zero when the code object loads.  Every completed
-// call leaves its counters at zero again (and rewrites everything else it
-// reads), so calls of any shape follow each other on it; calls that overlap
+// GPU the library runs on, zero when the code object loads.  Its first
+// kDecodeStaticCounterBytes hold the counters of every call and nothing else;
+// every completed call leaves them at zero again and rewrites everything else
+// it reads, so calls of any shape follow each other on it; calls that overlap
 // on one GPU race.  Host code never uses the array's name as an address: the
 // per-device address comes from hipGetSymbolAddress.
 // ---------------------------------------------------------------------------

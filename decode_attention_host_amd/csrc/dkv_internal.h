@@ -166,18 +166,18 @@ struct DecodeArgs {
   int32_t fused;                 // 1: merge in the kernel (last finisher per sequence and KV head)
   DecodeTemplate tmpl;
   // workspace
-  int32_t* counters;             // error flags, exit count, [2 Hkv] item queues (decode_queue)
-  int32_t* group_cnt;            // fused: [batch * Hkv][2] items done, partials written
+  int32_t* counters;             // error flags, exit count, the two tiers' unit queues (decode_queue)
+  int32_t* group_cnt;            // fused: [max_slots][Hkv] units done per group of slots (at the
+                                 // group's first slot), then [batch][Hkv] groups done
   const int32_t* tier_counts;    // paged: [batch][4] host pages, HBM pages, host tokens, HBM tokens
   const int32_t* tier_pages;     // paged: [2][batch][max_pages] physical pages, host tier then HBM
-  // split form: one normalised partial per item
-  float* part_o;                 // [S][Hq][D]
-  float* part_lse;               // [S][Hq]
-  int32_t* split_offsets;        // [batch + 1] (written by workgroup 0)
-  // fused form
-  float* run_o;                  // [batch * Hkv][max_slots][G][D] partials of workgroup runs
-  float* run_lse;                // [batch * Hkv][max_slots][G]
-  int32_t max_slots;
+  // one normalised partial per (item, KV head): the caller's arrays (split
+  // form) or the workspace's (fused form, where each sequence's item slots
+  // are followed by one for its appended token)
+  float* part_o;                 // [max_slots][Hq][D]
+  float* part_lse;               // [max_slots][Hq]
+  int32_t* split_offsets;        // split form: [batch + 1] (written by workgroup 0)
+  int32_t max_slots;             // slots part_o and part_lse hold
   int32_t new_tokens;            // 1: each sequence first appends a token at pos_new[b]
   float* out_o;                  // [batch][Hq][D]
   float* out_lse;                // [batch][Hq] or NULL
@@ -194,15 +194,15 @@ struct DecodeArgs {
 // Counter words of the decode workspace (int32 offsets from `counters`): the
 // error flags first, at a place no other shape uses for a counter (they are
 // sticky, while every counter returns to zero at the end of each call), then
-// the exit count, then the item queues (host KV heads, then HBM KV heads).
+// the exit count, then the unit queues (host tier, then HBM tier).
 DKV_HD constexpr int decode_error_word() { return 0; }
 DKV_HD constexpr int decode_exit_counter() { return 1; }
-DKV_HD constexpr int decode_queue(int hkv, bool host, int kvh) { return 2 + (host ? 0 : hkv) + kvh; }
-DKV_HD constexpr int decode_counter_words(int hkv) { return 2 + 2 * hkv; }
+DKV_HD constexpr int decode_queue(bool host) { return host ? 2 : 3; }
+DKV_HD constexpr int decode_counter_words() { return 4; }
 constexpr int kDecodeErrLayout = 1;     // a contiguous sequence's rows exceed its stride or pool
 constexpr int kDecodeErrPage = 2;       // a page entry is negative or beyond its tier's pool
 constexpr int kDecodeErrSlot = 4;       // an appended token has no valid cache slot
-constexpr int kDecodeErrCapacity = 8;   // a partial slot beyond the workspace (never expected)
+constexpr int kDecodeErrCapacity = 8;   // the call needs more partial slots than it was given (nothing computed)
 
 struct MergeArgs {
   const float* part_o;
@@ -339,6 +339,10 @@ int launch_decode(const DecodeArgs& a, void* stream);
 // The static decode scratch of the current device (dkv_decode.hip): its
 // device address (from hipGetSymbolAddress, once per device) and size.
 constexpr size_t kDecodeStaticScratchBytes = DKV_STATIC_SCRATCH_BYTES;
+// Its first kDecodeStaticCounterBytes hold the counters of every call and
+// nothing else, so they are zero at the start of a call whatever the shape of
+// the call before it (each call leaves its counters at zero).
+constexpr size_t kDecodeStaticCounterBytes = 1u << 20;
 constexpr int kMaxDevices = 64;
 int decode_static_scratch(void** ptr, size_t* bytes);
 int launch_merge(const MergeArgs& a, void* stream);

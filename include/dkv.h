@@ -164,7 +164,9 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
  * lengths and bytes per tier those lengths give.
  *
  * Workspace (device memory, 256-byte aligned): zero-filled before its first
- * use; every call leaves its counters at zero again, so it is reused as is.
+ * use; every call leaves its counters at zero again, so calls of the same
+ * shape (descriptor, batch, heads, ratio) reuse it as is.  Where the counters
+ * lie depends on the shape: zero it again before a call of another shape.
  * Calls that share a workspace must not overlap (they race).  The call
  * allocates nothing and never synchronises, so it may be captured into a HIP
  * graph: each replay reads the lengths and positions present in device
@@ -178,8 +180,9 @@ dkv_status dkv_project_rope_append(const dkv_kv_desc* kv, int32_t batch,
  * ---------------------------------------------------------------------- */
 typedef struct dkv_plan_info {
   int64_t workspace_bytes; /* device workspace the call needs */
-  int32_t num_splits;      /* decode: split bound S (step: partial slots per sequence
-                              and KV head); prefill: splits of the plan */
+  int32_t num_splits;      /* decode: split bound S (step: partial slots in the
+                              workspace, S plus one per sequence); prefill: splits
+                              of the plan */
   int32_t host_items;      /* work items in the host tier (per KV head) */
   int32_t dev_items;       /* work items in the HBM tier (per KV head) */
   int32_t host_wgs;        /* workgroups streaming the host tier */
@@ -232,11 +235,12 @@ dkv_status dkv_plan_inspect(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_
  * rotated at that position in fp64 and rounded once to bf16, and the query
  * attends to the seq_lens[b] cached tokens plus the new one (read from
  * registers, as stored).  With no new token (k_new = v_new = x = NULL) the
- * query attends to the cached tokens only.  The partials of each (sequence,
- * KV head) are merged by log-sum-exp inside the same launch (the last
- * workgroup to finish one merges it): out_o [batch][Hq][D] fp32, out_lse
- * [batch][Hq] fp32 (or NULL).  A sequence with nothing to attend gets
- * out_o = 0 and out_lse = -inf.
+ * query attends to the cached tokens only.  Work is cut and queued as in
+ * dkv_decode_attn_split; the partials of each (sequence, KV head) are merged
+ * by log-sum-exp inside the same launch, in groups of up to 16 (the last
+ * workgroup to finish a group merges it, the last group merges the groups):
+ * out_o [batch][Hq][D] fp32, out_lse [batch][Hq] fp32 (or NULL).  A sequence
+ * with nothing to attend gets out_o = 0 and out_lse = -inf.
  *
  * One kernel launch (plus the paged layout's tier lists and, with x, the
  * projection).  Workspace from dkv_decode_step_plan (hidden = 0 without

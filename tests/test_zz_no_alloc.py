@@ -1,7 +1,9 @@
 """The allocation-free decode step (dkv_decode_step_static) against the step on
 a caller workspace (dkv_decode_step): same outputs within the parity bar and
-the same appended cache rows, on two calls in a row (the second smaller, so the
-static scratch holds the first call's contents when the second starts)."""
+the same appended cache rows, on calls in a row: the second smaller, so the
+static scratch holds the first call's contents when the second starts, and a
+third larger than both, whose counters would reach where the earlier calls kept
+partials and page lists if the scratch did not keep its counters apart."""
 import math
 
 import numpy as np
@@ -75,9 +77,11 @@ def _case(dk, lens, hq, hkv, d, frac, seed):
     return outs, rows
 
 
-def test_static_scratch_step_matches_workspace_step_twice(dk):
-    # first call: 3 sequences, 32 / 8 heads; second call smaller: 1 sequence, 8 / 2 heads, D = 64
-    for lens, hq, hkv, d, frac, seed in (([700, 16, 1500], 32, 8, 128, 0.8, 91), ([300], 8, 2, 64, 0.5, 92)):
+def test_static_scratch_step_matches_workspace_step_in_a_row(dk):
+    # first call: 3 sequences, 32 / 8 heads; second call smaller: 1 sequence, 8 / 2 heads, D = 64;
+    # third call larger: 6 sequences, 32 / 8 heads
+    for lens, hq, hkv, d, frac, seed in (([700, 16, 1500], 32, 8, 128, 0.8, 91), ([300], 8, 2, 64, 0.5, 92),
+                                         ([2000, 5, 900, 64, 3100, 1], 32, 8, 128, 0.3, 93)):
         (ref, got), (ra, rb) = _case(dk, lens, hq, hkv, d, frac, seed)
         eo = float(np.abs(got[0] - ref[0]).max())
         el = float(np.abs(got[1] - ref[1]).max())
@@ -90,8 +94,9 @@ def test_static_scratch_rejects_oversized_shapes(dk):
     import torch
     from decode_attention_host_amd.cache_build import paged_cache
     from decode_attention_host_amd._lib import DkvError
-    # 512 sequences x 32 heads: the run partials exceed the static scratch
-    B, hq, hkv, d = 512, 32, 32, 128
+    # 512 sequences x 128 query heads: the partial slots (about 1800 of
+    # 128 x 128 fp32) exceed the static scratch
+    B, hq, hkv, d = 512, 128, 16, 128
     pt = np.zeros((B, 1), dtype=np.int32)
     cache = dk.KVCache(hkv, d, host_rows=0, dev_rows=16, page_size=16, page_table=pt)
     q = torch.zeros((B, hq, d), dtype=torch.int16, device="cuda")
