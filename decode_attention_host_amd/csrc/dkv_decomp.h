@@ -10,9 +10,8 @@
 // contiguous layout, the tier's rows in order; paged layout, the tier's pages
 // in logical order).  An item is a run of ordinals of one sequence in one
 // tier, processed once per KV head.  Each tier has `team` workgroups per KV
-// head: the fused form binds each to one KV head and walks that head's items
-// in order; the split form walks (item, KV head) units in order, KV head
-// fastest, over all of the tier's workgroups.
+// head (Hkv * team in all), which take the tier's (item, KV head) units in
+// order, KV head fastest, from one queue.
 // SplitKernel README, Overview: both tiers stream at the same time; Key
 // Features: attention over a host/device partitioned KV cache.
 #pragma once
@@ -35,7 +34,7 @@ constexpr int32_t kDecodeChunkCap = 1 << 22;
 
 // Fixed on the host from the call's shape alone (no lengths).
 struct DecodeTemplate {
-  int32_t hkv;      // KV heads = teams per tier
+  int32_t hkv;      // KV heads
   int32_t team_h;   // host-tier workgroups per KV head (0: no host tier)
   int32_t team_d;   // HBM-tier workgroups per KV head (0: no HBM tier)
   int32_t upw_h;    // items per workgroup the host chunk size aims at
@@ -88,14 +87,14 @@ DKV_HD inline DecodeSizes decode_sizes(const DecodeTemplate& t, int64_t tot_h, i
   z.ch = decode_chunk(tot_h, t.team_h, t.upw_h, t.floor_h, t.align, t.tuned_h);
   z.cd = decode_chunk(tot_d, t.team_d, t.upw_d, t.floor_d, t.align, t.tuned_d);
   z.cs = (int32_t)(decomp_cdiv(z.cd / 4, t.align) * t.align);
-  // Guided tail: with items of a few thousand tokens the workgroups of a team
+  // Guided tail: with items of a few thousand tokens the workgroups of a tier
   // run out of work up to one item apart, so the last part of every HBM range
   // (about two tail items per workgroup in all) is cut into quarter-size
   // items that come after every other HBM item.
   z.guided = (t.guided && t.tuned_d <= 0 && z.cs >= 512 && t.team_d > 0 &&
               tot_d >= (int64_t)z.cd * t.team_d * 4) ? 1 : 0;
   if (z.guided) {
-    const int64_t want = 4 * (int64_t)t.team_d * z.cs;  // twice the tail tokens, per team
+    const int64_t want = 4 * (int64_t)t.team_d * z.cs;  // twice the tail tokens, per KV head
     z.tail_num = tot_d < want ? tot_d : want;           // fraction min(1/2, 2 team cs / tot)
     z.tail_den = 2 * tot_d;
   } else {
