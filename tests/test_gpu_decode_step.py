@@ -180,6 +180,52 @@ def test_max_batch_512_both_forms(dk):
     cache.free()
 
 
+@pytest.mark.parametrize("ratio", [0.0, 0.5])
+def test_step_merge_group_boundaries(dk, ratio):
+    """The fused step folds a sequence's partial slots (its new token's, then one
+    per item) in groups of 16 and then folds the groups.  With one-tile items
+    (64 tokens) the cached lengths below give 1, 2, 16, 17, 18, 33, 34 and 81
+    slots: a single slot, one partial group, one full group, a last group of
+    one slot (its own result) or of two, and five full groups plus one; at
+    r = 0.5 the items of a sequence lie in both tiers.  With and without the
+    new token, against the oracle (and, without it, the split form)."""
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    lens, hq, hkv, d, th = [0, 1, 64, 960, 1024, 1025, 2048, 2049, 5120], 8, 2, 64, 1e4
+    B = len(lens)
+    full = [L + 1 for L in lens]
+    ks, vs = kv_raw(95, full, hkv, d)
+    qb = query(95, B, hq, d)
+    dk.set_tuning(host_chunk=64, dev_chunk=64)
+    try:
+        cache = contiguous_cache(hkv, d, full, ratio, ks, vs, th, upto=lens)
+        k_new = _bits(np.stack([k[L] for k, L in zip(ks, lens)]))
+        v_new = _bits(np.stack([v[L] for v, L in zip(vs, lens)]))
+        o, lse = dk.decode_step(cache, _bits(qb), _dev(lens), _dev(lens), ratio, 1 / math.sqrt(d), th,
+                                k_new=k_new, v_new=v_new)
+        torch.cuda.synchronize()
+        ro, rl = _oracle_step(qb, ks, vs, lens, th)
+        o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        for b, L in enumerate(lens):
+            _check(o[b], lse[b], ro[b], rl[b], f"r={ratio} cached {L} + new token")
+        cache.free()
+        # no new token: the cached tokens only (the first sequence has none)
+        cache = contiguous_cache(hkv, d, lens, ratio, ks, vs, th)
+        qpos = _dev([max(0, L - 1) for L in lens])
+        o, lse = dk.decode_step(cache, _bits(qb), qpos, _dev(lens), ratio, 1 / math.sqrt(d), th)
+        o2, l2, _ = dk.decode(cache, _bits(qb), qpos, _dev(lens), ratio, 1 / math.sqrt(d), th)
+        torch.cuda.synchronize()
+        o, lse, o2, l2 = (t.cpu().numpy().astype(np.float64) for t in (o, lse, o2, l2))
+        assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+        assert np.abs(o[1:] - o2[1:]).max() < 1e-5 and np.abs(lse[1:] - l2[1:]).max() < 1e-5
+        for b, L in enumerate(lens[1:], start=1):
+            rob, rlb = O.decode_sequence(qb[b], ks[b][:L], vs[b][:L], L - 1, th, 1 / math.sqrt(d))
+            _check(o[b], lse[b], rob, rlb, f"r={ratio} cached {L}, no new token")
+        cache.free()
+    finally:
+        dk.reset_tuning()
+
+
 def test_step_without_new_token_equals_split_form(dk):
     # no new token: the fused launch attends to the cached tokens only and must
     # agree with the split form (attention + merge) and the oracle
