@@ -226,6 +226,30 @@ def test_step_merge_group_boundaries(dk, ratio):
         dk.reset_tuning()
 
 
+def test_step_merge_folds_groups_in_chunks(dk):
+    """A sequence with more group results than the final fold stages at once
+    (288 lse values per head at D = 64, G = 8): 300,000 cached tokens in
+    one-tile items give 4,689 slots per KV head, so 294 groups, folded in two
+    chunks.  Against the oracle over every head."""
+    import torch
+    from decode_attention_host_amd.cache_build import contiguous_cache
+    L, hq, hkv, d, th = 300000, 16, 2, 64, 5e5
+    ks, vs = kv_raw(96, [L + 1], hkv, d)
+    qb = query(96, 1, hq, d)
+    dk.set_tuning(dev_chunk=64)
+    try:
+        cache = contiguous_cache(hkv, d, [L + 1], 0.0, ks, vs, th, upto=[L])
+        o, lse = dk.decode_step(cache, _bits(qb), _dev([L]), _dev([L]), 0.0, 1 / math.sqrt(d), th,
+                                k_new=_bits(ks[0][L:L + 1]), v_new=_bits(vs[0][L:L + 1]))
+        torch.cuda.synchronize()
+        cache.free()
+    finally:
+        dk.reset_tuning()
+    ro, rl = _oracle_step(qb, ks, vs, [L], th)
+    _check(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+           "300k tokens, 294 merge groups")
+
+
 def test_step_without_new_token_equals_split_form(dk):
     # no new token: the fused launch attends to the cached tokens only and must
     # agree with the split form (attention + merge) and the oracle
