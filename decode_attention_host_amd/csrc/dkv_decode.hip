@@ -27,7 +27,8 @@
 //     needs no host work beyond argument checks.
 //   * Queues.  Each tier has one queue of (item, KV head) units with the KV
 //     head fastest, taken in order (first by index, then by an atomic
-//     counter), so the workgroups of a tier stream neighbouring rows of the
+//     counter, or round-robin when a tier has at most two units per
+//     workgroup), so the workgroups of a tier stream neighbouring rows of the
 //     same token range at once (DRAM page locality).  Fused form: the
 //     appended tokens, one unit per (sequence, KV head), follow the HBM
 //     tier's attention units in its queue, so the first workgroups to run out
@@ -368,9 +369,31 @@ __device__ void build_prefix(const DecodeArgs& a, DecodeLds& L) {
     th += nh;
     td += nd;
   }
-  th = wave_sum64(th);
-  td = wave_sum64(td);
+  if (B == 1) {  // one sequence (workgroup-uniform): lane 0 holds the totals
+    th = __shfl(th, 0);
+    td = __shfl(td, 0);
+  } else {
+    th = wave_sum64(th);
+    td = wave_sum64(td);
+  }
   const DecodeSizes z = decode_sizes(a.tmpl, th, td);
+  if (B == 1) {  // no scans: the prefix of one sequence is its item counts
+    if (lane == 0) {
+      const DecodeSeqItems s = decode_seq_items(z, a.tmpl.align, L.nh[0], L.nd[0]);
+      L.ph[0] = 0;
+      L.pm[0] = 0;
+      L.pt[0] = 0;
+      L.off[0] = 0;
+      L.t0[0] = (int32_t)s.t0;
+      L.ph[1] = s.uh;
+      L.pm[1] = s.um;
+      L.pt[1] = s.ut;
+      L.off[1] = s.uh + s.um + s.ut;
+      L.z = z;
+    }
+    if (err) atomicOr(&a.counters[decode_error_word()], err);
+    return;
+  }
   int ch = 0, cm = 0, ct = 0, cs = 0;  // running totals of earlier chunks of 64 sequences
   for (int base = 0; base < B; base += 64) {
     const int b = base + lane;
@@ -735,6 +758,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // after the attention units of the HBM tier (of the host tier when there is
   // no HBM tier), so the first workgroups to run out of units take them.
   const int n_new = (FUSED && a.new_tokens && fits && (T.team_d > 0 ? !host_role : host_role)) ? B * a.hkv : 0;
+  // A tier with at most two units per workgroup deals them round-robin (the
+  // next unit of a workgroup is its current one plus the workgroup count):
+  // with so few, the queue balances nothing, and its atomic would put a round
+  // trip at the end of every unit.
+  const bool dealt = n_units + n_new <= 2 * role_wgs;
 
   u32x4 kreg[NC], vreg[NC];
   // Paged: the physical page of each of this thread's chunks of a tile, from
@@ -844,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(v_lds + r * S::kPitch + col * 16) = vreg[c];
       }
       const bool last = tile + 1 == ntiles;
-      if (last && tid == 0) s_next = role_wgs + atomicAdd(qctr, 1);
+      if (last && tid == 0) s_next = dealt ? i + role_wgs : role_wgs + atomicAdd(qctr, 1);
       __syncthreads();
       // keep one tile in flight: the next tile of this item, or the first
       // tile of the next item while this item's last tile is computed
@@ -989,7 +1017,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int pr = i - n_units;
       kvh = pr % a.hkv;
       new_token(pr / a.hkv);
-      if (tid == 0) s_next = role_wgs + atomicAdd(qctr, 1);
+      if (tid == 0) s_next = dealt ? i + role_wgs : role_wgs + atomicAdd(qctr, 1);
       __syncthreads();
       i = __builtin_amdgcn_readfirstlane(s_next);
     }

@@ -41,7 +41,7 @@ struct DecodeTemplate {
   int32_t upw_d;    // items per workgroup the HBM chunk size aims at
   int32_t floor_h;  // fewest tokens per host item
   int32_t floor_d;  // fewest tokens per HBM item
-  int32_t align;    // item granularity: a multiple of 64 and of the page size
+  int32_t align;    // item granularity: a power of two, 64 or the page size
   int32_t guided;   // 1: the end of each long HBM range is cut finer
   int32_t tuned_h;  // > 0: fixed host item length (tokens, multiple of align)
   int32_t tuned_d;  // > 0: fixed HBM item length
@@ -67,17 +67,33 @@ struct DecodeSeqItems {
   int64_t t0;        // first tail ordinal of the HBM range (= its length when no tail)
 };
 
-DKV_HD inline int64_t decomp_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Quotient of a >= 0 by b > 0: a 32-bit division when both fit in 32 bits (on
+// the GPU a 64-bit division is a long software sequence, a 32-bit one a
+// short one), else a 64-bit one; the same exact result either way.
+DKV_HD inline int64_t decomp_div(int64_t a, int64_t b) {
+  if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
+DKV_HD inline int64_t decomp_cdiv(int64_t a, int64_t b) {
+  if (a < 0) return (a + b - 1) / b;
+  const int64_t q = decomp_div(a, b);
+  return q * b == a ? q : q + 1;
+}
+
+// x >= 0 rounded up / down to a multiple of align, a power of two.
+DKV_HD inline int64_t decomp_round_up(int64_t x, int32_t align) { return (x + align - 1) & ~(int64_t)(align - 1); }
+DKV_HD inline int64_t decomp_round_down(int64_t x, int32_t align) { return x & ~(int64_t)(align - 1); }
 
 // Tokens per item: enough that a tier's `team` workgroups see about `upw`
 // items each, at least floor_tok, a multiple of align, at most the cap.
 DKV_HD inline int32_t decode_chunk(int64_t tokens, int32_t team, int32_t upw, int32_t floor_tok, int32_t align,
                                    int32_t tuned) {
-  if (tuned > 0) return (int32_t)(decomp_cdiv(tuned, align) * align);
+  if (tuned > 0) return (int32_t)decomp_round_up(tuned, align);
   int64_t c = (team > 0 && tokens > 0) ? decomp_cdiv(tokens, (int64_t)team * (upw > 0 ? upw : 1)) : 1;
   if (c < floor_tok) c = floor_tok;
-  c = decomp_cdiv(c, align) * align;
-  const int64_t cap = (int64_t)kDecodeChunkCap / align * align;
+  c = decomp_round_up(c, align);
+  const int64_t cap = decomp_round_down(kDecodeChunkCap, align);
   return (int32_t)(c < cap ? c : cap);
 }
 
@@ -86,7 +102,7 @@ DKV_HD inline DecodeSizes decode_sizes(const DecodeTemplate& t, int64_t tot_h, i
   DecodeSizes z{};
   z.ch = decode_chunk(tot_h, t.team_h, t.upw_h, t.floor_h, t.align, t.tuned_h);
   z.cd = decode_chunk(tot_d, t.team_d, t.upw_d, t.floor_d, t.align, t.tuned_d);
-  z.cs = (int32_t)(decomp_cdiv(z.cd / 4, t.align) * t.align);
+  z.cs = (int32_t)decomp_round_up(z.cd / 4, t.align);
   // Guided tail: with items of a few thousand tokens the workgroups of a tier
   // run out of work up to one item apart, so the last part of every HBM range
   // (about two tail items per workgroup in all) is cut into quarter-size
@@ -109,7 +125,7 @@ DKV_HD inline DecodeSeqItems decode_seq_items(const DecodeSizes& z, int32_t alig
   DecodeSeqItems s{};
   s.uh = nh > 0 ? (int32_t)decomp_cdiv(nh, z.ch) : 0;
   // nd < 2^31 and tail_num <= 4 * team * cs <= 2^32 keep the product in range
-  const int64_t tail = z.guided ? (nd * z.tail_num / z.tail_den) / align * align : 0;
+  const int64_t tail = z.guided ? decomp_round_down(decomp_div(nd * z.tail_num, z.tail_den), align) : 0;
   s.t0 = nd - tail;
   s.um = s.t0 > 0 ? (int32_t)decomp_cdiv(s.t0, z.cd) : 0;
   s.ut = tail > 0 ? (int32_t)decomp_cdiv(tail, z.cs) : 0;
@@ -140,11 +156,11 @@ DKV_HD inline int64_t decode_max_splits(const DecodeTemplate& t, int32_t batch, 
   int64_t s = 0;
   if (t.team_h > 0) {
     const int64_t by_len = t.tuned_h > 0 ? decomp_cdiv(host_cap, t.tuned_h) : (int64_t)t.team_h * t.upw_h;
-    s += by_len + host_cap / (kDecodeChunkCap / t.align * t.align) + batch;
+    s += by_len + host_cap / decomp_round_down(kDecodeChunkCap, t.align) + batch;
   }
   if (t.team_d > 0) {
     const int64_t by_len = t.tuned_d > 0 ? decomp_cdiv(dev_cap, t.tuned_d) : (int64_t)t.team_d * t.upw_d;
-    s += by_len + dev_cap / (kDecodeChunkCap / t.align * t.align) + batch;  // main items
+    s += by_len + dev_cap / decomp_round_down(kDecodeChunkCap, t.align) + batch;  // main items
     if (t.guided && t.tuned_d <= 0) s += 2 * (int64_t)t.team_d + batch;   // tail items
   }
   return s;
