@@ -657,15 +657,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   };
 
   // Fused form, appended token of (b, kvh): rotate its key at pos_new[b]
-  // (fp64, one bf16 rounding), store K and V in the token's cache slot, and
-  // write its one-token partial (o = v, lse = its scaled score) into the
-  // sequence's first slot.
+  // (fp64, one bf16 rounding), write its one-token partial (o = v, lse = its
+  // scaled score) into the sequence's first slot, count it, and store K and V
+  // in the token's cache slot.  The token's own loads are issued before the
+  // query rotation, and the cache stores after the count: nothing in this
+  // launch reads the cache row, and waiting for their acknowledgement (a PCIe
+  // write for a host slot) would delay the count.
   auto new_token = [&](int b) {
-    if (q_b != b || q_kvh != kvh) rotate_q(b);
+    const int kvd = a.hkv * D;
     const int p = a.pos_new ? a.pos_new[b] : a.seq_lens[b];
+    int64_t Lb = PAGED ? 0 : a.seq_lens[b];
+    // this thread's inputs: K pair (i, i + D/2) for tid < D/2, V dims (i, i + D/2) for D/2 <= tid < D
+    const int i = tid < D / 2 ? tid : tid - D / 2;
+    float in0 = 0.f, in1 = 0.f;
+    if (tid < D) {
+      const size_t base = tid < D / 2 ? (size_t)kvh * D : (size_t)kvd + kvh * D;  // projection: K then V
+      if (a.kv_proj) {
+        const float* src = a.kv_proj + (size_t)b * 2 * kvd + base;
+        in0 = src[i];
+        in1 = src[i + D / 2];
+      } else {
+        const uint16_t* src = (tid < D / 2 ? a.k_new : a.v_new) + (size_t)b * kvd + kvh * D;
+        in0 = bf16_to_f32(src[i]);
+        in1 = bf16_to_f32(src[i + D / 2]);
+      }
+    }
+    if (q_b != b || q_kvh != kvh) rotate_q(b);
     float* kr = reinterpret_cast<float*>(k_lds);  // rotated key (bf16 values) [D]
     float* vr = kr + D;                           // value [D]
-    const int kvd = a.hkv * D;
     // slot of (b, p)
     uint16_t* sk = nullptr;
     uint16_t* sv = nullptr;
@@ -682,7 +701,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           }
         }
       } else {
-        int64_t Lb = a.seq_lens[b];
         if (Lb < 0) Lb = 0;
         int64_t nh, nd, ph;
         contig_tiers(a.ratio, Lb, Lb + 1, &nh, &nd, &ph);
@@ -699,37 +717,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
     if (!sk && tid == 0) atomicOr(&a.counters[decode_error_word()], kDecodeErrSlot);
+    // bf16 bits this thread stores into the cache row after the count
+    uint32_t out0 = 0, out1 = 0;
     if (tid < D / 2) {
-      const int i = tid;
-      double xl, xh;
-      if (a.kv_proj) {
-        const float* kp = a.kv_proj + (size_t)b * 2 * kvd + kvh * D;
-        xl = (double)kp[i];
-        xh = (double)kp[i + D / 2];
-      } else {
-        const uint16_t* kp = a.k_new + (size_t)b * kvd + kvh * D;
-        xl = (double)bf16_to_f32(kp[i]);
-        xh = (double)bf16_to_f32(kp[i + D / 2]);
-      }
       double sn, cs;
       sincos((double)p * a.freq.f[i], &sn, &cs);
-      const uint32_t yl = f64_to_bf16(xl * cs - xh * sn);
-      const uint32_t yh = f64_to_bf16(xh * cs + xl * sn);
-      kr[i] = bf16_to_f32(yl);
-      kr[i + D / 2] = bf16_to_f32(yh);
-      if (sk) {
-        sk[i] = (uint16_t)yl;
-        sk[i + D / 2] = (uint16_t)yh;
-      }
+      const double xl = (double)in0, xh = (double)in1;
+      out0 = f64_to_bf16(xl * cs - xh * sn);
+      out1 = f64_to_bf16(xh * cs + xl * sn);
+      kr[i] = bf16_to_f32(out0);
+      kr[i + D / 2] = bf16_to_f32(out1);
     } else if (tid < D) {
-      const int i = tid - D / 2;
-      for (int d = i; d < D; d += D / 2) {
-        uint32_t vb;
-        if (a.kv_proj) vb = f32_to_bf16(a.kv_proj[(size_t)b * 2 * kvd + kvd + kvh * D + d]);
-        else vb = a.v_new[(size_t)b * kvd + kvh * D + d];
-        vr[d] = bf16_to_f32(vb);
-        if (sv) sv[d] = (uint16_t)vb;
-      }
+      // V is stored as given (bf16), or rounded once from the fp32 projection
+      out0 = a.kv_proj ? f32_to_bf16(in0) : (__float_as_uint(in0) >> 16);
+      out1 = a.kv_proj ? f32_to_bf16(in1) : (__float_as_uint(in1) >> 16);
+      vr[i] = bf16_to_f32(out0);
+      vr[i + D / 2] = bf16_to_f32(out1);
     }
     __syncthreads();
     const int slot = seq_first(b);
@@ -751,6 +754,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     wait_stores();
     __syncthreads();
     arrive(b, 0);
+    if (tid < D / 2) {
+      if (sk) {
+        sk[i] = (uint16_t)out0;
+        sk[i + D / 2] = (uint16_t)out1;
+      }
+    } else if (tid < D) {
+      if (sv) {
+        sv[i] = (uint16_t)out0;
+        sv[i + D / 2] = (uint16_t)out1;
+      }
+    }
   };
 
   int units_done = 0;
