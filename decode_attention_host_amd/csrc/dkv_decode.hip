@@ -539,6 +539,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         wl[idx] = coherent_load1(pr_l, ((s0 + (c0 + k) * step) * a.hq + hq0 + h) * 4);
       }
     };
+    // A fold whose partials fit U per thread (a group of 16 at D = 128,
+    // G = 4) issues their output loads before the lse values are staged, so
+    // both arrive in one round trip; indices past n reload partial n - 1,
+    // which the accumulation skips.  Contiguous layout only: the registers
+    // would take the paged kernels past 256 (one wave per SIMD).
+    const bool pre = !PAGED && n <= U * NSG && n <= CAPN;
+    floatx4 opre[U];
+    if (pre) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) opre[u] = coherent_load4(pr_o, o_off(min(sg + u * NSG, n - 1)));
+    }
     __syncthreads();  // earlier users of the tile buffers and a_lds are done
     for (int c0 = 0; c0 < n; c0 += CAPN) {
       const int cn = min(CAPN, n - c0);
@@ -583,6 +594,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         wl[idx] = (M == -INFINITY || x == -INFINITY) ? 0.f : expf(x - M) / a_lds[1][h];
       }
       __syncthreads();
+      if (pre) {  // one chunk (n <= CAPN), outputs already in registers
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kk = sg + u * NSG;
+          if (kk < cn) {
+            const float w = wl[kk * G + hc];
+            if (w != 0.f) acc += w * opre[u];
+          }
+        }
+        continue;
+      }
       int k = sg;
       for (; k + (U - 1) * NSG < cn; k += U * NSG) {
         floatx4 o[U];
@@ -1047,9 +1069,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
   }
 
-  // Last workgroup out clears the item queues for the next call on this workspace.
+  // Last workgroup out clears the item queues for the next call on this
+  // workspace.  When neither tier took units from its queue (both dealt
+  // round-robin, as every workgroup finds from the same lengths), no counter
+  // moved and the exit count, a round trip at the end of the launch, is
+  // skipped.
+  const auto queue_used = [&](bool host) {
+    const int wgs = a.hkv * (host ? T.team_h : T.team_d);
+    const int units = fits ? (host ? L.ph[B] : L.pm[B] + L.pt[B]) * a.hkv : 0;
+    const int news = (FUSED && a.new_tokens && fits && (T.team_d > 0 ? !host : host)) ? B * a.hkv : 0;
+    return wgs > 0 && units + news > 2 * wgs;
+  };
+  const bool queues = queue_used(true) || queue_used(false);
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && queues) {
     wait_stores();
     const int ec = decode_exit_counter();
     const int done = atomicAdd(&a.counters[ec], 1) + 1;
