@@ -310,7 +310,12 @@ def test_step_with_projection(dk):
     cache.free()
 
 
-def test_workspace_is_left_zeroed_and_clean(dk):
+@pytest.mark.parametrize("queued", [False, True])
+def test_workspace_is_left_zeroed_and_clean(dk, queued):
+    # Dealt: few units per workgroup, dealt round-robin, no queue counter
+    # moves.  Queued: one workgroup per KV head and tier and one-tile items,
+    # so both tiers take units from their counters and the last workgroup out
+    # resets them; three calls in a row on one workspace stay right.
     import torch
     from decode_attention_host_amd.cache_build import paged_cache
     hkv, hq, d, th = 8, 32, 128, 5e5
@@ -319,18 +324,25 @@ def test_workspace_is_left_zeroed_and_clean(dk):
     ks, vs = kv_raw(85, full, hkv, d)
     pt, nh, nd = paged_table(85, full, 16, 0.5)
     cache = paged_cache(hkv, d, full, pt, nh, nd, ks, vs, th, upto=lens)
-    ws = dk.decode_step_workspace(cache, 2, hq, 0.0)
-    qb = query(85, 2, hq, d)
-    for _ in range(3):
-        dk.decode_step(cache, _bits(qb), _dev(lens), _dev(lens), 0.0, 1 / math.sqrt(d), th,
-                       k_new=_bits(np.stack([k[L] for k, L in zip(ks, lens)])),
-                       v_new=_bits(np.stack([v[L] for v, L in zip(vs, lens)])), workspace=ws)
-    torch.cuda.synchronize()
-    # queues, exit count, error word and the (sequence, KV head) counters
-    head = ws[:512].cpu().numpy()
-    assert np.all(head == 0), np.nonzero(head)
-    assert dk.decode_errors(cache, ws) == 0
-    cache.free()
+    if queued:
+        dk.set_tuning(host_wgs=hkv, dev_wgs=hkv, host_chunk=64, dev_chunk=64)
+    try:
+        ws = dk.decode_step_workspace(cache, 2, hq, 0.0)
+        qb = query(85, 2, hq, d)
+        for _ in range(3):
+            o, lse = dk.decode_step(cache, _bits(qb), _dev(lens), _dev(lens), 0.0, 1 / math.sqrt(d), th,
+                                    k_new=_bits(np.stack([k[L] for k, L in zip(ks, lens)])),
+                                    v_new=_bits(np.stack([v[L] for v, L in zip(vs, lens)])), workspace=ws)
+        torch.cuda.synchronize()
+        # queues, exit count, error word and the (sequence, KV head) counters
+        head = ws[:512].cpu().numpy()
+        assert np.all(head == 0), np.nonzero(head)
+        assert dk.decode_errors(cache, ws) == 0
+        ro, rl = _oracle_step(qb, ks, vs, lens, th)
+        _check(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"third call ({'queued' if queued else 'dealt'})")
+    finally:
+        dk.reset_tuning()
+        cache.free()
 
 
 def test_layout_violation_is_flagged_not_read(dk):
