@@ -155,6 +155,8 @@ SIGNATURES = {
     "dkv_kernel_timing_read": (I32, [I32, C.POINTER(I32), C.POINTER(F64)]),
     "dkv_attn_trace": (I32, [P, I32]),
     "dkv_prefill_plan": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, F64, C.POINTER(PlanInfo)]),
+    "dkv_plan_cache_release_captured": (I32, []),
+    "dkv_plan_cache_stats": (I32, [C.POINTER(I32), C.POINTER(I32), C.POINTER(I64)]),
     "dkv_prefill_attn_split": (I32, [C.POINTER(KvDesc), I32, I32, P, P, P, P, F64, F32, F64, P, SZ, P, P,
                                      P, I32, P]),
 }

@@ -590,6 +590,19 @@ class StepGraph:
         self.graph.replay()
 
 
+def plan_cache_stats() -> dict:
+    """dkv_plan_cache_stats: prefill plans cached, held by captured graphs, pinned bytes."""
+    n, k, b = C.c_int32(), C.c_int32(), C.c_int64()
+    check(lib().dkv_plan_cache_stats(C.byref(n), C.byref(k), C.byref(b)))
+    return {"entries": n.value, "captured": k.value, "pinned_bytes": b.value}
+
+
+def plan_cache_release_captured():
+    """dkv_plan_cache_release_captured: call once every graph that captured a
+    prefill call has been destroyed."""
+    check(lib().dkv_plan_cache_release_captured())
+
+
 def prefill_plan(cache: KVCache, batch: int, num_q_heads: int, q_start, q_pos0, seq_lens,
                  ratio: float) -> dict:
     """dkv_prefill_plan (host int32 arrays)."""

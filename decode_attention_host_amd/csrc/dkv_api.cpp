@@ -182,6 +182,21 @@ dkv_status validate_ratio(double r) {
 std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e);
 std::shared_ptr<PlanEntry> cache_find(const std::string& key);
 
+// Drops the least recently used entries not held by a captured graph until
+// the cache is within its capacity (caller holds c.mu); the dropped entries
+// go to *evicted, to be released outside the lock.
+void cache_trim(PlanCache& c, std::vector<std::shared_ptr<PlanEntry>>* evicted) {
+  auto lit = c.lru.end();
+  while (c.map.size() > PlanCache::kCap && lit != c.lru.begin()) {
+    --lit;
+    auto mit = c.map.find(*lit);
+    if (mit->second.first->captured) continue;
+    evicted->push_back(mit->second.first);
+    c.map.erase(mit);
+    lit = c.lru.erase(lit);
+  }
+}
+
 // Stores a freshly built plan in the cache (or returns the entry another
 // thread stored first) and evicts unreferenced old entries.
 std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<PlanEntry> e) {
@@ -196,15 +211,7 @@ std::shared_ptr<PlanEntry> cache_insert(const std::string& key, std::shared_ptr<
     } else {
       c.lru.push_front(key);
       c.map.emplace(key, std::make_pair(e, c.lru.begin()));
-      auto lit = c.lru.end();
-      while (c.map.size() > PlanCache::kCap && lit != c.lru.begin()) {
-        --lit;
-        auto mit = c.map.find(*lit);
-        if (mit->second.first->captured) continue;
-        evicted.push_back(mit->second.first);
-        c.map.erase(mit);
-        lit = c.lru.erase(lit);
-      }
+      cache_trim(c, &evicted);
     }
   }
   // evicted images are freed (after a device synchronisation) by the last
@@ -691,6 +698,35 @@ extern "C" {
 const char* dkv_last_error(void) { return g_last_error.c_str(); }
 
 int32_t dkv_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+dkv_status dkv_plan_cache_release_captured(void) {
+  PlanCache& c = cache();
+  std::vector<std::shared_ptr<PlanEntry>> evicted;
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (auto& kv : c.map) kv.second.first->captured = false;
+    cache_trim(c, &evicted);
+  }
+  evicted.clear();  // images freed by their last reference (after a device synchronisation)
+  return ok();
+}
+
+dkv_status dkv_plan_cache_stats(int32_t* entries, int32_t* captured, int64_t* pinned_bytes) {
+  if (!entries || !captured || !pinned_bytes) return set_err(DKV_ERR_INVALID, "entries, captured and pinned_bytes are required");
+  PlanCache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  int32_t n = 0, k = 0;
+  int64_t bytes = 0;
+  for (const auto& kv : c.map) {
+    ++n;
+    if (kv.second.first->captured) ++k;
+    bytes += (int64_t)kv.second.first->bytes;
+  }
+  *entries = n;
+  *captured = k;
+  *pinned_bytes = bytes;
+  return ok();
+}
 
 dkv_status dkv_split_point(double ratio, int64_t length, int64_t* n_host) {
   if (!n_host) return set_err(DKV_ERR_INVALID, "n_host is NULL");

@@ -314,10 +314,28 @@ dkv_status dkv_decode_errors(const dkv_kv_desc* kv, const void* workspace, int32
  * copied once into an HBM staging pool inside the workspace (one read over
  * the host link instead of one per block), within the staging budget of
  * dkv_tuning.stage_max_mib; the workspace size includes that pool.
+ *
+ * Plans are built on the host from the call's host arrays and cached per
+ * shape (up to 64, least recently used dropped first) as images in pinned
+ * host memory; each call copies its image into the workspace on its stream.
+ * An image is freed when dropped and no call holds it, after a device
+ * synchronisation (uploads from it may still be queued).  A plan uploaded
+ * while the stream is capturing a graph is kept, whatever the cache's size,
+ * because the graph's copy reads that image on every replay.
  * ---------------------------------------------------------------------- */
 dkv_status dkv_prefill_plan(const dkv_kv_desc* kv, int32_t batch, int32_t num_q_heads,
                             const int32_t* q_start, const int32_t* q_pos0, const int32_t* seq_lens,
                             double offload_ratio, dkv_plan_info* info);
+
+/* Prefill plan cache.  dkv_plan_cache_release_captured: the caller has
+ * destroyed every graph that captured a prefill call, so their plans are kept
+ * no longer; the cache drops entries down to its capacity (freeing their
+ * images as above) and treats them like any other from now on.  Replaying a
+ * graph that captured a prefill call after this call is undefined.
+ * dkv_plan_cache_stats: entries in the cache, how many of them a captured
+ * graph holds, and their pinned bytes (host pointers, all required). */
+dkv_status dkv_plan_cache_release_captured(void);
+dkv_status dkv_plan_cache_stats(int32_t* entries, int32_t* captured, int64_t* pinned_bytes);
 
 /* Prefill planner introspection (no HIP calls; used by CPU tests): the plan
  * dkv_prefill_plan (fused = 0) or dkv_prefill_fused_plan (fused = 1) would

@@ -388,3 +388,13 @@ def test_staged_plan_layout_and_validation(L):
         assert L.dkv_decode_staged_plan(C.byref(xp), hq, 64, 0.5, 64, C.byref(info)) == dkv_lib.DKV_ERR_UNSUPPORTED
     finally:
         reset_tuning()
+
+
+def test_plan_cache_stats_and_release_without_a_gpu(L):
+    # nothing is captured without a GPU, and releasing captured plans then
+    # drops nothing (the cache is within its capacity) and makes no HIP call
+    n, k, b = C.c_int32(-1), C.c_int32(-1), C.c_int64(-1)
+    assert L.dkv_plan_cache_stats(C.byref(n), C.byref(k), C.byref(b)) == dkv_lib.DKV_OK
+    assert k.value == 0 and 0 <= n.value <= 64 and b.value >= 0
+    assert L.dkv_plan_cache_release_captured() == dkv_lib.DKV_OK
+    assert L.dkv_plan_cache_stats(None, C.byref(k), C.byref(b)) == dkv_lib.DKV_ERR_INVALID

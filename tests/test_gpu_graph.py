@@ -139,4 +139,16 @@ def test_graph_replays_fused_prefill(dk):
     o = ref_o.cpu().numpy().astype(np.float64)[q_start[1]:, [0, 9, 31]]
     l = ref_l.cpu().numpy().astype(np.float64)[q_start[1]:, [0, 9, 31]]
     assert np.abs(o - ro).max() < 2e-3 and np.abs(l - rl).max() < 2e-3
+    # the captured plan is held while its graph may replay, and released on
+    # request once the graph is gone (the helper's graph went out of scope)
+    torch.cuda.synchronize()
+    st = dk.plan_cache_stats()
+    assert st["captured"] >= 1 and st["pinned_bytes"] > 0, st
+    dk.plan_cache_release_captured()
+    st2 = dk.plan_cache_stats()
+    assert st2["captured"] == 0 and st2["entries"] >= 1, st2
+    # the plan still serves eager calls
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(Bufs.out_o, ref_o) and torch.equal(Bufs.out_lse, ref_l)
     cache.free()
