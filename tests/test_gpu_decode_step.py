@@ -345,6 +345,42 @@ def test_workspace_is_left_zeroed_and_clean(dk, queued):
         cache.free()
 
 
+@pytest.mark.parametrize("queued", [False, True])
+def test_split_form_buffers_reused(dk, queued):
+    # The split form on one set of buffers, three calls in a row, with its
+    # units dealt round-robin or (one workgroup per KV head and tier, one-tile
+    # items) taken from the queue counters: the counters are back at zero
+    # after every call and each call matches the oracle.
+    import torch
+    from decode_attention_host_amd.cache_build import paged_cache
+    hkv, hq, d, th = 8, 32, 128, 5e5
+    lens = [700, 33]
+    ks, vs = kv_raw(86, lens, hkv, d)
+    pt, nh, nd = paged_table(86, lens, 16, 0.5)
+    cache = paged_cache(hkv, d, lens, pt, nh, nd, ks, vs, th)
+    if queued:
+        dk.set_tuning(host_wgs=hkv, dev_wgs=hkv, host_chunk=64, dev_chunk=64)
+    try:
+        qb = query(86, 2, hq, d)
+        bufs = dk.alloc_decode_buffers(cache, 2, hq, lens, 0.0)
+        ro, rl = [], []
+        for b, L in enumerate(lens):
+            o1, l1 = O.decode_sequence(qb[b], ks[b], vs[b], L - 1, th, 1 / math.sqrt(d))
+            ro.append(o1)
+            rl.append(l1)
+        for call in range(3):
+            o, lse, _ = dk.decode(cache, _bits(qb), _dev([L - 1 for L in lens]), lens, 0.0, 1 / math.sqrt(d), th,
+                                  bufs=bufs)
+            torch.cuda.synchronize()
+            assert np.all(bufs.workspace[:16].cpu().numpy() == 0), "queue counters left set"
+            _check(o.cpu().numpy(), lse.cpu().numpy(), np.stack(ro), np.stack(rl),
+                   f"split form call {call} ({'queued' if queued else 'dealt'})")
+        assert dk.decode_errors(cache, bufs.workspace) == 0
+    finally:
+        dk.reset_tuning()
+        cache.free()
+
+
 def test_layout_violation_is_flagged_not_read(dk):
     # a length beyond the contiguous layout: the sequence is skipped and
     # flagged; the others are still right
