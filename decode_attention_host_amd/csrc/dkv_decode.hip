@@ -605,21 +605,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
         continue;
       }
-      int k = sg;
-      for (; k + (U - 1) * NSG < cn; k += U * NSG) {
+      // U loads in flight per thread in every round, the last one included:
+      // indices past the chunk reload its last partial and are skipped
+      for (int k = sg; k < cn; k += U * NSG) {
         floatx4 o[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) o[u] = coherent_load4(pr_o, o_off(c0 + k + u * NSG));
+        for (int u = 0; u < U; ++u) o[u] = coherent_load4(pr_o, o_off(c0 + min(k + u * NSG, cn - 1)));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float w = wl[(k + u * NSG) * G + hc];
-          if (w != 0.f) acc += w * o[u];
+          const int kk = k + u * NSG;
+          if (kk < cn) {
+            const float w = wl[kk * G + hc];
+            if (w != 0.f) acc += w * o[u];
+          }
         }
-      }
-      for (; k < cn; k += NSG) {
-        const floatx4 o = coherent_load4(pr_o, o_off(c0 + k));
-        const float w = wl[k * G + hc];
-        if (w != 0.f) acc += w * o;
       }
     }
     *reinterpret_cast<floatx4*>(red + sg * G * D + c * 4) = acc;
