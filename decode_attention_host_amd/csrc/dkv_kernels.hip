@@ -946,26 +946,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeArgs a) {
   const float* po = a.part_o + (size_t)h * D + slice * DW + d4;
   const size_t srow = (size_t)a.hq * D;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = s0 + g;
-  for (; s + (U - 1) * NG < s1; s += U * NG) {
+  // U splits in flight per thread in every round, the last one included:
+  // indices past the list reload its last split and are skipped
+  for (int s = s0 + g; s < s1; s += U * NG) {
     float x[U];
     float4 o[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      x[k] = lse[(size_t)(s + k * NG) * a.hq];
-      o[k] = *reinterpret_cast<const float4*>(po + (size_t)(s + k * NG) * srow);
+      const int sk = min(s + k * NG, s1 - 1);
+      x[k] = lse[(size_t)sk * a.hq];
+      o[k] = *reinterpret_cast<const float4*>(po + (size_t)sk * srow);
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
+      if (s + k * NG >= s1) continue;
       const float w = (x[k] == -INFINITY) ? 0.f : expf(x[k] - M);
       acc.x += w * o[k].x; acc.y += w * o[k].y; acc.z += w * o[k].z; acc.w += w * o[k].w;
     }
-  }
-  for (; s < s1; s += NG) {
-    const float x = lse[(size_t)s * a.hq];
-    const float w = (x == -INFINITY) ? 0.f : expf(x - M);
-    const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * srow);
-    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
   }
   *reinterpret_cast<float4*>(&sm_o[g][d4]) = acc;
   __syncthreads();
@@ -1028,6 +1025,8 @@ __global__ __launch_bounds__(kMergeWaveThreads) void merge_lse_wave_kernel(Merge
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  // (pairs here have one split or a few: the leftovers are loaded one at a
+  // time, since a full round of U would mostly reload the last split)
   int s = s0;
   for (; s + U <= s1; s += U) {
     float x[U], v[U][E];
